@@ -1,0 +1,70 @@
+"""Pins of the oracle's fused LoRA linear (CPU only)."""
+import numpy as np
+import torch
+
+from oracle import linear
+from oracle.numerics import bf16_round
+from oracle.nvfp4 import quantize
+from workloads import bf16_bits, lora_bf16
+
+
+def _case(seed, m, n, k, r, wscale=0.02):
+    rng = np.random.default_rng(seed)
+    w = (rng.standard_normal((n, k)) * wscale).astype(np.float32)
+    x = bf16_bits(rng.standard_normal((m, k), dtype=np.float32))
+    a, b = lora_bf16(r, k, n, seed + 1)
+    return w, x, a, b
+
+
+def test_float64_path_matches_exact_rationals():
+    for seed, (m, n, k, r) in enumerate([(2, 3, 32, 2), (1, 4, 16, 1), (3, 2, 48, 3)]):
+        w, x, a, b = _case(seed, m, n, k, r)
+        codes, scales, st = quantize(w)
+        y64 = linear.lora_linear_f64(x, codes, scales, st, a, b, 2.0)
+        exact = linear.lora_linear_exact(x, codes, scales, st, a, b, 2.0)
+        ex = np.array([[float(v) for v in row] for row in exact])
+        assert np.allclose(y64, ex, rtol=1e-13, atol=0)
+        assert np.array_equal(bf16_round(y64), bf16_round(ex))
+
+
+def test_lora_terms_reduce():
+    w, x, a, b = _case(20, 4, 64, 128, 8)
+    codes, scales, st = quantize(w)
+    base = linear.lora_linear(x, codes, scales, st)
+    assert np.array_equal(linear.lora_linear(x, codes, scales, st, a, np.zeros_like(b), 2.0), base)
+    assert np.array_equal(linear.lora_linear(x, codes, scales, st, a, b, 0.0), base)
+    # W = 0: y is the LoRA product alone; check against torch's CPU float64 matmul
+    zc = np.zeros_like(codes)
+    zs = np.zeros_like(scales)
+    y = linear.lora_linear(x, zc, zs, np.float32(0.0), a, b, 2.0)
+    xt = torch.from_numpy((x.astype(np.uint32) << 16).view(np.float32).astype(np.float64))
+    at = torch.from_numpy((a.astype(np.uint32) << 16).view(np.float32).astype(np.float64))
+    bt = torch.from_numpy((b.astype(np.uint32) << 16).view(np.float32).astype(np.float64))
+    ref = 2.0 * torch.matmul(torch.matmul(xt, at.T), bt.T)
+    assert np.array_equal(y, bf16_round(ref.numpy()))
+
+
+def test_homogeneity_and_row_selection():
+    w, x, a, b = _case(21, 3, 40, 64, 4)
+    codes, scales, st = quantize(w)
+    y = linear.lora_linear(x, codes, scales, st, a, b, 2.0)
+    x2 = bf16_bits(((x.astype(np.uint32) << 16).view(np.float32) * 2).astype(np.float32))
+    y2 = linear.lora_linear(x2, codes, scales, st, a, b, 2.0)
+    assert np.array_equal(y2, 2 * y)
+    rows = np.array([0, 7, 39, 12])
+    assert np.array_equal(linear.lora_linear(x, codes, scales, st, a, b, 2.0, rows=rows), y[:, rows])
+
+
+def test_base_product_against_torch_dequant():
+    # an independent dequantisation: torch CPU float8 decode of the scale bytes
+    w, x, _, _ = _case(22, 5, 32, 64, 1)
+    codes, scales, st = quantize(w)
+    grid = torch.tensor([0, .5, 1, 1.5, 2, 3, 4, 6], dtype=torch.float64)
+    c = torch.from_numpy(codes.astype(np.int64))
+    c4 = torch.stack([c & 15, c >> 4], dim=-1).reshape(32, 64)
+    val = grid[c4 & 7] * torch.where((c4 & 8) > 0, -1.0, 1.0)
+    sb = torch.from_numpy(scales).view(torch.float8_e4m3fn).to(torch.float64)
+    wd = val * sb.repeat_interleave(16, dim=1) * float(st)
+    xt = torch.from_numpy((x.astype(np.uint32) << 16).view(np.float32).astype(np.float64))
+    ref = bf16_round((xt @ wd.T).numpy())
+    assert np.array_equal(linear.lora_linear(x, codes, scales, st), ref)
