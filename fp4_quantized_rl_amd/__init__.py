@@ -1,0 +1,269 @@
+"""NVFP4 + LoRA + AQN rollout hot path for MI355X (gfx950).
+
+Thin ctypes binding of ``libfp4rl.so`` (C ABI declared in include/fp4rl.h).
+This module only marshals arguments: it checks dtype/shape/device/contiguity
+of torch tensors, allocates outputs and workspaces with torch, and passes raw
+device pointers plus torch's current HIP stream. Every step of the
+computation runs in the library's HIP kernels. There is no CPU fallback: if
+the library is not built, every call raises.
+
+Operations (names follow the C ABI):
+  nvfp4_quantize(w)                         -> NVFP4Weight(codes, scales, tensor_scale)
+  fp4_lora_linear(x, wq, lora_a, lora_b, s) -> y = x deq(Wq)^T + s (x A^T) B^T  (bf16)
+  lora_down / fp4_linear_lora_up            -> the two halves of fp4_lora_linear
+  aqn_sigma(s0, s1, k, K)                   -> exponential AQN noise level
+  aqn_rmsnorm(x, w, sigma, seed, step, ...) -> RMSNorm with W_noise = w + sigma z
+  philox_words(seed, step, norm_id, n)      -> raw Philox4x32-10 output blocks
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from dataclasses import dataclass
+
+__all__ = [
+    "LIB_PATH", "Fp4rlError", "load_library", "NVFP4Weight", "nvfp4_quantize", "fp4_lora_linear",
+    "lora_down", "fp4_linear_lora_up", "aqn_sigma", "aqn_rmsnorm", "philox_words",
+    "EXPORTED_SYMBOLS",
+]
+
+LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libfp4rl.so")
+
+F32, BF16 = 0, 1
+_c = ctypes
+_P = _c.c_void_p
+_I64 = _c.c_int64
+_STATUS = _c.c_int32
+
+# name -> (restype, argtypes); must match include/fp4rl.h
+_SIGNATURES = {
+    "fp4rl_status_string": (_c.c_char_p, [_c.c_int32]),
+    "fp4rl_last_error": (_c.c_char_p, []),
+    "fp4rl_abi_version": (_c.c_int32, []),
+    "fp4rl_nvfp4_quantize_workspace": (_c.c_size_t, [_I64, _I64]),
+    "fp4rl_nvfp4_quantize": (_STATUS, [_P, _c.c_int32, _I64, _I64, _P, _P, _P, _P, _c.c_size_t, _P]),
+    "fp4rl_fp4_lora_linear_workspace": (_c.c_size_t, [_I64, _I64, _I64, _I64]),
+    "fp4rl_fp4_lora_linear": (_STATUS, [_P, _I64, _I64, _I64, _P, _P, _P, _P, _P, _I64, _c.c_float, _P, _P,
+                                        _c.c_size_t, _P]),
+    "fp4rl_lora_down": (_STATUS, [_P, _I64, _I64, _P, _I64, _c.c_float, _P, _P]),
+    "fp4rl_fp4_linear_lora_up": (_STATUS, [_P, _I64, _I64, _I64, _P, _P, _P, _P, _P, _I64, _P, _P]),
+    "fp4rl_aqn_sigma": (_c.c_float, [_c.c_float, _c.c_float, _c.c_int32, _c.c_int32]),
+    "fp4rl_aqn_rmsnorm": (_STATUS, [_P, _I64, _I64, _P, _c.c_float, _c.c_uint64, _c.c_uint64, _c.c_uint32,
+                                    _c.c_float, _P, _P, _P]),
+    "fp4rl_philox_words": (_STATUS, [_c.c_uint64, _c.c_uint64, _c.c_uint32, _I64, _P, _P]),
+}
+EXPORTED_SYMBOLS = tuple(_SIGNATURES)
+
+_LIB = None
+
+
+class Fp4rlError(RuntimeError):
+    """A libfp4rl call returned a non-zero status (or the library is missing)."""
+
+    def __init__(self, status: int, detail: str):
+        self.status = status
+        super().__init__(detail)
+
+
+def load_library() -> ctypes.CDLL:
+    """Load libfp4rl.so once; raises Fp4rlError if it has not been built."""
+    global _LIB
+    if _LIB is None:
+        if not os.path.exists(LIB_PATH):
+            raise Fp4rlError(-1, f"{LIB_PATH} is missing: build it with "
+                                 "`python -m fp4_quantized_rl_amd.build` (hipcc, gfx950)")
+        lib = ctypes.CDLL(LIB_PATH)
+        for name, (res, args) in _SIGNATURES.items():
+            fn = getattr(lib, name)
+            fn.restype = res
+            fn.argtypes = args
+        _LIB = lib
+    return _LIB
+
+
+def _check(status: int, what: str) -> None:
+    if status != 0:
+        lib = load_library()
+        name = lib.fp4rl_status_string(status).decode()
+        detail = lib.fp4rl_last_error().decode()
+        raise Fp4rlError(status, f"{what}: {name}: {detail}")
+
+
+def _torch():
+    import torch
+    return torch
+
+
+def _stream(device) -> int:
+    torch = _torch()
+    return torch.cuda.current_stream(device).cuda_stream
+
+
+def _ptr(t):
+    return None if t is None else t.data_ptr()
+
+
+def _dev_tensor(t, name, dtypes, ndim=None):
+    torch = _torch()
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if t.device.type != "cuda":
+        raise ValueError(f"{name} must be on a GPU device (got {t.device})")
+    if t.dtype not in dtypes:
+        raise TypeError(f"{name} has dtype {t.dtype}, expected one of {dtypes}")
+    if ndim is not None and t.dim() != ndim:
+        raise ValueError(f"{name} must be {ndim}-D, got shape {tuple(t.shape)}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    return t
+
+
+@dataclass
+class NVFP4Weight:
+    """An NVFP4 matrix [n, k]: codes uint8 [n, k/2], scales uint8 [n, k/16], tensor_scale fp32 [1]."""
+
+    codes: "object"
+    scales: "object"
+    tensor_scale: "object"
+
+    @property
+    def shape(self):
+        return (self.codes.shape[0], self.codes.shape[1] * 2)
+
+    @property
+    def nbytes(self) -> int:
+        return self.codes.numel() + self.scales.numel() + 4
+
+
+def nvfp4_quantize(w, out: NVFP4Weight | None = None) -> NVFP4Weight:
+    """NVFP4-quantise a [n, k] fp32 or bf16 weight (k % 16 == 0) on its device."""
+    torch = _torch()
+    _dev_tensor(w, "w", (torch.float32, torch.bfloat16), 2)
+    n, k = w.shape
+    if out is None:
+        out = NVFP4Weight(torch.empty((n, k // 2), dtype=torch.uint8, device=w.device),
+                          torch.empty((n, k // 16), dtype=torch.uint8, device=w.device),
+                          torch.empty((1,), dtype=torch.float32, device=w.device))
+    lib = load_library()
+    ws_bytes = lib.fp4rl_nvfp4_quantize_workspace(n, k)
+    ws = torch.empty(max(ws_bytes, 16), dtype=torch.uint8, device=w.device)
+    dt = F32 if w.dtype == torch.float32 else BF16
+    with torch.cuda.device(w.device):
+        _check(lib.fp4rl_nvfp4_quantize(_ptr(w), dt, n, k, _ptr(out.codes), _ptr(out.scales),
+                                        _ptr(out.tensor_scale), _ptr(ws), ws_bytes, _stream(w.device)),
+               "nvfp4_quantize")
+    return out
+
+
+def _linear_args(x, wq: NVFP4Weight):
+    torch = _torch()
+    _dev_tensor(x, "x", (torch.bfloat16,), 2)
+    _dev_tensor(wq.codes, "codes", (torch.uint8,), 2)
+    _dev_tensor(wq.scales, "scales", (torch.uint8,), 2)
+    _dev_tensor(wq.tensor_scale, "tensor_scale", (torch.float32,))
+    m, k = x.shape
+    n = wq.codes.shape[0]
+    if wq.codes.shape[1] * 2 != k or wq.scales.shape != (n, k // 16):
+        raise ValueError(f"x [{m},{k}] does not match the NVFP4 weight {tuple(wq.codes.shape)}")
+    return m, n, k
+
+
+def fp4_lora_linear(x, wq: NVFP4Weight, lora_a=None, lora_b=None, lora_scale: float = 0.0,
+                    out=None, workspace=None):
+    """y = bf16(x deq(Wq)^T + lora_scale (x A^T) B^T); x bf16 [m, k], A [r, k], B [n, r]."""
+    torch = _torch()
+    m, n, k = _linear_args(x, wq)
+    r = 0
+    if lora_a is not None or lora_b is not None:
+        _dev_tensor(lora_a, "lora_a", (torch.bfloat16,), 2)
+        _dev_tensor(lora_b, "lora_b", (torch.bfloat16,), 2)
+        r = lora_a.shape[0]
+        if lora_a.shape != (r, k) or lora_b.shape != (n, r):
+            raise ValueError("LoRA shapes must be A [r, k] and B [n, r]")
+    if out is None:
+        out = torch.empty((m, n), dtype=torch.bfloat16, device=x.device)
+    lib = load_library()
+    ws_bytes = lib.fp4rl_fp4_lora_linear_workspace(m, n, k, r)
+    if workspace is None and ws_bytes:
+        workspace = torch.empty(ws_bytes, dtype=torch.uint8, device=x.device)
+    with torch.cuda.device(x.device):
+        _check(lib.fp4rl_fp4_lora_linear(_ptr(x), m, n, k, _ptr(wq.codes), _ptr(wq.scales),
+                                         _ptr(wq.tensor_scale), _ptr(lora_a), _ptr(lora_b), r,
+                                         float(lora_scale), _ptr(out), _ptr(workspace),
+                                         0 if workspace is None else workspace.numel(),
+                                         _stream(x.device)),
+               "fp4_lora_linear")
+    return out
+
+
+def lora_down(x, lora_a, lora_scale: float, out=None):
+    """t = lora_scale * x A^T in fp32 [m, r]."""
+    torch = _torch()
+    _dev_tensor(x, "x", (torch.bfloat16,), 2)
+    _dev_tensor(lora_a, "lora_a", (torch.bfloat16,), 2)
+    m, k = x.shape
+    r = lora_a.shape[0]
+    if lora_a.shape[1] != k:
+        raise ValueError("lora_a must be [r, k]")
+    if out is None:
+        out = torch.empty((m, r), dtype=torch.float32, device=x.device)
+    with torch.cuda.device(x.device):
+        _check(load_library().fp4rl_lora_down(_ptr(x), m, k, _ptr(lora_a), r, float(lora_scale), _ptr(out),
+                                              _stream(x.device)), "lora_down")
+    return out
+
+
+def fp4_linear_lora_up(x, wq: NVFP4Weight, t=None, lora_b=None, out=None):
+    """y = bf16(s_t x deq^T + t B^T) with t fp32 [m, r] from lora_down (or None)."""
+    torch = _torch()
+    m, n, k = _linear_args(x, wq)
+    r = 0
+    if t is not None:
+        _dev_tensor(t, "t", (torch.float32,), 2)
+        _dev_tensor(lora_b, "lora_b", (torch.bfloat16,), 2)
+        r = t.shape[1]
+        if t.shape[0] != m or lora_b.shape != (n, r):
+            raise ValueError("t must be [m, r] and lora_b [n, r]")
+    if out is None:
+        out = torch.empty((m, n), dtype=torch.bfloat16, device=x.device)
+    with torch.cuda.device(x.device):
+        _check(load_library().fp4rl_fp4_linear_lora_up(_ptr(x), m, n, k, _ptr(wq.codes), _ptr(wq.scales),
+                                                       _ptr(wq.tensor_scale), _ptr(t), _ptr(lora_b), r,
+                                                       _ptr(out), _stream(x.device)),
+               "fp4_linear_lora_up")
+    return out
+
+
+def aqn_sigma(sigma_start: float, sigma_end: float, k: int, num_stages: int) -> float:
+    """sigma_k = sigma_start (sigma_end / sigma_start)^(k / (K - 1)); NaN for bad arguments."""
+    return float(load_library().fp4rl_aqn_sigma(sigma_start, sigma_end, k, num_stages))
+
+
+def aqn_rmsnorm(x, w, sigma: float, seed: int, step: int, norm_id: int, eps: float,
+                out=None, w_noise_out=None):
+    """bf16 RMSNorm of x [m, d] with the noisy weight w + sigma * PhiloxNormal(seed, step, norm_id)."""
+    torch = _torch()
+    _dev_tensor(x, "x", (torch.bfloat16,), 2)
+    _dev_tensor(w, "w", (torch.float32,), 1)
+    m, d = x.shape
+    if w.shape[0] != d:
+        raise ValueError("w must have length d")
+    if w_noise_out is not None:
+        _dev_tensor(w_noise_out, "w_noise_out", (torch.float32,), 1)
+    if out is None:
+        out = torch.empty_like(x)
+    with torch.cuda.device(x.device):
+        _check(load_library().fp4rl_aqn_rmsnorm(_ptr(x), m, d, _ptr(w), float(sigma), int(seed), int(step),
+                                                int(norm_id), float(eps), _ptr(out), _ptr(w_noise_out),
+                                                _stream(x.device)), "aqn_rmsnorm")
+    return out
+
+
+def philox_words(seed: int, step: int, norm_id: int, n_blocks: int, device="cuda"):
+    """Raw Philox4x32-10 words of counter blocks 0..n_blocks-1: uint32 as int32 tensor [n_blocks, 4]."""
+    torch = _torch()
+    out = torch.empty((max(n_blocks, 1), 4), dtype=torch.int32, device=device)
+    with torch.cuda.device(out.device):
+        _check(load_library().fp4rl_philox_words(int(seed), int(step), int(norm_id), int(n_blocks), _ptr(out),
+                                                 _stream(out.device)), "philox_words")
+    return out[:n_blocks]

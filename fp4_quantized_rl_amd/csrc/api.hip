@@ -1,0 +1,260 @@
+// C ABI of libfp4rl: argument validation, device check, dispatch.
+// Declarations, semantics and error behaviour are documented in include/fp4rl.h.
+#include <atomic>
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+
+#include "fp4rl.h"
+#include "launch.hpp"
+
+namespace {
+
+thread_local char g_err[512] = "";
+
+fp4rl_status fail(fp4rl_status s, const char* fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  std::vsnprintf(g_err, sizeof(g_err), fmt, ap);
+  va_end(ap);
+  return s;
+}
+
+fp4rl_status ok() {
+  g_err[0] = '\0';
+  return FP4RL_OK;
+}
+
+bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+
+constexpr int64_t kMaxDim = (int64_t)1 << 31;  // kernels index rows and columns with int
+constexpr int kMaxDevices = 64;
+std::atomic<int> g_dev_state[kMaxDevices];  // 0 unknown, 1 gfx950, 2 other arch
+
+fp4rl_status check_device() {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return fail(FP4RL_ERR_HIP, "hipGetDevice: %s", hipGetErrorString(e));
+  if (dev < 0 || dev >= kMaxDevices) return fail(FP4RL_ERR_HIP, "device ordinal %d out of range", dev);
+  int s = g_dev_state[dev].load(std::memory_order_acquire);
+  if (s == 0) {
+    hipDeviceProp_t p;
+    e = hipGetDeviceProperties(&p, dev);
+    if (e != hipSuccess) return fail(FP4RL_ERR_HIP, "hipGetDeviceProperties: %s", hipGetErrorString(e));
+    s = std::strncmp(p.gcnArchName, "gfx950", 6) == 0 ? 1 : 2;
+    g_dev_state[dev].store(s, std::memory_order_release);
+    if (s == 2) return fail(FP4RL_ERR_ARCH, "device %d is %s, not gfx950", dev, p.gcnArchName);
+  }
+  if (s != 1) return fail(FP4RL_ERR_ARCH, "device %d is not gfx950", dev);
+  return FP4RL_OK;
+}
+
+fp4rl_status launched(hipError_t e, const char* what) {
+  if (e != hipSuccess) return fail(FP4RL_ERR_HIP, "%s launch: %s", what, hipGetErrorString(e));
+  return ok();
+}
+
+size_t round_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
+
+#define FP4RL_REQUIRE(cond, status, ...) \
+  do {                                   \
+    if (!(cond)) return fail(status, __VA_ARGS__); \
+  } while (0)
+
+#define FP4RL_CHECK(expr)              \
+  do {                                 \
+    fp4rl_status s_ = (expr);          \
+    if (s_ != FP4RL_OK) return s_;     \
+  } while (0)
+
+fp4rl_status check_linear_shape(int64_t m, int64_t n, int64_t k, int64_t r) {
+  FP4RL_REQUIRE(m >= 0 && n >= 0 && k >= 0 && r >= 0, FP4RL_ERR_SHAPE,
+                "negative size (m=%lld n=%lld k=%lld r=%lld)", (long long)m, (long long)n, (long long)k, (long long)r);
+  FP4RL_REQUIRE(k > 0 && k % 16 == 0, FP4RL_ERR_SHAPE, "k=%lld must be a positive multiple of 16", (long long)k);
+  FP4RL_REQUIRE(m < kMaxDim && n < kMaxDim && k < kMaxDim, FP4RL_ERR_SHAPE, "dimension >= 2^31");
+  FP4RL_REQUIRE(r <= fp4rl::kMaxRank, FP4RL_ERR_SHAPE, "rank r=%lld exceeds %lld", (long long)r,
+                (long long)fp4rl::kMaxRank);
+  return FP4RL_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* fp4rl_status_string(int32_t status) {
+  switch (status) {
+    case FP4RL_OK: return "FP4RL_OK";
+    case FP4RL_ERR_NULL: return "FP4RL_ERR_NULL";
+    case FP4RL_ERR_SHAPE: return "FP4RL_ERR_SHAPE";
+    case FP4RL_ERR_DTYPE: return "FP4RL_ERR_DTYPE";
+    case FP4RL_ERR_ALIGN: return "FP4RL_ERR_ALIGN";
+    case FP4RL_ERR_WORKSPACE: return "FP4RL_ERR_WORKSPACE";
+    case FP4RL_ERR_ARCH: return "FP4RL_ERR_ARCH";
+    case FP4RL_ERR_HIP: return "FP4RL_ERR_HIP";
+    case FP4RL_ERR_VALUE: return "FP4RL_ERR_VALUE";
+    default: return "FP4RL_UNKNOWN_STATUS";
+  }
+}
+
+const char* fp4rl_last_error(void) { return g_err; }
+
+int32_t fp4rl_abi_version(void) { return FP4RL_ABI_VERSION; }
+
+// ---------------------------------------------------------------- quantise --
+
+size_t fp4rl_nvfp4_quantize_workspace(int64_t n, int64_t k) {
+  (void)n;
+  (void)k;
+  return fp4rl::quantize_workspace_bytes();
+}
+
+fp4rl_status fp4rl_nvfp4_quantize(const void* w, int32_t w_dtype, int64_t n, int64_t k, uint8_t* codes,
+                                  uint8_t* scales, float* tensor_scale, void* workspace, size_t workspace_bytes,
+                                  fp4rl_stream stream) {
+  FP4RL_REQUIRE(n >= 0 && k >= 0, FP4RL_ERR_SHAPE, "negative size (n=%lld k=%lld)", (long long)n, (long long)k);
+  FP4RL_REQUIRE(k % 16 == 0, FP4RL_ERR_SHAPE, "k=%lld is not a multiple of 16", (long long)k);
+  FP4RL_REQUIRE(n < kMaxDim && k < kMaxDim && n * k < ((int64_t)1 << 46), FP4RL_ERR_SHAPE, "matrix too large");
+  FP4RL_REQUIRE(w_dtype == FP4RL_F32 || w_dtype == FP4RL_BF16, FP4RL_ERR_DTYPE, "w_dtype=%d", (int)w_dtype);
+  FP4RL_REQUIRE(tensor_scale != nullptr, FP4RL_ERR_NULL, "tensor_scale is NULL");
+  FP4RL_REQUIRE(aligned(tensor_scale, 4), FP4RL_ERR_ALIGN, "tensor_scale not 4-byte aligned");
+  const bool empty = n == 0 || k == 0;
+  if (!empty) {
+    FP4RL_REQUIRE(w && codes && scales, FP4RL_ERR_NULL, "w, codes and scales must be non-NULL");
+    FP4RL_REQUIRE(workspace != nullptr, FP4RL_ERR_WORKSPACE, "workspace is NULL");
+    FP4RL_REQUIRE(workspace_bytes >= fp4rl::quantize_workspace_bytes(), FP4RL_ERR_WORKSPACE,
+                  "workspace %zu < %zu bytes", workspace_bytes, fp4rl::quantize_workspace_bytes());
+    FP4RL_REQUIRE(aligned(w, 16) && aligned(codes, 16) && aligned(scales, 16) && aligned(workspace, 16),
+                  FP4RL_ERR_ALIGN, "w, codes, scales and workspace must be 16-byte aligned");
+  }
+  FP4RL_CHECK(check_device());
+  return launched(fp4rl::launch_quantize(w, w_dtype == FP4RL_BF16, n, k, codes, scales, tensor_scale,
+                                         static_cast<uint32_t*>(workspace), stream),
+                  "nvfp4_quantize");
+}
+
+// ------------------------------------------------------------------ linear --
+
+size_t fp4rl_fp4_lora_linear_workspace(int64_t m, int64_t n, int64_t k, int64_t r) {
+  (void)n;
+  (void)k;
+  if (m <= 0 || r <= 0) return 0;
+  return round_up((size_t)m * (size_t)r * sizeof(float), 256);
+}
+
+fp4rl_status fp4rl_lora_down(const uint16_t* x, int64_t m, int64_t k, const uint16_t* lora_a, int64_t r,
+                             float lora_scale, float* t, fp4rl_stream stream) {
+  FP4RL_CHECK(check_linear_shape(m, 1, k, r));
+  FP4RL_REQUIRE(std::isfinite(lora_scale), FP4RL_ERR_VALUE, "lora_scale is not finite");
+  if (m == 0 || r == 0) return ok();
+  FP4RL_REQUIRE(x && lora_a && t, FP4RL_ERR_NULL, "x, lora_a and t must be non-NULL");
+  FP4RL_REQUIRE(aligned(x, 16) && aligned(lora_a, 16) && aligned(t, 16), FP4RL_ERR_ALIGN,
+                "x, lora_a and t must be 16-byte aligned");
+  FP4RL_CHECK(check_device());
+  return launched(fp4rl::launch_lora_down(x, m, k, lora_a, r, lora_scale, t, stream), "lora_down");
+}
+
+static fp4rl_status check_linear_main(const uint16_t* x, int64_t m, int64_t n, int64_t k, const uint8_t* codes,
+                                      const uint8_t* scales, const float* tensor_scale, const float* t,
+                                      const uint16_t* lora_b, int64_t r, uint16_t* y) {
+  FP4RL_REQUIRE(x && codes && scales && tensor_scale && y, FP4RL_ERR_NULL,
+                "x, codes, scales, tensor_scale and y must be non-NULL");
+  FP4RL_REQUIRE(aligned(x, 16) && aligned(codes, 16) && aligned(scales, 16) && aligned(y, 16), FP4RL_ERR_ALIGN,
+                "x, codes, scales and y must be 16-byte aligned");
+  FP4RL_REQUIRE(aligned(tensor_scale, 4), FP4RL_ERR_ALIGN, "tensor_scale not 4-byte aligned");
+  if (r > 0) {
+    FP4RL_REQUIRE(t && lora_b, FP4RL_ERR_NULL, "r > 0 needs t and lora_b");
+    FP4RL_REQUIRE(aligned(t, 16) && aligned(lora_b, 16), FP4RL_ERR_ALIGN, "t and lora_b must be 16-byte aligned");
+  }
+  (void)m;
+  (void)n;
+  (void)k;
+  return FP4RL_OK;
+}
+
+fp4rl_status fp4rl_fp4_linear_lora_up(const uint16_t* x, int64_t m, int64_t n, int64_t k, const uint8_t* codes,
+                                      const uint8_t* scales, const float* tensor_scale, const float* t,
+                                      const uint16_t* lora_b, int64_t r, uint16_t* y, fp4rl_stream stream) {
+  FP4RL_CHECK(check_linear_shape(m, n, k, r));
+  if (m == 0 || n == 0) return ok();
+  FP4RL_CHECK(check_linear_main(x, m, n, k, codes, scales, tensor_scale, t, lora_b, r, y));
+  FP4RL_CHECK(check_device());
+  return launched(fp4rl::launch_fp4_linear(x, m, n, k, codes, scales, tensor_scale, r > 0 ? t : nullptr,
+                                           r > 0 ? lora_b : nullptr, r, y, stream),
+                  "fp4_linear");
+}
+
+fp4rl_status fp4rl_fp4_lora_linear(const uint16_t* x, int64_t m, int64_t n, int64_t k, const uint8_t* codes,
+                                   const uint8_t* scales, const float* tensor_scale, const uint16_t* lora_a,
+                                   const uint16_t* lora_b, int64_t r, float lora_scale, uint16_t* y,
+                                   void* workspace, size_t workspace_bytes, fp4rl_stream stream) {
+  FP4RL_CHECK(check_linear_shape(m, n, k, r));
+  FP4RL_REQUIRE(std::isfinite(lora_scale), FP4RL_ERR_VALUE, "lora_scale is not finite");
+  FP4RL_REQUIRE((lora_a == nullptr) == (lora_b == nullptr), FP4RL_ERR_NULL,
+                "lora_a and lora_b must both be NULL or both be set");
+  if (lora_a == nullptr) r = 0;
+  if (m == 0 || n == 0) return ok();
+  float* t = static_cast<float*>(workspace);
+  if (r > 0) {
+    const size_t need = fp4rl_fp4_lora_linear_workspace(m, n, k, r);
+    FP4RL_REQUIRE(workspace != nullptr && workspace_bytes >= need, FP4RL_ERR_WORKSPACE,
+                  "workspace %zu < %zu bytes", workspace_bytes, need);
+    FP4RL_REQUIRE(aligned(lora_a, 16) && aligned(workspace, 16), FP4RL_ERR_ALIGN,
+                  "lora_a and workspace must be 16-byte aligned");
+  }
+  FP4RL_CHECK(check_linear_main(x, m, n, k, codes, scales, tensor_scale, t, lora_b, r, y));
+  FP4RL_CHECK(check_device());
+  if (r > 0) {
+    fp4rl_status s = launched(fp4rl::launch_lora_down(x, m, k, lora_a, r, lora_scale, t, stream), "lora_down");
+    if (s != FP4RL_OK) return s;
+  }
+  return launched(fp4rl::launch_fp4_linear(x, m, n, k, codes, scales, tensor_scale, r > 0 ? t : nullptr,
+                                           r > 0 ? lora_b : nullptr, r, y, stream),
+                  "fp4_linear");
+}
+
+// --------------------------------------------------------------------- AQN --
+
+float fp4rl_aqn_sigma(float sigma_start, float sigma_end, int32_t k, int32_t num_stages) {
+  if (num_stages < 1 || k < 0 || k >= num_stages || !(sigma_start > 0.0f) || !(sigma_end > 0.0f) ||
+      !std::isfinite(sigma_start) || !std::isfinite(sigma_end))
+    return std::nanf("");
+  if (num_stages == 1) return sigma_start;
+  const double frac = (double)k / (double)(num_stages - 1);
+  return (float)((double)sigma_start * std::pow((double)sigma_end / (double)sigma_start, frac));
+}
+
+fp4rl_status fp4rl_aqn_rmsnorm(const uint16_t* x, int64_t m, int64_t d, const float* w, float sigma, uint64_t seed,
+                               uint64_t step, uint32_t norm_id, float eps, uint16_t* y, float* w_noise_out,
+                               fp4rl_stream stream) {
+  FP4RL_REQUIRE(m >= 0 && d >= 0, FP4RL_ERR_SHAPE, "negative size (m=%lld d=%lld)", (long long)m, (long long)d);
+  FP4RL_REQUIRE(std::isfinite(sigma) && sigma >= 0.0f, FP4RL_ERR_VALUE, "sigma must be finite and >= 0");
+  FP4RL_REQUIRE(std::isfinite(eps) && eps >= 0.0f, FP4RL_ERR_VALUE, "eps must be finite and >= 0");
+  if ((m == 0 && w_noise_out == nullptr) || d == 0) return ok();
+  FP4RL_REQUIRE(d <= fp4rl::kAqnMaxD, FP4RL_ERR_SHAPE, "d=%lld exceeds %lld", (long long)d,
+                (long long)fp4rl::kAqnMaxD);
+  FP4RL_REQUIRE(m < kMaxDim * 64, FP4RL_ERR_SHAPE, "too many rows");
+  FP4RL_REQUIRE(w != nullptr, FP4RL_ERR_NULL, "w is NULL");
+  FP4RL_REQUIRE(aligned(w, 16), FP4RL_ERR_ALIGN, "w must be 16-byte aligned");
+  if (m > 0) {
+    FP4RL_REQUIRE(x && y, FP4RL_ERR_NULL, "x and y must be non-NULL");
+    FP4RL_REQUIRE(aligned(x, 16) && aligned(y, 16), FP4RL_ERR_ALIGN, "x and y must be 16-byte aligned");
+  }
+  FP4RL_REQUIRE(w_noise_out == nullptr || aligned(w_noise_out, 16), FP4RL_ERR_ALIGN,
+                "w_noise_out must be 16-byte aligned");
+  FP4RL_CHECK(check_device());
+  return launched(fp4rl::launch_aqn_rmsnorm(x, m, d, w, sigma, seed, step, norm_id, eps, y, w_noise_out, stream),
+                  "aqn_rmsnorm");
+}
+
+fp4rl_status fp4rl_philox_words(uint64_t seed, uint64_t step, uint32_t norm_id, int64_t n_blocks, uint32_t* out,
+                                fp4rl_stream stream) {
+  FP4RL_REQUIRE(n_blocks >= 0 && n_blocks <= ((int64_t)1 << 32), FP4RL_ERR_SHAPE, "n_blocks out of range");
+  if (n_blocks == 0) return ok();
+  FP4RL_REQUIRE(out != nullptr, FP4RL_ERR_NULL, "out is NULL");
+  FP4RL_REQUIRE(aligned(out, 16), FP4RL_ERR_ALIGN, "out must be 16-byte aligned");
+  FP4RL_CHECK(check_device());
+  return launched(fp4rl::launch_philox_words(seed, step, norm_id, n_blocks, out, stream), "philox_words");
+}
+
+}  // extern "C"

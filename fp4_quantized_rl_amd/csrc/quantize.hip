@@ -1,0 +1,195 @@
+// NVFP4 block quantiser for gfx950.
+//
+// Follows the QeRL explainer page ("NVFP4 quantization and LoRA": frozen
+// weights held in 4-bit NVFP4) and the TRACE article ("Engineering view of
+// the mechanism": a small group of values shares one scale and each value
+// rounds up or down to a neighbouring grid point). Format: 16-element blocks
+// along K, one OCP E4M3 scale byte per block, one fp32 tensor scale, E2M1
+// codes packed two per byte (even element in the low nibble).
+//
+// Two HBM-bound passes, because the global amax is a true dependency of
+// every block scale:
+//   1. amax_kernel: grid-stride |w| max as uint32 bit patterns (exact and
+//      order-free for non-negative floats); one partial per workgroup.
+//   2. encode_kernel: every workgroup reduces the partials to amax itself
+//      (no atomics, no memset, no third launch), then each quad of lanes
+//      owns one 16-element block: 16-byte loads, quad max by two xor
+//      shuffles, E4M3 byte, and 16 exact nearest-even E2M1 codes.
+// Exactness: every comparison of |x| with a grid midpoint m*D is the sign of
+// fmaf(m, D, -|x|); the exact difference is 0 or at least 2^-149 in
+// magnitude once D >= 2^-100 (blocks with smaller D are rescaled by 2^64,
+// exactly), so the fused result has the exact sign.
+#include <algorithm>
+
+#include "device.hpp"
+#include "launch.hpp"
+
+namespace fp4rl {
+namespace {
+
+constexpr int kThreads = 256;
+constexpr int kUnroll = 4;
+
+__device__ __forceinline__ uint32_t absbits(float v) { return __float_as_uint(v) & 0x7FFFFFFFu; }
+
+// |.| maximum of one 16-byte vector, as fp32 bit patterns.
+template <bool BF16>
+__device__ __forceinline__ uint32_t vec_absmax(uint4 v) {
+  if constexpr (BF16) {
+    uint32_t m = max(max((v.x << 16) & 0x7FFF0000u, v.x & 0x7FFF0000u),
+                     max((v.y << 16) & 0x7FFF0000u, v.y & 0x7FFF0000u));
+    return max(m, max(max((v.z << 16) & 0x7FFF0000u, v.z & 0x7FFF0000u),
+                      max((v.w << 16) & 0x7FFF0000u, v.w & 0x7FFF0000u)));
+  } else {
+    return max(max(v.x & 0x7FFFFFFFu, v.y & 0x7FFFFFFFu), max(v.z & 0x7FFFFFFFu, v.w & 0x7FFFFFFFu));
+  }
+}
+
+template <bool BF16>
+__global__ __launch_bounds__(kThreads) void amax_kernel(const uint4* __restrict__ w, int64_t nvec,
+                                                         uint32_t* __restrict__ partial) {
+  const int64_t stride = (int64_t)gridDim.x * kThreads;
+  int64_t i = (int64_t)blockIdx.x * kThreads + threadIdx.x;
+  uint32_t mx = 0;
+  for (; i + (kUnroll - 1) * stride < nvec; i += kUnroll * stride) {
+    uint4 v[kUnroll];
+#pragma unroll
+    for (int u = 0; u < kUnroll; ++u) v[u] = w[i + u * stride];
+#pragma unroll
+    for (int u = 0; u < kUnroll; ++u) mx = max(mx, vec_absmax<BF16>(v[u]));
+  }
+  for (; i < nvec; i += stride) mx = max(mx, vec_absmax<BF16>(w[i]));
+  mx = wave_max_u32(mx);
+  __shared__ uint32_t red[kThreads / kWave];
+  if ((threadIdx.x & (kWave - 1)) == 0) red[threadIdx.x / kWave] = mx;
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    uint32_t m = red[0];
+#pragma unroll
+    for (int j = 1; j < kThreads / kWave; ++j) m = max(m, red[j]);
+    partial[blockIdx.x] = m;
+  }
+}
+
+// Nearest E4M3 byte to r >= 0, ties to even, saturating at 448 (0x7E).
+__device__ __forceinline__ uint32_t e4m3_encode(float r) {
+  if (!(r < 448.0f)) return 0x7Eu;
+  if (r < 0x1p-6f) return (uint32_t)__builtin_rintf(r * 512.0f);  // subnormal grid m*2^-9; 8 -> 0x08
+  uint32_t b = __float_as_uint(r);
+  b += 0x7FFFFu + ((b >> 20) & 1u);  // round the 23-bit mantissa to 3 bits, half to even
+  return min((b >> 20) - (120u << 3), 0x7Eu);
+}
+
+// E2M1 code of x for block step D (Ds = D or D*2^64, xs = 1 or 2^64).
+__device__ __forceinline__ uint32_t e2m1_encode(float x, bool dzero, float Ds, float xs) {
+#pragma clang fp contract(off)
+  const float ax = fabsf(x) * xs;
+  uint32_t k = (uint32_t)(fmaf(0.25f, Ds, -ax) < 0.0f) + (uint32_t)(fmaf(0.75f, Ds, -ax) <= 0.0f) +
+               (uint32_t)(fmaf(1.25f, Ds, -ax) < 0.0f) + (uint32_t)(fmaf(1.75f, Ds, -ax) <= 0.0f) +
+               (uint32_t)(fmaf(2.5f, Ds, -ax) < 0.0f) + (uint32_t)(fmaf(3.5f, Ds, -ax) <= 0.0f) +
+               (uint32_t)(fmaf(5.0f, Ds, -ax) < 0.0f);
+  k = dzero ? 0u : k;
+  return k | ((__float_as_uint(x) >> 28) & 8u);
+}
+
+template <bool BF16>
+__device__ __forceinline__ void load_quarter(const void* w, int64_t idx, float v[4]) {
+  if constexpr (BF16) {
+    const uint2 r = ld_nt8(reinterpret_cast<const uint2*>(w) + idx);
+    v[0] = bf16_lo(r.x); v[1] = bf16_hi(r.x); v[2] = bf16_lo(r.y); v[3] = bf16_hi(r.y);
+  } else {
+    const uint4 r = ld_nt16(reinterpret_cast<const uint4*>(w) + idx);
+    v[0] = __uint_as_float(r.x); v[1] = __uint_as_float(r.y); v[2] = __uint_as_float(r.z); v[3] = __uint_as_float(r.w);
+  }
+}
+
+template <bool BF16>
+__global__ __launch_bounds__(kThreads) void encode_kernel(const void* __restrict__ w, int64_t nblk,
+                                                           const uint32_t* __restrict__ partial,
+                                                           int npartial, uint8_t* __restrict__ codes,
+                                                           uint8_t* __restrict__ scales,
+                                                           float* __restrict__ tensor_scale) {
+#pragma clang fp contract(off)
+  __shared__ uint32_t red[kThreads / kWave];
+  uint32_t mx = 0;
+  for (int i = threadIdx.x; i < npartial; i += kThreads) mx = max(mx, partial[i]);
+  mx = wave_max_u32(mx);
+  if ((threadIdx.x & (kWave - 1)) == 0) red[threadIdx.x / kWave] = mx;
+  __syncthreads();
+  mx = red[0];
+#pragma unroll
+  for (int j = 1; j < kThreads / kWave; ++j) mx = max(mx, red[j]);
+  const float st = __uint_as_float(mx) / 2688.0f;  // IEEE division
+  if (blockIdx.x == 0 && threadIdx.x == 0) *tensor_scale = st;
+  const float six_st = 6.0f * st;
+
+  const int q = threadIdx.x & 3;  // quarter of the block this lane holds
+  const int64_t nquads = (int64_t)gridDim.x * (kThreads / 4);
+  uint16_t* code16 = reinterpret_cast<uint16_t*>(codes);
+  for (int64_t b0 = ((int64_t)blockIdx.x * kThreads + threadIdx.x) / 4; b0 < nblk;
+       b0 += kUnroll * nquads) {
+    float v[kUnroll][4];
+#pragma unroll
+    for (int u = 0; u < kUnroll; ++u) {
+      const int64_t b = b0 + u * nquads;
+      if (b < nblk) load_quarter<BF16>(w, 4 * b + q, v[u]);
+    }
+#pragma unroll
+    for (int u = 0; u < kUnroll; ++u) {
+      const int64_t b = b0 + u * nquads;
+      if (b >= nblk) break;  // uniform across the quad
+      uint32_t ab = max(max(absbits(v[u][0]), absbits(v[u][1])), max(absbits(v[u][2]), absbits(v[u][3])));
+      ab = max(ab, (uint32_t)__shfl_xor((int)ab, 1, kWave));
+      ab = max(ab, (uint32_t)__shfl_xor((int)ab, 2, kWave));
+      const float a_b = __uint_as_float(ab);
+      const uint32_t byte = (st != 0.0f && a_b != 0.0f) ? e4m3_encode(a_b / six_st) : 0u;
+      const float D = e4m3_to_f32(byte) * st;
+      const bool tiny = D < 0x1p-100f;
+      const float Ds = tiny ? D * 0x1p64f : D;
+      const float xs = tiny ? 0x1p64f : 1.0f;
+      const bool dz = D == 0.0f;
+      const uint32_t c = e2m1_encode(v[u][0], dz, Ds, xs) | (e2m1_encode(v[u][1], dz, Ds, xs) << 4) |
+                         (e2m1_encode(v[u][2], dz, Ds, xs) << 8) | (e2m1_encode(v[u][3], dz, Ds, xs) << 12);
+      code16[4 * b + q] = (uint16_t)c;
+      if (q == 0) scales[b] = (uint8_t)byte;
+    }
+  }
+}
+
+__global__ void write_zero_scale(float* tensor_scale) { *tensor_scale = 0.0f; }
+
+}  // namespace
+
+size_t quantize_workspace_bytes() { return kAmaxPartials * sizeof(uint32_t); }
+
+hipError_t launch_quantize(const void* w, bool w_bf16, int64_t n, int64_t k, uint8_t* codes,
+                           uint8_t* scales, float* tensor_scale, uint32_t* partial,
+                           hipStream_t stream) {
+  const int64_t elems = n * k;
+  if (elems == 0) {
+    hipLaunchKernelGGL(write_zero_scale, dim3(1), dim3(1), 0, stream, tensor_scale);
+    return hipGetLastError();
+  }
+  const int64_t nvec = elems / (w_bf16 ? 8 : 4);  // k % 16 == 0, so vectors never straddle
+  const int64_t g1 = std::min<int64_t>(kAmaxPartials, std::max<int64_t>(1, (nvec + kThreads * kUnroll - 1) / (kThreads * kUnroll)));
+  if (w_bf16)
+    hipLaunchKernelGGL(amax_kernel<true>, dim3((unsigned)g1), dim3(kThreads), 0, stream,
+                       reinterpret_cast<const uint4*>(w), nvec, partial);
+  else
+    hipLaunchKernelGGL(amax_kernel<false>, dim3((unsigned)g1), dim3(kThreads), 0, stream,
+                       reinterpret_cast<const uint4*>(w), nvec, partial);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  const int64_t nblk = elems / 16;
+  const int64_t per_wg = (kThreads / 4) * kUnroll;
+  const int64_t g2 = std::min<int64_t>(8192, (nblk + per_wg - 1) / per_wg);
+  if (w_bf16)
+    hipLaunchKernelGGL(encode_kernel<true>, dim3((unsigned)g2), dim3(kThreads), 0, stream, w, nblk,
+                       partial, (int)g1, codes, scales, tensor_scale);
+  else
+    hipLaunchKernelGGL(encode_kernel<false>, dim3((unsigned)g2), dim3(kThreads), 0, stream, w, nblk,
+                       partial, (int)g1, codes, scales, tensor_scale);
+  return hipGetLastError();
+}
+
+}  // namespace fp4rl

@@ -1,0 +1,158 @@
+/*
+ * fp4rl.h — C ABI of the NVFP4 + LoRA + AQN rollout hot path for MI355X (gfx950).
+ *
+ * Three operations make up the quantised rollout forward that QeRL describes:
+ *
+ *   fp4rl_nvfp4_quantize   NVFP4 block quantiser of a frozen weight matrix
+ *                          (QeRL explainer page, "NVFP4 quantization and LoRA";
+ *                          TRACE article, "Engineering view of the mechanism":
+ *                          small groups share one scale, each value rounds up or
+ *                          down to a grid point).
+ *   fp4rl_fp4_lora_linear  W4A16 linear with the LoRA update fused in,
+ *                          y = x deq(Wq)^T + s (x A^T) B^T (QeRL explainer,
+ *                          "NVFP4 quantization and LoRA" and "Experimental
+ *                          details": NVFP4 weights with 16-bit LoRA, rollout
+ *                          through a W4A16 kernel).
+ *   fp4rl_aqn_rmsnorm      RMSNorm whose scale carries the adaptive quantisation
+ *                          noise, W_noise = Z_noise + w (QeRL explainer, "Adaptive
+ *                          Quantization Noise": the exponential scheduler and the
+ *                          zero-overhead fold into the norm, with its equation).
+ *
+ * Conventions for every call:
+ *  - Pointers are DEVICE pointers unless marked [host]. Array pointers must be
+ *    16-byte aligned (tensor_scale: 4-byte); otherwise FP4RL_ERR_ALIGN.
+ *  - Matrices are dense row-major. bf16 is passed as uint16_t bit patterns.
+ *  - The caller owns every buffer, workspaces included. The library allocates
+ *    and frees nothing, keeps no state across calls except a per-device
+ *    "is gfx950" flag, and never synchronises: work is queued on `stream`
+ *    (NULL = the legacy default stream) and the call returns at once.
+ *  - Arguments are validated before anything is queued; on error nothing is
+ *    written and a non-zero status is returned, with a detail string in
+ *    fp4rl_last_error() (thread-local). A failed launch returns FP4RL_ERR_HIP.
+ *    Device faults surface at the caller's next synchronisation, as in HIP.
+ *  - Sizes are int64_t; a size of 0 is an empty no-op (OK).
+ *  - Outputs must not alias inputs. Results for non-finite inputs are
+ *    unspecified (the quantiser then writes a non-finite tensor scale).
+ *  - Calls on different streams are independent; the library is thread-safe.
+ *  - Every result is deterministic: no floating-point atomics are used, so
+ *    repeated calls on the same inputs give identical bytes.
+ */
+#ifndef FP4RL_H
+#define FP4RL_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define FP4RL_ABI_VERSION 1
+
+/* Same object as HIP's hipStream_t. */
+typedef struct ihipStream_t* fp4rl_stream;
+
+typedef enum fp4rl_status {
+  FP4RL_OK = 0,
+  FP4RL_ERR_NULL = 1,      /* a required pointer is NULL */
+  FP4RL_ERR_SHAPE = 2,     /* negative size, k not a multiple of 16, r > 256, d too large */
+  FP4RL_ERR_DTYPE = 3,     /* unknown dtype code */
+  FP4RL_ERR_ALIGN = 4,     /* pointer not aligned as stated above */
+  FP4RL_ERR_WORKSPACE = 5, /* workspace NULL or smaller than the matching *_workspace() size */
+  FP4RL_ERR_ARCH = 6,      /* the current device is not gfx950 */
+  FP4RL_ERR_HIP = 7,       /* a HIP runtime call failed; text in fp4rl_last_error() */
+  FP4RL_ERR_VALUE = 8      /* a scalar is out of range (negative or non-finite sigma/eps/scale) */
+} fp4rl_status;
+
+typedef enum fp4rl_dtype { FP4RL_F32 = 0, FP4RL_BF16 = 1 } fp4rl_dtype;
+
+/* [host] Static name of a status code. */
+const char* fp4rl_status_string(int32_t status);
+/* [host] Detail of the last failed call on this thread ("" if none). */
+const char* fp4rl_last_error(void);
+/* [host] FP4RL_ABI_VERSION of the built library. */
+int32_t fp4rl_abi_version(void);
+
+/* ------------------------------------------------------------------------
+ * NVFP4 quantiser.
+ *
+ * W [n][k] (fp32 or bf16, w_dtype) -> codes [n][k/2] bytes, scales [n][k/16]
+ * bytes, tensor_scale [1] fp32. k % 16 == 0.
+ *   s_t  = fp32(amax / 2688), amax = max|W| (2688 = 6 * 448);
+ *   byte = E4M3 (OCP e4m3fn, nearest-even, saturating at 448, subnormals kept)
+ *          of r_b = fp32(a_b / fp32(6 s_t)), a_b = max|block|; 0 if s_t == 0;
+ *   code = sign(x) << 3 | k, where g_k * fp32(S_b s_t) is the E2M1 grid point
+ *          {0,.5,1,1.5,2,3,4,6} nearest to |x| in exact arithmetic, ties to even k.
+ *   Blocks run along k; element 2j of a row is the low nibble of byte j.
+ * Two kernels: a tensor-amax pass (per-workgroup partial maxima in the
+ * workspace, no atomics) and an encode pass that re-reads W.
+ * Workspace: fp4rl_nvfp4_quantize_workspace(n, k) bytes, 16-byte aligned.
+ * ---------------------------------------------------------------------- */
+size_t fp4rl_nvfp4_quantize_workspace(int64_t n, int64_t k);
+fp4rl_status fp4rl_nvfp4_quantize(const void* w, int32_t w_dtype, int64_t n, int64_t k,
+                                  uint8_t* codes, uint8_t* scales, float* tensor_scale,
+                                  void* workspace, size_t workspace_bytes, fp4rl_stream stream);
+
+/* ------------------------------------------------------------------------
+ * Fused W4A16 + LoRA linear:
+ *   y[m][n] = bf16_rne( s_t * sum_k x[m][k] g(code[n][k]) S_b(n,k)
+ *                       + sum_j t[m][j] B[n][j] ),   t = lora_scale * x A^T.
+ * x bf16 [m][k]; codes/scales/tensor_scale as produced by fp4rl_nvfp4_quantize
+ * for an [n][k] matrix; A bf16 [r][k]; B bf16 [n][r]; y bf16 [m][n].
+ * k % 16 == 0; 0 <= r <= 256; r == 0 or lora_a == lora_b == NULL means no
+ * LoRA term. Accumulation is fp32; the output is rounded once to bf16.
+ * Launches the LoRA down-projection (when r > 0) and then the main kernel,
+ * chosen by m: an MFMA skinny kernel for decode-shaped m, a tiled MFMA GEMM
+ * with LDS-dequantised weight tiles for prefill-shaped m.
+ * Workspace: fp4rl_fp4_lora_linear_workspace(m, n, k, r) bytes (holds t).
+ * ---------------------------------------------------------------------- */
+size_t fp4rl_fp4_lora_linear_workspace(int64_t m, int64_t n, int64_t k, int64_t r);
+fp4rl_status fp4rl_fp4_lora_linear(const uint16_t* x, int64_t m, int64_t n, int64_t k,
+                                   const uint8_t* codes, const uint8_t* scales,
+                                   const float* tensor_scale, const uint16_t* lora_a,
+                                   const uint16_t* lora_b, int64_t r, float lora_scale,
+                                   uint16_t* y, void* workspace, size_t workspace_bytes,
+                                   fp4rl_stream stream);
+
+/* The two halves of fp4rl_fp4_lora_linear, for callers that produce t
+ * elsewhere or time the main kernel alone.
+ * fp4rl_lora_down: t [m][r] fp32 = lora_scale * x A^T (fp32 accumulate).
+ * fp4rl_fp4_linear_lora_up: y = bf16(s_t * x deq^T + t B^T); t may be NULL
+ * (with r == 0) for the base product alone. */
+fp4rl_status fp4rl_lora_down(const uint16_t* x, int64_t m, int64_t k, const uint16_t* lora_a,
+                             int64_t r, float lora_scale, float* t, fp4rl_stream stream);
+fp4rl_status fp4rl_fp4_linear_lora_up(const uint16_t* x, int64_t m, int64_t n, int64_t k,
+                                      const uint8_t* codes, const uint8_t* scales,
+                                      const float* tensor_scale, const float* t,
+                                      const uint16_t* lora_b, int64_t r, uint16_t* y,
+                                      fp4rl_stream stream);
+
+/* ------------------------------------------------------------------------
+ * AQN.
+ * fp4rl_aqn_sigma [host]: sigma_k = sigma_start (sigma_end/sigma_start)^(k/(K-1)),
+ *   computed in double and returned as float; K == 1 gives sigma_start.
+ *   Returns NaN for K < 1, k outside [0, K), or non-positive sigmas.
+ * fp4rl_aqn_rmsnorm: with z = PhiloxNormal(seed, step, norm_id)[0:d],
+ *   w_noise[i] = w[i] + sigma z[i]                     (one vector per call)
+ *   y[m][i]   = bf16_rne(w_noise[i] x[m][i] / sqrt(mean_i x[m][i]^2 + eps)).
+ *   x, y bf16 [m][d]; w fp32 [d]; w_noise_out fp32 [d] or NULL.
+ *   1 <= d <= 16384; sigma >= 0, eps >= 0, both finite. m == 0 with w_noise_out
+ *   != NULL still writes the noisy weight.
+ *   PhiloxNormal: Philox4x32-10 (Salmon et al., SC'11) of counter
+ *   (q, norm_id, step_lo, step_hi) and key (seed_lo, seed_hi) gives words
+ *   (o0..o3); each pair (a, b) in ((o0,o1), (o2,o3)) becomes
+ *   u1 = ((a>>8)+1) 2^-24, u2 = (b>>8) 2^-24, rho = sqrt(-2 ln u1), and
+ *   z[4q..4q+3] = (rho cos 2pi u2, rho sin 2pi u2) of pair 0, then of pair 1.
+ * fp4rl_philox_words: the raw words of blocks q = 0..n_blocks-1, [n_blocks][4].
+ * ---------------------------------------------------------------------- */
+float fp4rl_aqn_sigma(float sigma_start, float sigma_end, int32_t k, int32_t num_stages);
+fp4rl_status fp4rl_aqn_rmsnorm(const uint16_t* x, int64_t m, int64_t d, const float* w,
+                               float sigma, uint64_t seed, uint64_t step, uint32_t norm_id,
+                               float eps, uint16_t* y, float* w_noise_out, fp4rl_stream stream);
+fp4rl_status fp4rl_philox_words(uint64_t seed, uint64_t step, uint32_t norm_id, int64_t n_blocks,
+                                uint32_t* out, fp4rl_stream stream);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* FP4RL_H */

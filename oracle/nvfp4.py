@@ -144,6 +144,26 @@ def quantize(w) -> tuple[np.ndarray, np.ndarray, np.float32]:
     return packed, sbytes, s_t
 
 
+def quantize_rows(w, rows) -> tuple[np.ndarray, np.ndarray, np.float32]:
+    """``quantize`` restricted to the given rows of W (s_t still from all of W).
+
+    Blocks never cross rows, so each row's codes and scale bytes depend only on
+    that row and the tensor scale; this is the same definition evaluated on a
+    sample, for matrices too large to encode whole on the CPU.
+    """
+    w = np.asarray(w, dtype=np.float32)
+    s_t = tensor_scale(w)
+    sub = w[np.asarray(rows)]
+    sbytes = block_scale_bytes(sub, s_t)
+    s_b = e4m3_value(sbytes).astype(np.float32)
+    d_b = (s_b * s_t).astype(np.float32)
+    d_el = np.repeat(d_b.astype(np.float64), BLOCK, axis=1)
+    idx = e2m1_index(np.abs(sub).astype(np.float64), d_el)
+    codes4 = (np.signbit(sub).astype(np.int64) << 3) | idx
+    packed = (codes4[:, 0::2] | (codes4[:, 1::2] << 4)).astype(np.uint8)
+    return packed, sbytes, s_t
+
+
 def unpack_codes(codes: np.ndarray) -> np.ndarray:
     """[N, K/2] packed bytes -> [N, K] 4-bit codes (element 2j = low nibble)."""
     c = np.asarray(codes, dtype=np.uint8)

@@ -1,0 +1,135 @@
+"""C-ABI checks that need no GPU: the library loads, exports every symbol the
+header declares, and rejects bad arguments before touching the device."""
+import ctypes
+import math
+import os
+import re
+
+import numpy as np
+import pytest
+
+import fp4_quantized_rl_amd as fr
+from oracle import aqn
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "fp4rl.h")
+
+OK, ERR_NULL, ERR_SHAPE, ERR_DTYPE, ERR_ALIGN, ERR_WORKSPACE, ERR_ARCH, ERR_HIP, ERR_VALUE = range(9)
+FAKE = 0x7F0000000000   # 16-byte aligned, never dereferenced: every call below fails validation first
+MIS = FAKE + 2          # misaligned
+
+
+def _declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(fp4rl_[a-z0-9_]+)\s*\(", text)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(fr.LIB_PATH):
+        from fp4_quantized_rl_amd.build import build
+        build()
+    return fr.load_library()
+
+
+def test_header_and_binding_agree():
+    assert _declared_functions() == sorted(fr.EXPORTED_SYMBOLS)
+
+
+def test_library_exports_every_declared_symbol(lib):
+    raw = ctypes.CDLL(fr.LIB_PATH)
+    for name in _declared_functions():
+        assert hasattr(raw, name), name
+    assert lib.fp4rl_abi_version() == 1
+
+
+def test_status_strings(lib):
+    names = [lib.fp4rl_status_string(i).decode() for i in range(9)]
+    assert names[0] == "FP4RL_OK" and names[ERR_ALIGN] == "FP4RL_ERR_ALIGN"
+    assert lib.fp4rl_status_string(99).decode() == "FP4RL_UNKNOWN_STATUS"
+
+
+def test_quantize_rejects_bad_arguments(lib):
+    q = lib.fp4rl_nvfp4_quantize
+    ws = lib.fp4rl_nvfp4_quantize_workspace(8, 32)
+    assert ws >= 4
+    assert q(FAKE, 0, 8, 24, FAKE, FAKE, FAKE, FAKE, ws, None) == ERR_SHAPE
+    assert q(FAKE, 0, -1, 32, FAKE, FAKE, FAKE, FAKE, ws, None) == ERR_SHAPE
+    assert q(FAKE, 7, 8, 32, FAKE, FAKE, FAKE, FAKE, ws, None) == ERR_DTYPE
+    assert q(None, 0, 8, 32, FAKE, FAKE, FAKE, FAKE, ws, None) == ERR_NULL
+    assert q(FAKE, 0, 8, 32, FAKE, FAKE, None, FAKE, ws, None) == ERR_NULL
+    assert q(FAKE, 0, 8, 32, FAKE, FAKE, FAKE, None, ws, None) == ERR_WORKSPACE
+    assert q(FAKE, 0, 8, 32, FAKE, FAKE, FAKE, FAKE, ws - 1, None) == ERR_WORKSPACE
+    assert q(MIS, 0, 8, 32, FAKE, FAKE, FAKE, FAKE, ws, None) == ERR_ALIGN
+    assert q(FAKE, 0, 8, 32, FAKE, FAKE, FAKE + 1, FAKE, ws, None) == ERR_ALIGN
+    q(FAKE, 0, 8, 24, FAKE, FAKE, FAKE, FAKE, ws, None)
+    assert "multiple of 16" in lib.fp4rl_last_error().decode()
+
+
+def test_linear_rejects_bad_arguments(lib):
+    f = lib.fp4rl_fp4_lora_linear
+    ws = lib.fp4rl_fp4_lora_linear_workspace(4, 8, 32, 8)
+    assert ws >= 4 * 8 * 4
+    args = dict(x=FAKE, m=4, n=8, k=32, c=FAKE, s=FAKE, ts=FAKE, a=FAKE, b=FAKE, r=8, ls=2.0, y=FAKE,
+                ws=FAKE, wsb=ws)
+
+    def call(**kw):
+        a = dict(args, **kw)
+        return f(a["x"], a["m"], a["n"], a["k"], a["c"], a["s"], a["ts"], a["a"], a["b"], a["r"], a["ls"],
+                 a["y"], a["ws"], a["wsb"], None)
+
+    assert call(k=24) == ERR_SHAPE
+    assert call(k=0) == ERR_SHAPE
+    assert call(r=257) == ERR_SHAPE
+    assert call(m=-1) == ERR_SHAPE
+    assert call(ls=float("nan")) == ERR_VALUE
+    assert call(a=None) == ERR_NULL
+    assert call(x=None) == ERR_NULL
+    assert call(wsb=ws - 1) == ERR_WORKSPACE
+    assert call(ws=None) == ERR_WORKSPACE
+    assert call(y=MIS) == ERR_ALIGN
+    assert call(ts=FAKE + 2) == ERR_ALIGN
+    assert call(m=0) == OK and call(n=0) == OK          # empty: no-op, nothing touched
+    assert lib.fp4rl_lora_down(FAKE, 4, 24, FAKE, 8, 1.0, FAKE, None) == ERR_SHAPE
+    assert lib.fp4rl_lora_down(FAKE, 4, 32, FAKE, 0, 1.0, FAKE, None) == OK
+    assert lib.fp4rl_fp4_linear_lora_up(FAKE, 4, 8, 32, FAKE, FAKE, FAKE, None, FAKE, 8, FAKE, None) == ERR_NULL
+
+
+def test_aqn_rejects_bad_arguments(lib):
+    f = lib.fp4rl_aqn_rmsnorm
+    assert f(FAKE, 4, 512, FAKE, -1.0, 0, 0, 0, 1e-6, FAKE, None, None) == ERR_VALUE
+    assert f(FAKE, 4, 512, FAKE, float("inf"), 0, 0, 0, 1e-6, FAKE, None, None) == ERR_VALUE
+    assert f(FAKE, 4, 512, FAKE, 0.01, 0, 0, 0, -1.0, FAKE, None, None) == ERR_VALUE
+    assert f(FAKE, 4, 16385, FAKE, 0.01, 0, 0, 0, 1e-6, FAKE, None, None) == ERR_SHAPE
+    assert f(FAKE, 4, 512, None, 0.01, 0, 0, 0, 1e-6, FAKE, None, None) == ERR_NULL
+    assert f(MIS, 4, 512, FAKE, 0.01, 0, 0, 0, 1e-6, FAKE, None, None) == ERR_ALIGN
+    assert f(FAKE, 0, 512, FAKE, 0.01, 0, 0, 0, 1e-6, FAKE, None, None) == OK
+    assert lib.fp4rl_philox_words(0, 0, 0, -1, FAKE, None) == ERR_SHAPE
+    assert lib.fp4rl_philox_words(0, 0, 0, 4, MIS, None) == ERR_ALIGN
+
+
+def test_aqn_sigma_host_function(lib):
+    for k in range(10):
+        # the C ABI takes fp32 sigmas: feed the oracle the same fp32 inputs
+        want = aqn.sigma_schedule(float(np.float32(1e-2)), float(np.float32(5e-4)), k, 10)
+        assert np.float32(lib.fp4rl_aqn_sigma(1e-2, 5e-4, k, 10)) == want
+    assert lib.fp4rl_aqn_sigma(0.3, 0.1, 0, 1) == np.float32(0.3)
+    assert math.isnan(lib.fp4rl_aqn_sigma(0.3, 0.1, 3, 3))
+    assert math.isnan(lib.fp4rl_aqn_sigma(-1.0, 0.1, 0, 3))
+
+
+def test_valid_call_without_gpu_reports_hip_error(lib):
+    import torch
+    if torch.cuda.device_count() > 0:
+        pytest.skip("a GPU is present; this checks the no-device path")
+    ws = lib.fp4rl_nvfp4_quantize_workspace(8, 32)
+    assert lib.fp4rl_nvfp4_quantize(FAKE, 0, 8, 32, FAKE, FAKE, FAKE, FAKE, ws, None) == ERR_HIP
+    assert lib.fp4rl_last_error().decode().startswith("hipGetDevice")
+
+
+def test_binding_fails_loudly_without_library(monkeypatch):
+    monkeypatch.setattr(fr, "LIB_PATH", "/nonexistent/libfp4rl.so")
+    monkeypatch.setattr(fr, "_LIB", None)
+    with pytest.raises(fr.Fp4rlError):
+        fr.load_library()

@@ -1,0 +1,162 @@
+"""GPU parity of the fused W4A16 + LoRA linear (and its two halves) vs the oracle."""
+import numpy as np
+import pytest
+import torch
+
+import fp4_quantized_rl_amd as fr
+from oracle import linear, nvfp4
+from oracle.numerics import bf16_to_f64, rel_l2
+from workloads import (LORA_SCALE, QWEN25_7B, QWEN25_32B, activations_bf16, bf16_bits, lora_bf16,
+                       normal_f32, single_linear_config, tensor_seed)
+
+from gpu_util import (REL_L2_TOL, bf16_from_dev, bf16_to_dev, device, f32_to_dev, nvfp4_to_dev, say)
+
+pytestmark = pytest.mark.gpu
+
+
+def _case(m, n, k, r, seed, wstd=0.02, bstd=0.01, outliers=0.0):
+    w = normal_f32((n, k), wstd, seed)
+    x = activations_bf16(m, k, seed + 1, outlier_frac=outliers)
+    a, b = lora_bf16(r, k, n, seed + 2, std=0.01)
+    if bstd != 0.01:
+        b = bf16_bits(normal_f32((n, r), bstd, seed + 3))
+    return w, x, a, b
+
+
+def _run(dev, x, q, a, b, s):
+    xt = bf16_to_dev(x, dev)
+    wq = nvfp4_to_dev(*q, dev)
+    at = bf16_to_dev(a, dev) if a is not None and a.shape[0] else None
+    bt = bf16_to_dev(b, dev) if b is not None and b.shape[1] else None
+    y = fr.fp4_lora_linear(xt, wq, at, bt, s)
+    torch.cuda.synchronize()
+    return bf16_from_dev(y)
+
+
+def _check(y_bits, y_ref, what, tol=REL_L2_TOL):
+    err = rel_l2(bf16_to_f64(y_bits), y_ref)
+    say(f"  {what}: rel-L2 {err:.3e}")
+    assert err <= tol, f"{what}: rel-L2 {err}"
+
+
+def test_single_linear_config():
+    """W 256x512 ~N(0,.02), x 4x512, LoRA r=8 s=2, seed 0: GPU quantiser feeds the GPU linear."""
+    dev = device()
+    cfg = single_linear_config(0)
+    q_ref = nvfp4.quantize(cfg["w"])
+    wq = fr.nvfp4_quantize(f32_to_dev(cfg["w"], dev))
+    y = fr.fp4_lora_linear(bf16_to_dev(cfg["x"], dev), wq, bf16_to_dev(cfg["lora_a"], dev),
+                           bf16_to_dev(cfg["lora_b"], dev), cfg["lora_scale"])
+    torch.cuda.synchronize()
+    ref = linear.lora_linear(cfg["x"], *q_ref, cfg["lora_a"], cfg["lora_b"], cfg["lora_scale"])
+    _check(bf16_from_dev(y), ref, "256x512 M=4 r=8")
+
+
+RAGGED = [  # (m, n, k, r)
+    (1, 1, 16, 0), (1, 37, 48, 1), (3, 15, 144, 5), (16, 64, 128, 8), (17, 100, 512, 32),
+    (33, 64, 160, 3), (64, 48, 256, 16), (65, 33, 96, 64), (127, 130, 384, 9), (128, 64, 512, 256),
+    (129, 72, 208, 32), (300, 100, 1040, 24), (5, 4100, 32, 8),
+]
+
+
+@pytest.mark.parametrize("m,n,k,r", RAGGED)
+def test_ragged_shapes(m, n, k, r):
+    dev = device()
+    w, x, a, b = _case(m, n, k, r, seed=m * 7919 + n * 31 + k)
+    q = nvfp4.quantize(w)
+    say(f"linear m={m} n={n} k={k} r={r}")
+    y = _run(dev, x, q, a, b, LORA_SCALE)
+    _check(y, linear.lora_linear(x, *q, a, b, LORA_SCALE), f"{m}x{n}x{k} r{r}")
+
+
+def test_lora_reductions_bit_identical():
+    dev = device()
+    m, n, k, r = 24, 96, 256, 16
+    w, x, a, b = _case(m, n, k, r, seed=42)
+    q = nvfp4.quantize(w)
+    base = _run(dev, x, q, None, None, 0.0)
+    assert np.array_equal(_run(dev, x, q, a, np.zeros_like(b), LORA_SCALE), base), "B = 0"
+    assert np.array_equal(_run(dev, x, q, a, b, 0.0), base), "s = 0"
+    _check(base, linear.lora_linear(x, *q), "base only")
+
+
+def test_lora_dominant():
+    """W x1e-3 and B ~ N(0,1): the LoRA path carries most of y."""
+    dev = device()
+    m, n, k, r = 8, 256, 512, 32
+    w, x, a, b = _case(m, n, k, r, seed=43, wstd=2e-5, bstd=1.0)
+    q = nvfp4.quantize(w)
+    y = _run(dev, x, q, a, b, LORA_SCALE)
+    ref = linear.lora_linear(x, *q, a, b, LORA_SCALE)
+    base = linear.lora_linear_f64(x, *q)
+    assert np.linalg.norm(base) < 0.1 * np.linalg.norm(ref)
+    _check(y, ref, "LoRA-dominant")
+
+
+def test_power_of_two_homogeneity_and_determinism():
+    dev = device()
+    m, n, k, r = 33, 200, 512, 8
+    w, x, a, b = _case(m, n, k, r, seed=44)
+    q = nvfp4.quantize(w)
+    y1 = _run(dev, x, q, a, b, LORA_SCALE)
+    x2 = bf16_bits(bf16_to_f64(x).astype(np.float32) * 2)
+    y2 = _run(dev, x2, q, a, b, LORA_SCALE)
+    assert np.array_equal(bf16_to_f64(y2), 2 * bf16_to_f64(y1))
+    assert np.array_equal(_run(dev, x, q, a, b, LORA_SCALE), y1)
+
+
+def test_halves_match_fused_call():
+    dev = device()
+    m, n, k, r = 40, 300, 640, 32
+    w, x, a, b = _case(m, n, k, r, seed=45)
+    q = nvfp4.quantize(w)
+    xt, wq = bf16_to_dev(x, dev), nvfp4_to_dev(*q, dev)
+    at, bt = bf16_to_dev(a, dev), bf16_to_dev(b, dev)
+    t = fr.lora_down(xt, at, LORA_SCALE)
+    y_halves = fr.fp4_linear_lora_up(xt, wq, t, bt)
+    y_fused = fr.fp4_lora_linear(xt, wq, at, bt, LORA_SCALE)
+    torch.cuda.synchronize()
+    assert torch.equal(y_halves, y_fused)
+    t_ref = linear.lora_down(x, a, LORA_SCALE)
+    assert rel_l2(t.cpu().numpy(), t_ref) < 1e-5
+
+
+def _full_size(dev, shapes, names, ms, r, config, outliers=0.0, sample=96):
+    """Whole layer of linears; the GPU quantiser packs W, the oracle checks sampled output features."""
+    rng = np.random.default_rng(config)
+    for name in names:
+        n, k = shapes[name]
+        seed = tensor_seed(config, 0, name)
+        w = normal_f32((n, k), 0.02, seed)
+        wq = fr.nvfp4_quantize(f32_to_dev(w, dev))
+        a, b = lora_bf16(r, k, n, seed + 17)
+        at, bt = bf16_to_dev(a, dev), bf16_to_dev(b, dev)
+        rows = np.sort(rng.choice(n, sample, replace=False))
+        q_rows = nvfp4.quantize_rows(w, rows)
+        for m in ms:
+            x = activations_bf16(m, k, seed + m, outlier_frac=outliers)
+            say(f"  {name} {n}x{k} M={m} r={r}")
+            y = fr.fp4_lora_linear(bf16_to_dev(x, dev), wq, at, bt, LORA_SCALE)
+            torch.cuda.synchronize()
+            y_rows = bf16_from_dev(y)[:, rows]
+            ref = linear.lora_linear(x, q_rows[0], q_rows[1], q_rows[2], a, b[rows], LORA_SCALE)
+            _check(y_rows, ref, f"{name} M={m}")
+        del wq, w
+
+
+def test_qwen7b_decode_layer():
+    """7B layer linears at M = 1, 8, 32, 64, r = 32 (sampled output features)."""
+    dev = device()
+    _full_size(dev, QWEN25_7B, ["qkv", "o", "gate", "up", "down"], [1, 8, 32, 64], 32, config=1)
+
+
+def test_qwen7b_prefill_outliers():
+    """7B qkv and down at M = 8192 with 0.1% outlier channels x20 (sampled output features)."""
+    dev = device()
+    _full_size(dev, QWEN25_7B, ["qkv", "down"], [8192], 32, config=2, outliers=0.001, sample=48)
+
+
+def test_qwen32b_decode_m128():
+    """32B layer linears at M = 128, r = 64 (sampled output features)."""
+    dev = device()
+    _full_size(dev, QWEN25_32B, ["qkv", "o", "gate", "down"], [128], 64, config=3, sample=64)

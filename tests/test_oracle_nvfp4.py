@@ -261,3 +261,14 @@ def test_zero_tensor_and_nonfinite():
         tensor_scale(np.array([[1.0, np.inf]], dtype=np.float32))
     with pytest.raises(ValueError):
         quantize(np.zeros((2, 24), dtype=np.float32))
+
+
+def test_quantize_rows_is_quantize_restricted():
+    from oracle.nvfp4 import quantize_rows
+    rng = np.random.default_rng(14)
+    w = (rng.standard_normal((50, 96)) * 0.02).astype(np.float32)
+    w[7, 3] = 1.0
+    p, s, st = quantize(w)
+    rows = np.array([49, 7, 0, 21])
+    p2, s2, st2 = quantize_rows(w, rows)
+    assert st2 == st and np.array_equal(p2, p[rows]) and np.array_equal(s2, s[rows])
