@@ -1,0 +1,413 @@
+#!/usr/bin/env python3
+"""Benchmark of the NVFP4 + LoRA + AQN rollout hot path on one MI355X.
+
+Workload (one "step"): a Qwen2.5-7B-shaped decode layer at token batches
+M = 1, 8, 32 and 64. For each M: AQN RMSNorm (hidden 3584) -> qkv
+(3584->4608); o (3584->3584); AQN RMSNorm -> gate and up (3584->18944);
+down (18944->3584). Every linear is the fused W4A16 NVFP4 + LoRA forward
+(r = 32, s = 2). Attention and SiLU are not part of this path, so o and down
+read fresh synthetic activations. Weights are random N(0, 0.02) drawn on
+the GPU, quantised by the library's own NVFP4 quantiser; 4 distinct layer
+copies (4 x 131 MB) are rotated so that the 256 MB Infinity Cache cannot
+serve a repeat and the weight stream comes from HBM.
+
+Printed: one JSON line. ``value`` is decode weight GB/s over the whole step
+(NVFP4 bytes of all linears / step time). ``roofline`` is for the dominant
+kernel (the main linear kernel instantiation with the largest share of the
+step), timed with HIP events around each of its launches on the stream it runs
+on. ``cpu_baseline`` times the CPU oracle single-core on a fixed sample of the
+same workload. Extra keys report the prefill GEMM (M = 8192) TFLOP/s, the
+quantiser and the AQN RMSNorm bandwidth.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0            # MI355X HBM3E, published
+BF16_PEAK_TFLOPS = 2500.0        # MI355X dense bf16 MFMA, published
+TOKENS = (1, 8, 32, 64)
+RANK = 32
+LORA_SCALE = 2.0
+SIGMA, EPS = 1e-2, 1e-6
+COPIES = 4
+PREFILL_M = 8192
+METRIC = "FP4+LoRA linear: decode weight GB/s, prefill TFLOP/s, % of roofline"
+
+
+def nvfp4_bytes(n, k):
+    return n * k // 2 + n * k // 16 + 4
+
+
+def main_kernel_bytes(m, n, k, r):
+    """Algorithmic bytes of one main linear launch: weights, B, t, x in, y out."""
+    return nvfp4_bytes(n, k) + 2 * n * r + 4 * m * r + 2 * m * k + 2 * m * n
+
+
+def linear_flops(m, n, k, r):
+    return 2 * m * n * k + 2 * m * r * (k + n)
+
+
+def parse_args():
+    p = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    p.add_argument("--gpus", type=int, default=1)
+    p.add_argument("--steps", type=int, default=20)
+    p.add_argument("--warmup", type=int, default=5)
+    p.add_argument("--cpu-seconds", type=float, default=15.0, help="target CPU time of the oracle sample")
+    p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--no-extras", action="store_true", help="skip prefill / quantiser / AQN extra timings")
+    return p.parse_args()
+
+
+# --------------------------------------------------------------------------- CPU oracle baseline
+
+def cpu_baseline(target_s: float):
+    """The oracle as it stands, one thread on one core, on a fixed row sample of the step."""
+    import numpy as np
+    from threadpoolctl import threadpool_limits
+
+    from oracle import aqn, linear, nvfp4
+    from workloads import QWEN25_7B, activations_bf16, lora_bf16, normal_f32
+
+    frac = 16  # every linear keeps 1/16 of its output rows
+    prep = []
+    for name, (n, k) in QWEN25_7B.items():
+        rows = n // frac
+        w = normal_f32((rows, k), 0.02, 7000 + len(prep))
+        codes, scales, st = nvfp4.quantize(w)
+        a, b = lora_bf16(RANK, k, rows, 7100 + len(prep))
+        prep.append((name, rows, k, codes, scales, st, a, b))
+    xs = {m: activations_bf16(m, 3584, 7200 + m) for m in TOKENS}
+    xd = {m: activations_bf16(m, 18944, 7300 + m) for m in TOKENS}
+    wnorm = np.ones(3584, np.float32)
+
+    def one_pass():
+        wbytes = 0
+        for m in TOKENS:
+            h, _ = aqn.aqn_rmsnorm(xs[m], wnorm, SIGMA, 1, 0, 0, EPS)
+            for name, rows, k, codes, scales, st, a, b in prep:
+                x = xd[m] if name == "down" else xs[m]
+                linear.lora_linear(x, codes, scales, st, a, b, LORA_SCALE)
+                wbytes += nvfp4_bytes(rows, k)
+        return wbytes
+
+    affinity = os.sched_getaffinity(0)
+    core = min(affinity)
+    os.sched_setaffinity(0, {core})
+    try:
+        with threadpool_limits(limits=1):
+            total_b, t0 = 0, time.perf_counter()
+            passes = 0
+            while True:
+                total_b += one_pass()
+                passes += 1
+                el = time.perf_counter() - t0
+                if el >= target_s or (passes >= 1 and el * (passes + 1) / passes > 2 * target_s):
+                    break
+    finally:
+        os.sched_setaffinity(0, affinity)
+    gbs = total_b / el / 1e9
+    return {"value": round(gbs, 6), "unit": "GB/s", "cores": 1, "kind": "oracle",
+            "sample": f"1/{frac} of every linear's output rows (qkv, o, gate, up, down), all of M = "
+                      f"{list(TOKENS)}, AQN RMSNorm on the full token rows; {passes} pass(es) in {el:.1f} s "
+                      f"on one core ({os.cpu_count()} visible)"}
+
+
+# --------------------------------------------------------------------------- GPU workload
+
+def build_layer(torch, fr, dev, shapes, seed):
+    layer = {}
+    fp32 = {}
+    for i, (name, (n, k)) in enumerate(shapes.items()):
+        g = torch.Generator(device=dev)
+        g.manual_seed(seed * 100 + i)
+        w = torch.randn((n, k), generator=g, device=dev, dtype=torch.float32).mul_(0.02)
+        layer[name] = fr.nvfp4_quantize(w)
+        fp32[name] = w
+    return layer, fp32
+
+
+def traffic_from_profile(kernel_name, launches):
+    """HBM bytes per launch measured by rocprofv3 PMC runs, if the committed summary is current."""
+    path = os.path.join(ROOT, "profiles", "pmc_traffic.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as fh:
+        rec = json.load(fh)
+    src = os.path.join(ROOT, "fp4_quantized_rl_amd", "csrc", "linear.hip")
+    sha = hashlib.sha256(open(src, "rb").read()).hexdigest()[:16]
+    if rec.get("linear_hip_sha") != sha:
+        return None
+    ent = rec.get("kernels", {}).get(kernel_name)
+    if not ent:
+        return None
+    return ent.get("bytes_per_launch")
+
+
+def main():
+    args = parse_args()
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print("bench.py measures one GPU only: this build has no multi-GPU path "
+              "(run with --gpus 1)", file=sys.stderr)
+        sys.exit(2)
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        cpu = cpu_baseline(args.cpu_seconds)
+
+    import torch
+
+    import fp4_quantized_rl_amd as fr
+    from workloads import QWEN25_7B
+
+    fr.load_library()
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    shapes = QWEN25_7B
+    hidden = 3584
+    inter = 18944
+
+    # weights: COPIES distinct NVFP4 layers, shared LoRA adapters, AQN weights
+    layers = []
+    fp32_first = None
+    for c in range(COPIES):
+        layer, fp32 = build_layer(torch, fr, dev, shapes, seed=1 + c)
+        layers.append(layer)
+        if c == 0 and not args.no_extras:
+            fp32_first = fp32
+        else:
+            del fp32
+    torch.cuda.synchronize()
+    g = torch.Generator(device=dev)
+    g.manual_seed(11)
+    lora = {}
+    for name, (n, k) in shapes.items():
+        a = torch.randn((RANK, k), generator=g, device=dev).mul_(0.01).to(torch.bfloat16)
+        b = torch.randn((n, RANK), generator=g, device=dev).mul_(0.01).to(torch.bfloat16)
+        lora[name] = (a, b)
+    wnorm = torch.ones(hidden, dtype=torch.float32, device=dev)
+
+    # activations and preallocated outputs / workspaces per token count
+    bufs = {}
+    for m in TOKENS:
+        xh = torch.randn((m, hidden), generator=g, device=dev).to(torch.bfloat16)
+        xo = torch.randn((m, hidden), generator=g, device=dev).to(torch.bfloat16)
+        xr = torch.randn((m, hidden), generator=g, device=dev).to(torch.bfloat16)
+        xd = torch.randn((m, inter), generator=g, device=dev).to(torch.bfloat16)
+        bufs[m] = {
+            "xh": xh, "xo": xo, "xr": xr, "xd": xd,
+            "h1": torch.empty_like(xh), "h2": torch.empty_like(xr),
+            "ws": {name: torch.empty(max(16, fr.load_library().fp4rl_fp4_lora_linear_workspace(m, n, k, RANK)),
+                                     dtype=torch.uint8, device=dev) for name, (n, k) in shapes.items()},
+            "t": {name: torch.empty((m, RANK), dtype=torch.float32, device=dev) for name in shapes},
+            "y": {name: torch.empty((m, n), dtype=torch.bfloat16, device=dev) for name, (n, k) in shapes.items()},
+        }
+    weight_bytes_step = sum(nvfp4_bytes(n, k) for n, k in shapes.values()) * len(TOKENS)
+    flops_step = sum(linear_flops(m, n, k, RANK) for m in TOKENS for n, k in shapes.values())
+    total_bytes_step = 0
+    for m in TOKENS:
+        total_bytes_step += 2 * (4 * m * hidden + 4 * hidden)  # two norms: x in, y out (+ w)
+        for n, k in shapes.values():
+            total_bytes_step += nvfp4_bytes(n, k) + 2 * RANK * (k + n) + 2 * m * (k + n) + 8 * m * RANK
+
+    def layer_input(B, name):
+        return B["h1"] if name == "qkv" else B["xo"] if name == "o" else B["h2"] if name in ("gate", "up") else B["xd"]
+
+    def step(s):
+        """One pass of the hot path at every token count, on weight copy (s + i) % COPIES."""
+        for mi, m in enumerate(TOKENS):
+            L = layers[(s + mi) % COPIES]
+            B = bufs[m]
+            fr.aqn_rmsnorm(B["xh"], wnorm, SIGMA, 1, s, 0, EPS, out=B["h1"])
+            fr.aqn_rmsnorm(B["xr"], wnorm, SIGMA, 1, s, 1, EPS, out=B["h2"])
+            for name in ("qkv", "o", "gate", "up", "down"):
+                a, b = lora[name]
+                fr.fp4_lora_linear(layer_input(B, name), L[name], a, b, LORA_SCALE, out=B["y"][name],
+                                   workspace=B["ws"][name])
+
+    for s in range(args.warmup):
+        step(s)
+    torch.cuda.synchronize()
+    # The step is launch-bound at small M, so it runs as HIP graphs: one per
+    # weight-copy rotation phase, captured once, replayed in the timed region.
+    graphs = []
+    for p in range(COPIES):
+        gr = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(gr):
+            step(p)
+        graphs.append(gr)
+    for s in range(args.warmup):
+        graphs[s % COPIES].replay()
+    torch.cuda.synchronize()
+
+    t0 = time.perf_counter()
+    for s in range(args.steps):
+        graphs[s % COPIES].replay()
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t0
+    ms_per_step = elapsed * 1e3 / args.steps
+    value = weight_bytes_step * args.steps / elapsed / 1e9
+    del graphs
+
+    # Per-kernel durations: for each (M, linear) a graph of back-to-back main-
+    # kernel launches over distinct weight buffers totalling >= 512 MB (twice
+    # the Infinity Cache), bracketed by HIP events on the launch stream.
+    clones = {}
+    for name, (n, k) in shapes.items():
+        lst = [layers[c][name] for c in range(COPIES)]
+        while sum(w.nbytes for w in lst) < 512 * 2**20:
+            src = lst[len(lst) % COPIES]
+            lst.append(src.clone())
+        clones[name] = lst
+    timing = {}
+    reps = 3
+    for m in TOKENS:
+        B = bufs[m]
+        for name, (n, k) in shapes.items():
+            x = layer_input(B, name)
+            a, b = lora[name]
+            t = fr.lora_down(x, a, LORA_SCALE, out=B["t"][name])
+            gr = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(gr):
+                for w in clones[name]:
+                    fr.fp4_linear_lora_up(x, w, t, b, out=B["y"][name])
+            gr.replay()
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            for _ in range(reps):
+                gr.replay()
+            e1.record()
+            torch.cuda.synchronize()
+            launches = reps * len(clones[name])
+            timing[(m, name)] = e0.elapsed_time(e1) * 1e-3 / launches
+            del gr
+    kname = {(m, name): fr.fp4_linear_kernel_name(m, n, k) for m in TOKENS for name, (n, k) in shapes.items()}
+    per_kernel = {}
+    for (m, name), dt in timing.items():
+        n, k = shapes[name]
+        d = per_kernel.setdefault(kname[(m, name)], {"time": 0.0, "launches": 0, "bytes": 0})
+        d["time"] += dt
+        d["launches"] += 1
+        d["bytes"] += main_kernel_bytes(m, n, k, RANK)
+    dom = max(per_kernel, key=lambda kn: per_kernel[kn]["time"])
+    dk = per_kernel[dom]
+    achieved = dk["bytes"] / dk["time"] / 1e9
+    traffic = traffic_from_profile(dom, dk["launches"])
+    roofline = {"bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic,
+                "kernel": dom, "avg_launch_us": round(dk["time"] / dk["launches"] * 1e6, 3),
+                "launches_per_step": dk["launches"],
+                "algorithmic_bytes_per_launch": int(dk["bytes"] / dk["launches"])}
+
+    step_roof_s = max(total_bytes_step / (HBM_PEAK_GBS * 1e9), flops_step / (BF16_PEAK_TFLOPS * 1e12))
+    breakdown = {
+        "step_roofline_frac": round(step_roof_s / (ms_per_step * 1e-3), 4),
+        "main_kernel_us": {f"M{m}/{name}": round(timing[(m, name)] * 1e6, 2) for m in TOKENS for name in shapes},
+        "main_kernel_weight_gbs": {f"M{m}/{name}": round(nvfp4_bytes(*shapes[name]) / timing[(m, name)] / 1e9, 1)
+                                   for m in TOKENS for name in shapes},
+        "main_kernels_share_of_step": round(sum(timing.values()) / (ms_per_step * 1e-3), 4),
+        "kernels": {kn: {"avg_us": round(v["time"] / v["launches"] * 1e6, 3), "launches_per_step": v["launches"],
+                         "GB/s": round(v["bytes"] / v["time"] / 1e9, 1)} for kn, v in sorted(per_kernel.items())},
+    }
+    del clones
+
+    extras = {}
+    if not args.no_extras:
+        extras = run_extras(torch, fr, dev, shapes, layers[0], lora, fp32_first)
+
+    out = {
+        "metric": METRIC, "value": round(value, 3), "unit": "GB/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": round(ms_per_step, 4), "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+        "config": {"workload": "Qwen2.5-7B-shaped decode layer: AQN RMSNorm x2 + qkv 3584->4608, "
+                               "o 3584->3584, gate/up 3584->18944, down 18944->3584 as NVFP4 W4A16 + LoRA",
+                   "tokens_per_pass": list(TOKENS), "lora_rank": RANK, "lora_scale": LORA_SCALE,
+                   "weight_copies_rotated": COPIES, "nvfp4_weight_bytes_per_step": weight_bytes_step,
+                   "parallelism": "single GPU"},
+        "roofline": roofline,
+        "cpu_baseline": cpu,
+        "breakdown": breakdown,
+    }
+    out.update(extras)
+    print(json.dumps(out))
+
+
+def run_extras(torch, fr, dev, shapes, layer, lora, fp32):
+    res = {}
+    g = torch.Generator(device=dev)
+    g.manual_seed(21)
+    # prefill: M = 8192 tokens (16 x 512) with 0.1% outlier channels x20
+    flops, ts = 0, []
+    xs = {}
+    for k in sorted({k for _, k in shapes.values()}):
+        x = torch.randn((PREFILL_M, k), generator=g, device=dev)
+        nout = round(0.001 * k)
+        ch = torch.randperm(k, generator=g, device=dev)[:nout]
+        x[:, ch] *= 20.0
+        xs[k] = x.to(torch.bfloat16)
+    ys = {name: torch.empty((PREFILL_M, n), dtype=torch.bfloat16, device=dev) for name, (n, k) in shapes.items()}
+    tbuf = torch.empty((PREFILL_M, RANK), dtype=torch.float32, device=dev)
+
+    def prefill_pass():
+        for name, (n, k) in shapes.items():
+            a, b = lora[name]
+            t = fr.lora_down(xs[k], a, LORA_SCALE, out=tbuf)
+            fr.fp4_linear_lora_up(xs[k], layer[name], t, b, out=ys[name])
+
+    prefill_pass()
+    torch.cuda.synchronize()
+    reps = 3
+    t0 = time.perf_counter()
+    for _ in range(reps):
+        prefill_pass()
+    torch.cuda.synchronize()
+    dt = (time.perf_counter() - t0) / reps
+    flops = sum(linear_flops(PREFILL_M, n, k, RANK) for n, k in shapes.values())
+    res["prefill"] = {"M": PREFILL_M, "tflops": round(flops / dt / 1e12, 2), "ms_per_layer": round(dt * 1e3, 3),
+                      "frac_of_bf16_peak": round(flops / dt / 1e12 / BF16_PEAK_TFLOPS, 4)}
+    del xs, ys
+
+    # quantiser: the layer's fp32 weights -> NVFP4 (two reads of W, one write of codes+scales)
+    if fp32 is not None:
+        outs = {name: fr.nvfp4_quantize(w) for name, w in fp32.items()}
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        reps = 3
+        for _ in range(reps):
+            for name, w in fp32.items():
+                fr.nvfp4_quantize(w, out=outs[name])
+        torch.cuda.synchronize()
+        dt = (time.perf_counter() - t0) / reps
+        params = sum(n * k for n, k in shapes.values())
+        two_pass = params * (2 * 4 + 0.5625)
+        res["quantize"] = {"input": "fp32", "params": params, "ms_per_layer": round(dt * 1e3, 3),
+                           "GB/s_two_pass": round(two_pass / dt / 1e9, 1),
+                           "frac_of_hbm": round(two_pass / dt / 1e9 / HBM_PEAK_GBS, 4)}
+    # AQN RMSNorm: 65536 x 5120 bf16 tokens
+    m, d = 65536, 5120
+    x = torch.randn((m, d), generator=g, device=dev).to(torch.bfloat16)
+    y = torch.empty_like(x)
+    w = torch.ones(d, dtype=torch.float32, device=dev)
+    fr.aqn_rmsnorm(x, w, SIGMA, 4, 0, 0, EPS, out=y)
+    torch.cuda.synchronize()
+    reps = 10
+    t0 = time.perf_counter()
+    for kk in range(reps):
+        fr.aqn_rmsnorm(x, w, fr.aqn_sigma(1e-2, 5e-4, kk, 10), 4, kk, 0, EPS, out=y)
+    torch.cuda.synchronize()
+    dt = (time.perf_counter() - t0) / reps
+    res["aqn_rmsnorm"] = {"shape": [m, d], "us_per_call": round(dt * 1e6, 2),
+                          "GB/s": round(4 * m * d / dt / 1e9, 1), "frac_of_hbm": round(4 * m * d / dt / 1e9 / HBM_PEAK_GBS, 4)}
+    return res
+
+
+if __name__ == "__main__":
+    main()

@@ -8,7 +8,8 @@ computation runs in the library's HIP kernels. There is no CPU fallback: if
 the library is not built, every call raises.
 
 Operations (names follow the C ABI):
-  nvfp4_quantize(w)                         -> NVFP4Weight(codes, scales, tensor_scale)
+  nvfp4_quantize(w, layout)                 -> NVFP4Weight(codes, scales, tensor_scale)
+  nvfp4_to_tiled(wq)                        -> row-major NVFP4 repacked into the tiled layout
   fp4_lora_linear(x, wq, lora_a, lora_b, s) -> y = x deq(Wq)^T + s (x A^T) B^T  (bf16)
   lora_down / fp4_linear_lora_up            -> the two halves of fp4_lora_linear
   aqn_sigma(s0, s1, k, K)                   -> exponential AQN noise level
@@ -22,14 +23,17 @@ import os
 from dataclasses import dataclass
 
 __all__ = [
-    "LIB_PATH", "Fp4rlError", "load_library", "NVFP4Weight", "nvfp4_quantize", "fp4_lora_linear",
-    "lora_down", "fp4_linear_lora_up", "aqn_sigma", "aqn_rmsnorm", "philox_words",
+    "LIB_PATH", "Fp4rlError", "load_library", "NVFP4Weight", "nvfp4_empty", "nvfp4_quantize", "nvfp4_to_tiled",
+    "fp4_lora_linear",
+    "lora_down", "fp4_linear_lora_up", "fp4_linear_kernel_name", "aqn_sigma", "aqn_rmsnorm", "philox_words",
     "EXPORTED_SYMBOLS",
 ]
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libfp4rl.so")
 
 F32, BF16 = 0, 1
+ROW_MAJOR, TILED = 0, 1
+_LAYOUTS = {"row_major": ROW_MAJOR, "tiled": TILED}
 _c = ctypes
 _P = _c.c_void_p
 _I64 = _c.c_int64
@@ -41,12 +45,17 @@ _SIGNATURES = {
     "fp4rl_last_error": (_c.c_char_p, []),
     "fp4rl_abi_version": (_c.c_int32, []),
     "fp4rl_nvfp4_quantize_workspace": (_c.c_size_t, [_I64, _I64]),
-    "fp4rl_nvfp4_quantize": (_STATUS, [_P, _c.c_int32, _I64, _I64, _P, _P, _P, _P, _c.c_size_t, _P]),
+    "fp4rl_nvfp4_codes_bytes": (_c.c_size_t, [_I64, _I64, _c.c_int32]),
+    "fp4rl_nvfp4_scales_bytes": (_c.c_size_t, [_I64, _I64, _c.c_int32]),
+    "fp4rl_nvfp4_quantize": (_STATUS, [_P, _c.c_int32, _I64, _I64, _c.c_int32, _P, _P, _P, _P, _c.c_size_t, _P]),
+    "fp4rl_nvfp4_to_tiled": (_STATUS, [_P, _P, _I64, _I64, _P, _P, _P]),
     "fp4rl_fp4_lora_linear_workspace": (_c.c_size_t, [_I64, _I64, _I64, _I64]),
     "fp4rl_fp4_lora_linear": (_STATUS, [_P, _I64, _I64, _I64, _P, _P, _P, _P, _P, _I64, _c.c_float, _P, _P,
                                         _c.c_size_t, _P]),
-    "fp4rl_lora_down": (_STATUS, [_P, _I64, _I64, _P, _I64, _c.c_float, _P, _P]),
+    "fp4rl_lora_down_workspace": (_c.c_size_t, [_I64, _I64, _I64]),
+    "fp4rl_lora_down": (_STATUS, [_P, _I64, _I64, _P, _I64, _c.c_float, _P, _P, _c.c_size_t, _P]),
     "fp4rl_fp4_linear_lora_up": (_STATUS, [_P, _I64, _I64, _I64, _P, _P, _P, _P, _P, _I64, _P, _P]),
+    "fp4rl_fp4_linear_kernel_name": (_c.c_char_p, [_I64, _I64, _I64]),
     "fp4rl_aqn_sigma": (_c.c_float, [_c.c_float, _c.c_float, _c.c_int32, _c.c_int32]),
     "fp4rl_aqn_rmsnorm": (_STATUS, [_P, _I64, _I64, _P, _c.c_float, _c.c_uint64, _c.c_uint64, _c.c_uint32,
                                     _c.c_float, _P, _P, _P]),
@@ -120,52 +129,89 @@ def _dev_tensor(t, name, dtypes, ndim=None):
 
 @dataclass
 class NVFP4Weight:
-    """An NVFP4 matrix [n, k]: codes uint8 [n, k/2], scales uint8 [n, k/16], tensor_scale fp32 [1]."""
+    """An NVFP4 matrix [n, k]: flat uint8 codes and scales (layout "row_major" or
+    "tiled", see include/fp4rl.h) and the fp32 tensor scale [1]."""
 
     codes: "object"
     scales: "object"
     tensor_scale: "object"
+    n: int
+    k: int
+    layout: str = "tiled"
 
     @property
     def shape(self):
-        return (self.codes.shape[0], self.codes.shape[1] * 2)
+        return (self.n, self.k)
 
     @property
     def nbytes(self) -> int:
         return self.codes.numel() + self.scales.numel() + 4
 
+    def clone(self) -> "NVFP4Weight":
+        return NVFP4Weight(self.codes.clone(), self.scales.clone(), self.tensor_scale.clone(), self.n, self.k,
+                           self.layout)
 
-def nvfp4_quantize(w, out: NVFP4Weight | None = None) -> NVFP4Weight:
+
+def nvfp4_empty(n: int, k: int, layout: str = "tiled", device="cuda") -> NVFP4Weight:
+    """Uninitialised NVFP4 storage for an [n, k] matrix in the given layout."""
+    torch = _torch()
+    lib = load_library()
+    lay = _LAYOUTS[layout]
+    cb = lib.fp4rl_nvfp4_codes_bytes(n, k, lay)
+    sb = lib.fp4rl_nvfp4_scales_bytes(n, k, lay)
+    return NVFP4Weight(torch.empty(max(cb, 16), dtype=torch.uint8, device=device)[:cb],
+                       torch.empty(max(sb, 16), dtype=torch.uint8, device=device)[:sb],
+                       torch.empty((1,), dtype=torch.float32, device=device), n, k, layout)
+
+
+def nvfp4_quantize(w, layout: str = "tiled", out: NVFP4Weight | None = None, workspace=None) -> NVFP4Weight:
     """NVFP4-quantise a [n, k] fp32 or bf16 weight (k % 16 == 0) on its device."""
     torch = _torch()
     _dev_tensor(w, "w", (torch.float32, torch.bfloat16), 2)
     n, k = w.shape
     if out is None:
-        out = NVFP4Weight(torch.empty((n, k // 2), dtype=torch.uint8, device=w.device),
-                          torch.empty((n, k // 16), dtype=torch.uint8, device=w.device),
-                          torch.empty((1,), dtype=torch.float32, device=w.device))
+        out = nvfp4_empty(n, k, layout, w.device)
+    elif (out.n, out.k, out.layout) != (n, k, layout):
+        raise ValueError("out does not match the weight shape / layout")
     lib = load_library()
     ws_bytes = lib.fp4rl_nvfp4_quantize_workspace(n, k)
-    ws = torch.empty(max(ws_bytes, 16), dtype=torch.uint8, device=w.device)
+    if workspace is None:
+        workspace = torch.empty(max(ws_bytes, 16), dtype=torch.uint8, device=w.device)
     dt = F32 if w.dtype == torch.float32 else BF16
     with torch.cuda.device(w.device):
-        _check(lib.fp4rl_nvfp4_quantize(_ptr(w), dt, n, k, _ptr(out.codes), _ptr(out.scales),
-                                        _ptr(out.tensor_scale), _ptr(ws), ws_bytes, _stream(w.device)),
+        _check(lib.fp4rl_nvfp4_quantize(_ptr(w), dt, n, k, _LAYOUTS[layout], _ptr(out.codes), _ptr(out.scales),
+                                        _ptr(out.tensor_scale), _ptr(workspace), workspace.numel(),
+                                        _stream(w.device)),
                "nvfp4_quantize")
+    return out
+
+
+def nvfp4_to_tiled(wq: NVFP4Weight) -> NVFP4Weight:
+    """Repack a row-major NVFP4 matrix into the tiled layout the linear kernels read."""
+    torch = _torch()
+    if wq.layout != "row_major":
+        raise ValueError("expected a row_major NVFP4 weight")
+    out = nvfp4_empty(wq.n, wq.k, "tiled", wq.codes.device)
+    out.tensor_scale.copy_(wq.tensor_scale)
+    with torch.cuda.device(wq.codes.device):
+        _check(load_library().fp4rl_nvfp4_to_tiled(_ptr(wq.codes), _ptr(wq.scales), wq.n, wq.k, _ptr(out.codes),
+                                                   _ptr(out.scales), _stream(wq.codes.device)),
+               "nvfp4_to_tiled")
     return out
 
 
 def _linear_args(x, wq: NVFP4Weight):
     torch = _torch()
     _dev_tensor(x, "x", (torch.bfloat16,), 2)
-    _dev_tensor(wq.codes, "codes", (torch.uint8,), 2)
-    _dev_tensor(wq.scales, "scales", (torch.uint8,), 2)
+    _dev_tensor(wq.codes, "codes", (torch.uint8,))
+    _dev_tensor(wq.scales, "scales", (torch.uint8,))
     _dev_tensor(wq.tensor_scale, "tensor_scale", (torch.float32,))
+    if wq.layout != "tiled":
+        raise ValueError("the linear kernels read the tiled NVFP4 layout (see nvfp4_to_tiled)")
     m, k = x.shape
-    n = wq.codes.shape[0]
-    if wq.codes.shape[1] * 2 != k or wq.scales.shape != (n, k // 16):
-        raise ValueError(f"x [{m},{k}] does not match the NVFP4 weight {tuple(wq.codes.shape)}")
-    return m, n, k
+    if wq.k != k:
+        raise ValueError(f"x [{m},{k}] does not match the NVFP4 weight [{wq.n},{wq.k}]")
+    return m, wq.n, k
 
 
 def fp4_lora_linear(x, wq: NVFP4Weight, lora_a=None, lora_b=None, lora_scale: float = 0.0,
@@ -196,7 +242,7 @@ def fp4_lora_linear(x, wq: NVFP4Weight, lora_a=None, lora_b=None, lora_scale: fl
     return out
 
 
-def lora_down(x, lora_a, lora_scale: float, out=None):
+def lora_down(x, lora_a, lora_scale: float, out=None, workspace=None):
     """t = lora_scale * x A^T in fp32 [m, r]."""
     torch = _torch()
     _dev_tensor(x, "x", (torch.bfloat16,), 2)
@@ -207,9 +253,13 @@ def lora_down(x, lora_a, lora_scale: float, out=None):
         raise ValueError("lora_a must be [r, k]")
     if out is None:
         out = torch.empty((m, r), dtype=torch.float32, device=x.device)
+    lib = load_library()
+    ws_bytes = lib.fp4rl_lora_down_workspace(m, k, r)
+    if workspace is None and ws_bytes:
+        workspace = torch.empty(ws_bytes, dtype=torch.uint8, device=x.device)
     with torch.cuda.device(x.device):
-        _check(load_library().fp4rl_lora_down(_ptr(x), m, k, _ptr(lora_a), r, float(lora_scale), _ptr(out),
-                                              _stream(x.device)), "lora_down")
+        _check(lib.fp4rl_lora_down(_ptr(x), m, k, _ptr(lora_a), r, float(lora_scale), _ptr(out), _ptr(workspace),
+                                   0 if workspace is None else workspace.numel(), _stream(x.device)), "lora_down")
     return out
 
 
@@ -232,6 +282,11 @@ def fp4_linear_lora_up(x, wq: NVFP4Weight, t=None, lora_b=None, out=None):
                                                        _ptr(out), _stream(x.device)),
                "fp4_linear_lora_up")
     return out
+
+
+def fp4_linear_kernel_name(m: int, n: int, k: int) -> str:
+    """Main-kernel instantiation the library launches for an [m, k] x [n, k]^T product."""
+    return load_library().fp4rl_fp4_linear_kernel_name(m, n, k).decode()
 
 
 def aqn_sigma(sigma_start: float, sigma_end: float, k: int, num_stages: int) -> float:

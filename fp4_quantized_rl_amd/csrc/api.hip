@@ -109,13 +109,24 @@ size_t fp4rl_nvfp4_quantize_workspace(int64_t n, int64_t k) {
   return fp4rl::quantize_workspace_bytes();
 }
 
-fp4rl_status fp4rl_nvfp4_quantize(const void* w, int32_t w_dtype, int64_t n, int64_t k, uint8_t* codes,
-                                  uint8_t* scales, float* tensor_scale, void* workspace, size_t workspace_bytes,
-                                  fp4rl_stream stream) {
+size_t fp4rl_nvfp4_codes_bytes(int64_t n, int64_t k, int32_t layout) {
+  if (n < 0 || k < 0 || k % 16 || (layout != FP4RL_ROW_MAJOR && layout != FP4RL_TILED)) return 0;
+  return (size_t)fp4rl::nvfp4_codes_bytes(n, k, layout == FP4RL_TILED);
+}
+
+size_t fp4rl_nvfp4_scales_bytes(int64_t n, int64_t k, int32_t layout) {
+  if (n < 0 || k < 0 || k % 16 || (layout != FP4RL_ROW_MAJOR && layout != FP4RL_TILED)) return 0;
+  return (size_t)fp4rl::nvfp4_scales_bytes(n, k, layout == FP4RL_TILED);
+}
+
+fp4rl_status fp4rl_nvfp4_quantize(const void* w, int32_t w_dtype, int64_t n, int64_t k, int32_t layout,
+                                  uint8_t* codes, uint8_t* scales, float* tensor_scale, void* workspace,
+                                  size_t workspace_bytes, fp4rl_stream stream) {
   FP4RL_REQUIRE(n >= 0 && k >= 0, FP4RL_ERR_SHAPE, "negative size (n=%lld k=%lld)", (long long)n, (long long)k);
   FP4RL_REQUIRE(k % 16 == 0, FP4RL_ERR_SHAPE, "k=%lld is not a multiple of 16", (long long)k);
-  FP4RL_REQUIRE(n < kMaxDim && k < kMaxDim && n * k < ((int64_t)1 << 46), FP4RL_ERR_SHAPE, "matrix too large");
+  FP4RL_REQUIRE(n < kMaxDim && k < kMaxDim && n * k < ((int64_t)1 << 36), FP4RL_ERR_SHAPE, "matrix too large");
   FP4RL_REQUIRE(w_dtype == FP4RL_F32 || w_dtype == FP4RL_BF16, FP4RL_ERR_DTYPE, "w_dtype=%d", (int)w_dtype);
+  FP4RL_REQUIRE(layout == FP4RL_ROW_MAJOR || layout == FP4RL_TILED, FP4RL_ERR_VALUE, "layout=%d", (int)layout);
   FP4RL_REQUIRE(tensor_scale != nullptr, FP4RL_ERR_NULL, "tensor_scale is NULL");
   FP4RL_REQUIRE(aligned(tensor_scale, 4), FP4RL_ERR_ALIGN, "tensor_scale not 4-byte aligned");
   const bool empty = n == 0 || k == 0;
@@ -128,30 +139,62 @@ fp4rl_status fp4rl_nvfp4_quantize(const void* w, int32_t w_dtype, int64_t n, int
                   FP4RL_ERR_ALIGN, "w, codes, scales and workspace must be 16-byte aligned");
   }
   FP4RL_CHECK(check_device());
-  return launched(fp4rl::launch_quantize(w, w_dtype == FP4RL_BF16, n, k, codes, scales, tensor_scale,
-                                         static_cast<uint32_t*>(workspace), stream),
+  return launched(fp4rl::launch_quantize(w, w_dtype == FP4RL_BF16, n, k, layout == FP4RL_TILED, codes, scales,
+                                         tensor_scale, static_cast<uint32_t*>(workspace), stream),
                   "nvfp4_quantize");
+}
+
+fp4rl_status fp4rl_nvfp4_to_tiled(const uint8_t* codes, const uint8_t* scales, int64_t n, int64_t k,
+                                  uint8_t* codes_tiled, uint8_t* scales_tiled, fp4rl_stream stream) {
+  FP4RL_REQUIRE(n >= 0 && k >= 0 && k % 16 == 0, FP4RL_ERR_SHAPE, "bad shape n=%lld k=%lld", (long long)n,
+                (long long)k);
+  FP4RL_REQUIRE(n < kMaxDim && k < kMaxDim && n * k < ((int64_t)1 << 36), FP4RL_ERR_SHAPE, "matrix too large");
+  if (n == 0 || k == 0) return ok();
+  FP4RL_REQUIRE(codes && scales && codes_tiled && scales_tiled, FP4RL_ERR_NULL, "NULL buffer");
+  FP4RL_REQUIRE(aligned(codes, 16) && aligned(scales, 16) && aligned(codes_tiled, 16) && aligned(scales_tiled, 16),
+                FP4RL_ERR_ALIGN, "buffers must be 16-byte aligned");
+  FP4RL_CHECK(check_device());
+  return launched(fp4rl::launch_to_tiled(codes, scales, n, k, codes_tiled, scales_tiled, stream), "nvfp4_to_tiled");
 }
 
 // ------------------------------------------------------------------ linear --
 
 size_t fp4rl_fp4_lora_linear_workspace(int64_t m, int64_t n, int64_t k, int64_t r) {
   (void)n;
-  (void)k;
-  if (m <= 0 || r <= 0) return 0;
-  return round_up((size_t)m * (size_t)r * sizeof(float), 256);
+  if (m <= 0 || r <= 0 || k <= 0) return 0;
+  const int slices = fp4rl::lora_slices(k, fp4rl::lora_splits(m, k, r));
+  return round_up((size_t)slices * (size_t)m * (size_t)r * sizeof(float), 256);
+}
+
+size_t fp4rl_lora_down_workspace(int64_t m, int64_t k, int64_t r) {
+  if (m <= 0 || r <= 0 || k <= 0) return 0;
+  const int slices = fp4rl::lora_slices(k, fp4rl::lora_splits(m, k, r));
+  return slices > 1 ? round_up((size_t)slices * (size_t)m * (size_t)r * sizeof(float), 256) : 0;
 }
 
 fp4rl_status fp4rl_lora_down(const uint16_t* x, int64_t m, int64_t k, const uint16_t* lora_a, int64_t r,
-                             float lora_scale, float* t, fp4rl_stream stream) {
+                             float lora_scale, float* t, void* workspace, size_t workspace_bytes,
+                             fp4rl_stream stream) {
   FP4RL_CHECK(check_linear_shape(m, 1, k, r));
   FP4RL_REQUIRE(std::isfinite(lora_scale), FP4RL_ERR_VALUE, "lora_scale is not finite");
   if (m == 0 || r == 0) return ok();
   FP4RL_REQUIRE(x && lora_a && t, FP4RL_ERR_NULL, "x, lora_a and t must be non-NULL");
   FP4RL_REQUIRE(aligned(x, 16) && aligned(lora_a, 16) && aligned(t, 16), FP4RL_ERR_ALIGN,
                 "x, lora_a and t must be 16-byte aligned");
+  const int splits = fp4rl::lora_splits(m, k, r);
+  const int slices = fp4rl::lora_slices(k, splits);
+  const size_t need = fp4rl_lora_down_workspace(m, k, r);
+  if (need) {
+    FP4RL_REQUIRE(workspace != nullptr && workspace_bytes >= need, FP4RL_ERR_WORKSPACE, "workspace %zu < %zu bytes",
+                  workspace_bytes, need);
+    FP4RL_REQUIRE(aligned(workspace, 16), FP4RL_ERR_ALIGN, "workspace must be 16-byte aligned");
+  }
   FP4RL_CHECK(check_device());
-  return launched(fp4rl::launch_lora_down(x, m, k, lora_a, r, lora_scale, t, stream), "lora_down");
+  float* part = slices > 1 ? static_cast<float*>(workspace) : t;
+  fp4rl_status s = launched(fp4rl::launch_lora_down(x, m, k, lora_a, r, lora_scale, splits, part, stream),
+                            "lora_down");
+  if (s != FP4RL_OK || slices == 1) return s;
+  return launched(fp4rl::launch_lora_reduce(part, slices, m * r, t, stream), "lora_reduce");
 }
 
 static fp4rl_status check_linear_main(const uint16_t* x, int64_t m, int64_t n, int64_t k, const uint8_t* codes,
@@ -179,7 +222,7 @@ fp4rl_status fp4rl_fp4_linear_lora_up(const uint16_t* x, int64_t m, int64_t n, i
   if (m == 0 || n == 0) return ok();
   FP4RL_CHECK(check_linear_main(x, m, n, k, codes, scales, tensor_scale, t, lora_b, r, y));
   FP4RL_CHECK(check_device());
-  return launched(fp4rl::launch_fp4_linear(x, m, n, k, codes, scales, tensor_scale, r > 0 ? t : nullptr,
+  return launched(fp4rl::launch_fp4_linear(x, m, n, k, codes, scales, tensor_scale, r > 0 ? t : nullptr, 1,
                                            r > 0 ? lora_b : nullptr, r, y, stream),
                   "fp4_linear");
 }
@@ -204,13 +247,22 @@ fp4rl_status fp4rl_fp4_lora_linear(const uint16_t* x, int64_t m, int64_t n, int6
   }
   FP4RL_CHECK(check_linear_main(x, m, n, k, codes, scales, tensor_scale, t, lora_b, r, y));
   FP4RL_CHECK(check_device());
+  int slices = 1;
   if (r > 0) {
-    fp4rl_status s = launched(fp4rl::launch_lora_down(x, m, k, lora_a, r, lora_scale, t, stream), "lora_down");
+    const int splits = fp4rl::lora_splits(m, k, r);
+    slices = fp4rl::lora_slices(k, splits);
+    fp4rl_status s = launched(fp4rl::launch_lora_down(x, m, k, lora_a, r, lora_scale, splits, t, stream), "lora_down");
     if (s != FP4RL_OK) return s;
   }
-  return launched(fp4rl::launch_fp4_linear(x, m, n, k, codes, scales, tensor_scale, r > 0 ? t : nullptr,
+  // the main kernel's epilogue sums the K-slices of t in slice order
+  return launched(fp4rl::launch_fp4_linear(x, m, n, k, codes, scales, tensor_scale, r > 0 ? t : nullptr, slices,
                                            r > 0 ? lora_b : nullptr, r, y, stream),
                   "fp4_linear");
+}
+
+const char* fp4rl_fp4_linear_kernel_name(int64_t m, int64_t n, int64_t k) {
+  if (check_linear_shape(m, n, k, 0) != FP4RL_OK || m == 0 || n == 0) return "";
+  return fp4rl::fp4_linear_kernel_name(m, n, k);
 }
 
 // --------------------------------------------------------------------- AQN --

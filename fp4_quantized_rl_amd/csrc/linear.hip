@@ -9,8 +9,10 @@
 //   y = bf16( s_t * sum_k x g(code) S_b  +  t B^T )   (skinny_kernel)
 //
 // Decode (small M) is bound by the weight stream: 0.5625 byte per weight
-// (nibble + 1/16 scale byte). skinny_kernel streams codes with 16-byte loads
-// (one lane = 32 consecutive k of one row = two blocks), dequantises in
+// (nibble + 1/16 scale byte). The weights come in the tiled NVFP4 layout
+// (16-row x 128-k tiles, 1 KB of codes + 128 B of scales, stored in the order
+// the MFMA lanes consume them), so every wave load is one contiguous 1 KB
+// (one lane = 32 consecutive k of one row = two blocks). It dequantises in
 // registers (hardware E2M1 convert at unit scale, times the E4M3 block
 // scale: exact in bf16) and feeds v_mfma_f32_16x16x32_bf16 with the weights
 // as the 16-row A operand and up to 8 tiles of 16 tokens as B operands. The
@@ -32,13 +34,17 @@ namespace {
 __device__ __forceinline__ uint4 ld16(const void* p) { return *reinterpret_cast<const uint4*>(p); }
 
 // ---------------------------------------------------------------------------
-// LoRA down-projection: t[m][j] = s * sum_k x[m][k] A[j][k].
-// One workgroup per 16x16 tile of t; its waves split K and reduce in LDS.
+// LoRA down-projection, split along K into `gridDim.z` slices of `kslice`:
+//   part[z][m][j] = s * sum_{k in slice z} x[m][k] A[j][k].
+// One workgroup per 16x16 tile of t and K slice; its waves take the 32-wide
+// steps of the slice round-robin, U steps' loads at a time, and reduce
+// through LDS. With one slice, `part` is t itself; otherwise the slices are
+// summed in slice order by lora_reduce_kernel or by the linear's epilogue.
 // ---------------------------------------------------------------------------
-template <int WAVES>
+template <int WAVES, int U = 4>
 __global__ __launch_bounds__(WAVES * kWave) void lora_down_kernel(const uint16_t* __restrict__ x, int M, int K,
                                                                    const uint16_t* __restrict__ a, int r, float s,
-                                                                   float* __restrict__ t) {
+                                                                   int kslice, float* __restrict__ part) {
   const int lane = threadIdx.x & (kWave - 1), wave = threadIdx.x / kWave;
   const int li = lane & 15, lg = lane >> 4;
   const int m0 = blockIdx.x * 16, j0 = blockIdx.y * 16;
@@ -46,22 +52,22 @@ __global__ __launch_bounds__(WAVES * kWave) void lora_down_kernel(const uint16_t
   const uint16_t* xr = x + (int64_t)min(m, M - 1) * K;
   const uint16_t* ar = a + (int64_t)min(j, r - 1) * K;
   const bool mv = m < M, jv = j < r;
+  const int kbeg = blockIdx.z * kslice;
+  const int kend = min(K, kbeg + kslice);
+  const int nsteps = (kend - kbeg + 31) / 32;
+  const int mine = nsteps > wave ? (nsteps - wave + WAVES - 1) / WAVES : 0;
   f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-  const int nsteps = (K + 31) / 32;
-  int c = wave;
-  for (; c + WAVES < nsteps; c += 2 * WAVES) {
-    const int k0 = 32 * c + 8 * lg, k1 = k0 + 32 * WAVES;
-    const uint4 z = make_uint4(0, 0, 0, 0);
-    const uint4 x0 = mv ? ld16(xr + k0) : z, a0 = jv ? ld16(ar + k0) : z;
-    const uint4 x1 = (mv && k1 < K) ? ld16(xr + k1) : z, a1 = (jv && k1 < K) ? ld16(ar + k1) : z;
-    acc = mfma16x16x32(as_bf16x8(x0), as_bf16x8(a0), acc);
-    acc = mfma16x16x32(as_bf16x8(x1), as_bf16x8(a1), acc);
-  }
-  for (; c < nsteps; c += WAVES) {
-    const int k0 = 32 * c + 8 * lg;
-    const uint4 z = make_uint4(0, 0, 0, 0);
-    const uint4 x0 = (mv && k0 < K) ? ld16(xr + k0) : z, a0 = (jv && k0 < K) ? ld16(ar + k0) : z;
-    acc = mfma16x16x32(as_bf16x8(x0), as_bf16x8(a0), acc);
+  for (int g0 = 0; g0 < mine; g0 += U) {
+    uint4 xv[U], av[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int k0 = kbeg + 32 * (wave + WAVES * (g0 + u)) + 8 * lg;
+      const bool kv = (g0 + u < mine) && k0 < kend;
+      xv[u] = (mv && kv) ? ld16(xr + k0) : make_uint4(0, 0, 0, 0);
+      av[u] = (jv && kv) ? ld16(ar + k0) : make_uint4(0, 0, 0, 0);
+    }
+#pragma unroll
+    for (int u = 0; u < U; ++u) acc = mfma16x16x32(as_bf16x8(xv[u]), as_bf16x8(av[u]), acc);
   }
   __shared__ f32x4 red[WAVES][kWave];
   red[wave][lane] = acc;
@@ -71,12 +77,22 @@ __global__ __launch_bounds__(WAVES * kWave) void lora_down_kernel(const uint16_t
 #pragma unroll
     for (int w = 1; w < WAVES; ++w) sum += red[w][lane];
     // lane holds rows 4*lg + v (tokens), column li (rank index)
+    float* dst = part + (int64_t)blockIdx.z * M * r;
 #pragma unroll
     for (int v = 0; v < 4; ++v) {
       const int mm = m0 + 4 * lg + v, jj = j0 + li;
-      if (mm < M && jj < r) t[(int64_t)mm * r + jj] = s * sum[v];
+      if (mm < M && jj < r) dst[(int64_t)mm * r + jj] = s * sum[v];
     }
   }
+}
+
+// t[i] = sum_{z < slices} part[z][i], summed in slice order (deterministic).
+__global__ void lora_reduce_kernel(const float* __restrict__ part, int slices, int64_t count, float* __restrict__ t) {
+  const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (i >= count) return;
+  float acc = part[i];
+  for (int z = 1; z < slices; ++z) acc += part[(int64_t)z * count + i];
+  t[i] = acc;
 }
 
 // ---------------------------------------------------------------------------
@@ -84,27 +100,35 @@ __global__ __launch_bounds__(WAVES * kWave) void lora_down_kernel(const uint16_t
 //   grid.x: row groups of 16*NT output features; grid.y: token groups of 16*MT.
 //   WAVES waves per workgroup split the 128-wide K chunks round-robin.
 // ---------------------------------------------------------------------------
-template <int MT, int NT, int WAVES>
+// U: chunks whose loads are in flight together; the code + activation
+// registers of a group (U * (4 NT + 16 MT)) are kept near 96 per lane (64
+// for 1024-thread workgroups, whose waves have at most 128 registers).
+constexpr int skinny_group(int mt, int nt, int waves) {
+  const int budget = waves >= 16 ? 64 : 96;
+  const int u = mt <= 4 ? budget / (4 * nt + 16 * mt) : 2;
+  return u > 0 ? u : 1;
+}
+template <int MT, int NT, int WAVES, int U = skinny_group(MT, NT, WAVES)>
 __global__ __launch_bounds__(WAVES * kWave) void skinny_kernel(
     const uint16_t* __restrict__ x, int M, int N, int K, const uint8_t* __restrict__ codes,
     const uint8_t* __restrict__ scales, const float* __restrict__ tensor_scale, const float* __restrict__ t,
-    const uint16_t* __restrict__ lb, int r, uint16_t* __restrict__ y) {
+    int tks, const uint16_t* __restrict__ lb, int r, uint16_t* __restrict__ y) {
   const int lane = threadIdx.x & (kWave - 1), wave = threadIdx.x / kWave;
   const int li = lane & 15, lg = lane >> 4;
   const int n0 = blockIdx.x * (16 * NT);
   const int m0 = blockIdx.y * (16 * MT);
-  const bool k32 = (K & 31) == 0;  // code rows are 16-byte aligned
-  const int64_t cst = K / 2, sst = K / 16;
-
-  const uint8_t* crow[NT];
-  const uint8_t* srow[NT];
-  bool nv[NT];
+  // Tiled weights: tile (rt, c) = 16 rows x 128 k; this lane's 16 code bytes
+  // sit at 16 * lane and its 2 scale bytes at 2 * lane of the tile.
+  const int RT = (N + 15) >> 4, KC = (K + 127) >> 7;
+  const uint8_t* ctile[NT];
+  const uint8_t* stile[NT];
+  bool tv[NT];
 #pragma unroll
   for (int i = 0; i < NT; ++i) {
-    const int n = n0 + 16 * i + li;
-    nv[i] = n < N;
-    crow[i] = codes + (int64_t)min(n, N - 1) * cst;
-    srow[i] = scales + (int64_t)min(n, N - 1) * sst;
+    const int rt = blockIdx.x * NT + i;
+    tv[i] = rt < RT;
+    ctile[i] = codes + (int64_t)min(rt, RT - 1) * KC * 1024 + 16 * lane;
+    stile[i] = scales + (int64_t)min(rt, RT - 1) * KC * 128 + 2 * lane;
   }
   const uint16_t* xrow[MT];
   bool mv[MT];
@@ -121,61 +145,78 @@ __global__ __launch_bounds__(WAVES * kWave) void skinny_kernel(
 #pragma unroll
     for (int j = 0; j < MT; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
 
+  // Each wave owns the 128-wide K chunks wave, wave+WAVES, ...; it issues the
+  // code, scale and (for MT <= 4) activation loads of U chunks at once, so a
+  // wave waits for memory about once per group, then dequantises and
+  // multiplies the chunks one by one. With MT = 8 the activation fragments of
+  // a chunk (128 registers) are loaded step by step instead.
+  constexpr bool XPRE = MT <= 4;
+  constexpr int XU = XPRE ? U : 1;
   const int nchunk = (K + 127) / 128;
-  for (int c = wave; c < nchunk; c += WAVES) {
-    const int kb = 128 * c + 32 * lg;  // first k of this lane's 32-wide slice
-    const int kv = K - kb;             // valid k from kb: >= 32, 16, or <= 0
-    uint32_t cw[NT][4];
-    uint32_t sw[NT];
+  const int mine = nchunk > wave ? (nchunk - wave + WAVES - 1) / WAVES : 0;
+  for (int g0 = 0; g0 < mine; g0 += U) {
+    uint32_t cw[U][NT][4];
+    uint32_t sw[U][NT];
+    uint4 xq[XU][4][MT];
 #pragma unroll
-    for (int i = 0; i < NT; ++i) {
-      cw[i][0] = cw[i][1] = cw[i][2] = cw[i][3] = 0u;
-      sw[i] = 0u;
-      if (nv[i] && kv > 0) {
-        const uint8_t* cp = crow[i] + kb / 2;
-        const uint8_t* sp = srow[i] + kb / 16;
-        if (kv >= 32 && k32) {
-          const uint4 v = ld16(cp);
-          cw[i][0] = v.x; cw[i][1] = v.y; cw[i][2] = v.z; cw[i][3] = v.w;
-          sw[i] = *reinterpret_cast<const uint16_t*>(sp);
-        } else {
-          const uint2 v = *reinterpret_cast<const uint2*>(cp);
-          cw[i][0] = v.x; cw[i][1] = v.y;
-          sw[i] = sp[0];
-          if (kv >= 32) {
-            const uint2 u = *reinterpret_cast<const uint2*>(cp + 8);
-            cw[i][2] = u.x; cw[i][3] = u.y;
-            sw[i] |= (uint32_t)sp[1] << 8;
-          }
-        }
-      }
-    }
-    float s0[NT], s1[NT];
-#pragma unroll
-    for (int i = 0; i < NT; ++i) {
-      s0[i] = e4m3_to_f32(sw[i] & 0xFFu);
-      s1[i] = e4m3_to_f32(sw[i] >> 8);
-    }
-#pragma unroll
-    for (int s = 0; s < 4; ++s) {
-      bf16x8 xv[MT];
-#pragma unroll
-      for (int j = 0; j < MT; ++j) {
-        uint4 v = make_uint4(0, 0, 0, 0);
-        if (mv[j] && 8 * s < kv) v = ld16(xrow[j] + kb + 8 * s);
-        xv[j] = as_bf16x8(v);
-      }
+    for (int u = 0; u < U; ++u) {
+      const int kb = 128 * (wave + WAVES * (g0 + u)) + 32 * lg;
+      const bool cv = g0 + u < mine;
+      const int kv = cv ? K - kb : 0;  // valid k from kb (the tile itself is zero-padded)
+      const int c = wave + WAVES * (g0 + u);
 #pragma unroll
       for (int i = 0; i < NT; ++i) {
-        const bf16x8 a = dequant8(cw[i][s], s < 2 ? s0[i] : s1[i]);
+        cw[u][i][0] = cw[u][i][1] = cw[u][i][2] = cw[u][i][3] = 0u;
+        sw[u][i] = 0u;
+        if (cv && tv[i]) {
+          const uint4 v = ld_nt16(ctile[i] + (int64_t)c * 1024);
+          cw[u][i][0] = v.x; cw[u][i][1] = v.y; cw[u][i][2] = v.z; cw[u][i][3] = v.w;
+          sw[u][i] = __builtin_nontemporal_load(reinterpret_cast<const uint16_t*>(stile[i] + (int64_t)c * 128));
+        }
+      }
+      if constexpr (XPRE) {
 #pragma unroll
-        for (int j = 0; j < MT; ++j) acc[i][j] = mfma16x16x32(a, xv[j], acc[i][j]);
+        for (int s = 0; s < 4; ++s)
+#pragma unroll
+          for (int j = 0; j < MT; ++j)
+            xq[u][s][j] = (mv[j] && 8 * s < kv) ? ld16(xrow[j] + kb + 8 * s) : make_uint4(0, 0, 0, 0);
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      if (g0 + u >= mine) break;  // uniform across the wave
+      const int kb = 128 * (wave + WAVES * (g0 + u)) + 32 * lg;
+      const int kv = K - kb;
+      float s0[NT], s1[NT];
+#pragma unroll
+      for (int i = 0; i < NT; ++i) {
+        s0[i] = e4m3_to_f32(sw[u][i] & 0xFFu);
+        s1[i] = e4m3_to_f32(sw[u][i] >> 8);
+      }
+#pragma unroll
+      for (int s = 0; s < 4; ++s) {
+        bf16x8 xv[MT];
+#pragma unroll
+        for (int j = 0; j < MT; ++j) {
+          if constexpr (XPRE) {
+            xv[j] = as_bf16x8(xq[u][s][j]);
+          } else {
+            xv[j] = as_bf16x8((mv[j] && 8 * s < kv) ? ld16(xrow[j] + kb + 8 * s) : make_uint4(0, 0, 0, 0));
+          }
+        }
+#pragma unroll
+        for (int i = 0; i < NT; ++i) {
+          const bf16x8 a = dequant8(cw[u][i][s], s < 2 ? s0[i] : s1[i]);
+#pragma unroll
+          for (int j = 0; j < MT; ++j) acc[i][j] = mfma16x16x32(a, xv[j], acc[i][j]);
+        }
       }
     }
   }
 
   const float st = *tensor_scale;
   const bool rvec = (r & 7) == 0;
+  const int64_t tstride = (int64_t)M * r;
   // Epilogue of one 16x16 tile: lane holds features n = n0+16i+4lg+v and token m = m0+16j+li.
   auto epilogue = [&](int i, int j, f32x4 v) {
     f32x4 lo = {0.f, 0.f, 0.f, 0.f};
@@ -190,10 +231,13 @@ __global__ __launch_bounds__(WAVES * kWave) void skinny_kernel(
           if (rvec) {
             if (na < N) bw = ld16(lb + (int64_t)na * r + jj);
             if (mb < M) {
-              const float4 t0 = *reinterpret_cast<const float4*>(t + (int64_t)mb * r + jj);
-              const float4 t1 = *reinterpret_cast<const float4*>(t + (int64_t)mb * r + jj + 4);
-              tv[0] = t0.x; tv[1] = t0.y; tv[2] = t0.z; tv[3] = t0.w;
-              tv[4] = t1.x; tv[5] = t1.y; tv[6] = t1.z; tv[7] = t1.w;
+              for (int q = 0; q < tks; ++q) {  // K-slices of t, summed in order
+                const float* tp = t + (int64_t)q * tstride + (int64_t)mb * r + jj;
+                const float4 t0 = *reinterpret_cast<const float4*>(tp);
+                const float4 t1 = *reinterpret_cast<const float4*>(tp + 4);
+                tv[0] += t0.x; tv[1] += t0.y; tv[2] += t0.z; tv[3] += t0.w;
+                tv[4] += t1.x; tv[5] += t1.y; tv[6] += t1.z; tv[7] += t1.w;
+              }
             }
           } else {
             uint32_t h[8];
@@ -201,7 +245,8 @@ __global__ __launch_bounds__(WAVES * kWave) void skinny_kernel(
             for (int e = 0; e < 8; ++e) {
               const bool ok = jj + e < r;
               h[e] = (ok && na < N) ? lb[(int64_t)na * r + jj + e] : 0u;
-              tv[e] = (ok && mb < M) ? t[(int64_t)mb * r + jj + e] : 0.f;
+              if (ok && mb < M)
+                for (int q = 0; q < tks; ++q) tv[e] += t[(int64_t)q * tstride + (int64_t)mb * r + jj + e];
             }
             bw = make_uint4(h[0] | (h[1] << 16), h[2] | (h[3] << 16), h[4] | (h[5] << 16), h[6] | (h[7] << 16));
           }
@@ -254,51 +299,39 @@ struct SkinnyCfg {
   int mt, nt, waves;
 };
 
-// Pick tile counts so that the launch has ~1.5k+ waves in flight (6 per CU)
-// while the LDS reduction buffer stays within 64 KB (waves*nt*mt <= 64).
+// Token tiles (16*mt) cover M; row tiles per workgroup (nt) grow with M so the
+// activation fragments a lane loads are reused across more weight rows; the
+// waves per workgroup split K so that ~4k waves are in flight (16 per CU),
+// within a 64 KB LDS reduction buffer (waves * nt * mt <= 64).
 SkinnyCfg pick_skinny(int64_t m, int64_t n, int64_t k) {
   const int mt = m <= 16 ? 1 : m <= 32 ? 2 : m <= 64 ? 4 : 8;
+  const int nt = m <= 16 ? 1 : m <= 32 ? 2 : m <= 64 ? 4 : 2;
   const int64_t gy = (m + 16 * mt - 1) / (16 * mt);
-  const int64_t nchunk = (k + 127) / 128;
-  SkinnyCfg best{mt, 2, 1};
-  int64_t best_waves = -1;
-  for (int nt : {4, 2}) {
-    if (mt == 8 && nt == 4) continue;  // accumulators + operands would exceed the register file
-    const int64_t groups = (n + 16 * nt - 1) / (16 * nt) * gy;
-    int wmax = std::min<int64_t>(16, 64 / (nt * mt));
-    wmax = (int)std::min<int64_t>(wmax, std::max<int64_t>(1, nchunk));
-    int w = 1;
-    while (w < wmax && groups * w < 1536) w *= 2;
-    w = std::min(w, wmax);
-    // round down to a power of two the templates provide
-    int wp = 1;
-    while (wp * 2 <= w) wp *= 2;
-    const int64_t tot = groups * wp;
-    if (tot >= 1536) return SkinnyCfg{mt, nt, wp};
-    if (tot > best_waves) {
-      best_waves = tot;
-      best = SkinnyCfg{mt, nt, wp};
-    }
-  }
-  return best;
+  const int64_t groups = (n + 16 * nt - 1) / (16 * nt) * gy;
+  const int64_t kc = (k + 127) / 128;
+  const int wmax = (int)std::min<int64_t>(std::min<int64_t>(16, 64 / (nt * mt)), std::max<int64_t>(1, kc));
+  int w = 1;
+  while (w * 2 <= wmax && groups * w < 4096) w *= 2;
+  return SkinnyCfg{mt, nt, w};
 }
 
 template <int MT, int NT, int W>
 hipError_t run_skinny(dim3 grid, hipStream_t st, const uint16_t* x, int M, int N, int K, const uint8_t* codes,
-                      const uint8_t* scales, const float* ts, const float* t, const uint16_t* b, int r, uint16_t* y) {
-  hipLaunchKernelGGL((skinny_kernel<MT, NT, W>), grid, dim3(W * kWave), 0, st, x, M, N, K, codes, scales, ts, t, b,
-                     r, y);
+                      const uint8_t* scales, const float* ts, const float* t, int tks, const uint16_t* b, int r,
+                      uint16_t* y) {
+  hipLaunchKernelGGL((skinny_kernel<MT, NT, W>), grid, dim3(W * kWave), 0, st, x, M, N, K, codes, scales, ts, t, tks,
+                     b, r, y);
   return hipGetLastError();
 }
 
 template <int MT, int NT>
 hipError_t run_skinny_w(int w, dim3 grid, hipStream_t st, const uint16_t* x, int M, int N, int K,
-                        const uint8_t* codes, const uint8_t* scales, const float* ts, const float* t,
+                        const uint8_t* codes, const uint8_t* scales, const float* ts, const float* t, int tks,
                         const uint16_t* b, int r, uint16_t* y) {
   // only waves * MT * NT <= 64 is instantiated: the reduction buffer is at most 64 KB of LDS
 #define FP4RL_CASE(W_)                                                                             \
   case W_:                                                                                         \
-    if constexpr (W_ * MT * NT <= 64) return run_skinny<MT, NT, W_>(grid, st, x, M, N, K, codes, scales, ts, t, b, r, y); \
+    if constexpr (W_ * MT * NT <= 64) return run_skinny<MT, NT, W_>(grid, st, x, M, N, K, codes, scales, ts, t, tks, b, r, y); \
     break;
   switch (w) {
     FP4RL_CASE(1) FP4RL_CASE(2) FP4RL_CASE(4) FP4RL_CASE(8) FP4RL_CASE(16)
@@ -310,29 +343,72 @@ hipError_t run_skinny_w(int w, dim3 grid, hipStream_t st, const uint16_t* x, int
 
 }  // namespace
 
+int lora_splits(int64_t m, int64_t k, int64_t r) {
+  (void)r;
+  if (m > 128) return 1;  // prefill: token tiles already fill the chip
+  // The linear's epilogue re-reads every slice for its 16*mt tokens: keep
+  // slices * mt <= 8 so that stays a few KB per workgroup.
+  const int mt = m <= 16 ? 1 : m <= 32 ? 2 : m <= 64 ? 4 : 8;
+  const int64_t by_k = std::max<int64_t>(1, k / 512);  // at least 512 k per slice
+  return (int)std::min<int64_t>(8 / mt, by_k);
+}
+
+static int64_t slice_len(int64_t k, int splits) { return ((k + splits - 1) / splits + 31) / 32 * 32; }
+
 hipError_t launch_lora_down(const uint16_t* x, int64_t m, int64_t k, const uint16_t* a, int64_t r, float lora_scale,
-                            float* t, hipStream_t stream) {
-  const dim3 grid((unsigned)((m + 15) / 16), (unsigned)((r + 15) / 16));
-  if (m <= 256)
+                            int splits, float* part, hipStream_t stream) {
+  const int64_t ks = slice_len(k, splits);
+  const dim3 grid((unsigned)((m + 15) / 16), (unsigned)((r + 15) / 16), (unsigned)((k + ks - 1) / ks));
+  if ((m + 15) / 16 * ((r + 15) / 16) * grid.z <= 256)
     hipLaunchKernelGGL(lora_down_kernel<16>, grid, dim3(16 * kWave), 0, stream, x, (int)m, (int)k, a, (int)r,
-                       lora_scale, t);
+                       lora_scale, (int)ks, part);
   else
     hipLaunchKernelGGL(lora_down_kernel<4>, grid, dim3(4 * kWave), 0, stream, x, (int)m, (int)k, a, (int)r,
-                       lora_scale, t);
+                       lora_scale, (int)ks, part);
   return hipGetLastError();
 }
 
+int lora_slices(int64_t k, int splits) {
+  const int64_t ks = slice_len(k, splits);
+  return (int)((k + ks - 1) / ks);
+}
+
+hipError_t launch_lora_reduce(const float* part, int slices, int64_t count, float* t, hipStream_t stream) {
+  hipLaunchKernelGGL(lora_reduce_kernel, dim3((unsigned)((count + 255) / 256)), dim3(256), 0, stream, part, slices,
+                     count, t);
+  return hipGetLastError();
+}
+
+const char* fp4_linear_kernel_name(int64_t m, int64_t n, int64_t k) {
+  static const char* const kNames[4][3][5] = {
+#define FP4RL_NAME_ROW(MT_, NT_)                                                                           \
+  {"skinny_kernel<" #MT_ ", " #NT_ ", 1>", "skinny_kernel<" #MT_ ", " #NT_ ", 2>",                          \
+   "skinny_kernel<" #MT_ ", " #NT_ ", 4>", "skinny_kernel<" #MT_ ", " #NT_ ", 8>",                          \
+   "skinny_kernel<" #MT_ ", " #NT_ ", 16>"}
+      {FP4RL_NAME_ROW(1, 1), FP4RL_NAME_ROW(1, 2), FP4RL_NAME_ROW(1, 4)},
+      {FP4RL_NAME_ROW(2, 1), FP4RL_NAME_ROW(2, 2), FP4RL_NAME_ROW(2, 4)},
+      {FP4RL_NAME_ROW(4, 1), FP4RL_NAME_ROW(4, 2), FP4RL_NAME_ROW(4, 4)},
+      {FP4RL_NAME_ROW(8, 1), FP4RL_NAME_ROW(8, 2), FP4RL_NAME_ROW(8, 4)},
+#undef FP4RL_NAME_ROW
+  };
+  const SkinnyCfg c = pick_skinny(m, n, k);
+  const int mi = c.mt == 1 ? 0 : c.mt == 2 ? 1 : c.mt == 4 ? 2 : 3;
+  const int ni = c.nt == 1 ? 0 : c.nt == 2 ? 1 : 2;
+  int wi = 0;
+  while ((1 << wi) < c.waves) ++wi;
+  return kNames[mi][ni][wi];
+}
+
 hipError_t launch_fp4_linear(const uint16_t* x, int64_t m, int64_t n, int64_t k, const uint8_t* codes,
-                             const uint8_t* scales, const float* tensor_scale, const float* t, const uint16_t* b,
-                             int64_t r, uint16_t* y, hipStream_t stream) {
+                             const uint8_t* scales, const float* tensor_scale, const float* t, int tks,
+                             const uint16_t* b, int64_t r, uint16_t* y, hipStream_t stream) {
   const SkinnyCfg cfg = pick_skinny(m, n, k);
   const dim3 grid((unsigned)((n + 16 * cfg.nt - 1) / (16 * cfg.nt)), (unsigned)((m + 16 * cfg.mt - 1) / (16 * cfg.mt)));
   const int M = (int)m, N = (int)n, K = (int)k, R = (int)r;
 #define FP4RL_SKINNY(MT_, NT_) \
   if (cfg.mt == MT_ && cfg.nt == NT_) \
-    return run_skinny_w<MT_, NT_>(cfg.waves, grid, stream, x, M, N, K, codes, scales, tensor_scale, t, b, R, y);
-  FP4RL_SKINNY(1, 2) FP4RL_SKINNY(1, 4) FP4RL_SKINNY(2, 2) FP4RL_SKINNY(2, 4)
-  FP4RL_SKINNY(4, 2) FP4RL_SKINNY(4, 4) FP4RL_SKINNY(8, 2)
+    return run_skinny_w<MT_, NT_>(cfg.waves, grid, stream, x, M, N, K, codes, scales, tensor_scale, t, tks, b, R, y);
+  FP4RL_SKINNY(1, 1) FP4RL_SKINNY(2, 2) FP4RL_SKINNY(4, 4) FP4RL_SKINNY(8, 2)
 #undef FP4RL_SKINNY
   return hipErrorInvalidValue;
 }

@@ -103,12 +103,33 @@ __device__ __forceinline__ void load_quarter(const void* w, int64_t idx, float v
   }
 }
 
-template <bool BF16>
+// Destination of block b's two code bytes of quarter q and of its scale byte.
+// Row-major: codes [n][k/2], scales [n][k/16]. Tiled: 16-row x 128-k tiles
+// (1 KB of codes + 128 B of scales each, tile (rt, c) at rt*kc + c), inside
+// which lane l = 16 g + i of a wave finds its 16 code bytes at 16 l and its
+// two scale bytes at 2 l: row i, k = 128 c + 32 g .. + 31.
+template <bool TILED>
+__device__ __forceinline__ void block_dest(int64_t b, int q, uint32_t kblocks, uint32_t kc, int64_t& code_off,
+                                           int64_t& scale_off) {
+  if constexpr (TILED) {
+    const uint32_t n = (uint32_t)b / kblocks, kb = (uint32_t)b - n * kblocks;
+    const uint32_t lane = 16u * ((kb & 7u) >> 1) + (n & 15u);
+    const int64_t tile = (int64_t)(n >> 4) * kc + (kb >> 3);
+    code_off = tile * 1024 + 16 * lane + 8 * (kb & 1u) + 2 * q;
+    scale_off = tile * 128 + 2 * lane + (kb & 1u);
+  } else {
+    code_off = 8 * b + 2 * q;
+    scale_off = b;
+  }
+}
+
+template <bool BF16, bool TILED>
 __global__ __launch_bounds__(kThreads) void encode_kernel(const void* __restrict__ w, int64_t nblk,
                                                            const uint32_t* __restrict__ partial,
                                                            int npartial, uint8_t* __restrict__ codes,
                                                            uint8_t* __restrict__ scales,
-                                                           float* __restrict__ tensor_scale) {
+                                                           float* __restrict__ tensor_scale, uint32_t kblocks,
+                                                           uint32_t kc) {
 #pragma clang fp contract(off)
   __shared__ uint32_t red[kThreads / kWave];
   uint32_t mx = 0;
@@ -125,7 +146,6 @@ __global__ __launch_bounds__(kThreads) void encode_kernel(const void* __restrict
 
   const int q = threadIdx.x & 3;  // quarter of the block this lane holds
   const int64_t nquads = (int64_t)gridDim.x * (kThreads / 4);
-  uint16_t* code16 = reinterpret_cast<uint16_t*>(codes);
   for (int64_t b0 = ((int64_t)blockIdx.x * kThreads + threadIdx.x) / 4; b0 < nblk;
        b0 += kUnroll * nquads) {
     float v[kUnroll][4];
@@ -150,25 +170,82 @@ __global__ __launch_bounds__(kThreads) void encode_kernel(const void* __restrict
       const bool dz = D == 0.0f;
       const uint32_t c = e2m1_encode(v[u][0], dz, Ds, xs) | (e2m1_encode(v[u][1], dz, Ds, xs) << 4) |
                          (e2m1_encode(v[u][2], dz, Ds, xs) << 8) | (e2m1_encode(v[u][3], dz, Ds, xs) << 12);
-      code16[4 * b + q] = (uint16_t)c;
-      if (q == 0) scales[b] = (uint8_t)byte;
+      int64_t co, so;
+      block_dest<TILED>(b, q, kblocks, kc, co, so);
+      *reinterpret_cast<uint16_t*>(codes + co) = (uint16_t)c;
+      if (q == 0) scales[so] = (uint8_t)byte;
     }
   }
 }
 
 __global__ void write_zero_scale(float* tensor_scale) { *tensor_scale = 0.0f; }
 
+// Zero fill (the padding of tiled buffers); a kernel rather than a memset so
+// that captured graphs hold only kernel nodes.
+__global__ void zero_fill(uint4* __restrict__ p, int64_t n16) {
+  for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n16; i += (int64_t)gridDim.x * blockDim.x)
+    p[i] = make_uint4(0, 0, 0, 0);
+}
+
+// Row-major NVFP4 -> tiled: one thread per 16-byte code piece of a tile.
+__global__ void to_tiled_kernel(const uint8_t* __restrict__ codes, const uint8_t* __restrict__ scales, int N, int K,
+                                int kc, int64_t pieces, uint8_t* __restrict__ codes_t, uint8_t* __restrict__ scales_t) {
+  const int64_t p = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (p >= pieces) return;
+  const int lane = (int)(p & 63);
+  const int64_t tile = p >> 6;
+  const int rt = (int)(tile / kc), c = (int)(tile - (int64_t)rt * kc);
+  const int n = 16 * rt + (lane & 15), k0 = 128 * c + 32 * (lane >> 4);
+  uint4 v = make_uint4(0, 0, 0, 0);
+  uint32_t sv = 0;
+  if (n < N && k0 < K) {
+    const uint8_t* cr = codes + (int64_t)n * (K / 2) + k0 / 2;
+    const uint8_t* sr = scales + (int64_t)n * (K / 16) + k0 / 16;
+    const uint2 a = *reinterpret_cast<const uint2*>(cr);  // rows are 8-byte aligned (K % 16 == 0)
+    v.x = a.x;
+    v.y = a.y;
+    sv = sr[0];
+    if (k0 + 16 < K) {
+      const uint2 b2 = *reinterpret_cast<const uint2*>(cr + 8);
+      v.z = b2.x;
+      v.w = b2.y;
+      sv |= (uint32_t)sr[1] << 8;
+    }
+  }
+  *reinterpret_cast<uint4*>(codes_t + tile * 1024 + 16 * lane) = v;
+  *reinterpret_cast<uint16_t*>(scales_t + tile * 128 + 2 * lane) = (uint16_t)sv;
+}
+
 }  // namespace
 
 size_t quantize_workspace_bytes() { return kAmaxPartials * sizeof(uint32_t); }
 
-hipError_t launch_quantize(const void* w, bool w_bf16, int64_t n, int64_t k, uint8_t* codes,
-                           uint8_t* scales, float* tensor_scale, uint32_t* partial,
-                           hipStream_t stream) {
+int64_t nvfp4_codes_bytes(int64_t n, int64_t k, bool tiled) {
+  return tiled ? ((n + 15) / 16) * ((k + 127) / 128) * 1024 : n * k / 2;
+}
+
+int64_t nvfp4_scales_bytes(int64_t n, int64_t k, bool tiled) {
+  return tiled ? ((n + 15) / 16) * ((k + 127) / 128) * 128 : n * k / 16;
+}
+
+static hipError_t fill_zero(uint8_t* p, int64_t bytes, hipStream_t stream) {
+  const int64_t n16 = bytes / 16;  // tiled buffers are whole tiles: multiples of 128 bytes
+  const int64_t grid = std::min<int64_t>(4096, (n16 + 255) / 256);
+  hipLaunchKernelGGL(zero_fill, dim3((unsigned)grid), dim3(256), 0, stream, reinterpret_cast<uint4*>(p), n16);
+  return hipGetLastError();
+}
+
+hipError_t launch_quantize(const void* w, bool w_bf16, int64_t n, int64_t k, bool tiled, uint8_t* codes,
+                           uint8_t* scales, float* tensor_scale, uint32_t* partial, hipStream_t stream) {
   const int64_t elems = n * k;
   if (elems == 0) {
     hipLaunchKernelGGL(write_zero_scale, dim3(1), dim3(1), 0, stream, tensor_scale);
     return hipGetLastError();
+  }
+  if (tiled && ((n & 15) != 0 || (k & 127) != 0)) {  // padding of partial tiles must read as zero
+    hipError_t e = fill_zero(codes, nvfp4_codes_bytes(n, k, true), stream);
+    if (e == hipSuccess) e = fill_zero(scales, nvfp4_scales_bytes(n, k, true), stream);
+    if (e != hipSuccess) return e;
   }
   const int64_t nvec = elems / (w_bf16 ? 8 : 4);  // k % 16 == 0, so vectors never straddle
   const int64_t g1 = std::min<int64_t>(kAmaxPartials, std::max<int64_t>(1, (nvec + kThreads * kUnroll - 1) / (kThreads * kUnroll)));
@@ -182,13 +259,26 @@ hipError_t launch_quantize(const void* w, bool w_bf16, int64_t n, int64_t k, uin
   if (e != hipSuccess) return e;
   const int64_t nblk = elems / 16;
   const int64_t per_wg = (kThreads / 4) * kUnroll;
-  const int64_t g2 = std::min<int64_t>(8192, (nblk + per_wg - 1) / per_wg);
-  if (w_bf16)
-    hipLaunchKernelGGL(encode_kernel<true>, dim3((unsigned)g2), dim3(kThreads), 0, stream, w, nblk,
-                       partial, (int)g1, codes, scales, tensor_scale);
-  else
-    hipLaunchKernelGGL(encode_kernel<false>, dim3((unsigned)g2), dim3(kThreads), 0, stream, w, nblk,
-                       partial, (int)g1, codes, scales, tensor_scale);
+  const dim3 grid((unsigned)std::min<int64_t>(8192, (nblk + per_wg - 1) / per_wg));
+  const uint32_t kblocks = (uint32_t)(k / 16), kc = (uint32_t)((k + 127) / 128);
+#define FP4RL_ENCODE(B_, T_) \
+  hipLaunchKernelGGL((encode_kernel<B_, T_>), grid, dim3(kThreads), 0, stream, w, nblk, partial, (int)g1, codes, \
+                     scales, tensor_scale, kblocks, kc)
+  if (w_bf16) {
+    if (tiled) FP4RL_ENCODE(true, true); else FP4RL_ENCODE(true, false);
+  } else {
+    if (tiled) FP4RL_ENCODE(false, true); else FP4RL_ENCODE(false, false);
+  }
+#undef FP4RL_ENCODE
+  return hipGetLastError();
+}
+
+hipError_t launch_to_tiled(const uint8_t* codes, const uint8_t* scales, int64_t n, int64_t k, uint8_t* codes_t,
+                           uint8_t* scales_t, hipStream_t stream) {
+  const int64_t kc = (k + 127) / 128;
+  const int64_t pieces = ((n + 15) / 16) * kc * 64;
+  hipLaunchKernelGGL(to_tiled_kernel, dim3((unsigned)((pieces + 255) / 256)), dim3(256), 0, stream, codes, scales,
+                     (int)n, (int)k, (int)kc, pieces, codes_t, scales_t);
   return hipGetLastError();
 }
 

@@ -76,35 +76,53 @@ int32_t fp4rl_abi_version(void);
 /* ------------------------------------------------------------------------
  * NVFP4 quantiser.
  *
- * W [n][k] (fp32 or bf16, w_dtype) -> codes [n][k/2] bytes, scales [n][k/16]
- * bytes, tensor_scale [1] fp32. k % 16 == 0.
+ * W [n][k] (fp32 or bf16, w_dtype) -> codes, scales, tensor_scale [1] fp32.
+ * k % 16 == 0; n * k < 2^36.
  *   s_t  = fp32(amax / 2688), amax = max|W| (2688 = 6 * 448);
  *   byte = E4M3 (OCP e4m3fn, nearest-even, saturating at 448, subnormals kept)
  *          of r_b = fp32(a_b / fp32(6 s_t)), a_b = max|block|; 0 if s_t == 0;
  *   code = sign(x) << 3 | k, where g_k * fp32(S_b s_t) is the E2M1 grid point
  *          {0,.5,1,1.5,2,3,4,6} nearest to |x| in exact arithmetic, ties to even k.
- *   Blocks run along k; element 2j of a row is the low nibble of byte j.
- * Two kernels: a tensor-amax pass (per-workgroup partial maxima in the
- * workspace, no atomics) and an encode pass that re-reads W.
- * Workspace: fp4rl_nvfp4_quantize_workspace(n, k) bytes, 16-byte aligned.
+ * Blocks are 16 consecutive elements of a row (along k).
+ * Layouts (fp4rl_nvfp4_codes_bytes / _scales_bytes give the sizes):
+ *   FP4RL_ROW_MAJOR  codes [n][k/2] (element 2j = low nibble of byte j),
+ *                    scales [n][k/16].
+ *   FP4RL_TILED      the operand layout of the linear kernels: 16-row x 128-k
+ *                    tiles, tile (rt, c) at index rt * ceil(k/128) + c, each
+ *                    1024 code bytes + 128 scale bytes. Inside a tile, the
+ *                    16 code bytes at offset 16 * (16 g + i) hold row 16 rt + i,
+ *                    k = 128 c + 32 g .. + 31 (low nibble first), and the 2
+ *                    scale bytes at 2 * (16 g + i) its blocks 8 c + 2 g, +1.
+ *                    Rows >= n and k >= k of partial tiles are zero.
+ * Two HBM passes (W is read twice): a tensor-amax pass that leaves
+ * per-workgroup partial maxima in the workspace (no atomics), and an encode
+ * pass. Workspace: fp4rl_nvfp4_quantize_workspace(n, k) bytes, 16-byte aligned.
+ * fp4rl_nvfp4_to_tiled repacks a row-major NVFP4 matrix into the tiled layout.
  * ---------------------------------------------------------------------- */
+typedef enum fp4rl_layout { FP4RL_ROW_MAJOR = 0, FP4RL_TILED = 1 } fp4rl_layout;
+
 size_t fp4rl_nvfp4_quantize_workspace(int64_t n, int64_t k);
-fp4rl_status fp4rl_nvfp4_quantize(const void* w, int32_t w_dtype, int64_t n, int64_t k,
+size_t fp4rl_nvfp4_codes_bytes(int64_t n, int64_t k, int32_t layout);
+size_t fp4rl_nvfp4_scales_bytes(int64_t n, int64_t k, int32_t layout);
+fp4rl_status fp4rl_nvfp4_quantize(const void* w, int32_t w_dtype, int64_t n, int64_t k, int32_t layout,
                                   uint8_t* codes, uint8_t* scales, float* tensor_scale,
                                   void* workspace, size_t workspace_bytes, fp4rl_stream stream);
+fp4rl_status fp4rl_nvfp4_to_tiled(const uint8_t* codes, const uint8_t* scales, int64_t n, int64_t k,
+                                  uint8_t* codes_tiled, uint8_t* scales_tiled, fp4rl_stream stream);
 
 /* ------------------------------------------------------------------------
  * Fused W4A16 + LoRA linear:
  *   y[m][n] = bf16_rne( s_t * sum_k x[m][k] g(code[n][k]) S_b(n,k)
  *                       + sum_j t[m][j] B[n][j] ),   t = lora_scale * x A^T.
- * x bf16 [m][k]; codes/scales/tensor_scale as produced by fp4rl_nvfp4_quantize
- * for an [n][k] matrix; A bf16 [r][k]; B bf16 [n][r]; y bf16 [m][n].
+ * x bf16 [m][k]; codes/scales/tensor_scale of an [n][k] matrix in the
+ * FP4RL_TILED layout; A bf16 [r][k]; B bf16 [n][r]; y bf16 [m][n].
  * k % 16 == 0; 0 <= r <= 256; r == 0 or lora_a == lora_b == NULL means no
  * LoRA term. Accumulation is fp32; the output is rounded once to bf16.
  * Launches the LoRA down-projection (when r > 0) and then the main kernel,
  * chosen by m: an MFMA skinny kernel for decode-shaped m, a tiled MFMA GEMM
  * with LDS-dequantised weight tiles for prefill-shaped m.
- * Workspace: fp4rl_fp4_lora_linear_workspace(m, n, k, r) bytes (holds t).
+ * Workspace: fp4rl_fp4_lora_linear_workspace(m, n, k, r) bytes: the K-split
+ * partial sums of t, which the main kernel's epilogue adds in a fixed order.
  * ---------------------------------------------------------------------- */
 size_t fp4rl_fp4_lora_linear_workspace(int64_t m, int64_t n, int64_t k, int64_t r);
 fp4rl_status fp4rl_fp4_lora_linear(const uint16_t* x, int64_t m, int64_t n, int64_t k,
@@ -116,16 +134,27 @@ fp4rl_status fp4rl_fp4_lora_linear(const uint16_t* x, int64_t m, int64_t n, int6
 
 /* The two halves of fp4rl_fp4_lora_linear, for callers that produce t
  * elsewhere or time the main kernel alone.
- * fp4rl_lora_down: t [m][r] fp32 = lora_scale * x A^T (fp32 accumulate).
+ * fp4rl_lora_down: t [m][r] fp32 = lora_scale * x A^T (fp32 accumulate). For
+ *   decode-shaped m the product is split along k over many workgroups; the
+ *   partial sums go to the workspace (fp4rl_lora_down_workspace bytes, 0 when
+ *   no split is used) and are added in a fixed order, so t is deterministic.
  * fp4rl_fp4_linear_lora_up: y = bf16(s_t * x deq^T + t B^T); t may be NULL
- * (with r == 0) for the base product alone. */
+ *   (with r == 0) for the base product alone. */
+size_t fp4rl_lora_down_workspace(int64_t m, int64_t k, int64_t r);
 fp4rl_status fp4rl_lora_down(const uint16_t* x, int64_t m, int64_t k, const uint16_t* lora_a,
-                             int64_t r, float lora_scale, float* t, fp4rl_stream stream);
+                             int64_t r, float lora_scale, float* t, void* workspace,
+                             size_t workspace_bytes, fp4rl_stream stream);
 fp4rl_status fp4rl_fp4_linear_lora_up(const uint16_t* x, int64_t m, int64_t n, int64_t k,
                                       const uint8_t* codes, const uint8_t* scales,
                                       const float* tensor_scale, const float* t,
                                       const uint16_t* lora_b, int64_t r, uint16_t* y,
                                       fp4rl_stream stream);
+
+/* [host] Name of the main-kernel instantiation fp4rl_fp4_linear_lora_up
+ * launches for this shape, as a demangler prints it (e.g.
+ * "skinny_kernel<4, 4, 4>"), so profiles can be matched to calls. Returns a
+ * static string; "" for invalid shapes. Touches no device. */
+const char* fp4rl_fp4_linear_kernel_name(int64_t m, int64_t n, int64_t k);
 
 /* ------------------------------------------------------------------------
  * AQN.

@@ -31,15 +31,49 @@ def u8_to_dev(a: np.ndarray, dev) -> torch.Tensor:
     return torch.from_numpy(np.ascontiguousarray(a, dtype=np.uint8)).to(dev)
 
 
+def tile_host(codes, scales, n, k):
+    """Row-major NVFP4 bytes -> the tiled layout (16-row x 128-k tiles), by index permutation.
+
+    Tile (rt, c): 1024 code bytes ordered [g][i][16 B] = row 16 rt + i, bytes
+    64 c + 16 g .. + 15; 128 scale bytes ordered [g][i][2] = blocks 8 c + 2 g, +1.
+    """
+    rt, kc = (n + 15) // 16, (k + 127) // 128
+    cp = np.zeros((rt * 16, kc * 64), np.uint8)
+    cp[:n, : k // 2] = codes
+    sp = np.zeros((rt * 16, kc * 8), np.uint8)
+    sp[:n, : k // 16] = scales
+    ct = cp.reshape(rt, 16, kc, 4, 16).transpose(0, 2, 3, 1, 4).reshape(-1)
+    st = sp.reshape(rt, 16, kc, 4, 2).transpose(0, 2, 3, 1, 4).reshape(-1)
+    return ct, st
+
+
+def untile_host(ct, st, n, k):
+    """Inverse of tile_host; also returns whether every padding byte is zero."""
+    rt, kc = (n + 15) // 16, (k + 127) // 128
+    cp = np.asarray(ct).reshape(rt, kc, 4, 16, 16).transpose(0, 3, 1, 2, 4).reshape(rt * 16, kc * 64)
+    sp = np.asarray(st).reshape(rt, kc, 4, 16, 2).transpose(0, 3, 1, 2, 4).reshape(rt * 16, kc * 8)
+    pad_zero = (not cp[n:].any() and not cp[:, k // 2:].any() and not sp[n:].any() and not sp[:, k // 16:].any())
+    return cp[:n, : k // 2].copy(), sp[:n, : k // 16].copy(), pad_zero
+
+
 def nvfp4_to_dev(codes, scales, s_t, dev) -> fr.NVFP4Weight:
-    return fr.NVFP4Weight(u8_to_dev(codes, dev), u8_to_dev(scales, dev),
-                          torch.tensor([np.float32(s_t)], dtype=torch.float32, device=dev))
+    """Upload an oracle (row-major) NVFP4 matrix in the tiled layout the linear reads."""
+    n, k = codes.shape[0], codes.shape[1] * 2
+    ct, st = tile_host(codes, scales, n, k)
+    return fr.NVFP4Weight(u8_to_dev(ct, dev), u8_to_dev(st, dev),
+                          torch.tensor([np.float32(s_t)], dtype=torch.float32, device=dev), n, k, "tiled")
 
 
 def nvfp4_from_dev(wq: fr.NVFP4Weight):
+    """Download an NVFP4 matrix as row-major (codes [n, k/2], scales [n, k/16], s_t)."""
     torch.cuda.synchronize()
-    return (wq.codes.cpu().numpy(), wq.scales.cpu().numpy(),
-            np.float32(wq.tensor_scale.cpu().numpy()[0]))
+    c, s = wq.codes.cpu().numpy(), wq.scales.cpu().numpy()
+    st = np.float32(wq.tensor_scale.cpu().numpy()[0])
+    if wq.layout == "tiled":
+        c, s, pad_zero = untile_host(c, s, wq.n, wq.k)
+        assert pad_zero, "tiled padding is not zero"
+        return c, s, st
+    return c.reshape(wq.n, wq.k // 2), s.reshape(wq.n, wq.k // 16), st
 
 
 def say(msg: str) -> None:

@@ -51,19 +51,24 @@ def test_status_strings(lib):
 
 
 def test_quantize_rejects_bad_arguments(lib):
-    q = lib.fp4rl_nvfp4_quantize
+    def q(w, dt, n, k, c, s, ts, wsp, wsb, layout=1):
+        return lib.fp4rl_nvfp4_quantize(w, dt, n, k, layout, c, s, ts, wsp, wsb, None)
+
     ws = lib.fp4rl_nvfp4_quantize_workspace(8, 32)
     assert ws >= 4
-    assert q(FAKE, 0, 8, 24, FAKE, FAKE, FAKE, FAKE, ws, None) == ERR_SHAPE
-    assert q(FAKE, 0, -1, 32, FAKE, FAKE, FAKE, FAKE, ws, None) == ERR_SHAPE
-    assert q(FAKE, 7, 8, 32, FAKE, FAKE, FAKE, FAKE, ws, None) == ERR_DTYPE
-    assert q(None, 0, 8, 32, FAKE, FAKE, FAKE, FAKE, ws, None) == ERR_NULL
-    assert q(FAKE, 0, 8, 32, FAKE, FAKE, None, FAKE, ws, None) == ERR_NULL
-    assert q(FAKE, 0, 8, 32, FAKE, FAKE, FAKE, None, ws, None) == ERR_WORKSPACE
-    assert q(FAKE, 0, 8, 32, FAKE, FAKE, FAKE, FAKE, ws - 1, None) == ERR_WORKSPACE
-    assert q(MIS, 0, 8, 32, FAKE, FAKE, FAKE, FAKE, ws, None) == ERR_ALIGN
-    assert q(FAKE, 0, 8, 32, FAKE, FAKE, FAKE + 1, FAKE, ws, None) == ERR_ALIGN
-    q(FAKE, 0, 8, 24, FAKE, FAKE, FAKE, FAKE, ws, None)
+    assert q(FAKE, 0, 8, 24, FAKE, FAKE, FAKE, FAKE, ws) == ERR_SHAPE
+    assert q(FAKE, 0, -1, 32, FAKE, FAKE, FAKE, FAKE, ws) == ERR_SHAPE
+    assert q(FAKE, 7, 8, 32, FAKE, FAKE, FAKE, FAKE, ws) == ERR_DTYPE
+    assert q(FAKE, 0, 8, 32, FAKE, FAKE, FAKE, FAKE, ws, layout=5) == ERR_VALUE
+    assert q(None, 0, 8, 32, FAKE, FAKE, FAKE, FAKE, ws) == ERR_NULL
+    assert q(FAKE, 0, 8, 32, FAKE, FAKE, None, FAKE, ws) == ERR_NULL
+    assert q(FAKE, 0, 8, 32, FAKE, FAKE, FAKE, None, ws) == ERR_WORKSPACE
+    assert q(FAKE, 0, 8, 32, FAKE, FAKE, FAKE, FAKE, ws - 1) == ERR_WORKSPACE
+    assert q(MIS, 0, 8, 32, FAKE, FAKE, FAKE, FAKE, ws) == ERR_ALIGN
+    assert q(FAKE, 0, 8, 32, FAKE, FAKE, FAKE + 1, FAKE, ws) == ERR_ALIGN
+    assert lib.fp4rl_nvfp4_to_tiled(FAKE, FAKE, 8, 24, FAKE, FAKE, None) == ERR_SHAPE
+    assert lib.fp4rl_nvfp4_to_tiled(FAKE, MIS, 8, 32, FAKE, FAKE, None) == ERR_ALIGN
+    q(FAKE, 0, 8, 24, FAKE, FAKE, FAKE, FAKE, ws)
     assert "multiple of 16" in lib.fp4rl_last_error().decode()
 
 
@@ -91,8 +96,12 @@ def test_linear_rejects_bad_arguments(lib):
     assert call(y=MIS) == ERR_ALIGN
     assert call(ts=FAKE + 2) == ERR_ALIGN
     assert call(m=0) == OK and call(n=0) == OK          # empty: no-op, nothing touched
-    assert lib.fp4rl_lora_down(FAKE, 4, 24, FAKE, 8, 1.0, FAKE, None) == ERR_SHAPE
-    assert lib.fp4rl_lora_down(FAKE, 4, 32, FAKE, 0, 1.0, FAKE, None) == OK
+    assert lib.fp4rl_lora_down(FAKE, 4, 24, FAKE, 8, 1.0, FAKE, FAKE, 1 << 20, None) == ERR_SHAPE
+    assert lib.fp4rl_lora_down(FAKE, 4, 32, FAKE, 0, 1.0, FAKE, None, 0, None) == OK
+    need = lib.fp4rl_lora_down_workspace(1, 3584, 32)
+    assert need >= 7 * 32 * 4
+    assert lib.fp4rl_lora_down(FAKE, 1, 3584, FAKE, 32, 1.0, FAKE, FAKE, need - 1, None) == ERR_WORKSPACE
+    assert lib.fp4rl_lora_down_workspace(8192, 3584, 32) == 0
     assert lib.fp4rl_fp4_linear_lora_up(FAKE, 4, 8, 32, FAKE, FAKE, FAKE, None, FAKE, 8, FAKE, None) == ERR_NULL
 
 
@@ -107,6 +116,15 @@ def test_aqn_rejects_bad_arguments(lib):
     assert f(FAKE, 0, 512, FAKE, 0.01, 0, 0, 0, 1e-6, FAKE, None, None) == OK
     assert lib.fp4rl_philox_words(0, 0, 0, -1, FAKE, None) == ERR_SHAPE
     assert lib.fp4rl_philox_words(0, 0, 0, 4, MIS, None) == ERR_ALIGN
+
+
+def test_layout_sizes(lib):
+    assert lib.fp4rl_nvfp4_codes_bytes(256, 512, 0) == 256 * 256
+    assert lib.fp4rl_nvfp4_scales_bytes(256, 512, 0) == 256 * 32
+    assert lib.fp4rl_nvfp4_codes_bytes(37, 80, 1) == 3 * 1 * 1024      # 3 row tiles x 1 k chunk
+    assert lib.fp4rl_nvfp4_scales_bytes(37, 80, 1) == 3 * 128
+    assert lib.fp4rl_nvfp4_codes_bytes(18944, 3584, 1) == 18944 * 3584 // 2
+    assert lib.fp4rl_nvfp4_codes_bytes(8, 24, 1) == 0                   # invalid k
 
 
 def test_aqn_sigma_host_function(lib):
@@ -124,7 +142,7 @@ def test_valid_call_without_gpu_reports_hip_error(lib):
     if torch.cuda.device_count() > 0:
         pytest.skip("a GPU is present; this checks the no-device path")
     ws = lib.fp4rl_nvfp4_quantize_workspace(8, 32)
-    assert lib.fp4rl_nvfp4_quantize(FAKE, 0, 8, 32, FAKE, FAKE, FAKE, FAKE, ws, None) == ERR_HIP
+    assert lib.fp4rl_nvfp4_quantize(FAKE, 0, 8, 32, 1, FAKE, FAKE, FAKE, FAKE, ws, None) == ERR_HIP
     assert lib.fp4rl_last_error().decode().startswith("hipGetDevice")
 
 

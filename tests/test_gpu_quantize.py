@@ -10,18 +10,18 @@ from oracle import nvfp4
 from workloads import (QWEN25_14B, bf16_bits, bf16_values, normal_f32, single_linear_config,
                        student_t3_weights, tensor_seed)
 
-from gpu_util import device, f32_to_dev, bf16_to_dev, nvfp4_from_dev, say
+from gpu_util import bf16_to_dev, device, f32_to_dev, nvfp4_from_dev, say, tile_host
 from test_oracle_nvfp4 import _load_golden
 
 pytestmark = pytest.mark.gpu
 
 
-def _gpu_quantize(w_np, dev, bf16=False):
+def _gpu_quantize(w_np, dev, bf16=False, layout="row_major"):
     if bf16:
         wt = bf16_to_dev(bf16_bits(w_np), dev)
     else:
         wt = f32_to_dev(w_np, dev)
-    return nvfp4_from_dev(fr.nvfp4_quantize(wt))
+    return nvfp4_from_dev(fr.nvfp4_quantize(wt, layout=layout))
 
 
 def _assert_exact(got, want, what):
@@ -60,7 +60,9 @@ def test_ragged_shapes(shape):
     dev = device()
     w = normal_f32(shape, 0.02, seed=shape[0] * 1000 + shape[1])
     say(f"quantize ragged {shape}")
-    _assert_exact(_gpu_quantize(w, dev), nvfp4.quantize(w), str(shape))
+    ref = nvfp4.quantize(w)
+    _assert_exact(_gpu_quantize(w, dev), ref, str(shape))
+    _assert_exact(_gpu_quantize(w, dev, layout="tiled"), ref, f"{shape} tiled")
     _assert_exact(_gpu_quantize(w, dev, bf16=True), nvfp4.quantize(bf16_values(bf16_bits(w))),
                   f"{shape} bf16")
 
@@ -121,6 +123,23 @@ def test_full_size_14b_heavy_tailed():
     _assert_exact((c[rows], s[rows], t), nvfp4.quantize_rows(w, rows), "14B gate rows")
 
 
+def test_tiled_layout_and_repack():
+    """The tiled quantiser output and the row-major -> tiled repack both equal the host permutation."""
+    dev = device()
+    for n, k in [(1, 16), (37, 80), (48, 384), (130, 272), (4608, 3584)]:
+        w = normal_f32((n, k), 0.02, n + k)
+        ref = nvfp4.quantize(w)
+        wt = f32_to_dev(w, dev)
+        tiled = fr.nvfp4_quantize(wt, layout="tiled")
+        _assert_exact(nvfp4_from_dev(tiled), ref, f"tiled {n}x{k}")
+        rm = fr.nvfp4_quantize(wt, layout="row_major")
+        rep = fr.nvfp4_to_tiled(rm)
+        torch.cuda.synchronize()
+        ct, st = tile_host(ref[0], ref[1], n, k)
+        assert np.array_equal(rep.codes.cpu().numpy(), ct) and np.array_equal(rep.scales.cpu().numpy(), st)
+        assert np.array_equal(tiled.codes.cpu().numpy(), ct) and np.array_equal(tiled.scales.cpu().numpy(), st)
+
+
 def test_repeat_runs_identical():
     dev = device()
     w = f32_to_dev(normal_f32((1024, 2048), 0.02, 9), dev)
@@ -131,6 +150,6 @@ def test_repeat_runs_identical():
 
 def test_empty_matrix_writes_zero_scale():
     dev = device()
-    wq = fr.nvfp4_quantize(torch.empty((0, 32), dtype=torch.float32, device=dev))
+    wq = fr.nvfp4_quantize(torch.empty((0, 32), dtype=torch.float32, device=dev), layout="row_major")
     torch.cuda.synchronize()
     assert float(wq.tensor_scale.cpu()[0]) == 0.0
