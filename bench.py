@@ -289,7 +289,7 @@ def main():
             launches = reps * len(clones[name])
             timing[(m, name)] = e0.elapsed_time(e1) * 1e-3 / launches
             del gr
-    kname = {(m, name): fr.fp4_linear_kernel_name(m, n, k) for m in TOKENS for name, (n, k) in shapes.items()}
+    kname = {(m, name): fr.fp4_linear_kernel_name(m, n, k, RANK) for m in TOKENS for name, (n, k) in shapes.items()}
     per_kernel = {}
     for (m, name), dt in timing.items():
         n, k = shapes[name]

@@ -55,7 +55,7 @@ _SIGNATURES = {
     "fp4rl_lora_down_workspace": (_c.c_size_t, [_I64, _I64, _I64]),
     "fp4rl_lora_down": (_STATUS, [_P, _I64, _I64, _P, _I64, _c.c_float, _P, _P, _c.c_size_t, _P]),
     "fp4rl_fp4_linear_lora_up": (_STATUS, [_P, _I64, _I64, _I64, _P, _P, _P, _P, _P, _I64, _P, _P]),
-    "fp4rl_fp4_linear_kernel_name": (_c.c_char_p, [_I64, _I64, _I64]),
+    "fp4rl_fp4_linear_kernel_name": (_c.c_char_p, [_I64, _I64, _I64, _I64]),
     "fp4rl_aqn_sigma": (_c.c_float, [_c.c_float, _c.c_float, _c.c_int32, _c.c_int32]),
     "fp4rl_aqn_rmsnorm": (_STATUS, [_P, _I64, _I64, _P, _c.c_float, _c.c_uint64, _c.c_uint64, _c.c_uint32,
                                     _c.c_float, _P, _P, _P]),
@@ -284,9 +284,9 @@ def fp4_linear_lora_up(x, wq: NVFP4Weight, t=None, lora_b=None, out=None):
     return out
 
 
-def fp4_linear_kernel_name(m: int, n: int, k: int) -> str:
-    """Main-kernel instantiation the library launches for an [m, k] x [n, k]^T product."""
-    return load_library().fp4rl_fp4_linear_kernel_name(m, n, k).decode()
+def fp4_linear_kernel_name(m: int, n: int, k: int, r: int = 0) -> str:
+    """Main-kernel instantiation the library launches for an [m, k] x [n, k]^T product with rank r."""
+    return load_library().fp4rl_fp4_linear_kernel_name(m, n, k, r).decode()
 
 
 def aqn_sigma(sigma_start: float, sigma_end: float, k: int, num_stages: int) -> float:

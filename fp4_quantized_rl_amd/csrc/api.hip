@@ -260,9 +260,9 @@ fp4rl_status fp4rl_fp4_lora_linear(const uint16_t* x, int64_t m, int64_t n, int6
                   "fp4_linear");
 }
 
-const char* fp4rl_fp4_linear_kernel_name(int64_t m, int64_t n, int64_t k) {
-  if (check_linear_shape(m, n, k, 0) != FP4RL_OK || m == 0 || n == 0) return "";
-  return fp4rl::fp4_linear_kernel_name(m, n, k);
+const char* fp4rl_fp4_linear_kernel_name(int64_t m, int64_t n, int64_t k, int64_t r) {
+  if (check_linear_shape(m, n, k, r) != FP4RL_OK || m == 0 || n == 0) return "";
+  return fp4rl::fp4_linear_kernel_name(m, n, k, r);
 }
 
 // --------------------------------------------------------------------- AQN --

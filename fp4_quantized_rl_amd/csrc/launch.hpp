@@ -35,7 +35,7 @@ int lora_slices(int64_t k, int splits);
 hipError_t launch_lora_down(const uint16_t* x, int64_t m, int64_t k, const uint16_t* a, int64_t r, float lora_scale,
                             int splits, float* part, hipStream_t stream);
 hipError_t launch_lora_reduce(const float* part, int slices, int64_t count, float* t, hipStream_t stream);
-const char* fp4_linear_kernel_name(int64_t m, int64_t n, int64_t k);
+const char* fp4_linear_kernel_name(int64_t m, int64_t n, int64_t k, int64_t r);
 hipError_t launch_fp4_linear(const uint16_t* x, int64_t m, int64_t n, int64_t k,
                              const uint8_t* codes, const uint8_t* scales, const float* tensor_scale,
                              const float* t, int tks, const uint16_t* b, int64_t r, uint16_t* y,

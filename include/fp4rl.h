@@ -150,11 +150,13 @@ fp4rl_status fp4rl_fp4_linear_lora_up(const uint16_t* x, int64_t m, int64_t n, i
                                       const uint16_t* lora_b, int64_t r, uint16_t* y,
                                       fp4rl_stream stream);
 
-/* [host] Name of the main-kernel instantiation fp4rl_fp4_linear_lora_up
- * launches for this shape, as a demangler prints it (e.g.
- * "skinny_kernel<4, 4, 4>"), so profiles can be matched to calls. Returns a
- * static string; "" for invalid shapes. Touches no device. */
-const char* fp4rl_fp4_linear_kernel_name(int64_t m, int64_t n, int64_t k);
+/* [host] Name of the main-kernel instantiation the linear launches for this
+ * shape and rank, as a demangler prints its template arguments (e.g.
+ * "gemv_kernel<1, 8, 8>", "skinny_kernel<4, 2, 8>"), so profiles can be
+ * matched to calls. Returns a static string; "" for invalid shapes. Touches
+ * no device. Kernels by m: a VALU GEMV (one or two tokens), an MFMA skinny
+ * kernel (decode batches up to 128 per launch column). */
+const char* fp4rl_fp4_linear_kernel_name(int64_t m, int64_t n, int64_t k, int64_t r);
 
 /* ------------------------------------------------------------------------
  * AQN.
