@@ -63,6 +63,15 @@ def parse_args():
     p.add_argument("--cpu-seconds", type=float, default=15.0, help="target CPU time of the oracle sample")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--no-extras", action="store_true", help="skip prefill / quantiser / AQN extra timings")
+    p.add_argument("--copy-calibration-mib", type=int, default=0,
+                   help="first run a plain device-to-device copy of this many MiB three times (the reference "
+                        "kernel that scales rocprofv3 FETCH_SIZE / WRITE_SIZE to bytes)")
+    p.add_argument("--summarize-pmc", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
+                   help="no GPU work: turn two rocprofv3 --pmc runs (FETCH_SIZE, WRITE_SIZE) of this script into "
+                        "profiles/pmc_traffic.json")
+    p.add_argument("--summarize-trace", nargs=2, metavar=("TRACE_DIR", "OUT_MD"),
+                   help="no GPU work: summarise a rocprofv3 --kernel-trace --stats run of this script")
+    p.add_argument("--command", default="", help="command line recorded in a summary")
     return p.parse_args()
 
 
@@ -134,25 +143,174 @@ def build_layer(torch, fr, dev, shapes, seed):
     return layer, fp32
 
 
-def traffic_from_profile(kernel_name, launches):
-    """HBM bytes per launch measured by rocprofv3 PMC runs, if the committed summary is current."""
-    path = os.path.join(ROOT, "profiles", "pmc_traffic.json")
-    if not os.path.exists(path):
+PMC_TRAFFIC = os.path.join(ROOT, "profiles", "fp4_lora_linear_qwen25_7b_decode_pmc_traffic.json")
+KERNEL_SOURCES = ("linear.hip", "device.hpp", "launch.hpp")
+
+
+def kernel_source_sha():
+    """Hash of the linear kernel sources: counter readings are void once these change."""
+    h = hashlib.sha256()
+    for f in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, "fp4_quantized_rl_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def short_kernel_name(full):
+    """'void fp4rl::(anonymous namespace)::gemv_kernel<1, 8, 8>(...)' -> 'gemv_kernel<1, 8, 8>'."""
+    full = full.replace("(anonymous namespace)::", "")
+    depth, end = 0, len(full)
+    for i, ch in enumerate(full):
+        if ch == "<":
+            depth += 1
+        elif ch == ">":
+            depth -= 1
+        elif ch == "(" and depth == 0:
+            end = i
+            break
+    s = full[:end]
+    if s.startswith("void "):
+        s = s[5:]
+    return s.rsplit("::", 1)[-1].strip()
+
+
+def same_kernel(short, name):
+    """A library kernel name may omit trailing defaulted template arguments."""
+    return short == name or (name.endswith(">") and short.startswith(name[:-1] + ","))
+
+
+def traffic_from_profile(kernel_name):
+    """HBM bytes per launch from the committed rocprofv3 PMC summary, if it is current."""
+    if not os.path.exists(PMC_TRAFFIC):
         return None
-    with open(path) as fh:
+    with open(PMC_TRAFFIC) as fh:
         rec = json.load(fh)
-    src = os.path.join(ROOT, "fp4_quantized_rl_amd", "csrc", "linear.hip")
-    sha = hashlib.sha256(open(src, "rb").read()).hexdigest()[:16]
-    if rec.get("linear_hip_sha") != sha:
+    if rec.get("kernel_source_sha") != kernel_source_sha():
         return None
     ent = rec.get("kernels", {}).get(kernel_name)
-    if not ent:
-        return None
-    return ent.get("bytes_per_launch")
+    return None if not ent else ent.get("hbm_bytes_per_launch")
+
+
+def _read_counters(d, counter):
+    """Per-dispatch values of one counter from a rocprofv3 --pmc csv run: [(kernel, value)]."""
+    import csv
+    import glob
+    out = []
+    for f in sorted(glob.glob(os.path.join(d, "**", "*counter_collection.csv"), recursive=True)):
+        with open(f, newline="") as fh:
+            for r in csv.DictReader(fh):
+                if r["Counter_Name"] == counter:
+                    out.append((r["Kernel_Name"], float(r["Counter_Value"])))
+    if not out:
+        raise SystemExit(f"no {counter} rows under {d}")
+    return out
+
+
+def summarize_pmc(fetch_dir, write_dir, copy_mib, command):
+    """FETCH_SIZE / WRITE_SIZE (KiB per dispatch) of every library kernel, scaled by a plain copy's reading."""
+    import fp4_quantized_rl_amd as fr
+    fetch, write = _read_counters(fetch_dir, "FETCH_SIZE"), _read_counters(write_dir, "WRITE_SIZE")
+    known = copy_mib * 2**20
+    if known <= 0:
+        raise SystemExit("--copy-calibration-mib must give the calibration copy size")
+
+    def copy_kib(rows):
+        vals = [v for k, v in rows if "copyBuffer" in k and v * 1024 > 0.5 * known]
+        if not vals:
+            raise SystemExit("calibration copy dispatches not found")
+        return sum(vals) / len(vals)
+
+    cf, cw = copy_kib(fetch), copy_kib(write)
+    ff, wf = cf * 1024 / known, cw * 1024 / known
+    from workloads import QWEN25_7B
+    names = sorted({fr.fp4_linear_kernel_name(m, n, k, RANK) for m in TOKENS for n, k in QWEN25_7B.values()})
+    kernels = {}
+    for name in names:
+        fv = [v for k, v in fetch if same_kernel(short_kernel_name(k), name)]
+        wv = [v for k, v in write if same_kernel(short_kernel_name(k), name)]
+        if not fv or not wv:
+            continue
+        fa, wa = sum(fv) / len(fv), sum(wv) / len(wv)
+        kernels[name] = {"dispatches": len(fv), "fetch_kib_avg": round(fa, 1), "write_kib_avg": round(wa, 1),
+                         "hbm_bytes_per_launch": int(fa * 1024 / ff + wa * 1024 / wf)}
+    rec = {"what": "rocprofv3 --pmc FETCH_SIZE and WRITE_SIZE runs of bench.py, per dispatch of each main linear "
+                   "kernel, averaged over that kernel's dispatches and divided by the factor a plain device copy "
+                   "of known size reads (counter KiB x 1024 / true bytes)",
+           "command": command, "kernel_source_sha": kernel_source_sha(),
+           "copy_calibration": {"bytes": known, "fetch_kib": round(cf, 1), "write_kib": round(cw, 1),
+                                "fetch_factor": round(ff, 4), "write_factor": round(wf, 4)},
+           "kernels": kernels}
+    with open(PMC_TRAFFIC, "w") as fh:
+        json.dump(rec, fh, indent=1)
+        fh.write("\n")
+    print(json.dumps(rec, indent=1))
+
+
+def summarize_trace(trace_dir, out_md, command):
+    """Markdown table from a rocprofv3 --kernel-trace --stats run: library kernels and their durations."""
+    import csv
+    import glob
+    stats = sorted(glob.glob(os.path.join(trace_dir, "**", "*kernel_stats.csv"), recursive=True))
+    if not stats:
+        raise SystemExit(f"no kernel_stats.csv under {trace_dir}")
+    rows = []
+    with open(stats[0], newline="") as fh:
+        for r in csv.DictReader(fh):
+            rows.append((short_kernel_name(r["Name"]), int(r["Calls"]), float(r["TotalDurationNs"]),
+                         float(r["AverageNs"]), float(r["MinNs"]), float(r["MaxNs"]), float(r["Percentage"])))
+    rows.sort(key=lambda t: -t[2])
+    # dispatches that ran back to back with the same kernel and grid: the
+    # per-kernel timing graphs, which the events in the JSON line bracket
+    b2b = {}
+    traces = sorted(glob.glob(os.path.join(trace_dir, "**", "*kernel_trace.csv"), recursive=True))
+    if traces:
+        with open(traces[0], newline="") as fh:
+            tr = sorted(csv.DictReader(fh), key=lambda r: int(r["Start_Timestamp"]))
+        key = [(r["Kernel_Name"], r["Grid_Size_X"], r["Grid_Size_Y"], r["Grid_Size_Z"]) for r in tr]
+        for i, r in enumerate(tr):
+            if (i > 0 and key[i - 1] == key[i]) or (i + 1 < len(tr) and key[i + 1] == key[i]):
+                lst = b2b.setdefault(short_kernel_name(r["Kernel_Name"]), [])
+                lst.append(int(r["End_Timestamp"]) - int(r["Start_Timestamp"]))
+    lines = ["# rocprofv3 kernel trace: " + os.path.basename(out_md).rsplit(".", 1)[0], "",
+             "Command (from the repository root):", "", "```", command, "```", "",
+             "'back to back' averages only the dispatches that ran next to a dispatch of the same kernel "
+             "and grid: the per-kernel timing graphs whose HIP-event average the JSON line reports.", "",
+             "| kernel | calls | total ms | avg us | min us | max us | % of GPU time | back-to-back calls | "
+             "back-to-back avg us |",
+             "|---|---:|---:|---:|---:|---:|---:|---:|---:|"]
+    for name, calls, tot, avg, mn, mx, pct in rows[:25]:
+        bb = b2b.get(name, [])
+        bbs = f"{len(bb)} | {sum(bb) / len(bb) / 1e3:.2f}" if bb else "0 | -"
+        lines.append(f"| `{name}` | {calls} | {tot / 1e6:.3f} | {avg / 1e3:.2f} | {mn / 1e3:.2f} | {mx / 1e3:.2f} "
+                     f"| {pct:.2f} | {bbs} |")
+    with open(out_md, "w") as fh:
+        fh.write("\n".join(lines) + "\n")
+    print("\n".join(lines))
+
+
+def progress(msg):
+    print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+
+def copy_calibration(torch, dev, mib):
+    """A plain device-to-device copy of known size, the yardstick for the traffic counters."""
+    n = mib * 2**20 // 4
+    src = torch.ones(n, dtype=torch.float32, device=dev)
+    dst = torch.empty_like(src)
+    for _ in range(3):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    del src, dst
 
 
 def main():
     args = parse_args()
+    if args.summarize_pmc:
+        summarize_pmc(*args.summarize_pmc, args.copy_calibration_mib, args.command)
+        return
+    if args.summarize_trace:
+        summarize_trace(*args.summarize_trace, args.command)
+        return
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
         print("bench.py measures one GPU only: this build has no multi-GPU path "
@@ -161,6 +319,7 @@ def main():
 
     cpu = None
     if not args.no_cpu_baseline:
+        progress("cpu oracle baseline")
         cpu = cpu_baseline(args.cpu_seconds)
 
     import torch
@@ -171,10 +330,13 @@ def main():
     fr.load_library()
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
+    if args.copy_calibration_mib > 0:
+        copy_calibration(torch, dev, args.copy_calibration_mib)
     shapes = QWEN25_7B
     hidden = 3584
     inter = 18944
 
+    progress("building weights")
     # weights: COPIES distinct NVFP4 layers, shared LoRA adapters, AQN weights
     layers = []
     fp32_first = None
@@ -233,6 +395,7 @@ def main():
                 fr.fp4_lora_linear(layer_input(B, name), L[name], a, b, LORA_SCALE, out=B["y"][name],
                                    workspace=B["ws"][name])
 
+    progress("warmup")
     for s in range(args.warmup):
         step(s)
     torch.cuda.synchronize()
@@ -248,6 +411,7 @@ def main():
         graphs[s % COPIES].replay()
     torch.cuda.synchronize()
 
+    progress("timed steps")
     t0 = time.perf_counter()
     for s in range(args.steps):
         graphs[s % COPIES].replay()
@@ -267,7 +431,8 @@ def main():
             src = lst[len(lst) % COPIES]
             lst.append(src.clone())
         clones[name] = lst
-    timing = {}
+    progress("per-kernel timing")
+    timing, timed_launches = {}, {}
     reps = 3
     for m in TOKENS:
         B = bufs[m]
@@ -287,24 +452,32 @@ def main():
             e1.record()
             torch.cuda.synchronize()
             launches = reps * len(clones[name])
-            timing[(m, name)] = e0.elapsed_time(e1) * 1e-3 / launches
+            total = e0.elapsed_time(e1) * 1e-3
+            timing[(m, name)] = total / launches
+            timed_launches[(m, name)] = (launches, total)
             del gr
     kname = {(m, name): fr.fp4_linear_kernel_name(m, n, k, RANK) for m in TOKENS for name, (n, k) in shapes.items()}
+    # share of the step: one launch per (M, linear); launch-weighted averages
+    # over the timed graphs (the way a kernel trace averages its dispatches)
     per_kernel = {}
     for (m, name), dt in timing.items():
         n, k = shapes[name]
-        d = per_kernel.setdefault(kname[(m, name)], {"time": 0.0, "launches": 0, "bytes": 0})
-        d["time"] += dt
-        d["launches"] += 1
-        d["bytes"] += main_kernel_bytes(m, n, k, RANK)
-    dom = max(per_kernel, key=lambda kn: per_kernel[kn]["time"])
+        launches, total = timed_launches[(m, name)]
+        d = per_kernel.setdefault(kname[(m, name)], {"step_time": 0.0, "per_step": 0, "time": 0.0, "launches": 0,
+                                                     "bytes": 0})
+        d["step_time"] += dt
+        d["per_step"] += 1
+        d["time"] += total
+        d["launches"] += launches
+        d["bytes"] += launches * main_kernel_bytes(m, n, k, RANK)
+    dom = max(per_kernel, key=lambda kn: per_kernel[kn]["step_time"])
     dk = per_kernel[dom]
     achieved = dk["bytes"] / dk["time"] / 1e9
-    traffic = traffic_from_profile(dom, dk["launches"])
+    traffic = traffic_from_profile(dom)
     roofline = {"bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                 "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic,
                 "kernel": dom, "avg_launch_us": round(dk["time"] / dk["launches"] * 1e6, 3),
-                "launches_per_step": dk["launches"],
+                "timed_launches": dk["launches"], "launches_per_step": dk["per_step"],
                 "algorithmic_bytes_per_launch": int(dk["bytes"] / dk["launches"])}
 
     step_roof_s = max(total_bytes_step / (HBM_PEAK_GBS * 1e9), flops_step / (BF16_PEAK_TFLOPS * 1e12))
@@ -314,13 +487,14 @@ def main():
         "main_kernel_weight_gbs": {f"M{m}/{name}": round(nvfp4_bytes(*shapes[name]) / timing[(m, name)] / 1e9, 1)
                                    for m in TOKENS for name in shapes},
         "main_kernels_share_of_step": round(sum(timing.values()) / (ms_per_step * 1e-3), 4),
-        "kernels": {kn: {"avg_us": round(v["time"] / v["launches"] * 1e6, 3), "launches_per_step": v["launches"],
+        "kernels": {kn: {"avg_us": round(v["time"] / v["launches"] * 1e6, 3), "launches_per_step": v["per_step"],
                          "GB/s": round(v["bytes"] / v["time"] / 1e9, 1)} for kn, v in sorted(per_kernel.items())},
     }
     del clones
 
     extras = {}
     if not args.no_extras:
+        progress("prefill, quantiser and AQN timings")
         extras = run_extras(torch, fr, dev, shapes, layers[0], lora, fp32_first)
 
     out = {
