@@ -367,8 +367,10 @@ def main():
         bufs[m] = {
             "xh": xh, "xo": xo, "xr": xr, "xd": xd,
             "h1": torch.empty_like(xh), "h2": torch.empty_like(xr),
-            "ws": {name: torch.empty(max(16, fr.load_library().fp4rl_fp4_lora_linear_workspace(m, n, k, RANK)),
-                                     dtype=torch.uint8, device=dev) for name, (n, k) in shapes.items()},
+            "ws": {name: fr.linear_workspace(fr.fp4_lora_linear_workspace_bytes(m, n, k, RANK), dev)
+                   for name, (n, k) in shapes.items()},
+            "ws_up": {name: fr.linear_workspace(fr.fp4_linear_lora_up_workspace_bytes(m, n, k), dev)
+                      for name, (n, k) in shapes.items()},
             "t": {name: torch.empty((m, RANK), dtype=torch.float32, device=dev) for name in shapes},
             "y": {name: torch.empty((m, n), dtype=torch.bfloat16, device=dev) for name, (n, k) in shapes.items()},
         }
@@ -443,7 +445,7 @@ def main():
             gr = torch.cuda.CUDAGraph()
             with torch.cuda.graph(gr):
                 for w in clones[name]:
-                    fr.fp4_linear_lora_up(x, w, t, b, out=B["y"][name])
+                    fr.fp4_linear_lora_up(x, w, t, b, out=B["y"][name], workspace=B["ws_up"][name])
             gr.replay()
             e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
             e0.record()

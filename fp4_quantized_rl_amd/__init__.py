@@ -25,7 +25,8 @@ from dataclasses import dataclass
 __all__ = [
     "LIB_PATH", "Fp4rlError", "load_library", "NVFP4Weight", "nvfp4_empty", "nvfp4_quantize", "nvfp4_to_tiled",
     "fp4_lora_linear",
-    "lora_down", "fp4_linear_lora_up", "fp4_linear_kernel_name", "aqn_sigma", "aqn_rmsnorm", "philox_words",
+    "lora_down", "fp4_linear_lora_up", "fp4_linear_kernel_name", "linear_workspace",
+    "fp4_lora_linear_workspace_bytes", "fp4_linear_lora_up_workspace_bytes", "aqn_sigma", "aqn_rmsnorm", "philox_words",
     "EXPORTED_SYMBOLS",
 ]
 
@@ -54,7 +55,9 @@ _SIGNATURES = {
                                         _c.c_size_t, _P]),
     "fp4rl_lora_down_workspace": (_c.c_size_t, [_I64, _I64, _I64]),
     "fp4rl_lora_down": (_STATUS, [_P, _I64, _I64, _P, _I64, _c.c_float, _P, _P, _c.c_size_t, _P]),
-    "fp4rl_fp4_linear_lora_up": (_STATUS, [_P, _I64, _I64, _I64, _P, _P, _P, _P, _P, _I64, _P, _P]),
+    "fp4rl_fp4_linear_lora_up_workspace": (_c.c_size_t, [_I64, _I64, _I64]),
+    "fp4rl_fp4_linear_lora_up": (_STATUS, [_P, _I64, _I64, _I64, _P, _P, _P, _P, _P, _I64, _P, _P, _c.c_size_t,
+                                           _P]),
     "fp4rl_fp4_linear_kernel_name": (_c.c_char_p, [_I64, _I64, _I64, _I64]),
     "fp4rl_aqn_sigma": (_c.c_float, [_c.c_float, _c.c_float, _c.c_int32, _c.c_int32]),
     "fp4rl_aqn_rmsnorm": (_STATUS, [_P, _I64, _I64, _P, _c.c_float, _c.c_uint64, _c.c_uint64, _c.c_uint32,
@@ -231,7 +234,7 @@ def fp4_lora_linear(x, wq: NVFP4Weight, lora_a=None, lora_b=None, lora_scale: fl
     lib = load_library()
     ws_bytes = lib.fp4rl_fp4_lora_linear_workspace(m, n, k, r)
     if workspace is None and ws_bytes:
-        workspace = torch.empty(ws_bytes, dtype=torch.uint8, device=x.device)
+        workspace = linear_workspace(ws_bytes, x.device)
     with torch.cuda.device(x.device):
         _check(lib.fp4rl_fp4_lora_linear(_ptr(x), m, n, k, _ptr(wq.codes), _ptr(wq.scales),
                                          _ptr(wq.tensor_scale), _ptr(lora_a), _ptr(lora_b), r,
@@ -263,7 +266,21 @@ def lora_down(x, lora_a, lora_scale: float, out=None, workspace=None):
     return out
 
 
-def fp4_linear_lora_up(x, wq: NVFP4Weight, t=None, lora_b=None, out=None):
+def linear_workspace(nbytes: int, device="cuda"):
+    """A zero-filled workspace for fp4_lora_linear / fp4_linear_lora_up (its counter words start at zero;
+    the library returns them to zero after every call, so the buffer can be reused)."""
+    return _torch().zeros(max(int(nbytes), 16), dtype=_torch().uint8, device=device)
+
+
+def fp4_lora_linear_workspace_bytes(m: int, n: int, k: int, r: int) -> int:
+    return load_library().fp4rl_fp4_lora_linear_workspace(m, n, k, r)
+
+
+def fp4_linear_lora_up_workspace_bytes(m: int, n: int, k: int) -> int:
+    return load_library().fp4rl_fp4_linear_lora_up_workspace(m, n, k)
+
+
+def fp4_linear_lora_up(x, wq: NVFP4Weight, t=None, lora_b=None, out=None, workspace=None):
     """y = bf16(s_t x deq^T + t B^T) with t fp32 [m, r] from lora_down (or None)."""
     torch = _torch()
     m, n, k = _linear_args(x, wq)
@@ -276,10 +293,15 @@ def fp4_linear_lora_up(x, wq: NVFP4Weight, t=None, lora_b=None, out=None):
             raise ValueError("t must be [m, r] and lora_b [n, r]")
     if out is None:
         out = torch.empty((m, n), dtype=torch.bfloat16, device=x.device)
+    lib = load_library()
+    ws_bytes = lib.fp4rl_fp4_linear_lora_up_workspace(m, n, k)
+    if workspace is None and ws_bytes:
+        workspace = linear_workspace(ws_bytes, x.device)
     with torch.cuda.device(x.device):
-        _check(load_library().fp4rl_fp4_linear_lora_up(_ptr(x), m, n, k, _ptr(wq.codes), _ptr(wq.scales),
-                                                       _ptr(wq.tensor_scale), _ptr(t), _ptr(lora_b), r,
-                                                       _ptr(out), _stream(x.device)),
+        _check(lib.fp4rl_fp4_linear_lora_up(_ptr(x), m, n, k, _ptr(wq.codes), _ptr(wq.scales),
+                                            _ptr(wq.tensor_scale), _ptr(t), _ptr(lora_b), r, _ptr(out),
+                                            _ptr(workspace), 0 if workspace is None else workspace.numel(),
+                                            _stream(x.device)),
                "fp4_linear_lora_up")
     return out
 

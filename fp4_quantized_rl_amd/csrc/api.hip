@@ -159,11 +159,29 @@ fp4rl_status fp4rl_nvfp4_to_tiled(const uint8_t* codes, const uint8_t* scales, i
 
 // ------------------------------------------------------------------ linear --
 
-size_t fp4rl_fp4_lora_linear_workspace(int64_t m, int64_t n, int64_t k, int64_t r) {
-  (void)n;
+// Linear workspaces: [counters, kLinearCounterBytes][t K-slices, fp32][main kernel K-split partials, fp32]
+// (the last two only as needed; nothing at all when neither is needed).
+static size_t lora_part_bytes(int64_t m, int64_t k, int64_t r) {
   if (m <= 0 || r <= 0 || k <= 0) return 0;
   const int slices = fp4rl::lora_slices(k, fp4rl::lora_splits(m, k, r));
   return round_up((size_t)slices * (size_t)m * (size_t)r * sizeof(float), 256);
+}
+
+static size_t main_part_bytes(int64_t m, int64_t n, int64_t k) {
+  if (m <= 0 || n <= 0 || k <= 0) return 0;
+  return fp4rl::linear_partial_bytes(m, n, k);
+}
+
+static size_t linear_ws_bytes(size_t tbytes, size_t pbytes) {
+  return tbytes + pbytes > 0 ? fp4rl::kLinearCounterBytes + tbytes + pbytes : 0;
+}
+
+size_t fp4rl_fp4_lora_linear_workspace(int64_t m, int64_t n, int64_t k, int64_t r) {
+  return linear_ws_bytes(lora_part_bytes(m, k, r), main_part_bytes(m, n, k));
+}
+
+size_t fp4rl_fp4_linear_lora_up_workspace(int64_t m, int64_t n, int64_t k) {
+  return linear_ws_bytes(0, main_part_bytes(m, n, k));
 }
 
 size_t fp4rl_lora_down_workspace(int64_t m, int64_t k, int64_t r) {
@@ -215,15 +233,28 @@ static fp4rl_status check_linear_main(const uint16_t* x, int64_t m, int64_t n, i
   return FP4RL_OK;
 }
 
+static fp4rl_status check_main_ws(void* ws, size_t ws_bytes, size_t need) {
+  if (need == 0) return FP4RL_OK;
+  FP4RL_REQUIRE(ws != nullptr && ws_bytes >= need, FP4RL_ERR_WORKSPACE, "workspace %zu < %zu bytes", ws_bytes, need);
+  FP4RL_REQUIRE(aligned(ws, 16), FP4RL_ERR_ALIGN, "workspace must be 16-byte aligned");
+  return FP4RL_OK;
+}
+
 fp4rl_status fp4rl_fp4_linear_lora_up(const uint16_t* x, int64_t m, int64_t n, int64_t k, const uint8_t* codes,
                                       const uint8_t* scales, const float* tensor_scale, const float* t,
-                                      const uint16_t* lora_b, int64_t r, uint16_t* y, fp4rl_stream stream) {
+                                      const uint16_t* lora_b, int64_t r, uint16_t* y, void* workspace,
+                                      size_t workspace_bytes, fp4rl_stream stream) {
   FP4RL_CHECK(check_linear_shape(m, n, k, r));
   if (m == 0 || n == 0) return ok();
   FP4RL_CHECK(check_linear_main(x, m, n, k, codes, scales, tensor_scale, t, lora_b, r, y));
+  const size_t pbytes = main_part_bytes(m, n, k);
+  FP4RL_CHECK(check_main_ws(workspace, workspace_bytes, linear_ws_bytes(0, pbytes)));
   FP4RL_CHECK(check_device());
+  uint8_t* ws = static_cast<uint8_t*>(workspace);
+  float* part = pbytes ? reinterpret_cast<float*>(ws + fp4rl::kLinearCounterBytes) : nullptr;
+  uint32_t* counters = pbytes ? reinterpret_cast<uint32_t*>(ws) : nullptr;
   return launched(fp4rl::launch_fp4_linear(x, m, n, k, codes, scales, tensor_scale, r > 0 ? t : nullptr, 1,
-                                           r > 0 ? lora_b : nullptr, r, y, stream),
+                                           r > 0 ? lora_b : nullptr, r, y, part, counters, stream),
                   "fp4_linear");
 }
 
@@ -237,14 +268,13 @@ fp4rl_status fp4rl_fp4_lora_linear(const uint16_t* x, int64_t m, int64_t n, int6
                 "lora_a and lora_b must both be NULL or both be set");
   if (lora_a == nullptr) r = 0;
   if (m == 0 || n == 0) return ok();
-  float* t = static_cast<float*>(workspace);
-  if (r > 0) {
-    const size_t need = fp4rl_fp4_lora_linear_workspace(m, n, k, r);
-    FP4RL_REQUIRE(workspace != nullptr && workspace_bytes >= need, FP4RL_ERR_WORKSPACE,
-                  "workspace %zu < %zu bytes", workspace_bytes, need);
-    FP4RL_REQUIRE(aligned(lora_a, 16) && aligned(workspace, 16), FP4RL_ERR_ALIGN,
-                  "lora_a and workspace must be 16-byte aligned");
-  }
+  const size_t tbytes = lora_part_bytes(m, k, r), pbytes = main_part_bytes(m, n, k);
+  FP4RL_CHECK(check_main_ws(workspace, workspace_bytes, linear_ws_bytes(tbytes, pbytes)));
+  if (r > 0) FP4RL_REQUIRE(aligned(lora_a, 16), FP4RL_ERR_ALIGN, "lora_a must be 16-byte aligned");
+  uint8_t* ws = static_cast<uint8_t*>(workspace);
+  float* t = tbytes ? reinterpret_cast<float*>(ws + fp4rl::kLinearCounterBytes) : nullptr;
+  float* part = pbytes ? reinterpret_cast<float*>(ws + fp4rl::kLinearCounterBytes + tbytes) : nullptr;
+  uint32_t* counters = pbytes ? reinterpret_cast<uint32_t*>(ws) : nullptr;
   FP4RL_CHECK(check_linear_main(x, m, n, k, codes, scales, tensor_scale, t, lora_b, r, y));
   FP4RL_CHECK(check_device());
   int slices = 1;
@@ -256,7 +286,7 @@ fp4rl_status fp4rl_fp4_lora_linear(const uint16_t* x, int64_t m, int64_t n, int6
   }
   // the main kernel's epilogue sums the K-slices of t in slice order
   return launched(fp4rl::launch_fp4_linear(x, m, n, k, codes, scales, tensor_scale, r > 0 ? t : nullptr, slices,
-                                           r > 0 ? lora_b : nullptr, r, y, stream),
+                                           r > 0 ? lora_b : nullptr, r, y, part, counters, stream),
                   "fp4_linear");
 }
 

@@ -36,9 +36,18 @@ hipError_t launch_lora_down(const uint16_t* x, int64_t m, int64_t k, const uint1
                             int splits, float* part, hipStream_t stream);
 hipError_t launch_lora_reduce(const float* part, int slices, int64_t count, float* t, hipStream_t stream);
 const char* fp4_linear_kernel_name(int64_t m, int64_t n, int64_t k, int64_t r);
+// Linear workspaces begin with kLinearCounters counter words (one per output
+// tile of a K-split launch; K is split only when there are fewer tiles). They
+// must be zero before the first call, and every launch leaves them at zero.
+// Its other regions (t slices, K-split partials) follow and never overlap
+// the counters, whatever shapes share the workspace.
+constexpr int kLinearCounters = 256;
+constexpr size_t kLinearCounterBytes = kLinearCounters * sizeof(uint32_t);
+// fp32 K-split partial sums of the main kernel (0 when K is not split)
+size_t linear_partial_bytes(int64_t m, int64_t n, int64_t k);
 hipError_t launch_fp4_linear(const uint16_t* x, int64_t m, int64_t n, int64_t k,
                              const uint8_t* codes, const uint8_t* scales, const float* tensor_scale,
-                             const float* t, int tks, const uint16_t* b, int64_t r, uint16_t* y,
-                             hipStream_t stream);
+                             const float* t, int tks, const uint16_t* b, int64_t r, uint16_t* y, float* part,
+                             uint32_t* counters, hipStream_t stream);
 
 }  // namespace fp4rl

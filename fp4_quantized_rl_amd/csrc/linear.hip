@@ -12,7 +12,7 @@
 // (nibble + 1/16 scale byte). The weights come in the tiled NVFP4 layout
 // (16-row x 128-k tiles, 1 KB of codes + 128 B of scales, stored in the order
 // the MFMA lanes consume them), so every wave load is one contiguous 1 KB
-// (one lane = 32 consecutive k of one row = two blocks). It dequantises in
+// (one lane = 32 k of one row, four groups of 8). It dequantises in
 // registers (hardware E2M1 convert at unit scale, times the E4M3 block
 // scale: exact in bf16) and feeds v_mfma_f32_16x16x32_bf16 with the weights
 // as the 16-row A operand and up to 8 tiles of 16 tokens as B operands. The
@@ -21,8 +21,10 @@
 // epilogue as extra MFMA steps, with t split into bf16 hi + lo parts.
 //
 // Within one MFMA the order of the 32 k values is free as long as A and B
-// use the same one, so a lane's 16-byte code load (k = 32g .. 32g+31 of a
-// 128-wide chunk, g = lane/16) supplies its slot in four consecutive MFMAs.
+// use the same one. Step j (0..3) of a 128-wide chunk takes k = 32 j .. 32 j
+// + 31: lane group g = lane/16 supplies k = 32 j + 8 g .. + 7, which is word j
+// of the lane's 16-byte code load. On the activation side the four lane
+// groups of one token then read 64 consecutive bytes per load instruction.
 #include <algorithm>
 
 #include "device.hpp"
@@ -32,6 +34,14 @@ namespace fp4rl {
 namespace {
 
 __device__ __forceinline__ uint4 ld16(const void* p) { return *reinterpret_cast<const uint4*>(p); }
+
+// The four E4M3 scale bytes of a tiled scale word, decoded exactly (OCP e4m3fn).
+__device__ __forceinline__ void scale4(uint32_t w, float (&sc)[4]) {
+  sc[0] = __builtin_amdgcn_cvt_f32_fp8((int)w, 0);
+  sc[1] = __builtin_amdgcn_cvt_f32_fp8((int)w, 1);
+  sc[2] = __builtin_amdgcn_cvt_f32_fp8((int)w, 2);
+  sc[3] = __builtin_amdgcn_cvt_f32_fp8((int)w, 3);
+}
 
 // ---------------------------------------------------------------------------
 // LoRA down-projection, split along K into `gridDim.z` slices of `kslice`:
@@ -96,6 +106,74 @@ __global__ void lora_reduce_kernel(const float* __restrict__ part, int slices, i
 }
 
 // ---------------------------------------------------------------------------
+// Epilogue of one 16x16 output tile held in MFMA D layout (lane = 16 g + i
+// holds features nb + 4 g + v, v = 0..3, of token mb + i):
+//   y = bf16(s_t * v + t B^T), t summed over its `tks` K-slices in slice order.
+// The LoRA product runs as MFMA steps over r in 32-wide pieces: B rows of the
+// tile are the A operand, t rows the B operand, t split into bf16 hi + lo.
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ void store_tile(f32x4 v, int nb, int mb, int lane, int M, int N, float st,
+                                           const float* __restrict__ t, int tks, const uint16_t* __restrict__ lb,
+                                           int r, uint16_t* __restrict__ y) {
+  const int li = lane & 15, lg = lane >> 4;
+  f32x4 lo = {0.f, 0.f, 0.f, 0.f};
+  if (r > 0) {
+    const bool rvec = (r & 7) == 0;
+    const int64_t tstride = (int64_t)M * r;
+    const int na = nb + li;  // B row for the A operand
+    const int ma = mb + li;  // t row for the B operand
+    for (int j0 = 0; j0 < r; j0 += 32) {
+      const int jj = j0 + 8 * lg;
+      uint4 bw = make_uint4(0, 0, 0, 0);
+      float tv[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+      if (jj < r) {
+        if (rvec) {
+          if (na < N) bw = ld16(lb + (int64_t)na * r + jj);
+          if (ma < M) {
+            for (int q = 0; q < tks; ++q) {  // K-slices of t, summed in order
+              const float* tp = t + (int64_t)q * tstride + (int64_t)ma * r + jj;
+              const float4 t0 = *reinterpret_cast<const float4*>(tp);
+              const float4 t1 = *reinterpret_cast<const float4*>(tp + 4);
+              tv[0] += t0.x; tv[1] += t0.y; tv[2] += t0.z; tv[3] += t0.w;
+              tv[4] += t1.x; tv[5] += t1.y; tv[6] += t1.z; tv[7] += t1.w;
+            }
+          }
+        } else {
+          uint32_t h[8];
+#pragma unroll
+          for (int e = 0; e < 8; ++e) {
+            const bool ok = jj + e < r;
+            h[e] = (ok && na < N) ? lb[(int64_t)na * r + jj + e] : 0u;
+            if (ok && ma < M)
+              for (int q = 0; q < tks; ++q) tv[e] += t[(int64_t)q * tstride + (int64_t)ma * r + jj + e];
+          }
+          bw = make_uint4(h[0] | (h[1] << 16), h[2] | (h[3] << 16), h[4] | (h[5] << 16), h[6] | (h[7] << 16));
+        }
+      }
+      uint4 th, tl;
+      split_bf16x8(tv, th, tl);
+      lo = mfma16x16x32(as_bf16x8(bw), as_bf16x8(th), lo);
+      lo = mfma16x16x32(as_bf16x8(bw), as_bf16x8(tl), lo);
+    }
+  }
+  const int m = mb + li;
+  const int nf = nb + 4 * lg;
+  if (m < M) {
+    uint32_t o[4];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) o[e] = f32_to_bf16(st * v[e] + lo[e]);
+    uint16_t* yp = y + (int64_t)m * N + nf;
+    if ((N & 3) == 0 && nf + 3 < N) {
+      *reinterpret_cast<uint2*>(yp) = make_uint2(o[0] | (o[1] << 16), o[2] | (o[3] << 16));
+    } else {
+#pragma unroll
+      for (int e = 0; e < 4; ++e)
+        if (nf + e < N) yp[e] = (uint16_t)o[e];
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
 // Skinny (decode) kernel.
 //   grid.x: row groups of 16*NT output features; grid.y: token groups of 16*MT.
 //   WAVES waves per workgroup split the 128-wide K chunks round-robin.
@@ -118,14 +196,15 @@ __global__ __launch_bounds__(WAVES * kWave) void skinny_kernel(
   const int n0 = blockIdx.x * (16 * NT);
   const int m0 = blockIdx.y * (16 * MT);
   // Tiled weights: tile (rt, c) = 16 rows x 128 k; this lane's 16 code bytes
-  // sit at 16 * lane and its 2 scale bytes at 2 * lane of the tile. Bases are
-  // wave-uniform (scalar registers); lanes add 32-bit offsets. Row tiles past
-  // the matrix are clamped to the last one (their rows are never stored).
+  // sit at 16 * lane of the tile and its scale word (byte j = the block of
+  // step j) at 4 * (16 (g / 2) + i). Bases are wave-uniform (scalar
+  // registers); lanes add 32-bit offsets. Row tiles past the matrix are
+  // clamped to the last one (their rows are never stored).
   const int RT = (N + 15) >> 4, KC = (K + 127) >> 7;
   const int rt0 = blockIdx.x * NT;
   const uint8_t* cbase = codes + (int64_t)rt0 * KC * 1024;  // uniform
   const uint8_t* sbase = scales + (int64_t)rt0 * KC * 128;  // uniform
-  const uint32_t clane = 16 * lane, slane = 2 * lane;
+  const uint32_t clane = 16 * lane, slane = 4 * (16 * (lg >> 1) + li);
   int toff[NT];  // tile offset of row tile i, in tiles (uniform)
 #pragma unroll
   for (int i = 0; i < NT; ++i) toff[i] = (min(rt0 + i, RT - 1) - rt0) * KC;
@@ -133,7 +212,7 @@ __global__ __launch_bounds__(WAVES * kWave) void skinny_kernel(
   const uint16_t* xbase = x + (int64_t)m0 * K;  // uniform
   uint32_t xoff[MT];
 #pragma unroll
-  for (int j = 0; j < MT; ++j) xoff[j] = (uint32_t)(min(m0 + 16 * j + li, M - 1) - m0) * (uint32_t)K + 32 * lg;
+  for (int j = 0; j < MT; ++j) xoff[j] = (uint32_t)(min(m0 + 16 * j + li, M - 1) - m0) * (uint32_t)K + 8 * lg;
   const bool kfull = (K & 127) == 0;  // every chunk holds 128 valid k
 
   f32x4 acc[NT][MT];
@@ -168,7 +247,7 @@ __global__ __launch_bounds__(WAVES * kWave) void skinny_kernel(
         const uint4 v = ld_nt16(ct + clane);
         G.cw[u][i][0] = v.x; G.cw[u][i][1] = v.y; G.cw[u][i][2] = v.z; G.cw[u][i][3] = v.w;
         const uint8_t* st = sbase + (int64_t)(toff[i] + c) * 128;
-        G.sw[u][i] = __builtin_nontemporal_load(reinterpret_cast<const uint16_t*>(st + slane));
+        G.sw[u][i] = __builtin_nontemporal_load(reinterpret_cast<const uint32_t*>(st + slane));
       }
       if constexpr (XPRE) {
         const uint16_t* xc = xbase + 128 * c;  // uniform
@@ -176,14 +255,14 @@ __global__ __launch_bounds__(WAVES * kWave) void skinny_kernel(
 #pragma unroll
           for (int s = 0; s < 4; ++s)
 #pragma unroll
-            for (int j = 0; j < MT; ++j) G.xq[u][s][j] = ld16(xc + xoff[j] + 8 * s);
+            for (int j = 0; j < MT; ++j) G.xq[u][s][j] = ld16(xc + xoff[j] + 32 * s);
         } else {  // last, partial chunk: k past K is not read
-          const int kv = K - 128 * c - 32 * lg;
+          const int kv = K - 128 * c - 8 * lg;
 #pragma unroll
           for (int s = 0; s < 4; ++s)
 #pragma unroll
             for (int j = 0; j < MT; ++j)
-              G.xq[u][s][j] = 8 * s < kv ? ld16(xc + xoff[j] + 8 * s) : make_uint4(0, 0, 0, 0);
+              G.xq[u][s][j] = 32 * s < kv ? ld16(xc + xoff[j] + 32 * s) : make_uint4(0, 0, 0, 0);
         }
       }
     }
@@ -193,14 +272,11 @@ __global__ __launch_bounds__(WAVES * kWave) void skinny_kernel(
     for (int u = 0; u < U; ++u) {
       if (g0 + u >= mine) break;  // uniform across the wave
       const int c = __builtin_amdgcn_readfirstlane(wave + WAVES * (g0 + u));
-      const int kv = K - 128 * c - 32 * lg;
+      const int kv = K - 128 * c - 8 * lg;
       const uint16_t* xc = xbase + 128 * c;
-      float s0[NT], s1[NT];
+      float sc[NT][4];
 #pragma unroll
-      for (int i = 0; i < NT; ++i) {
-        s0[i] = __builtin_amdgcn_cvt_f32_fp8((int)G.sw[u][i], 0);  // OCP E4M3, exact
-        s1[i] = __builtin_amdgcn_cvt_f32_fp8((int)G.sw[u][i], 1);
-      }
+      for (int i = 0; i < NT; ++i) scale4(G.sw[u][i], sc[i]);
 #pragma unroll
       for (int s = 0; s < 4; ++s) {
         bf16x8 xv[MT];
@@ -209,12 +285,12 @@ __global__ __launch_bounds__(WAVES * kWave) void skinny_kernel(
           if constexpr (XPRE) {
             xv[j] = as_bf16x8(G.xq[u][s][j]);
           } else {
-            xv[j] = as_bf16x8((kfull || 8 * s < kv) ? ld16(xc + xoff[j] + 8 * s) : make_uint4(0, 0, 0, 0));
+            xv[j] = as_bf16x8((kfull || 32 * s < kv) ? ld16(xc + xoff[j] + 32 * s) : make_uint4(0, 0, 0, 0));
           }
         }
 #pragma unroll
         for (int i = 0; i < NT; ++i) {
-          const bf16x8 a = dequant8(G.cw[u][i][s], s < 2 ? s0[i] : s1[i]);
+          const bf16x8 a = dequant8(G.cw[u][i][s], sc[i][s]);
 #pragma unroll
           for (int j = 0; j < MT; ++j) acc[i][j] = mfma16x16x32(a, xv[j], acc[i][j]);
         }
@@ -232,63 +308,8 @@ __global__ __launch_bounds__(WAVES * kWave) void skinny_kernel(
   }
 
   const float st = *tensor_scale;
-  const bool rvec = (r & 7) == 0;
-  const int64_t tstride = (int64_t)M * r;
-  // Epilogue of one 16x16 tile: lane holds features n = n0+16i+4lg+v and token m = m0+16j+li.
   auto epilogue = [&](int i, int j, f32x4 v) {
-    f32x4 lo = {0.f, 0.f, 0.f, 0.f};
-    if (r > 0) {
-      const int na = n0 + 16 * i + li;  // B row for the A operand
-      const int mb = m0 + 16 * j + li;  // t row for the B operand
-      for (int j0 = 0; j0 < r; j0 += 32) {
-        const int jj = j0 + 8 * lg;
-        uint4 bw = make_uint4(0, 0, 0, 0);
-        float tv[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
-        if (jj < r) {
-          if (rvec) {
-            if (na < N) bw = ld16(lb + (int64_t)na * r + jj);
-            if (mb < M) {
-              for (int q = 0; q < tks; ++q) {  // K-slices of t, summed in order
-                const float* tp = t + (int64_t)q * tstride + (int64_t)mb * r + jj;
-                const float4 t0 = *reinterpret_cast<const float4*>(tp);
-                const float4 t1 = *reinterpret_cast<const float4*>(tp + 4);
-                tv[0] += t0.x; tv[1] += t0.y; tv[2] += t0.z; tv[3] += t0.w;
-                tv[4] += t1.x; tv[5] += t1.y; tv[6] += t1.z; tv[7] += t1.w;
-              }
-            }
-          } else {
-            uint32_t h[8];
-#pragma unroll
-            for (int e = 0; e < 8; ++e) {
-              const bool ok = jj + e < r;
-              h[e] = (ok && na < N) ? lb[(int64_t)na * r + jj + e] : 0u;
-              if (ok && mb < M)
-                for (int q = 0; q < tks; ++q) tv[e] += t[(int64_t)q * tstride + (int64_t)mb * r + jj + e];
-            }
-            bw = make_uint4(h[0] | (h[1] << 16), h[2] | (h[3] << 16), h[4] | (h[5] << 16), h[6] | (h[7] << 16));
-          }
-        }
-        uint4 th, tl;
-        split_bf16x8(tv, th, tl);
-        lo = mfma16x16x32(as_bf16x8(bw), as_bf16x8(th), lo);
-        lo = mfma16x16x32(as_bf16x8(bw), as_bf16x8(tl), lo);
-      }
-    }
-    const int m = m0 + 16 * j + li;
-    const int nf = n0 + 16 * i + 4 * lg;
-    if (m < M) {
-      uint32_t o[4];
-#pragma unroll
-      for (int e = 0; e < 4; ++e) o[e] = f32_to_bf16(st * v[e] + lo[e]);
-      uint16_t* yp = y + (int64_t)m * N + nf;
-      if ((N & 3) == 0 && nf + 3 < N) {
-        *reinterpret_cast<uint2*>(yp) = make_uint2(o[0] | (o[1] << 16), o[2] | (o[3] << 16));
-      } else {
-#pragma unroll
-        for (int e = 0; e < 4; ++e)
-          if (nf + e < N) yp[e] = (uint16_t)o[e];
-      }
-    }
+    store_tile(v, n0 + 16 * i, m0 + 16 * j, lane, M, N, st, t, tks, lb, r, y);
   };
 
   if constexpr (WAVES == 1) {
@@ -310,6 +331,231 @@ __global__ __launch_bounds__(WAVES * kWave) void skinny_kernel(
       epilogue(tl / MT, tl % MT, sum);
     }
   }
+}
+
+// ---------------------------------------------------------------------------
+// Split-K MFMA kernel for 16 < M <= 128 tokens.
+//   grid.x: groups of TM row tiles (16 TM output features); grid.y: groups of
+//   TN token tiles; grid.z: ranges of `cpz` 128-wide K chunks. The W waves of
+//   a workgroup take the chunks of its range round-robin and each covers all
+//   TM x TN output tiles, so one activation fragment feeds TM MFMAs and one
+//   weight fragment TN.
+//   Activations pass through a private LDS slab per wave. The L1 merges the
+//   addresses of consecutive lanes only, and the MFMA operand layout puts
+//   consecutive lanes on different tokens (different rows of x); so a chunk
+//   is loaded with 16 lanes per token row (contiguous 256 B), written to LDS
+//   and read back in operand layout (rows padded to 272 B: conflict-free).
+//   The waves' sums are reduced through LDS in wave order. With one K range
+//   the workgroup stores y; otherwise it writes its fp32 partial tile to
+//   part[z], and the last workgroup of the tile to arrive (a per-tile counter
+//   in the workspace) adds the partials in z order, stores y and clears the
+//   counter, so results do not depend on arrival order and the counters are
+//   zero again when the kernel ends.
+// ---------------------------------------------------------------------------
+constexpr int kXRow = 136;  // bf16 per LDS token row: 128 + 8 of padding
+
+template <int TM, int TN, int W>
+__global__ __launch_bounds__(W * kWave) void splitk_kernel(
+    const uint16_t* __restrict__ x, int M, int N, int K, const uint8_t* __restrict__ codes,
+    const uint8_t* __restrict__ scales, const float* __restrict__ tensor_scale, const float* __restrict__ t, int tks,
+    const uint16_t* __restrict__ lb, int r, uint16_t* __restrict__ y, int cpz, int nsplit, float* __restrict__ part,
+    uint32_t* __restrict__ counters) {
+  static_assert(TM <= 4, "the reduction reuses the activation slabs: TM * TN KB <= TN * 4.25 KB");
+  constexpr int TOK = 16 * TN;
+  __shared__ __align__(16) uint16_t xs[W][TOK * kXRow];
+  __shared__ uint32_t last_flag;
+  const int lane = threadIdx.x & (kWave - 1);
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
+  const int li = lane & 15, lg = lane >> 4;
+  const int RT = (N + 15) >> 4, KC = (K + 127) >> 7;
+  // XCD-aware order of a 1-D grid: workgroups are dealt to the 8 XCDs in
+  // turn, so workgroup L runs on XCD L % 8. All token groups and K ranges of
+  // a row group get consecutive slots of one XCD: its weights are fetched
+  // into that XCD's L2 once, and its partial sums stay there.
+  const int GX = (RT + TM - 1) / TM, GT = (M + TOK - 1) / TOK;
+  const int inner = (int)(blockIdx.x >> 3) % (GT * nsplit);
+  const int rg = (int)((blockIdx.x >> 3) / (GT * nsplit)) * 8 + (int)(blockIdx.x & 7);
+  if (rg >= GX) return;  // padding of the row-group count to a multiple of 8
+  const int tg = inner % GT, kz = inner / GT;
+  const int rt0 = rg * TM, n0 = 16 * rt0, m0 = tg * TOK;
+  const int cbeg = kz * cpz, cend = min(KC, cbeg + cpz);
+  const int nch = max(0, cend - cbeg);
+  const int mine = nch > wave ? (nch - wave + W - 1) / W : 0;
+
+  const uint8_t* cbase = codes + (int64_t)rt0 * KC * 1024;  // uniform
+  const uint8_t* sbase = scales + (int64_t)rt0 * KC * 128;
+  const uint32_t clane = 16 * lane, slane = 4 * (16 * (lg >> 1) + li);
+  int toff[TM];  // row tiles past the matrix are clamped to the last (never stored)
+#pragma unroll
+  for (int i = 0; i < TM; ++i) toff[i] = (min(rt0 + i, RT - 1) - rt0) * KC;
+  // Coalesced activation load: instruction q covers token rows 4 q + lg, 16 B
+  // per lane, at a wave-uniform chunk base plus a 32-bit lane offset. Tokens
+  // past M are clamped to the last one (their outputs are never stored).
+  uint32_t xoff[TN * 4];  // bytes
+#pragma unroll
+  for (int q = 0; q < TN * 4; ++q) xoff[q] = 2u * ((uint32_t)min(m0 + 4 * q + lg, M - 1) * (uint32_t)K + 8 * li);
+  uint16_t* slab = xs[wave];
+
+  struct WStage {
+    uint32_t cw[TM][4];
+    uint32_t sw[TM];
+  };
+  struct XStage {
+    uint4 v[TN * 4];
+  };
+  auto chunk_of = [&](int q) { return __builtin_amdgcn_readfirstlane(cbeg + wave + W * q); };
+  auto load_w = [&](int q, WStage& S) {
+    const int c = chunk_of(q);
+#pragma unroll
+    for (int i = 0; i < TM; ++i) {
+      const uint4 v = ld_nt16(cbase + (int64_t)(toff[i] + c) * 1024 + clane);
+      S.cw[i][0] = v.x; S.cw[i][1] = v.y; S.cw[i][2] = v.z; S.cw[i][3] = v.w;
+      S.sw[i] = __builtin_nontemporal_load(reinterpret_cast<const uint32_t*>(sbase + (int64_t)(toff[i] + c) * 128 + slane));
+    }
+  };
+  auto load_x = [&](int q, XStage& S) {
+    const int c = chunk_of(q);
+    const uint8_t* xc = reinterpret_cast<const uint8_t*>(x + 128 * c);  // uniform
+    if (c < KC - 1 || (K & 127) == 0) {
+#pragma unroll
+      for (int j = 0; j < TN * 4; ++j) S.v[j] = ld16(xc + xoff[j]);
+    } else {  // the last, partial chunk: pieces past K read as zero (K % 16 == 0: a piece is all in or out)
+      const bool kin = 128 * c + 8 * li < K;
+#pragma unroll
+      for (int j = 0; j < TN * 4; ++j) S.v[j] = kin ? ld16(xc + xoff[j]) : make_uint4(0, 0, 0, 0);
+    }
+  };
+  auto store_x = [&](const XStage& S) {
+#pragma unroll
+    for (int q = 0; q < TN * 4; ++q) *reinterpret_cast<uint4*>(slab + (4 * q + lg) * kXRow + 8 * li) = S.v[q];
+  };
+
+  f32x4 acc[TM][TN];
+#pragma unroll
+  for (int i = 0; i < TM; ++i)
+#pragma unroll
+    for (int j = 0; j < TN; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  auto compute = [&](const WStage& S) {
+    float sc[TM][4];
+#pragma unroll
+    for (int i = 0; i < TM; ++i) scale4(S.sw[i], sc[i]);
+#pragma unroll
+    for (int st = 0; st < 4; ++st) {
+      bf16x8 xv[TN];
+#pragma unroll
+      for (int j = 0; j < TN; ++j)
+        xv[j] = as_bf16x8(*reinterpret_cast<const uint4*>(slab + (16 * j + li) * kXRow + 32 * st + 8 * lg));
+#pragma unroll
+      for (int i = 0; i < TM; ++i) {
+        const bf16x8 a = dequant8(S.cw[i][st], sc[i][st]);
+#pragma unroll
+        for (int j = 0; j < TN; ++j) acc[i][j] = mfma16x16x32(a, xv[j], acc[i][j]);
+      }
+    }
+  };
+
+  // Pipeline: a ring of D weight stages (D chunks of weights in flight:
+  // enough to cover HBM latency with one or two waves per SIMD), the next
+  // chunk's activations in registers while the current one is in LDS. The
+  // ring is unrolled so every stage lives in fixed registers. The slab is
+  // rewritten only after this wave's reads of it were issued (LDS operations
+  // of one wave complete in order).
+  constexpr int D = 4;
+  WStage ws[D];
+  XStage xr;
+#pragma unroll
+  for (int u = 0; u < D; ++u)
+    if (u < mine) load_w(u, ws[u]);
+  if (mine > 0) load_x(0, xr);
+  for (int q0 = 0; q0 < mine; q0 += D) {
+#pragma unroll
+    for (int u = 0; u < D; ++u) {
+      const int q = q0 + u;
+      if (q >= mine) break;  // uniform across the wave
+      store_x(xr);
+      if (q + 1 < mine) load_x(q + 1, xr);
+      compute(ws[u]);
+      if (q + D < mine) load_w(q + D, ws[u]);
+    }
+  }
+
+  // Reduce the waves' sums: wave w's tiles go to its own slab, then tile e is
+  // summed over the waves, in wave order, by wave e % W.
+  float* red = reinterpret_cast<float*>(slab);
+#pragma unroll
+  for (int i = 0; i < TM; ++i)
+#pragma unroll
+    for (int j = 0; j < TN; ++j) *reinterpret_cast<f32x4*>(red + ((i * TN + j) * kWave + lane) * 4) = acc[i][j];
+  __syncthreads();
+  const float st = *tensor_scale;
+  constexpr int NTILE = TM * TN;
+  f32x4 sums[(NTILE + W - 1) / W];
+#pragma unroll
+  for (int e0 = 0; e0 < (NTILE + W - 1) / W; ++e0) {
+    const int e = wave + W * e0;
+    f32x4 sum = {0.f, 0.f, 0.f, 0.f};
+    if (e < NTILE) {
+#pragma unroll
+      for (int w = 0; w < W; ++w)
+        sum += *reinterpret_cast<const f32x4*>(reinterpret_cast<const float*>(xs[w]) + (e * kWave + lane) * 4);
+    }
+    sums[e0] = sum;
+  }
+  if (nsplit == 1) {
+#pragma unroll
+    for (int e0 = 0; e0 < (NTILE + W - 1) / W; ++e0) {
+      const int e = wave + W * e0;
+      if (e < NTILE) store_tile(sums[e0], n0 + 16 * (e / TN), m0 + 16 * (e % TN), lane, M, N, st, t, tks, lb, r, y);
+    }
+    return;
+  }
+  // K split over workgroups: publish this range's partial tile. The partials
+  // and the counter are agent-scope atomic accesses (coherent across the
+  // chip's L2 slices without flushing them); every lane waits for its stores
+  // to complete before the workgroup barrier, and the counter is bumped only
+  // after that barrier, so a workgroup that sees the last count sees every
+  // partial.
+  const int64_t zstride = (int64_t)M * N;
+#pragma unroll
+  for (int e0 = 0; e0 < (NTILE + W - 1) / W; ++e0) {
+    const int e = wave + W * e0;
+    if (e < NTILE) {
+      const int m = m0 + 16 * (e % TN) + li, nf = n0 + 16 * (e / TN) + 4 * lg;
+      if (m < M) {
+        float* pp = part + kz * zstride + (int64_t)m * N + nf;
+#pragma unroll
+        for (int v = 0; v < 4; ++v)
+          if (nf + v < N) __hip_atomic_store(pp + v, sums[e0][v], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      }
+    }
+  }
+  __builtin_amdgcn_s_waitcnt(0);  // this lane's stores are complete
+  __syncthreads();
+  uint32_t* ctr = counters + tg * GX + rg;
+  if (threadIdx.x == 0)
+    last_flag = __hip_atomic_fetch_add(ctr, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == (uint32_t)nsplit - 1 ? 1u : 0u;
+  __syncthreads();
+  if (last_flag == 0u) return;
+#pragma unroll
+  for (int e0 = 0; e0 < (NTILE + W - 1) / W; ++e0) {
+    const int e = wave + W * e0;
+    if (e < NTILE) {
+      const int m = m0 + 16 * (e % TN) + li, nf = n0 + 16 * (e / TN) + 4 * lg;
+      f32x4 sum = {0.f, 0.f, 0.f, 0.f};
+      if (m < M) {
+        const float* pp = part + (int64_t)m * N + nf;
+        for (int z = 0; z < nsplit; ++z) {  // fixed order: results do not depend on arrival
+#pragma unroll
+          for (int v = 0; v < 4; ++v)
+            if (nf + v < N)
+              sum[v] += __hip_atomic_load(pp + z * zstride + v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        }
+      }
+      store_tile(sum, n0 + 16 * (e / TN), m0 + 16 * (e % TN), lane, M, N, st, t, tks, lb, r, y);
+    }
+  }
+  if (threadIdx.x == 0) __hip_atomic_store(ctr, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
 // ---------------------------------------------------------------------------
@@ -343,7 +589,7 @@ __global__ __launch_bounds__(WAVES * kWave) void gemv_kernel(
   const int mine = nchunk > wave ? (nchunk - wave + WAVES - 1) / WAVES : 0;
   const uint8_t* cbase = codes + (int64_t)rt * KC * 1024;
   const uint8_t* sbase = scales + (int64_t)rt * KC * 128;
-  const uint32_t clane = 16 * lane, slane = 2 * lane;
+  const uint32_t clane = 16 * lane, slane = 4 * (16 * (lg >> 1) + li);
 
   struct Group {
     uint32_t cw[U][4];
@@ -355,7 +601,7 @@ __global__ __launch_bounds__(WAVES * kWave) void gemv_kernel(
       const int c = __builtin_amdgcn_readfirstlane(min(wave + WAVES * (g0 + u), nchunk - 1));
       const uint4 v = ld_nt16(cbase + (int64_t)c * 1024 + clane);
       G.cw[u][0] = v.x; G.cw[u][1] = v.y; G.cw[u][2] = v.z; G.cw[u][3] = v.w;
-      G.sw[u] = __builtin_nontemporal_load(reinterpret_cast<const uint16_t*>(sbase + (int64_t)c * 128 + slane));
+      G.sw[u] = __builtin_nontemporal_load(reinterpret_cast<const uint32_t*>(sbase + (int64_t)c * 128 + slane));
     }
   };
   Group ga, gb;
@@ -401,32 +647,25 @@ __global__ __launch_bounds__(WAVES * kWave) void gemv_kernel(
       for (int m = 0; m < MTOK; ++m)
 #pragma unroll
         for (int q = 0; q < 4; ++q)
-          xv[m][q] = *reinterpret_cast<const uint4*>(xs + m * Kp + 128 * c + 32 * lg + 8 * q);
+          xv[m][q] = *reinterpret_cast<const uint4*>(xs + m * Kp + 128 * c + 32 * q + 8 * lg);
+      float sc[4];
+      scale4(G.sw[u], sc);
 #pragma unroll
-      for (int blk = 0; blk < 2; ++blk) {
-        const float sc = blk == 0 ? __builtin_amdgcn_cvt_f32_fp8((int)G.sw[u], 0)
-                                  : __builtin_amdgcn_cvt_f32_fp8((int)G.sw[u], 1);
-        float p[MTOK];
+      for (int q = 0; q < 4; ++q) {  // word q: 8 codes, half of one block
+        const uint32_t w = G.cw[u][q];
+        const bf16x2 g0v = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, 1.0f, 0);
+        const bf16x2 g1v = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, 1.0f, 1);
+        const bf16x2 g2v = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, 1.0f, 2);
+        const bf16x2 g3v = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, 1.0f, 3);
 #pragma unroll
-        for (int m = 0; m < MTOK; ++m) p[m] = 0.0f;
-#pragma unroll
-        for (int d = 0; d < 2; ++d) {
-          const uint32_t w = G.cw[u][2 * blk + d];
-          const bf16x2 g0v = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, 1.0f, 0);
-          const bf16x2 g1v = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, 1.0f, 1);
-          const bf16x2 g2v = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, 1.0f, 2);
-          const bf16x2 g3v = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, 1.0f, 3);
-#pragma unroll
-          for (int m = 0; m < MTOK; ++m) {
-            const uint4 xq = xv[m][2 * blk + d];  // x[k .. k+7] of this dword's 8 codes
-            p[m] = __builtin_amdgcn_fdot2_f32_bf16(g0v, __builtin_bit_cast(bf16x2, xq.x), p[m], false);
-            p[m] = __builtin_amdgcn_fdot2_f32_bf16(g1v, __builtin_bit_cast(bf16x2, xq.y), p[m], false);
-            p[m] = __builtin_amdgcn_fdot2_f32_bf16(g2v, __builtin_bit_cast(bf16x2, xq.z), p[m], false);
-            p[m] = __builtin_amdgcn_fdot2_f32_bf16(g3v, __builtin_bit_cast(bf16x2, xq.w), p[m], false);
-          }
+        for (int m = 0; m < MTOK; ++m) {
+          const uint4 xq = xv[m][q];  // x[k .. k+7] of this word's 8 codes
+          float p = __builtin_amdgcn_fdot2_f32_bf16(g0v, __builtin_bit_cast(bf16x2, xq.x), 0.0f, false);
+          p = __builtin_amdgcn_fdot2_f32_bf16(g1v, __builtin_bit_cast(bf16x2, xq.y), p, false);
+          p = __builtin_amdgcn_fdot2_f32_bf16(g2v, __builtin_bit_cast(bf16x2, xq.z), p, false);
+          p = __builtin_amdgcn_fdot2_f32_bf16(g3v, __builtin_bit_cast(bf16x2, xq.w), p, false);
+          acc[m] = fmaf(sc[q], p, acc[m]);
         }
-#pragma unroll
-        for (int m = 0; m < MTOK; ++m) acc[m] = fmaf(sc, p[m], acc[m]);
       }
     }
   };
@@ -589,6 +828,74 @@ hipError_t run_gemv_w(int w, hipStream_t st, const uint16_t* x, int M, int N, in
   }
 }
 
+// Split-K MFMA path: 16 < m <= 128 (decode-shaped batches).
+// TM = 4 row tiles (64 features) per workgroup, TN token tiles (up to 64
+// tokens per workgroup, more go to grid.y), W = 4 waves. K is split over
+// grid.z until about 256 workgroups are in flight, while every wave keeps at
+// least one chunk and the fp32 partials (written and read once) stay within
+// a third of the weight bytes.
+struct SplitkCfg {
+  int tn, w, s, cpz, gx, gy;
+};
+#ifdef FP4RL_TUNING
+int g_tune_s = 0, g_tune_w = 0;  // scratch builds only: forced split and waves
+#endif
+
+static bool use_splitk(int64_t m) { return m > 16 && m <= 128; }
+
+static SplitkCfg pick_splitk(int64_t m, int64_t n, int64_t k) {
+  SplitkCfg c;
+  c.tn = 2;
+  c.w = 4;
+  c.gx = (int)((n + 63) / 64);
+  c.gy = (int)((m + 16 * c.tn - 1) / (16 * c.tn));
+  const int64_t kc = (k + 127) / 128;
+  const double wbytes = (double)n * (double)k * 0.5625;
+  int s = 1;
+  while ((int64_t)c.gx * c.gy * s < 256 && (kc + 2 * s - 1) / (2 * s) >= c.w &&
+         4.0 * (double)(2 * s) * (double)m * (double)n * 2.0 <= wbytes / 3.0)
+    s *= 2;
+#ifdef FP4RL_TUNING
+  if (g_tune_s > 0) s = g_tune_s;
+  if (g_tune_w > 0) c.w = g_tune_w;
+#endif
+  c.cpz = (int)((kc + s - 1) / s);
+  c.s = (int)((kc + c.cpz - 1) / c.cpz);  // no empty K range
+  if ((int64_t)c.gx * c.gy > kLinearCounters) c.s = 1, c.cpz = (int)kc;  // a split needs one counter per tile
+  return c;
+}
+
+size_t linear_partial_bytes(int64_t m, int64_t n, int64_t k) {
+  if (!use_splitk(m)) return 0;
+  const SplitkCfg c = pick_splitk(m, n, k);
+  if (c.s == 1) return 0;
+  return ((size_t)c.s * (size_t)m * (size_t)n * sizeof(float) + 255) / 256 * 256;
+}
+
+template <int TN, int W>
+hipError_t run_splitk(const SplitkCfg& c, hipStream_t st, const uint16_t* x, int M, int N, int K, const uint8_t* codes,
+                      const uint8_t* scales, const float* ts, const float* t, int tks, const uint16_t* b, int r,
+                      uint16_t* y, float* part, uint32_t* counters) {
+  const unsigned grid = (unsigned)(8 * ((c.gx + 7) / 8) * c.gy * c.s);
+  hipLaunchKernelGGL((splitk_kernel<4, TN, W>), dim3(grid), dim3(W * kWave), 0, st, x, M, N, K, codes, scales, ts, t,
+                     tks, b, r, y, c.cpz, c.s, c.s > 1 ? part : nullptr, c.s > 1 ? counters : nullptr);
+  return hipGetLastError();
+}
+
+static hipError_t launch_splitk(const SplitkCfg& c, hipStream_t st, const uint16_t* x, int M, int N, int K,
+                                const uint8_t* codes, const uint8_t* scales, const float* ts, const float* t, int tks,
+                                const uint16_t* b, int r, uint16_t* y, float* part, uint32_t* counters) {
+#define FP4RL_SPLITK(TN_, W_) \
+  if (c.tn == TN_ && c.w == W_) \
+    return run_splitk<TN_, W_>(c, st, x, M, N, K, codes, scales, ts, t, tks, b, r, y, part, counters);
+  FP4RL_SPLITK(2, 4)
+#ifdef FP4RL_TUNING
+  FP4RL_SPLITK(2, 2) FP4RL_SPLITK(2, 8)
+#endif
+#undef FP4RL_SPLITK
+  return hipErrorInvalidValue;
+}
+
 const char* fp4_linear_kernel_name(int64_t m, int64_t n, int64_t k, int64_t r) {
   static const char* const kNames[4][3][5] = {
 #define FP4RL_NAME_ROW(MT_, NT_)                                                                           \
@@ -611,6 +918,15 @@ const char* fp4_linear_kernel_name(int64_t m, int64_t n, int64_t k, int64_t r) {
     while ((1 << wi) < gemv_waves(n, k)) ++wi;
     return kGemv[m - 1][wi];
   }
+  if (use_splitk(m)) {
+    const SplitkCfg sc = pick_splitk(m, n, k);
+    static const char* const kSplitk[2][4] = {
+        {"splitk_kernel<4, 2, 1>", "splitk_kernel<4, 2, 2>", "splitk_kernel<4, 2, 4>", "splitk_kernel<4, 2, 8>"},
+        {"splitk_kernel<4, 4, 1>", "splitk_kernel<4, 4, 2>", "splitk_kernel<4, 4, 4>", "splitk_kernel<4, 4, 8>"}};
+    int wi = 0;
+    while ((1 << wi) < sc.w) ++wi;
+    return kSplitk[sc.tn == 2 ? 0 : 1][wi];
+  }
   const SkinnyCfg c = pick_skinny(m, n, k);
   const int mi = c.mt == 1 ? 0 : c.mt == 2 ? 1 : c.mt == 4 ? 2 : 3;
   const int ni = c.nt == 1 ? 0 : c.nt == 2 ? 1 : 2;
@@ -621,13 +937,17 @@ const char* fp4_linear_kernel_name(int64_t m, int64_t n, int64_t k, int64_t r) {
 
 hipError_t launch_fp4_linear(const uint16_t* x, int64_t m, int64_t n, int64_t k, const uint8_t* codes,
                              const uint8_t* scales, const float* tensor_scale, const float* t, int tks,
-                             const uint16_t* b, int64_t r, uint16_t* y, hipStream_t stream) {
+                             const uint16_t* b, int64_t r, uint16_t* y, float* part, uint32_t* counters,
+                             hipStream_t stream) {
   const int M = (int)m, N = (int)n, K = (int)k, R = (int)r;
   if (use_gemv(m, n, k, r)) {
     const int w = gemv_waves(n, k);
     return m == 1 ? run_gemv_w<1>(w, stream, x, M, N, K, codes, scales, tensor_scale, t, tks, b, R, y)
                   : run_gemv_w<2>(w, stream, x, M, N, K, codes, scales, tensor_scale, t, tks, b, R, y);
   }
+  if (use_splitk(m))
+    return launch_splitk(pick_splitk(m, n, k), stream, x, M, N, K, codes, scales, tensor_scale, t, tks, b, R, y, part,
+                         counters);
   const SkinnyCfg cfg = pick_skinny(m, n, k);
   const dim3 grid((unsigned)((n + 16 * cfg.nt - 1) / (16 * cfg.nt)), (unsigned)((m + 16 * cfg.mt - 1) / (16 * cfg.mt)));
 #define FP4RL_SKINNY(MT_, NT_) \

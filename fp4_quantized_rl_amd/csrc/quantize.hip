@@ -105,18 +105,22 @@ __device__ __forceinline__ void load_quarter(const void* w, int64_t idx, float v
 
 // Destination of block b's two code bytes of quarter q and of its scale byte.
 // Row-major: codes [n][k/2], scales [n][k/16]. Tiled: 16-row x 128-k tiles
-// (1 KB of codes + 128 B of scales each, tile (rt, c) at rt*kc + c), inside
-// which lane l = 16 g + i of a wave finds its 16 code bytes at 16 l and its
-// two scale bytes at 2 l: row i, k = 128 c + 32 g .. + 31.
+// (1 KB of codes + 128 B of scales each, tile (rt, c) at rt*kc + c). Inside a
+// tile, lane l = 16 g + i of a wave finds its 16 code bytes at 16 l, word j of
+// them holding row i, k = 128 c + 32 j + 8 g .. + 7; the scale word 16 p + i
+// holds in byte j the scale of block 8 c + 2 j + p. So a block kb (8 per
+// chunk) lands in word j = kb/2 of lane groups g = 2 (kb & 1) and g + 1, and
+// its quarter q (4 elements) in group g + q/2, byte 2 (q & 1) of the word.
 template <bool TILED>
 __device__ __forceinline__ void block_dest(int64_t b, int q, uint32_t kblocks, uint32_t kc, int64_t& code_off,
                                            int64_t& scale_off) {
   if constexpr (TILED) {
     const uint32_t n = (uint32_t)b / kblocks, kb = (uint32_t)b - n * kblocks;
-    const uint32_t lane = 16u * ((kb & 7u) >> 1) + (n & 15u);
+    const uint32_t i = n & 15u, kq = kb & 7u, p = kq & 1u, j = kq >> 1;
+    const uint32_t g = 2u * p + ((uint32_t)q >> 1);
     const int64_t tile = (int64_t)(n >> 4) * kc + (kb >> 3);
-    code_off = tile * 1024 + 16 * lane + 8 * (kb & 1u) + 2 * q;
-    scale_off = tile * 128 + 2 * lane + (kb & 1u);
+    code_off = tile * 1024 + 16 * (16 * g + i) + 4 * j + 2 * (q & 1);
+    scale_off = tile * 128 + 4 * (16 * p + i) + j;
   } else {
     code_off = 8 * b + 2 * q;
     scale_off = b;
@@ -187,33 +191,33 @@ __global__ void zero_fill(uint4* __restrict__ p, int64_t n16) {
     p[i] = make_uint4(0, 0, 0, 0);
 }
 
-// Row-major NVFP4 -> tiled: one thread per 16-byte code piece of a tile.
+// Row-major NVFP4 -> tiled: one thread per lane piece of a tile (16 code
+// bytes; lanes of groups 0 and 1 also write the scale word p = g).
 __global__ void to_tiled_kernel(const uint8_t* __restrict__ codes, const uint8_t* __restrict__ scales, int N, int K,
                                 int kc, int64_t pieces, uint8_t* __restrict__ codes_t, uint8_t* __restrict__ scales_t) {
   const int64_t p = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
   if (p >= pieces) return;
-  const int lane = (int)(p & 63);
+  const int lane = (int)(p & 63), g = lane >> 4, i = lane & 15;
   const int64_t tile = p >> 6;
   const int rt = (int)(tile / kc), c = (int)(tile - (int64_t)rt * kc);
-  const int n = 16 * rt + (lane & 15), k0 = 128 * c + 32 * (lane >> 4);
-  uint4 v = make_uint4(0, 0, 0, 0);
+  const int n = 16 * rt + i;
+  uint32_t w[4] = {0u, 0u, 0u, 0u};
   uint32_t sv = 0;
-  if (n < N && k0 < K) {
-    const uint8_t* cr = codes + (int64_t)n * (K / 2) + k0 / 2;
-    const uint8_t* sr = scales + (int64_t)n * (K / 16) + k0 / 16;
-    const uint2 a = *reinterpret_cast<const uint2*>(cr);  // rows are 8-byte aligned (K % 16 == 0)
-    v.x = a.x;
-    v.y = a.y;
-    sv = sr[0];
-    if (k0 + 16 < K) {
-      const uint2 b2 = *reinterpret_cast<const uint2*>(cr + 8);
-      v.z = b2.x;
-      v.w = b2.y;
-      sv |= (uint32_t)sr[1] << 8;
+  if (n < N) {
+    const uint8_t* cr = codes + (int64_t)n * (K / 2);
+    const uint8_t* sr = scales + (int64_t)n * (K / 16);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int k0 = 128 * c + 32 * j + 8 * g;  // 8 codes = 4 bytes, 4-byte aligned (K % 16 == 0)
+      if (k0 < K) w[j] = *reinterpret_cast<const uint32_t*>(cr + k0 / 2);
+      if (g < 2) {
+        const int kb = 8 * c + 2 * j + g;  // scale word p = g
+        if (16 * kb < K) sv |= (uint32_t)sr[kb] << (8 * j);
+      }
     }
   }
-  *reinterpret_cast<uint4*>(codes_t + tile * 1024 + 16 * lane) = v;
-  *reinterpret_cast<uint16_t*>(scales_t + tile * 128 + 2 * lane) = (uint16_t)sv;
+  *reinterpret_cast<uint4*>(codes_t + tile * 1024 + 16 * lane) = make_uint4(w[0], w[1], w[2], w[3]);
+  if (g < 2) *reinterpret_cast<uint32_t*>(scales_t + tile * 128 + 4 * (16 * g + i)) = sv;
 }
 
 }  // namespace

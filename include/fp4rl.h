@@ -90,10 +90,13 @@ int32_t fp4rl_abi_version(void);
  *   FP4RL_TILED      the operand layout of the linear kernels: 16-row x 128-k
  *                    tiles, tile (rt, c) at index rt * ceil(k/128) + c, each
  *                    1024 code bytes + 128 scale bytes. Inside a tile, the
- *                    16 code bytes at offset 16 * (16 g + i) hold row 16 rt + i,
- *                    k = 128 c + 32 g .. + 31 (low nibble first), and the 2
- *                    scale bytes at 2 * (16 g + i) its blocks 8 c + 2 g, +1.
- *                    Rows >= n and k >= k of partial tiles are zero.
+ *                    16 code bytes at offset 16 * (16 g + i) (g = 0..3,
+ *                    i = 0..15) hold row 16 rt + i: their 4-byte word j
+ *                    (j = 0..3) holds k = 128 c + 32 j + 8 g .. + 7, low nibble
+ *                    first. The scale word at byte 4 * (16 p + i) (p = 0, 1)
+ *                    holds in its byte j the scale of row 16 rt + i, block
+ *                    8 c + 2 j + p. Rows >= n and k >= k of partial tiles are
+ *                    zero.
  * Two HBM passes (W is read twice): a tensor-amax pass that leaves
  * per-workgroup partial maxima in the workspace (no atomics), and an encode
  * pass. Workspace: fp4rl_nvfp4_quantize_workspace(n, k) bytes, 16-byte aligned.
@@ -119,10 +122,18 @@ fp4rl_status fp4rl_nvfp4_to_tiled(const uint8_t* codes, const uint8_t* scales, i
  * k % 16 == 0; 0 <= r <= 256; r == 0 or lora_a == lora_b == NULL means no
  * LoRA term. Accumulation is fp32; the output is rounded once to bf16.
  * Launches the LoRA down-projection (when r > 0) and then the main kernel,
- * chosen by m: an MFMA skinny kernel for decode-shaped m, a tiled MFMA GEMM
- * with LDS-dequantised weight tiles for prefill-shaped m.
- * Workspace: fp4rl_fp4_lora_linear_workspace(m, n, k, r) bytes: the K-split
- * partial sums of t, which the main kernel's epilogue adds in a fixed order.
+ * chosen by m (see fp4rl_fp4_linear_kernel_name).
+ * Workspace: fp4rl_fp4_lora_linear_workspace(m, n, k, r) bytes (0 when
+ * neither split below is used), 16-byte aligned. It starts with 256 counter
+ * words (1 KB); then come the K-split partial sums of t and, for shapes with
+ * few output tiles, the main kernel's K-split partial sums of y (the last
+ * workgroup of a tile to finish, found through its counter, adds them). All
+ * partial sums are added in a fixed order, so results do not depend on
+ * scheduling. The counter words must be zero before the first call (e.g. a
+ * zero-filled workspace); every call returns them to zero and no other data
+ * is ever stored there, so one workspace, sized for the largest call, serves
+ * any sequence of linear calls and shapes (but not calls that run at the
+ * same time).
  * ---------------------------------------------------------------------- */
 size_t fp4rl_fp4_lora_linear_workspace(int64_t m, int64_t n, int64_t k, int64_t r);
 fp4rl_status fp4rl_fp4_lora_linear(const uint16_t* x, int64_t m, int64_t n, int64_t k,
@@ -139,16 +150,19 @@ fp4rl_status fp4rl_fp4_lora_linear(const uint16_t* x, int64_t m, int64_t n, int6
  *   partial sums go to the workspace (fp4rl_lora_down_workspace bytes, 0 when
  *   no split is used) and are added in a fixed order, so t is deterministic.
  * fp4rl_fp4_linear_lora_up: y = bf16(s_t * x deq^T + t B^T); t may be NULL
- *   (with r == 0) for the base product alone. */
+ *   (with r == 0) for the base product alone. Workspace:
+ *   fp4rl_fp4_linear_lora_up_workspace(m, n, k) bytes (0 for most shapes),
+ *   laid out and reused as fp4rl_fp4_lora_linear's (counter words first). */
 size_t fp4rl_lora_down_workspace(int64_t m, int64_t k, int64_t r);
 fp4rl_status fp4rl_lora_down(const uint16_t* x, int64_t m, int64_t k, const uint16_t* lora_a,
                              int64_t r, float lora_scale, float* t, void* workspace,
                              size_t workspace_bytes, fp4rl_stream stream);
+size_t fp4rl_fp4_linear_lora_up_workspace(int64_t m, int64_t n, int64_t k);
 fp4rl_status fp4rl_fp4_linear_lora_up(const uint16_t* x, int64_t m, int64_t n, int64_t k,
                                       const uint8_t* codes, const uint8_t* scales,
                                       const float* tensor_scale, const float* t,
                                       const uint16_t* lora_b, int64_t r, uint16_t* y,
-                                      fp4rl_stream stream);
+                                      void* workspace, size_t workspace_bytes, fp4rl_stream stream);
 
 /* [host] Name of the main-kernel instantiation the linear launches for this
  * shape and rank, as a demangler prints its template arguments (e.g.

@@ -34,24 +34,26 @@ def u8_to_dev(a: np.ndarray, dev) -> torch.Tensor:
 def tile_host(codes, scales, n, k):
     """Row-major NVFP4 bytes -> the tiled layout (16-row x 128-k tiles), by index permutation.
 
-    Tile (rt, c): 1024 code bytes ordered [g][i][16 B] = row 16 rt + i, bytes
-    64 c + 16 g .. + 15; 128 scale bytes ordered [g][i][2] = blocks 8 c + 2 g, +1.
+    Tile (rt, c): 1024 code bytes ordered [g][i][j][4 B], word j of lane
+    16 g + i = row 16 rt + i, bytes 64 c + 16 j + 4 g .. + 3 (k = 128 c + 32 j
+    + 8 g .. + 7); 128 scale bytes ordered [p][i][j] = block 8 c + 2 j + p.
     """
     rt, kc = (n + 15) // 16, (k + 127) // 128
     cp = np.zeros((rt * 16, kc * 64), np.uint8)
     cp[:n, : k // 2] = codes
     sp = np.zeros((rt * 16, kc * 8), np.uint8)
     sp[:n, : k // 16] = scales
-    ct = cp.reshape(rt, 16, kc, 4, 16).transpose(0, 2, 3, 1, 4).reshape(-1)
-    st = sp.reshape(rt, 16, kc, 4, 2).transpose(0, 2, 3, 1, 4).reshape(-1)
+    # cp axes (rt, i, c, j, g, e) -> (rt, c, g, i, j, e); sp axes (rt, i, c, j, p) -> (rt, c, p, i, j)
+    ct = cp.reshape(rt, 16, kc, 4, 4, 4).transpose(0, 2, 4, 1, 3, 5).reshape(-1)
+    st = sp.reshape(rt, 16, kc, 4, 2).transpose(0, 2, 4, 1, 3).reshape(-1)
     return ct, st
 
 
 def untile_host(ct, st, n, k):
     """Inverse of tile_host; also returns whether every padding byte is zero."""
     rt, kc = (n + 15) // 16, (k + 127) // 128
-    cp = np.asarray(ct).reshape(rt, kc, 4, 16, 16).transpose(0, 3, 1, 2, 4).reshape(rt * 16, kc * 64)
-    sp = np.asarray(st).reshape(rt, kc, 4, 16, 2).transpose(0, 3, 1, 2, 4).reshape(rt * 16, kc * 8)
+    cp = np.asarray(ct).reshape(rt, kc, 4, 16, 4, 4).transpose(0, 3, 1, 4, 2, 5).reshape(rt * 16, kc * 64)
+    sp = np.asarray(st).reshape(rt, kc, 2, 16, 4).transpose(0, 3, 1, 4, 2).reshape(rt * 16, kc * 8)
     pad_zero = (not cp[n:].any() and not cp[:, k // 2:].any() and not sp[n:].any() and not sp[:, k // 16:].any())
     return cp[:n, : k // 2].copy(), sp[:n, : k // 16].copy(), pad_zero
 

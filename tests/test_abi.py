@@ -102,7 +102,16 @@ def test_linear_rejects_bad_arguments(lib):
     assert need >= 7 * 32 * 4
     assert lib.fp4rl_lora_down(FAKE, 1, 3584, FAKE, 32, 1.0, FAKE, FAKE, need - 1, None) == ERR_WORKSPACE
     assert lib.fp4rl_lora_down_workspace(8192, 3584, 32) == 0
-    assert lib.fp4rl_fp4_linear_lora_up(FAKE, 4, 8, 32, FAKE, FAKE, FAKE, None, FAKE, 8, FAKE, None) == ERR_NULL
+    assert lib.fp4rl_fp4_linear_lora_up(FAKE, 4, 8, 32, FAKE, FAKE, FAKE, None, FAKE, 8, FAKE, None, 0,
+                                        None) == ERR_NULL
+    # K split over workgroups (decode-shaped m, few output tiles): fp32 partials + counters
+    need = lib.fp4rl_fp4_linear_lora_up_workspace(64, 3584, 18944)
+    assert need >= 2 * 64 * 3584 * 4
+    assert lib.fp4rl_fp4_linear_lora_up(FAKE, 64, 3584, 18944, FAKE, FAKE, FAKE, None, None, 0, FAKE, FAKE, need - 1,
+                                        None) == ERR_WORKSPACE
+    assert lib.fp4rl_fp4_linear_lora_up_workspace(1, 3584, 18944) == 0
+    assert (lib.fp4rl_fp4_lora_linear_workspace(64, 3584, 18944, 32)
+            >= lib.fp4rl_fp4_linear_lora_up_workspace(64, 3584, 18944) + 64 * 32 * 4)
 
 
 def test_aqn_rejects_bad_arguments(lib):

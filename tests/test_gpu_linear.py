@@ -69,6 +69,44 @@ def test_ragged_shapes(m, n, k, r):
     _check(y, linear.lora_linear(x, *q, a, b, LORA_SCALE), f"{m}x{n}x{k} r{r}")
 
 
+SPLITK = [  # (m, n, k, r): few output tiles and a long K, so K is also split over workgroups
+    (17, 40, 4096, 8), (20, 38, 4112, 4), (33, 100, 8192, 32), (64, 130, 6144, 16), (100, 72, 16384, 24),
+    (128, 64, 12288, 64),
+]
+
+
+@pytest.mark.parametrize("m,n,k,r", SPLITK)
+def test_split_k_shapes(m, n, k, r):
+    dev = device()
+    assert fr.fp4_linear_lora_up_workspace_bytes(m, n, k) > 0, "shape no longer splits K over workgroups"
+    w, x, a, b = _case(m, n, k, r, seed=m * 131 + n * 17 + k)
+    q = nvfp4.quantize(w)
+    say(f"linear split-K m={m} n={n} k={k} r={r} ({fr.fp4_linear_kernel_name(m, n, k, r)})")
+    y = _run(dev, x, q, a, b, LORA_SCALE)
+    _check(y, linear.lora_linear(x, *q, a, b, LORA_SCALE), f"{m}x{n}x{k} r{r}")
+
+
+def test_workspace_reuse_across_shapes():
+    """One zero-filled workspace serves a sequence of split-K and plain calls, twice over: every result
+    equals the result with a fresh workspace, bit for bit (the counters are back at zero after each call)."""
+    dev = device()
+    shapes = [(33, 100, 8192, 32), (64, 130, 6144, 16), (8, 96, 512, 8), (20, 38, 4112, 4)]
+    cases = []
+    for i, (m, n, k, r) in enumerate(shapes):
+        w, x, a, b = _case(m, n, k, r, seed=900 + i)
+        q = nvfp4.quantize(w)
+        cases.append((bf16_to_dev(x, dev), nvfp4_to_dev(*q, dev), bf16_to_dev(a, dev), bf16_to_dev(b, dev)))
+    big = max(fr.fp4_lora_linear_workspace_bytes(m, n, k, r) for m, n, k, r in shapes)
+    shared = fr.linear_workspace(big, dev)
+    fresh = [fr.fp4_lora_linear(*c, LORA_SCALE) for c in cases]
+    for rep in range(2):
+        for i, c in enumerate(cases):
+            y = fr.fp4_lora_linear(*c, LORA_SCALE, workspace=shared)
+            torch.cuda.synchronize()
+            assert torch.equal(y, fresh[i]), f"pass {rep}, shape {shapes[i]}"
+    say(f"  {len(shapes)} shapes x 2 passes on one workspace: identical")
+
+
 def test_lora_reductions_bit_identical():
     dev = device()
     m, n, k, r = 24, 96, 256, 16
