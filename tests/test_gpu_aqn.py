@@ -65,12 +65,25 @@ def test_noise_only_exposes_z():
     _check(x, np.zeros(5120, np.float32), 1.0, 11, 3, 7, 1e-6, dev, "w=0 sigma=1")
 
 
-@pytest.mark.parametrize("m,d", [(1, 1), (3, 7), (5, 100), (130, 513), (2, 4097), (17, 16384), (9, 8200)])
+@pytest.mark.parametrize("m,d", [(1, 1), (3, 7), (5, 100), (130, 513), (2, 4097), (17, 16384), (9, 8200),
+                                 (1, 3584), (16, 264), (64, 5120), (256, 3584), (257, 3584)])
 def test_ragged_shapes(m, d):
     dev = device()
     x = activations_bf16(m, d, m * 100 + d)
     w = np.random.default_rng(d).uniform(0.5, 1.5, d).astype(np.float32)
     _check(x, w, 1e-2, 5, 1, 2, 1e-6, dev, f"m={m} d={d}")
+
+
+def test_few_rows_and_many_rows_paths_agree():
+    """Up to 256 rows the columns are split over workgroups; beyond, one wave per row. Both sum the
+    squares in the same order, so the first 256 rows of a 257-row batch equal the 256-row result."""
+    dev = device()
+    d = 3584
+    x = activations_bf16(257, d, 77)
+    w = np.random.default_rng(3).uniform(0.5, 1.5, d).astype(np.float32)
+    y_many, wn_many = _run(dev, x, w, 1e-2, 5, 2, 1, 1e-6)
+    y_few, wn_few = _run(dev, x[:256], w, 1e-2, 5, 2, 1, 1e-6)
+    assert np.array_equal(y_many[:256], y_few) and np.array_equal(wn_many, wn_few)
 
 
 def test_zero_rows_still_writes_noise():
