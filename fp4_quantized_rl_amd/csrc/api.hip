@@ -73,6 +73,8 @@ fp4rl_status check_linear_shape(int64_t m, int64_t n, int64_t k, int64_t r) {
                 "negative size (m=%lld n=%lld k=%lld r=%lld)", (long long)m, (long long)n, (long long)k, (long long)r);
   FP4RL_REQUIRE(k > 0 && k % 16 == 0, FP4RL_ERR_SHAPE, "k=%lld must be a positive multiple of 16", (long long)k);
   FP4RL_REQUIRE(m < kMaxDim && n < kMaxDim && k < kMaxDim, FP4RL_ERR_SHAPE, "dimension >= 2^31");
+  // the kernels address activations with 32-bit byte offsets
+  FP4RL_REQUIRE(m * k < ((int64_t)1 << 31), FP4RL_ERR_SHAPE, "m * k = %lld must be below 2^31", (long long)(m * k));
   FP4RL_REQUIRE(r <= fp4rl::kMaxRank, FP4RL_ERR_SHAPE, "rank r=%lld exceeds %lld", (long long)r,
                 (long long)fp4rl::kMaxRank);
   return FP4RL_OK;

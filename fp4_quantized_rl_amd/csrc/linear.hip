@@ -26,6 +26,7 @@
 // of the lane's 16-byte code load. On the activation side the four lane
 // groups of one token then read 64 consecutive bytes per load instruction.
 #include <algorithm>
+#include <type_traits>
 
 #include "device.hpp"
 #include "launch.hpp"
@@ -34,6 +35,17 @@ namespace fp4rl {
 namespace {
 
 __device__ __forceinline__ uint4 ld16(const void* p) { return *reinterpret_cast<const uint4*>(p); }
+
+// Calls f(I, J) for every (I, J) < (TI, TJ) with compile-time indices, so that
+// register arrays indexed by them never fall back to scratch memory (a plain
+// loop over a large inlined body may be left rolled).
+template <int TI, int TJ, int E = 0, class F>
+__device__ __forceinline__ void for_tiles(F&& f) {
+  if constexpr (E < TI * TJ) {
+    f(std::integral_constant<int, E / TJ>{}, std::integral_constant<int, E % TJ>{});
+    for_tiles<TI, TJ, E + 1>(f);
+  }
+}
 
 // The four E4M3 scale bytes of a tiled scale word, decoded exactly (OCP e4m3fn).
 __device__ __forceinline__ void scale4(uint32_t w, float (&sc)[4]) {
@@ -159,13 +171,13 @@ __device__ __forceinline__ void store_tile(f32x4 v, int nb, int mb, int lane, in
   const int m = mb + li;
   const int nf = nb + 4 * lg;
   if (m < M) {
-    uint32_t o[4];
-#pragma unroll
-    for (int e = 0; e < 4; ++e) o[e] = f32_to_bf16(st * v[e] + lo[e]);
+    const uint32_t o01 = pack_bf16x2(st * v[0] + lo[0], st * v[1] + lo[1]);
+    const uint32_t o23 = pack_bf16x2(st * v[2] + lo[2], st * v[3] + lo[3]);
     uint16_t* yp = y + (int64_t)m * N + nf;
     if ((N & 3) == 0 && nf + 3 < N) {
-      *reinterpret_cast<uint2*>(yp) = make_uint2(o[0] | (o[1] << 16), o[2] | (o[3] << 16));
+      *reinterpret_cast<uint2*>(yp) = make_uint2(o01, o23);
     } else {
+      const uint32_t o[4] = {o01 & 0xFFFFu, o01 >> 16, o23 & 0xFFFFu, o23 >> 16};
 #pragma unroll
       for (int e = 0; e < 4; ++e)
         if (nf + e < N) yp[e] = (uint16_t)o[e];
@@ -559,6 +571,218 @@ __global__ __launch_bounds__(W * kWave) void splitk_kernel(
 }
 
 // ---------------------------------------------------------------------------
+// Prefill GEMM (M > 128 tokens): a workgroup computes 256 output features x
+// 128 tokens over all of K; wave w owns features 64 w .. 64 w + 63 (TM = 4
+// row tiles) against all 8 token tiles, so one dequantised weight fragment
+// feeds 8 MFMAs and one activation fragment 4.
+//   Activation chunks (128 tokens x 128 k, 32 KB) are loaded by all threads
+//   with consecutive threads on consecutive 16-byte pieces of a token row,
+//   held one chunk ahead in registers and written to one of two LDS slabs
+//   (rows padded to 272 B), from which every wave reads its B operands in
+//   the MFMA layout. Weights go to registers two chunks ahead. One barrier
+//   per chunk.
+//   Grid order is XCD-aware: the 8 XCDs take workgroups in turn, and each
+//   XCD works through super-tiles of 8 row groups x 4 token groups, so the
+//   workgroups that run together on one XCD share their weights and
+//   activations in its L2.
+// ---------------------------------------------------------------------------
+constexpr int kPfRows = 256, kPfTok = 128;
+
+__global__ __launch_bounds__(256) void prefill_kernel(
+    const uint16_t* __restrict__ x, int M, int N, int K, const uint8_t* __restrict__ codes,
+    const uint8_t* __restrict__ scales, const float* __restrict__ tensor_scale, const float* __restrict__ t, int tks,
+    const uint16_t* __restrict__ lb, int r, uint16_t* __restrict__ y) {
+  constexpr int TM = 4, TN = 8, W = 4, D = 2;
+  constexpr int NTH = W * kWave;
+  constexpr int XPT = kPfTok * 16 / NTH;  // 16-byte activation pieces per thread and chunk (8)
+  __shared__ __align__(16) uint16_t xs[2][kPfTok * kXRow];
+  const int lane = threadIdx.x & (kWave - 1);
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
+  const int li = lane & 15, lg = lane >> 4;
+  const int RT = (N + 15) >> 4, KC = (K + 127) >> 7;
+  const int GR = (N + kPfRows - 1) / kPfRows, GT = (M + kPfTok - 1) / kPfTok;
+  // workgroup -> (row group, token group): XCD = L % 8; slot j = L / 8 of that
+  // XCD; super-tile s = 8 (j / 32) + XCD covers row groups 8 sr .. +7 and
+  // token groups 4 stt .. +3, its 32 tiles taken row group fastest
+  const int L = blockIdx.x, xcd = L & 7, j = L >> 3;
+  const int s = 8 * (j >> 5) + xcd, within = j & 31;
+  const int nstt = (GT + 3) / 4;
+  const int sr = s / nstt, stt = s - sr * nstt;
+  const int rg = 8 * sr + (within & 7), tg = 4 * stt + (within >> 3);
+  if (rg >= GR || tg >= GT) return;
+  const int rt0 = rg * (kPfRows / 16) + wave * TM, n0 = 16 * rt0, m0 = tg * kPfTok;
+
+  const uint8_t* cbase = codes + (int64_t)rt0 * KC * 1024;  // uniform per wave
+  const uint8_t* sbase = scales + (int64_t)rt0 * KC * 128;
+  const uint32_t clane = 16 * lane, slane = 4 * (16 * (lg >> 1) + li);
+  int toff[TM];  // row tiles past the matrix are clamped to the last (never stored)
+#pragma unroll
+  for (int i = 0; i < TM; ++i) toff[i] = (min(rt0 + i, RT - 1) - rt0) * KC;
+  uint32_t xoff[XPT];  // bytes; tokens past M clamped to the last one (never stored)
+  uint32_t xlds[XPT];  // bf16 units
+#pragma unroll
+  for (int q = 0; q < XPT; ++q) {
+    const int p = threadIdx.x + NTH * q, row = p >> 4, pc = p & 15;
+    xoff[q] = 2u * ((uint32_t)min(m0 + row, M - 1) * (uint32_t)K + 8 * pc);
+    xlds[q] = row * kXRow + 8 * pc;
+  }
+
+  struct WStage {
+    uint32_t cw[TM][4];
+    uint32_t sw[TM];
+  };
+  auto load_w = [&](int c, WStage& S) {
+#pragma unroll
+    for (int i = 0; i < TM; ++i) {
+      const uint4 v = ld_nt16(cbase + (int64_t)(toff[i] + c) * 1024 + clane);
+      S.cw[i][0] = v.x; S.cw[i][1] = v.y; S.cw[i][2] = v.z; S.cw[i][3] = v.w;
+      S.sw[i] = __builtin_nontemporal_load(reinterpret_cast<const uint32_t*>(sbase + (int64_t)(toff[i] + c) * 128 + slane));
+    }
+  };
+  uint4 xr[XPT];
+  auto load_x = [&](int c) {
+    const uint8_t* xc = reinterpret_cast<const uint8_t*>(x + 128 * c);  // uniform
+    if (c < KC - 1 || (K & 127) == 0) {
+#pragma unroll
+      for (int q = 0; q < XPT; ++q) xr[q] = ld16(xc + xoff[q]);
+    } else {  // the last, partial chunk: pieces past K read as zero (K % 16 == 0: a piece is all in or out)
+#pragma unroll
+      for (int q = 0; q < XPT; ++q) {
+        const int pc = (threadIdx.x + NTH * q) & 15;
+        xr[q] = 128 * c + 8 * pc < K ? ld16(xc + xoff[q]) : make_uint4(0, 0, 0, 0);
+      }
+    }
+  };
+  auto store_x = [&](uint16_t* slab) {
+#pragma unroll
+    for (int q = 0; q < XPT; ++q) *reinterpret_cast<uint4*>(slab + xlds[q]) = xr[q];
+  };
+
+  f32x4 acc[TM][TN];
+#pragma unroll
+  for (int i = 0; i < TM; ++i)
+#pragma unroll
+    for (int jj = 0; jj < TN; ++jj) acc[i][jj] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  // Per 32-k step: 8 activation fragments from LDS, 32 MFMAs; the weight
+  // fragments of the next step are dequantised meanwhile (software
+  // pipelined), and the scheduler is asked to interleave one MFMA with two
+  // of those VALU instructions, so the dequantisation hides under the MFMAs.
+  auto compute = [&](const WStage& S, const uint16_t* slab) {
+    float sc[TM][4];
+#pragma unroll
+    for (int i = 0; i < TM; ++i) scale4(S.sw[i], sc[i]);
+    bf16x8 a[TM], an[TM];
+#pragma unroll
+    for (int i = 0; i < TM; ++i) a[i] = dequant8(S.cw[i][0], sc[i][0]);
+#pragma unroll
+    for (int st = 0; st < 4; ++st) {
+      bf16x8 b[TN];
+#pragma unroll
+      for (int jj = 0; jj < TN; ++jj)
+        b[jj] = as_bf16x8(*reinterpret_cast<const uint4*>(slab + (16 * jj + li) * kXRow + 32 * st + 8 * lg));
+      if (st < 3) {
+#pragma unroll
+        for (int i = 0; i < TM; ++i) an[i] = dequant8(S.cw[i][st + 1], sc[i][st + 1]);
+      }
+#pragma unroll
+      for (int jj = 0; jj < TN; ++jj)
+#pragma unroll
+        for (int i = 0; i < TM; ++i) acc[i][jj] = mfma16x16x32(a[i], b[jj], acc[i][jj]);
+#pragma unroll
+      for (int g = 0; g < TM * TN; ++g) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // one MFMA
+        __builtin_amdgcn_sched_group_barrier(0x002, 2, 0);  // two VALU
+      }
+      if (st < 3) {
+#pragma unroll
+        for (int i = 0; i < TM; ++i) a[i] = an[i];
+      }
+    }
+  };
+
+  // chunk q is read from slab q % 2; after the barrier of iteration q the
+  // registers (chunk q + 1) go to the other slab and chunk q + 2 is loaded;
+  // weights of chunk q + D go into the stage chunk q used
+  WStage ws[D];
+#pragma unroll
+  for (int u = 0; u < D; ++u)
+    if (u < KC) load_w(u, ws[u]);
+  load_x(0);
+  store_x(xs[0]);
+  if (KC > 1) load_x(1);
+  for (int q0 = 0; q0 < KC; q0 += D) {
+#pragma unroll
+    for (int u = 0; u < D; ++u) {
+      const int q = q0 + u;
+      if (q >= KC) break;  // uniform across the workgroup
+      __syncthreads();     // slab q % 2 is complete; slab (q + 1) % 2 is no longer read
+      if (q + 1 < KC) {
+        store_x(xs[(u + 1) & 1]);
+        if (q + 2 < KC) load_x(q + 2);
+      }
+      compute(ws[u], xs[u & 1]);
+      if (q + D < KC) load_w(q + D, ws[u]);
+    }
+  }
+
+  // Epilogue: acc *= s_t, then t B^T is accumulated onto it by MFMA, 32
+  // ranks at a time, from LDS: the workgroup stages its 128 t rows (K-slices
+  // summed in order, split into bf16 hi + lo) and its 256 B rows in the freed
+  // slabs (rows padded to 80 B: conflict-free 16-byte reads).
+  const float st = *tensor_scale;
+  for_tiles<TM, TN>([&](auto I, auto J) { acc[I][J] *= st; });
+  if (r > 0) {
+    constexpr int LROW = 40;  // bf16 per staged row: 32 ranks + 8 of padding
+    uint16_t* bl = xs[0];                 // [256][LROW] B rows
+    uint16_t* th = bl + kPfRows * LROW;   // [128][LROW] t, high bf16 part
+    uint16_t* tlo = th + kPfTok * LROW;   // [128][LROW] t, low bf16 part
+    const int n0wg = rg * kPfRows;
+    const int64_t tstride = (int64_t)M * r;
+    for (int j0 = 0; j0 < r; j0 += 32) {
+      __syncthreads();  // the slabs (or the previous piece) are no longer read
+      for (int e = threadIdx.x; e < kPfTok * 32; e += NTH) {  // t piece: 128 tokens x 32 ranks
+        const int tok = e >> 5, jj = e & 31, m = m0 + tok, j = j0 + jj;
+        float v = 0.0f;
+        if (m < M && j < r)
+          for (int q = 0; q < tks; ++q) v += t[q * tstride + (int64_t)m * r + j];
+        const uint32_t h = f32_to_bf16(v);
+        th[tok * LROW + jj] = (uint16_t)h;
+        tlo[tok * LROW + jj] = (uint16_t)f32_to_bf16(v - __uint_as_float(h << 16));
+      }
+      for (int e = threadIdx.x; e < kPfRows * 32; e += NTH) {  // B piece: 256 rows x 32 ranks
+        const int row = e >> 5, jj = e & 31, n = n0wg + row, j = j0 + jj;
+        bl[row * LROW + jj] = (n < N && j < r) ? lb[(int64_t)n * r + j] : (uint16_t)0;
+      }
+      __syncthreads();
+      for_tiles<TM, TN>([&](auto I, auto J) {
+        const bf16x8 a = as_bf16x8(*reinterpret_cast<const uint4*>(bl + (wave * 64 + 16 * I + li) * LROW + 8 * lg));
+        const bf16x8 bh = as_bf16x8(*reinterpret_cast<const uint4*>(th + (16 * J + li) * LROW + 8 * lg));
+        const bf16x8 bo = as_bf16x8(*reinterpret_cast<const uint4*>(tlo + (16 * J + li) * LROW + 8 * lg));
+        acc[I][J] = mfma16x16x32(a, bh, acc[I][J]);
+        acc[I][J] = mfma16x16x32(a, bo, acc[I][J]);
+      });
+    }
+  }
+  // lane holds features n0 + 16 I + 4 lg + v of token m0 + 16 J + li
+  const bool nvec = (N & 3) == 0;
+  for_tiles<TM, TN>([&](auto I, auto J) {
+    const int m = m0 + 16 * J + li, nf = n0 + 16 * I + 4 * lg;
+    if (m < M) {
+      uint16_t* yp = y + (int64_t)m * N + nf;
+      const f32x4 v = acc[I][J];
+      if (nvec && nf + 3 < N) {
+        *reinterpret_cast<uint2*>(yp) = make_uint2(pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3]));
+      } else {
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+          if (nf + e < N) yp[e] = (uint16_t)f32_to_bf16(v[e]);
+      }
+    }
+  });
+}
+
+// ---------------------------------------------------------------------------
 // GEMV kernel for one or two tokens (VALU, no MFMA).
 //   One workgroup per 16-row weight tile; its WAVES waves take the 128-wide K
 //   chunks round-robin, U chunks per software-pipeline group (two register
@@ -918,6 +1142,7 @@ const char* fp4_linear_kernel_name(int64_t m, int64_t n, int64_t k, int64_t r) {
     while ((1 << wi) < gemv_waves(n, k)) ++wi;
     return kGemv[m - 1][wi];
   }
+  if (m > 128) return "prefill_kernel";
   if (use_splitk(m)) {
     const SplitkCfg sc = pick_splitk(m, n, k);
     static const char* const kSplitk[2][4] = {
@@ -948,6 +1173,14 @@ hipError_t launch_fp4_linear(const uint16_t* x, int64_t m, int64_t n, int64_t k,
   if (use_splitk(m))
     return launch_splitk(pick_splitk(m, n, k), stream, x, M, N, K, codes, scales, tensor_scale, t, tks, b, R, y, part,
                          counters);
+  if (m > 128) {
+    const int64_t gr = (n + kPfRows - 1) / kPfRows, gt = (m + kPfTok - 1) / kPfTok;
+    const int64_t supers = (gr + 7) / 8 * ((gt + 3) / 4);  // super-tiles of 8 x 4 workgroups, dealt to 8 XCDs
+    const int64_t grid = 8 * 32 * ((supers + 7) / 8);
+    hipLaunchKernelGGL(prefill_kernel, dim3((unsigned)grid), dim3(256), 0, stream, x, M, N, K, codes, scales,
+                       tensor_scale, t, tks, b, R, y);
+    return hipGetLastError();
+  }
   const SkinnyCfg cfg = pick_skinny(m, n, k);
   const dim3 grid((unsigned)((n + 16 * cfg.nt - 1) / (16 * cfg.nt)), (unsigned)((m + 16 * cfg.mt - 1) / (16 * cfg.mt)));
 #define FP4RL_SKINNY(MT_, NT_) \

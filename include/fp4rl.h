@@ -119,8 +119,9 @@ fp4rl_status fp4rl_nvfp4_to_tiled(const uint8_t* codes, const uint8_t* scales, i
  *                       + sum_j t[m][j] B[n][j] ),   t = lora_scale * x A^T.
  * x bf16 [m][k]; codes/scales/tensor_scale of an [n][k] matrix in the
  * FP4RL_TILED layout; A bf16 [r][k]; B bf16 [n][r]; y bf16 [m][n].
- * k % 16 == 0; 0 <= r <= 256; r == 0 or lora_a == lora_b == NULL means no
- * LoRA term. Accumulation is fp32; the output is rounded once to bf16.
+ * k % 16 == 0; m * k < 2^31; 0 <= r <= 256; r == 0 or lora_a == lora_b ==
+ * NULL means no LoRA term. Accumulation is fp32; the output is rounded once
+ * to bf16.
  * Launches the LoRA down-projection (when r > 0) and then the main kernel,
  * chosen by m (see fp4rl_fp4_linear_kernel_name).
  * Workspace: fp4rl_fp4_lora_linear_workspace(m, n, k, r) bytes (0 when

@@ -86,6 +86,21 @@ def test_split_k_shapes(m, n, k, r):
     _check(y, linear.lora_linear(x, *q, a, b, LORA_SCALE), f"{m}x{n}x{k} r{r}")
 
 
+PREFILL = [  # (m, n, k, r): more than 128 tokens (256-feature x 128-token workgroup tiles), ragged in every dim
+    (129, 16, 128, 0), (200, 270, 400, 8), (384, 512, 1024, 16), (1000, 520, 2064, 32), (2048, 300, 4096, 64),
+]
+
+
+@pytest.mark.parametrize("m,n,k,r", PREFILL)
+def test_prefill_shapes(m, n, k, r):
+    dev = device()
+    w, x, a, b = _case(m, n, k, r, seed=m * 13 + n * 7 + k, outliers=0.001)
+    q = nvfp4.quantize(w)
+    say(f"linear prefill m={m} n={n} k={k} r={r} ({fr.fp4_linear_kernel_name(m, n, k, r)})")
+    y = _run(dev, x, q, a, b, LORA_SCALE)
+    _check(y, linear.lora_linear(x, *q, a, b, LORA_SCALE), f"{m}x{n}x{k} r{r}")
+
+
 def test_workspace_reuse_across_shapes():
     """One zero-filled workspace serves a sequence of split-K and plain calls, twice over: every result
     equals the result with a fresh workspace, bit for bit (the counters are back at zero after each call)."""
