@@ -140,23 +140,34 @@ __global__ __launch_bounds__(kThreads) void aqn_rmsnorm_kernel(
 
 // Few rows (decode batches): the noise of d columns would cost each
 // workgroup far more than its rows, so workgroups split the columns instead.
-// Workgroup (slice, group) makes the noise of its kColSlice columns only, sums
-// the squares of its (up to kColRows) full rows — read again by every slice,
-// from L2 — and writes its slice of those rows. The row sums use the same
-// lane order and wave reduction as the row kernel above, so both give the
-// same result.
+// Workgroup (slice, group) makes the noise of its kColSlice columns only
+// (wave 0), while each of its waves loads one full row into registers — the
+// same row is loaded by every slice, mostly from L2 — sums its squares in the
+// same lane order and wave reduction as the row kernel above (so both give
+// the same result), and writes its slice of the row from those registers.
 constexpr int kColSlice = 256;  // columns per workgroup (64 Philox blocks)
-constexpr int kColRows = 16;    // rows per workgroup
 
 __global__ __launch_bounds__(kThreads) void aqn_rmsnorm_cols_kernel(
     const uint16_t* __restrict__ x, int m, int d, const float* __restrict__ w, float sigma, uint32_t seed_lo,
     uint32_t seed_hi, uint32_t step_lo, uint32_t step_hi, uint32_t norm_id, float eps, uint16_t* __restrict__ y,
     float* __restrict__ w_noise_out) {
   __shared__ __align__(16) float wn[kColSlice];
-  __shared__ float inv[kColRows];
   const int col0 = blockIdx.x * kColSlice;
-  const int row0 = blockIdx.y * kColRows;
-  const int rows = min(kColRows, m - row0);
+  const int lane = threadIdx.x & (kWave - 1);
+  const int wv = threadIdx.x / kWave;
+  const int row = blockIdx.y * kRowsPerWg + wv;
+  const int nv = d >> 3;  // 16-byte chunks of 8 bf16 per row
+  // this wave's row, first kRegChunks chunks per lane in registers
+  uint4 reg[kRegChunks];
+  float ss = 0.0f;
+  const uint4* xv = reinterpret_cast<const uint4*>(x + (int64_t)min(row, max(m - 1, 0)) * d);
+  if (row < m) {
+#pragma unroll
+    for (int c = 0; c < kRegChunks; ++c) {
+      const int vi = lane + kWave * c;
+      if (vi < nv) reg[c] = xv[vi];
+    }
+  }
   if (threadIdx.x < kColSlice / 4) {
     const int q = col0 / 4 + threadIdx.x;  // Philox block of columns 4 q .. 4 q + 3
     const uint4 o = philox4x32_10(make_uint4((uint32_t)q, norm_id, step_lo, step_hi), seed_lo, seed_hi);
@@ -171,29 +182,23 @@ __global__ __launch_bounds__(kThreads) void aqn_rmsnorm_cols_kernel(
       if (i < d && blockIdx.y == 0 && w_noise_out != nullptr) w_noise_out[i] = v;
     }
   }
-  const int lane = threadIdx.x & (kWave - 1);
-  const int wv = threadIdx.x / kWave;
-  const float inv_d = 1.0f / (float)d;
-  const int nv = d >> 3;  // 16-byte chunks of 8 bf16 per row
-  for (int r = wv; r < rows; r += kRowsPerWg) {
-    const uint4* xv = reinterpret_cast<const uint4*>(x + (int64_t)(row0 + r) * d);
-    float ss = 0.0f;
-    for (int vi = lane; vi < nv; vi += kWave) ss += sumsq8(xv[vi]);
-    ss = wave_sum(ss);
-    if (lane == 0) inv[r] = 1.0f / sqrtf(ss * inv_d + eps);
-  }
   __syncthreads();
-  // this slice of every row: kColSlice / 8 chunks per row
-  constexpr int CPR = kColSlice / 8;
-  for (int e = threadIdx.x; e < rows * CPR; e += kThreads) {
-    const int r = e / CPR, ch = e - r * CPR;
-    const int vi = col0 / 8 + ch;
-    if (vi < nv) {
-      const int64_t off = (int64_t)(row0 + r) * d;
-      const uint4 v = *reinterpret_cast<const uint4*>(x + off + 8 * vi);
-      *reinterpret_cast<uint4*>(y + off + 8 * vi) = norm8(v, wn + 8 * ch, inv[r]);
-    }
+  if (row >= m) return;
+#pragma unroll
+  for (int c = 0; c < kRegChunks; ++c)
+    if (lane + kWave * c < nv) ss += sumsq8(reg[c]);
+  for (int vi = lane + kWave * kRegChunks; vi < nv; vi += kWave) ss += sumsq8(xv[vi]);
+  ss = wave_sum(ss);
+  const float inv = 1.0f / sqrtf(ss * (1.0f / (float)d) + eps);
+  uint4* yv = reinterpret_cast<uint4*>(y + (int64_t)row * d);
+  const int v0 = col0 / 8, v1 = min(nv, v0 + kColSlice / 8);  // this slice's chunks
+#pragma unroll
+  for (int c = 0; c < kRegChunks; ++c) {
+    const int vi = lane + kWave * c;
+    if (vi >= v0 && vi < v1) yv[vi] = norm8(reg[c], wn + 8 * (vi - v0), inv);
   }
+  for (int vi = lane + kWave * kRegChunks; vi < v1; vi += kWave)  // rows wider than the registers hold
+    if (vi >= v0) yv[vi] = norm8(xv[vi], wn + 8 * (vi - v0), inv);
 }
 
 __global__ void philox_words_kernel(uint32_t seed_lo, uint32_t seed_hi, uint32_t step_lo,
@@ -214,7 +219,7 @@ hipError_t launch_aqn_rmsnorm(const uint16_t* x, int64_t m, int64_t d, const flo
   if (vec && m <= 256) {  // few rows: split the columns (and the noise) over workgroups
     // m == 0 still runs one row group: the noisy weight is written even without rows
     const dim3 grid((unsigned)((d + kColSlice - 1) / kColSlice),
-                    (unsigned)std::max<int64_t>(1, (m + kColRows - 1) / kColRows));
+                    (unsigned)std::max<int64_t>(1, (m + kRowsPerWg - 1) / kRowsPerWg));
     hipLaunchKernelGGL(aqn_rmsnorm_cols_kernel, grid, dim3(kThreads), 0, stream, x, (int)m, (int)d, w, sigma, sl0,
                        sh0, tl0, th0, norm_id, eps, y, w_noise_out);
     return hipGetLastError();

@@ -982,11 +982,10 @@ hipError_t run_skinny_w(int w, dim3 grid, hipStream_t st, const uint16_t* x, int
 int lora_splits(int64_t m, int64_t k, int64_t r) {
   (void)r;
   if (m > 128) return 1;  // prefill: token tiles already fill the chip
-  // The linear's epilogue re-reads every slice for its 16*mt tokens: keep
-  // slices * mt <= 8 so that stays a few KB per workgroup.
-  const int mt = m <= 16 ? 1 : m <= 32 ? 2 : m <= 64 ? 4 : 8;
-  const int64_t by_k = std::max<int64_t>(1, k / 512);  // at least 512 k per slice
-  return (int)std::min<int64_t>(8 / mt, by_k);
+  // Up to 8 K-slices of at least 512 k (the linear's epilogue adds them in
+  // order): enough workgroups for a long K without a separate reduction.
+  const int64_t by_k = std::max<int64_t>(1, k / 512);
+  return (int)std::min<int64_t>(8, by_k);
 }
 
 static int64_t slice_len(int64_t k, int splits) { return ((k + splits - 1) / splits + 31) / 32 * 32; }
