@@ -1016,10 +1016,13 @@ hipError_t launch_lora_reduce(const float* part, int slices, int64_t count, floa
 
 // GEMV path: one or two tokens, when the staged tokens and LoRA operands fit
 // in 64 KB of LDS.
+// Waves per row tile: as many as keep the whole grid resident in one round
+// (about 4096 waves), so every wave issues all its loads at once and the
+// kernel pays its load -> reduce -> store latency chain once.
 static int gemv_waves(int64_t n, int64_t k) {
   const int64_t rt = (n + 15) / 16, kc = (k + 127) / 128;
   int w = 1;
-  while (w < 16 && w < kc && rt * w < 8192) w *= 2;
+  while (w < 16 && w < kc && rt * w * 2 <= 4096) w *= 2;
   return w;
 }
 
@@ -1030,7 +1033,7 @@ static bool use_gemv(int64_t m, int64_t n, int64_t k, int64_t r) {
 template <int MTOK, int W>
 hipError_t run_gemv(hipStream_t st, const uint16_t* x, int M, int N, int K, const uint8_t* codes, const uint8_t* scales,
                     const float* ts, const float* t, int tks, const uint16_t* b, int r, uint16_t* y) {
-  constexpr int U = W >= 16 ? 4 : 8;
+  constexpr int U = 4;
   const size_t lds = gemv_lds_bytes(MTOK, K, r, W);
   hipLaunchKernelGGL((gemv_kernel<MTOK, W, U>), dim3((unsigned)((N + 15) / 16)), dim3(W * kWave), lds, st, x, M, N, K,
                      codes, scales, ts, t, tks, b, r, y);
@@ -1132,9 +1135,9 @@ const char* fp4_linear_kernel_name(int64_t m, int64_t n, int64_t k, int64_t r) {
 #undef FP4RL_NAME_ROW
   };
   static const char* const kGemv[2][5] = {
-      {"gemv_kernel<1, 1, 8>", "gemv_kernel<1, 2, 8>", "gemv_kernel<1, 4, 8>", "gemv_kernel<1, 8, 8>",
+      {"gemv_kernel<1, 1, 4>", "gemv_kernel<1, 2, 4>", "gemv_kernel<1, 4, 4>", "gemv_kernel<1, 8, 4>",
        "gemv_kernel<1, 16, 4>"},
-      {"gemv_kernel<2, 1, 8>", "gemv_kernel<2, 2, 8>", "gemv_kernel<2, 4, 8>", "gemv_kernel<2, 8, 8>",
+      {"gemv_kernel<2, 1, 4>", "gemv_kernel<2, 2, 4>", "gemv_kernel<2, 4, 4>", "gemv_kernel<2, 8, 4>",
        "gemv_kernel<2, 16, 4>"}};
   if (use_gemv(m, n, k, r)) {
     int wi = 0;
