@@ -420,9 +420,10 @@ __global__ __launch_bounds__(W * kWave) void splitk_kernel(
     const int c = chunk_of(q);
 #pragma unroll
     for (int i = 0; i < TM; ++i) {
-      const uint4 v = ld_nt16(cbase + (int64_t)(toff[i] + c) * 1024 + clane);
+      // plain (cached) loads: the token groups of a row group reuse these tiles from L2
+      const uint4 v = ld16(cbase + (int64_t)(toff[i] + c) * 1024 + clane);
       S.cw[i][0] = v.x; S.cw[i][1] = v.y; S.cw[i][2] = v.z; S.cw[i][3] = v.w;
-      S.sw[i] = __builtin_nontemporal_load(reinterpret_cast<const uint32_t*>(sbase + (int64_t)(toff[i] + c) * 128 + slane));
+      S.sw[i] = *reinterpret_cast<const uint32_t*>(sbase + (int64_t)(toff[i] + c) * 128 + slane);
     }
   };
   auto load_x = [&](int q, XStage& S) {
@@ -473,22 +474,23 @@ __global__ __launch_bounds__(W * kWave) void splitk_kernel(
   // ring is unrolled so every stage lives in fixed registers. The slab is
   // rewritten only after this wave's reads of it were issued (LDS operations
   // of one wave complete in order).
-  constexpr int D = 4;
+  constexpr int D = 3, UNR = 6;  // weight stages; unrolled by lcm(D, 2) so both rings use fixed registers
   WStage ws[D];
-  XStage xr;
+  XStage xr[2];  // activations of chunks q + 1 and q + 2 in flight while chunk q is computed
 #pragma unroll
   for (int u = 0; u < D; ++u)
     if (u < mine) load_w(u, ws[u]);
-  if (mine > 0) load_x(0, xr);
-  for (int q0 = 0; q0 < mine; q0 += D) {
+  if (mine > 0) load_x(0, xr[0]);
+  if (mine > 1) load_x(1, xr[1]);
+  for (int q0 = 0; q0 < mine; q0 += UNR) {
 #pragma unroll
-    for (int u = 0; u < D; ++u) {
+    for (int u = 0; u < UNR; ++u) {
       const int q = q0 + u;
       if (q >= mine) break;  // uniform across the wave
-      store_x(xr);
-      if (q + 1 < mine) load_x(q + 1, xr);
-      compute(ws[u]);
-      if (q + D < mine) load_w(q + D, ws[u]);
+      store_x(xr[u & 1]);
+      if (q + 2 < mine) load_x(q + 2, xr[u & 1]);
+      compute(ws[u % D]);
+      if (q + D < mine) load_w(q + D, ws[u % D]);
     }
   }
 
@@ -572,9 +574,9 @@ __global__ __launch_bounds__(W * kWave) void splitk_kernel(
 
 // ---------------------------------------------------------------------------
 // Prefill GEMM (M > 128 tokens): a workgroup computes 256 output features x
-// 128 tokens over all of K; wave w owns features 64 w .. 64 w + 63 (TM = 4
-// row tiles) against all 8 token tiles, so one dequantised weight fragment
-// feeds 8 MFMAs and one activation fragment 4.
+// 128 tokens over all of K; each of its 256 / (16 TM) waves owns TM row tiles
+// (16 TM features) against all 8 token tiles, so one dequantised weight
+// fragment feeds 8 MFMAs and one activation fragment TM.
 //   Activation chunks (128 tokens x 128 k, 32 KB) are loaded by all threads
 //   with consecutive threads on consecutive 16-byte pieces of a token row,
 //   held one chunk ahead in registers and written to one of two LDS slabs
@@ -588,11 +590,12 @@ __global__ __launch_bounds__(W * kWave) void splitk_kernel(
 // ---------------------------------------------------------------------------
 constexpr int kPfRows = 256, kPfTok = 128;
 
-__global__ __launch_bounds__(256) void prefill_kernel(
+template <int TM>
+__global__ __launch_bounds__(kPfRows / 16 / TM * kWave) void prefill_kernel(
     const uint16_t* __restrict__ x, int M, int N, int K, const uint8_t* __restrict__ codes,
     const uint8_t* __restrict__ scales, const float* __restrict__ tensor_scale, const float* __restrict__ t, int tks,
     const uint16_t* __restrict__ lb, int r, uint16_t* __restrict__ y) {
-  constexpr int TM = 4, TN = 8, W = 4, D = 2;
+  constexpr int TN = 8, W = kPfRows / 16 / TM, D = 2;
   constexpr int NTH = W * kWave;
   constexpr int XPT = kPfTok * 16 / NTH;  // 16-byte activation pieces per thread and chunk (8)
   __shared__ __align__(16) uint16_t xs[2][kPfTok * kXRow];
@@ -618,14 +621,21 @@ __global__ __launch_bounds__(256) void prefill_kernel(
   int toff[TM];  // row tiles past the matrix are clamped to the last (never stored)
 #pragma unroll
   for (int i = 0; i < TM; ++i) toff[i] = (min(rt0 + i, RT - 1) - rt0) * KC;
-  uint32_t xoff[XPT];  // bytes; tokens past M clamped to the last one (never stored)
-  uint32_t xlds[XPT];  // bf16 units
-#pragma unroll
-  for (int q = 0; q < XPT; ++q) {
-    const int p = threadIdx.x + NTH * q, row = p >> 4, pc = p & 15;
-    xoff[q] = 2u * ((uint32_t)min(m0 + row, M - 1) * (uint32_t)K + 8 * pc);
-    xlds[q] = row * kXRow + 8 * pc;
-  }
+  // activation piece q of this thread: token row (threadIdx.x >> 4) + XR q
+  // (XR = threads / 16), 16 bytes at 16 (threadIdx.x & 15) of the chunk;
+  // tokens past M are clamped to the last one (never stored). Full token
+  // groups use a constant stride.
+  constexpr int XR = NTH / 16;
+  static_assert(XPT * XR == kPfTok, "the pieces of a chunk cover its token rows");
+  const int xrow0 = threadIdx.x >> 4, xpc = threadIdx.x & 15;
+  const bool xfull = m0 + kPfTok <= M;
+  const uint32_t xoff0 = 2u * ((uint32_t)min(m0 + xrow0, M - 1) * (uint32_t)K + 8 * xpc);
+  const uint32_t xstride = 2u * XR * (uint32_t)K;  // XR token rows
+  auto xoff = [&](int q) -> uint32_t {
+    return xfull ? xoff0 + (uint32_t)q * xstride
+                 : 2u * ((uint32_t)min(m0 + xrow0 + XR * q, M - 1) * (uint32_t)K + 8 * xpc);
+  };
+  const uint32_t xlds0 = xrow0 * kXRow + 8 * xpc;  // bf16 units; piece q adds XR q rows
 
   struct WStage {
     uint32_t cw[TM][4];
@@ -634,28 +644,28 @@ __global__ __launch_bounds__(256) void prefill_kernel(
   auto load_w = [&](int c, WStage& S) {
 #pragma unroll
     for (int i = 0; i < TM; ++i) {
-      const uint4 v = ld_nt16(cbase + (int64_t)(toff[i] + c) * 1024 + clane);
+      // plain (cached) loads: the other token groups of the super-tile reuse these tiles from L2
+      const uint4 v = ld16(cbase + (int64_t)(toff[i] + c) * 1024 + clane);
       S.cw[i][0] = v.x; S.cw[i][1] = v.y; S.cw[i][2] = v.z; S.cw[i][3] = v.w;
-      S.sw[i] = __builtin_nontemporal_load(reinterpret_cast<const uint32_t*>(sbase + (int64_t)(toff[i] + c) * 128 + slane));
+      S.sw[i] = *reinterpret_cast<const uint32_t*>(sbase + (int64_t)(toff[i] + c) * 128 + slane);
     }
   };
-  uint4 xr[XPT];
-  auto load_x = [&](int c) {
+  struct XStage {
+    uint4 v[XPT];
+  };
+  auto load_x = [&](int c, XStage& X) {
     const uint8_t* xc = reinterpret_cast<const uint8_t*>(x + 128 * c);  // uniform
     if (c < KC - 1 || (K & 127) == 0) {
 #pragma unroll
-      for (int q = 0; q < XPT; ++q) xr[q] = ld16(xc + xoff[q]);
+      for (int q = 0; q < XPT; ++q) X.v[q] = ld16(xc + xoff(q));
     } else {  // the last, partial chunk: pieces past K read as zero (K % 16 == 0: a piece is all in or out)
 #pragma unroll
-      for (int q = 0; q < XPT; ++q) {
-        const int pc = (threadIdx.x + NTH * q) & 15;
-        xr[q] = 128 * c + 8 * pc < K ? ld16(xc + xoff[q]) : make_uint4(0, 0, 0, 0);
-      }
+      for (int q = 0; q < XPT; ++q) X.v[q] = 128 * c + 8 * xpc < K ? ld16(xc + xoff(q)) : make_uint4(0, 0, 0, 0);
     }
   };
-  auto store_x = [&](uint16_t* slab) {
+  auto store_x = [&](const XStage& X, uint16_t* slab) {
 #pragma unroll
-    for (int q = 0; q < XPT; ++q) *reinterpret_cast<uint4*>(slab + xlds[q]) = xr[q];
+    for (int q = 0; q < XPT; ++q) *reinterpret_cast<uint4*>(slab + xlds0 + q * XR * kXRow) = X.v[q];
   };
 
   f32x4 acc[TM][TN];
@@ -702,15 +712,18 @@ __global__ __launch_bounds__(256) void prefill_kernel(
   };
 
   // chunk q is read from slab q % 2; after the barrier of iteration q the
-  // registers (chunk q + 1) go to the other slab and chunk q + 2 is loaded;
-  // weights of chunk q + D go into the stage chunk q used
+  // register stage holding chunk q + 1 goes to the other slab and is reloaded
+  // with chunk q + 3 (two iterations to arrive); weights of chunk q + D go
+  // into the stage chunk q used
   WStage ws[D];
+  XStage xr[2];
 #pragma unroll
   for (int u = 0; u < D; ++u)
     if (u < KC) load_w(u, ws[u]);
-  load_x(0);
-  store_x(xs[0]);
-  if (KC > 1) load_x(1);
+  load_x(0, xr[0]);
+  if (KC > 1) load_x(1, xr[1]);
+  store_x(xr[0], xs[0]);
+  if (KC > 2) load_x(2, xr[0]);
   for (int q0 = 0; q0 < KC; q0 += D) {
 #pragma unroll
     for (int u = 0; u < D; ++u) {
@@ -718,8 +731,8 @@ __global__ __launch_bounds__(256) void prefill_kernel(
       if (q >= KC) break;  // uniform across the workgroup
       __syncthreads();     // slab q % 2 is complete; slab (q + 1) % 2 is no longer read
       if (q + 1 < KC) {
-        store_x(xs[(u + 1) & 1]);
-        if (q + 2 < KC) load_x(q + 2);
+        store_x(xr[(u + 1) & 1], xs[(u + 1) & 1]);
+        if (q + 3 < KC) load_x(q + 3, xr[(u + 1) & 1]);
       }
       compute(ws[u], xs[u & 1]);
       if (q + D < KC) load_w(q + D, ws[u]);
@@ -756,7 +769,7 @@ __global__ __launch_bounds__(256) void prefill_kernel(
       }
       __syncthreads();
       for_tiles<TM, TN>([&](auto I, auto J) {
-        const bf16x8 a = as_bf16x8(*reinterpret_cast<const uint4*>(bl + (wave * 64 + 16 * I + li) * LROW + 8 * lg));
+        const bf16x8 a = as_bf16x8(*reinterpret_cast<const uint4*>(bl + (wave * 16 * TM + 16 * I + li) * LROW + 8 * lg));
         const bf16x8 bh = as_bf16x8(*reinterpret_cast<const uint4*>(th + (16 * J + li) * LROW + 8 * lg));
         const bf16x8 bo = as_bf16x8(*reinterpret_cast<const uint4*>(tlo + (16 * J + li) * LROW + 8 * lg));
         acc[I][J] = mfma16x16x32(a, bh, acc[I][J]);
@@ -1144,7 +1157,7 @@ const char* fp4_linear_kernel_name(int64_t m, int64_t n, int64_t k, int64_t r) {
     while ((1 << wi) < gemv_waves(n, k)) ++wi;
     return kGemv[m - 1][wi];
   }
-  if (m > 128) return "prefill_kernel";
+  if (m > 128) return "prefill_kernel<2>";
   if (use_splitk(m)) {
     const SplitkCfg sc = pick_splitk(m, n, k);
     static const char* const kSplitk[2][4] = {
@@ -1179,7 +1192,20 @@ hipError_t launch_fp4_linear(const uint16_t* x, int64_t m, int64_t n, int64_t k,
     const int64_t gr = (n + kPfRows - 1) / kPfRows, gt = (m + kPfTok - 1) / kPfTok;
     const int64_t supers = (gr + 7) / 8 * ((gt + 3) / 4);  // super-tiles of 8 x 4 workgroups, dealt to 8 XCDs
     const int64_t grid = 8 * 32 * ((supers + 7) / 8);
-    hipLaunchKernelGGL(prefill_kernel, dim3((unsigned)grid), dim3(256), 0, stream, x, M, N, K, codes, scales,
+#ifdef FP4RL_TUNING
+    if (g_tune_w == 4 || g_tune_w == 1) {
+      if (g_tune_w == 4)
+        hipLaunchKernelGGL(prefill_kernel<4>, dim3((unsigned)grid), dim3(256), 0, stream, x, M, N, K, codes, scales,
+                           tensor_scale, t, tks, b, R, y);
+      else
+        hipLaunchKernelGGL(prefill_kernel<1>, dim3((unsigned)grid), dim3(1024), 0, stream, x, M, N, K, codes, scales,
+                           tensor_scale, t, tks, b, R, y);
+      return hipGetLastError();
+    }
+#endif
+    // 8 waves of 32 features x 128 tokens: two waves per SIMD hide each
+    // other's LDS, barrier and load waits
+    hipLaunchKernelGGL(prefill_kernel<2>, dim3((unsigned)grid), dim3(512), 0, stream, x, M, N, K, codes, scales,
                        tensor_scale, t, tks, b, R, y);
     return hipGetLastError();
   }
