@@ -35,6 +35,7 @@ HBM_PEAK_GBS = 8000.0            # MI355X HBM3E, published
 BF16_PEAK_TFLOPS = 2500.0        # MI355X dense bf16 MFMA, published
 TOKENS = (1, 8, 32, 64)
 RANK = 32
+RANK_32B = 64
 LORA_SCALE = 2.0
 SIGMA, EPS = 1e-2, 1e-6
 COPIES = 4
@@ -339,14 +340,10 @@ def main():
     progress("building weights")
     # weights: COPIES distinct NVFP4 layers, shared LoRA adapters, AQN weights
     layers = []
-    fp32_first = None
     for c in range(COPIES):
         layer, fp32 = build_layer(torch, fr, dev, shapes, seed=1 + c)
         layers.append(layer)
-        if c == 0 and not args.no_extras:
-            fp32_first = fp32
-        else:
-            del fp32
+        del fp32
     torch.cuda.synchronize()
     g = torch.Generator(device=dev)
     g.manual_seed(11)
@@ -497,7 +494,7 @@ def main():
     extras = {}
     if not args.no_extras:
         progress("prefill, quantiser and AQN timings")
-        extras = run_extras(torch, fr, dev, shapes, layers[0], lora, fp32_first)
+        extras = run_extras(torch, fr, dev, shapes, layers[0], lora, None)
 
     out = {
         "metric": METRIC, "value": round(value, 3), "unit": "GB/s", "n_gpus": 1, "steps": args.steps,
@@ -551,22 +548,36 @@ def run_extras(torch, fr, dev, shapes, layer, lora, fp32):
                       "frac_of_bf16_peak": round(flops / dt / 1e12 / BF16_PEAK_TFLOPS, 4)}
     del xs, ys
 
-    # quantiser: the layer's fp32 weights -> NVFP4 (two reads of W, one write of codes+scales)
-    if fp32 is not None:
-        outs = {name: fr.nvfp4_quantize(w) for name, w in fp32.items()}
+    # quantiser on 14B shapes: one layer's five matrices, 0.02 t(3) weights with
+    # 1e-4 outliers x50, fp32 (and bf16) input -> NVFP4; the 48 layers repeat
+    # these shapes, so the 48-layer time is this layer's time x 48
+    from workloads import QWEN25_14B, student_t3_weights_torch, tensor_seed
+    del fp32
+    w14 = {name: student_t3_weights_torch((n, k), tensor_seed(4, 0, name), dev) for name, (n, k) in QWEN25_14B.items()}
+    params = sum(n * k for n, k in QWEN25_14B.values())
+    for dt in ("fp32", "bf16"):
+        ws = w14 if dt == "fp32" else {name: w.to(torch.bfloat16) for name, w in w14.items()}
+        outs = {name: fr.nvfp4_quantize(w) for name, w in ws.items()}
         torch.cuda.synchronize()
-        t0 = time.perf_counter()
         reps = 3
+        t0 = time.perf_counter()
         for _ in range(reps):
-            for name, w in fp32.items():
+            for name, w in ws.items():
                 fr.nvfp4_quantize(w, out=outs[name])
         torch.cuda.synchronize()
-        dt = (time.perf_counter() - t0) / reps
-        params = sum(n * k for n, k in shapes.values())
-        two_pass = params * (2 * 4 + 0.5625)
-        res["quantize"] = {"input": "fp32", "params": params, "ms_per_layer": round(dt * 1e3, 3),
-                           "GB/s_two_pass": round(two_pass / dt / 1e9, 1),
-                           "frac_of_hbm": round(two_pass / dt / 1e9 / HBM_PEAK_GBS, 4)}
+        dt_s = (time.perf_counter() - t0) / reps
+        esz = 4 if dt == "fp32" else 2
+        two_pass = params * (2 * esz + 0.5625)
+        res[f"quantize_{dt}"] = {"shapes": "Qwen2.5-14B layer (qkv 7168x5120, o 5120x5120, gate/up 13824x5120, "
+                                           "down 5120x13824), 0.02 t(3) + 1e-4 outliers x50",
+                                 "params_per_layer": params, "ms_per_layer": round(dt_s * 1e3, 3),
+                                 "ms_48_layers": round(dt_s * 48e3, 2),
+                                 "GB/s_two_pass": round(two_pass / dt_s / 1e9, 1),
+                                 "frac_of_hbm": round(two_pass / dt_s / 1e9 / HBM_PEAK_GBS, 4)}
+        del outs
+        if dt == "bf16":
+            del ws
+    del w14
     # AQN RMSNorm: 65536 x 5120 bf16 tokens
     m, d = 65536, 5120
     x = torch.randn((m, d), generator=g, device=dev).to(torch.bfloat16)
@@ -582,7 +593,72 @@ def run_extras(torch, fr, dev, shapes, layer, lora, fp32):
     dt = (time.perf_counter() - t0) / reps
     res["aqn_rmsnorm"] = {"shape": [m, d], "us_per_call": round(dt * 1e6, 2),
                           "GB/s": round(4 * m * d / dt / 1e9, 1), "frac_of_hbm": round(4 * m * d / dt / 1e9 / HBM_PEAK_GBS, 4)}
+    del x, y
+    res["decode_32b"] = run_decode_32b(torch, fr, dev)
     return res
+
+
+def run_decode_32b(torch, fr, dev, layers=64, m=128, r=RANK_32B):
+    """Qwen2.5-32B-shaped decode over all 64 layers' linears (NVFP4, ~17.5 GB resident), M = 128, r = 64,
+    AQN RMSNorm before qkv and before gate/up in each layer. Attention and SiLU are not on this path, so
+    o and down read fresh synthetic activations. One pass is captured as a HIP graph and replayed."""
+    from workloads import QWEN25_32B, tensor_seed
+    shapes = QWEN25_32B
+    hidden, inter = 5120, 27648
+    g = torch.Generator(device=dev)
+    wts, lora = [], []
+    for layer in range(layers):
+        wl, ll = {}, {}
+        for name, (n, k) in shapes.items():
+            g.manual_seed(tensor_seed(3, layer, name))
+            w = torch.randn((n, k), generator=g, device=dev, dtype=torch.float32).mul_(0.02)
+            wl[name] = fr.nvfp4_quantize(w)
+            del w
+            ll[name] = (torch.randn((r, k), generator=g, device=dev).mul_(0.01).to(torch.bfloat16),
+                        torch.randn((n, r), generator=g, device=dev).mul_(0.01).to(torch.bfloat16))
+        wts.append(wl)
+        lora.append(ll)
+    g.manual_seed(3)
+    xh, xo, xr = (torch.randn((m, hidden), generator=g, device=dev).to(torch.bfloat16) for _ in range(3))
+    xd = torch.randn((m, inter), generator=g, device=dev).to(torch.bfloat16)
+    h1, h2 = torch.empty_like(xh), torch.empty_like(xr)
+    wn = torch.ones(hidden, dtype=torch.float32, device=dev)
+    ys = {name: torch.empty((m, n), dtype=torch.bfloat16, device=dev) for name, (n, k) in shapes.items()}
+    wsb = max(fr.fp4_lora_linear_workspace_bytes(m, n, k, r) for n, k in shapes.values())
+    ws = fr.linear_workspace(wsb, dev)
+    inp = {"qkv": h1, "o": xo, "gate": h2, "up": h2, "down": xd}
+
+    def one_pass():
+        for layer in range(layers):
+            fr.aqn_rmsnorm(xh, wn, SIGMA, 3, 0, 2 * layer, EPS, out=h1)
+            fr.aqn_rmsnorm(xr, wn, SIGMA, 3, 0, 2 * layer + 1, EPS, out=h2)
+            for name in ("qkv", "o", "gate", "up", "down"):
+                a, b = lora[layer][name]
+                fr.fp4_lora_linear(inp[name], wts[layer][name], a, b, LORA_SCALE, out=ys[name], workspace=ws)
+
+    one_pass()
+    torch.cuda.synchronize()
+    gr = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(gr):
+        one_pass()
+    gr.replay()
+    torch.cuda.synchronize()
+    reps = 3
+    t0 = time.perf_counter()
+    for _ in range(reps):
+        gr.replay()
+    torch.cuda.synchronize()
+    dt = (time.perf_counter() - t0) / reps
+    wbytes = layers * sum(nvfp4_bytes(n, k) for n, k in shapes.values())
+    flops = layers * sum(linear_flops(m, n, k, r) for n, k in shapes.values())
+    total_bytes = layers * (sum(nvfp4_bytes(n, k) + 2 * r * (k + n) + 2 * m * (k + n) for n, k in shapes.values())
+                            + 2 * 4 * m * hidden)
+    roof_s = max(total_bytes / (HBM_PEAK_GBS * 1e9), flops / (BF16_PEAK_TFLOPS * 1e12))
+    del gr, wts, lora
+    return {"layers": layers, "M": m, "lora_rank": r, "ms_per_pass": round(dt * 1e3, 3),
+            "weight_GB/s": round(wbytes / dt / 1e9, 1), "tflops": round(flops / dt / 1e12, 1),
+            "nvfp4_weight_bytes": wbytes, "roofline_ms": round(roof_s * 1e3, 3),
+            "frac_of_roofline": round(roof_s / dt, 4)}
 
 
 if __name__ == "__main__":

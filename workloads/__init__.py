@@ -93,6 +93,24 @@ def lora_bf16(r: int, k: int, n: int, seed: int, std: float = LORA_STD):
     return bf16_bits(a), bf16_bits(b)
 
 
+def student_t3_weights_torch(shape, seed: int, device, scale: float = 0.02,
+                             outlier_p: float = 1e-4, outlier_gain: float = 50.0):
+    """The same heavy-tailed recipe drawn on a device with torch's generator (for timing runs):
+    0.02 * z0 / sqrt((z1^2 + z2^2 + z3^2) / 3), Bernoulli(1e-4) positions x50. fp32."""
+    import torch
+    g = torch.Generator(device=device)
+    g.manual_seed(seed)
+    z0 = torch.randn(shape, generator=g, device=device, dtype=torch.float32)
+    den = torch.zeros(shape, device=device, dtype=torch.float32)
+    for _ in range(3):
+        den.add_(torch.randn(shape, generator=g, device=device, dtype=torch.float32).square_())
+    w = z0.div_(den.div_(3.0).sqrt_()).mul_(scale)
+    del den
+    hit = torch.rand(shape, generator=g, device=device) < outlier_p
+    w[hit] *= outlier_gain
+    return w
+
+
 def student_t3_weights(shape, seed: int, scale: float = 0.02,
                        outlier_p: float = 1e-4, outlier_gain: float = 50.0) -> np.ndarray:
     """Heavy-tailed weights: 0.02 * t(nu=3), Bernoulli(1e-4) positions x50.
