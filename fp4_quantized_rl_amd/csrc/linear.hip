@@ -953,6 +953,16 @@ struct SkinnyCfg {
 // within a 64 KB LDS reduction buffer (waves * nt * mt <= 64).
 SkinnyCfg pick_skinny(int64_t m, int64_t n, int64_t k) {
   const int mt = m <= 16 ? 1 : m <= 32 ? 2 : m <= 64 ? 4 : 8;
+  if (m <= 16 && n >= 4096) {
+    // wide matrices: two row tiles share each activation fragment (halves the
+    // activation re-reads); 4 waves when that still leaves >= 512 workgroups
+    const int64_t groups = (n + 31) / 32;
+    const int64_t kc = (k + 127) / 128;
+    const int w = (int)std::min<int64_t>(groups >= 512 ? 4 : 8, std::max<int64_t>(1, kc));
+    int wp = 1;
+    while (wp * 2 <= w) wp *= 2;
+    return SkinnyCfg{1, 2, wp};
+  }
   const int nt = m <= 16 ? 1 : 2;
   const int64_t gy = (m + 16 * mt - 1) / (16 * mt);
   const int64_t groups = (n + 16 * nt - 1) / (16 * nt) * gy;
@@ -1214,7 +1224,7 @@ hipError_t launch_fp4_linear(const uint16_t* x, int64_t m, int64_t n, int64_t k,
 #define FP4RL_SKINNY(MT_, NT_) \
   if (cfg.mt == MT_ && cfg.nt == NT_) \
     return run_skinny_w<MT_, NT_>(cfg.waves, grid, stream, x, M, N, K, codes, scales, tensor_scale, t, tks, b, R, y);
-  FP4RL_SKINNY(1, 1) FP4RL_SKINNY(2, 2) FP4RL_SKINNY(4, 2) FP4RL_SKINNY(8, 2)
+  FP4RL_SKINNY(1, 1) FP4RL_SKINNY(1, 2) FP4RL_SKINNY(2, 2) FP4RL_SKINNY(4, 2) FP4RL_SKINNY(8, 2)
 #undef FP4RL_SKINNY
   return hipErrorInvalidValue;
 }
