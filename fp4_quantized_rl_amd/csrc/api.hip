@@ -256,7 +256,7 @@ fp4rl_status fp4rl_fp4_linear_lora_up(const uint16_t* x, int64_t m, int64_t n, i
   float* part = pbytes ? reinterpret_cast<float*>(ws + fp4rl::kLinearCounterBytes) : nullptr;
   uint32_t* counters = pbytes ? reinterpret_cast<uint32_t*>(ws) : nullptr;
   return launched(fp4rl::launch_fp4_linear(x, m, n, k, codes, scales, tensor_scale, r > 0 ? t : nullptr, 1,
-                                           r > 0 ? lora_b : nullptr, r, y, part, counters, stream),
+                                           r > 0 ? lora_b : nullptr, r, y, part, counters, fp4rl::LoraFuse{}, stream),
                   "fp4_linear");
 }
 
@@ -280,15 +280,35 @@ fp4rl_status fp4rl_fp4_lora_linear(const uint16_t* x, int64_t m, int64_t n, int6
   FP4RL_CHECK(check_linear_main(x, m, n, k, codes, scales, tensor_scale, t, lora_b, r, y));
   FP4RL_CHECK(check_device());
   int slices = 1;
+  fp4rl::LoraFuse lf{};
   if (r > 0) {
     const int splits = fp4rl::lora_splits(m, k, r);
     slices = fp4rl::lora_slices(k, splits);
-    fp4rl_status s = launched(fp4rl::launch_lora_down(x, m, k, lora_a, r, lora_scale, splits, t, stream), "lora_down");
-    if (s != FP4RL_OK) return s;
+    if (fp4rl::linear_fuses_lora(m, n, k)) {
+      // t is made by the first workgroups of the linear's own launch (into
+      // slice 0 of the t region); counter words carry their hand-off
+      lf.a = lora_a;
+      lf.s = lora_scale;
+      lf.kslice = (int)fp4rl::lora_slice_len(k, splits);
+      lf.slices = slices;
+      lf.mtiles = (int)((m + 15) / 16);
+      lf.rtiles = (int)((r + 15) / 16);
+      lf.producers = (int)round_up((size_t)lf.mtiles * lf.rtiles * slices, 8);
+      lf.part = t;
+      lf.tctr = reinterpret_cast<uint32_t*>(ws) + fp4rl::kLoraTileCtrOffset;
+      lf.done = reinterpret_cast<uint32_t*>(ws) + fp4rl::kLoraDoneOffset;
+      lf.lines = reinterpret_cast<uint32_t*>(ws) + fp4rl::kLoraLineOffset;
+    } else {
+      fp4rl_status s =
+          launched(fp4rl::launch_lora_down(x, m, k, lora_a, r, lora_scale, splits, t, stream), "lora_down");
+      if (s != FP4RL_OK) return s;
+    }
   }
-  // the main kernel's epilogue sums the K-slices of t in slice order
-  return launched(fp4rl::launch_fp4_linear(x, m, n, k, codes, scales, tensor_scale, r > 0 ? t : nullptr, slices,
-                                           r > 0 ? lora_b : nullptr, r, y, part, counters, stream),
+  // the main kernel's epilogue sums the K-slices of t in slice order (fused
+  // producers have already summed them into slice 0)
+  return launched(fp4rl::launch_fp4_linear(x, m, n, k, codes, scales, tensor_scale, r > 0 ? t : nullptr,
+                                           lf.producers > 0 ? 1 : slices,
+                                           r > 0 ? lora_b : nullptr, r, y, part, counters, lf, stream),
                   "fp4_linear");
 }
 

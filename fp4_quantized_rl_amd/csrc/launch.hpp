@@ -36,18 +36,56 @@ hipError_t launch_lora_down(const uint16_t* x, int64_t m, int64_t k, const uint1
                             int splits, float* part, hipStream_t stream);
 hipError_t launch_lora_reduce(const float* part, int slices, int64_t count, float* t, hipStream_t stream);
 const char* fp4_linear_kernel_name(int64_t m, int64_t n, int64_t k, int64_t r);
-// Linear workspaces begin with kLinearCounters counter words (one per output
-// tile of a K-split launch; K is split only when there are fewer tiles). They
-// must be zero before the first call, and every launch leaves them at zero.
-// Its other regions (t slices, K-split partials) follow and never overlap
-// the counters, whatever shapes share the workspace.
-constexpr int kLinearCounters = 256;
+// Linear workspaces begin with kLinearCounters counter words: one per output
+// tile of a K-split launch (K is split only when there are at most
+// kSplitCounters tiles), then the fused LoRA hand-off words. They must be
+// zero before the first call, and every launch leaves them at zero. The
+// other regions (t slices, K-split partials) follow and never overlap the
+// counters, whatever shapes share the workspace.
+constexpr int kSplitCounters = 256;      // words [0, 256): K-split tile counters
+constexpr int kLoraTileCounters = 128;   // words [256, 384): one per 16x16 tile of t (m <= 128, r <= 256)
+constexpr int kLoraTileCtrOffset = 256;
+constexpr int kLoraDoneOffset = 384;     // word 384: finished tiles of t
+constexpr int kLoraGroups = 64;          // ready flags: one 256-byte line per group of output tiles
+constexpr int kLoraLineWords = 64;
+constexpr int kLoraLineOffset = 512;     // line g: words 512 + 64 g (flag), + 1 (count)
+constexpr int kLinearCounters = kLoraLineOffset + kLoraGroups * kLoraLineWords;
 constexpr size_t kLinearCounterBytes = kLinearCounters * sizeof(uint32_t);
+
+// LoRA down-projection fused into a main-kernel launch. The first
+// `producers` workgroups of the grid each compute one K-slice of one 16x16
+// tile of t into part[slice]; the last producer of a tile (counted in
+// tctr[tile]) adds its slices in slice order into part[0], clears tctr[tile]
+// and counts the finished tile in done[0]; the producer that finishes the
+// last tile clears done[0] and raises the ready flag of every group's line.
+// The workgroup that writes output tile i of y (the last of its K split)
+// belongs to group i % groups; it waits (a bounded wait) for its group's
+// flag just before its epilogue, then counts itself on that line, and the
+// group's last one clears the line. Spreading the consumers over many lines
+// keeps same-address atomics few. Producers have the lowest workgroup ids
+// and never wait on consumers, so they are dispatched first and always
+// finish.
+struct LoraFuse {
+  const uint16_t* a = nullptr;  // A [r][K]; nullptr: no fused producers (t ready-made, or r == 0)
+  float s = 0.0f;               // lora_scale
+  int kslice = 0, slices = 0;   // k per slice (a multiple of 32), number of slices (<= 8)
+  int mtiles = 0, rtiles = 0;   // 16x16 tiles of t
+  int producers = 0;            // producer workgroups (a multiple of 8, so the grid's XCD order is kept)
+  int consumers = 0;            // set by the launcher: output tiles of y (one waiting workgroup each)
+  int groups = 0;               // set by the launcher: min(kLoraGroups, consumers)
+  float* part = nullptr;        // t slices [slices][M][r]; t itself ends up in slice 0
+  uint32_t* tctr = nullptr;     // per-tile slice counters (mtiles * rtiles <= kLoraTileCounters)
+  uint32_t* done = nullptr;     // finished tiles of t
+  uint32_t* lines = nullptr;    // kLoraGroups lines of kLoraLineWords words: ready flag, consumer count
+};
+// whether the main kernel chosen for this shape runs fused LoRA producers
+bool linear_fuses_lora(int64_t m, int64_t n, int64_t k);
+int64_t lora_slice_len(int64_t k, int splits);
 // fp32 K-split partial sums of the main kernel (0 when K is not split)
 size_t linear_partial_bytes(int64_t m, int64_t n, int64_t k);
 hipError_t launch_fp4_linear(const uint16_t* x, int64_t m, int64_t n, int64_t k,
                              const uint8_t* codes, const uint8_t* scales, const float* tensor_scale,
                              const float* t, int tks, const uint16_t* b, int64_t r, uint16_t* y, float* part,
-                             uint32_t* counters, hipStream_t stream);
+                             uint32_t* counters, LoraFuse lf, hipStream_t stream);
 
 }  // namespace fp4rl

@@ -35,6 +35,24 @@ namespace fp4rl {
 namespace {
 
 __device__ __forceinline__ uint4 ld16(const void* p) { return *reinterpret_cast<const uint4*>(p); }
+// Buffer descriptor word 3 for raw (untyped) 32-bit element access on gfx950.
+constexpr int kBufferWord3 = 0x00020000;
+typedef uint32_t v4u32 __attribute__((ext_vector_type(4)));
+// Cache policy of agent-coherent loads: SC1 (the bits the compiler gives an
+// agent-scope atomic load), so data stored by another XCD is seen.
+constexpr int kCoherent = 16;
+__device__ __forceinline__ f32x4 ld_coherent16(__amdgpu_buffer_rsrc_t rs, int byte_off) {
+  return __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(rs, byte_off, 0, kCoherent));
+}
+__device__ __forceinline__ float ld_coherent4(__amdgpu_buffer_rsrc_t rs, int byte_off) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rs, byte_off, 0, kCoherent));
+}
+__device__ __forceinline__ void st_coherent16(f32x4 v, __amdgpu_buffer_rsrc_t rs, int byte_off) {
+  __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(v4u32, v), rs, byte_off, 0, kCoherent);
+}
+__device__ __forceinline__ void st_coherent4(float v, __amdgpu_buffer_rsrc_t rs, int byte_off) {
+  __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(uint32_t, v), rs, byte_off, 0, kCoherent);
+}
 
 // Calls f(I, J) for every (I, J) < (TI, TJ) with compile-time indices, so that
 // register arrays indexed by them never fall back to scratch memory (a plain
@@ -63,18 +81,20 @@ __device__ __forceinline__ void scale4(uint32_t w, float (&sc)[4]) {
 // through LDS. With one slice, `part` is t itself; otherwise the slices are
 // summed in slice order by lora_reduce_kernel or by the linear's epilogue.
 // ---------------------------------------------------------------------------
-template <int WAVES, int U = 4>
-__global__ __launch_bounds__(WAVES * kWave) void lora_down_kernel(const uint16_t* __restrict__ x, int M, int K,
-                                                                   const uint16_t* __restrict__ a, int r, float s,
-                                                                   int kslice, float* __restrict__ part) {
+// One 16x16 tile of t (tokens m0.., ranks j0..) for K slice z, by WAVES
+// waves; red: WAVES x 64 f32x4 of LDS. COHERENT stores are agent-scope
+// atomics, for readers in the same launch on another XCD.
+template <int WAVES, bool COHERENT, int U = 4>
+__device__ __forceinline__ void lora_tile(const uint16_t* __restrict__ x, int M, int K,
+                                          const uint16_t* __restrict__ a, int r, float s, int kslice, int m0, int j0,
+                                          int z, f32x4* red, float* __restrict__ part) {
   const int lane = threadIdx.x & (kWave - 1), wave = threadIdx.x / kWave;
   const int li = lane & 15, lg = lane >> 4;
-  const int m0 = blockIdx.x * 16, j0 = blockIdx.y * 16;
   const int m = m0 + li, j = j0 + li;
   const uint16_t* xr = x + (int64_t)min(m, M - 1) * K;
   const uint16_t* ar = a + (int64_t)min(j, r - 1) * K;
   const bool mv = m < M, jv = j < r;
-  const int kbeg = blockIdx.z * kslice;
+  const int kbeg = z * kslice;
   const int kend = min(K, kbeg + kslice);
   const int nsteps = (kend - kbeg + 31) / 32;
   const int mine = nsteps > wave ? (nsteps - wave + WAVES - 1) / WAVES : 0;
@@ -91,19 +111,139 @@ __global__ __launch_bounds__(WAVES * kWave) void lora_down_kernel(const uint16_t
 #pragma unroll
     for (int u = 0; u < U; ++u) acc = mfma16x16x32(as_bf16x8(xv[u]), as_bf16x8(av[u]), acc);
   }
-  __shared__ f32x4 red[WAVES][kWave];
-  red[wave][lane] = acc;
+  red[wave * kWave + lane] = acc;
   __syncthreads();
   if (wave == 0) {
-    f32x4 sum = red[0][lane];
+    f32x4 sum = red[lane];
 #pragma unroll
-    for (int w = 1; w < WAVES; ++w) sum += red[w][lane];
+    for (int w = 1; w < WAVES; ++w) sum += red[w * kWave + lane];
     // lane holds rows 4*lg + v (tokens), column li (rank index)
-    float* dst = part + (int64_t)blockIdx.z * M * r;
+    float* dst = part + (int64_t)z * M * r;
 #pragma unroll
     for (int v = 0; v < 4; ++v) {
       const int mm = m0 + 4 * lg + v, jj = j0 + li;
-      if (mm < M && jj < r) dst[(int64_t)mm * r + jj] = s * sum[v];
+      if (mm < M && jj < r) {
+        if constexpr (COHERENT)
+          __hip_atomic_store(dst + (int64_t)mm * r + jj, s * sum[v], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        else
+          dst[(int64_t)mm * r + jj] = s * sum[v];
+      }
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// LoRA down-projection, split along K into `gridDim.z` slices of `kslice`:
+//   part[z][m][j] = s * sum_{k in slice z} x[m][k] A[j][k].
+// One workgroup per 16x16 tile of t and K slice; its waves take the 32-wide
+// steps of the slice round-robin, U steps' loads at a time, and reduce
+// through LDS. With one slice, `part` is t itself; otherwise the slices are
+// summed in slice order by lora_reduce_kernel or by the linear's epilogue.
+// ---------------------------------------------------------------------------
+template <int WAVES>
+__global__ __launch_bounds__(WAVES * kWave) void lora_down_kernel(const uint16_t* __restrict__ x, int M, int K,
+                                                                   const uint16_t* __restrict__ a, int r, float s,
+                                                                   int kslice, float* __restrict__ part) {
+  __shared__ f32x4 red[WAVES * kWave];
+  lora_tile<WAVES, false>(x, M, K, a, r, s, kslice, blockIdx.x * 16, blockIdx.y * 16, blockIdx.z, red, part);
+}
+
+// Fused producers and the consumers' side of the handshake (LoraFuse).
+// `flag`: one word of LDS.
+template <int WAVES>
+__device__ __forceinline__ void lora_produce(const LoraFuse& L, int pid, const uint16_t* __restrict__ x, int M, int K,
+                                             int r, f32x4* red, uint32_t* flag) {
+  const int ntile = L.mtiles * L.rtiles;
+  if (pid >= ntile * L.slices) return;  // padding of the producer count to a multiple of 8
+  const int z = pid / ntile, tile = pid - z * ntile;
+  const int m0 = 16 * (tile % L.mtiles), j0 = 16 * (tile / L.mtiles);
+  lora_tile<WAVES, true>(x, M, K, L.a, r, L.s, L.kslice, m0, j0, z, red, L.part);
+  __builtin_amdgcn_s_waitcnt(0);  // this lane's stores of its slice are complete
+  __syncthreads();
+  if (L.slices > 1) {
+    if (threadIdx.x == 0)
+      *flag = __hip_atomic_fetch_add(L.tctr + tile, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) ==
+              (uint32_t)L.slices - 1;
+    __syncthreads();
+    if (*flag == 0u) return;
+    // the tile's last slice: t = part[0] + ... + part[slices-1], added in
+    // slice order, into part[0]
+    // (all slices' loads in flight at once: slices <= 8, and the t region,
+    // slices * M * r floats, is far below 2^31 bytes)
+    const int zbytes = 4 * M * r;
+    const __amdgpu_buffer_rsrc_t prs = __builtin_amdgcn_make_buffer_rsrc(L.part, 0, L.slices * zbytes, kBufferWord3);
+    for (int e = threadIdx.x; e < 256; e += WAVES * kWave) {
+      const int mm = m0 + (e >> 4), jj = j0 + (e & 15);
+      if (mm < M && jj < r) {
+        const int off = 4 * (mm * r + jj);
+        float v[8];
+#pragma unroll
+        for (int q = 0; q < 8; ++q) v[q] = ld_coherent4(prs, min(q, L.slices - 1) * zbytes + off);
+        float acc = 0.0f;
+#pragma unroll
+        for (int q = 0; q < 8; ++q)
+          if (q < L.slices) acc += v[q];
+        st_coherent4(acc, prs, off);
+      }
+    }
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
+    if (threadIdx.x == 0) __hip_atomic_store(L.tctr + tile, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  }
+  // this tile of t is complete; the workgroup that completes the last one
+  // raises every group's ready flag
+  if (threadIdx.x == 0)
+    *flag = __hip_atomic_fetch_add(L.done, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == (uint32_t)ntile - 1;
+  __syncthreads();
+  if (*flag != 0u) {
+    if (threadIdx.x == 0) __hip_atomic_store(L.done, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    if ((int)threadIdx.x < L.groups)
+      __hip_atomic_store(L.lines + kLoraLineWords * threadIdx.x, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  }
+}
+
+// Consumers' side, for the workgroup that writes output tile `tile` of y
+// (thread 0 does the memory accesses). It reads its group's ready flag early
+// (lora_poll), so the latency overlaps other work; lora_wait then returns at
+// once if it was set, else polls (bounded: a missing producer gives wrong
+// results, never a hang). Right after its wait the consumer counts itself on
+// its group's line (lora_release) and, once its epilogue is issued, the
+// group's last consumer clears the line (lora_reset_if_last).
+__device__ __forceinline__ uint32_t* lora_line(const LoraFuse& L, int tile) {
+  return L.lines + kLoraLineWords * (tile % L.groups);
+}
+
+__device__ __forceinline__ uint32_t lora_poll(const LoraFuse& L, int tile) {
+  return (L.producers > 0 && threadIdx.x == 0)
+             ? __hip_atomic_load(lora_line(L, tile), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)
+             : 0u;
+}
+
+__device__ __forceinline__ void lora_wait(const LoraFuse& L, int tile, uint32_t seen) {
+  if (L.producers > 0 && threadIdx.x == 0) {
+    const uint32_t* f = lora_line(L, tile);
+    for (int it = 0; seen == 0u && it < (1 << 22); ++it) {
+      __builtin_amdgcn_s_sleep(8);
+      seen = __hip_atomic_load(f, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
+  }
+  __syncthreads();
+}
+
+__device__ __forceinline__ uint32_t lora_release(const LoraFuse& L, int tile) {
+  return (L.producers > 0 && threadIdx.x == 0)
+             ? __hip_atomic_fetch_add(lora_line(L, tile) + 1, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)
+             : 0u;
+}
+
+__device__ __forceinline__ void lora_reset_if_last(const LoraFuse& L, int tile, uint32_t released_before) {
+  if (L.producers > 0 && threadIdx.x == 0) {
+    const int g = tile % L.groups;
+    const int members = L.consumers / L.groups + (g < L.consumers % L.groups ? 1 : 0);
+    if (released_before == (uint32_t)members - 1) {
+      uint32_t* f = lora_line(L, tile);
+      __hip_atomic_store(f, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      __hip_atomic_store(f + 1, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     }
   }
 }
@@ -124,12 +264,19 @@ __global__ void lora_reduce_kernel(const float* __restrict__ part, int slices, i
 // The LoRA product runs as MFMA steps over r in 32-wide pieces: B rows of the
 // tile are the A operand, t rows the B operand, t split into bf16 hi + lo.
 // ---------------------------------------------------------------------------
+// COH: t was written by other workgroups of this launch, so it is read with
+// agent-coherent loads (16 bytes at a time, through a buffer descriptor).
+// KB: K-slices of t loaded at once.
+template <bool COH = false, int KB = 4>
 __device__ __forceinline__ void store_tile(f32x4 v, int nb, int mb, int lane, int M, int N, float st,
                                            const float* __restrict__ t, int tks, const uint16_t* __restrict__ lb,
                                            int r, uint16_t* __restrict__ y) {
   const int li = lane & 15, lg = lane >> 4;
   f32x4 lo = {0.f, 0.f, 0.f, 0.f};
   if (r > 0) {
+    // (unused, and removed by the compiler, unless COH)
+    const __amdgpu_buffer_rsrc_t trs =
+        __builtin_amdgcn_make_buffer_rsrc(const_cast<float*>(t), 0, (int)(4 * (int64_t)tks * M * r), kBufferWord3);
     const bool rvec = (r & 7) == 0;
     const int64_t tstride = (int64_t)M * r;
     const int na = nb + li;  // B row for the A operand
@@ -142,12 +289,34 @@ __device__ __forceinline__ void store_tile(f32x4 v, int nb, int mb, int lane, in
         if (rvec) {
           if (na < N) bw = ld16(lb + (int64_t)na * r + jj);
           if (ma < M) {
-            for (int q = 0; q < tks; ++q) {  // K-slices of t, summed in order
-              const float* tp = t + (int64_t)q * tstride + (int64_t)ma * r + jj;
-              const float4 t0 = *reinterpret_cast<const float4*>(tp);
-              const float4 t1 = *reinterpret_cast<const float4*>(tp + 4);
-              tv[0] += t0.x; tv[1] += t0.y; tv[2] += t0.z; tv[3] += t0.w;
-              tv[4] += t1.x; tv[5] += t1.y; tv[6] += t1.z; tv[7] += t1.w;
+            // K-slices of t, summed in order; a batch's loads are all in
+            // flight at once (the last slice stands in for missing ones)
+            const int64_t o0 = (int64_t)ma * r + jj;
+            if constexpr (COH) {  // one slice (the producers added them)
+              const f32x4 p0 = ld_coherent16(trs, (int)(4 * o0)), p1 = ld_coherent16(trs, (int)(4 * o0) + 16);
+#pragma unroll
+              for (int e = 0; e < 4; ++e) tv[e] += p0[e], tv[e + 4] += p1[e];
+            } else if (tks == 1) {
+              const f32x4* tp = reinterpret_cast<const f32x4*>(t + o0);
+              const f32x4 p0 = tp[0], p1 = tp[1];
+#pragma unroll
+              for (int e = 0; e < 4; ++e) tv[e] += p0[e], tv[e + 4] += p1[e];
+            } else {
+              for (int q0 = 0; q0 < tks; q0 += KB) {
+                f32x4 p[KB][2];
+#pragma unroll
+                for (int u = 0; u < KB; ++u) {
+                  const f32x4* tp = reinterpret_cast<const f32x4*>(t + (int64_t)min(q0 + u, tks - 1) * tstride + o0);
+                  p[u][0] = tp[0];
+                  p[u][1] = tp[1];
+                }
+#pragma unroll
+                for (int u = 0; u < KB; ++u)
+                  if (q0 + u < tks) {
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) tv[e] += p[u][0][e], tv[e + 4] += p[u][1][e];
+                  }
+              }
             }
           }
         } else {
@@ -157,7 +326,13 @@ __device__ __forceinline__ void store_tile(f32x4 v, int nb, int mb, int lane, in
             const bool ok = jj + e < r;
             h[e] = (ok && na < N) ? lb[(int64_t)na * r + jj + e] : 0u;
             if (ok && ma < M)
-              for (int q = 0; q < tks; ++q) tv[e] += t[(int64_t)q * tstride + (int64_t)ma * r + jj + e];
+              for (int q = 0; q < tks; ++q) {
+                const int64_t o = (int64_t)q * tstride + (int64_t)ma * r + jj + e;
+                if constexpr (COH)
+                  tv[e] += ld_coherent4(trs, (int)(4 * o));
+                else
+                  tv[e] += t[o];
+              }
           }
           bw = make_uint4(h[0] | (h[1] << 16), h[2] | (h[3] << 16), h[4] | (h[5] << 16), h[6] | (h[7] << 16));
         }
@@ -321,7 +496,7 @@ __global__ __launch_bounds__(WAVES * kWave) void skinny_kernel(
 
   const float st = *tensor_scale;
   auto epilogue = [&](int i, int j, f32x4 v) {
-    store_tile(v, n0 + 16 * i, m0 + 16 * j, lane, M, N, st, t, tks, lb, r, y);
+    store_tile<false, (WAVES >= 16 ? 1 : 4)>(v, n0 + 16 * i, m0 + 16 * j, lane, M, N, st, t, tks, lb, r, y);
   };
 
   if constexpr (WAVES == 1) {
@@ -371,11 +546,16 @@ __global__ __launch_bounds__(W * kWave) void splitk_kernel(
     const uint16_t* __restrict__ x, int M, int N, int K, const uint8_t* __restrict__ codes,
     const uint8_t* __restrict__ scales, const float* __restrict__ tensor_scale, const float* __restrict__ t, int tks,
     const uint16_t* __restrict__ lb, int r, uint16_t* __restrict__ y, int cpz, int nsplit, float* __restrict__ part,
-    uint32_t* __restrict__ counters) {
+    uint32_t* __restrict__ counters, LoraFuse lf) {
   static_assert(TM <= 4, "the reduction reuses the activation slabs: TM * TN KB <= TN * 4.25 KB");
   constexpr int TOK = 16 * TN;
   __shared__ __align__(16) uint16_t xs[W][TOK * kXRow];
   __shared__ uint32_t last_flag;
+  if ((int)blockIdx.x < lf.producers) {  // fused LoRA down-projection
+    lora_produce<W>(lf, blockIdx.x, x, M, K, r, reinterpret_cast<f32x4*>(&xs[0][0]), &last_flag);
+    return;
+  }
+  const unsigned bid = blockIdx.x - lf.producers;  // producers are a multiple of 8: the XCD order holds
   const int lane = threadIdx.x & (kWave - 1);
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
   const int li = lane & 15, lg = lane >> 4;
@@ -385,8 +565,8 @@ __global__ __launch_bounds__(W * kWave) void splitk_kernel(
   // a row group get consecutive slots of one XCD: its weights are fetched
   // into that XCD's L2 once, and its partial sums stay there.
   const int GX = (RT + TM - 1) / TM, GT = (M + TOK - 1) / TOK;
-  const int inner = (int)(blockIdx.x >> 3) % (GT * nsplit);
-  const int rg = (int)((blockIdx.x >> 3) / (GT * nsplit)) * 8 + (int)(blockIdx.x & 7);
+  const int inner = (int)(bid >> 3) % (GT * nsplit);
+  const int rg = (int)((bid >> 3) / (GT * nsplit)) * 8 + (int)(bid & 7);
   if (rg >= GX) return;  // padding of the row-group count to a multiple of 8
   const int tg = inner % GT, kz = inner / GT;
   const int rt0 = rg * TM, n0 = 16 * rt0, m0 = tg * TOK;
@@ -496,6 +676,8 @@ __global__ __launch_bounds__(W * kWave) void splitk_kernel(
 
   // Reduce the waves' sums: wave w's tiles go to its own slab, then tile e is
   // summed over the waves, in wave order, by wave e % W.
+  const int ytile = tg * GX + rg;  // this workgroup's output tile (its K-split counter, its LoRA group)
+  const uint32_t t_seen = nsplit == 1 ? lora_poll(lf, ytile) : 0u;  // fused LoRA: read early, checked below
   float* red = reinterpret_cast<float*>(slab);
 #pragma unroll
   for (int i = 0; i < TM; ++i)
@@ -517,11 +699,19 @@ __global__ __launch_bounds__(W * kWave) void splitk_kernel(
     sums[e0] = sum;
   }
   if (nsplit == 1) {
+    lora_wait(lf, ytile, t_seen);
+    const uint32_t released = lora_release(lf, ytile);
 #pragma unroll
     for (int e0 = 0; e0 < (NTILE + W - 1) / W; ++e0) {
       const int e = wave + W * e0;
-      if (e < NTILE) store_tile(sums[e0], n0 + 16 * (e / TN), m0 + 16 * (e % TN), lane, M, N, st, t, tks, lb, r, y);
+      if (e < NTILE) {
+        if (lf.producers > 0)
+          store_tile<true>(sums[e0], n0 + 16 * (e / TN), m0 + 16 * (e % TN), lane, M, N, st, t, tks, lb, r, y);
+        else
+          store_tile(sums[e0], n0 + 16 * (e / TN), m0 + 16 * (e % TN), lane, M, N, st, t, tks, lb, r, y);
+      }
     }
+    lora_reset_if_last(lf, ytile, released);
     return;
   }
   // K split over workgroups: publish this range's partial tile. The partials
@@ -530,27 +720,42 @@ __global__ __launch_bounds__(W * kWave) void splitk_kernel(
   // to complete before the workgroup barrier, and the counter is bumped only
   // after that barrier, so a workgroup that sees the last count sees every
   // partial.
-  const int64_t zstride = (int64_t)M * N;
+  // Partials are addressed through a buffer descriptor (byte offsets; the
+  // host keeps all nsplit * M * N of them below 2^31 bytes) so that 16-byte
+  // accesses can carry the agent-coherent cache policy.
+  const int zbytes = 4 * M * N;
+  const __amdgpu_buffer_rsrc_t prs = __builtin_amdgcn_make_buffer_rsrc(part, 0, nsplit * zbytes, kBufferWord3);
+  const bool nvec = (N & 3) == 0;  // rows of 16-byte aligned groups of four
 #pragma unroll
   for (int e0 = 0; e0 < (NTILE + W - 1) / W; ++e0) {
     const int e = wave + W * e0;
     if (e < NTILE) {
       const int m = m0 + 16 * (e % TN) + li, nf = n0 + 16 * (e / TN) + 4 * lg;
       if (m < M) {
-        float* pp = part + kz * zstride + (int64_t)m * N + nf;
+        const int off = kz * zbytes + 4 * (m * N + nf);
+        if (nvec) {
+          if (nf < N) st_coherent16(sums[e0], prs, off);
+        } else {
 #pragma unroll
-        for (int v = 0; v < 4; ++v)
-          if (nf + v < N) __hip_atomic_store(pp + v, sums[e0][v], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+          for (int v = 0; v < 4; ++v)
+            if (nf + v < N) st_coherent4(sums[e0][v], prs, off + 4 * v);
+        }
       }
     }
   }
   __builtin_amdgcn_s_waitcnt(0);  // this lane's stores are complete
   __syncthreads();
-  uint32_t* ctr = counters + tg * GX + rg;
-  if (threadIdx.x == 0)
-    last_flag = __hip_atomic_fetch_add(ctr, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == (uint32_t)nsplit - 1 ? 1u : 0u;
+  uint32_t* ctr = counters + ytile;
+  uint32_t t_seen2 = 0u;
+  if (threadIdx.x == 0) {
+    t_seen2 = lora_poll(lf, ytile);  // in flight together with the tile count
+    const uint32_t before = __hip_atomic_fetch_add(ctr, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    last_flag = before == (uint32_t)nsplit - 1 ? 1u : 0u;
+  }
   __syncthreads();
   if (last_flag == 0u) return;
+  lora_wait(lf, ytile, t_seen2);
+  const uint32_t released = lora_release(lf, ytile);
 #pragma unroll
   for (int e0 = 0; e0 < (NTILE + W - 1) / W; ++e0) {
     const int e = wave + W * e0;
@@ -558,18 +763,36 @@ __global__ __launch_bounds__(W * kWave) void splitk_kernel(
       const int m = m0 + 16 * (e % TN) + li, nf = n0 + 16 * (e / TN) + 4 * lg;
       f32x4 sum = {0.f, 0.f, 0.f, 0.f};
       if (m < M) {
-        const float* pp = part + (int64_t)m * N + nf;
-        for (int z = 0; z < nsplit; ++z) {  // fixed order: results do not depend on arrival
+        // all of a batch's loads in flight at once, added in split order
+        // (results do not depend on arrival); elements past N are summed but
+        // never stored, and reads past the buffer return zero
+        const int off = 4 * (m * N + nf);
+        constexpr int kB = 8;
+        for (int z0 = 0; z0 < nsplit; z0 += kB) {
+          f32x4 pz[kB];
 #pragma unroll
-          for (int v = 0; v < 4; ++v)
-            if (nf + v < N)
-              sum[v] += __hip_atomic_load(pp + z * zstride + v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+          for (int u = 0; u < kB; ++u) {
+            const int zo = min(z0 + u, nsplit - 1) * zbytes + off;
+            if (nvec) {
+              pz[u] = ld_coherent16(prs, zo);
+            } else {
+#pragma unroll
+              for (int v = 0; v < 4; ++v) pz[u][v] = ld_coherent4(prs, zo + 4 * v);
+            }
+          }
+#pragma unroll
+          for (int u = 0; u < kB; ++u)
+            if (z0 + u < nsplit) sum += pz[u];
         }
       }
-      store_tile(sum, n0 + 16 * (e / TN), m0 + 16 * (e % TN), lane, M, N, st, t, tks, lb, r, y);
+      if (lf.producers > 0)
+        store_tile<true>(sum, n0 + 16 * (e / TN), m0 + 16 * (e % TN), lane, M, N, st, t, tks, lb, r, y);
+      else
+        store_tile(sum, n0 + 16 * (e / TN), m0 + 16 * (e % TN), lane, M, N, st, t, tks, lb, r, y);
     }
   }
   if (threadIdx.x == 0) __hip_atomic_store(ctr, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  lora_reset_if_last(lf, ytile, released);
 }
 
 // ---------------------------------------------------------------------------
@@ -1011,7 +1234,7 @@ int lora_splits(int64_t m, int64_t k, int64_t r) {
   return (int)std::min<int64_t>(8, by_k);
 }
 
-static int64_t slice_len(int64_t k, int splits) { return ((k + splits - 1) / splits + 31) / 32 * 32; }
+static int64_t slice_len(int64_t k, int splits) { return lora_slice_len(k, splits); }
 
 hipError_t launch_lora_down(const uint16_t* x, int64_t m, int64_t k, const uint16_t* a, int64_t r, float lora_scale,
                             int splits, float* part, hipStream_t stream) {
@@ -1110,7 +1333,7 @@ static SplitkCfg pick_splitk(int64_t m, int64_t n, int64_t k) {
 #endif
   c.cpz = (int)((kc + s - 1) / s);
   c.s = (int)((kc + c.cpz - 1) / c.cpz);  // no empty K range
-  if ((int64_t)c.gx * c.gy > kLinearCounters) c.s = 1, c.cpz = (int)kc;  // a split needs one counter per tile
+  if ((int64_t)c.gx * c.gy > kSplitCounters) c.s = 1, c.cpz = (int)kc;  // a split needs one counter per tile
   return c;
 }
 
@@ -1124,19 +1347,25 @@ size_t linear_partial_bytes(int64_t m, int64_t n, int64_t k) {
 template <int TN, int W>
 hipError_t run_splitk(const SplitkCfg& c, hipStream_t st, const uint16_t* x, int M, int N, int K, const uint8_t* codes,
                       const uint8_t* scales, const float* ts, const float* t, int tks, const uint16_t* b, int r,
-                      uint16_t* y, float* part, uint32_t* counters) {
-  const unsigned grid = (unsigned)(8 * ((c.gx + 7) / 8) * c.gy * c.s);
+                      uint16_t* y, float* part, uint32_t* counters, LoraFuse lf) {
+  // (a split has s * gx * gy < 512, so its partials stay below 4 MB)
+  if (c.s > 1 && (int64_t)c.s * M * N * 4 > INT32_MAX) return hipErrorInvalidValue;
+  const int main_grid = 8 * ((c.gx + 7) / 8) * c.gy * c.s;
+  lf.consumers = c.gx * c.gy;  // one waiting workgroup per output tile (the last of its K split)
+  lf.groups = std::min(kLoraGroups, lf.consumers);
+  const unsigned grid = (unsigned)(lf.producers + main_grid);
   hipLaunchKernelGGL((splitk_kernel<4, TN, W>), dim3(grid), dim3(W * kWave), 0, st, x, M, N, K, codes, scales, ts, t,
-                     tks, b, r, y, c.cpz, c.s, c.s > 1 ? part : nullptr, c.s > 1 ? counters : nullptr);
+                     tks, b, r, y, c.cpz, c.s, c.s > 1 ? part : nullptr, c.s > 1 ? counters : nullptr, lf);
   return hipGetLastError();
 }
 
 static hipError_t launch_splitk(const SplitkCfg& c, hipStream_t st, const uint16_t* x, int M, int N, int K,
                                 const uint8_t* codes, const uint8_t* scales, const float* ts, const float* t, int tks,
-                                const uint16_t* b, int r, uint16_t* y, float* part, uint32_t* counters) {
+                                const uint16_t* b, int r, uint16_t* y, float* part, uint32_t* counters,
+                                const LoraFuse& lf) {
 #define FP4RL_SPLITK(TN_, W_) \
   if (c.tn == TN_ && c.w == W_) \
-    return run_splitk<TN_, W_>(c, st, x, M, N, K, codes, scales, ts, t, tks, b, r, y, part, counters);
+    return run_splitk<TN_, W_>(c, st, x, M, N, K, codes, scales, ts, t, tks, b, r, y, part, counters, lf);
   FP4RL_SPLITK(2, 4)
 #ifdef FP4RL_TUNING
   FP4RL_SPLITK(2, 2) FP4RL_SPLITK(2, 8)
@@ -1185,10 +1414,21 @@ const char* fp4_linear_kernel_name(int64_t m, int64_t n, int64_t k, int64_t r) {
   return kNames[mi][ni][wi];
 }
 
+bool linear_fuses_lora(int64_t m, int64_t n, int64_t k) {
+  (void)n;
+  (void)k;
+  return use_splitk(m);
+}
+
+int64_t lora_slice_len(int64_t k, int splits) { return ((k + splits - 1) / splits + 31) / 32 * 32; }
+
 hipError_t launch_fp4_linear(const uint16_t* x, int64_t m, int64_t n, int64_t k, const uint8_t* codes,
                              const uint8_t* scales, const float* tensor_scale, const float* t, int tks,
                              const uint16_t* b, int64_t r, uint16_t* y, float* part, uint32_t* counters,
-                             hipStream_t stream) {
+                             LoraFuse lf, hipStream_t stream) {
+  if (lf.producers > 0 &&
+      (!linear_fuses_lora(m, n, k) || lf.mtiles * lf.rtiles > kLoraTileCounters || tks != 1 || lf.slices > 8))
+    return hipErrorInvalidValue;
   const int M = (int)m, N = (int)n, K = (int)k, R = (int)r;
   if (use_gemv(m, n, k, r)) {
     const int w = gemv_waves(n, k);
@@ -1197,7 +1437,7 @@ hipError_t launch_fp4_linear(const uint16_t* x, int64_t m, int64_t n, int64_t k,
   }
   if (use_splitk(m))
     return launch_splitk(pick_splitk(m, n, k), stream, x, M, N, K, codes, scales, tensor_scale, t, tks, b, R, y, part,
-                         counters);
+                         counters, lf);
   if (m > 128) {
     const int64_t gr = (n + kPfRows - 1) / kPfRows, gt = (m + kPfTok - 1) / kPfTok;
     const int64_t supers = (gr + 7) / 8 * ((gt + 3) / 4);  // super-tiles of 8 x 4 workgroups, dealt to 8 XCDs

@@ -122,11 +122,18 @@ fp4rl_status fp4rl_nvfp4_to_tiled(const uint8_t* codes, const uint8_t* scales, i
  * k % 16 == 0; m * k < 2^31; 0 <= r <= 256; r == 0 or lora_a == lora_b ==
  * NULL means no LoRA term. Accumulation is fp32; the output is rounded once
  * to bf16.
- * Launches the LoRA down-projection (when r > 0) and then the main kernel,
- * chosen by m (see fp4rl_fp4_linear_kernel_name).
+ * For 16 < m <= 128 one launch does all of it: its first workgroups compute
+ * t = lora_scale * x A^T (in K slices; the last slice of each 16x16 tile of t
+ * to finish adds the slices) and the others wait for t only before their
+ * epilogue. Otherwise the LoRA down-projection (when r > 0) and then the main
+ * kernel are launched, the kernel chosen by m (see
+ * fp4rl_fp4_linear_kernel_name).
  * Workspace: fp4rl_fp4_lora_linear_workspace(m, n, k, r) bytes (0 when
- * neither split below is used), 16-byte aligned. It starts with 256 counter
- * words (1 KB); then come the K-split partial sums of t and, for shapes with
+ * neither split below is used), 16-byte aligned. It starts with 4608
+ * counter words (18 KB: K-split tile counters, then the hand-off words of the
+ * in-launch LoRA producers, spread over 64 lines of 256 bytes so that few
+ * workgroups share an atomic address); then come the K-split partial sums of
+ * t and, for shapes with
  * few output tiles, the main kernel's K-split partial sums of y (the last
  * workgroup of a tile to finish, found through its counter, adds them). All
  * partial sums are added in a fixed order, so results do not depend on

@@ -86,6 +86,39 @@ def test_split_k_shapes(m, n, k, r):
     _check(y, linear.lora_linear(x, *q, a, b, LORA_SCALE), f"{m}x{n}x{k} r{r}")
 
 
+# a linear workspace starts with 4608 counter words: K-split tile counters,
+# t tile counters, finished-tile count, 64 ready-flag lines of 256 bytes
+COUNTER_BYTES = 4 * (512 + 64 * 64)
+
+FUSED = [  # (m, n, k, r): 16 < m <= 128 with r > 0 computes t inside the linear's launch, in K slices
+    (17, 64, 2048, 13), (33, 50, 1040, 7), (40, 300, 4096, 32), (100, 4608, 3584, 32), (128, 96, 4096, 256),
+]
+
+
+@pytest.mark.parametrize("m,n,k,r", FUSED)
+def test_fused_lora_shapes(m, n, k, r):
+    """Ragged ranks (scalar t loads), several K slices of t, and the most tiles of t (m = 128, r = 256)."""
+    dev = device()
+    w, x, a, b = _case(m, n, k, r, seed=m * 53 + n * 3 + k + r)
+    q = nvfp4.quantize(w)
+    say(f"linear fused LoRA m={m} n={n} k={k} r={r} ({fr.fp4_linear_kernel_name(m, n, k, r)})")
+    xt, wq = bf16_to_dev(x, dev), nvfp4_to_dev(*q, dev)
+    at, bt = bf16_to_dev(a, dev), bf16_to_dev(b, dev)
+    ws = fr.linear_workspace(fr.fp4_lora_linear_workspace_bytes(m, n, k, r), dev)
+    y1 = fr.fp4_lora_linear(xt, wq, at, bt, LORA_SCALE, workspace=ws)
+    y2 = fr.fp4_lora_linear(xt, wq, at, bt, LORA_SCALE, workspace=ws)
+    torch.cuda.synchronize()
+    _check(bf16_from_dev(y1), linear.lora_linear(x, *q, a, b, LORA_SCALE), f"{m}x{n}x{k} r{r}")
+    assert torch.equal(y1, y2), "second call on the same workspace differs"
+    cb = COUNTER_BYTES
+    assert not bool(ws[:cb].any()), "counter words not back at zero"
+    # the producers leave t (all K slices added) in the first slice, right after the counters
+    t_fused = ws[cb:cb + 4 * m * r].view(torch.float32).reshape(m, r).cpu().numpy()
+    err = rel_l2(t_fused, linear.lora_down(x, a, LORA_SCALE))
+    say(f"  t: rel-L2 {err:.3e}")
+    assert err < 1e-5
+
+
 PREFILL = [  # (m, n, k, r): more than 128 tokens (256-feature x 128-token workgroup tiles), ragged in every dim
     (129, 16, 128, 0), (200, 270, 400, 8), (384, 512, 1024, 16), (1000, 520, 2064, 32), (2048, 300, 4096, 64),
 ]
