@@ -377,10 +377,17 @@ template <int MT, int NT, int WAVES, int U = skinny_group(MT, NT, WAVES)>
 __global__ __launch_bounds__(WAVES * kWave) void skinny_kernel(
     const uint16_t* __restrict__ x, int M, int N, int K, const uint8_t* __restrict__ codes,
     const uint8_t* __restrict__ scales, const float* __restrict__ tensor_scale, const float* __restrict__ t,
-    int tks, const uint16_t* __restrict__ lb, int r, uint16_t* __restrict__ y) {
+    int tks, const uint16_t* __restrict__ lb, int r, uint16_t* __restrict__ y, LoraFuse lf) {
+  __shared__ f32x4 red[WAVES][NT * MT][kWave];  // the waves' sums; fused LoRA producers use its first WAVES KB
+  __shared__ uint32_t pflag;
+  if ((int)blockIdx.x < lf.producers) {  // fused LoRA down-projection (grid.y is 1 then)
+    lora_produce<WAVES>(lf, blockIdx.x, x, M, K, r, &red[0][0][0], &pflag);
+    return;
+  }
+  const int bx = blockIdx.x - lf.producers;
   const int lane = threadIdx.x & (kWave - 1), wave = threadIdx.x / kWave;
   const int li = lane & 15, lg = lane >> 4;
-  const int n0 = blockIdx.x * (16 * NT);
+  const int n0 = bx * (16 * NT);
   const int m0 = blockIdx.y * (16 * MT);
   // Tiled weights: tile (rt, c) = 16 rows x 128 k; this lane's 16 code bytes
   // sit at 16 * lane of the tile and its scale word (byte j = the block of
@@ -388,7 +395,7 @@ __global__ __launch_bounds__(WAVES * kWave) void skinny_kernel(
   // registers); lanes add 32-bit offsets. Row tiles past the matrix are
   // clamped to the last one (their rows are never stored).
   const int RT = (N + 15) >> 4, KC = (K + 127) >> 7;
-  const int rt0 = blockIdx.x * NT;
+  const int rt0 = bx * NT;
   const uint8_t* cbase = codes + (int64_t)rt0 * KC * 1024;  // uniform
   const uint8_t* sbase = scales + (int64_t)rt0 * KC * 128;  // uniform
   const uint32_t clane = 16 * lane, slane = 4 * (16 * (lg >> 1) + li);
@@ -496,27 +503,37 @@ __global__ __launch_bounds__(WAVES * kWave) void skinny_kernel(
 
   const float st = *tensor_scale;
   auto epilogue = [&](int i, int j, f32x4 v) {
-    store_tile<false, (WAVES >= 16 ? 1 : 4)>(v, n0 + 16 * i, m0 + 16 * j, lane, M, N, st, t, tks, lb, r, y);
+    if (lf.producers > 0)
+      store_tile<true>(v, n0 + 16 * i, m0 + 16 * j, lane, M, N, st, t, tks, lb, r, y);
+    else
+      store_tile<false, (WAVES >= 16 ? 1 : 4)>(v, n0 + 16 * i, m0 + 16 * j, lane, M, N, st, t, tks, lb, r, y);
   };
+  const int ytile = blockIdx.y * (gridDim.x - lf.producers) + bx;  // fused LoRA group
+  const uint32_t t_seen = lora_poll(lf, ytile);
 
   if constexpr (WAVES == 1) {
+    lora_wait(lf, ytile, t_seen);
+    const uint32_t released = lora_release(lf, ytile);
 #pragma unroll
     for (int i = 0; i < NT; ++i)
 #pragma unroll
       for (int j = 0; j < MT; ++j) epilogue(i, j, acc[i][j]);
+    lora_reset_if_last(lf, ytile, released);
   } else {
-    __shared__ f32x4 red[WAVES][NT * MT][kWave];
 #pragma unroll
     for (int i = 0; i < NT; ++i)
 #pragma unroll
       for (int j = 0; j < MT; ++j) red[wave][i * MT + j][lane] = acc[i][j];
     __syncthreads();
+    lora_wait(lf, ytile, t_seen);
+    const uint32_t released = lora_release(lf, ytile);
     for (int tl = wave; tl < NT * MT; tl += WAVES) {
       f32x4 sum = red[0][tl][lane];
 #pragma unroll
       for (int w = 1; w < WAVES; ++w) sum += red[w][tl][lane];
       epilogue(tl / MT, tl % MT, sum);
     }
+    lora_reset_if_last(lf, ytile, released);
   }
 }
 
@@ -1030,7 +1047,9 @@ __global__ __launch_bounds__(kPfRows / 16 / TM * kWave) void prefill_kernel(
 //   MFMA path's dequantisation cost. Lane groups and waves are reduced by
 //   shuffles and LDS in a fixed order. The LoRA operands (B rows of the tile
 //   and t, its K-slices summed in order) are staged in LDS before the main
-//   loop so their load latency overlaps it.
+//   loop so their load latency overlaps it; when t is made by producer
+//   workgroups of the same launch, it is staged after the main loop, once
+//   their ready flag is seen.
 // ---------------------------------------------------------------------------
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 
@@ -1038,13 +1057,19 @@ template <int MTOK, int WAVES, int U>
 __global__ __launch_bounds__(WAVES * kWave) void gemv_kernel(
     const uint16_t* __restrict__ x, int M, int N, int K, const uint8_t* __restrict__ codes,
     const uint8_t* __restrict__ scales, const float* __restrict__ tensor_scale, const float* __restrict__ t,
-    int tks, const uint16_t* __restrict__ lb, int r, uint16_t* __restrict__ y) {
+    int tks, const uint16_t* __restrict__ lb, int r, uint16_t* __restrict__ y, LoraFuse lf) {
   extern __shared__ __align__(16) uint8_t smem[];
+  __shared__ uint32_t pflag;
+  if ((int)blockIdx.x < lf.producers) {  // fused LoRA down-projection (the launch gives >= WAVES KB of LDS)
+    lora_produce<WAVES>(lf, blockIdx.x, x, M, K, r, reinterpret_cast<f32x4*>(smem), &pflag);
+    return;
+  }
+  const bool fused = lf.producers > 0;  // t comes from this launch: staged after the main loop
   const int lane = threadIdx.x & (kWave - 1);
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
   const int li = lane & 15, lg = lane >> 4;
   const int KC = (K + 127) >> 7, Kp = KC * 128;
-  const int rt = blockIdx.x;
+  const int rt = blockIdx.x - lf.producers;
   const int nchunk = KC;
   const int mine = nchunk > wave ? (nchunk - wave + WAVES - 1) / WAVES : 0;
   const uint8_t* cbase = codes + (int64_t)rt * KC * 1024;
@@ -1080,12 +1105,14 @@ __global__ __launch_bounds__(WAVES * kWave) void gemv_kernel(
     *reinterpret_cast<uint4*>(xs + m * Kp + kk) = v;
   }
   const int64_t tstride = (int64_t)M * r;
-  for (int i = threadIdx.x; i < MTOK * r; i += WAVES * kWave) {
-    const int m = i / r, j = i - m * r;
-    float a = 0.0f;
-    if (m < M)
-      for (int q = 0; q < tks; ++q) a += t[q * tstride + (int64_t)m * r + j];  // slice order
-    tsum[i] = a;
+  if (!fused) {
+    for (int i = threadIdx.x; i < MTOK * r; i += WAVES * kWave) {
+      const int m = i / r, j = i - m * r;
+      float a = 0.0f;
+      if (m < M)
+        for (int q = 0; q < tks; ++q) a += t[q * tstride + (int64_t)m * r + j];  // slice order
+      tsum[i] = a;
+    }
   }
   for (int i = threadIdx.x; i < 16 * r; i += WAVES * kWave) {
     const int row = i / r, j = i - row * r;
@@ -1143,11 +1170,21 @@ __global__ __launch_bounds__(WAVES * kWave) void gemv_kernel(
     acc[m] += __shfl_xor(acc[m], 16, kWave);
     acc[m] += __shfl_xor(acc[m], 32, kWave);
   }
+  const uint32_t t_seen = lora_poll(lf, rt);
   if (lg == 0) {
 #pragma unroll
     for (int m = 0; m < MTOK; ++m) red[(wave * MTOK + m) * 16 + li] = acc[m];
   }
   __syncthreads();
+  uint32_t released = 0u;
+  if (fused) {  // wait for t, then stage it (one slice, coherent loads)
+    lora_wait(lf, rt, t_seen);
+    released = lora_release(lf, rt);
+    const __amdgpu_buffer_rsrc_t trs =
+        __builtin_amdgcn_make_buffer_rsrc(const_cast<float*>(t), 0, 4 * M * r, kBufferWord3);
+    for (int i = threadIdx.x; i < MTOK * r; i += WAVES * kWave) tsum[i] = i < M * r ? ld_coherent4(trs, 4 * i) : 0.0f;
+    __syncthreads();
+  }
   if (threadIdx.x < 16 * MTOK) {
     const int row = threadIdx.x & 15, m = threadIdx.x >> 4;
     const int n = 16 * rt + row;
@@ -1159,6 +1196,7 @@ __global__ __launch_bounds__(WAVES * kWave) void gemv_kernel(
       y[(int64_t)m * N + n] = (uint16_t)f32_to_bf16(*tensor_scale * sum + lo);
     }
   }
+  if (fused) lora_reset_if_last(lf, rt, released);
 }
 
 size_t gemv_lds_bytes(int mtok, int64_t k, int64_t r, int waves) {
@@ -1174,46 +1212,46 @@ struct SkinnyCfg {
 // activation fragments a lane loads are reused across more weight rows; the
 // waves per workgroup split K so that ~4k waves are in flight (16 per CU),
 // within a 64 KB LDS reduction buffer (waves * nt * mt <= 64).
+// 3..16 tokens (one 16-token tile).
 SkinnyCfg pick_skinny(int64_t m, int64_t n, int64_t k) {
-  const int mt = m <= 16 ? 1 : m <= 32 ? 2 : m <= 64 ? 4 : 8;
-  if (m <= 16 && n >= 4096) {
+  (void)m;
+  const int64_t kc = (k + 127) / 128;
+  if (n >= 4096) {
     // wide matrices: two row tiles share each activation fragment (halves the
     // activation re-reads); 4 waves when that still leaves >= 512 workgroups
     const int64_t groups = (n + 31) / 32;
-    const int64_t kc = (k + 127) / 128;
     const int w = (int)std::min<int64_t>(groups >= 512 ? 4 : 8, std::max<int64_t>(1, kc));
     int wp = 1;
     while (wp * 2 <= w) wp *= 2;
     return SkinnyCfg{1, 2, wp};
   }
-  const int nt = m <= 16 ? 1 : 2;
-  const int64_t gy = (m + 16 * mt - 1) / (16 * mt);
-  const int64_t groups = (n + 16 * nt - 1) / (16 * nt) * gy;
-  const int64_t kc = (k + 127) / 128;
-  const int wcap = mt == 1 ? 16 : 8;  // 1024-thread groups leave 128 registers per lane: MT = 1 only
-  const int wmax = (int)std::min<int64_t>(std::min<int64_t>(wcap, 64 / (nt * mt)), std::max<int64_t>(1, kc));
+  const int64_t groups = (n + 15) / 16;
+  const int wmax = (int)std::min<int64_t>(16, std::max<int64_t>(1, kc));
   int w = 1;
   while (w * 2 <= wmax && groups * w < 4096) w *= 2;
-  return SkinnyCfg{mt, nt, w};
+  return SkinnyCfg{1, 1, w};
 }
 
 template <int MT, int NT, int W>
 hipError_t run_skinny(dim3 grid, hipStream_t st, const uint16_t* x, int M, int N, int K, const uint8_t* codes,
                       const uint8_t* scales, const float* ts, const float* t, int tks, const uint16_t* b, int r,
-                      uint16_t* y) {
-  hipLaunchKernelGGL((skinny_kernel<MT, NT, W>), grid, dim3(W * kWave), 0, st, x, M, N, K, codes, scales, ts, t, tks,
-                     b, r, y);
+                      uint16_t* y, LoraFuse lf) {
+  if (lf.producers > 0 && grid.y != 1) return hipErrorInvalidValue;  // producers index grid.x
+  lf.consumers = (int)(grid.x * grid.y);
+  lf.groups = std::min(kLoraGroups, lf.consumers);
+  hipLaunchKernelGGL((skinny_kernel<MT, NT, W>), dim3(grid.x + lf.producers, grid.y), dim3(W * kWave), 0, st, x, M, N,
+                     K, codes, scales, ts, t, tks, b, r, y, lf);
   return hipGetLastError();
 }
 
 template <int MT, int NT>
 hipError_t run_skinny_w(int w, dim3 grid, hipStream_t st, const uint16_t* x, int M, int N, int K,
                         const uint8_t* codes, const uint8_t* scales, const float* ts, const float* t, int tks,
-                        const uint16_t* b, int r, uint16_t* y) {
+                        const uint16_t* b, int r, uint16_t* y, const LoraFuse& lf) {
   // only waves * MT * NT <= 64 is instantiated: the reduction buffer is at most 64 KB of LDS
 #define FP4RL_CASE(W_)                                                                             \
   case W_:                                                                                         \
-    if constexpr (W_ * MT * NT <= 64 && (W_ < 16 || MT == 1)) return run_skinny<MT, NT, W_>(grid, st, x, M, N, K, codes, scales, ts, t, tks, b, r, y); \
+    if constexpr (W_ * MT * NT <= 64 && (W_ < 16 || MT == 1)) return run_skinny<MT, NT, W_>(grid, st, x, M, N, K, codes, scales, ts, t, tks, b, r, y, lf); \
     break;
   switch (w) {
     FP4RL_CASE(1) FP4RL_CASE(2) FP4RL_CASE(4) FP4RL_CASE(8) FP4RL_CASE(16)
@@ -1278,24 +1316,27 @@ static bool use_gemv(int64_t m, int64_t n, int64_t k, int64_t r) {
 
 template <int MTOK, int W>
 hipError_t run_gemv(hipStream_t st, const uint16_t* x, int M, int N, int K, const uint8_t* codes, const uint8_t* scales,
-                    const float* ts, const float* t, int tks, const uint16_t* b, int r, uint16_t* y) {
+                    const float* ts, const float* t, int tks, const uint16_t* b, int r, uint16_t* y, LoraFuse lf) {
   constexpr int U = 4;
-  const size_t lds = gemv_lds_bytes(MTOK, K, r, W);
-  hipLaunchKernelGGL((gemv_kernel<MTOK, W, U>), dim3((unsigned)((N + 15) / 16)), dim3(W * kWave), lds, st, x, M, N, K,
-                     codes, scales, ts, t, tks, b, r, y);
+  size_t lds = gemv_lds_bytes(MTOK, K, r, W);
+  if (lf.producers > 0) lds = std::max(lds, (size_t)W * kWave * sizeof(float) * 4);  // producers' reduction
+  lf.consumers = (N + 15) / 16;
+  lf.groups = std::min(kLoraGroups, lf.consumers);
+  hipLaunchKernelGGL((gemv_kernel<MTOK, W, U>), dim3((unsigned)(lf.consumers + lf.producers)), dim3(W * kWave), lds, st,
+                     x, M, N, K, codes, scales, ts, t, tks, b, r, y, lf);
   return hipGetLastError();
 }
 
 template <int MTOK>
 hipError_t run_gemv_w(int w, hipStream_t st, const uint16_t* x, int M, int N, int K, const uint8_t* codes,
                       const uint8_t* scales, const float* ts, const float* t, int tks, const uint16_t* b, int r,
-                      uint16_t* y) {
+                      uint16_t* y, const LoraFuse& lf) {
   switch (w) {
-    case 1: return run_gemv<MTOK, 1>(st, x, M, N, K, codes, scales, ts, t, tks, b, r, y);
-    case 2: return run_gemv<MTOK, 2>(st, x, M, N, K, codes, scales, ts, t, tks, b, r, y);
-    case 4: return run_gemv<MTOK, 4>(st, x, M, N, K, codes, scales, ts, t, tks, b, r, y);
-    case 8: return run_gemv<MTOK, 8>(st, x, M, N, K, codes, scales, ts, t, tks, b, r, y);
-    case 16: return run_gemv<MTOK, 16>(st, x, M, N, K, codes, scales, ts, t, tks, b, r, y);
+    case 1: return run_gemv<MTOK, 1>(st, x, M, N, K, codes, scales, ts, t, tks, b, r, y, lf);
+    case 2: return run_gemv<MTOK, 2>(st, x, M, N, K, codes, scales, ts, t, tks, b, r, y, lf);
+    case 4: return run_gemv<MTOK, 4>(st, x, M, N, K, codes, scales, ts, t, tks, b, r, y, lf);
+    case 8: return run_gemv<MTOK, 8>(st, x, M, N, K, codes, scales, ts, t, tks, b, r, y, lf);
+    case 16: return run_gemv<MTOK, 16>(st, x, M, N, K, codes, scales, ts, t, tks, b, r, y, lf);
     default: return hipErrorInvalidValue;
   }
 }
@@ -1375,15 +1416,12 @@ static hipError_t launch_splitk(const SplitkCfg& c, hipStream_t st, const uint16
 }
 
 const char* fp4_linear_kernel_name(int64_t m, int64_t n, int64_t k, int64_t r) {
-  static const char* const kNames[4][3][5] = {
+  static const char* const kNames[2][5] = {
 #define FP4RL_NAME_ROW(MT_, NT_)                                                                           \
   {"skinny_kernel<" #MT_ ", " #NT_ ", 1>", "skinny_kernel<" #MT_ ", " #NT_ ", 2>",                          \
    "skinny_kernel<" #MT_ ", " #NT_ ", 4>", "skinny_kernel<" #MT_ ", " #NT_ ", 8>",                          \
    "skinny_kernel<" #MT_ ", " #NT_ ", 16>"}
-      {FP4RL_NAME_ROW(1, 1), FP4RL_NAME_ROW(1, 2), FP4RL_NAME_ROW(1, 4)},
-      {FP4RL_NAME_ROW(2, 1), FP4RL_NAME_ROW(2, 2), FP4RL_NAME_ROW(2, 4)},
-      {FP4RL_NAME_ROW(4, 1), FP4RL_NAME_ROW(4, 2), FP4RL_NAME_ROW(4, 4)},
-      {FP4RL_NAME_ROW(8, 1), FP4RL_NAME_ROW(8, 2), FP4RL_NAME_ROW(8, 4)},
+      FP4RL_NAME_ROW(1, 1), FP4RL_NAME_ROW(1, 2),
 #undef FP4RL_NAME_ROW
   };
   static const char* const kGemv[2][5] = {
@@ -1407,17 +1445,15 @@ const char* fp4_linear_kernel_name(int64_t m, int64_t n, int64_t k, int64_t r) {
     return kSplitk[sc.tn == 2 ? 0 : 1][wi];
   }
   const SkinnyCfg c = pick_skinny(m, n, k);
-  const int mi = c.mt == 1 ? 0 : c.mt == 2 ? 1 : c.mt == 4 ? 2 : 3;
-  const int ni = c.nt == 1 ? 0 : c.nt == 2 ? 1 : 2;
   int wi = 0;
   while ((1 << wi) < c.waves) ++wi;
-  return kNames[mi][ni][wi];
+  return kNames[c.nt == 1 ? 0 : 1][wi];
 }
 
 bool linear_fuses_lora(int64_t m, int64_t n, int64_t k) {
   (void)n;
   (void)k;
-  return use_splitk(m);
+  return m <= 128;  // every decode kernel (GEMV, skinny: one token group; split-K)
 }
 
 int64_t lora_slice_len(int64_t k, int splits) { return ((k + splits - 1) / splits + 31) / 32 * 32; }
@@ -1432,8 +1468,8 @@ hipError_t launch_fp4_linear(const uint16_t* x, int64_t m, int64_t n, int64_t k,
   const int M = (int)m, N = (int)n, K = (int)k, R = (int)r;
   if (use_gemv(m, n, k, r)) {
     const int w = gemv_waves(n, k);
-    return m == 1 ? run_gemv_w<1>(w, stream, x, M, N, K, codes, scales, tensor_scale, t, tks, b, R, y)
-                  : run_gemv_w<2>(w, stream, x, M, N, K, codes, scales, tensor_scale, t, tks, b, R, y);
+    return m == 1 ? run_gemv_w<1>(w, stream, x, M, N, K, codes, scales, tensor_scale, t, tks, b, R, y, lf)
+                  : run_gemv_w<2>(w, stream, x, M, N, K, codes, scales, tensor_scale, t, tks, b, R, y, lf);
   }
   if (use_splitk(m))
     return launch_splitk(pick_splitk(m, n, k), stream, x, M, N, K, codes, scales, tensor_scale, t, tks, b, R, y, part,
@@ -1459,12 +1495,13 @@ hipError_t launch_fp4_linear(const uint16_t* x, int64_t m, int64_t n, int64_t k,
                        tensor_scale, t, tks, b, R, y);
     return hipGetLastError();
   }
+  // 3..16 tokens: one token tile, so grid.y is 1
   const SkinnyCfg cfg = pick_skinny(m, n, k);
   const dim3 grid((unsigned)((n + 16 * cfg.nt - 1) / (16 * cfg.nt)), (unsigned)((m + 16 * cfg.mt - 1) / (16 * cfg.mt)));
 #define FP4RL_SKINNY(MT_, NT_) \
   if (cfg.mt == MT_ && cfg.nt == NT_) \
-    return run_skinny_w<MT_, NT_>(cfg.waves, grid, stream, x, M, N, K, codes, scales, tensor_scale, t, tks, b, R, y);
-  FP4RL_SKINNY(1, 1) FP4RL_SKINNY(1, 2) FP4RL_SKINNY(2, 2) FP4RL_SKINNY(4, 2) FP4RL_SKINNY(8, 2)
+    return run_skinny_w<MT_, NT_>(cfg.waves, grid, stream, x, M, N, K, codes, scales, tensor_scale, t, tks, b, R, y, lf);
+  FP4RL_SKINNY(1, 1) FP4RL_SKINNY(1, 2)
 #undef FP4RL_SKINNY
   return hipErrorInvalidValue;
 }

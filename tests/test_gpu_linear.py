@@ -90,8 +90,10 @@ def test_split_k_shapes(m, n, k, r):
 # t tile counters, finished-tile count, 64 ready-flag lines of 256 bytes
 COUNTER_BYTES = 4 * (512 + 64 * 64)
 
-FUSED = [  # (m, n, k, r): 16 < m <= 128 with r > 0 computes t inside the linear's launch, in K slices
-    (17, 64, 2048, 13), (33, 50, 1040, 7), (40, 300, 4096, 32), (100, 4608, 3584, 32), (128, 96, 4096, 256),
+FUSED = [  # (m, n, k, r): m <= 128 with r > 0 computes t inside the linear's launch, in K slices
+    (1, 300, 4096, 32), (2, 100, 2048, 16), (1, 4608, 3584, 32), (8, 5000, 3584, 32), (13, 200, 1040, 7),
+    (16, 18944, 3584, 32), (17, 64, 2048, 13), (33, 50, 1040, 7), (40, 300, 4096, 32), (100, 4608, 3584, 32),
+    (128, 96, 4096, 256),
 ]
 
 
