@@ -48,8 +48,9 @@ def nvfp4_bytes(n, k):
 
 
 def main_kernel_bytes(m, n, k, r):
-    """Algorithmic bytes of one main linear launch: weights, B, t, x in, y out."""
-    return nvfp4_bytes(n, k) + 2 * n * r + 4 * m * r + 2 * m * k + 2 * m * n
+    """Algorithmic bytes of one linear launch (up to 128 tokens one launch also makes t = s x A^T):
+    weights, A, B, x in, y out."""
+    return nvfp4_bytes(n, k) + 2 * r * k + 2 * n * r + 2 * m * k + 2 * m * n
 
 
 def linear_flops(m, n, k, r):
@@ -260,22 +261,31 @@ def summarize_trace(trace_dir, out_md, command):
             rows.append((short_kernel_name(r["Name"]), int(r["Calls"]), float(r["TotalDurationNs"]),
                          float(r["AverageNs"]), float(r["MinNs"]), float(r["MaxNs"]), float(r["Percentage"])))
     rows.sort(key=lambda t: -t[2])
-    # dispatches that ran back to back with the same kernel and grid: the
-    # per-kernel timing graphs, which the events in the JSON line bracket
+    # dispatches in runs of at least RUN back-to-back dispatches of the same
+    # kernel and grid: the per-kernel timing graphs (dozens of launches over
+    # weight copies), which the events in the JSON line bracket; a layer pass
+    # never repeats one kernel and grid that often
+    RUN = 8
     b2b = {}
     traces = sorted(glob.glob(os.path.join(trace_dir, "**", "*kernel_trace.csv"), recursive=True))
     if traces:
         with open(traces[0], newline="") as fh:
             tr = sorted(csv.DictReader(fh), key=lambda r: int(r["Start_Timestamp"]))
         key = [(r["Kernel_Name"], r["Grid_Size_X"], r["Grid_Size_Y"], r["Grid_Size_Z"]) for r in tr]
-        for i, r in enumerate(tr):
-            if (i > 0 and key[i - 1] == key[i]) or (i + 1 < len(tr) and key[i + 1] == key[i]):
-                lst = b2b.setdefault(short_kernel_name(r["Kernel_Name"]), [])
-                lst.append(int(r["End_Timestamp"]) - int(r["Start_Timestamp"]))
+        i = 0
+        while i < len(tr):
+            j = i
+            while j + 1 < len(tr) and key[j + 1] == key[i]:
+                j += 1
+            if j - i + 1 >= RUN:
+                lst = b2b.setdefault(short_kernel_name(tr[i]["Kernel_Name"]), [])
+                lst.extend(int(r["End_Timestamp"]) - int(r["Start_Timestamp"]) for r in tr[i:j + 1])
+            i = j + 1
     lines = ["# rocprofv3 kernel trace: " + os.path.basename(out_md).rsplit(".", 1)[0], "",
              "Command (from the repository root):", "", "```", command, "```", "",
-             "'back to back' averages only the dispatches that ran next to a dispatch of the same kernel "
-             "and grid: the per-kernel timing graphs whose HIP-event average the JSON line reports.", "",
+             "'back to back' averages only the dispatches in runs of at least 8 consecutive dispatches of the "
+             "same kernel and grid: the per-kernel timing graphs whose HIP-event average the JSON line reports.",
+             "",
              "| kernel | calls | total ms | avg us | min us | max us | % of GPU time | back-to-back calls | "
              "back-to-back avg us |",
              "|---|---:|---:|---:|---:|---:|---:|---:|---:|"]
@@ -366,9 +376,6 @@ def main():
             "h1": torch.empty_like(xh), "h2": torch.empty_like(xr),
             "ws": {name: fr.linear_workspace(fr.fp4_lora_linear_workspace_bytes(m, n, k, RANK), dev)
                    for name, (n, k) in shapes.items()},
-            "ws_up": {name: fr.linear_workspace(fr.fp4_linear_lora_up_workspace_bytes(m, n, k), dev)
-                      for name, (n, k) in shapes.items()},
-            "t": {name: torch.empty((m, RANK), dtype=torch.float32, device=dev) for name in shapes},
             "y": {name: torch.empty((m, n), dtype=torch.bfloat16, device=dev) for name, (n, k) in shapes.items()},
         }
     weight_bytes_step = sum(nvfp4_bytes(n, k) for n, k in shapes.values()) * len(TOKENS)
@@ -420,9 +427,10 @@ def main():
     value = weight_bytes_step * args.steps / elapsed / 1e9
     del graphs
 
-    # Per-kernel durations: for each (M, linear) a graph of back-to-back main-
-    # kernel launches over distinct weight buffers totalling >= 512 MB (twice
-    # the Infinity Cache), bracketed by HIP events on the launch stream.
+    # Per-kernel durations: for each (M, linear) a graph of back-to-back linear
+    # launches (the fused launch the step runs) over distinct weight buffers
+    # totalling >= 512 MB (twice the Infinity Cache), bracketed by HIP events
+    # on the launch stream.
     clones = {}
     for name, (n, k) in shapes.items():
         lst = [layers[c][name] for c in range(COPIES)]
@@ -438,11 +446,10 @@ def main():
         for name, (n, k) in shapes.items():
             x = layer_input(B, name)
             a, b = lora[name]
-            t = fr.lora_down(x, a, LORA_SCALE, out=B["t"][name])
             gr = torch.cuda.CUDAGraph()
             with torch.cuda.graph(gr):
                 for w in clones[name]:
-                    fr.fp4_linear_lora_up(x, w, t, b, out=B["y"][name], workspace=B["ws_up"][name])
+                    fr.fp4_lora_linear(x, w, a, b, LORA_SCALE, out=B["y"][name], workspace=B["ws"][name])
             gr.replay()
             e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
             e0.record()
@@ -527,13 +534,13 @@ def run_extras(torch, fr, dev, shapes, layer, lora, fp32):
         x[:, ch] *= 20.0
         xs[k] = x.to(torch.bfloat16)
     ys = {name: torch.empty((PREFILL_M, n), dtype=torch.bfloat16, device=dev) for name, (n, k) in shapes.items()}
-    tbuf = torch.empty((PREFILL_M, RANK), dtype=torch.float32, device=dev)
+    pws = fr.linear_workspace(max(fr.fp4_lora_linear_workspace_bytes(PREFILL_M, n, k, RANK)
+                                  for n, k in shapes.values()), dev)
 
     def prefill_pass():
         for name, (n, k) in shapes.items():
             a, b = lora[name]
-            t = fr.lora_down(xs[k], a, LORA_SCALE, out=tbuf)
-            fr.fp4_linear_lora_up(xs[k], layer[name], t, b, out=ys[name])
+            fr.fp4_lora_linear(xs[k], layer[name], a, b, LORA_SCALE, out=ys[name], workspace=pws)
 
     prefill_pass()
     torch.cuda.synchronize()
