@@ -404,6 +404,9 @@ __global__ __launch_bounds__(WAVES * kWave) void skinny_kernel(
   for (int i = 0; i < NT; ++i) toff[i] = (min(rt0 + i, RT - 1) - rt0) * KC;
   // Activations: tokens past M are clamped to the last token (columns never stored).
   const uint16_t* xbase = x + (int64_t)m0 * K;  // uniform
+  // the same rows through a buffer descriptor (32-bit byte offsets: the host keeps 2 M K below 2^31)
+  const __amdgpu_buffer_rsrc_t xrs = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<uint16_t*>(xbase), 0, (int)(2u * (uint32_t)(min(M - m0, 16 * MT)) * (uint32_t)K), kBufferWord3);
   uint32_t xoff[MT];
 #pragma unroll
   for (int j = 0; j < MT; ++j) xoff[j] = (uint32_t)(min(m0 + 16 * j + li, M - 1) - m0) * (uint32_t)K + 8 * lg;
@@ -444,19 +447,18 @@ __global__ __launch_bounds__(WAVES * kWave) void skinny_kernel(
         G.sw[u][i] = __builtin_nontemporal_load(reinterpret_cast<const uint32_t*>(st + slane));
       }
       if constexpr (XPRE) {
-        const uint16_t* xc = xbase + 128 * c;  // uniform
-        if (kfull || c < nchunk - 1) {
+        // pieces past K get an offset beyond the buffer and read as zero (no
+        // per-lane branch: the compiler then waits for exactly the loads
+        // each use needs)
+        const int kv = K - 128 * c - 8 * lg;
 #pragma unroll
-          for (int s = 0; s < 4; ++s)
+        for (int s = 0; s < 4; ++s) {
+          const uint32_t kout = 32 * s < kv ? 0u : 0x80000000u;
 #pragma unroll
-            for (int j = 0; j < MT; ++j) G.xq[u][s][j] = ld16(xc + xoff[j] + 32 * s);
-        } else {  // last, partial chunk: k past K is not read
-          const int kv = K - 128 * c - 8 * lg;
-#pragma unroll
-          for (int s = 0; s < 4; ++s)
-#pragma unroll
-            for (int j = 0; j < MT; ++j)
-              G.xq[u][s][j] = 32 * s < kv ? ld16(xc + xoff[j] + 32 * s) : make_uint4(0, 0, 0, 0);
+          for (int j = 0; j < MT; ++j)
+            G.xq[u][s][j] = __builtin_bit_cast(
+                uint4, __builtin_amdgcn_raw_buffer_load_b128(xrs, (int)((2u * (xoff[j] + 128u * c + 32u * s)) | kout),
+                                                             0, 0));
         }
       }
     }
@@ -491,14 +493,31 @@ __global__ __launch_bounds__(WAVES * kWave) void skinny_kernel(
       }
     }
   };
+  // Two groups in flight. In the steady state every load is issued
+  // unconditionally (a group past this wave's chunks loads clamped chunks),
+  // so the compiler waits for exactly the loads a group uses, never for the
+  // group in flight; the last one or two groups run after the loop.
   Group ga, gb;
-  if (mine > 0) load_group(0, ga);
-  for (int g0 = 0; g0 < mine; g0 += 2 * U) {
-    if (g0 + U < mine) load_group(g0 + U, gb);
+  load_group(0, ga);
+  // (the scheduling barriers keep a group's loads together at its start:
+  // sunk into the previous group's arithmetic they would each be waited on
+  // at once)
+  int g0 = 0;
+  for (; g0 + 2 * U < mine; g0 += 2 * U) {
+    load_group(g0 + U, gb);
+    __builtin_amdgcn_sched_barrier(0);
     compute_group(g0, ga);
-    if (g0 + U >= mine) break;
-    if (g0 + 2 * U < mine) load_group(g0 + 2 * U, ga);
+    load_group(g0 + 2 * U, ga);
+    __builtin_amdgcn_sched_barrier(0);
     compute_group(g0 + U, gb);
+  }
+  if (g0 + U < mine) {
+    load_group(g0 + U, gb);
+    __builtin_amdgcn_sched_barrier(0);
+    compute_group(g0, ga);
+    compute_group(g0 + U, gb);
+  } else {
+    compute_group(g0, ga);
   }
 
   const float st = *tensor_scale;
@@ -617,8 +636,8 @@ __global__ __launch_bounds__(W * kWave) void splitk_kernel(
     const int c = chunk_of(q);
 #pragma unroll
     for (int i = 0; i < TM; ++i) {
-      // plain (cached) loads: the token groups of a row group reuse these tiles from L2
-      const uint4 v = ld16(cbase + (int64_t)(toff[i] + c) * 1024 + clane);
+      // streaming loads: a row group's token groups follow each other on one XCD and find the tiles in L2
+      const uint4 v = ld_nt16(cbase + (int64_t)(toff[i] + c) * 1024 + clane);
       S.cw[i][0] = v.x; S.cw[i][1] = v.y; S.cw[i][2] = v.z; S.cw[i][3] = v.w;
       S.sw[i] = *reinterpret_cast<const uint32_t*>(sbase + (int64_t)(toff[i] + c) * 128 + slane);
     }
@@ -1466,6 +1485,8 @@ hipError_t launch_fp4_linear(const uint16_t* x, int64_t m, int64_t n, int64_t k,
       (!linear_fuses_lora(m, n, k) || lf.mtiles * lf.rtiles > kLoraTileCounters || tks != 1 || lf.slices > 8))
     return hipErrorInvalidValue;
   const int M = (int)m, N = (int)n, K = (int)k, R = (int)r;
+  // the skinny kernel addresses activations with 32-bit byte offsets
+  if (m > 2 && m <= 16 && 2 * m * k > INT32_MAX) return hipErrorInvalidValue;
   if (use_gemv(m, n, k, r)) {
     const int w = gemv_waves(n, k);
     return m == 1 ? run_gemv_w<1>(w, stream, x, M, N, K, codes, scales, tensor_scale, t, tks, b, R, y, lf)

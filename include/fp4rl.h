@@ -119,14 +119,15 @@ fp4rl_status fp4rl_nvfp4_to_tiled(const uint8_t* codes, const uint8_t* scales, i
  *                       + sum_j t[m][j] B[n][j] ),   t = lora_scale * x A^T.
  * x bf16 [m][k]; codes/scales/tensor_scale of an [n][k] matrix in the
  * FP4RL_TILED layout; A bf16 [r][k]; B bf16 [n][r]; y bf16 [m][n].
- * k % 16 == 0; m * k < 2^31; 0 <= r <= 256; r == 0 or lora_a == lora_b ==
+ * k % 16 == 0; m * k < 2^31 (< 2^30 for 3 <= m <= 16); 0 <= r <= 256;
+ * r == 0 or lora_a == lora_b ==
  * NULL means no LoRA term. Accumulation is fp32; the output is rounded once
  * to bf16.
- * For 16 < m <= 128 one launch does all of it: its first workgroups compute
+ * For m <= 128 one launch does all of it: its first workgroups compute
  * t = lora_scale * x A^T (in K slices; the last slice of each 16x16 tile of t
  * to finish adds the slices) and the others wait for t only before their
- * epilogue. Otherwise the LoRA down-projection (when r > 0) and then the main
- * kernel are launched, the kernel chosen by m (see
+ * epilogue. For m > 128 the LoRA down-projection (when r > 0) and then the
+ * main kernel are launched. The main kernel is chosen by m (see
  * fp4rl_fp4_linear_kernel_name).
  * Workspace: fp4rl_fp4_lora_linear_workspace(m, n, k, r) bytes (0 when
  * neither split below is used), 16-byte aligned. It starts with 4608

@@ -204,7 +204,14 @@ def test_halves_match_fused_call():
     y_halves = fr.fp4_linear_lora_up(xt, wq, t, bt)
     y_fused = fr.fp4_lora_linear(xt, wq, at, bt, LORA_SCALE)
     torch.cuda.synchronize()
-    assert torch.equal(y_halves, y_fused)
+    # t is summed by differently shaped workgroups in the two calls (fp32
+    # rounding order differs), so the outputs agree to bf16 rounding, and each
+    # matches the oracle
+    ref = linear.lora_linear(x, *q, a, b, LORA_SCALE)
+    _check(bf16_from_dev(y_halves), ref, "halves")
+    _check(bf16_from_dev(y_fused), ref, "fused")
+    diff = (y_halves.float() - y_fused.float()).abs()
+    assert float(diff.max()) <= 2.0 ** -7 * float(y_fused.float().abs().max())
     t_ref = linear.lora_down(x, a, LORA_SCALE)
     assert rel_l2(t.cpu().numpy(), t_ref) < 1e-5
 
