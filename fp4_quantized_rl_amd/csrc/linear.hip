@@ -833,9 +833,10 @@ __global__ __launch_bounds__(W * kWave) void splitk_kernel(
 
 // ---------------------------------------------------------------------------
 // Prefill GEMM (M > 128 tokens): a workgroup computes 256 output features x
-// 128 tokens over all of K; each of its 256 / (16 TM) waves owns TM row tiles
-// (16 TM features) against all 8 token tiles, so one dequantised weight
-// fragment feeds 8 MFMAs and one activation fragment TM.
+// 128 tokens over all of K with (256 / 16 TM) x (8 / TN) waves; each owns TM
+// row tiles (16 TM features) against TN of the 8 token tiles, so one
+// dequantised weight fragment feeds TN MFMAs and one activation fragment TM.
+// The LDS reads per MFMA fall with TM, the dequantisation per MFMA with TN.
 //   Activation chunks (128 tokens x 128 k, 32 KB) are loaded by all threads
 //   with consecutive threads on consecutive 16-byte pieces of a token row,
 //   held one chunk ahead in registers and written to one of two LDS slabs
@@ -849,12 +850,12 @@ __global__ __launch_bounds__(W * kWave) void splitk_kernel(
 // ---------------------------------------------------------------------------
 constexpr int kPfRows = 256, kPfTok = 128;
 
-template <int TM>
-__global__ __launch_bounds__(kPfRows / 16 / TM * kWave) void prefill_kernel(
+template <int TM, int TN = 8>
+__global__ __launch_bounds__(kPfRows / 16 / TM * (8 / TN) * kWave) void prefill_kernel(
     const uint16_t* __restrict__ x, int M, int N, int K, const uint8_t* __restrict__ codes,
     const uint8_t* __restrict__ scales, const float* __restrict__ tensor_scale, const float* __restrict__ t, int tks,
     const uint16_t* __restrict__ lb, int r, uint16_t* __restrict__ y) {
-  constexpr int TN = 8, W = kPfRows / 16 / TM, D = 2;
+  constexpr int FG = kPfRows / 16 / TM, W = FG * (8 / TN), D = 2;  // FG feature groups of waves
   constexpr int NTH = W * kWave;
   constexpr int XPT = kPfTok * 16 / NTH;  // 16-byte activation pieces per thread and chunk (8)
   __shared__ __align__(16) uint16_t xs[2][kPfTok * kXRow];
@@ -872,7 +873,9 @@ __global__ __launch_bounds__(kPfRows / 16 / TM * kWave) void prefill_kernel(
   const int sr = s / nstt, stt = s - sr * nstt;
   const int rg = 8 * sr + (within & 7), tg = 4 * stt + (within >> 3);
   if (rg >= GR || tg >= GT) return;
-  const int rt0 = rg * (kPfRows / 16) + wave * TM, n0 = 16 * rt0, m0 = tg * kPfTok;
+  const int fw = wave % FG, tw = wave / FG;  // this wave's feature group and token-tile group
+  const int rt0 = rg * (kPfRows / 16) + fw * TM, n0 = 16 * rt0, m0 = tg * kPfTok;
+  const int tt0 = tw * TN;  // first token tile of this wave
 
   const uint8_t* cbase = codes + (int64_t)rt0 * KC * 1024;  // uniform per wave
   const uint8_t* sbase = scales + (int64_t)rt0 * KC * 128;
@@ -886,21 +889,33 @@ __global__ __launch_bounds__(kPfRows / 16 / TM * kWave) void prefill_kernel(
   // groups use a constant stride.
   constexpr int XR = NTH / 16;
   static_assert(XPT * XR == kPfTok, "the pieces of a chunk cover its token rows");
+  // Offsets are bytes from this token group's first row, through a buffer
+  // descriptor (32-bit offsets: the host keeps 256 K below 2^31); a piece
+  // past K gets an offset with bit 31 set and reads as zero.
   const int xrow0 = threadIdx.x >> 4, xpc = threadIdx.x & 15;
   const bool xfull = m0 + kPfTok <= M;
-  const uint32_t xoff0 = 2u * ((uint32_t)min(m0 + xrow0, M - 1) * (uint32_t)K + 8 * xpc);
+  const uint32_t xoff0 = 2u * ((uint32_t)xrow0 * (uint32_t)K + 8 * xpc);
   const uint32_t xstride = 2u * XR * (uint32_t)K;  // XR token rows
   auto xoff = [&](int q) -> uint32_t {
     return xfull ? xoff0 + (uint32_t)q * xstride
-                 : 2u * ((uint32_t)min(m0 + xrow0 + XR * q, M - 1) * (uint32_t)K + 8 * xpc);
+                 : 2u * ((uint32_t)(min(m0 + xrow0 + XR * q, M - 1) - m0) * (uint32_t)K + 8 * xpc);
   };
+  const __amdgpu_buffer_rsrc_t xrs = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<uint16_t*>(x + (int64_t)m0 * K), 0, (int)(2u * (uint32_t)min(kPfTok, M - m0) * (uint32_t)K),
+      kBufferWord3);
   const uint32_t xlds0 = xrow0 * kXRow + 8 * xpc;  // bf16 units; piece q adds XR q rows
 
   struct WStage {
     uint32_t cw[TM][4];
     uint32_t sw[TM];
   };
+  // Every load of the main loop is issued unconditionally (chunks past the
+  // last are clamped to it: loaded, never used), so the compiler can count
+  // the loads in flight and wait for exactly the ones a step uses; skipped
+  // or per-lane loads make it wait for all of them, which drains the
+  // prefetch every chunk.
   auto load_w = [&](int c, WStage& S) {
+    c = min(c, KC - 1);
 #pragma unroll
     for (int i = 0; i < TM; ++i) {
       // plain (cached) loads: the other token groups of the super-tile reuse these tiles from L2
@@ -913,14 +928,12 @@ __global__ __launch_bounds__(kPfRows / 16 / TM * kWave) void prefill_kernel(
     uint4 v[XPT];
   };
   auto load_x = [&](int c, XStage& X) {
-    const uint8_t* xc = reinterpret_cast<const uint8_t*>(x + 128 * c);  // uniform
-    if (c < KC - 1 || (K & 127) == 0) {
+    c = min(c, KC - 1);
+    // pieces past K (K % 16 == 0: a piece is all in or out) read as zero
+    const uint32_t kout = 128 * c + 8 * xpc < K ? 0u : 0x80000000u;
 #pragma unroll
-      for (int q = 0; q < XPT; ++q) X.v[q] = ld16(xc + xoff(q));
-    } else {  // the last, partial chunk: pieces past K read as zero (K % 16 == 0: a piece is all in or out)
-#pragma unroll
-      for (int q = 0; q < XPT; ++q) X.v[q] = 128 * c + 8 * xpc < K ? ld16(xc + xoff(q)) : make_uint4(0, 0, 0, 0);
-    }
+    for (int q = 0; q < XPT; ++q)
+      X.v[q] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(xrs, (int)((xoff(q) + 256u * c) | kout), 0, 0));
   };
   auto store_x = [&](const XStage& X, uint16_t* slab) {
 #pragma unroll
@@ -949,7 +962,7 @@ __global__ __launch_bounds__(kPfRows / 16 / TM * kWave) void prefill_kernel(
       bf16x8 b[TN];
 #pragma unroll
       for (int jj = 0; jj < TN; ++jj)
-        b[jj] = as_bf16x8(*reinterpret_cast<const uint4*>(slab + (16 * jj + li) * kXRow + 32 * st + 8 * lg));
+        b[jj] = as_bf16x8(*reinterpret_cast<const uint4*>(slab + (16 * (tt0 + jj) + li) * kXRow + 32 * st + 8 * lg));
       if (st < 3) {
 #pragma unroll
         for (int i = 0; i < TM; ++i) an[i] = dequant8(S.cw[i][st + 1], sc[i][st + 1]);
@@ -958,10 +971,11 @@ __global__ __launch_bounds__(kPfRows / 16 / TM * kWave) void prefill_kernel(
       for (int jj = 0; jj < TN; ++jj)
 #pragma unroll
         for (int i = 0; i < TM; ++i) acc[i][jj] = mfma16x16x32(a[i], b[jj], acc[i][jj]);
+      constexpr int VPM = (TM * 17 + TM * TN - 1) / (TM * TN);  // VALU of the next step's dequantisation per MFMA
 #pragma unroll
       for (int g = 0; g < TM * TN; ++g) {
-        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // one MFMA
-        __builtin_amdgcn_sched_group_barrier(0x002, 2, 0);  // two VALU
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);    // one MFMA
+        __builtin_amdgcn_sched_group_barrier(0x002, VPM, 0);  // VPM VALU
       }
       if (st < 3) {
 #pragma unroll
@@ -977,24 +991,22 @@ __global__ __launch_bounds__(kPfRows / 16 / TM * kWave) void prefill_kernel(
   WStage ws[D];
   XStage xr[2];
 #pragma unroll
-  for (int u = 0; u < D; ++u)
-    if (u < KC) load_w(u, ws[u]);
+  for (int u = 0; u < D; ++u) load_w(u, ws[u]);
   load_x(0, xr[0]);
-  if (KC > 1) load_x(1, xr[1]);
+  load_x(1, xr[1]);
   store_x(xr[0], xs[0]);
-  if (KC > 2) load_x(2, xr[0]);
+  load_x(2, xr[0]);
   for (int q0 = 0; q0 < KC; q0 += D) {
 #pragma unroll
     for (int u = 0; u < D; ++u) {
       const int q = q0 + u;
       if (q >= KC) break;  // uniform across the workgroup
       __syncthreads();     // slab q % 2 is complete; slab (q + 1) % 2 is no longer read
-      if (q + 1 < KC) {
-        store_x(xr[(u + 1) & 1], xs[(u + 1) & 1]);
-        if (q + 3 < KC) load_x(q + 3, xr[(u + 1) & 1]);
-      }
+      // chunk q + 1 to the other slab (after the last chunk: a copy of it, never read)
+      store_x(xr[(u + 1) & 1], xs[(u + 1) & 1]);
+      load_x(q + 3, xr[(u + 1) & 1]);
       compute(ws[u], xs[u & 1]);
-      if (q + D < KC) load_w(q + D, ws[u]);
+      load_w(q + D, ws[u]);
     }
   }
 
@@ -1028,18 +1040,18 @@ __global__ __launch_bounds__(kPfRows / 16 / TM * kWave) void prefill_kernel(
       }
       __syncthreads();
       for_tiles<TM, TN>([&](auto I, auto J) {
-        const bf16x8 a = as_bf16x8(*reinterpret_cast<const uint4*>(bl + (wave * 16 * TM + 16 * I + li) * LROW + 8 * lg));
-        const bf16x8 bh = as_bf16x8(*reinterpret_cast<const uint4*>(th + (16 * J + li) * LROW + 8 * lg));
-        const bf16x8 bo = as_bf16x8(*reinterpret_cast<const uint4*>(tlo + (16 * J + li) * LROW + 8 * lg));
+        const bf16x8 a = as_bf16x8(*reinterpret_cast<const uint4*>(bl + (fw * 16 * TM + 16 * I + li) * LROW + 8 * lg));
+        const bf16x8 bh = as_bf16x8(*reinterpret_cast<const uint4*>(th + (16 * (tt0 + J) + li) * LROW + 8 * lg));
+        const bf16x8 bo = as_bf16x8(*reinterpret_cast<const uint4*>(tlo + (16 * (tt0 + J) + li) * LROW + 8 * lg));
         acc[I][J] = mfma16x16x32(a, bh, acc[I][J]);
         acc[I][J] = mfma16x16x32(a, bo, acc[I][J]);
       });
     }
   }
-  // lane holds features n0 + 16 I + 4 lg + v of token m0 + 16 J + li
+  // lane holds features n0 + 16 I + 4 lg + v of token m0 + 16 (tt0 + J) + li
   const bool nvec = (N & 3) == 0;
   for_tiles<TM, TN>([&](auto I, auto J) {
-    const int m = m0 + 16 * J + li, nf = n0 + 16 * I + 4 * lg;
+    const int m = m0 + 16 * (tt0 + J) + li, nf = n0 + 16 * I + 4 * lg;
     if (m < M) {
       uint16_t* yp = y + (int64_t)m * N + nf;
       const f32x4 v = acc[I][J];
@@ -1500,6 +1512,11 @@ hipError_t launch_fp4_linear(const uint16_t* x, int64_t m, int64_t n, int64_t k,
     const int64_t supers = (gr + 7) / 8 * ((gt + 3) / 4);  // super-tiles of 8 x 4 workgroups, dealt to 8 XCDs
     const int64_t grid = 8 * 32 * ((supers + 7) / 8);
 #ifdef FP4RL_TUNING
+    if (g_tune_w == 44) {
+      hipLaunchKernelGGL((prefill_kernel<4, 4>), dim3((unsigned)grid), dim3(512), 0, stream, x, M, N, K, codes, scales,
+                         tensor_scale, t, tks, b, R, y);
+      return hipGetLastError();
+    }
     if (g_tune_w == 4 || g_tune_w == 1) {
       if (g_tune_w == 4)
         hipLaunchKernelGGL(prefill_kernel<4>, dim3((unsigned)grid), dim3(256), 0, stream, x, M, N, K, codes, scales,
