@@ -577,8 +577,8 @@ __global__ __launch_bounds__(WAVES * kWave) void skinny_kernel(
 // ---------------------------------------------------------------------------
 constexpr int kXRow = 136;  // bf16 per LDS token row: 128 + 8 of padding
 
-template <int TM, int TN, int W>
-__global__ __launch_bounds__(W * kWave) void splitk_kernel(
+template <int TM, int TN, int W, int D>
+__global__ __launch_bounds__(W * kWave) __attribute__((amdgpu_waves_per_eu(D == 2 ? 3 : 1))) void splitk_kernel(
     const uint16_t* __restrict__ x, int M, int N, int K, const uint8_t* __restrict__ codes,
     const uint8_t* __restrict__ scales, const float* __restrict__ tensor_scale, const float* __restrict__ t, int tks,
     const uint16_t* __restrict__ lb, int r, uint16_t* __restrict__ y, int cpz, int nsplit, float* __restrict__ part,
@@ -684,27 +684,32 @@ __global__ __launch_bounds__(W * kWave) void splitk_kernel(
     }
   };
 
-  // Pipeline: a ring of D weight stages (D chunks of weights in flight:
-  // enough to cover HBM latency with one or two waves per SIMD), the next
-  // chunk's activations in registers while the current one is in LDS. The
+  // Pipeline: a ring of D weight stages (D chunks of weights in flight) and
+  // XS activation stages in registers while the current chunk is in LDS.
+  // D = 3 with two activation stages covers HBM latency at one wave per
+  // SIMD (shapes with few workgroups); D = 2 with one activation stage
+  // needs few enough registers for three waves per SIMD, which hide each
+  // other's latency when the grid has more than one workgroup per CU. The
   // ring is unrolled so every stage lives in fixed registers. The slab is
   // rewritten only after this wave's reads of it were issued (LDS operations
   // of one wave complete in order).
-  constexpr int D = 3, UNR = 6;  // weight stages; unrolled by lcm(D, 2) so both rings use fixed registers
+  static_assert(D == 2 || D == 3, "two or three weight stages");
+  constexpr int XS = D - 1, UNR = D * XS;  // unrolled by lcm(D, XS) so both rings use fixed registers
   WStage ws[D];
-  XStage xr[2];  // activations of chunks q + 1 and q + 2 in flight while chunk q is computed
+  XStage xr[XS];  // activations of chunks q + 1 .. q + XS in flight while chunk q is computed
 #pragma unroll
   for (int u = 0; u < D; ++u)
     if (u < mine) load_w(u, ws[u]);
-  if (mine > 0) load_x(0, xr[0]);
-  if (mine > 1) load_x(1, xr[1]);
+#pragma unroll
+  for (int u = 0; u < XS; ++u)
+    if (u < mine) load_x(u, xr[u]);
   for (int q0 = 0; q0 < mine; q0 += UNR) {
 #pragma unroll
     for (int u = 0; u < UNR; ++u) {
       const int q = q0 + u;
       if (q >= mine) break;  // uniform across the wave
-      store_x(xr[u & 1]);
-      if (q + 2 < mine) load_x(q + 2, xr[u & 1]);
+      store_x(xr[u % XS]);
+      if (q + XS < mine) load_x(q + XS, xr[u % XS]);
       compute(ws[u % D]);
       if (q + D < mine) load_w(q + D, ws[u % D]);
     }
@@ -1235,6 +1240,14 @@ size_t gemv_lds_bytes(int mtok, int64_t k, int64_t r, int waves) {
   return (size_t)(mtok * kp * 2 + (mtok * r + 16 * r) * 4 + waves * mtok * 16 * 4);
 }
 
+#ifdef FP4RL_TUNING
+// scratch builds only: launch shapes forced from the environment
+int tune_env(const char* name) {
+  const char* v = getenv(name);
+  return v ? atoi(v) : 0;
+}
+#endif
+
 struct SkinnyCfg {
   int mt, nt, waves;
 };
@@ -1297,6 +1310,9 @@ hipError_t run_skinny_w(int w, dim3 grid, hipStream_t st, const uint16_t* x, int
 int lora_splits(int64_t m, int64_t k, int64_t r) {
   (void)r;
   if (m > 128) return 1;  // prefill: token tiles already fill the chip
+#ifdef FP4RL_TUNING
+  if (tune_env("FP4RL_TUNE_SLICES") > 0) return tune_env("FP4RL_TUNE_SLICES");
+#endif
   // Up to 8 K-slices of at least 512 k (the linear's epilogue adds them in
   // order): enough workgroups for a long K without a separate reduction.
   const int64_t by_k = std::max<int64_t>(1, k / 512);
@@ -1379,11 +1395,8 @@ hipError_t run_gemv_w(int w, hipStream_t st, const uint16_t* x, int M, int N, in
 // least one chunk and the fp32 partials (written and read once) stay within
 // a third of the weight bytes.
 struct SplitkCfg {
-  int tn, w, s, cpz, gx, gy;
+  int tn, w, s, cpz, gx, gy, d;
 };
-#ifdef FP4RL_TUNING
-int g_tune_s = 0, g_tune_w = 0;  // scratch builds only: forced split and waves
-#endif
 
 static bool use_splitk(int64_t m) { return m > 16 && m <= 128; }
 
@@ -1400,12 +1413,23 @@ static SplitkCfg pick_splitk(int64_t m, int64_t n, int64_t k) {
          4.0 * (double)(2 * s) * (double)m * (double)n * 2.0 <= wbytes / 3.0)
     s *= 2;
 #ifdef FP4RL_TUNING
-  if (g_tune_s > 0) s = g_tune_s;
-  if (g_tune_w > 0) c.w = g_tune_w;
+  if (tune_env("FP4RL_TUNE_S") > 0) s = tune_env("FP4RL_TUNE_S");
+  if (tune_env("FP4RL_TUNE_TN") > 0) {
+    c.tn = tune_env("FP4RL_TUNE_TN");
+    c.gy = (int)((m + 16 * c.tn - 1) / (16 * c.tn));
+  }
 #endif
   c.cpz = (int)((kc + s - 1) / s);
   c.s = (int)((kc + c.cpz - 1) / c.cpz);  // no empty K range
   if ((int64_t)c.gx * c.gy > kSplitCounters) c.s = 1, c.cpz = (int)kc;  // a split needs one counter per tile
+  // more output tiles than CUs (wide matrices): the lighter pipeline at three
+  // waves per SIMD; fewer: the deeper one, which hides latency at one wave
+  // per SIMD (measured: gate 3584 -> 18944 at 64 tokens 28.8 -> 26.1 us,
+  // while o 3584 -> 3584 is 1 us slower with it)
+  c.d = (int64_t)c.gx * c.gy > 256 ? 2 : 3;
+#ifdef FP4RL_TUNING
+  if (tune_env("FP4RL_TUNE_D") > 0) c.d = tune_env("FP4RL_TUNE_D");
+#endif
   return c;
 }
 
@@ -1416,7 +1440,7 @@ size_t linear_partial_bytes(int64_t m, int64_t n, int64_t k) {
   return ((size_t)c.s * (size_t)m * (size_t)n * sizeof(float) + 255) / 256 * 256;
 }
 
-template <int TN, int W>
+template <int TN, int W, int D>
 hipError_t run_splitk(const SplitkCfg& c, hipStream_t st, const uint16_t* x, int M, int N, int K, const uint8_t* codes,
                       const uint8_t* scales, const float* ts, const float* t, int tks, const uint16_t* b, int r,
                       uint16_t* y, float* part, uint32_t* counters, LoraFuse lf) {
@@ -1426,7 +1450,7 @@ hipError_t run_splitk(const SplitkCfg& c, hipStream_t st, const uint16_t* x, int
   lf.consumers = c.gx * c.gy;  // one waiting workgroup per output tile (the last of its K split)
   lf.groups = std::min(kLoraGroups, lf.consumers);
   const unsigned grid = (unsigned)(lf.producers + main_grid);
-  hipLaunchKernelGGL((splitk_kernel<4, TN, W>), dim3(grid), dim3(W * kWave), 0, st, x, M, N, K, codes, scales, ts, t,
+  hipLaunchKernelGGL((splitk_kernel<4, TN, W, D>), dim3(grid), dim3(W * kWave), 0, st, x, M, N, K, codes, scales, ts, t,
                      tks, b, r, y, c.cpz, c.s, c.s > 1 ? part : nullptr, c.s > 1 ? counters : nullptr, lf);
   return hipGetLastError();
 }
@@ -1435,12 +1459,14 @@ static hipError_t launch_splitk(const SplitkCfg& c, hipStream_t st, const uint16
                                 const uint8_t* codes, const uint8_t* scales, const float* ts, const float* t, int tks,
                                 const uint16_t* b, int r, uint16_t* y, float* part, uint32_t* counters,
                                 const LoraFuse& lf) {
-#define FP4RL_SPLITK(TN_, W_) \
-  if (c.tn == TN_ && c.w == W_) \
-    return run_splitk<TN_, W_>(c, st, x, M, N, K, codes, scales, ts, t, tks, b, r, y, part, counters, lf);
+#define FP4RL_SPLITK(TN_, W_)                                                                              \
+  if (c.tn == TN_ && c.w == W_ && c.d == 2)                                                                 \
+    return run_splitk<TN_, W_, 2>(c, st, x, M, N, K, codes, scales, ts, t, tks, b, r, y, part, counters, lf); \
+  if (c.tn == TN_ && c.w == W_ && c.d == 3)                                                                 \
+    return run_splitk<TN_, W_, 3>(c, st, x, M, N, K, codes, scales, ts, t, tks, b, r, y, part, counters, lf);
   FP4RL_SPLITK(2, 4)
 #ifdef FP4RL_TUNING
-  FP4RL_SPLITK(2, 2) FP4RL_SPLITK(2, 8)
+  FP4RL_SPLITK(4, 4)
 #endif
 #undef FP4RL_SPLITK
   return hipErrorInvalidValue;
@@ -1468,12 +1494,9 @@ const char* fp4_linear_kernel_name(int64_t m, int64_t n, int64_t k, int64_t r) {
   if (m > 128) return "prefill_kernel<2>";
   if (use_splitk(m)) {
     const SplitkCfg sc = pick_splitk(m, n, k);
-    static const char* const kSplitk[2][4] = {
-        {"splitk_kernel<4, 2, 1>", "splitk_kernel<4, 2, 2>", "splitk_kernel<4, 2, 4>", "splitk_kernel<4, 2, 8>"},
-        {"splitk_kernel<4, 4, 1>", "splitk_kernel<4, 4, 2>", "splitk_kernel<4, 4, 4>", "splitk_kernel<4, 4, 8>"}};
-    int wi = 0;
-    while ((1 << wi) < sc.w) ++wi;
-    return kSplitk[sc.tn == 2 ? 0 : 1][wi];
+    static const char* const kSplitk[2][2] = {{"splitk_kernel<4, 2, 4, 2>", "splitk_kernel<4, 2, 4, 3>"},
+                                              {"splitk_kernel<4, 4, 4, 2>", "splitk_kernel<4, 4, 4, 3>"}};
+    return kSplitk[sc.tn == 2 ? 0 : 1][sc.d == 2 ? 0 : 1];
   }
   const SkinnyCfg c = pick_skinny(m, n, k);
   int wi = 0;
@@ -1512,6 +1535,7 @@ hipError_t launch_fp4_linear(const uint16_t* x, int64_t m, int64_t n, int64_t k,
     const int64_t supers = (gr + 7) / 8 * ((gt + 3) / 4);  // super-tiles of 8 x 4 workgroups, dealt to 8 XCDs
     const int64_t grid = 8 * 32 * ((supers + 7) / 8);
 #ifdef FP4RL_TUNING
+    const int g_tune_w = tune_env("FP4RL_TUNE_PREFILL");
     if (g_tune_w == 44) {
       hipLaunchKernelGGL((prefill_kernel<4, 4>), dim3((unsigned)grid), dim3(512), 0, stream, x, M, N, K, codes, scales,
                          tensor_scale, t, tks, b, R, y);
