@@ -81,13 +81,21 @@ __device__ __forceinline__ uint32_t e4m3_encode(float r) {
 }
 
 // E2M1 code of x for block step D (Ds = D or D*2^64, xs = 1 or 2^64).
+// E2M1 code of x for block scale D (Ds = D, or D * 2^64 with xs = 2^64 for
+// tiny D). The magnitude index k is the number of grid midpoints m_i * D
+// (m = 0.25, 0.75, 1.25, 1.75, 2.5, 3.5, 5) that |x| passes, where a tie goes
+// to the even index: |x| must exceed the midpoints below an odd index
+// (0.25, 1.25, 2.5, 5) and reach those below an even one (0.75, 1.75, 3.5).
+// The passes are monotone in |x|, so k is found by binary search: three
+// exact sign tests instead of seven.
 __device__ __forceinline__ uint32_t e2m1_encode(float x, bool dzero, float Ds, float xs) {
 #pragma clang fp contract(off)
   const float ax = fabsf(x) * xs;
-  uint32_t k = (uint32_t)(fmaf(0.25f, Ds, -ax) < 0.0f) + (uint32_t)(fmaf(0.75f, Ds, -ax) <= 0.0f) +
-               (uint32_t)(fmaf(1.25f, Ds, -ax) < 0.0f) + (uint32_t)(fmaf(1.75f, Ds, -ax) <= 0.0f) +
-               (uint32_t)(fmaf(2.5f, Ds, -ax) < 0.0f) + (uint32_t)(fmaf(3.5f, Ds, -ax) <= 0.0f) +
-               (uint32_t)(fmaf(5.0f, Ds, -ax) < 0.0f);
+  const bool t4 = fmaf(1.75f, Ds, -ax) <= 0.0f;  // k >= 4
+  const bool t2 = fmaf(t4 ? 3.5f : 0.75f, Ds, -ax) <= 0.0f;  // k >= 4 t4 + 2
+  const float mlo = t4 ? (t2 ? 5.0f : 2.5f) : (t2 ? 1.25f : 0.25f);
+  const bool t1 = fmaf(mlo, Ds, -ax) < 0.0f;  // k odd
+  uint32_t k = 4u * (uint32_t)t4 + 2u * (uint32_t)t2 + (uint32_t)t1;
   k = dzero ? 0u : k;
   return k | ((__float_as_uint(x) >> 28) & 8u);
 }
@@ -111,17 +119,19 @@ __device__ __forceinline__ void load_quarter(const void* w, int64_t idx, float v
 // holds in byte j the scale of block 8 c + 2 j + p. So a block kb (8 per
 // chunk) lands in word j = kb/2 of lane groups g = 2 (kb & 1) and g + 1, and
 // its quarter q (4 elements) in group g + q/2, byte 2 (q & 1) of the word.
+// Destination of quarter q (elements 4q .. 4q+3) of block kb of row n.
 template <bool TILED>
-__device__ __forceinline__ void block_dest(int64_t b, int q, uint32_t kblocks, uint32_t kc, int64_t& code_off,
+__device__ __forceinline__ void block_dest(int64_t b, uint32_t n, uint32_t kb, int q, uint32_t kc, int64_t& code_off,
                                            int64_t& scale_off) {
   if constexpr (TILED) {
-    const uint32_t n = (uint32_t)b / kblocks, kb = (uint32_t)b - n * kblocks;
     const uint32_t i = n & 15u, kq = kb & 7u, p = kq & 1u, j = kq >> 1;
     const uint32_t g = 2u * p + ((uint32_t)q >> 1);
     const int64_t tile = (int64_t)(n >> 4) * kc + (kb >> 3);
     code_off = tile * 1024 + 16 * (16 * g + i) + 4 * j + 2 * (q & 1);
     scale_off = tile * 128 + 4 * (16 * p + i) + j;
   } else {
+    (void)n;
+    (void)kb;
     code_off = 8 * b + 2 * q;
     scale_off = b;
   }
@@ -133,7 +143,7 @@ __global__ __launch_bounds__(kThreads) void encode_kernel(const void* __restrict
                                                            int npartial, uint8_t* __restrict__ codes,
                                                            uint8_t* __restrict__ scales,
                                                            float* __restrict__ tensor_scale, uint32_t kblocks,
-                                                           uint32_t kc) {
+                                                           uint32_t kc, uint32_t step_rows, uint32_t step_kb) {
 #pragma clang fp contract(off)
   __shared__ uint32_t red[kThreads / kWave];
   uint32_t mx = 0;
@@ -150,8 +160,12 @@ __global__ __launch_bounds__(kThreads) void encode_kernel(const void* __restrict
 
   const int q = threadIdx.x & 3;  // quarter of the block this lane holds
   const int64_t nquads = (int64_t)gridDim.x * (kThreads / 4);
-  for (int64_t b0 = ((int64_t)blockIdx.x * kThreads + threadIdx.x) / 4; b0 < nblk;
-       b0 += kUnroll * nquads) {
+  // Row n and block kb of block b = n kblocks + kb, kept incrementally: a
+  // step of nquads blocks is step_rows rows plus step_kb blocks (host
+  // division), so the loop divides nothing.
+  int64_t b0 = ((int64_t)blockIdx.x * kThreads + threadIdx.x) / 4;
+  uint32_t rn = (uint32_t)(b0 / kblocks), rkb = (uint32_t)(b0 - (int64_t)rn * kblocks);
+  for (; b0 < nblk; b0 += kUnroll * nquads) {
     float v[kUnroll][4];
 #pragma unroll
     for (int u = 0; u < kUnroll; ++u) {
@@ -175,9 +189,12 @@ __global__ __launch_bounds__(kThreads) void encode_kernel(const void* __restrict
       const uint32_t c = e2m1_encode(v[u][0], dz, Ds, xs) | (e2m1_encode(v[u][1], dz, Ds, xs) << 4) |
                          (e2m1_encode(v[u][2], dz, Ds, xs) << 8) | (e2m1_encode(v[u][3], dz, Ds, xs) << 12);
       int64_t co, so;
-      block_dest<TILED>(b, q, kblocks, kc, co, so);
+      block_dest<TILED>(b, rn, rkb, q, kc, co, so);
       *reinterpret_cast<uint16_t*>(codes + co) = (uint16_t)c;
       if (q == 0) scales[so] = (uint8_t)byte;
+      rkb += step_kb;
+      rn += step_rows;
+      if (rkb >= kblocks) rkb -= kblocks, ++rn;
     }
   }
 }
@@ -265,9 +282,11 @@ hipError_t launch_quantize(const void* w, bool w_bf16, int64_t n, int64_t k, boo
   const int64_t per_wg = (kThreads / 4) * kUnroll;
   const dim3 grid((unsigned)std::min<int64_t>(8192, (nblk + per_wg - 1) / per_wg));
   const uint32_t kblocks = (uint32_t)(k / 16), kc = (uint32_t)((k + 127) / 128);
+  const int64_t nquads = (int64_t)grid.x * (kThreads / 4);  // blocks between a lane's consecutive blocks
+  const uint32_t step_rows = (uint32_t)(nquads / kblocks), step_kb = (uint32_t)(nquads % kblocks);
 #define FP4RL_ENCODE(B_, T_) \
   hipLaunchKernelGGL((encode_kernel<B_, T_>), grid, dim3(kThreads), 0, stream, w, nblk, partial, (int)g1, codes, \
-                     scales, tensor_scale, kblocks, kc)
+                     scales, tensor_scale, kblocks, kc, step_rows, step_kb)
   if (w_bf16) {
     if (tiled) FP4RL_ENCODE(true, true); else FP4RL_ENCODE(true, false);
   } else {
