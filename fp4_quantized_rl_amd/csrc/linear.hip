@@ -578,7 +578,7 @@ __global__ __launch_bounds__(WAVES * kWave) void skinny_kernel(
 constexpr int kXRow = 136;  // bf16 per LDS token row: 128 + 8 of padding
 
 template <int TM, int TN, int W, int D>
-__global__ __launch_bounds__(W * kWave) __attribute__((amdgpu_waves_per_eu(D == 2 ? 3 : 1))) void splitk_kernel(
+__global__ __launch_bounds__(W * kWave) __attribute__((amdgpu_waves_per_eu(D == 2 ? (TM <= 2 ? 4 : 3) : 1))) void splitk_kernel(
     const uint16_t* __restrict__ x, int M, int N, int K, const uint8_t* __restrict__ codes,
     const uint8_t* __restrict__ scales, const float* __restrict__ tensor_scale, const float* __restrict__ t, int tks,
     const uint16_t* __restrict__ lb, int r, uint16_t* __restrict__ y, int cpz, int nsplit, float* __restrict__ part,
@@ -1389,13 +1389,14 @@ hipError_t run_gemv_w(int w, hipStream_t st, const uint16_t* x, int M, int N, in
 }
 
 // Split-K MFMA path: 16 < m <= 128 (decode-shaped batches).
-// TM = 4 row tiles (64 features) per workgroup, TN token tiles (up to 64
-// tokens per workgroup, more go to grid.y), W = 4 waves. K is split over
+// TM = 4 row tiles (64 features; 2 for narrow matrices with short K) per
+// workgroup, TN token tiles (32 tokens per workgroup, more go to further
+// token groups), W = 4 waves. K is split over
 // grid.z until about 256 workgroups are in flight, while every wave keeps at
 // least one chunk and the fp32 partials (written and read once) stay within
 // a third of the weight bytes.
 struct SplitkCfg {
-  int tn, w, s, cpz, gx, gy, d;
+  int tn, w, s, cpz, gx, gy, d, tm;
 };
 
 static bool use_splitk(int64_t m) { return m > 16 && m <= 128; }
@@ -1404,9 +1405,14 @@ static SplitkCfg pick_splitk(int64_t m, int64_t n, int64_t k) {
   SplitkCfg c;
   c.tn = 2;
   c.w = 4;
-  c.gx = (int)((n + 63) / 64);
   c.gy = (int)((m + 16 * c.tn - 1) / (16 * c.tn));
   const int64_t kc = (k + 127) / 128;
+  // Narrow, short matrices (at most one 64-feature tile per CU, K <= 8192):
+  // two row tiles per wave, so twice the workgroups share the work without
+  // splitting K further (measured: o 3584 -> 3584 at 32 tokens 13.7 -> 10.0
+  // us). Long K keeps four row tiles: its K splits already fill the chip.
+  c.tm = (n + 63) / 64 * c.gy <= 256 && kc <= 64 ? 2 : 4;
+  c.gx = (int)((n + 16 * c.tm - 1) / (16 * c.tm));
   const double wbytes = (double)n * (double)k * 0.5625;
   int s = 1;
   while ((int64_t)c.gx * c.gy * s < 256 && (kc + 2 * s - 1) / (2 * s) >= c.w &&
@@ -1414,6 +1420,10 @@ static SplitkCfg pick_splitk(int64_t m, int64_t n, int64_t k) {
     s *= 2;
 #ifdef FP4RL_TUNING
   if (tune_env("FP4RL_TUNE_S") > 0) s = tune_env("FP4RL_TUNE_S");
+  if (tune_env("FP4RL_TUNE_TM") > 0) {
+    c.tm = tune_env("FP4RL_TUNE_TM");
+    c.gx = (int)((n + 16 * c.tm - 1) / (16 * c.tm));
+  }
   if (tune_env("FP4RL_TUNE_TN") > 0) {
     c.tn = tune_env("FP4RL_TUNE_TN");
     c.gy = (int)((m + 16 * c.tn - 1) / (16 * c.tn));
@@ -1440,7 +1450,7 @@ size_t linear_partial_bytes(int64_t m, int64_t n, int64_t k) {
   return ((size_t)c.s * (size_t)m * (size_t)n * sizeof(float) + 255) / 256 * 256;
 }
 
-template <int TN, int W, int D>
+template <int TN, int W, int D, int TM = 4>
 hipError_t run_splitk(const SplitkCfg& c, hipStream_t st, const uint16_t* x, int M, int N, int K, const uint8_t* codes,
                       const uint8_t* scales, const float* ts, const float* t, int tks, const uint16_t* b, int r,
                       uint16_t* y, float* part, uint32_t* counters, LoraFuse lf) {
@@ -1450,7 +1460,7 @@ hipError_t run_splitk(const SplitkCfg& c, hipStream_t st, const uint16_t* x, int
   lf.consumers = c.gx * c.gy;  // one waiting workgroup per output tile (the last of its K split)
   lf.groups = std::min(kLoraGroups, lf.consumers);
   const unsigned grid = (unsigned)(lf.producers + main_grid);
-  hipLaunchKernelGGL((splitk_kernel<4, TN, W, D>), dim3(grid), dim3(W * kWave), 0, st, x, M, N, K, codes, scales, ts, t,
+  hipLaunchKernelGGL((splitk_kernel<TM, TN, W, D>), dim3(grid), dim3(W * kWave), 0, st, x, M, N, K, codes, scales, ts, t,
                      tks, b, r, y, c.cpz, c.s, c.s > 1 ? part : nullptr, c.s > 1 ? counters : nullptr, lf);
   return hipGetLastError();
 }
@@ -1464,10 +1474,15 @@ static hipError_t launch_splitk(const SplitkCfg& c, hipStream_t st, const uint16
     return run_splitk<TN_, W_, 2>(c, st, x, M, N, K, codes, scales, ts, t, tks, b, r, y, part, counters, lf); \
   if (c.tn == TN_ && c.w == W_ && c.d == 3)                                                                 \
     return run_splitk<TN_, W_, 3>(c, st, x, M, N, K, codes, scales, ts, t, tks, b, r, y, part, counters, lf);
-  FP4RL_SPLITK(2, 4)
+  if (c.tm == 2 && c.tn == 2 && c.w == 4 && c.d == 2)
+    return run_splitk<2, 4, 2, 2>(c, st, x, M, N, K, codes, scales, ts, t, tks, b, r, y, part, counters, lf);
+  if (c.tm == 2 && c.tn == 2 && c.w == 4 && c.d == 3)
+    return run_splitk<2, 4, 3, 2>(c, st, x, M, N, K, codes, scales, ts, t, tks, b, r, y, part, counters, lf);
+  if (c.tm != 4) return hipErrorInvalidValue;
 #ifdef FP4RL_TUNING
   FP4RL_SPLITK(4, 4)
 #endif
+  FP4RL_SPLITK(2, 4)
 #undef FP4RL_SPLITK
   return hipErrorInvalidValue;
 }
@@ -1494,9 +1509,10 @@ const char* fp4_linear_kernel_name(int64_t m, int64_t n, int64_t k, int64_t r) {
   if (m > 128) return "prefill_kernel<2>";
   if (use_splitk(m)) {
     const SplitkCfg sc = pick_splitk(m, n, k);
-    static const char* const kSplitk[2][2] = {{"splitk_kernel<4, 2, 4, 2>", "splitk_kernel<4, 2, 4, 3>"},
+    static const char* const kSplitk[3][2] = {{"splitk_kernel<2, 2, 4, 2>", "splitk_kernel<2, 2, 4, 3>"},
+                                              {"splitk_kernel<4, 2, 4, 2>", "splitk_kernel<4, 2, 4, 3>"},
                                               {"splitk_kernel<4, 4, 4, 2>", "splitk_kernel<4, 4, 4, 3>"}};
-    return kSplitk[sc.tn == 2 ? 0 : 1][sc.d == 2 ? 0 : 1];
+    return kSplitk[sc.tm == 2 ? 0 : sc.tn == 2 ? 1 : 2][sc.d == 2 ? 0 : 1];
   }
   const SkinnyCfg c = pick_skinny(m, n, k);
   int wi = 0;
