@@ -1259,6 +1259,10 @@ struct SkinnyCfg {
 // 3..16 tokens (one 16-token tile).
 SkinnyCfg pick_skinny(int64_t m, int64_t n, int64_t k) {
   (void)m;
+#ifdef FP4RL_TUNING
+  if (tune_env("FP4RL_TUNE_SK_W") > 0)
+    return SkinnyCfg{1, tune_env("FP4RL_TUNE_SK_NT") > 0 ? tune_env("FP4RL_TUNE_SK_NT") : 1, tune_env("FP4RL_TUNE_SK_W")};
+#endif
   const int64_t kc = (k + 127) / 128;
   if (n >= 4096) {
     // wide matrices: two row tiles share each activation fragment (halves the
@@ -1272,7 +1276,9 @@ SkinnyCfg pick_skinny(int64_t m, int64_t n, int64_t k) {
   const int64_t groups = (n + 15) / 16;
   const int wmax = (int)std::min<int64_t>(16, std::max<int64_t>(1, kc));
   int w = 1;
-  while (w * 2 <= wmax && groups * w < 4096) w *= 2;
+  // (doubling also keeps at least four chunks per wave: o 3584 -> 3584 at 8
+  // tokens 7.5 -> 7.0 us with 4 waves instead of 16)
+  while (w * 2 <= wmax && groups * w < 4096 && 8 * w <= kc) w *= 2;
   return SkinnyCfg{1, 1, w};
 }
 
@@ -1348,12 +1354,18 @@ hipError_t launch_lora_reduce(const float* part, int slices, int64_t count, floa
 // GEMV path: one or two tokens, when the staged tokens and LoRA operands fit
 // in 64 KB of LDS.
 // Waves per row tile: as many as keep the whole grid resident in one round
-// (about 4096 waves), so every wave issues all its loads at once and the
-// kernel pays its load -> reduce -> store latency chain once.
+// (up to about 8192 waves, eight per SIMD) while every wave keeps at least
+// four chunks, so every wave issues all its loads at once and the kernel
+// pays its load -> reduce -> store latency chain once (measured: gate
+// 3584 -> 18944 14.2 -> 12.8 us with 4 waves per tile instead of 2; o
+// 3584 -> 3584 7.3 -> 7.1 us with 4 instead of 16).
 static int gemv_waves(int64_t n, int64_t k) {
   const int64_t rt = (n + 15) / 16, kc = (k + 127) / 128;
   int w = 1;
-  while (w < 16 && w < kc && rt * w * 2 <= 4096) w *= 2;
+  while (w < 16 && 8 * w <= kc && rt * w * 2 <= 8192) w *= 2;  // doubling keeps >= 4 chunks per wave
+#ifdef FP4RL_TUNING
+  if (tune_env("FP4RL_TUNE_GEMV_W") > 0) w = tune_env("FP4RL_TUNE_GEMV_W");
+#endif
   return w;
 }
 
@@ -1478,6 +1490,12 @@ static hipError_t launch_splitk(const SplitkCfg& c, hipStream_t st, const uint16
     return run_splitk<2, 4, 2, 2>(c, st, x, M, N, K, codes, scales, ts, t, tks, b, r, y, part, counters, lf);
   if (c.tm == 2 && c.tn == 2 && c.w == 4 && c.d == 3)
     return run_splitk<2, 4, 3, 2>(c, st, x, M, N, K, codes, scales, ts, t, tks, b, r, y, part, counters, lf);
+#ifdef FP4RL_TUNING
+  if (c.tm == 2 && c.tn == 4 && c.d == 2)
+    return run_splitk<4, 4, 2, 2>(c, st, x, M, N, K, codes, scales, ts, t, tks, b, r, y, part, counters, lf);
+  if (c.tm == 2 && c.tn == 4 && c.d == 3)
+    return run_splitk<4, 4, 3, 2>(c, st, x, M, N, K, codes, scales, ts, t, tks, b, r, y, part, counters, lf);
+#endif
   if (c.tm != 4) return hipErrorInvalidValue;
 #ifdef FP4RL_TUNING
   FP4RL_SPLITK(4, 4)
