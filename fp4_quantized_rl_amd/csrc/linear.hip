@@ -1444,11 +1444,12 @@ static SplitkCfg pick_splitk(int64_t m, int64_t n, int64_t k) {
   c.cpz = (int)((kc + s - 1) / s);
   c.s = (int)((kc + c.cpz - 1) / c.cpz);  // no empty K range
   if ((int64_t)c.gx * c.gy > kSplitCounters) c.s = 1, c.cpz = (int)kc;  // a split needs one counter per tile
-  // more output tiles than CUs (wide matrices): the lighter pipeline at three
-  // waves per SIMD; fewer: the deeper one, which hides latency at one wave
-  // per SIMD (measured: gate 3584 -> 18944 at 64 tokens 28.8 -> 26.1 us,
-  // while o 3584 -> 3584 is 1 us slower with it)
-  c.d = (int64_t)c.gx * c.gy > 256 ? 2 : 3;
+  // more output tiles than CUs (wide matrices) or long K: the lighter
+  // pipeline at three waves per SIMD; otherwise the deeper one, which hides
+  // latency at one wave per SIMD (measured: gate 3584 -> 18944 at 64 tokens
+  // 28.8 -> 26.1 us, down 18944 -> 3584 at 32 tokens 22.9 -> 21.8 us, while
+  // o 3584 -> 3584 is 1 us slower with it)
+  c.d = (int64_t)c.gx * c.gy > 256 || kc > 64 ? 2 : 3;
 #ifdef FP4RL_TUNING
   if (tune_env("FP4RL_TUNE_D") > 0) c.d = tune_env("FP4RL_TUNE_D");
 #endif
