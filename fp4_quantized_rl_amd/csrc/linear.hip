@@ -1248,6 +1248,15 @@ int tune_env(const char* name) {
 }
 #endif
 
+// More than 128 tokens: the prefill GEMM (128-token tiles, each weight
+// dequantised once per 128 tokens).
+static bool use_prefill(int64_t m) {
+#ifdef FP4RL_TUNING
+  if (tune_env("FP4RL_TUNE_PF_MIN") > 0) return m >= tune_env("FP4RL_TUNE_PF_MIN");
+#endif
+  return m > 128;
+}
+
 struct SkinnyCfg {
   int mt, nt, waves;
 };
@@ -1315,7 +1324,7 @@ hipError_t run_skinny_w(int w, dim3 grid, hipStream_t st, const uint16_t* x, int
 
 int lora_splits(int64_t m, int64_t k, int64_t r) {
   (void)r;
-  if (m > 128) return 1;  // prefill: token tiles already fill the chip
+  if (use_prefill(m)) return 1;  // prefill: token tiles already fill the chip
 #ifdef FP4RL_TUNING
   if (tune_env("FP4RL_TUNE_SLICES") > 0) return tune_env("FP4RL_TUNE_SLICES");
 #endif
@@ -1411,7 +1420,7 @@ struct SplitkCfg {
   int tn, w, s, cpz, gx, gy, d, tm;
 };
 
-static bool use_splitk(int64_t m) { return m > 16 && m <= 128; }
+static bool use_splitk(int64_t m) { return m > 16 && !use_prefill(m); }
 
 static SplitkCfg pick_splitk(int64_t m, int64_t n, int64_t k) {
   SplitkCfg c;
@@ -1525,7 +1534,7 @@ const char* fp4_linear_kernel_name(int64_t m, int64_t n, int64_t k, int64_t r) {
     while ((1 << wi) < gemv_waves(n, k)) ++wi;
     return kGemv[m - 1][wi];
   }
-  if (m > 128) return "prefill_kernel<2>";
+  if (use_prefill(m)) return "prefill_kernel<2>";
   if (use_splitk(m)) {
     const SplitkCfg sc = pick_splitk(m, n, k);
     static const char* const kSplitk[3][2] = {{"splitk_kernel<2, 2, 4, 2>", "splitk_kernel<2, 2, 4, 3>"},
@@ -1542,7 +1551,7 @@ const char* fp4_linear_kernel_name(int64_t m, int64_t n, int64_t k, int64_t r) {
 bool linear_fuses_lora(int64_t m, int64_t n, int64_t k) {
   (void)n;
   (void)k;
-  return m <= 128;  // every decode kernel (GEMV, skinny: one token group; split-K)
+  return !use_prefill(m);  // every decode kernel (GEMV, skinny: one token group; split-K)
 }
 
 int64_t lora_slice_len(int64_t k, int splits) { return ((k + splits - 1) / splits + 31) / 32 * 32; }
@@ -1565,7 +1574,7 @@ hipError_t launch_fp4_linear(const uint16_t* x, int64_t m, int64_t n, int64_t k,
   if (use_splitk(m))
     return launch_splitk(pick_splitk(m, n, k), stream, x, M, N, K, codes, scales, tensor_scale, t, tks, b, R, y, part,
                          counters, lf);
-  if (m > 128) {
+  if (use_prefill(m)) {
     const int64_t gr = (n + kPfRows - 1) / kPfRows, gt = (m + kPfTok - 1) / kPfTok;
     const int64_t supers = (gr + 7) / 8 * ((gt + 3) / 4);  // super-tiles of 8 x 4 workgroups, dealt to 8 XCDs
     const int64_t grid = 8 * 32 * ((supers + 7) / 8);
