@@ -60,14 +60,15 @@ __device__ __forceinline__ float sumsq8(uint4 v) {
   return ((a * a + b * b) + (c * c + d * d)) + ((e * e + f * f) + (g * g + h * h));
 }
 
+// (outputs rounded to bf16 by the hardware RNE convert, two per instruction)
 __device__ __forceinline__ uint4 norm8(uint4 v, const float* wn, float inv) {
   const float4 w0 = *reinterpret_cast<const float4*>(wn);
   const float4 w1 = *reinterpret_cast<const float4*>(wn + 4);
   uint4 o;
-  o.x = f32_to_bf16(bf16_lo(v.x) * inv * w0.x) | (f32_to_bf16(bf16_hi(v.x) * inv * w0.y) << 16);
-  o.y = f32_to_bf16(bf16_lo(v.y) * inv * w0.z) | (f32_to_bf16(bf16_hi(v.y) * inv * w0.w) << 16);
-  o.z = f32_to_bf16(bf16_lo(v.z) * inv * w1.x) | (f32_to_bf16(bf16_hi(v.z) * inv * w1.y) << 16);
-  o.w = f32_to_bf16(bf16_lo(v.w) * inv * w1.z) | (f32_to_bf16(bf16_hi(v.w) * inv * w1.w) << 16);
+  o.x = pack_bf16x2(bf16_lo(v.x) * inv * w0.x, bf16_hi(v.x) * inv * w0.y);
+  o.y = pack_bf16x2(bf16_lo(v.y) * inv * w0.z, bf16_hi(v.y) * inv * w0.w);
+  o.z = pack_bf16x2(bf16_lo(v.z) * inv * w1.x, bf16_hi(v.z) * inv * w1.y);
+  o.w = pack_bf16x2(bf16_lo(v.w) * inv * w1.z, bf16_hi(v.w) * inv * w1.w);
   return o;
 }
 
@@ -225,9 +226,14 @@ hipError_t launch_aqn_rmsnorm(const uint16_t* x, int64_t m, int64_t d, const flo
     return hipGetLastError();
   }
   const int64_t rows_wg = (m + kRowsPerWg - 1) / kRowsPerWg;
-  // Enough workgroups to fill 256 CUs several times over while the per-
-  // workgroup noise prologue (d/4 Philox blocks) stays small next to the rows.
-  const int64_t grid = std::max<int64_t>(1, std::min<int64_t>(rows_wg, 1024));
+  // Enough workgroups to fill 256 CUs several times over (eight per CU) while
+  // the per-workgroup noise prologue (d/4 Philox blocks) stays small next to
+  // the rows: 65536 x 5120 takes 286 us with 2048 workgroups, 327 with 1024
+  // and 316 with 4096.
+  int64_t grid = std::max<int64_t>(1, std::min<int64_t>(rows_wg, 2048));
+#ifdef FP4RL_TUNING
+  if (const char* g = getenv("FP4RL_TUNE_AQN_GRID")) grid = std::max<int64_t>(1, std::min<int64_t>(rows_wg, atoi(g)));
+#endif
   const size_t lds = (size_t)((d + 7) / 8) * 8 * sizeof(float);
   const uint32_t sl = (uint32_t)seed, sh = (uint32_t)(seed >> 32);
   const uint32_t tl = (uint32_t)step, th = (uint32_t)(step >> 32);
