@@ -178,15 +178,32 @@ __global__ __launch_bounds__(kThreads) void encode_kernel(const void* __restrict
 // those tiles, then writes them with 16-byte stores: each tile's 1 KB of
 // codes and 128 B of scales are contiguous, and consecutive chunks of a row
 // tile are consecutive tiles, so the region is one contiguous run. (Writing
-// each quad's 2-byte share straight to the tiled layout touched eight
-// 64-byte lines per store instruction and cost 18% of the encode pass.)
-// Quad (row i, r) takes blocks r, r + 4, ... of the region's row i; a wave's
-// load instruction covers 4 rows x 256 contiguous bytes (fp32). Elements past
-// N or K (padding) encode as zero codes with a zero scale byte, so the tiled
-// buffers need no separate fill.
+// each lane's share straight to the tiled layout touched eight 64-byte
+// lines per store instruction and cost 18% of the encode pass.)
+// Two lanes share a block, eight elements each: the block max takes one xor
+// shuffle, the E4M3 byte is computed once per eight elements, and the eight
+// codes are one 4-byte word of the tile (word j of lane slot (g, i)). Pair
+// (row i, r) takes blocks r, r + 8, r + 16, r + 24 of the region's row i; a
+// wave's load instruction covers 4 rows x 128 contiguous elements.
+// Elements past N or K (padding) encode as zero codes with a zero scale
+// byte, so the tiled buffers need no separate fill.
 constexpr int kRegionChunks = 4;
 constexpr int kRegionBlocks = 8 * kRegionChunks;  // per row
-constexpr int kBlocksPerQuad = kRegionBlocks / 4;
+constexpr int kBlocksPerPair = kRegionBlocks / 8;
+
+template <bool BF16>
+__device__ __forceinline__ void load_half(const void* w, int64_t elem, float v[8]) {
+  if constexpr (BF16) {
+    const uint4 r = ld_nt16(reinterpret_cast<const uint16_t*>(w) + elem);
+    v[0] = bf16_lo(r.x); v[1] = bf16_hi(r.x); v[2] = bf16_lo(r.y); v[3] = bf16_hi(r.y);
+    v[4] = bf16_lo(r.z); v[5] = bf16_hi(r.z); v[6] = bf16_lo(r.w); v[7] = bf16_hi(r.w);
+  } else {
+    const float* p = reinterpret_cast<const float*>(w) + elem;
+    const uint4 a = ld_nt16(p), b = ld_nt16(p + 4);
+    v[0] = __uint_as_float(a.x); v[1] = __uint_as_float(a.y); v[2] = __uint_as_float(a.z); v[3] = __uint_as_float(a.w);
+    v[4] = __uint_as_float(b.x); v[5] = __uint_as_float(b.y); v[6] = __uint_as_float(b.z); v[7] = __uint_as_float(b.w);
+  }
+}
 
 template <bool BF16>
 __global__ __launch_bounds__(kThreads) void encode_tiled_kernel(const void* __restrict__ w, int n, int k,
@@ -209,29 +226,31 @@ __global__ __launch_bounds__(kThreads) void encode_tiled_kernel(const void* __re
   if (blockIdx.x == 0 && threadIdx.x == 0) *tensor_scale = st;
   const float six_st = 6.0f * st;
 
-  const int q = threadIdx.x & 3, qd = threadIdx.x >> 2;
-  const int i = qd >> 2, r = qd & 3;  // row within the tile, quad within the row
+  const int h = threadIdx.x & 1, pd = threadIdx.x >> 1;  // half of the block, pair
+  const int i = pd >> 3, r = pd & 7;                     // row within the tile, pair within the row
   const int kc = (k + 127) >> 7, kblocks = k >> 4;
   const int ngroups = (kc + kRegionChunks - 1) / kRegionChunks;
   const int64_t regions = (int64_t)((n + 15) >> 4) * ngroups;
   for (int64_t reg = blockIdx.x; reg < regions; reg += gridDim.x) {
     const int rt = (int)(reg / ngroups), cg = (int)(reg - (int64_t)rt * ngroups);
     const int row = 16 * rt + i, kb0 = kRegionBlocks * cg;
-    float v[kBlocksPerQuad][4];
+    float v[kBlocksPerPair][8];
 #pragma unroll
-    for (int u = 0; u < kBlocksPerQuad; ++u) {
-      const int kb = kb0 + r + 4 * u;
+    for (int u = 0; u < kBlocksPerPair; ++u) {
+      const int kb = kb0 + r + 8 * u;
       if (row < n && kb < kblocks) {
-        load_quarter<BF16>(w, ((int64_t)row * k + 16 * kb) / 4 + q, v[u]);
+        load_half<BF16>(w, (int64_t)row * k + 16 * kb + 8 * h, v[u]);
       } else {
-        v[u][0] = v[u][1] = v[u][2] = v[u][3] = 0.0f;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) v[u][e] = 0.0f;
       }
     }
 #pragma unroll
-    for (int u = 0; u < kBlocksPerQuad; ++u) {
-      uint32_t ab = max(max(absbits(v[u][0]), absbits(v[u][1])), max(absbits(v[u][2]), absbits(v[u][3])));
+    for (int u = 0; u < kBlocksPerPair; ++u) {
+      uint32_t ab = 0;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) ab = max(ab, absbits(v[u][e]));
       ab = max(ab, (uint32_t)__shfl_xor((int)ab, 1, kWave));
-      ab = max(ab, (uint32_t)__shfl_xor((int)ab, 2, kWave));
       const float a_b = __uint_as_float(ab);
       const uint32_t byte = (st != 0.0f && a_b != 0.0f) ? e4m3_encode(a_b / six_st) : 0u;
       const float D = e4m3_to_f32(byte) * st;
@@ -239,13 +258,14 @@ __global__ __launch_bounds__(kThreads) void encode_tiled_kernel(const void* __re
       const float Ds = tiny ? D * 0x1p64f : D;
       const float xs = tiny ? 0x1p64f : 1.0f;
       const bool dz = D == 0.0f;
-      const uint32_t c = e2m1_encode(v[u][0], dz, Ds, xs) | (e2m1_encode(v[u][1], dz, Ds, xs) << 4) |
-                         (e2m1_encode(v[u][2], dz, Ds, xs) << 8) | (e2m1_encode(v[u][3], dz, Ds, xs) << 12);
-      // tiled position of this quarter (block kb of row i: tile kb / 8, kq = kb % 8)
-      const int kbl = r + 4 * u, t = kbl >> 3, kq = kbl & 7, p = kq & 1, j = kq >> 1;
-      const int g = 2 * p + (q >> 1);
-      *reinterpret_cast<uint16_t*>(img + 1024 * t + 16 * (16 * g + i) + 4 * j + 2 * (q & 1)) = (uint16_t)c;
-      if (q == 0) img[kRegionChunks * 1024 + 128 * t + 4 * (16 * p + i) + j] = (uint8_t)byte;
+      uint32_t c = 0;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) c |= e2m1_encode(v[u][e], dz, Ds, xs) << (4 * e);
+      // tiled position of this half block (block kb of row i: tile kb / 8, kq = kb % 8)
+      const int kbl = r + 8 * u, t = kbl >> 3, kq = kbl & 7, p = kq & 1, j = kq >> 1;
+      const int g = 2 * p + h;
+      *reinterpret_cast<uint32_t*>(img + 1024 * t + 16 * (16 * g + i) + 4 * j) = c;
+      if (h == 0) img[kRegionChunks * 1024 + 128 * t + 4 * (16 * p + i) + j] = (uint8_t)byte;
     }
     __syncthreads();
     const int tiles = min(kRegionChunks, kc - kRegionChunks * cg);  // tiles of this region inside the matrix
