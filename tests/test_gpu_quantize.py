@@ -126,7 +126,9 @@ def test_full_size_14b_heavy_tailed():
 def test_tiled_layout_and_repack():
     """The tiled quantiser output and the row-major -> tiled repack both equal the host permutation."""
     dev = device()
-    for n, k in [(1, 16), (37, 80), (48, 384), (130, 272), (4608, 3584)]:
+    # (33, 640): five chunks, so a second, partial region of tiles; (20, 1296):
+    # a ragged last chunk in the eleventh tile column
+    for n, k in [(1, 16), (37, 80), (48, 384), (130, 272), (33, 640), (20, 1296), (4608, 3584)]:
         w = normal_f32((n, k), 0.02, n + k)
         ref = nvfp4.quantize(w)
         wt = f32_to_dev(w, dev)
@@ -138,6 +140,21 @@ def test_tiled_layout_and_repack():
         ct, st = tile_host(ref[0], ref[1], n, k)
         assert np.array_equal(rep.codes.cpu().numpy(), ct) and np.array_equal(rep.scales.cpu().numpy(), st)
         assert np.array_equal(tiled.codes.cpu().numpy(), ct) and np.array_equal(tiled.scales.cpu().numpy(), st)
+
+
+def test_tiled_bf16_input_ragged():
+    """bf16 weights into the tiled layout, ragged in both dimensions, equal the host permutation."""
+    dev = device()
+    for n, k in [(21, 656), (300, 5120)]:
+        w = normal_f32((n, k), 0.02, 3 * n + k)
+        wb = bf16_bits(w)
+        ref = nvfp4.quantize(bf16_values(wb))
+        say(f"quantize bf16 {n}x{k} tiled")
+        tiled = fr.nvfp4_quantize(bf16_to_dev(wb, dev), layout="tiled")
+        torch.cuda.synchronize()
+        ct, st = tile_host(ref[0], ref[1], n, k)
+        assert np.array_equal(tiled.codes.cpu().numpy(), ct) and np.array_equal(tiled.scales.cpu().numpy(), st)
+        assert np.float32(tiled.tensor_scale.cpu().numpy()[0]) == ref[2]
 
 
 def test_repeat_runs_identical():
