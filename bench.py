@@ -581,6 +581,25 @@ def run_extras(torch, fr, dev, shapes, layer, lora, fp32):
                                  "ms_48_layers": round(dt_s * 48e3, 2),
                                  "GB/s_two_pass": round(two_pass / dt_s / 1e9, 1),
                                  "frac_of_hbm": round(two_pass / dt_s / 1e9 / HBM_PEAK_GBS, 4)}
+        if dt == "fp32":
+            # the same pass also writing the rounding record (1 bit per weight)
+            recs = {name: torch.empty((w.shape[0], w.shape[1] // 8), dtype=torch.uint8, device=dev)
+                    for name, w in ws.items()}
+            for name, w in ws.items():
+                fr.nvfp4_quantize(w, out=outs[name], round_up=recs[name])
+            torch.cuda.synchronize()
+            t0 = time.perf_counter()
+            for _ in range(reps):
+                for name, w in ws.items():
+                    fr.nvfp4_quantize(w, out=outs[name], round_up=recs[name])
+            torch.cuda.synchronize()
+            dt_r = (time.perf_counter() - t0) / reps
+            rec_bytes = two_pass + params / 8
+            res["quantize_fp32_with_rounding_record"] = {
+                "ms_per_layer": round(dt_r * 1e3, 3), "GB/s_two_pass": round(rec_bytes / dt_r / 1e9, 1),
+                "frac_of_hbm": round(rec_bytes / dt_r / 1e9 / HBM_PEAK_GBS, 4),
+                "record_bytes_per_layer": params // 8}
+            del recs
         del outs
         if dt == "bf16":
             del ws

@@ -8,7 +8,7 @@ computation runs in the library's HIP kernels. There is no CPU fallback: if
 the library is not built, every call raises.
 
 Operations (names follow the C ABI):
-  nvfp4_quantize(w, layout)                 -> NVFP4Weight(codes, scales, tensor_scale)
+  nvfp4_quantize(w, layout[, round_up])     -> NVFP4Weight(codes, scales, tensor_scale) [+ rounding record]
   nvfp4_to_tiled(wq)                        -> row-major NVFP4 repacked into the tiled layout
   fp4_lora_linear(x, wq, lora_a, lora_b, s) -> y = x deq(Wq)^T + s (x A^T) B^T  (bf16)
   lora_down / fp4_linear_lora_up            -> the two halves of fp4_lora_linear
@@ -50,6 +50,8 @@ _SIGNATURES = {
     "fp4rl_nvfp4_scales_bytes": (_c.c_size_t, [_I64, _I64, _c.c_int32]),
     "fp4rl_nvfp4_quantize": (_STATUS, [_P, _c.c_int32, _I64, _I64, _c.c_int32, _P, _P, _P, _P, _c.c_size_t, _P]),
     "fp4rl_nvfp4_to_tiled": (_STATUS, [_P, _P, _I64, _I64, _P, _P, _P]),
+    "fp4rl_nvfp4_quantize_record": (_STATUS, [_P, _c.c_int32, _I64, _I64, _c.c_int32, _P, _P, _P, _P, _P,
+                                              _c.c_size_t, _P]),
     "fp4rl_fp4_lora_linear_workspace": (_c.c_size_t, [_I64, _I64, _I64, _I64]),
     "fp4rl_fp4_lora_linear": (_STATUS, [_P, _I64, _I64, _I64, _P, _P, _P, _P, _P, _I64, _c.c_float, _P, _P,
                                         _c.c_size_t, _P]),
@@ -167,8 +169,13 @@ def nvfp4_empty(n: int, k: int, layout: str = "tiled", device="cuda") -> NVFP4We
                        torch.empty((1,), dtype=torch.float32, device=device), n, k, layout)
 
 
-def nvfp4_quantize(w, layout: str = "tiled", out: NVFP4Weight | None = None, workspace=None) -> NVFP4Weight:
-    """NVFP4-quantise a [n, k] fp32 or bf16 weight (k % 16 == 0) on its device."""
+def nvfp4_quantize(w, layout: str = "tiled", out: NVFP4Weight | None = None, workspace=None,
+                   round_up=None) -> NVFP4Weight:
+    """NVFP4-quantise a [n, k] fp32 or bf16 weight (k % 16 == 0) on its device.
+
+    round_up: optional uint8 [n, k // 8] device tensor that receives the
+    rounding record (bit e of byte j: element 8 j + e rounded up in magnitude).
+    """
     torch = _torch()
     _dev_tensor(w, "w", (torch.float32, torch.bfloat16), 2)
     n, k = w.shape
@@ -182,10 +189,19 @@ def nvfp4_quantize(w, layout: str = "tiled", out: NVFP4Weight | None = None, wor
         workspace = torch.empty(max(ws_bytes, 16), dtype=torch.uint8, device=w.device)
     dt = F32 if w.dtype == torch.float32 else BF16
     with torch.cuda.device(w.device):
-        _check(lib.fp4rl_nvfp4_quantize(_ptr(w), dt, n, k, _LAYOUTS[layout], _ptr(out.codes), _ptr(out.scales),
-                                        _ptr(out.tensor_scale), _ptr(workspace), workspace.numel(),
-                                        _stream(w.device)),
-               "nvfp4_quantize")
+        if round_up is None:
+            _check(lib.fp4rl_nvfp4_quantize(_ptr(w), dt, n, k, _LAYOUTS[layout], _ptr(out.codes), _ptr(out.scales),
+                                            _ptr(out.tensor_scale), _ptr(workspace), workspace.numel(),
+                                            _stream(w.device)),
+                   "nvfp4_quantize")
+        else:
+            _dev_tensor(round_up, "round_up", (torch.uint8,), 2)
+            if tuple(round_up.shape) != (n, k // 8) or round_up.device != w.device:
+                raise ValueError("round_up must be uint8 [n, k // 8] on the weight's device")
+            _check(lib.fp4rl_nvfp4_quantize_record(_ptr(w), dt, n, k, _LAYOUTS[layout], _ptr(out.codes),
+                                                   _ptr(out.scales), _ptr(out.tensor_scale), _ptr(round_up),
+                                                   _ptr(workspace), workspace.numel(), _stream(w.device)),
+                   "nvfp4_quantize_record")
     return out
 
 

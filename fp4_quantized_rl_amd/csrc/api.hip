@@ -127,9 +127,9 @@ size_t fp4rl_nvfp4_scales_bytes(int64_t n, int64_t k, int32_t layout) {
   return (size_t)fp4rl::nvfp4_scales_bytes(n, k, layout == FP4RL_TILED);
 }
 
-fp4rl_status fp4rl_nvfp4_quantize(const void* w, int32_t w_dtype, int64_t n, int64_t k, int32_t layout,
-                                  uint8_t* codes, uint8_t* scales, float* tensor_scale, void* workspace,
-                                  size_t workspace_bytes, fp4rl_stream stream) {
+static fp4rl_status quantize_impl(const void* w, int32_t w_dtype, int64_t n, int64_t k, int32_t layout,
+                                  uint8_t* codes, uint8_t* scales, float* tensor_scale, uint8_t* record,
+                                  void* workspace, size_t workspace_bytes, fp4rl_stream stream) {
   FP4RL_REQUIRE(n >= 0 && k >= 0, FP4RL_ERR_SHAPE, "negative size (n=%lld k=%lld)", (long long)n, (long long)k);
   FP4RL_REQUIRE(k % 16 == 0, FP4RL_ERR_SHAPE, "k=%lld is not a multiple of 16", (long long)k);
   FP4RL_REQUIRE(n < kMaxDim && k < kMaxDim && n * k < ((int64_t)1 << 36), FP4RL_ERR_SHAPE, "matrix too large");
@@ -148,8 +148,24 @@ fp4rl_status fp4rl_nvfp4_quantize(const void* w, int32_t w_dtype, int64_t n, int
   }
   FP4RL_CHECK(check_device());
   return launched(fp4rl::launch_quantize(w, w_dtype == FP4RL_BF16, n, k, layout == FP4RL_TILED, codes, scales,
-                                         tensor_scale, static_cast<uint32_t*>(workspace), stream),
+                                         tensor_scale, empty ? nullptr : record, static_cast<uint32_t*>(workspace),
+                                         stream),
                   "nvfp4_quantize");
+}
+
+fp4rl_status fp4rl_nvfp4_quantize(const void* w, int32_t w_dtype, int64_t n, int64_t k, int32_t layout,
+                                  uint8_t* codes, uint8_t* scales, float* tensor_scale, void* workspace,
+                                  size_t workspace_bytes, fp4rl_stream stream) {
+  return quantize_impl(w, w_dtype, n, k, layout, codes, scales, tensor_scale, nullptr, workspace, workspace_bytes,
+                       stream);
+}
+
+fp4rl_status fp4rl_nvfp4_quantize_record(const void* w, int32_t w_dtype, int64_t n, int64_t k, int32_t layout,
+                                         uint8_t* codes, uint8_t* scales, float* tensor_scale, uint8_t* round_up,
+                                         void* workspace, size_t workspace_bytes, fp4rl_stream stream) {
+  FP4RL_REQUIRE(n == 0 || k == 0 || round_up != nullptr, FP4RL_ERR_NULL, "round_up is NULL");
+  return quantize_impl(w, w_dtype, n, k, layout, codes, scales, tensor_scale, round_up, workspace, workspace_bytes,
+                       stream);
 }
 
 fp4rl_status fp4rl_nvfp4_to_tiled(const uint8_t* codes, const uint8_t* scales, int64_t n, int64_t k,

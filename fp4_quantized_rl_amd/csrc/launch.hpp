@@ -14,8 +14,10 @@ constexpr int kAmaxPartials = 1024;  // workgroups of the amax pass = partial ma
 size_t quantize_workspace_bytes();
 int64_t nvfp4_codes_bytes(int64_t n, int64_t k, bool tiled);
 int64_t nvfp4_scales_bytes(int64_t n, int64_t k, bool tiled);
+// record: NULL, or the rounding record [n][k/8] (bit e of byte j: element 8j+e rounded up in magnitude)
 hipError_t launch_quantize(const void* w, bool w_bf16, int64_t n, int64_t k, bool tiled, uint8_t* codes,
-                           uint8_t* scales, float* tensor_scale, uint32_t* partial, hipStream_t stream);
+                           uint8_t* scales, float* tensor_scale, uint8_t* record, uint32_t* partial,
+                           hipStream_t stream);
 hipError_t launch_to_tiled(const uint8_t* codes, const uint8_t* scales, int64_t n, int64_t k, uint8_t* codes_t,
                            uint8_t* scales_t, hipStream_t stream);
 

@@ -102,6 +102,18 @@ __device__ __forceinline__ uint32_t e2m1_encode(float x, bool dzero, float Ds, f
   return k | ((__float_as_uint(x) >> 28) & 8u);
 }
 
+// Rounding record (TRACE article, "Engineering view of the mechanism": each
+// value is rounded up or down to a neighbouring grid point, and the rollout
+// side records that choice): 1 when the chosen grid point g_k * D exceeds |x|
+// (the magnitude was rounded up), by the same exact sign test as the
+// midpoints; 0 when rounded down or hit exactly, and for D == 0.
+__device__ __forceinline__ uint32_t e2m1_rounded_up(uint32_t code, float x, bool dzero, float Ds, float xs) {
+#pragma clang fp contract(off)
+  const uint32_t k = code & 7u;
+  const float g = k < 4u ? 0.5f * (float)k : (k == 7u ? 6.0f : (float)(k - 2u));
+  return (!dzero && fmaf(g, Ds, -(fabsf(x) * xs)) > 0.0f) ? 1u : 0u;
+}
+
 template <bool BF16>
 __device__ __forceinline__ void load_quarter(const void* w, int64_t idx, float v[4]) {
   if constexpr (BF16) {
@@ -121,12 +133,13 @@ __device__ __forceinline__ void load_quarter(const void* w, int64_t idx, float v
 // holds in byte j the scale of block 8 c + 2 j + p. So a block kb (8 per
 // chunk) lands in word j = kb/2 of lane groups g = 2 (kb & 1) and g + 1, and
 // its quarter q (4 elements) in group g + q/2, byte 2 (q & 1) of the word.
-template <bool BF16>
+template <bool BF16, bool REC>
 __global__ __launch_bounds__(kThreads) void encode_kernel(const void* __restrict__ w, int64_t nblk,
                                                            const uint32_t* __restrict__ partial,
                                                            int npartial, uint8_t* __restrict__ codes,
                                                            uint8_t* __restrict__ scales,
-                                                           float* __restrict__ tensor_scale) {
+                                                           float* __restrict__ tensor_scale,
+                                                           uint8_t* __restrict__ record) {
 #pragma clang fp contract(off)
   __shared__ uint32_t red[kThreads / kWave];
   uint32_t mx = 0;
@@ -169,6 +182,13 @@ __global__ __launch_bounds__(kThreads) void encode_kernel(const void* __restrict
       // row-major: the block's 8 code bytes, then its scale byte
       *reinterpret_cast<uint16_t*>(codes + 8 * b + 2 * q) = (uint16_t)c;
       if (q == 0) scales[b] = (uint8_t)byte;
+      if constexpr (REC) {  // this quarter's 4 bits; the even lane of a pair stores the byte
+        uint32_t nib = 0;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) nib |= e2m1_rounded_up(c >> (4 * e), v[u][e], dz, Ds, xs) << e;
+        const uint32_t other = (uint32_t)__shfl_xor((int)nib, 1, kWave);
+        if ((q & 1) == 0) record[2 * b + (q >> 1)] = (uint8_t)(nib | (other << 4));
+      }
     }
   }
 }
@@ -205,12 +225,13 @@ __device__ __forceinline__ void load_half(const void* w, int64_t elem, float v[8
   }
 }
 
-template <bool BF16>
+template <bool BF16, bool REC>
 __global__ __launch_bounds__(kThreads) void encode_tiled_kernel(const void* __restrict__ w, int n, int k,
                                                                  const uint32_t* __restrict__ partial, int npartial,
                                                                  uint8_t* __restrict__ codes,
                                                                  uint8_t* __restrict__ scales,
-                                                                 float* __restrict__ tensor_scale) {
+                                                                 float* __restrict__ tensor_scale,
+                                                                 uint8_t* __restrict__ record) {
 #pragma clang fp contract(off)
   __shared__ uint32_t red[kThreads / kWave];
   __shared__ __align__(16) uint8_t img[kRegionChunks * (1024 + 128)];  // codes of the region's tiles, then scales
@@ -266,6 +287,15 @@ __global__ __launch_bounds__(kThreads) void encode_tiled_kernel(const void* __re
       const int g = 2 * p + h;
       *reinterpret_cast<uint32_t*>(img + 1024 * t + 16 * (16 * g + i) + 4 * j) = c;
       if (h == 0) img[kRegionChunks * 1024 + 128 * t + 4 * (16 * p + i) + j] = (uint8_t)byte;
+      if constexpr (REC) {  // row-major record: this half block is byte 2 kb + h of the row
+        const int kb = kb0 + kbl;
+        if (row < n && kb < kblocks) {
+          uint32_t bits = 0;
+#pragma unroll
+          for (int e = 0; e < 8; ++e) bits |= e2m1_rounded_up(c >> (4 * e), v[u][e], dz, Ds, xs) << e;
+          record[(int64_t)row * (k >> 3) + 2 * kb + h] = (uint8_t)bits;
+        }
+      }
     }
     __syncthreads();
     const int tiles = min(kRegionChunks, kc - kRegionChunks * cg);  // tiles of this region inside the matrix
@@ -324,7 +354,8 @@ int64_t nvfp4_scales_bytes(int64_t n, int64_t k, bool tiled) {
 }
 
 hipError_t launch_quantize(const void* w, bool w_bf16, int64_t n, int64_t k, bool tiled, uint8_t* codes,
-                           uint8_t* scales, float* tensor_scale, uint32_t* partial, hipStream_t stream) {
+                           uint8_t* scales, float* tensor_scale, uint8_t* record, uint32_t* partial,
+                           hipStream_t stream) {
   const int64_t elems = n * k;
   if (elems == 0) {
     hipLaunchKernelGGL(write_zero_scale, dim3(1), dim3(1), 0, stream, tensor_scale);
@@ -346,20 +377,26 @@ hipError_t launch_quantize(const void* w, bool w_bf16, int64_t n, int64_t k, boo
   if (tiled) {  // whole tiles per workgroup (padding written as zero)
     const int64_t regions = ((n + 15) / 16) * ((k / 128 + (k % 128 != 0) + kRegionChunks - 1) / kRegionChunks);
     const dim3 tgrid((unsigned)std::min<int64_t>(8192, regions));
-    if (w_bf16)
-      hipLaunchKernelGGL(encode_tiled_kernel<true>, tgrid, dim3(kThreads), 0, stream, w, (int)n, (int)k, partial,
-                         (int)g1, codes, scales, tensor_scale);
-    else
-      hipLaunchKernelGGL(encode_tiled_kernel<false>, tgrid, dim3(kThreads), 0, stream, w, (int)n, (int)k, partial,
-                         (int)g1, codes, scales, tensor_scale);
+#define FP4RL_TILED(B_, R_)                                                                                  \
+  hipLaunchKernelGGL((encode_tiled_kernel<B_, R_>), tgrid, dim3(kThreads), 0, stream, w, (int)n, (int)k, partial, \
+                     (int)g1, codes, scales, tensor_scale, record)
+    if (w_bf16) {
+      if (record) FP4RL_TILED(true, true); else FP4RL_TILED(true, false);
+    } else {
+      if (record) FP4RL_TILED(false, true); else FP4RL_TILED(false, false);
+    }
+#undef FP4RL_TILED
     return hipGetLastError();
   }
-  if (w_bf16)
-    hipLaunchKernelGGL(encode_kernel<true>, grid, dim3(kThreads), 0, stream, w, nblk, partial, (int)g1, codes, scales,
-                       tensor_scale);
-  else
-    hipLaunchKernelGGL(encode_kernel<false>, grid, dim3(kThreads), 0, stream, w, nblk, partial, (int)g1, codes, scales,
-                       tensor_scale);
+#define FP4RL_ROWS(B_, R_)                                                                                    \
+  hipLaunchKernelGGL((encode_kernel<B_, R_>), grid, dim3(kThreads), 0, stream, w, nblk, partial, (int)g1, codes, \
+                     scales, tensor_scale, record)
+  if (w_bf16) {
+    if (record) FP4RL_ROWS(true, true); else FP4RL_ROWS(true, false);
+  } else {
+    if (record) FP4RL_ROWS(false, true); else FP4RL_ROWS(false, false);
+  }
+#undef FP4RL_ROWS
   return hipGetLastError();
 }
 

@@ -113,6 +113,22 @@ fp4rl_status fp4rl_nvfp4_quantize(const void* w, int32_t w_dtype, int64_t n, int
 fp4rl_status fp4rl_nvfp4_to_tiled(const uint8_t* codes, const uint8_t* scales, int64_t n, int64_t k,
                                   uint8_t* codes_tiled, uint8_t* scales_tiled, fp4rl_stream stream);
 
+/* Quantise as fp4rl_nvfp4_quantize (same codes, scales and tensor scale, same
+ * arguments and errors) and also write the rounding record the rollout side
+ * keeps for the trainer (TRACE article, "TRACE's core idea" and "Engineering
+ * view of the mechanism": each value is rounded up or down to a neighbouring
+ * grid point, and the trainer replays the rollout's choices from a compact
+ * record; the pages leave the format open).
+ * round_up [n][k/8] bytes, row-major in both layouts, any alignment, owned by
+ * the caller: bit e (LSB first) of byte j of row i is 1 when element
+ * 8 j + e was rounded up in magnitude, i.e. g_k * fp32(S_b s_t) > |x| for its
+ * code; 0 when rounded down or exact, and in blocks with fp32(S_b s_t) == 0.
+ * With the scale bytes this fixes the grid neighbours of every value.
+ * round_up == NULL with n, k > 0: FP4RL_ERR_NULL. */
+fp4rl_status fp4rl_nvfp4_quantize_record(const void* w, int32_t w_dtype, int64_t n, int64_t k, int32_t layout,
+                                         uint8_t* codes, uint8_t* scales, float* tensor_scale, uint8_t* round_up,
+                                         void* workspace, size_t workspace_bytes, fp4rl_stream stream);
+
 /* ------------------------------------------------------------------------
  * Fused W4A16 + LoRA linear:
  *   y[m][n] = bf16_rne( s_t * sum_k x[m][k] g(code[n][k]) S_b(n,k)

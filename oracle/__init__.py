@@ -4,8 +4,8 @@ Plain, slow, obviously correct numpy (float64) implementations of what the
 rollout hot path computes:
 
 * ``nvfp4``  – the NVFP4 block quantiser (16-element blocks, one E4M3 scale
-  per block, one FP32 tensor scale, values on the E2M1 grid) and its exact
-  dequantisation;
+  per block, one FP32 tensor scale, values on the E2M1 grid), its exact
+  dequantisation and the per-value rounding record (rounded up or down);
 * ``linear`` – y = x deq(Wq)^T + s (x A^T) B^T, the W4A16 linear with the
   LoRA update;
 * ``aqn``    – the Adaptive Quantization Noise RMSNorm: the exponential sigma

@@ -164,6 +164,37 @@ def quantize_rows(w, rows) -> tuple[np.ndarray, np.ndarray, np.float32]:
     return packed, sbytes, s_t
 
 
+def rounding_record(w) -> np.ndarray:
+    """Per-element rounding direction of ``quantize(w)``: uint8 [N, K/8] bit mask.
+
+    TRACE article (sns.style), "Engineering view of the mechanism": under
+    block scaling every value is rounded up or down to a neighbouring grid
+    point, a discrete per-value choice, and the rollout side records its
+    quantisation so that the trainer can reproduce it ("TRACE's core idea":
+    rollout-guided rounding, with a compact cache of that information). The
+    pages do not fix the record's format; the reading taken here is one bit
+    per element: 1 when the magnitude was rounded up, i.e. the chosen grid
+    point g_k * D_b (D_b = fp32(S_b * s_t), the grid the codes were chosen
+    on) exceeds |x|; 0 when it was rounded down or hit exactly, and for blocks
+    with D_b == 0. Bit e of byte j holds element 8 j + e of the row. Together
+    with the scale bytes this is the record the trainer needs: the rounding
+    of x is floor or ceil on the grid, and the bit says which.
+
+    g_k has at most 2 significant bits and D_b at most 24, so the float64
+    product and the comparison are exact.
+    """
+    w = np.asarray(w, dtype=np.float32)
+    packed, sbytes, s_t = quantize(w)
+    s_b = e4m3_value(sbytes).astype(np.float32)
+    d_b = (s_b * s_t).astype(np.float32)
+    d_el = np.repeat(d_b.astype(np.float64), BLOCK, axis=1)
+    g = E2M1_GRID[unpack_codes(packed) & 7]
+    up = (g * d_el > np.abs(w).astype(np.float64)).astype(np.uint8)
+    n, k = w.shape
+    bits = up.reshape(n, k // 8, 8) << np.arange(8, dtype=np.uint8)
+    return bits.sum(axis=2).astype(np.uint8)
+
+
 def unpack_codes(codes: np.ndarray) -> np.ndarray:
     """[N, K/2] packed bytes -> [N, K] 4-bit codes (element 2j = low nibble)."""
     c = np.asarray(codes, dtype=np.uint8)

@@ -72,6 +72,19 @@ def test_quantize_rejects_bad_arguments(lib):
     assert "multiple of 16" in lib.fp4rl_last_error().decode()
 
 
+def test_quantize_record_rejects_bad_arguments(lib):
+    """The record entry point validates like fp4rl_nvfp4_quantize, and needs its round_up buffer."""
+    def qr(w, n, k, ru, wsb, layout=1):
+        return lib.fp4rl_nvfp4_quantize_record(w, 0, n, k, layout, FAKE, FAKE, FAKE, ru, FAKE, wsb, None)
+
+    ws = lib.fp4rl_nvfp4_quantize_workspace(8, 32)
+    assert qr(FAKE, 8, 32, None, ws) == ERR_NULL
+    assert "round_up" in lib.fp4rl_last_error().decode()
+    assert qr(FAKE, 8, 24, FAKE, ws) == ERR_SHAPE
+    assert qr(MIS, 8, 32, FAKE, ws) == ERR_ALIGN
+    assert qr(FAKE, 8, 32, FAKE, ws - 1) == ERR_WORKSPACE
+
+
 def test_linear_rejects_bad_arguments(lib):
     f = lib.fp4rl_fp4_lora_linear
     ws = lib.fp4rl_fp4_lora_linear_workspace(4, 8, 32, 8)

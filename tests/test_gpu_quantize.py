@@ -85,9 +85,8 @@ def test_edge_values():
         _assert_exact(_gpu_quantize(w, dev), nvfp4.quantize(w), name)
 
 
-def test_adversarial_midpoints():
+def _adversarial_weights():
     """Every row holds exact grid points, midpoints and their fp32 neighbours for its block scales."""
-    dev = device()
     rng = np.random.default_rng(6)
     n, k = 512, 256
     w = np.zeros((n, k), np.float32)
@@ -104,6 +103,12 @@ def test_adversarial_midpoints():
                                                      np.nextafter(pts, np.float32(0))))
             vals = vals * np.where(rng.random(16) < 0.5, -1, 1)
             w[i, 16 * b:16 * b + 16] = vals.astype(np.float32)
+    return w
+
+
+def test_adversarial_midpoints():
+    dev = device()
+    w = _adversarial_weights()
     say("quantize adversarial midpoints 512x256")
     _assert_exact(_gpu_quantize(w, dev), nvfp4.quantize(w), "adversarial")
 
@@ -155,6 +160,36 @@ def test_tiled_bf16_input_ragged():
         ct, st = tile_host(ref[0], ref[1], n, k)
         assert np.array_equal(tiled.codes.cpu().numpy(), ct) and np.array_equal(tiled.scales.cpu().numpy(), st)
         assert np.float32(tiled.tensor_scale.cpu().numpy()[0]) == ref[2]
+
+
+@pytest.mark.parametrize("layout", ["row_major", "tiled"])
+def test_rounding_record(layout):
+    """The rounding record (1 bit per element: rounded up in magnitude) is bit-exact, and the
+    codes and scales of the recording call equal the plain quantiser's."""
+    dev = device()
+    rng = np.random.default_rng(12)
+    cases = {
+        "37x80": normal_f32((37, 80), 0.02, 37),
+        "20x1296": normal_f32((20, 1296), 0.02, 20),
+        "1024x2048": normal_f32((1024, 2048), 0.02, 1024),
+        "adversarial": _adversarial_weights(),
+        "wide_range": (rng.standard_normal((16, 128)) * 10.0 ** rng.integers(-30, 30, (16, 128))).astype(np.float32),
+        "zeros": np.zeros((4, 64), np.float32),
+    }
+    for name, w in cases.items():
+        for bf16 in (False, True):
+            wr = bf16_values(bf16_bits(w)) if bf16 else w
+            n, k = w.shape
+            say(f"rounding record {name} {layout}{' bf16' if bf16 else ''}")
+            wt = bf16_to_dev(bf16_bits(w), dev) if bf16 else f32_to_dev(w, dev)
+            ru = torch.empty((n, k // 8), dtype=torch.uint8, device=dev)
+            q = fr.nvfp4_quantize(wt, layout=layout, round_up=ru)
+            torch.cuda.synchronize()
+            _assert_exact(nvfp4_from_dev(q), nvfp4.quantize(wr), f"{name} record call")
+            want = nvfp4.rounding_record(wr)
+            got = ru.cpu().numpy()
+            nbad = int(np.count_nonzero(got != want))
+            assert nbad == 0, f"{name} {layout} bf16={bf16}: {nbad} record bytes differ"
 
 
 def test_repeat_runs_identical():

@@ -152,6 +152,68 @@ def test_exact_midpoint_ties_go_to_even_index():
     assert list(c4[0, :7]) == [0, 2, 2, 4, 4, 6, 6]
 
 
+# ----------------------------------------------------- rounding record ----
+
+def _record_bits(w):
+    rec = nvfp4.rounding_record(w)
+    return np.unpackbits(rec, axis=1, bitorder="little")
+
+
+@pytest.mark.parametrize("seed,k", [(3, 16), (4, 48)])
+def test_rounding_record_brute_force(seed, k):
+    """The bit is 1 exactly when the brute-force nearest grid value exceeds |x| (rationals)."""
+    rng = np.random.default_rng(seed)
+    w = (rng.standard_normal((4, k)) * 0.02).astype(np.float32)
+    w[0, :4] = 0.0
+    c4, sbytes, s_t = _codes_of(w)
+    bits = _record_bits(w)
+    for n in range(4):
+        for kk in range(k):
+            d = Fraction(float(np.float32(np.float32(e4m3_value(sbytes[n, kk // 16])) * s_t)))
+            code = _brute_force_codes(w[n, kk], np.float32(float(d)))
+            up = GRID[code & 7] * d > abs(Fraction(float(w[n, kk])))
+            assert bits[n, kk] == int(up), (n, kk)
+
+
+def test_rounding_record_closed_cases():
+    """Exact grid points and saturated values round down (0); values just below a grid point
+    that round to it round up (1); an all-zero block records 0."""
+    d = 0.4375                                  # s_t = 2^-10, block byte 0x7E: D exact
+    blk = np.zeros((2, 16), dtype=np.float32)
+    grid = np.array([0.5, 1, 1.5, 2, 3, 4, 6]) * d
+    blk[0, :7] = grid                           # exact grid points
+    blk[0, 7:14] = np.nextafter(grid.astype(np.float32), np.float32(0))  # just below: up
+    blk[0, 15] = 2.625                          # the amax (= 6 D): exact, down
+    blk[1, :] = 0.0
+    bits = _record_bits(blk)
+    c4, sbytes, s_t = _codes_of(blk)
+    assert s_t == np.float32(2.0 ** -10) and sbytes[0, 0] == 0x7E
+    assert list(bits[0, :7]) == [0] * 7
+    assert list(bits[0, 7:14]) == [1] * 7
+    assert bits[0, 15] == 0 and not bits[1].any()
+    # |x| beyond 6 D: block 1's r_b = 1.0625 ties to the E4M3 value 1.0 (even), so
+    # D = 2^-10 and its max element sits at 6.375 D: saturated to 6 D, rounded down
+    sat = np.zeros((1, 32), dtype=np.float32)
+    sat[0, 0] = 2.625                           # tensor amax: s_t = 2^-10
+    sat[0, 16] = np.float32(1.0625 * 6 * 2.0 ** -10)
+    c4s, sb, st2 = _codes_of(sat)
+    assert st2 == np.float32(2.0 ** -10) and sb[0, 1] == 0x38
+    assert c4s[0, 16] & 7 == 7
+    assert _record_bits(sat)[0, 16] == 0
+
+
+def test_rounding_record_sign_symmetry_and_bound():
+    """-W gives the same record; a 1 means the grid value exceeds |x| by at most half a step."""
+    rng = np.random.default_rng(11)
+    w = (rng.standard_normal((8, 64)) * 0.02).astype(np.float32)
+    assert np.array_equal(nvfp4.rounding_record(w), nvfp4.rounding_record(-w))
+    packed, sbytes, s_t = quantize(w)
+    deq = np.abs(dequantize(packed, sbytes, s_t))
+    bits = _record_bits(w).astype(bool)
+    # dequantize uses the exact S_b * s_t; the record uses fp32(S_b * s_t): they agree to 2^-24
+    assert np.all(deq[bits] >= np.abs(w[bits]) * (1 - 2.0 ** -23))
+
+
 # ------------------------------------------------------------- golden ----
 
 def _load_golden(path):
