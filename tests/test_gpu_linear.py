@@ -86,6 +86,25 @@ def test_split_k_shapes(m, n, k, r):
     _check(y, linear.lora_linear(x, *q, a, b, LORA_SCALE), f"{m}x{n}x{k} r{r}")
 
 
+SPLITK_CONFIGS = [  # (m, n, k, r, kernel): every split-K instantiation, ragged in n and k
+    (33, 1000, 1040, 8, "splitk_kernel<2, 2, 4, 3>"),    # two row tiles per wave, three weight stages
+    (64, 4600, 3568, 32, "splitk_kernel<2, 2, 4, 2>"),   # two row tiles, two stages (> 256 output tiles)
+    (40, 9000, 3568, 16, "splitk_kernel<4, 2, 4, 2>"),   # four row tiles (wide), two stages
+    (48, 700, 9232, 16, "splitk_kernel<4, 2, 4, 2>"),    # long K: four row tiles, K split over workgroups
+]
+
+
+@pytest.mark.parametrize("m,n,k,r,kernel", SPLITK_CONFIGS)
+def test_split_k_launch_configs(m, n, k, r, kernel):
+    dev = device()
+    assert fr.fp4_linear_kernel_name(m, n, k, r) == kernel
+    w, x, a, b = _case(m, n, k, r, seed=m * 97 + n * 13 + k)
+    q = nvfp4.quantize(w)
+    say(f"linear {kernel} m={m} n={n} k={k} r={r}")
+    y = _run(dev, x, q, a, b, LORA_SCALE)
+    _check(y, linear.lora_linear(x, *q, a, b, LORA_SCALE), f"{m}x{n}x{k} r{r}")
+
+
 # a linear workspace starts with 4608 counter words: K-split tile counters,
 # t tile counters, finished-tile count, 64 ready-flag lines of 256 bytes
 COUNTER_BYTES = 4 * (512 + 64 * 64)
