@@ -57,3 +57,35 @@ def test_graph_replays_match_eager(m, n, k):
         fr.fp4_lora_linear(other_x, other_wq, other_a, other_b, 2.0)  # unrelated eager work in between
         torch.cuda.synchronize()
     say(f"  M={m} {n}x{k}: 4 replays identical to eager")
+
+
+@pytest.mark.parametrize("layout,dtype", [("tiled", torch.float32), ("row_major", torch.bfloat16)])
+def test_quantizer_graph_replays_match_eager(layout, dtype):
+    """The quantiser (both passes, with the rounding record) captured in a graph, ragged in n and k:
+    every replay writes the eager codes, scale bytes, tensor scale and record (no memset nodes)."""
+    dev = device()
+    n, k = 300, 1296
+    g = torch.Generator(device=dev)
+    g.manual_seed(5)
+    w = torch.randn((n, k), generator=g, device=dev).mul_(0.02).to(dtype)
+    out = fr.nvfp4_empty(n, k, layout, dev)
+    ru = torch.empty((n, k // 8), dtype=torch.uint8, device=dev)
+    ws = torch.empty(1 << 16, dtype=torch.uint8, device=dev)
+    fr.nvfp4_quantize(w, layout=layout, out=out, workspace=ws, round_up=ru)
+    torch.cuda.synchronize()
+    ref = [out.codes.clone(), out.scales.clone(), out.tensor_scale.clone(), ru.clone()]
+    gr = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(gr):
+        fr.nvfp4_quantize(w, layout=layout, out=out, workspace=ws, round_up=ru)
+    other = torch.randn((64, 256), generator=g, device=dev)
+    for i in range(4):
+        for t in (out.codes, out.scales, out.tensor_scale, ru):
+            t.zero_()
+        torch.cuda.synchronize()
+        gr.replay()
+        torch.cuda.synchronize()
+        got = [out.codes, out.scales, out.tensor_scale, ru]
+        assert all(torch.equal(a, b) for a, b in zip(got, ref)), f"replay {i} differs from eager"
+        fr.nvfp4_quantize(other, layout="tiled")  # unrelated eager work in between (its own workspace)
+        torch.cuda.synchronize()
+    say(f"  quantiser {layout} {dtype}: 4 replays identical to eager")
