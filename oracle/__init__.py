@@ -8,6 +8,7 @@ rollout hot path computes:
   dequantisation and the per-value rounding record (rounded up or down);
 * ``linear`` – y = x deq(Wq)^T + s (x A^T) B^T, the W4A16 linear with the
   LoRA update;
+* ``lora_backward`` – dX, dA and dB of that linear (the base stays frozen);
 * ``aqn``    – the Adaptive Quantization Noise RMSNorm: the exponential sigma
   schedule, Philox4x32-10 + Box-Muller noise, and the noisy-weight RMSNorm;
 * ``numerics`` – bf16 round-to-nearest-even and the rel-L2 metric.
@@ -22,4 +23,4 @@ here is pinned by a ``-m "not gpu"`` test against something other than
 itself (closed forms, brute force, torch CPU casts, torch's Philox header),
 except where a docstring says "parity unpinned".
 """
-from . import numerics, nvfp4, linear, aqn  # noqa: F401
+from . import numerics, nvfp4, linear, lora_backward, aqn  # noqa: F401
