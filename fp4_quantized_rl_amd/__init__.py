@@ -12,6 +12,7 @@ Operations (names follow the C ABI):
   nvfp4_to_tiled(wq)                        -> row-major NVFP4 repacked into the tiled layout
   fp4_lora_linear(x, wq, lora_a, lora_b, s) -> y = x deq(Wq)^T + s (x A^T) B^T  (bf16)
   lora_down / fp4_linear_lora_up            -> the two halves of fp4_lora_linear
+  fp4_lora_linear_backward(dy, x, wq, A, B, s) -> (dx bf16, dA fp32, dB fp32), the base frozen
   aqn_sigma(s0, s1, k, K)                   -> exponential AQN noise level
   aqn_rmsnorm(x, w, sigma, seed, step, ...) -> RMSNorm with W_noise = w + sigma z
   philox_words(seed, step, norm_id, n)      -> raw Philox4x32-10 output blocks
@@ -24,7 +25,7 @@ from dataclasses import dataclass
 
 __all__ = [
     "LIB_PATH", "Fp4rlError", "load_library", "NVFP4Weight", "nvfp4_empty", "nvfp4_quantize", "nvfp4_to_tiled",
-    "fp4_lora_linear",
+    "fp4_lora_linear", "fp4_lora_linear_backward", "fp4_lora_linear_backward_workspace_bytes",
     "lora_down", "fp4_linear_lora_up", "fp4_linear_kernel_name", "linear_workspace",
     "fp4_lora_linear_workspace_bytes", "fp4_linear_lora_up_workspace_bytes", "aqn_sigma", "aqn_rmsnorm", "philox_words",
     "EXPORTED_SYMBOLS",
@@ -61,6 +62,9 @@ _SIGNATURES = {
     "fp4rl_fp4_linear_lora_up": (_STATUS, [_P, _I64, _I64, _I64, _P, _P, _P, _P, _P, _I64, _P, _P, _c.c_size_t,
                                            _P]),
     "fp4rl_fp4_linear_kernel_name": (_c.c_char_p, [_I64, _I64, _I64, _I64]),
+    "fp4rl_fp4_lora_linear_backward_workspace": (_c.c_size_t, [_I64, _I64, _I64, _I64, _c.c_int32]),
+    "fp4rl_fp4_lora_linear_backward": (_STATUS, [_P, _P, _I64, _I64, _I64, _P, _P, _P, _P, _P, _I64, _c.c_float,
+                                                 _P, _P, _P, _P, _c.c_size_t, _P]),
     "fp4rl_aqn_sigma": (_c.c_float, [_c.c_float, _c.c_float, _c.c_int32, _c.c_int32]),
     "fp4rl_aqn_rmsnorm": (_STATUS, [_P, _I64, _I64, _P, _c.c_float, _c.c_uint64, _c.c_uint64, _c.c_uint32,
                                     _c.c_float, _P, _P, _P]),
@@ -259,6 +263,46 @@ def fp4_lora_linear(x, wq: NVFP4Weight, lora_a=None, lora_b=None, lora_scale: fl
                                          _stream(x.device)),
                "fp4_lora_linear")
     return out
+
+
+def fp4_lora_linear_backward_workspace_bytes(m: int, n: int, k: int, r: int, want_dx: bool = True) -> int:
+    return load_library().fp4rl_fp4_lora_linear_backward_workspace(m, n, k, r, int(bool(want_dx)))
+
+
+def fp4_lora_linear_backward(dy, x, wq: NVFP4Weight, lora_a=None, lora_b=None, lora_scale: float = 0.0,
+                             want_dx: bool = True, workspace=None):
+    """(dx, grad_a, grad_b) of y = x deq(Wq)^T + s (x A^T) B^T for dy bf16 [m, n].
+
+    dx is bf16 [m, k] (None when want_dx is False); grad_a fp32 [r, k] and
+    grad_b fp32 [n, r] (None without adapters). The base weight gets no gradient.
+    """
+    torch = _torch()
+    m, n, k = _linear_args(x, wq)
+    _dev_tensor(dy, "dy", (torch.bfloat16,), 2)
+    if dy.shape != (m, n):
+        raise ValueError(f"dy must be [{m}, {n}]")
+    r = 0
+    if lora_a is not None or lora_b is not None:
+        _dev_tensor(lora_a, "lora_a", (torch.bfloat16,), 2)
+        _dev_tensor(lora_b, "lora_b", (torch.bfloat16,), 2)
+        r = lora_a.shape[0]
+        if lora_a.shape != (r, k) or lora_b.shape != (n, r):
+            raise ValueError("LoRA shapes must be A [r, k] and B [n, r]")
+    dev = x.device
+    dx = torch.empty((m, k), dtype=torch.bfloat16, device=dev) if want_dx else None
+    ga = torch.empty((r, k), dtype=torch.float32, device=dev) if r else None
+    gb = torch.empty((n, r), dtype=torch.float32, device=dev) if r else None
+    lib = load_library()
+    ws_bytes = lib.fp4rl_fp4_lora_linear_backward_workspace(m, n, k, r, int(bool(want_dx)))
+    if workspace is None:
+        workspace = torch.empty(max(ws_bytes, 256), dtype=torch.uint8, device=dev)
+    with torch.cuda.device(dev):
+        _check(lib.fp4rl_fp4_lora_linear_backward(_ptr(dy), _ptr(x), m, n, k, _ptr(wq.codes), _ptr(wq.scales),
+                                                  _ptr(wq.tensor_scale), _ptr(lora_a), _ptr(lora_b), r,
+                                                  float(lora_scale), _ptr(dx), _ptr(ga), _ptr(gb), _ptr(workspace),
+                                                  workspace.numel(), _stream(dev)),
+               "fp4_lora_linear_backward")
+    return dx, ga, gb
 
 
 def lora_down(x, lora_a, lora_scale: float, out=None, workspace=None):

@@ -339,6 +339,74 @@ const char* fp4rl_fp4_linear_kernel_name(int64_t m, int64_t n, int64_t k, int64_
   return fp4rl::fp4_linear_kernel_name(m, n, k, r);
 }
 
+// ---------------------------------------------------------------- backward --
+
+static fp4rl_status check_backward_shape(int64_t m, int64_t n, int64_t k, int64_t r) {
+  FP4RL_REQUIRE(m >= 0 && n >= 0 && k >= 0 && r >= 0, FP4RL_ERR_SHAPE,
+                "negative size (m=%lld n=%lld k=%lld r=%lld)", (long long)m, (long long)n, (long long)k, (long long)r);
+  FP4RL_REQUIRE(k > 0 && k % 16 == 0, FP4RL_ERR_SHAPE, "k=%lld must be a positive multiple of 16", (long long)k);
+  FP4RL_REQUIRE(n % 8 == 0, FP4RL_ERR_SHAPE, "n=%lld must be a multiple of 8", (long long)n);
+  // the GEMM kernels address one 128-row operand tile with 32-bit byte offsets
+  FP4RL_REQUIRE(n < ((int64_t)1 << 22) && k < ((int64_t)1 << 22) && m < kMaxDim, FP4RL_ERR_SHAPE,
+                "n and k must be below 2^22, m below 2^31");
+  FP4RL_REQUIRE(r <= fp4rl::kMaxRank, FP4RL_ERR_SHAPE, "rank r=%lld exceeds %lld", (long long)r,
+                (long long)fp4rl::kMaxRank);
+  return FP4RL_OK;
+}
+
+size_t fp4rl_fp4_lora_linear_backward_workspace(int64_t m, int64_t n, int64_t k, int64_t r, int32_t want_dx) {
+  if (check_backward_shape(m, n, k, r) != FP4RL_OK || m == 0 || n == 0) return 0;
+  return fp4rl::backward_workspace(m, n, k, r, want_dx != 0, nullptr, nullptr);
+}
+
+fp4rl_status fp4rl_fp4_lora_linear_backward(const uint16_t* dy, const uint16_t* x, int64_t m, int64_t n, int64_t k,
+                                            const uint8_t* codes, const uint8_t* scales, const float* tensor_scale,
+                                            const uint16_t* lora_a, const uint16_t* lora_b, int64_t r,
+                                            float lora_scale, uint16_t* dx, float* grad_a, float* grad_b,
+                                            void* workspace, size_t workspace_bytes, fp4rl_stream stream) {
+  FP4RL_CHECK(check_backward_shape(m, n, k, r));
+  FP4RL_REQUIRE(std::isfinite(lora_scale), FP4RL_ERR_VALUE, "lora_scale is not finite");
+  FP4RL_REQUIRE((lora_a == nullptr) == (lora_b == nullptr), FP4RL_ERR_NULL,
+                "lora_a and lora_b must both be NULL or both be set");
+  if (lora_a == nullptr) r = 0;
+  FP4RL_REQUIRE(dx != nullptr || r > 0, FP4RL_ERR_NULL, "nothing to compute: dx is NULL and there are no adapters");
+  if (r > 0) {
+    FP4RL_REQUIRE(grad_a && grad_b, FP4RL_ERR_NULL, "r > 0 needs grad_a and grad_b");
+    FP4RL_REQUIRE(aligned(lora_a, 16) && aligned(lora_b, 16) && aligned(grad_a, 16) && aligned(grad_b, 16),
+                  FP4RL_ERR_ALIGN, "lora_a, lora_b, grad_a and grad_b must be 16-byte aligned");
+  }
+  if (dx) FP4RL_REQUIRE(aligned(dx, 16), FP4RL_ERR_ALIGN, "dx must be 16-byte aligned");
+  if (m == 0 || n == 0) {
+    // empty sums: every gradient is zero (dX and dA when n == 0, dA and dB when m == 0)
+    if (m == 0 && n == 0) return ok();
+    FP4RL_CHECK(check_device());
+    hipError_t e = hipSuccess;
+    if (dx && m > 0) e = fp4rl::launch_zero_words(dx, m * k / 2, stream);
+    if (e == hipSuccess && r > 0) e = fp4rl::launch_zero_words(grad_a, r * k, stream);
+    if (e == hipSuccess && r > 0 && n > 0) e = fp4rl::launch_zero_words(grad_b, n * r, stream);
+    return launched(e, "zero_words");
+  }
+  FP4RL_REQUIRE(dy != nullptr && aligned(dy, 16), dy ? FP4RL_ERR_ALIGN : FP4RL_ERR_NULL,
+                "dy must be non-NULL and 16-byte aligned");
+  if (r > 0) FP4RL_REQUIRE(x != nullptr && aligned(x, 16), x ? FP4RL_ERR_ALIGN : FP4RL_ERR_NULL,
+                           "x must be non-NULL and 16-byte aligned when r > 0");
+  if (dx) {
+    FP4RL_REQUIRE(codes && scales && tensor_scale, FP4RL_ERR_NULL, "dX needs codes, scales and tensor_scale");
+    FP4RL_REQUIRE(aligned(codes, 16) && aligned(scales, 16) && aligned(tensor_scale, 4), FP4RL_ERR_ALIGN,
+                  "codes and scales must be 16-byte aligned, tensor_scale 4-byte aligned");
+  }
+  const size_t need = fp4rl::backward_workspace(m, n, k, r, dx != nullptr, nullptr, nullptr);
+  FP4RL_REQUIRE(workspace != nullptr && workspace_bytes >= need, FP4RL_ERR_WORKSPACE, "workspace %zu < %zu bytes",
+                workspace_bytes, need);
+  FP4RL_REQUIRE(aligned(workspace, 256), FP4RL_ERR_ALIGN, "workspace must be 256-byte aligned");
+  FP4RL_CHECK(check_device());
+  fp4rl::BackwardWs w;
+  fp4rl::backward_workspace(m, n, k, r, dx != nullptr, &w, workspace);
+  return launched(fp4rl::launch_lora_backward(dy, x, m, n, k, codes, scales, tensor_scale, r > 0 ? lora_a : nullptr,
+                                              r > 0 ? lora_b : nullptr, r, lora_scale, dx, grad_a, grad_b, w, stream),
+                  "fp4_lora_linear_backward");
+}
+
 // --------------------------------------------------------------------- AQN --
 
 float fp4rl_aqn_sigma(float sigma_start, float sigma_end, int32_t k, int32_t num_stages) {

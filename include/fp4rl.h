@@ -198,6 +198,37 @@ fp4rl_status fp4rl_fp4_linear_lora_up(const uint16_t* x, int64_t m, int64_t n, i
 const char* fp4rl_fp4_linear_kernel_name(int64_t m, int64_t n, int64_t k, int64_t r);
 
 /* ------------------------------------------------------------------------
+ * LoRA backward through the frozen NVFP4 base (QeRL explainer, "NVFP4
+ * quantization and LoRA": the quantised base stays frozen, only the
+ * low-rank adapters are trained). For y = x deq(Wq)^T + s (x A^T) B^T and
+ * the incoming gradient dy = dL/dy:
+ *   dx     = dy deq(Wq) + s (dy B) A      bf16 [m][k] (rounded once, nearest-even)
+ *   grad_a = s (dy B)^T x                 fp32 [r][k]
+ *   grad_b = s dy^T (x A^T)               fp32 [n][r]
+ * There is no gradient for the base.
+ * Arguments: dy bf16 [m][n]; x bf16 [m][k] (read only when r > 0);
+ *   codes/scales/tensor_scale: the weight in the tiled layout, as for
+ *   fp4rl_fp4_lora_linear (read only when dx is set); lora_a bf16 [r][k] and
+ *   lora_b bf16 [n][r], both NULL (r ignored) or both set.
+ *   dx may be NULL (adapter gradients only, e.g. for a first layer); with no
+ *   adapters dx is required.
+ * Shapes: k a positive multiple of 16, n a multiple of 8, n and k below
+ *   2^22, 0 <= r <= 256. m == 0 or n == 0 writes zeros where a sum is empty.
+ * Workspace: fp4rl_fp4_lora_linear_backward_workspace(m, n, k, r, dx != NULL)
+ *   bytes, 256-byte aligned, caller-owned, no initial contents needed. It
+ *   holds the transposed dequantised weight (2 k n bytes, with dx), the
+ *   transposed adapters, t = s x A^T and h = s dy B, and the partial sums of
+ *   the adapter gradients.
+ * Errors: FP4RL_ERR_SHAPE, _NULL, _ALIGN, _VALUE (lora_scale not finite),
+ *   _WORKSPACE; nothing is launched on error. Asynchronous on `stream`. */
+size_t fp4rl_fp4_lora_linear_backward_workspace(int64_t m, int64_t n, int64_t k, int64_t r, int32_t want_dx);
+fp4rl_status fp4rl_fp4_lora_linear_backward(const uint16_t* dy, const uint16_t* x, int64_t m, int64_t n, int64_t k,
+                                            const uint8_t* codes, const uint8_t* scales, const float* tensor_scale,
+                                            const uint16_t* lora_a, const uint16_t* lora_b, int64_t r,
+                                            float lora_scale, uint16_t* dx, float* grad_a, float* grad_b,
+                                            void* workspace, size_t workspace_bytes, fp4rl_stream stream);
+
+/* ------------------------------------------------------------------------
  * AQN.
  * fp4rl_aqn_sigma [host]: sigma_k = sigma_start (sigma_end/sigma_start)^(k/(K-1)),
  *   computed in double and returned as float; K == 1 gives sigma_start.

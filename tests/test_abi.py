@@ -129,6 +129,43 @@ def test_linear_rejects_bad_arguments(lib):
             >= lib.fp4rl_fp4_linear_lora_up_workspace(64, 3584, 18944) + 64 * 32 * 4)
 
 
+def test_backward_rejects_bad_arguments(lib):
+    f = lib.fp4rl_fp4_lora_linear_backward
+    ws = lib.fp4rl_fp4_lora_linear_backward_workspace(4, 8, 32, 8, 1)
+    # Wt [k][n] bf16, Bt, At2, t, h, hs: each region 256-byte aligned
+    assert ws >= 32 * 8 * 2 + 8 * 8 * 2 + 32 * 16 * 2 + 2 * 4 * 8 * 4 + 4 * 16 * 2
+    assert lib.fp4rl_fp4_lora_linear_backward_workspace(4, 8, 32, 8, 0) < ws
+    assert lib.fp4rl_fp4_lora_linear_backward_workspace(4, 12, 32, 8, 1) == 0  # n % 8 != 0: invalid
+    args = dict(dy=FAKE, x=FAKE, m=4, n=8, k=32, c=FAKE, s=FAKE, ts=FAKE, a=FAKE, b=FAKE, r=8, ls=2.0, dx=FAKE,
+                ga=FAKE, gb=FAKE, ws=FAKE, wsb=ws)
+
+    def call(**kw):
+        a = dict(args, **kw)
+        return f(a["dy"], a["x"], a["m"], a["n"], a["k"], a["c"], a["s"], a["ts"], a["a"], a["b"], a["r"], a["ls"],
+                 a["dx"], a["ga"], a["gb"], a["ws"], a["wsb"], None)
+
+    assert call(k=24) == ERR_SHAPE
+    assert call(n=12) == ERR_SHAPE
+    assert call(r=257) == ERR_SHAPE
+    assert call(k=1 << 22) == ERR_SHAPE
+    assert call(ls=float("inf")) == ERR_VALUE
+    assert call(a=None) == ERR_NULL
+    assert call(a=None, b=None, dx=None) == ERR_NULL     # nothing to compute
+    assert call(ga=None) == ERR_NULL
+    assert call(dy=None) == ERR_NULL
+    assert call(x=None) == ERR_NULL
+    assert call(c=None) == ERR_NULL
+    assert call(dx=MIS) == ERR_ALIGN
+    assert call(gb=MIS) == ERR_ALIGN
+    assert call(wsb=ws - 1) == ERR_WORKSPACE
+    assert call(ws=None) == ERR_WORKSPACE
+    assert call(ws=FAKE + 16) == ERR_ALIGN
+    assert call(m=0, n=0) == OK
+    # x and the weight are not read when they are not needed
+    assert call(a=None, b=None, x=None, ga=None, gb=None, wsb=lib.fp4rl_fp4_lora_linear_backward_workspace(
+        4, 8, 32, 0, 1)) == ERR_HIP
+
+
 def test_aqn_rejects_bad_arguments(lib):
     f = lib.fp4rl_aqn_rmsnorm
     assert f(FAKE, 4, 512, FAKE, -1.0, 0, 0, 0, 1e-6, FAKE, None, None) == ERR_VALUE
