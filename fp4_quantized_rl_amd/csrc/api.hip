@@ -347,8 +347,8 @@ static fp4rl_status check_backward_shape(int64_t m, int64_t n, int64_t k, int64_
   FP4RL_REQUIRE(k > 0 && k % 16 == 0, FP4RL_ERR_SHAPE, "k=%lld must be a positive multiple of 16", (long long)k);
   FP4RL_REQUIRE(n % 8 == 0, FP4RL_ERR_SHAPE, "n=%lld must be a multiple of 8", (long long)n);
   // the GEMM kernels address one 128-row operand tile with 32-bit byte offsets
-  FP4RL_REQUIRE(n < ((int64_t)1 << 22) && k < ((int64_t)1 << 22) && m < kMaxDim, FP4RL_ERR_SHAPE,
-                "n and k must be below 2^22, m below 2^31");
+  FP4RL_REQUIRE(n < ((int64_t)1 << 22) && k < ((int64_t)1 << 22) && m < ((int64_t)1 << 22), FP4RL_ERR_SHAPE,
+                "m, n and k must be below 2^22");
   FP4RL_REQUIRE(r <= fp4rl::kMaxRank, FP4RL_ERR_SHAPE, "rank r=%lld exceeds %lld", (long long)r,
                 (long long)fp4rl::kMaxRank);
   return FP4RL_OK;

@@ -5,21 +5,21 @@
 // y = x deq(Wq)^T + s (x A^T) B^T the backward needs
 //   dX = dY deq(Wq) + s (dY B) A,   dA = s (dY B)^T x,   dB = s dY^T (x A^T).
 //
-// The contraction of dX runs over the output features n, across the rows of
-// the tiled weight, whose codes are contiguous along k. Work is split as:
-//   1. dequant_t_kernel: the tiled NVFP4 weight -> Wt = g S_b as bf16 [K][N]
-//      (exact: every g S_b has at most 6 significant bits), one pass.
-//   2. transpose_u16_kernel: B -> Bt [r][N]; A -> At2 [K][2 rp] = (A^T | A^T),
-//      rank columns r..rp zero.
-//   3. nt_gemm_kernel (bf16 MFMA 16x16x32, fp32 accumulate): with both
-//      operands contiguous along the contraction,
-//        t = s x A^T     [M][r] fp32,
-//        h = s dY Bt^T   [M][r] fp32, also split into bf16 hi | lo [M][2 rp],
-//        dX = s_t dY Wt^T + (hi | lo) At2^T, rounded once to bf16.
-//      The LoRA term of dX is a second contraction segment of the same
-//      kernel; the hi + lo split keeps h to ~2^-17 relative.
-//   4. tn_grad_kernel (fp32 VALU, M split over workgroups, slices summed in
-//      order by reduce_kernel): dA = h^T x, dB = dY^T t.
+// Every product runs on one bf16 MFMA GEMM kernel whose operands are both
+// contiguous along the contraction (nt_gemm_kernel), so the other operands
+// are first laid out that way:
+//   1. dequant_t_kernel: the tiled NVFP4 weight (codes contiguous along k)
+//      -> Wt = g S_b as bf16 [K][N], exact (every g S_b has at most 6
+//      significant bits).
+//   2. transposes: B -> Bt [r][N]; A -> At2 [K][2 rp] = (A^T | A^T); dY and x
+//      -> dYt [N][mp], Xt [K][mp], so that tokens become a contraction.
+//   3. t = s x A^T and h = s dY B (contraction split over workgroups, fp32
+//      partials), each summed and split into bf16 hi + lo (v = hi + lo to
+//      ~2^-17 relative): tst, hst [2 rp][mp] and hs [M][2 rp].
+//   4. dX = s_t dY Wt^T + (hi | lo of h) At2^T, one launch with two
+//      contraction segments, rounded once to bf16.
+//   5. dB = dYt (tst)^T and dA = hst Xt^T (token contraction split over
+//      workgroups); fold_kernel adds the slices and the hi and lo halves.
 #include <algorithm>
 
 #include "device.hpp"
@@ -93,30 +93,62 @@ __global__ __launch_bounds__(256) void transpose_u16_kernel(const uint16_t* __re
   }
 }
 
+
+// out[c][i] = in[i][c] with 16-byte accesses on both sides (cols, ldo and
+// rows_pad multiples of 8); rows rows..rows_pad of out are zero.
+__global__ __launch_bounds__(256) void transpose16_kernel(const uint16_t* __restrict__ in, int rows, int cols,
+                                                          uint16_t* __restrict__ out, int ldo, int rows_pad) {
+  __shared__ __align__(16) uint16_t tl[64][66];
+  const int c0 = 64 * blockIdx.x, r0 = 64 * blockIdx.y;
+#pragma unroll
+  for (int p = 0; p < 2; ++p) {
+    const int e = threadIdx.x + 256 * p, i = e >> 3, cp = 8 * (e & 7);
+    uint4 v = make_uint4(0u, 0u, 0u, 0u);
+    if (r0 + i < rows && c0 + cp < cols) v = *reinterpret_cast<const uint4*>(in + (int64_t)(r0 + i) * cols + c0 + cp);
+    uint32_t* d = reinterpret_cast<uint32_t*>(&tl[i][cp]);
+    d[0] = v.x; d[1] = v.y; d[2] = v.z; d[3] = v.w;
+  }
+  __syncthreads();
+#pragma unroll
+  for (int p = 0; p < 2; ++p) {
+    const int e = threadIdx.x + 256 * p, cc = e >> 3, ip = 8 * (e & 7);
+    if (c0 + cc < cols && r0 + ip < rows_pad) {
+      uint32_t w[4];
+#pragma unroll
+      for (int t = 0; t < 4; ++t) w[t] = (uint32_t)tl[ip + 2 * t][cc] | ((uint32_t)tl[ip + 2 * t + 1][cc] << 16);
+      *reinterpret_cast<uint4*>(out + (int64_t)(c0 + cc) * ldo + r0 + ip) = make_uint4(w[0], w[1], w[2], w[3]);
+    }
+  }
+}
+
 // ---------------------------------------------------------------------------
 // 3. C[m][q] = alpha sum_c L1[m][c] R1[q][c] (+ sum_c L2[m][c] R2[q][c]), bf16
-// operands with rows contiguous along c (c % 8 == 0), fp32 accumulation.
-// A workgroup computes a 128 (m) x 128 (q) tile with 4 waves of 64 x 64
-// (4 x 4 MFMA tiles each). Contraction chunks of 64 are loaded to registers
-// one chunk ahead and written to one of two LDS slabs per operand (rows
-// padded to 144 B: conflict-free 16-byte fragment reads); one barrier per
-// chunk. Rows past M or Q are clamped (loaded, never stored); pieces past c
-// read as zero through the buffer descriptor's range.
+// operands with rows contiguous along c (row strides and lengths multiples of
+// 8), fp32 accumulation. A workgroup computes a 128 (m) x 128 (q) tile with 4
+// waves of 64 x 64 (4 x 4 MFMA tiles each) over one slice of the
+// contraction (blockIdx.y; one slice unless the launch splits it).
+// Contraction chunks of 64 are loaded to registers one chunk ahead and
+// written to one of two LDS slabs per operand (rows padded to 144 B:
+// conflict-free 16-byte fragment reads); one barrier per chunk. Rows past M
+// or Q are clamped (loaded, never stored); pieces past the slice read as
+// zero (their offsets fall outside the buffer descriptor's range).
 // A lane's result holds q = 4 g + v of MFMA column li = m, so stores are
-// 4 consecutive outputs of one row.
+// 4 consecutive outputs of one row. Outputs: bf16 y [M][Q], or fp32
+// part[slice][M][Q].
 // ---------------------------------------------------------------------------
 constexpr int kGT = 128, kGC = 64, kGPitch = kGC + 8;
 
 struct Seg {
-  const uint16_t* l = nullptr;  // [M][c]
-  const uint16_t* r = nullptr;  // [Q][c]
+  const uint16_t* l = nullptr;  // [M][ld]
+  const uint16_t* r = nullptr;  // [Q][ld]
+  int ld = 0;                   // row stride of both operands (elements)
   int c = 0;                    // contraction length (0: no segment)
+  int slice = 0;                // contraction per blockIdx.y (a multiple of kGC; >= c: unsplit)
 };
 
 template <bool BF16OUT>
 __global__ __launch_bounds__(256) void nt_gemm_kernel(Seg s1, Seg s2, int M, int Q, const float* __restrict__ alpha_dev,
-                                                      float alpha, uint16_t* __restrict__ ybf, float* __restrict__ yf,
-                                                      uint16_t* __restrict__ ysplit, int rp) {
+                                                      float alpha, uint16_t* __restrict__ ybf, float* __restrict__ part) {
   __shared__ __align__(16) uint16_t ls[2][kGT * kGPitch];
   __shared__ __align__(16) uint16_t rs[2][kGT * kGPitch];
   const int MT = (M + kGT - 1) / kGT;
@@ -133,23 +165,23 @@ __global__ __launch_bounds__(256) void nt_gemm_kernel(Seg s1, Seg s2, int M, int
 #pragma unroll
     for (int j = 0; j < 4; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  auto run = [&](const Seg& S) {
-    const int C = S.c, NC = (C + kGC - 1) / kGC;
+  auto run = [&](const Seg& S, int c0, int clen) {
+    const int NC = (clen + kGC - 1) / kGC;
     const int lrows = min(kGT, M - m0), rrows = min(kGT, Q - q0);
     const __amdgpu_buffer_rsrc_t lrs = __builtin_amdgcn_make_buffer_rsrc(
-        const_cast<uint16_t*>(S.l + (int64_t)m0 * C), 0, 2 * lrows * C, kRsrcWord3);
+        const_cast<uint16_t*>(S.l + (int64_t)m0 * S.ld + c0), 0, 2 * ((lrows - 1) * S.ld + clen), kRsrcWord3);
     const __amdgpu_buffer_rsrc_t rrs = __builtin_amdgcn_make_buffer_rsrc(
-        const_cast<uint16_t*>(S.r + (int64_t)q0 * C), 0, 2 * rrows * C, kRsrcWord3);
+        const_cast<uint16_t*>(S.r + (int64_t)q0 * S.ld + c0), 0, 2 * ((rrows - 1) * S.ld + clen), kRsrcWord3);
     uint32_t loff[4], roff[4];
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      loff[i] = 2u * ((uint32_t)min(prow + 32 * i, lrows - 1) * (uint32_t)C + 8 * pcol);
-      roff[i] = 2u * ((uint32_t)min(prow + 32 * i, rrows - 1) * (uint32_t)C + 8 * pcol);
+      loff[i] = 2u * ((uint32_t)min(prow + 32 * i, lrows - 1) * (uint32_t)S.ld + 8 * pcol);
+      roff[i] = 2u * ((uint32_t)min(prow + 32 * i, rrows - 1) * (uint32_t)S.ld + 8 * pcol);
     }
     uint4 lv[4], rv[4];
     auto load = [&](int ch) {
       ch = min(ch, NC - 1);
-      const uint32_t out = kGC * ch + 8 * pcol < C ? 0u : 0x80000000u;
+      const uint32_t out = kGC * ch + 8 * pcol < clen ? 0u : 0x80000000u;
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         lv[i] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(lrs, (int)((loff[i] + 2u * kGC * ch) | out), 0, 0));
@@ -191,14 +223,16 @@ __global__ __launch_bounds__(256) void nt_gemm_kernel(Seg s1, Seg s2, int M, int
     }
   };
 
-  run(s1);
+  const int c0 = blockIdx.y * s1.slice;
+  run(s1, c0, min(s1.slice, s1.c - c0));
   const float al = alpha_dev ? *alpha_dev : alpha;
 #pragma unroll
   for (int i = 0; i < 4; ++i)
 #pragma unroll
     for (int j = 0; j < 4; ++j) acc[i][j] *= al;
-  if (s2.c > 0) run(s2);
+  if (s2.c > 0) run(s2, 0, s2.c);  // only with an unsplit first segment
 
+  float* pout = part ? part + (int64_t)blockIdx.y * M * Q : nullptr;
 #pragma unroll
   for (int i = 0; i < 4; ++i)
 #pragma unroll
@@ -216,135 +250,111 @@ __global__ __launch_bounds__(256) void nt_gemm_kernel(Seg s1, Seg s2, int M, int
             if (q + e < Q) yp[e] = (uint16_t)f32_to_bf16(v[e]);
         }
       } else {
+        float* yp = pout + (int64_t)m * Q + q;
+        if (q + 3 < Q && (Q & 3) == 0) {
+          *reinterpret_cast<float4*>(yp) = make_float4(v[0], v[1], v[2], v[3]);
+        } else {
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          if (q + e < Q) yf[(int64_t)m * Q + q + e] = v[e];
-          if (ysplit && q + e < rp) {
-            const float f = q + e < Q ? v[e] : 0.0f;
-            const uint32_t hb = f32_to_bf16(f);
-            ysplit[(int64_t)m * 2 * rp + q + e] = (uint16_t)hb;
-            ysplit[(int64_t)m * 2 * rp + rp + q + e] = (uint16_t)f32_to_bf16(f - __uint_as_float(hb << 16));
-          }
+          for (int e = 0; e < 4; ++e)
+            if (q + e < Q) yp[e] = v[e];
         }
       }
     }
 }
 
 // ---------------------------------------------------------------------------
-// 4. part[slice][p][q] = sum over the slice's rows m of L[m][p] R[m][q]
-// (fp32 FMA, rows in order). 64 x 64 output tiles, 16 rows of each operand
-// per step staged in LDS as fp32; a thread owns 4 x 4 outputs.
+// 4. Finishing kernels (slices summed in order).
+// rank_split_kernel: v = sum_s part[s][m][j] (m < M, j < r) split into bf16
+//   hi + lo; written as sp [M][2 rp] (hi | lo) and/or spt [2 rp][mp]
+//   (transposed, for contractions over tokens). Ranks r..rp and tokens
+//   M..mp are zero.
+// fold_kernel: out[a][b] = sum_s (part[s][a lda + b] + part[s][a lda + b + off]),
+//   the hi and lo halves of a contraction against a split operand.
 // ---------------------------------------------------------------------------
-template <typename T>
-__device__ __forceinline__ float ld_f32(const T* p, int64_t i) {
-  if constexpr (sizeof(T) == 2) return __uint_as_float((uint32_t)p[i] << 16);  // bf16
-  else return p[i];
-}
-
-template <typename TL, typename TR>
-__global__ __launch_bounds__(256) void tn_grad_kernel(const TL* __restrict__ L, int P, const TR* __restrict__ R, int Q,
-                                                      int M, int mslice, float* __restrict__ part) {
-  __shared__ __align__(16) float lsh[16][64];
-  __shared__ __align__(16) float rsh[16][64];
-  const int PT = (P + 63) / 64;
-  const int pt = blockIdx.x % PT, qt = blockIdx.x / PT;
-  const int p0 = 64 * pt, q0 = 64 * qt;
-  const int mb = blockIdx.y * mslice, me = min(M, mb + mslice);
-  const int tp = threadIdx.x >> 4, tq = threadIdx.x & 15;
-  const int er = threadIdx.x >> 4, ec = 4 * (threadIdx.x & 15);
-  float acc[4][4] = {};
-  for (int m0 = mb; m0 < me; m0 += 16) {
-    const int m = m0 + er;
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const int p = p0 + ec + j, q = q0 + ec + j;
-      lsh[er][ec + j] = (m < me && p < P) ? ld_f32(L, (int64_t)m * P + p) : 0.0f;
-      rsh[er][ec + j] = (m < me && q < Q) ? ld_f32(R, (int64_t)m * Q + q) : 0.0f;
-    }
-    __syncthreads();
-#pragma unroll
-    for (int mm = 0; mm < 16; ++mm) {
-      const float4 lv = *reinterpret_cast<const float4*>(&lsh[mm][4 * tp]);
-      const float4 rv = *reinterpret_cast<const float4*>(&rsh[mm][4 * tq]);
-      const float l4[4] = {lv.x, lv.y, lv.z, lv.w}, r4[4] = {rv.x, rv.y, rv.z, rv.w};
-#pragma unroll
-      for (int a = 0; a < 4; ++a)
-#pragma unroll
-        for (int b = 0; b < 4; ++b) acc[a][b] = fmaf(l4[a], r4[b], acc[a][b]);
-    }
-    __syncthreads();
-  }
-  float* out = part + (int64_t)blockIdx.y * P * Q;
-#pragma unroll
-  for (int a = 0; a < 4; ++a) {
-    const int p = p0 + 4 * tp + a;
-    if (p >= P) continue;
-#pragma unroll
-    for (int b = 0; b < 4; ++b) {
-      const int q = q0 + 4 * tq + b;
-      if (q < Q) out[(int64_t)p * Q + q] = acc[a][b];
-    }
-  }
-}
-
-// out[i] = sum_s part[s][i], slices in order
-__global__ __launch_bounds__(256) void slice_sum_kernel(const float* __restrict__ part, int slices, int64_t count,
-                                                        float* __restrict__ out) {
-  for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < count; i += (int64_t)gridDim.x * 256) {
+__global__ __launch_bounds__(256) void rank_split_kernel(const float* __restrict__ part, int slices, int M, int r,
+                                                         int rp, int mp, uint16_t* __restrict__ sp,
+                                                         uint16_t* __restrict__ spt) {
+  const int64_t count = (int64_t)rp * mp;
+  const int64_t sstride = (int64_t)M * r;
+  for (int64_t e = (int64_t)blockIdx.x * 256 + threadIdx.x; e < count; e += (int64_t)gridDim.x * 256) {
+    const int j = (int)(e / mp), m = (int)(e - (int64_t)j * mp);  // tokens fastest: spt rows are contiguous
     float v = 0.0f;
-    for (int s = 0; s < slices; ++s) v += part[(int64_t)s * count + i];
-    out[i] = v;
+    if (m < M && j < r)
+      for (int s = 0; s < slices; ++s) v += part[s * sstride + (int64_t)m * r + j];
+    const uint32_t hb = f32_to_bf16(v);
+    const uint16_t hi = (uint16_t)hb, lo = (uint16_t)f32_to_bf16(v - __uint_as_float(hb << 16));
+    if (spt) {
+      spt[(int64_t)j * mp + m] = hi;
+      spt[(int64_t)(rp + j) * mp + m] = lo;
+    }
+    if (sp && m < M) {
+      sp[(int64_t)m * 2 * rp + j] = hi;
+      sp[(int64_t)m * 2 * rp + rp + j] = lo;
+    }
   }
 }
 
-int grad_slices(int64_t m, int64_t p, int64_t q) {
-  const int64_t tiles = ((p + 63) / 64) * ((q + 63) / 64);
-  int64_t s = (1024 + tiles - 1) / tiles;
-  s = std::min<int64_t>(s, std::max<int64_t>(1, m / 256));
-  return (int)std::max<int64_t>(1, std::min<int64_t>(s, 32));
+__global__ __launch_bounds__(256) void fold_kernel(const float* __restrict__ part, int slices, int64_t sstride, int A,
+                                                   int B, int lda, int64_t off, float* __restrict__ out) {
+  const int64_t count = (int64_t)A * B;
+  for (int64_t e = (int64_t)blockIdx.x * 256 + threadIdx.x; e < count; e += (int64_t)gridDim.x * 256) {
+    const int a = (int)(e / B), b = (int)(e - (int64_t)a * B);
+    const int64_t i = (int64_t)a * lda + b;
+    float v = 0.0f;
+    for (int s = 0; s < slices; ++s) v += part[s * sstride + i] + part[s * sstride + i + off];
+    out[e] = v;
+  }
 }
 
-int grad_mslice(int64_t m, int slices) { return (int)(((m + slices - 1) / slices + 15) / 16 * 16); }
+__global__ __launch_bounds__(256) void zero_kernel(uint32_t* __restrict__ p, int64_t words) {
+  for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < words; i += (int64_t)gridDim.x * 256) p[i] = 0u;
+}
 
 size_t al256(size_t v) { return (v + 255) / 256 * 256; }
 
-template <typename TL, typename TR>
-hipError_t launch_tn(const TL* L, int64_t p, const TR* R, int64_t q, int64_t m, float* part, float* out,
-                     hipStream_t st) {
-  const int slices0 = grad_slices(m, p, q);
-  const int mslice = grad_mslice(m, slices0);
-  const int slices = (int)((m + mslice - 1) / mslice);
-  const unsigned tiles = (unsigned)(((p + 63) / 64) * ((q + 63) / 64));
-  float* dst = slices > 1 ? part : out;
-  hipLaunchKernelGGL((tn_grad_kernel<TL, TR>), dim3(tiles, (unsigned)slices), dim3(256), 0, st, L, (int)p, R, (int)q,
-                     (int)m, mslice, dst);
-  if (slices > 1) {
-    const int64_t count = p * q;
-    const unsigned grid = (unsigned)std::min<int64_t>((count + 255) / 256, 4096);
-    hipLaunchKernelGGL(slice_sum_kernel, dim3(grid), dim3(256), 0, st, part, slices, count, out);
-  }
+// Contraction slices for a launch of `tiles` output tiles: enough workgroups
+// to fill the chip (>= 512), each slice at least 512 long (a multiple of the
+// 64-wide chunk).
+int nt_slice_len(int64_t tiles, int64_t c) {
+  int64_t s = (512 + tiles - 1) / tiles;
+  s = std::max<int64_t>(1, std::min<int64_t>(s, c / 512));
+  const int64_t len = ((c + s - 1) / s + kGC - 1) / kGC * kGC;
+  return (int)len;
+}
+int nt_slices(int64_t tiles, int64_t c) {
+  const int64_t len = nt_slice_len(tiles, c);
+  return (int)((c + len - 1) / len);
+}
+int64_t nt_tiles(int64_t m, int64_t q) { return ((m + kGT - 1) / kGT) * ((q + kGT - 1) / kGT); }
+
+hipError_t launch_nt_bf16(Seg s1, Seg s2, int64_t m, int64_t q, const float* alpha_dev, uint16_t* y, hipStream_t st) {
+  s1.slice = s1.c;
+  hipLaunchKernelGGL(nt_gemm_kernel<true>, dim3((unsigned)nt_tiles(m, q)), dim3(256), 0, st, s1, s2, (int)m, (int)q,
+                     alpha_dev, 0.0f, y, nullptr);
   return hipGetLastError();
 }
 
-hipError_t launch_nt(bool bf16out, Seg s1, Seg s2, int64_t m, int64_t q, const float* alpha_dev, float alpha,
-                     uint16_t* ybf, float* yf, uint16_t* ysplit, int64_t rp, hipStream_t st) {
-  const unsigned grid = (unsigned)(((m + kGT - 1) / kGT) * ((q + kGT - 1) / kGT));
-  if (bf16out)
-    hipLaunchKernelGGL(nt_gemm_kernel<true>, dim3(grid), dim3(256), 0, st, s1, s2, (int)m, (int)q, alpha_dev, alpha,
-                       ybf, yf, ysplit, (int)rp);
-  else
-    hipLaunchKernelGGL(nt_gemm_kernel<false>, dim3(grid), dim3(256), 0, st, s1, s2, (int)m, (int)q, alpha_dev, alpha,
-                       ybf, yf, ysplit, (int)rp);
-  return hipGetLastError();
+// fp32 partial products part[slice][m][q]; returns the number of slices
+int launch_nt_part(Seg s1, int64_t m, int64_t q, float alpha, float* part, hipStream_t st) {
+  const int64_t tiles = nt_tiles(m, q);
+  s1.slice = nt_slice_len(tiles, s1.c);
+  const int slices = nt_slices(tiles, s1.c);
+  hipLaunchKernelGGL(nt_gemm_kernel<false>, dim3((unsigned)tiles, (unsigned)slices), dim3(256), 0, st, s1, Seg{},
+                     (int)m, (int)q, nullptr, alpha, nullptr, part);
+  return slices;
 }
+
+unsigned flat_grid(int64_t count) { return (unsigned)std::max<int64_t>(1, std::min<int64_t>((count + 255) / 256, 8192)); }
 
 }  // namespace
 
-// Workspace regions, in order, each 256-byte aligned:
-//   Wt [k][n] bf16 (only with dX), Bt [r][n] bf16, At2 [k][2 rp] bf16,
-//   t [m][r] fp32, h [m][r] fp32, hs [m][2 rp] bf16, slice partials fp32.
+// Workspace regions, in order, each 256-byte aligned (rp = r rounded up to 8,
+// mp = m rounded up to 8):
+//   Wt [k][n] bf16 (dX only); with adapters: Bt [r][n], At2 [k][2 rp] (dX
+//   only), dYt [n][mp], Xt [k][mp], hs [m][2 rp] (dX only), hst and tst
+//   [2 rp][mp] (bf16), and the fp32 slice partials of every split product.
 size_t backward_workspace(int64_t m, int64_t n, int64_t k, int64_t r, bool want_dx, BackwardWs* w, void* base) {
-  const int64_t rp = (r + 7) / 8 * 8;
+  const int64_t rp = (r + 7) / 8 * 8, mp = (m + 7) / 8 * 8;
   size_t off = 0;
   auto take = [&](size_t bytes) {
     const size_t o = off;
@@ -356,12 +366,17 @@ size_t backward_workspace(int64_t m, int64_t n, int64_t k, int64_t r, bool want_
   if (r > 0) {
     v.bt = reinterpret_cast<uint16_t*>(take((size_t)r * n * 2));
     if (want_dx) v.at2 = reinterpret_cast<uint16_t*>(take((size_t)k * 2 * rp * 2));
-    v.t = reinterpret_cast<float*>(take((size_t)m * r * 4));
-    v.h = reinterpret_cast<float*>(take((size_t)m * r * 4));
+    v.dyt = reinterpret_cast<uint16_t*>(take((size_t)n * mp * 2));
+    v.xt = reinterpret_cast<uint16_t*>(take((size_t)k * mp * 2));
     if (want_dx) v.hs = reinterpret_cast<uint16_t*>(take((size_t)m * 2 * rp * 2));
-    const int sa = grad_slices(m, r, k), sb = grad_slices(m, n, r);
-    const size_t pa = sa > 1 ? (size_t)sa * r * k * 4 : 0, pb = sb > 1 ? (size_t)sb * n * r * 4 : 0;
-    if (pa || pb) v.part = reinterpret_cast<float*>(take(std::max(pa, pb)));
+    v.hst = reinterpret_cast<uint16_t*>(take((size_t)2 * rp * mp * 2));
+    v.tst = reinterpret_cast<uint16_t*>(take((size_t)2 * rp * mp * 2));
+    // partials: t (x A^T), h (dY Bt^T), dB (dYt tst^T), dA (hst Xt^T)
+    const size_t pt = (size_t)nt_slices(nt_tiles(m, r), k) * m * r;
+    const size_t ph = (size_t)nt_slices(nt_tiles(m, r), n) * m * r;
+    const size_t pb = (size_t)nt_slices(nt_tiles(n, 2 * rp), mp) * n * 2 * rp;
+    const size_t pa = (size_t)nt_slices(nt_tiles(2 * rp, k), mp) * 2 * rp * k;
+    v.part = reinterpret_cast<float*>(take(4 * std::max(std::max(pt, ph), std::max(pb, pa))));
   }
   if (w) *w = v;
   return off;
@@ -371,7 +386,7 @@ hipError_t launch_lora_backward(const uint16_t* dy, const uint16_t* x, int64_t m
                                 const uint8_t* codes, const uint8_t* scales, const float* tensor_scale,
                                 const uint16_t* a, const uint16_t* b, int64_t r, float s, uint16_t* dx, float* da,
                                 float* db, const BackwardWs& w, hipStream_t st) {
-  const int64_t rp = (r + 7) / 8 * 8;
+  const int64_t rp = (r + 7) / 8 * 8, mp = (m + 7) / 8 * 8;
   hipError_t e = hipSuccess;
   if (dx) {
     const int64_t kc = (k + 127) / 128, rg = ((n + 15) / 16 + 3) / 4;
@@ -384,33 +399,45 @@ hipError_t launch_lora_backward(const uint16_t* dy, const uint16_t* x, int64_t m
                        st, b, (int)n, (int)r, w.bt, (int)n, 0, (int)n);
     if (dx)
       for (int half = 0; half < 2; ++half)
-        hipLaunchKernelGGL(transpose_u16_kernel, dim3((unsigned)((k + 63) / 64), (unsigned)((rp + 63) / 64)),
-                           dim3(256), 0, st, a, (int)r, (int)k, w.at2, (int)(2 * rp), (int)(half * rp), (int)rp);
+        hipLaunchKernelGGL(transpose16_kernel, dim3((unsigned)((k + 63) / 64), (unsigned)((rp + 63) / 64)), dim3(256),
+                           0, st, a, (int)r, (int)k, w.at2 + half * rp, (int)(2 * rp), (int)rp);
+    // tokens become the contraction of dA and dB: dY and x transposed, zero-padded to mp tokens
+    hipLaunchKernelGGL(transpose16_kernel, dim3((unsigned)((n + 63) / 64), (unsigned)((mp + 63) / 64)), dim3(256), 0,
+                       st, dy, (int)m, (int)n, w.dyt, (int)mp, (int)mp);
+    hipLaunchKernelGGL(transpose16_kernel, dim3((unsigned)((k + 63) / 64), (unsigned)((mp + 63) / 64)), dim3(256), 0,
+                       st, x, (int)m, (int)k, w.xt, (int)mp, (int)mp);
     if ((e = hipGetLastError()) != hipSuccess) return e;
-    // t = s x A^T, h = s dY B (and its bf16 hi | lo split for the dX segment)
-    if ((e = launch_nt(false, Seg{x, a, (int)k}, Seg{}, m, r, nullptr, s, nullptr, w.t, nullptr, 0, st)) != hipSuccess)
-      return e;
-    if ((e = launch_nt(false, Seg{dy, w.bt, (int)n}, Seg{}, m, r, nullptr, s, nullptr, w.h, dx ? w.hs : nullptr, rp,
-                       st)) != hipSuccess)
-      return e;
+    // t = s x A^T -> tst (hi | lo, transposed)
+    int sl = launch_nt_part(Seg{x, a, (int)k, (int)k}, m, r, s, w.part, st);
+    hipLaunchKernelGGL(rank_split_kernel, dim3(flat_grid(rp * mp)), dim3(256), 0, st, w.part, sl, (int)m, (int)r,
+                       (int)rp, (int)mp, nullptr, w.tst);
+    // h = s dY B -> hst (transposed) and hs (for the LoRA segment of dX)
+    sl = launch_nt_part(Seg{dy, w.bt, (int)n, (int)n}, m, r, s, w.part, st);
+    hipLaunchKernelGGL(rank_split_kernel, dim3(flat_grid(rp * mp)), dim3(256), 0, st, w.part, sl, (int)m, (int)r,
+                       (int)rp, (int)mp, dx ? w.hs : nullptr, w.hst);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
   }
   if (dx) {
-    const Seg lora = r > 0 ? Seg{w.hs, w.at2, (int)(2 * rp)} : Seg{};
-    if ((e = launch_nt(true, Seg{dy, w.wt, (int)n}, lora, m, k, tensor_scale, 0.0f, dx, nullptr, nullptr, 0, st)) !=
-        hipSuccess)
-      return e;
+    const Seg lora = r > 0 ? Seg{w.hs, w.at2, (int)(2 * rp), (int)(2 * rp)} : Seg{};
+    if ((e = launch_nt_bf16(Seg{dy, w.wt, (int)n, (int)n}, lora, m, k, tensor_scale, dx, st)) != hipSuccess) return e;
   }
   if (r > 0) {
-    if ((e = launch_tn<float, uint16_t>(w.h, r, x, k, m, w.part, da, st)) != hipSuccess) return e;  // dA = h^T x
-    if ((e = launch_tn<uint16_t, float>(dy, n, w.t, r, m, w.part, db, st)) != hipSuccess) return e;  // dB = dY^T t
+    // dB[n][j] = sum_m dY[m][n] t[m][j]: rows n of dYt against the 2 rp rows of tst, halves folded
+    int sl = launch_nt_part(Seg{w.dyt, w.tst, (int)mp, (int)mp}, n, 2 * rp, 1.0f, w.part, st);
+    hipLaunchKernelGGL(fold_kernel, dim3(flat_grid(n * r)), dim3(256), 0, st, w.part, sl, (int64_t)n * 2 * rp, (int)n,
+                       (int)r, (int)(2 * rp), (int64_t)rp, db);
+    // dA[j][k] = sum_m h[m][j] x[m][k]: the 2 rp rows of hst against rows k of Xt
+    sl = launch_nt_part(Seg{w.hst, w.xt, (int)mp, (int)mp}, 2 * rp, k, 1.0f, w.part, st);
+    hipLaunchKernelGGL(fold_kernel, dim3(flat_grid(r * k)), dim3(256), 0, st, w.part, sl, (int64_t)2 * rp * k, (int)r,
+                       (int)k, (int)k, (int64_t)rp * k, da);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
   }
   return hipSuccess;
 }
 
 hipError_t launch_zero_words(void* p, int64_t words, hipStream_t st) {
   if (words <= 0) return hipSuccess;
-  const unsigned grid = (unsigned)std::min<int64_t>((words + 255) / 256, 4096);
-  hipLaunchKernelGGL(slice_sum_kernel, dim3(grid), dim3(256), 0, st, nullptr, 0, words, static_cast<float*>(p));
+  hipLaunchKernelGGL(zero_kernel, dim3(flat_grid(words)), dim3(256), 0, st, static_cast<uint32_t*>(p), words);
   return hipGetLastError();
 }
 

@@ -92,16 +92,18 @@ hipError_t launch_fp4_linear(const uint16_t* x, int64_t m, int64_t n, int64_t k,
 
 // ---- LoRA backward -------------------------------------------------------------
 // Workspace regions of the backward (see backward_workspace): the transposed
-// dequantised weight, the transposed adapters, t and h = s dY B (fp32), h split
-// into bf16 hi | lo, and the fp32 slice partials of the adapter gradients.
+// dequantised weight, the transposed adapters and activations, t and h split
+// into bf16 hi | lo, and fp32 partial products.
 struct BackwardWs {
   uint16_t* wt = nullptr;   // [k][n] bf16, g S_b (dX only)
   uint16_t* bt = nullptr;   // [r][n] bf16
   uint16_t* at2 = nullptr;  // [k][2 rp] bf16, (A^T | A^T), rp = r rounded up to 8 (dX only)
-  float* t = nullptr;       // [m][r] s x A^T
-  float* h = nullptr;       // [m][r] s dY B
-  uint16_t* hs = nullptr;   // [m][2 rp] bf16 hi | lo of h (dX only)
-  float* part = nullptr;    // slice partials of dA / dB (when M is split)
+  uint16_t* dyt = nullptr;  // [n][mp] bf16, dY transposed (mp = m rounded up to 8; tokens past m zero)
+  uint16_t* xt = nullptr;   // [k][mp] bf16, x transposed
+  uint16_t* hs = nullptr;   // [m][2 rp] bf16 hi | lo of h = s dY B (dX only)
+  uint16_t* hst = nullptr;  // [2 rp][mp] bf16, hi | lo of h transposed
+  uint16_t* tst = nullptr;  // [2 rp][mp] bf16, hi | lo of t = s x A^T transposed
+  float* part = nullptr;    // fp32 partial products of the contraction-split launches
 };
 // Bytes of the backward workspace; with `w` and `base`, also its regions.
 size_t backward_workspace(int64_t m, int64_t n, int64_t k, int64_t r, bool want_dx, BackwardWs* w, void* base);

@@ -212,13 +212,14 @@ const char* fp4rl_fp4_linear_kernel_name(int64_t m, int64_t n, int64_t k, int64_
  *   lora_b bf16 [n][r], both NULL (r ignored) or both set.
  *   dx may be NULL (adapter gradients only, e.g. for a first layer); with no
  *   adapters dx is required.
- * Shapes: k a positive multiple of 16, n a multiple of 8, n and k below
+ * Shapes: k a positive multiple of 16, n a multiple of 8, m, n and k below
  *   2^22, 0 <= r <= 256. m == 0 or n == 0 writes zeros where a sum is empty.
  * Workspace: fp4rl_fp4_lora_linear_backward_workspace(m, n, k, r, dx != NULL)
  *   bytes, 256-byte aligned, caller-owned, no initial contents needed. It
- *   holds the transposed dequantised weight (2 k n bytes, with dx), the
- *   transposed adapters, t = s x A^T and h = s dy B, and the partial sums of
- *   the adapter gradients.
+ *   holds the transposed dequantised weight (2 k n bytes, with dx); with
+ *   adapters also dy and x transposed (2 (n + k) m bytes), the transposed
+ *   adapters, t = s x A^T and h = s dy B split into bf16 pairs, and fp32
+ *   partial products.
  * Errors: FP4RL_ERR_SHAPE, _NULL, _ALIGN, _VALUE (lora_scale not finite),
  *   _WORKSPACE; nothing is launched on error. Asynchronous on `stream`. */
 size_t fp4rl_fp4_lora_linear_backward_workspace(int64_t m, int64_t n, int64_t k, int64_t r, int32_t want_dx);
