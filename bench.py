@@ -65,6 +65,8 @@ def parse_args():
     p.add_argument("--cpu-seconds", type=float, default=15.0, help="target CPU time of the oracle sample")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--no-extras", action="store_true", help="skip prefill / quantiser / AQN extra timings")
+    p.add_argument("--backward-only", action="store_true",
+                   help="time only the LoRA backward of the 7B layer at 8192 tokens (--steps passes)")
     p.add_argument("--copy-calibration-mib", type=int, default=0,
                    help="first run a plain device-to-device copy of this many MiB three times (the reference "
                         "kernel that scales rocprofv3 FETCH_SIZE / WRITE_SIZE to bytes)")
@@ -363,6 +365,15 @@ def main():
         b = torch.randn((n, RANK), generator=g, device=dev).mul_(0.01).to(torch.bfloat16)
         lora[name] = (a, b)
     wnorm = torch.ones(hidden, dtype=torch.float32, device=dev)
+    if args.backward_only:
+        progress("LoRA backward timing")
+        gb = torch.Generator(device=dev)
+        gb.manual_seed(21)
+        xs = {k: torch.randn((PREFILL_M, k), generator=gb, device=dev).to(torch.bfloat16)
+              for k in sorted({k for _, k in shapes.values()})}
+        print(json.dumps({"lora_backward": run_backward(torch, fr, dev, shapes, layers[0], lora, xs, gb,
+                                                        max(1, args.steps))}))
+        return
 
     # activations and preallocated outputs / workspaces per token count
     bufs = {}
@@ -553,6 +564,7 @@ def run_extras(torch, fr, dev, shapes, layer, lora, fp32):
     flops = sum(linear_flops(PREFILL_M, n, k, RANK) for n, k in shapes.values())
     res["prefill"] = {"M": PREFILL_M, "tflops": round(flops / dt / 1e12, 2), "ms_per_layer": round(dt * 1e3, 3),
                       "frac_of_bf16_peak": round(flops / dt / 1e12 / BF16_PEAK_TFLOPS, 4)}
+    res["lora_backward"] = run_backward(torch, fr, dev, shapes, layer, lora, xs, g, reps)
     del xs, ys
 
     # quantiser on 14B shapes: one layer's five matrices, 0.02 t(3) weights with
@@ -622,6 +634,34 @@ def run_extras(torch, fr, dev, shapes, layer, lora, fp32):
     del x, y
     res["decode_32b"] = run_decode_32b(torch, fr, dev)
     return res
+
+
+def run_backward(torch, fr, dev, shapes, layer, lora, xs, g, reps):
+    """Backward through the frozen base (the training half of the step): the
+    layer's five linears and adapters, M = 8192 tokens, dY ~ N(0, 0.05^2);
+    dX, dA and dB of every linear per pass."""
+    dys = {name: (torch.randn((PREFILL_M, n), generator=g, device=dev) * 0.05).to(torch.bfloat16)
+           for name, (n, k) in shapes.items()}
+    bws = torch.empty(max(fr.fp4_lora_linear_backward_workspace_bytes(PREFILL_M, n, k, RANK)
+                          for n, k in shapes.values()), dtype=torch.uint8, device=dev)
+
+    def backward_pass():
+        for name, (n, k) in shapes.items():
+            a, b = lora[name]
+            fr.fp4_lora_linear_backward(dys[name], xs[k], layer[name], a, b, LORA_SCALE, workspace=bws)
+
+    backward_pass()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(reps):
+        backward_pass()
+    torch.cuda.synchronize()
+    dt = (time.perf_counter() - t0) / reps
+    # dX base 2MNK; LoRA: t and dA 2MrK each, h and dB 2MNr each, the dX LoRA term 2MrK
+    bflops = sum(2 * PREFILL_M * n * k + 2 * PREFILL_M * RANK * (3 * k + 2 * n) for n, k in shapes.values())
+    return {"M": PREFILL_M, "r": RANK, "tflops": round(bflops / dt / 1e12, 2), "ms_per_layer": round(dt * 1e3, 3),
+            "frac_of_bf16_peak": round(bflops / dt / 1e12 / BF16_PEAK_TFLOPS, 4),
+            "workspace_GB": round(bws.numel() / 1e9, 3)}
 
 
 def run_decode_32b(torch, fr, dev, layers=64, m=128, r=RANK_32B):

@@ -7,6 +7,7 @@
 #include <cstring>
 
 #include "fp4rl.h"
+#include "backward.hpp"
 #include "launch.hpp"
 
 namespace {

@@ -23,7 +23,7 @@
 #include <algorithm>
 
 #include "device.hpp"
-#include "launch.hpp"
+#include "backward.hpp"
 
 namespace fp4rl {
 namespace {
@@ -146,54 +146,56 @@ struct Seg {
   int slice = 0;                // contraction per blockIdx.y (a multiple of kGC; >= c: unsplit)
 };
 
-template <bool BF16OUT>
+template <bool BF16OUT, int WM>
 __global__ __launch_bounds__(256) void nt_gemm_kernel(Seg s1, Seg s2, int M, int Q, const float* __restrict__ alpha_dev,
                                                       float alpha, uint16_t* __restrict__ ybf, float* __restrict__ part) {
-  __shared__ __align__(16) uint16_t ls[2][kGT * kGPitch];
+  constexpr int TMM = kGT * WM;  // m rows of the workgroup tile (each wave: 64 WM x 64)
+  __shared__ __align__(16) uint16_t ls[2][TMM * kGPitch];
   __shared__ __align__(16) uint16_t rs[2][kGT * kGPitch];
-  const int MT = (M + kGT - 1) / kGT;
+  const int MT = (M + TMM - 1) / TMM;
   const int mt = blockIdx.x % MT, qt = blockIdx.x / MT;
-  const int m0 = kGT * mt, q0 = kGT * qt;
+  const int m0 = TMM * mt, q0 = kGT * qt;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int li = lane & 15, lg = lane >> 4;
   const int wm = wave & 1, wq = wave >> 1;
   const int prow = threadIdx.x >> 3, pcol = threadIdx.x & 7;  // piece: rows prow + 32 i, bf16 8 pcol .. + 7
 
-  f32x4 acc[4][4];
+  f32x4 acc[4][4 * WM];
 #pragma unroll
   for (int i = 0; i < 4; ++i)
 #pragma unroll
-    for (int j = 0; j < 4; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int j = 0; j < 4 * WM; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
 
   auto run = [&](const Seg& S, int c0, int clen) {
     const int NC = (clen + kGC - 1) / kGC;
-    const int lrows = min(kGT, M - m0), rrows = min(kGT, Q - q0);
+    const int lrows = min(TMM, M - m0), rrows = min(kGT, Q - q0);
     const __amdgpu_buffer_rsrc_t lrs = __builtin_amdgcn_make_buffer_rsrc(
         const_cast<uint16_t*>(S.l + (int64_t)m0 * S.ld + c0), 0, 2 * ((lrows - 1) * S.ld + clen), kRsrcWord3);
     const __amdgpu_buffer_rsrc_t rrs = __builtin_amdgcn_make_buffer_rsrc(
         const_cast<uint16_t*>(S.r + (int64_t)q0 * S.ld + c0), 0, 2 * ((rrows - 1) * S.ld + clen), kRsrcWord3);
-    uint32_t loff[4], roff[4];
+    uint32_t loff[4 * WM], roff[4];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      loff[i] = 2u * ((uint32_t)min(prow + 32 * i, lrows - 1) * (uint32_t)S.ld + 8 * pcol);
-      roff[i] = 2u * ((uint32_t)min(prow + 32 * i, rrows - 1) * (uint32_t)S.ld + 8 * pcol);
-    }
-    uint4 lv[4], rv[4];
+    for (int i = 0; i < 4 * WM; ++i) loff[i] = 2u * ((uint32_t)min(prow + 32 * i, lrows - 1) * (uint32_t)S.ld + 8 * pcol);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) roff[i] = 2u * ((uint32_t)min(prow + 32 * i, rrows - 1) * (uint32_t)S.ld + 8 * pcol);
+    uint4 lv[4 * WM], rv[4];
     auto load = [&](int ch) {
       ch = min(ch, NC - 1);
       const uint32_t out = kGC * ch + 8 * pcol < clen ? 0u : 0x80000000u;
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
+      for (int i = 0; i < 4 * WM; ++i)
         lv[i] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(lrs, (int)((loff[i] + 2u * kGC * ch) | out), 0, 0));
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
         rv[i] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rrs, (int)((roff[i] + 2u * kGC * ch) | out), 0, 0));
-      }
     };
     auto store = [&](int slab) {
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
+      for (int i = 0; i < 4 * WM; ++i)
         *reinterpret_cast<uint4*>(&ls[slab][(prow + 32 * i) * kGPitch + 8 * pcol]) = lv[i];
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
         *reinterpret_cast<uint4*>(&rs[slab][(prow + 32 * i) * kGPitch + 8 * pcol]) = rv[i];
-      }
     };
     __syncthreads();  // the slabs of a previous segment are no longer read
     load(0);
@@ -209,16 +211,17 @@ __global__ __launch_bounds__(256) void nt_gemm_kernel(Seg s1, Seg s2, int M, int
       const uint16_t* rsl = rs[ch & 1];
 #pragma unroll
       for (int st = 0; st < kGC / 32; ++st) {
-        bf16x8 a[4], b[4];
+        bf16x8 a[4], b[4 * WM];
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
+        for (int i = 0; i < 4; ++i)
           a[i] = as_bf16x8(*reinterpret_cast<const uint4*>(rsl + (64 * wq + 16 * i + li) * kGPitch + 32 * st + 8 * lg));
-          b[i] = as_bf16x8(*reinterpret_cast<const uint4*>(lsl + (64 * wm + 16 * i + li) * kGPitch + 32 * st + 8 * lg));
-        }
+#pragma unroll
+        for (int j = 0; j < 4 * WM; ++j)
+          b[j] = as_bf16x8(*reinterpret_cast<const uint4*>(lsl + (64 * WM * wm + 16 * j + li) * kGPitch + 32 * st + 8 * lg));
 #pragma unroll
         for (int i = 0; i < 4; ++i)
 #pragma unroll
-          for (int j = 0; j < 4; ++j) acc[i][j] = mfma16x16x32(a[i], b[j], acc[i][j]);
+          for (int j = 0; j < 4 * WM; ++j) acc[i][j] = mfma16x16x32(a[i], b[j], acc[i][j]);
       }
     }
   };
@@ -229,15 +232,15 @@ __global__ __launch_bounds__(256) void nt_gemm_kernel(Seg s1, Seg s2, int M, int
 #pragma unroll
   for (int i = 0; i < 4; ++i)
 #pragma unroll
-    for (int j = 0; j < 4; ++j) acc[i][j] *= al;
+    for (int j = 0; j < 4 * WM; ++j) acc[i][j] *= al;
   if (s2.c > 0) run(s2, 0, s2.c);  // only with an unsplit first segment
 
   float* pout = part ? part + (int64_t)blockIdx.y * M * Q : nullptr;
 #pragma unroll
   for (int i = 0; i < 4; ++i)
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const int m = m0 + 64 * wm + 16 * j + li, q = q0 + 64 * wq + 16 * i + 4 * lg;
+    for (int j = 0; j < 4 * WM; ++j) {
+      const int m = m0 + 64 * WM * wm + 16 * j + li, q = q0 + 64 * wq + 16 * i + 4 * lg;
       if (m >= M) continue;
       const f32x4 v = acc[i][j];
       if constexpr (BF16OUT) {
@@ -329,8 +332,9 @@ int64_t nt_tiles(int64_t m, int64_t q) { return ((m + kGT - 1) / kGT) * ((q + kG
 
 hipError_t launch_nt_bf16(Seg s1, Seg s2, int64_t m, int64_t q, const float* alpha_dev, uint16_t* y, hipStream_t st) {
   s1.slice = s1.c;
-  hipLaunchKernelGGL(nt_gemm_kernel<true>, dim3((unsigned)nt_tiles(m, q)), dim3(256), 0, st, s1, s2, (int)m, (int)q,
-                     alpha_dev, 0.0f, y, nullptr);
+  // a 256 x 128 tile (WM = 2: 128 x 64 per wave, one workgroup per CU) measured slower than 128 x 128
+  hipLaunchKernelGGL((nt_gemm_kernel<true, 1>), dim3((unsigned)nt_tiles(m, q)), dim3(256), 0, st, s1, s2, (int)m,
+                     (int)q, alpha_dev, 0.0f, y, nullptr);
   return hipGetLastError();
 }
 
@@ -339,7 +343,7 @@ int launch_nt_part(Seg s1, int64_t m, int64_t q, float alpha, float* part, hipSt
   const int64_t tiles = nt_tiles(m, q);
   s1.slice = nt_slice_len(tiles, s1.c);
   const int slices = nt_slices(tiles, s1.c);
-  hipLaunchKernelGGL(nt_gemm_kernel<false>, dim3((unsigned)tiles, (unsigned)slices), dim3(256), 0, st, s1, Seg{},
+  hipLaunchKernelGGL((nt_gemm_kernel<false, 1>), dim3((unsigned)tiles, (unsigned)slices), dim3(256), 0, st, s1, Seg{},
                      (int)m, (int)q, nullptr, alpha, nullptr, part);
   return slices;
 }
