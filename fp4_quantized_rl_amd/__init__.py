@@ -13,6 +13,7 @@ Operations (names follow the C ABI):
   fp4_lora_linear(x, wq, lora_a, lora_b, s) -> y = x deq(Wq)^T + s (x A^T) B^T  (bf16)
   lora_down / fp4_linear_lora_up            -> the two halves of fp4_lora_linear
   fp4_lora_linear_backward(dy, x, wq, A, B, s) -> (dx bf16, dA fp32, dB fp32), the base frozen
+  fp8_quantize(w) / fp8_lora_linear(x, w8, A, B, s) -> FP8 (E4M3, per-row scale) rollout weights, W8A16
   aqn_sigma(s0, s1, k, K)                   -> exponential AQN noise level
   aqn_rmsnorm(x, w, sigma, seed, step, ...) -> RMSNorm with W_noise = w + sigma z
   philox_words(seed, step, norm_id, n)      -> raw Philox4x32-10 output blocks
@@ -26,6 +27,7 @@ from dataclasses import dataclass
 __all__ = [
     "LIB_PATH", "Fp4rlError", "load_library", "NVFP4Weight", "nvfp4_empty", "nvfp4_quantize", "nvfp4_to_tiled",
     "fp4_lora_linear", "fp4_lora_linear_backward", "fp4_lora_linear_backward_workspace_bytes",
+    "FP8Weight", "fp8_quantize", "fp8_lora_linear",
     "lora_down", "fp4_linear_lora_up", "fp4_linear_kernel_name", "linear_workspace",
     "fp4_lora_linear_workspace_bytes", "fp4_linear_lora_up_workspace_bytes", "aqn_sigma", "aqn_rmsnorm", "philox_words",
     "EXPORTED_SYMBOLS",
@@ -62,6 +64,10 @@ _SIGNATURES = {
     "fp4rl_fp4_linear_lora_up": (_STATUS, [_P, _I64, _I64, _I64, _P, _P, _P, _P, _P, _I64, _P, _P, _c.c_size_t,
                                            _P]),
     "fp4rl_fp4_linear_kernel_name": (_c.c_char_p, [_I64, _I64, _I64, _I64]),
+    "fp4rl_fp8_quantize": (_STATUS, [_P, _c.c_int32, _I64, _I64, _P, _P, _P]),
+    "fp4rl_fp8_lora_linear_workspace": (_c.c_size_t, [_I64, _I64, _I64, _I64]),
+    "fp4rl_fp8_lora_linear": (_STATUS, [_P, _I64, _I64, _I64, _P, _P, _P, _P, _I64, _c.c_float, _P, _P, _c.c_size_t,
+                                        _P]),
     "fp4rl_fp4_lora_linear_backward_workspace": (_c.c_size_t, [_I64, _I64, _I64, _I64, _c.c_int32]),
     "fp4rl_fp4_lora_linear_backward": (_STATUS, [_P, _P, _I64, _I64, _I64, _P, _P, _P, _P, _P, _I64, _c.c_float,
                                                  _P, _P, _P, _P, _c.c_size_t, _P]),
@@ -262,6 +268,56 @@ def fp4_lora_linear(x, wq: NVFP4Weight, lora_a=None, lora_b=None, lora_scale: fl
                                          0 if workspace is None else workspace.numel(),
                                          _stream(x.device)),
                "fp4_lora_linear")
+    return out
+
+
+@dataclass
+class FP8Weight:
+    """E4M3 codes [n, k] (uint8) and fp32 row scales [n] on the device."""
+    codes: object
+    scales: object
+
+
+def fp8_quantize(w) -> FP8Weight:
+    """w fp32 or bf16 [n, k] -> FP8Weight (nearest E4M3 of w / s_n, s_n = amax_n / 448)."""
+    torch = _torch()
+    _dev_tensor(w, "w", (torch.float32, torch.bfloat16), 2)
+    n, k = w.shape
+    codes = torch.empty((n, k), dtype=torch.uint8, device=w.device)
+    scales = torch.empty((n,), dtype=torch.float32, device=w.device)
+    with torch.cuda.device(w.device):
+        _check(load_library().fp4rl_fp8_quantize(_ptr(w), BF16 if w.dtype == torch.bfloat16 else F32, n, k,
+                                                 _ptr(codes), _ptr(scales), _stream(w.device)), "fp8_quantize")
+    return FP8Weight(codes, scales)
+
+
+def fp8_lora_linear(x, w8: FP8Weight, lora_a=None, lora_b=None, lora_scale: float = 0.0, out=None, workspace=None):
+    """y = bf16(x deq(W8)^T + lora_scale (x A^T) B^T); x bf16 [m, k]."""
+    torch = _torch()
+    _dev_tensor(x, "x", (torch.bfloat16,), 2)
+    _dev_tensor(w8.codes, "codes", (torch.uint8,), 2)
+    _dev_tensor(w8.scales, "scales", (torch.float32,), 1)
+    m, k = x.shape
+    n = w8.codes.shape[0]
+    if w8.codes.shape[1] != k or w8.scales.shape[0] != n:
+        raise ValueError("x [m, k], codes [n, k] and scales [n] do not match")
+    r = 0
+    if lora_a is not None or lora_b is not None:
+        _dev_tensor(lora_a, "lora_a", (torch.bfloat16,), 2)
+        _dev_tensor(lora_b, "lora_b", (torch.bfloat16,), 2)
+        r = lora_a.shape[0]
+        if lora_a.shape != (r, k) or lora_b.shape != (n, r):
+            raise ValueError("LoRA shapes must be A [r, k] and B [n, r]")
+    if out is None:
+        out = torch.empty((m, n), dtype=torch.bfloat16, device=x.device)
+    lib = load_library()
+    need = lib.fp4rl_fp8_lora_linear_workspace(m, n, k, r)
+    if workspace is None:
+        workspace = torch.empty(max(need, 256), dtype=torch.uint8, device=x.device)
+    with torch.cuda.device(x.device):
+        _check(lib.fp4rl_fp8_lora_linear(_ptr(x), m, n, k, _ptr(w8.codes), _ptr(w8.scales), _ptr(lora_a),
+                                         _ptr(lora_b), r, float(lora_scale), _ptr(out), _ptr(workspace),
+                                         workspace.numel(), _stream(x.device)), "fp8_lora_linear")
     return out
 
 

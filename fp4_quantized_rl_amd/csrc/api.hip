@@ -8,6 +8,7 @@
 
 #include "fp4rl.h"
 #include "backward.hpp"
+#include "fp8.hpp"
 #include "launch.hpp"
 
 namespace {
@@ -406,6 +407,65 @@ fp4rl_status fp4rl_fp4_lora_linear_backward(const uint16_t* dy, const uint16_t* 
   return launched(fp4rl::launch_lora_backward(dy, x, m, n, k, codes, scales, tensor_scale, r > 0 ? lora_a : nullptr,
                                               r > 0 ? lora_b : nullptr, r, lora_scale, dx, grad_a, grad_b, w, stream),
                   "fp4_lora_linear_backward");
+}
+
+// --------------------------------------------------------------------- FP8 --
+
+fp4rl_status fp4rl_fp8_quantize(const void* w, int32_t w_dtype, int64_t n, int64_t k, uint8_t* codes,
+                                float* row_scales, fp4rl_stream stream) {
+  FP4RL_REQUIRE(n >= 0 && k > 0 && k % 16 == 0, FP4RL_ERR_SHAPE, "need n >= 0 and k a positive multiple of 16 "
+                "(n=%lld k=%lld)", (long long)n, (long long)k);
+  FP4RL_REQUIRE(n < kMaxDim && k < ((int64_t)1 << 22), FP4RL_ERR_SHAPE, "n below 2^31 and k below 2^22 required");
+  FP4RL_REQUIRE(w_dtype == FP4RL_F32 || w_dtype == FP4RL_BF16, FP4RL_ERR_DTYPE, "w_dtype=%d", (int)w_dtype);
+  if (n == 0) return ok();
+  FP4RL_REQUIRE(w && codes && row_scales, FP4RL_ERR_NULL, "w, codes and row_scales must be non-NULL");
+  FP4RL_REQUIRE(aligned(w, 16) && aligned(codes, 16) && aligned(row_scales, 4), FP4RL_ERR_ALIGN,
+                "w and codes must be 16-byte aligned, row_scales 4-byte aligned");
+  FP4RL_CHECK(check_device());
+  return launched(fp4rl::launch_fp8_quantize(w, w_dtype == FP4RL_BF16, n, k, codes, row_scales, stream),
+                  "fp8_quantize");
+}
+
+static fp4rl_status check_fp8_shape(int64_t m, int64_t n, int64_t k, int64_t r) {
+  FP4RL_REQUIRE(m >= 0 && n >= 0 && r >= 0 && k > 0 && k % 16 == 0, FP4RL_ERR_SHAPE,
+                "bad shape (m=%lld n=%lld k=%lld r=%lld)", (long long)m, (long long)n, (long long)k, (long long)r);
+  FP4RL_REQUIRE(m < ((int64_t)1 << 22) && n < ((int64_t)1 << 22) && k < ((int64_t)1 << 22), FP4RL_ERR_SHAPE,
+                "m, n and k must be below 2^22");
+  FP4RL_REQUIRE(r <= fp4rl::kMaxRank, FP4RL_ERR_SHAPE, "rank r=%lld exceeds %lld", (long long)r,
+                (long long)fp4rl::kMaxRank);
+  return FP4RL_OK;
+}
+
+size_t fp4rl_fp8_lora_linear_workspace(int64_t m, int64_t n, int64_t k, int64_t r) {
+  if (check_fp8_shape(m, n, k, r) != FP4RL_OK || m == 0 || n == 0) return 0;
+  return fp4rl::fp8_linear_workspace(m, n, k, r, nullptr, nullptr);
+}
+
+fp4rl_status fp4rl_fp8_lora_linear(const uint16_t* x, int64_t m, int64_t n, int64_t k, const uint8_t* codes,
+                                   const float* row_scales, const uint16_t* lora_a, const uint16_t* lora_b, int64_t r,
+                                   float lora_scale, uint16_t* y, void* workspace, size_t workspace_bytes,
+                                   fp4rl_stream stream) {
+  FP4RL_CHECK(check_fp8_shape(m, n, k, r));
+  FP4RL_REQUIRE(std::isfinite(lora_scale), FP4RL_ERR_VALUE, "lora_scale is not finite");
+  FP4RL_REQUIRE((lora_a == nullptr) == (lora_b == nullptr), FP4RL_ERR_NULL,
+                "lora_a and lora_b must both be NULL or both be set");
+  if (lora_a == nullptr) r = 0;
+  if (m == 0 || n == 0) return ok();
+  FP4RL_REQUIRE(x && codes && row_scales && y, FP4RL_ERR_NULL, "x, codes, row_scales and y must be non-NULL");
+  FP4RL_REQUIRE(aligned(x, 16) && aligned(codes, 16) && aligned(y, 16) && aligned(row_scales, 4), FP4RL_ERR_ALIGN,
+                "x, codes and y must be 16-byte aligned, row_scales 4-byte aligned");
+  if (r > 0)
+    FP4RL_REQUIRE(aligned(lora_a, 16) && aligned(lora_b, 16), FP4RL_ERR_ALIGN, "lora_a and lora_b must be 16-byte aligned");
+  const size_t need = fp4rl::fp8_linear_workspace(m, n, k, r, nullptr, nullptr);
+  FP4RL_REQUIRE(workspace != nullptr && workspace_bytes >= need, FP4RL_ERR_WORKSPACE, "workspace %zu < %zu bytes",
+                workspace_bytes, need);
+  FP4RL_REQUIRE(aligned(workspace, 256), FP4RL_ERR_ALIGN, "workspace must be 256-byte aligned");
+  FP4RL_CHECK(check_device());
+  fp4rl::Fp8Ws w;
+  fp4rl::fp8_linear_workspace(m, n, k, r, &w, workspace);
+  return launched(fp4rl::launch_fp8_linear(x, m, n, k, codes, row_scales, r > 0 ? lora_a : nullptr,
+                                           r > 0 ? lora_b : nullptr, r, lora_scale, y, w, stream),
+                  "fp8_lora_linear");
 }
 
 // --------------------------------------------------------------------- AQN --

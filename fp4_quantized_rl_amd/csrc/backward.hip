@@ -22,13 +22,13 @@
 //      workgroups); fold_kernel adds the slices and the hi and lo halves.
 #include <algorithm>
 
-#include "device.hpp"
 #include "backward.hpp"
+#include "device.hpp"
+#include "gemm_nt.hpp"
 
 namespace fp4rl {
 namespace {
 
-constexpr int kRsrcWord3 = 0x00020000;
 
 // ---------------------------------------------------------------------------
 // 1. Transposed dequantisation. A workgroup takes 4 row tiles (64 features)
@@ -122,150 +122,6 @@ __global__ __launch_bounds__(256) void transpose16_kernel(const uint16_t* __rest
 }
 
 // ---------------------------------------------------------------------------
-// 3. C[m][q] = alpha sum_c L1[m][c] R1[q][c] (+ sum_c L2[m][c] R2[q][c]), bf16
-// operands with rows contiguous along c (row strides and lengths multiples of
-// 8), fp32 accumulation. A workgroup computes a 128 (m) x 128 (q) tile with 4
-// waves of 64 x 64 (4 x 4 MFMA tiles each) over one slice of the
-// contraction (blockIdx.y; one slice unless the launch splits it).
-// Contraction chunks of 64 are loaded to registers one chunk ahead and
-// written to one of two LDS slabs per operand (rows padded to 144 B:
-// conflict-free 16-byte fragment reads); one barrier per chunk. Rows past M
-// or Q are clamped (loaded, never stored); pieces past the slice read as
-// zero (their offsets fall outside the buffer descriptor's range).
-// A lane's result holds q = 4 g + v of MFMA column li = m, so stores are
-// 4 consecutive outputs of one row. Outputs: bf16 y [M][Q], or fp32
-// part[slice][M][Q].
-// ---------------------------------------------------------------------------
-constexpr int kGT = 128, kGC = 64, kGPitch = kGC + 8;
-
-struct Seg {
-  const uint16_t* l = nullptr;  // [M][ld]
-  const uint16_t* r = nullptr;  // [Q][ld]
-  int ld = 0;                   // row stride of both operands (elements)
-  int c = 0;                    // contraction length (0: no segment)
-  int slice = 0;                // contraction per blockIdx.y (a multiple of kGC; >= c: unsplit)
-};
-
-template <bool BF16OUT, int WM>
-__global__ __launch_bounds__(256) void nt_gemm_kernel(Seg s1, Seg s2, int M, int Q, const float* __restrict__ alpha_dev,
-                                                      float alpha, uint16_t* __restrict__ ybf, float* __restrict__ part) {
-  constexpr int TMM = kGT * WM;  // m rows of the workgroup tile (each wave: 64 WM x 64)
-  __shared__ __align__(16) uint16_t ls[2][TMM * kGPitch];
-  __shared__ __align__(16) uint16_t rs[2][kGT * kGPitch];
-  const int MT = (M + TMM - 1) / TMM;
-  const int mt = blockIdx.x % MT, qt = blockIdx.x / MT;
-  const int m0 = TMM * mt, q0 = kGT * qt;
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int li = lane & 15, lg = lane >> 4;
-  const int wm = wave & 1, wq = wave >> 1;
-  const int prow = threadIdx.x >> 3, pcol = threadIdx.x & 7;  // piece: rows prow + 32 i, bf16 8 pcol .. + 7
-
-  f32x4 acc[4][4 * WM];
-#pragma unroll
-  for (int i = 0; i < 4; ++i)
-#pragma unroll
-    for (int j = 0; j < 4 * WM; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
-
-  auto run = [&](const Seg& S, int c0, int clen) {
-    const int NC = (clen + kGC - 1) / kGC;
-    const int lrows = min(TMM, M - m0), rrows = min(kGT, Q - q0);
-    const __amdgpu_buffer_rsrc_t lrs = __builtin_amdgcn_make_buffer_rsrc(
-        const_cast<uint16_t*>(S.l + (int64_t)m0 * S.ld + c0), 0, 2 * ((lrows - 1) * S.ld + clen), kRsrcWord3);
-    const __amdgpu_buffer_rsrc_t rrs = __builtin_amdgcn_make_buffer_rsrc(
-        const_cast<uint16_t*>(S.r + (int64_t)q0 * S.ld + c0), 0, 2 * ((rrows - 1) * S.ld + clen), kRsrcWord3);
-    uint32_t loff[4 * WM], roff[4];
-#pragma unroll
-    for (int i = 0; i < 4 * WM; ++i) loff[i] = 2u * ((uint32_t)min(prow + 32 * i, lrows - 1) * (uint32_t)S.ld + 8 * pcol);
-#pragma unroll
-    for (int i = 0; i < 4; ++i) roff[i] = 2u * ((uint32_t)min(prow + 32 * i, rrows - 1) * (uint32_t)S.ld + 8 * pcol);
-    uint4 lv[4 * WM], rv[4];
-    auto load = [&](int ch) {
-      ch = min(ch, NC - 1);
-      const uint32_t out = kGC * ch + 8 * pcol < clen ? 0u : 0x80000000u;
-#pragma unroll
-      for (int i = 0; i < 4 * WM; ++i)
-        lv[i] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(lrs, (int)((loff[i] + 2u * kGC * ch) | out), 0, 0));
-#pragma unroll
-      for (int i = 0; i < 4; ++i)
-        rv[i] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rrs, (int)((roff[i] + 2u * kGC * ch) | out), 0, 0));
-    };
-    auto store = [&](int slab) {
-#pragma unroll
-      for (int i = 0; i < 4 * WM; ++i)
-        *reinterpret_cast<uint4*>(&ls[slab][(prow + 32 * i) * kGPitch + 8 * pcol]) = lv[i];
-#pragma unroll
-      for (int i = 0; i < 4; ++i)
-        *reinterpret_cast<uint4*>(&rs[slab][(prow + 32 * i) * kGPitch + 8 * pcol]) = rv[i];
-    };
-    __syncthreads();  // the slabs of a previous segment are no longer read
-    load(0);
-    store(0);
-    load(1);
-    for (int ch = 0; ch < NC; ++ch) {
-      __syncthreads();  // slab ch % 2 is complete; the other is no longer read
-      if (ch + 1 < NC) {
-        store((ch + 1) & 1);
-        load(ch + 2);
-      }
-      const uint16_t* lsl = ls[ch & 1];
-      const uint16_t* rsl = rs[ch & 1];
-#pragma unroll
-      for (int st = 0; st < kGC / 32; ++st) {
-        bf16x8 a[4], b[4 * WM];
-#pragma unroll
-        for (int i = 0; i < 4; ++i)
-          a[i] = as_bf16x8(*reinterpret_cast<const uint4*>(rsl + (64 * wq + 16 * i + li) * kGPitch + 32 * st + 8 * lg));
-#pragma unroll
-        for (int j = 0; j < 4 * WM; ++j)
-          b[j] = as_bf16x8(*reinterpret_cast<const uint4*>(lsl + (64 * WM * wm + 16 * j + li) * kGPitch + 32 * st + 8 * lg));
-#pragma unroll
-        for (int i = 0; i < 4; ++i)
-#pragma unroll
-          for (int j = 0; j < 4 * WM; ++j) acc[i][j] = mfma16x16x32(a[i], b[j], acc[i][j]);
-      }
-    }
-  };
-
-  const int c0 = blockIdx.y * s1.slice;
-  run(s1, c0, min(s1.slice, s1.c - c0));
-  const float al = alpha_dev ? *alpha_dev : alpha;
-#pragma unroll
-  for (int i = 0; i < 4; ++i)
-#pragma unroll
-    for (int j = 0; j < 4 * WM; ++j) acc[i][j] *= al;
-  if (s2.c > 0) run(s2, 0, s2.c);  // only with an unsplit first segment
-
-  float* pout = part ? part + (int64_t)blockIdx.y * M * Q : nullptr;
-#pragma unroll
-  for (int i = 0; i < 4; ++i)
-#pragma unroll
-    for (int j = 0; j < 4 * WM; ++j) {
-      const int m = m0 + 64 * WM * wm + 16 * j + li, q = q0 + 64 * wq + 16 * i + 4 * lg;
-      if (m >= M) continue;
-      const f32x4 v = acc[i][j];
-      if constexpr (BF16OUT) {
-        uint16_t* yp = ybf + (int64_t)m * Q + q;
-        if (q + 3 < Q) {  // Q % 4 == 0 here (Q = K, a multiple of 16)
-          *reinterpret_cast<uint2*>(yp) = make_uint2(pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3]));
-        } else {
-#pragma unroll
-          for (int e = 0; e < 4; ++e)
-            if (q + e < Q) yp[e] = (uint16_t)f32_to_bf16(v[e]);
-        }
-      } else {
-        float* yp = pout + (int64_t)m * Q + q;
-        if (q + 3 < Q && (Q & 3) == 0) {
-          *reinterpret_cast<float4*>(yp) = make_float4(v[0], v[1], v[2], v[3]);
-        } else {
-#pragma unroll
-          for (int e = 0; e < 4; ++e)
-            if (q + e < Q) yp[e] = v[e];
-        }
-      }
-    }
-}
-
-// ---------------------------------------------------------------------------
 // 4. Finishing kernels (slices summed in order).
 // rank_split_kernel: v = sum_s part[s][m][j] (m < M, j < r) split into bf16
 //   hi + lo; written as sp [M][2 rp] (hi | lo) and/or spt [2 rp][mp]
@@ -315,26 +171,11 @@ __global__ __launch_bounds__(256) void zero_kernel(uint32_t* __restrict__ p, int
 
 size_t al256(size_t v) { return (v + 255) / 256 * 256; }
 
-// Contraction slices for a launch of `tiles` output tiles: enough workgroups
-// to fill the chip (>= 512), each slice at least 512 long (a multiple of the
-// 64-wide chunk).
-int nt_slice_len(int64_t tiles, int64_t c) {
-  int64_t s = (512 + tiles - 1) / tiles;
-  s = std::max<int64_t>(1, std::min<int64_t>(s, c / 512));
-  const int64_t len = ((c + s - 1) / s + kGC - 1) / kGC * kGC;
-  return (int)len;
-}
-int nt_slices(int64_t tiles, int64_t c) {
-  const int64_t len = nt_slice_len(tiles, c);
-  return (int)((c + len - 1) / len);
-}
-int64_t nt_tiles(int64_t m, int64_t q) { return ((m + kGT - 1) / kGT) * ((q + kGT - 1) / kGT); }
-
 hipError_t launch_nt_bf16(Seg s1, Seg s2, int64_t m, int64_t q, const float* alpha_dev, uint16_t* y, hipStream_t st) {
   s1.slice = s1.c;
   // a 256 x 128 tile (WM = 2: 128 x 64 per wave, one workgroup per CU) measured slower than 128 x 128
   hipLaunchKernelGGL((nt_gemm_kernel<true, 1>), dim3((unsigned)nt_tiles(m, q)), dim3(256), 0, st, s1, s2, (int)m,
-                     (int)q, alpha_dev, 0.0f, y, nullptr);
+                     (int)q, alpha_dev, 0.0f, nullptr, y, nullptr);
   return hipGetLastError();
 }
 
@@ -344,7 +185,7 @@ int launch_nt_part(Seg s1, int64_t m, int64_t q, float alpha, float* part, hipSt
   s1.slice = nt_slice_len(tiles, s1.c);
   const int slices = nt_slices(tiles, s1.c);
   hipLaunchKernelGGL((nt_gemm_kernel<false, 1>), dim3((unsigned)tiles, (unsigned)slices), dim3(256), 0, st, s1, Seg{},
-                     (int)m, (int)q, nullptr, alpha, nullptr, part);
+                     (int)m, (int)q, nullptr, alpha, nullptr, nullptr, part);
   return slices;
 }
 

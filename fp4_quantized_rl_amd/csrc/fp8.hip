@@ -1,0 +1,222 @@
+// FP8 (OCP E4M3) rollout weights and their W8A16 linear with LoRA (gfx950).
+//
+// Low-precision rollout engines commonly run the policy in FP8 while the
+// trainer keeps BF16 (gist.science summary of adaptive importance sampling
+// for quantized RL, "Problem definition"); FP8 halves the rollout model's
+// memory ("Experimental results"). Format: one E4M3 byte per weight, one
+// fp32 scale per output row, s_n = amax_n / 448; the code of w is the
+// nearest E4M3 value to the fp32 quotient w / s_n (ties to even, saturating
+// at 448, no -0). The linear is
+//   y = bf16(sum_k x[m,k] e4m3(code[n,k]) s_n + s (x A^T)[m] . B[n]).
+//
+// Kernels:
+//   fp8_quantize_kernel: one workgroup per row: the row's amax (exact max of
+//     |w| bit patterns), s_n, then the codes, 16 bytes per store.
+//   nt_gemm_kernel<false, 1, true>: x (bf16) against the E4M3 rows, converted
+//     to bf16 exactly on the way into LDS (v_cvt_pk_f32_fp8), fp32
+//     accumulation scaled per row by s_n; the contraction is split over
+//     workgroups when there are few output tiles (decode), partials fp32.
+//   t = s x A^T from the same GEMM kernel on A (bf16), its slices summed by
+//   slice_sum_kernel. With enough output tiles (prefill) the linear writes
+//   bf16 y in one launch, the LoRA term accumulated as a second contraction
+//   segment (t as bf16 hi | lo against B twice: lora_operands_kernel);
+//   split (decode), fp8_finish_kernel makes y = bf16(sum of slices + t . B[n]).
+#include <algorithm>
+
+#include "device.hpp"
+#include "fp8.hpp"
+#include "gemm_nt.hpp"
+
+namespace fp4rl {
+namespace {
+
+// Nearest finite E4M3 magnitude byte to a non-negative fp32 value, ties to
+// even (round to 3 mantissa bits; subnormals are multiples of 2^-9).
+__device__ __forceinline__ uint32_t e4m3_rne(float a) {
+  if (!(a < 448.0f)) return 0x7Eu;  // saturate (a >= 448, or rounding up past 448 below)
+  if (a < 0x1p-6f) return (uint32_t)__builtin_rintf(a * 512.0f);  // subnormal: m 2^-9, m = 8 is 2^-6 (byte 0x08)
+  uint32_t u = __float_as_uint(a);
+  u += 0x7FFFFu + ((u >> 20) & 1u);  // round the 23-bit mantissa to 3 bits, ties to even
+  const uint32_t e = (u >> 23) - 120u, m = (u >> 20) & 7u;  // E4M3 exponent field: unbiased + 7
+  return min((e << 3) | m, 0x7Eu);
+}
+
+template <bool BF16>
+__device__ __forceinline__ float4 load4(const void* w, int64_t i) {
+  if constexpr (BF16) {
+    const uint2 v = *reinterpret_cast<const uint2*>(static_cast<const uint16_t*>(w) + i);
+    return make_float4(bf16_lo(v.x), bf16_hi(v.x), bf16_lo(v.y), bf16_hi(v.y));
+  } else {
+    return *reinterpret_cast<const float4*>(static_cast<const float*>(w) + i);
+  }
+}
+
+template <bool BF16>
+__global__ __launch_bounds__(256) void fp8_quantize_kernel(const void* __restrict__ w, int K,
+                                                           uint8_t* __restrict__ codes, float* __restrict__ scales) {
+  __shared__ uint32_t red[4];
+  const int64_t row = blockIdx.x;
+  const int64_t base = row * K;
+  uint32_t mx = 0;
+  for (int k = 4 * threadIdx.x; k < K; k += 1024) {
+    const float4 v = load4<BF16>(w, base + k);
+    mx = max(mx, max(max(__float_as_uint(v.x) & 0x7FFFFFFFu, __float_as_uint(v.y) & 0x7FFFFFFFu),
+                     max(__float_as_uint(v.z) & 0x7FFFFFFFu, __float_as_uint(v.w) & 0x7FFFFFFFu)));
+  }
+  mx = wave_max_u32(mx);
+  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = mx;
+  __syncthreads();
+  mx = max(max(red[0], red[1]), max(red[2], red[3]));
+  const float s = __uint_as_float(mx) / 448.0f;  // correctly rounded division
+  if (threadIdx.x == 0) scales[row] = s;
+  // 16 elements per thread and step: four float4 loads, one 16-byte store
+  for (int k = 16 * threadIdx.x; k < K; k += 4096) {
+    uint32_t o[4];
+#pragma unroll
+    for (int d = 0; d < 4; ++d) {
+      const float4 v = load4<BF16>(w, base + k + 4 * d);
+      const float f[4] = {v.x, v.y, v.z, v.w};
+      uint32_t word = 0;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const float q = s > 0.0f ? f[e] / s : 0.0f;
+        uint32_t c = e4m3_rne(fabsf(q));
+        if (q < 0.0f && c != 0u) c |= 0x80u;
+        word |= c << (8 * e);
+      }
+      o[d] = word;
+    }
+    *reinterpret_cast<uint4*>(codes + base + k) = make_uint4(o[0], o[1], o[2], o[3]);
+  }
+}
+
+__global__ __launch_bounds__(256) void slice_sum_kernel(const float* __restrict__ part, int slices, int64_t count,
+                                                        float* __restrict__ out) {
+  for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < count; i += (int64_t)gridDim.x * 256) {
+    float v = 0.0f;
+    for (int s = 0; s < slices; ++s) v += part[(int64_t)s * count + i];
+    out[i] = v;
+  }
+}
+
+// y[m][n] = bf16(sum_s part[s][m][n] + sum_j t[m][j] B[n][j]); slices and
+// ranks in order
+__global__ __launch_bounds__(256) void fp8_finish_kernel(const float* __restrict__ part, int slices, int M, int N,
+                                                         const float* __restrict__ t, const uint16_t* __restrict__ b,
+                                                         int r, uint16_t* __restrict__ y) {
+  const int64_t count = (int64_t)M * N;
+  for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < count; i += (int64_t)gridDim.x * 256) {
+    float v = 0.0f;
+    for (int s = 0; s < slices; ++s) v += part[(int64_t)s * count + i];
+    if (r > 0) {
+      const int m = (int)(i / N), n = (int)(i - (int64_t)m * N);
+      float l = 0.0f;
+      for (int j = 0; j < r; ++j) l = fmaf(t[(int64_t)m * r + j], bf16_lo(b[(int64_t)n * r + j]), l);
+      v += l;
+    }
+    y[i] = (uint16_t)f32_to_bf16(v);
+  }
+}
+
+// ts[m][0..2rp) = bf16 hi | lo of t[m][0..r) (zero past r); b2[n][0..2rp) =
+// (B[n] | B[n]) (zero past r): the LoRA term as a second contraction segment
+__global__ __launch_bounds__(256) void lora_operands_kernel(const float* __restrict__ t, const uint16_t* __restrict__ b,
+                                                            int M, int N, int r, int rp, uint16_t* __restrict__ ts,
+                                                            uint16_t* __restrict__ b2) {
+  const int64_t nt = (int64_t)M * rp, count = nt + (int64_t)N * rp;
+  for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < count; i += (int64_t)gridDim.x * 256) {
+    if (i < nt) {
+      const int m = (int)(i / rp), j = (int)(i - (int64_t)m * rp);
+      const float v = j < r ? t[(int64_t)m * r + j] : 0.0f;
+      const uint32_t hb = f32_to_bf16(v);
+      ts[(int64_t)m * 2 * rp + j] = (uint16_t)hb;
+      ts[(int64_t)m * 2 * rp + rp + j] = (uint16_t)f32_to_bf16(v - __uint_as_float(hb << 16));
+    } else {
+      const int64_t e = i - nt;
+      const int n = (int)(e / rp), j = (int)(e - (int64_t)n * rp);
+      const uint16_t v = j < r ? b[(int64_t)n * r + j] : (uint16_t)0;
+      b2[(int64_t)n * 2 * rp + j] = v;
+      b2[(int64_t)n * 2 * rp + rp + j] = v;
+    }
+  }
+}
+
+unsigned flat_grid8(int64_t count) {
+  return (unsigned)std::max<int64_t>(1, std::min<int64_t>((count + 255) / 256, 8192));
+}
+
+size_t al256(size_t v) { return (v + 255) / 256 * 256; }
+
+}  // namespace
+
+hipError_t launch_fp8_quantize(const void* w, bool w_bf16, int64_t n, int64_t k, uint8_t* codes, float* scales,
+                               hipStream_t st) {
+  if (w_bf16)
+    hipLaunchKernelGGL(fp8_quantize_kernel<true>, dim3((unsigned)n), dim3(256), 0, st, w, (int)k, codes, scales);
+  else
+    hipLaunchKernelGGL(fp8_quantize_kernel<false>, dim3((unsigned)n), dim3(256), 0, st, w, (int)k, codes, scales);
+  return hipGetLastError();
+}
+
+// Workspace: y partials [S][m][n] fp32 when the contraction is split; with
+// adapters t partials [St][m][r], t [m][r] fp32 and, unsplit, the bf16 LoRA
+// segment operands ts [m][2 rp], b2 [n][2 rp].
+size_t fp8_linear_workspace(int64_t m, int64_t n, int64_t k, int64_t r, Fp8Ws* w, void* base) {
+  size_t off = 0;
+  auto take = [&](size_t bytes) {
+    const size_t o = off;
+    off += al256(bytes);
+    return base ? reinterpret_cast<float*>(static_cast<uint8_t*>(base) + o) : nullptr;
+  };
+  Fp8Ws v{};
+  const int sl = nt_slices(nt_tiles(m, n), k);
+  const int64_t rp = (r + 7) / 8 * 8;
+  if (sl > 1) v.ypart = take((size_t)sl * m * n * 4);
+  if (r > 0) {
+    v.tpart = take((size_t)nt_slices(nt_tiles(m, r), k) * m * r * 4);
+    v.t = take((size_t)m * r * 4);
+    if (sl == 1) {
+      v.ts = reinterpret_cast<uint16_t*>(take((size_t)m * 2 * rp * 2));
+      v.b2 = reinterpret_cast<uint16_t*>(take((size_t)n * 2 * rp * 2));
+    }
+  }
+  if (w) *w = v;
+  return off;
+}
+
+hipError_t launch_fp8_linear(const uint16_t* x, int64_t m, int64_t n, int64_t k, const uint8_t* codes,
+                             const float* scales, const uint16_t* a, const uint16_t* b, int64_t r, float s,
+                             uint16_t* y, const Fp8Ws& w, hipStream_t st) {
+  if (r > 0) {
+    const int64_t tiles = nt_tiles(m, r);
+    Seg sa{x, a, (int)k, (int)k, nt_slice_len(tiles, k)};
+    const int sl = nt_slices(tiles, k);
+    hipLaunchKernelGGL((nt_gemm_kernel<false, 1>), dim3((unsigned)tiles, (unsigned)sl), dim3(256), 0, st, sa, Seg{},
+                       (int)m, (int)r, nullptr, s, nullptr, nullptr, w.tpart);
+    hipLaunchKernelGGL(slice_sum_kernel, dim3(flat_grid8(m * r)), dim3(256), 0, st, w.tpart, sl, m * r, w.t);
+  }
+  const int64_t tiles = nt_tiles(m, n);
+  Seg sw{x, codes, (int)k, (int)k, nt_slice_len(tiles, k)};
+  const int sl = nt_slices(tiles, k);
+  if (sl == 1) {
+    // enough output tiles (prefill): bf16 out in one launch, the LoRA term as
+    // a second segment (t split into bf16 hi | lo against B twice)
+    Seg lora{};
+    if (r > 0) {
+      const int64_t rp = (r + 7) / 8 * 8;
+      hipLaunchKernelGGL(lora_operands_kernel, dim3(flat_grid8((m + n) * rp)), dim3(256), 0, st, w.t, b, (int)m,
+                         (int)n, (int)r, (int)rp, w.ts, w.b2);
+      lora = Seg{w.ts, w.b2, (int)(2 * rp), (int)(2 * rp), (int)(2 * rp)};
+    }
+    hipLaunchKernelGGL((nt_gemm_kernel<true, 1, true>), dim3((unsigned)tiles), dim3(256), 0, st, sw, lora, (int)m,
+                       (int)n, nullptr, 1.0f, scales, y, nullptr);
+    return hipGetLastError();
+  }
+  hipLaunchKernelGGL((nt_gemm_kernel<false, 1, true>), dim3((unsigned)tiles, (unsigned)sl), dim3(256), 0, st, sw,
+                     Seg{}, (int)m, (int)n, nullptr, 1.0f, scales, nullptr, w.ypart);
+  hipLaunchKernelGGL(fp8_finish_kernel, dim3(flat_grid8(m * n)), dim3(256), 0, st, w.ypart, sl, (int)m, (int)n,
+                     r > 0 ? w.t : nullptr, r > 0 ? b : nullptr, (int)r, y);
+  return hipGetLastError();
+}
+
+}  // namespace fp4rl

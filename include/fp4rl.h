@@ -230,6 +230,30 @@ fp4rl_status fp4rl_fp4_lora_linear_backward(const uint16_t* dy, const uint16_t* 
                                             void* workspace, size_t workspace_bytes, fp4rl_stream stream);
 
 /* ------------------------------------------------------------------------
+ * FP8 rollout weights (gist.science summary of adaptive importance sampling
+ * for quantized RL, "Problem definition" and "Experimental results": the
+ * rollout engine runs in FP8 while the trainer keeps BF16, halving the
+ * rollout model's memory). The page fixes no layout; this library's reading:
+ * OCP E4M3 bytes [n][k] (bias 7, max 448, no -0 codes) and one fp32 scale per
+ * output row, s_n = amax_n / 448 (0 for an all-zero row).
+ * fp4rl_fp8_quantize: w fp32 or bf16 [n][k] -> codes [n][k], row_scales [n];
+ *   code = nearest E4M3 value to the fp32 quotient w / s_n, ties to even,
+ *   saturating at 448. k a positive multiple of 16, below 2^22.
+ * fp4rl_fp8_lora_linear: y = bf16(x deq(W8)^T + s (x A^T) B^T), W8A16:
+ *   x bf16 [m][k], deq(W8)[n][k] = e4m3(code) s_n, lora_a bf16 [r][k] and
+ *   lora_b bf16 [n][r] (both NULL or both set), y bf16 [m][n]; m, n, k below
+ *   2^22. Workspace: fp4rl_fp8_lora_linear_workspace(m, n, k, r) bytes,
+ *   256-byte aligned, no initial contents needed (fp32 partial products).
+ * Errors as for the NVFP4 calls; nothing is launched on error. */
+fp4rl_status fp4rl_fp8_quantize(const void* w, int32_t w_dtype, int64_t n, int64_t k, uint8_t* codes,
+                                float* row_scales, fp4rl_stream stream);
+size_t fp4rl_fp8_lora_linear_workspace(int64_t m, int64_t n, int64_t k, int64_t r);
+fp4rl_status fp4rl_fp8_lora_linear(const uint16_t* x, int64_t m, int64_t n, int64_t k, const uint8_t* codes,
+                                   const float* row_scales, const uint16_t* lora_a, const uint16_t* lora_b, int64_t r,
+                                   float lora_scale, uint16_t* y, void* workspace, size_t workspace_bytes,
+                                   fp4rl_stream stream);
+
+/* ------------------------------------------------------------------------
  * AQN.
  * fp4rl_aqn_sigma [host]: sigma_k = sigma_start (sigma_end/sigma_start)^(k/(K-1)),
  *   computed in double and returned as float; K == 1 gives sigma_start.

@@ -166,6 +166,35 @@ def test_backward_rejects_bad_arguments(lib):
         4, 8, 32, 0, 1)) == ERR_HIP
 
 
+def test_fp8_rejects_bad_arguments(lib):
+    q = lib.fp4rl_fp8_quantize
+    assert q(FAKE, 0, 8, 24, FAKE, FAKE, None) == ERR_SHAPE
+    assert q(FAKE, 0, 8, 0, FAKE, FAKE, None) == ERR_SHAPE
+    assert q(FAKE, 5, 8, 32, FAKE, FAKE, None) == ERR_DTYPE
+    assert q(None, 0, 8, 32, FAKE, FAKE, None) == ERR_NULL
+    assert q(MIS, 0, 8, 32, FAKE, FAKE, None) == ERR_ALIGN
+    assert q(FAKE, 0, 0, 32, None, None, None) == OK
+    f = lib.fp4rl_fp8_lora_linear
+    ws = lib.fp4rl_fp8_lora_linear_workspace(4, 8, 32, 8)
+    assert ws >= 4 * 8 * 4 + 4 * 8 * 4
+    args = dict(x=FAKE, m=4, n=8, k=32, c=FAKE, s=FAKE, a=FAKE, b=FAKE, r=8, ls=2.0, y=FAKE, ws=FAKE, wsb=ws)
+
+    def call(**kw):
+        a = dict(args, **kw)
+        return f(a["x"], a["m"], a["n"], a["k"], a["c"], a["s"], a["a"], a["b"], a["r"], a["ls"], a["y"], a["ws"],
+                 a["wsb"], None)
+
+    assert call(k=24) == ERR_SHAPE
+    assert call(r=257) == ERR_SHAPE
+    assert call(ls=float("nan")) == ERR_VALUE
+    assert call(a=None) == ERR_NULL
+    assert call(c=None) == ERR_NULL
+    assert call(y=MIS) == ERR_ALIGN
+    assert call(wsb=ws - 1) == ERR_WORKSPACE
+    assert call(ws=FAKE + 16) == ERR_ALIGN
+    assert call(m=0) == OK and call(n=0) == OK
+
+
 def test_aqn_rejects_bad_arguments(lib):
     f = lib.fp4rl_aqn_rmsnorm
     assert f(FAKE, 4, 512, FAKE, -1.0, 0, 0, 0, 1e-6, FAKE, None, None) == ERR_VALUE
