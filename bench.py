@@ -565,6 +565,7 @@ def run_extras(torch, fr, dev, shapes, layer, lora, fp32):
     res["prefill"] = {"M": PREFILL_M, "tflops": round(flops / dt / 1e12, 2), "ms_per_layer": round(dt * 1e3, 3),
                       "frac_of_bf16_peak": round(flops / dt / 1e12 / BF16_PEAK_TFLOPS, 4)}
     res["lora_backward"] = run_backward(torch, fr, dev, shapes, layer, lora, xs, g, reps)
+    res["fp8_linear"] = run_fp8(torch, fr, dev, shapes, lora, xs, g)
     del xs, ys
 
     # quantiser on 14B shapes: one layer's five matrices, 0.02 t(3) weights with
@@ -662,6 +663,45 @@ def run_backward(torch, fr, dev, shapes, layer, lora, xs, g, reps):
     return {"M": PREFILL_M, "r": RANK, "tflops": round(bflops / dt / 1e12, 2), "ms_per_layer": round(dt * 1e3, 3),
             "frac_of_bf16_peak": round(bflops / dt / 1e12 / BF16_PEAK_TFLOPS, 4),
             "workspace_GB": round(bws.numel() / 1e9, 3)}
+
+
+def run_fp8(torch, fr, dev, shapes, lora, xs, g):
+    """FP8 (E4M3, per-row scale) W8A16 rollout linears of the same 7B layer and
+    adapters: decode at 1, 8, 32, 64 tokens (FP8 weight GB/s) and the
+    8192-token prefill (TFLOP/s)."""
+    w8 = {name: fr.fp8_quantize(torch.randn((n, k), generator=g, device=dev).mul_(0.02))
+          for name, (n, k) in shapes.items()}
+    wbytes = sum(n * k + 4 * n for n, k in shapes.values())
+    out = {}
+    for m in TOKENS + (PREFILL_M,):
+        xm = xs if m == PREFILL_M else {k: torch.randn((m, k), generator=g, device=dev).to(torch.bfloat16)
+                                       for k in {k for _, k in shapes.values()}}
+        ys = {name: torch.empty((m, n), dtype=torch.bfloat16, device=dev) for name, (n, k) in shapes.items()}
+        wss = {name: torch.empty(max(fr.fp8_lora_linear_workspace_bytes(m, n, k, RANK), 256), dtype=torch.uint8,
+                                 device=dev) for name, (n, k) in shapes.items()}
+
+        def one():
+            for name, (n, k) in shapes.items():
+                a, b = lora[name]
+                fr.fp8_lora_linear(xm[k], w8[name], a, b, LORA_SCALE, out=ys[name], workspace=wss[name])
+
+        one()
+        torch.cuda.synchronize()
+        reps = 3 if m == PREFILL_M else 20
+        t0 = time.perf_counter()
+        for _ in range(reps):
+            one()
+        torch.cuda.synchronize()
+        dt = (time.perf_counter() - t0) / reps
+        flops = sum(linear_flops(m, n, k, RANK) for n, k in shapes.values())
+        if m == PREFILL_M:
+            out["prefill"] = {"M": m, "ms_per_layer": round(dt * 1e3, 3), "tflops": round(flops / dt / 1e12, 2),
+                              "frac_of_bf16_peak": round(flops / dt / 1e12 / BF16_PEAK_TFLOPS, 4)}
+        else:
+            out[f"decode_M{m}"] = {"us_per_layer": round(dt * 1e6, 1), "weight_GB/s": round(wbytes / dt / 1e9, 1),
+                                   "frac_of_hbm": round(wbytes / dt / 1e9 / HBM_PEAK_GBS, 4)}
+        del ys, wss
+    return out
 
 
 def run_decode_32b(torch, fr, dev, layers=64, m=128, r=RANK_32B):

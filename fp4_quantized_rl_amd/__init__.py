@@ -27,7 +27,7 @@ from dataclasses import dataclass
 __all__ = [
     "LIB_PATH", "Fp4rlError", "load_library", "NVFP4Weight", "nvfp4_empty", "nvfp4_quantize", "nvfp4_to_tiled",
     "fp4_lora_linear", "fp4_lora_linear_backward", "fp4_lora_linear_backward_workspace_bytes",
-    "FP8Weight", "fp8_quantize", "fp8_lora_linear",
+    "FP8Weight", "fp8_quantize", "fp8_lora_linear", "fp8_lora_linear_workspace_bytes",
     "lora_down", "fp4_linear_lora_up", "fp4_linear_kernel_name", "linear_workspace",
     "fp4_lora_linear_workspace_bytes", "fp4_linear_lora_up_workspace_bytes", "aqn_sigma", "aqn_rmsnorm", "philox_words",
     "EXPORTED_SYMBOLS",
@@ -289,6 +289,10 @@ def fp8_quantize(w) -> FP8Weight:
         _check(load_library().fp4rl_fp8_quantize(_ptr(w), BF16 if w.dtype == torch.bfloat16 else F32, n, k,
                                                  _ptr(codes), _ptr(scales), _stream(w.device)), "fp8_quantize")
     return FP8Weight(codes, scales)
+
+
+def fp8_lora_linear_workspace_bytes(m: int, n: int, k: int, r: int) -> int:
+    return load_library().fp4rl_fp8_lora_linear_workspace(m, n, k, r)
 
 
 def fp8_lora_linear(x, w8: FP8Weight, lora_a=None, lora_b=None, lora_scale: float = 0.0, out=None, workspace=None):
