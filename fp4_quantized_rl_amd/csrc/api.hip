@@ -431,6 +431,8 @@ static fp4rl_status check_fp8_shape(int64_t m, int64_t n, int64_t k, int64_t r) 
                 "bad shape (m=%lld n=%lld k=%lld r=%lld)", (long long)m, (long long)n, (long long)k, (long long)r);
   FP4RL_REQUIRE(m < ((int64_t)1 << 22) && n < ((int64_t)1 << 22) && k < ((int64_t)1 << 22), FP4RL_ERR_SHAPE,
                 "m, n and k must be below 2^22");
+  // the LoRA down-projection addresses activations with 32-bit byte offsets
+  FP4RL_REQUIRE(m * k < ((int64_t)1 << 30), FP4RL_ERR_SHAPE, "m * k = %lld must be below 2^30", (long long)(m * k));
   FP4RL_REQUIRE(r <= fp4rl::kMaxRank, FP4RL_ERR_SHAPE, "rank r=%lld exceeds %lld", (long long)r,
                 (long long)fp4rl::kMaxRank);
   return FP4RL_OK;

@@ -16,8 +16,8 @@
 //     to bf16 exactly on the way into LDS (v_cvt_pk_f32_fp8), fp32
 //     accumulation scaled per row by s_n; the contraction is split over
 //     workgroups when there are few output tiles (decode), partials fp32.
-//   t = s x A^T from the same GEMM kernel on A (bf16), its slices summed by
-//   slice_sum_kernel. With enough output tiles (prefill) the linear writes
+//   t = s x A^T in K-slices by the NVFP4 linear's LoRA down-projection
+//   kernel; the finishing kernels add the slices in order. With enough output tiles (prefill) the linear writes
 //   bf16 y in one launch, the LoRA term accumulated as a second contraction
 //   segment (t as bf16 hi | lo against B twice: lora_operands_kernel);
 //   split (decode), fp8_finish_kernel makes y = bf16(sum of slices + t . B[n]).
@@ -26,6 +26,7 @@
 #include "device.hpp"
 #include "fp8.hpp"
 #include "gemm_nt.hpp"
+#include "launch.hpp"
 
 namespace fp4rl {
 namespace {
@@ -90,44 +91,60 @@ __global__ __launch_bounds__(256) void fp8_quantize_kernel(const void* __restric
   }
 }
 
-__global__ __launch_bounds__(256) void slice_sum_kernel(const float* __restrict__ part, int slices, int64_t count,
-                                                        float* __restrict__ out) {
-  for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < count; i += (int64_t)gridDim.x * 256) {
-    float v = 0.0f;
-    for (int s = 0; s < slices; ++s) v += part[(int64_t)s * count + i];
-    out[i] = v;
-  }
-}
-
-// y[m][n] = bf16(sum_s part[s][m][n] + sum_j t[m][j] B[n][j]); slices and
-// ranks in order
+// y[m][n] = bf16(sum_s part[s][m][n] + sum_j t[m][j] B[n][j]), t the sum of
+// its K-slices tpart[q][m][j]; slices, K-slices and ranks in order
 __global__ __launch_bounds__(256) void fp8_finish_kernel(const float* __restrict__ part, int slices, int M, int N,
-                                                         const float* __restrict__ t, const uint16_t* __restrict__ b,
-                                                         int r, uint16_t* __restrict__ y) {
-  const int64_t count = (int64_t)M * N;
+                                                         const float* __restrict__ tpart, int tsl,
+                                                         const uint16_t* __restrict__ b, int r,
+                                                         uint16_t* __restrict__ y) {
+  const int64_t count = (int64_t)M * N, tstride = (int64_t)M * r;
   for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < count; i += (int64_t)gridDim.x * 256) {
     float v = 0.0f;
     for (int s = 0; s < slices; ++s) v += part[(int64_t)s * count + i];
     if (r > 0) {
       const int m = (int)(i / N), n = (int)(i - (int64_t)m * N);
+      const float* tm = tpart + (int64_t)m * r;
+      const uint16_t* bn = b + (int64_t)n * r;
       float l = 0.0f;
-      for (int j = 0; j < r; ++j) l = fmaf(t[(int64_t)m * r + j], bf16_lo(b[(int64_t)n * r + j]), l);
+      int j = 0;
+      if ((r & 7) == 0)  // B and t rows 16-byte aligned: 8 ranks per step, same order
+        for (; j < r; j += 8) {
+          const uint4 bv = *reinterpret_cast<const uint4*>(bn + j);
+          float4 t0 = *reinterpret_cast<const float4*>(tm + j), t1 = *reinterpret_cast<const float4*>(tm + j + 4);
+          for (int q = 1; q < tsl; ++q) {
+            const float4 u0 = *reinterpret_cast<const float4*>(tm + q * tstride + j);
+            const float4 u1 = *reinterpret_cast<const float4*>(tm + q * tstride + j + 4);
+            t0.x += u0.x; t0.y += u0.y; t0.z += u0.z; t0.w += u0.w;
+            t1.x += u1.x; t1.y += u1.y; t1.z += u1.z; t1.w += u1.w;
+          }
+          l = fmaf(t0.x, bf16_lo(bv.x), l); l = fmaf(t0.y, bf16_hi(bv.x), l);
+          l = fmaf(t0.z, bf16_lo(bv.y), l); l = fmaf(t0.w, bf16_hi(bv.y), l);
+          l = fmaf(t1.x, bf16_lo(bv.z), l); l = fmaf(t1.y, bf16_hi(bv.z), l);
+          l = fmaf(t1.z, bf16_lo(bv.w), l); l = fmaf(t1.w, bf16_hi(bv.w), l);
+        }
+      for (; j < r; ++j) {
+        float tj = tm[j];
+        for (int q = 1; q < tsl; ++q) tj += tm[q * tstride + j];
+        l = fmaf(tj, bf16_lo(bn[j]), l);
+      }
       v += l;
     }
     y[i] = (uint16_t)f32_to_bf16(v);
   }
 }
 
-// ts[m][0..2rp) = bf16 hi | lo of t[m][0..r) (zero past r); b2[n][0..2rp) =
+// ts[m][0..2rp) = bf16 hi | lo of t[m][0..r) (its K-slices summed in order; zero past r); b2[n][0..2rp) =
 // (B[n] | B[n]) (zero past r): the LoRA term as a second contraction segment
-__global__ __launch_bounds__(256) void lora_operands_kernel(const float* __restrict__ t, const uint16_t* __restrict__ b,
-                                                            int M, int N, int r, int rp, uint16_t* __restrict__ ts,
-                                                            uint16_t* __restrict__ b2) {
+__global__ __launch_bounds__(256) void lora_operands_kernel(const float* __restrict__ t, int tsl,
+                                                            const uint16_t* __restrict__ b, int M, int N, int r, int rp,
+                                                            uint16_t* __restrict__ ts, uint16_t* __restrict__ b2) {
   const int64_t nt = (int64_t)M * rp, count = nt + (int64_t)N * rp;
   for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < count; i += (int64_t)gridDim.x * 256) {
     if (i < nt) {
       const int m = (int)(i / rp), j = (int)(i - (int64_t)m * rp);
-      const float v = j < r ? t[(int64_t)m * r + j] : 0.0f;
+      float v = 0.0f;
+      if (j < r)
+        for (int q = 0; q < tsl; ++q) v += t[(int64_t)q * M * r + (int64_t)m * r + j];
       const uint32_t hb = f32_to_bf16(v);
       ts[(int64_t)m * 2 * rp + j] = (uint16_t)hb;
       ts[(int64_t)m * 2 * rp + rp + j] = (uint16_t)f32_to_bf16(v - __uint_as_float(hb << 16));
@@ -139,6 +156,125 @@ __global__ __launch_bounds__(256) void lora_operands_kernel(const float* __restr
       b2[(int64_t)n * 2 * rp + rp + j] = v;
     }
   }
+}
+
+// ---------------------------------------------------------------------------
+// Decode (M <= 64): a workgroup takes 64 weight rows (four 16-row MFMA
+// tiles) and one K-slice; its four waves take the slice's 64-k chunks in
+// turn (adjacent chunks of the same rows at once), two chunks in flight per
+// wave. A lane loads 16 E4M3 bytes per weight tile and chunk straight into
+// registers (row li, k = 16 g .. + 15 of the chunk) and converts them
+// exactly to bf16; its token fragments (token li, the same 16 k) come from
+// x through the cache. The MFMA's k order is permuted the same way on both
+// operands (slot (step s, group g, e) holds k = 16 g + 8 s + e), so the sum
+// is unchanged. The waves' sums are added in wave order through LDS, scaled
+// by s_n and written as fp32 partials [slice][M][N]; fp8_finish_kernel adds
+// the slices and the LoRA term.
+// ---------------------------------------------------------------------------
+constexpr int kDecRows = 64;
+
+template <int T>
+__global__ __launch_bounds__(256) void fp8_decode_kernel(const uint16_t* __restrict__ x, int M, int N, int K,
+                                                         const uint8_t* __restrict__ codes,
+                                                         const float* __restrict__ scales, int slice,
+                                                         float* __restrict__ part) {
+  __shared__ f32x4 red[3][4 * T][64];
+  const int k0 = blockIdx.y * slice, klen = min(slice, K - k0);
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int li = lane & 15, lg = lane >> 4;
+  const int n0 = blockIdx.x * kDecRows;
+  const uint8_t* wrow[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) wrow[i] = codes + (int64_t)min(n0 + 16 * i + li, N - 1) * K + k0 + 16 * lg;
+  const uint16_t* xrow[T];  // tokens past M are clamped (their columns are never stored)
+#pragma unroll
+  for (int j = 0; j < T; ++j) xrow[j] = x + (int64_t)min(16 * j + li, M - 1) * K + k0 + 16 * lg;
+  f32x4 acc[4][T];
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < T; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+  const int nch = (klen + 63) / 64;
+  for (int c0 = wave; c0 < nch; c0 += 8) {
+    uint4 wv[2][4], xv[2][T][2];
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+      const int ch = c0 + 4 * u;
+      const bool in = ch < nch && 64 * ch + 16 * lg < klen;  // klen % 16 == 0: all 16 values in or out
+#pragma unroll
+      for (int i = 0; i < 4; ++i) wv[u][i] = in ? ld_nt16(wrow[i] + 64 * ch) : make_uint4(0u, 0u, 0u, 0u);
+#pragma unroll
+      for (int j = 0; j < T; ++j)
+#pragma unroll
+        for (int h = 0; h < 2; ++h)
+          xv[u][j][h] = in ? *reinterpret_cast<const uint4*>(xrow[j] + 64 * ch + 8 * h) : make_uint4(0u, 0u, 0u, 0u);
+    }
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+      bf16x8 a[2][4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const uint32_t w4[4] = {wv[u][i].x, wv[u][i].y, wv[u][i].z, wv[u][i].w};
+        uint32_t o[8];
+#pragma unroll
+        for (int d = 0; d < 4; ++d) {
+          const f32x2 lo = __builtin_amdgcn_cvt_pk_f32_fp8(w4[d], false), hi = __builtin_amdgcn_cvt_pk_f32_fp8(w4[d], true);
+          o[2 * d] = pack_hi16(lo.x, lo.y);
+          o[2 * d + 1] = pack_hi16(hi.x, hi.y);
+        }
+        a[0][i] = __builtin_bit_cast(bf16x8, make_uint4(o[0], o[1], o[2], o[3]));
+        a[1][i] = __builtin_bit_cast(bf16x8, make_uint4(o[4], o[5], o[6], o[7]));
+      }
+#pragma unroll
+      for (int st = 0; st < 2; ++st)
+#pragma unroll
+        for (int j = 0; j < T; ++j) {
+          const bf16x8 b = as_bf16x8(xv[u][j][st]);
+#pragma unroll
+          for (int i = 0; i < 4; ++i) acc[i][j] = mfma16x16x32(a[st][i], b, acc[i][j]);
+        }
+    }
+  }
+  if (wave > 0) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int j = 0; j < T; ++j) red[wave - 1][i * T + j][lane] = acc[i][j];
+  }
+  __syncthreads();
+  if (wave > 0) return;
+  // lane holds rows n0 + 16 i + 4 g + v of token 16 j + li
+  float* out = part + (int64_t)blockIdx.y * M * N;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int n = n0 + 16 * i + 4 * lg;
+#pragma unroll
+    for (int j = 0; j < T; ++j) {
+      const f32x4 v = ((acc[i][j] + red[0][i * T + j][lane]) + red[1][i * T + j][lane]) + red[2][i * T + j][lane];
+      const int m = 16 * j + li;
+      if (m >= M) continue;
+#pragma unroll
+      for (int e = 0; e < 4; ++e)
+        if (n + e < N) out[(int64_t)m * N + n + e] = v[e] * scales[n + e];
+    }
+  }
+}
+
+// K-slices of the decode kernel: about 512 workgroups (64-row groups x
+// slices), each slice a multiple of 64 and at least 256 long.
+struct DecSplit {
+  int t = 0, slice = 0, slices = 0;
+};
+DecSplit dec_split(int64_t m, int64_t n, int64_t k) {
+  DecSplit d;
+  d.t = m <= 16 ? 1 : m <= 32 ? 2 : 4;
+  const int64_t groups = (n + kDecRows - 1) / kDecRows;
+  int64_t want = (512 + groups - 1) / groups;
+  want = std::max<int64_t>(1, std::min<int64_t>(want, k / 256));
+  const int64_t len = ((k + want - 1) / want + 63) / 64 * 64;
+  d.slice = (int)len;
+  d.slices = (int)((k + len - 1) / len);
+  return d;
 }
 
 unsigned flat_grid8(int64_t count) {
@@ -158,8 +294,8 @@ hipError_t launch_fp8_quantize(const void* w, bool w_bf16, int64_t n, int64_t k,
   return hipGetLastError();
 }
 
-// Workspace: y partials [S][m][n] fp32 when the contraction is split; with
-// adapters t partials [St][m][r], t [m][r] fp32 and, unsplit, the bf16 LoRA
+// Workspace: y partials [S][m][n] fp32 for decode or a split contraction; with
+// adapters the K-slices of t [St][m][r] fp32 and, unsplit, the bf16 LoRA
 // segment operands ts [m][2 rp], b2 [n][2 rp].
 size_t fp8_linear_workspace(int64_t m, int64_t n, int64_t k, int64_t r, Fp8Ws* w, void* base) {
   size_t off = 0;
@@ -169,13 +305,15 @@ size_t fp8_linear_workspace(int64_t m, int64_t n, int64_t k, int64_t r, Fp8Ws* w
     return base ? reinterpret_cast<float*>(static_cast<uint8_t*>(base) + o) : nullptr;
   };
   Fp8Ws v{};
-  const int sl = nt_slices(nt_tiles(m, n), k);
+  // decode (m <= 64) always writes partials; otherwise only a split contraction does
+  const bool dec = m <= 64;
+  const int sl = dec ? dec_split(m, n, k).slices : nt_slices(nt_tiles(m, n), k);
+  const bool parts = dec || sl > 1;
   const int64_t rp = (r + 7) / 8 * 8;
-  if (sl > 1) v.ypart = take((size_t)sl * m * n * 4);
+  if (parts) v.ypart = take((size_t)sl * m * n * 4);
   if (r > 0) {
-    v.tpart = take((size_t)nt_slices(nt_tiles(m, r), k) * m * r * 4);
-    v.t = take((size_t)m * r * 4);
-    if (sl == 1) {
+    v.tpart = take((size_t)lora_slices(k, lora_splits(m, k, r)) * m * r * 4);
+    if (!parts) {
       v.ts = reinterpret_cast<uint16_t*>(take((size_t)m * 2 * rp * 2));
       v.b2 = reinterpret_cast<uint16_t*>(take((size_t)n * 2 * rp * 2));
     }
@@ -187,13 +325,28 @@ size_t fp8_linear_workspace(int64_t m, int64_t n, int64_t k, int64_t r, Fp8Ws* w
 hipError_t launch_fp8_linear(const uint16_t* x, int64_t m, int64_t n, int64_t k, const uint8_t* codes,
                              const float* scales, const uint16_t* a, const uint16_t* b, int64_t r, float s,
                              uint16_t* y, const Fp8Ws& w, hipStream_t st) {
-  if (r > 0) {
-    const int64_t tiles = nt_tiles(m, r);
-    Seg sa{x, a, (int)k, (int)k, nt_slice_len(tiles, k)};
-    const int sl = nt_slices(tiles, k);
-    hipLaunchKernelGGL((nt_gemm_kernel<false, 1>), dim3((unsigned)tiles, (unsigned)sl), dim3(256), 0, st, sa, Seg{},
-                       (int)m, (int)r, nullptr, s, nullptr, nullptr, w.tpart);
-    hipLaunchKernelGGL(slice_sum_kernel, dim3(flat_grid8(m * r)), dim3(256), 0, st, w.tpart, sl, m * r, w.t);
+  int tsl = 0;
+  if (r > 0) {  // t = s x A^T in K-slices (the NVFP4 linear's LoRA down-projection kernel)
+    const int splits = lora_splits(m, k, r);
+    tsl = lora_slices(k, splits);
+    const hipError_t e = launch_lora_down(x, m, k, a, r, s, splits, w.tpart, st);
+    if (e != hipSuccess) return e;
+  }
+  if (m <= 64) {
+    const DecSplit d = dec_split(m, n, k);
+    const dim3 grid((unsigned)((n + kDecRows - 1) / kDecRows), (unsigned)d.slices);
+    if (d.t == 1)
+      hipLaunchKernelGGL(fp8_decode_kernel<1>, grid, dim3(256), 0, st, x, (int)m, (int)n, (int)k, codes, scales, d.slice,
+                         w.ypart);
+    else if (d.t == 2)
+      hipLaunchKernelGGL(fp8_decode_kernel<2>, grid, dim3(256), 0, st, x, (int)m, (int)n, (int)k, codes, scales, d.slice,
+                         w.ypart);
+    else
+      hipLaunchKernelGGL(fp8_decode_kernel<4>, grid, dim3(256), 0, st, x, (int)m, (int)n, (int)k, codes, scales, d.slice,
+                         w.ypart);
+    hipLaunchKernelGGL(fp8_finish_kernel, dim3(flat_grid8(m * n)), dim3(256), 0, st, w.ypart, d.slices, (int)m, (int)n,
+                       w.tpart, tsl, r > 0 ? b : nullptr, (int)r, y);
+    return hipGetLastError();
   }
   const int64_t tiles = nt_tiles(m, n);
   Seg sw{x, codes, (int)k, (int)k, nt_slice_len(tiles, k)};
@@ -204,8 +357,8 @@ hipError_t launch_fp8_linear(const uint16_t* x, int64_t m, int64_t n, int64_t k,
     Seg lora{};
     if (r > 0) {
       const int64_t rp = (r + 7) / 8 * 8;
-      hipLaunchKernelGGL(lora_operands_kernel, dim3(flat_grid8((m + n) * rp)), dim3(256), 0, st, w.t, b, (int)m,
-                         (int)n, (int)r, (int)rp, w.ts, w.b2);
+      hipLaunchKernelGGL(lora_operands_kernel, dim3(flat_grid8((m + n) * rp)), dim3(256), 0, st, w.tpart, tsl, b,
+                         (int)m, (int)n, (int)r, (int)rp, w.ts, w.b2);
       lora = Seg{w.ts, w.b2, (int)(2 * rp), (int)(2 * rp), (int)(2 * rp)};
     }
     hipLaunchKernelGGL((nt_gemm_kernel<true, 1, true>), dim3((unsigned)tiles), dim3(256), 0, st, sw, lora, (int)m,
@@ -215,7 +368,7 @@ hipError_t launch_fp8_linear(const uint16_t* x, int64_t m, int64_t n, int64_t k,
   hipLaunchKernelGGL((nt_gemm_kernel<false, 1, true>), dim3((unsigned)tiles, (unsigned)sl), dim3(256), 0, st, sw,
                      Seg{}, (int)m, (int)n, nullptr, 1.0f, scales, nullptr, w.ypart);
   hipLaunchKernelGGL(fp8_finish_kernel, dim3(flat_grid8(m * n)), dim3(256), 0, st, w.ypart, sl, (int)m, (int)n,
-                     r > 0 ? w.t : nullptr, r > 0 ? b : nullptr, (int)r, y);
+                     w.tpart, tsl, r > 0 ? b : nullptr, (int)r, y);
   return hipGetLastError();
 }
 

@@ -14,8 +14,7 @@ hipError_t launch_fp8_quantize(const void* w, bool w_bf16, int64_t n, int64_t k,
 
 struct Fp8Ws {
   float* ypart = nullptr;  // [S][m][n] partial products of the base (S contraction slices)
-  float* tpart = nullptr;  // [St][m][r] partials of t = s x A^T
-  float* t = nullptr;      // [m][r]
+  float* tpart = nullptr;  // [St][m][r] K-slices of t = s x A^T
   uint16_t* ts = nullptr;  // [m][2 rp] bf16 hi | lo of t (unsplit launches; rp = r rounded up to 8)
   uint16_t* b2 = nullptr;  // [n][2 rp] bf16 (B | B)
 };
