@@ -67,6 +67,8 @@ def parse_args():
     p.add_argument("--no-extras", action="store_true", help="skip prefill / quantiser / AQN extra timings")
     p.add_argument("--backward-only", action="store_true",
                    help="time only the LoRA backward of the 7B layer at 8192 tokens (--steps passes)")
+    p.add_argument("--fp8-only", action="store_true",
+                   help="time only the FP8 (E4M3) linears of the 7B layer: decode 1..64 tokens and the prefill")
     p.add_argument("--copy-calibration-mib", type=int, default=0,
                    help="first run a plain device-to-device copy of this many MiB three times (the reference "
                         "kernel that scales rocprofv3 FETCH_SIZE / WRITE_SIZE to bytes)")
@@ -365,6 +367,14 @@ def main():
         b = torch.randn((n, RANK), generator=g, device=dev).mul_(0.01).to(torch.bfloat16)
         lora[name] = (a, b)
     wnorm = torch.ones(hidden, dtype=torch.float32, device=dev)
+    if args.fp8_only:
+        progress("FP8 linear timing")
+        gb = torch.Generator(device=dev)
+        gb.manual_seed(21)
+        xs = {k: torch.randn((PREFILL_M, k), generator=gb, device=dev).to(torch.bfloat16)
+              for k in sorted({k for _, k in shapes.values()})}
+        print(json.dumps({"fp8_linear": run_fp8(torch, fr, dev, shapes, lora, xs, gb)}))
+        return
     if args.backward_only:
         progress("LoRA backward timing")
         gb = torch.Generator(device=dev)
