@@ -10,6 +10,7 @@ rollout hot path computes:
   LoRA update;
 * ``lora_backward`` – dX, dA and dB of that linear (the base stays frozen);
 * ``fp8``    – the FP8 (E4M3, per-row scale) rollout weights and their W8A16 linear;
+* ``gate_up`` – gate and up projections of one input with the SiLU-gated product;
 * ``aqn``    – the Adaptive Quantization Noise RMSNorm: the exponential sigma
   schedule, Philox4x32-10 + Box-Muller noise, and the noisy-weight RMSNorm;
 * ``numerics`` – bf16 round-to-nearest-even and the rel-L2 metric.
@@ -24,4 +25,4 @@ here is pinned by a ``-m "not gpu"`` test against something other than
 itself (closed forms, brute force, torch CPU casts, torch's Philox header),
 except where a docstring says "parity unpinned".
 """
-from . import numerics, nvfp4, linear, lora_backward, fp8, aqn  # noqa: F401
+from . import numerics, nvfp4, linear, lora_backward, fp8, gate_up, aqn  # noqa: F401
