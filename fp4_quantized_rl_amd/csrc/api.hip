@@ -9,6 +9,7 @@
 #include "fp4rl.h"
 #include "backward.hpp"
 #include "fp8.hpp"
+#include "gate_up.hpp"
 #include "launch.hpp"
 
 namespace {
@@ -407,6 +408,52 @@ fp4rl_status fp4rl_fp4_lora_linear_backward(const uint16_t* dy, const uint16_t* 
   return launched(fp4rl::launch_lora_backward(dy, x, m, n, k, codes, scales, tensor_scale, r > 0 ? lora_a : nullptr,
                                               r > 0 ? lora_b : nullptr, r, lora_scale, dx, grad_a, grad_b, w, stream),
                   "fp4_lora_linear_backward");
+}
+
+// ----------------------------------------------------------------- gate/up --
+
+size_t fp4rl_fp4_gate_up_silu_workspace(int64_t m, int64_t n, int64_t k, int64_t r) {
+  if (check_linear_shape(m, n, k, r) != FP4RL_OK || m == 0 || n == 0 || m > fp4rl::kGateUpMaxTokens) return 0;
+  return fp4rl::gate_up_workspace(m, k, r);
+}
+
+fp4rl_status fp4rl_fp4_gate_up_silu(const uint16_t* x, int64_t m, int64_t n, int64_t k, const uint8_t* gate_codes,
+                                    const uint8_t* gate_scales, const float* gate_tensor_scale,
+                                    const uint8_t* up_codes, const uint8_t* up_scales, const float* up_tensor_scale,
+                                    const uint16_t* lora_a_gate, const uint16_t* lora_b_gate,
+                                    const uint16_t* lora_a_up, const uint16_t* lora_b_up, int64_t r,
+                                    float lora_scale, uint16_t* h, void* workspace, size_t workspace_bytes,
+                                    fp4rl_stream stream) {
+  FP4RL_CHECK(check_linear_shape(m, n, k, r));
+  FP4RL_REQUIRE(m <= fp4rl::kGateUpMaxTokens, FP4RL_ERR_SHAPE, "m=%lld exceeds %lld tokens", (long long)m,
+                (long long)fp4rl::kGateUpMaxTokens);
+  FP4RL_REQUIRE(std::isfinite(lora_scale), FP4RL_ERR_VALUE, "lora_scale is not finite");
+  const bool any = lora_a_gate || lora_b_gate || lora_a_up || lora_b_up;
+  const bool all = lora_a_gate && lora_b_gate && lora_a_up && lora_b_up;
+  FP4RL_REQUIRE(any == all, FP4RL_ERR_NULL, "the four adapters must all be NULL or all be set");
+  if (!all) r = 0;
+  if (m == 0 || n == 0) return ok();
+  FP4RL_REQUIRE(x && gate_codes && gate_scales && gate_tensor_scale && up_codes && up_scales && up_tensor_scale && h,
+                FP4RL_ERR_NULL, "x, both weights and h must be non-NULL");
+  FP4RL_REQUIRE(aligned(x, 16) && aligned(gate_codes, 16) && aligned(gate_scales, 16) && aligned(up_codes, 16) &&
+                    aligned(up_scales, 16) && aligned(h, 16) && aligned(gate_tensor_scale, 4) &&
+                    aligned(up_tensor_scale, 4),
+                FP4RL_ERR_ALIGN, "x, codes, scales and h must be 16-byte aligned, tensor scales 4-byte aligned");
+  if (r > 0)
+    FP4RL_REQUIRE(aligned(lora_a_gate, 16) && aligned(lora_b_gate, 16) && aligned(lora_a_up, 16) &&
+                      aligned(lora_b_up, 16),
+                  FP4RL_ERR_ALIGN, "adapters must be 16-byte aligned");
+  const size_t need = fp4rl::gate_up_workspace(m, k, r);
+  if (need) {
+    FP4RL_REQUIRE(workspace != nullptr && workspace_bytes >= need, FP4RL_ERR_WORKSPACE, "workspace %zu < %zu bytes",
+                  workspace_bytes, need);
+    FP4RL_REQUIRE(aligned(workspace, 256), FP4RL_ERR_ALIGN, "workspace must be 256-byte aligned");
+  }
+  FP4RL_CHECK(check_device());
+  return launched(fp4rl::launch_gate_up(x, m, n, k, gate_codes, gate_scales, gate_tensor_scale, up_codes, up_scales,
+                                        up_tensor_scale, lora_a_gate, lora_b_gate, lora_a_up, lora_b_up, r,
+                                        lora_scale, static_cast<float*>(workspace), h, stream),
+                  "fp4_gate_up_silu");
 }
 
 // --------------------------------------------------------------------- FP8 --

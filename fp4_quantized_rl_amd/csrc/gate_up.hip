@@ -1,0 +1,214 @@
+// Gate and up projections of one input in one launch, with the SiLU-gated
+// product as epilogue (gfx950), for decode batches (M <= 128).
+//
+// The Qwen2.5 models that QeRL trains (QeRL explainer, experiments) gate
+// their MLP: h = SiLU(gate) * up, where gate and up are two linears of the
+// same input. Here both are NVFP4 + LoRA linears (own weights, tensor scale
+// and adapters), and
+//   h = bf16(SiLU(g) * u),  g = s_tg acc_g + tg . Bg[n],  u = s_tu acc_u + tu . Bu[n],
+// with g and u kept in fp32 (one rounding, of h), SiLU(v) = v / (1 + e^-v).
+//
+// gate_up_kernel<T>: one workgroup per 16-row weight tile of BOTH matrices
+// (the same output features n); its four waves take the 128-k chunks in
+// turn. Per chunk a lane loads 16 code bytes and 4 scale bytes of each tile
+// (word j of the tiled layout: row i, k = 32 j + 8 g .. + 7) and, for each of
+// the T token tiles, its 16-byte token fragments (token i, the same k), and
+// issues 4 x T MFMAs per matrix. Each wave scales its sums by the tensor
+// scales; waves 0 and 1 add the gate's and the up's LoRA terms by MFMA (t in
+// bf16 hi + lo against the B rows); the four waves' sums are added in wave
+// order through LDS, and every thread takes outputs in turn for the gated
+// product.
+// t_g = s x Ag^T and t_u = s x Au^T come from the linear's LoRA
+// down-projection kernel.
+#include <algorithm>
+
+#include "device.hpp"
+#include "gate_up.hpp"
+#include "launch.hpp"
+
+namespace fp4rl {
+namespace {
+
+// the four OCP E4M3 bytes of w as fp32 (exact)
+__device__ __forceinline__ void e4m3_scales(uint32_t w, float (&sc)[4]) {
+  sc[0] = __builtin_amdgcn_cvt_f32_fp8((int)w, 0);
+  sc[1] = __builtin_amdgcn_cvt_f32_fp8((int)w, 1);
+  sc[2] = __builtin_amdgcn_cvt_f32_fp8((int)w, 2);
+  sc[3] = __builtin_amdgcn_cvt_f32_fp8((int)w, 3);
+}
+
+// acc[j] += t[tokens of tile j] . B[rows of tile rt] by MFMA, 32 ranks per
+// step: A operand = B row li (ranks 32 q + 8 g .. + 7), B operand = t of
+// token 16 j + li split into bf16 hi + lo (two MFMAs: t kept to ~2^-17).
+// Rows and tokens past N and M are clamped (never stored), ranks past r zero.
+template <int T>
+__device__ __forceinline__ void lora_mfma(f32x4 (&acc)[T], const float* __restrict__ t,
+                                          const uint16_t* __restrict__ b, int r, int M, int N, int rt, int li, int lg) {
+  const uint16_t* brow = b + (int64_t)min(16 * rt + li, N - 1) * r;
+  const bool vec = (r & 7) == 0;
+  for (int q0 = 0; q0 < r; q0 += 32) {
+    const int q = q0 + 8 * lg;
+    uint32_t bw[4];
+    if (vec) {
+      const uint4 v = q < r ? *reinterpret_cast<const uint4*>(brow + q) : make_uint4(0u, 0u, 0u, 0u);
+      bw[0] = v.x; bw[1] = v.y; bw[2] = v.z; bw[3] = v.w;
+    } else {
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const uint32_t lo = q + 2 * e < r ? brow[q + 2 * e] : 0u, hi = q + 2 * e + 1 < r ? brow[q + 2 * e + 1] : 0u;
+        bw[e] = lo | (hi << 16);
+      }
+    }
+    const bf16x8 a = __builtin_bit_cast(bf16x8, make_uint4(bw[0], bw[1], bw[2], bw[3]));
+#pragma unroll
+    for (int j = 0; j < T; ++j) {
+      const float* trow = t + (int64_t)min(16 * j + li, M - 1) * r;
+      float tv[8];
+      if (vec && q < r) {
+        const float4 t0 = *reinterpret_cast<const float4*>(trow + q), t1 = *reinterpret_cast<const float4*>(trow + q + 4);
+        tv[0] = t0.x; tv[1] = t0.y; tv[2] = t0.z; tv[3] = t0.w; tv[4] = t1.x; tv[5] = t1.y; tv[6] = t1.z; tv[7] = t1.w;
+      } else {
+#pragma unroll
+        for (int e = 0; e < 8; ++e) tv[e] = q + e < r ? trow[q + e] : 0.0f;
+      }
+      uint4 th, tl;
+      split_bf16x8(tv, th, tl);
+      acc[j] = mfma16x16x32(a, as_bf16x8(th), acc[j]);
+      acc[j] = mfma16x16x32(a, as_bf16x8(tl), acc[j]);
+    }
+  }
+}
+
+template <int T>
+__global__ __launch_bounds__(256) void gate_up_kernel(const uint16_t* __restrict__ x, int M, int N, int K,
+                                                      const uint8_t* __restrict__ cg, const uint8_t* __restrict__ sg,
+                                                      const float* __restrict__ stg, const uint8_t* __restrict__ cu,
+                                                      const uint8_t* __restrict__ su, const float* __restrict__ stu,
+                                                      const float* __restrict__ tg, const float* __restrict__ tu,
+                                                      const uint16_t* __restrict__ bg,
+                                                      const uint16_t* __restrict__ bu, int r,
+                                                      uint16_t* __restrict__ h) {
+  __shared__ f32x4 red[4][2 * T][64];
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int li = lane & 15, lg = lane >> 4;
+  const int rt = blockIdx.x, KC = (K + 127) >> 7;
+  const int64_t tile0 = (int64_t)rt * KC;
+  const uint8_t* gcode = cg + tile0 * 1024 + 16 * lane;
+  const uint8_t* ucode = cu + tile0 * 1024 + 16 * lane;
+  const uint8_t* gsc = sg + tile0 * 128 + 4 * (16 * (lg >> 1) + li);
+  const uint8_t* usc = su + tile0 * 128 + 4 * (16 * (lg >> 1) + li);
+  const uint16_t* xrow[T];  // tokens past M are clamped (their columns are never stored)
+#pragma unroll
+  for (int j = 0; j < T; ++j) xrow[j] = x + (int64_t)min(16 * j + li, M - 1) * K + 8 * lg;
+  f32x4 ag[T], au[T];
+#pragma unroll
+  for (int j = 0; j < T; ++j) ag[j] = au[j] = f32x4{0.f, 0.f, 0.f, 0.f};
+  for (int c = wave; c < KC; c += 4) {
+    const uint4 wg = ld_nt16(gcode + (int64_t)c * 1024), wu = ld_nt16(ucode + (int64_t)c * 1024);
+    const uint32_t sgw = *reinterpret_cast<const uint32_t*>(gsc + (int64_t)c * 128);
+    const uint32_t suw = *reinterpret_cast<const uint32_t*>(usc + (int64_t)c * 128);
+    uint4 xv[4][T];
+#pragma unroll
+    for (int st = 0; st < 4; ++st) {
+      const int k = 128 * c + 32 * st + 8 * lg;  // K % 16 == 0: 8 values all in or all out
+#pragma unroll
+      for (int j = 0; j < T; ++j)
+        xv[st][j] = k < K ? *reinterpret_cast<const uint4*>(xrow[j] + 128 * c + 32 * st) : make_uint4(0u, 0u, 0u, 0u);
+    }
+    const uint32_t cwg[4] = {wg.x, wg.y, wg.z, wg.w}, cwu[4] = {wu.x, wu.y, wu.z, wu.w};
+    float scg[4], scu[4];
+    e4m3_scales(sgw, scg);
+    e4m3_scales(suw, scu);
+#pragma unroll
+    for (int st = 0; st < 4; ++st) {
+      const bf16x8 a_g = dequant8(cwg[st], scg[st]);
+      const bf16x8 a_u = dequant8(cwu[st], scu[st]);
+#pragma unroll
+      for (int j = 0; j < T; ++j) {
+        const bf16x8 b = as_bf16x8(xv[st][j]);
+        ag[j] = mfma16x16x32(a_g, b, ag[j]);
+        au[j] = mfma16x16x32(a_u, b, au[j]);
+      }
+    }
+  }
+  // each wave's partial sums times the tensor scales; the LoRA terms are
+  // added by MFMA, the gate's by wave 0 and the up's by wave 1
+  const float sgt = *stg, sut = *stu;
+#pragma unroll
+  for (int j = 0; j < T; ++j) {
+    ag[j] *= sgt;
+    au[j] *= sut;
+  }
+  if (r > 0 && wave == 0) lora_mfma<T>(ag, tg, bg, r, M, N, rt, li, lg);
+  if (r > 0 && wave == 1) lora_mfma<T>(au, tu, bu, r, M, N, rt, li, lg);
+#pragma unroll
+  for (int j = 0; j < T; ++j) {
+    red[wave][j][lane] = ag[j];
+    red[wave][T + j][lane] = au[j];
+  }
+  __syncthreads();
+  // output e = (token tl, feature row rl of the tile): the four waves' sums in
+  // wave order, then the gated product
+  for (int e = threadIdx.x; e < 256 * T; e += 256) {
+    const int tl = e >> 4, rl = e & 15;
+    const int m = tl, n = 16 * rt + rl;
+    if (m >= M || n >= N) continue;
+    const int j = tl >> 4, ln = 16 * (rl >> 2) + (tl & 15), v = rl & 3;
+    const float g = ((red[0][j][ln][v] + red[1][j][ln][v]) + red[2][j][ln][v]) + red[3][j][ln][v];
+    const float u = ((red[0][T + j][ln][v] + red[1][T + j][ln][v]) + red[2][T + j][ln][v]) + red[3][T + j][ln][v];
+    h[(int64_t)m * N + n] = (uint16_t)f32_to_bf16(g / (1.0f + expf(-g)) * u);
+  }
+}
+
+}  // namespace
+
+int gate_up_token_tiles(int64_t m) { return m <= 16 ? 1 : m <= 32 ? 2 : m <= 64 ? 4 : 8; }
+
+hipError_t launch_gate_up(const uint16_t* x, int64_t m, int64_t n, int64_t k, const uint8_t* cg, const uint8_t* sg,
+                          const float* stg, const uint8_t* cu, const uint8_t* su, const float* stu,
+                          const uint16_t* ag, const uint16_t* bg, const uint16_t* au, const uint16_t* bu, int64_t r,
+                          float s, float* ws, uint16_t* h, hipStream_t st) {
+  const float *tg = nullptr, *tu = nullptr;
+  if (r > 0) {
+    // t = s x A^T in K-slices, the slices added in order into t (when split)
+    const int splits = lora_splits(m, k, r);
+    const int tsl = lora_slices(k, splits);
+    const size_t part = ((size_t)tsl * m * r + 63) / 64 * 64, one = ((size_t)m * r + 63) / 64 * 64;
+    float* pg = ws;
+    float* pu = ws + part;
+    hipError_t e = launch_lora_down(x, m, k, ag, r, s, splits, pg, st);
+    if (e == hipSuccess) e = launch_lora_down(x, m, k, au, r, s, splits, pu, st);
+    if (e == hipSuccess && tsl > 1) {
+      float* sgs = ws + 2 * part;
+      float* sus = sgs + one;
+      e = launch_lora_reduce(pg, tsl, m * r, sgs, st);
+      if (e == hipSuccess) e = launch_lora_reduce(pu, tsl, m * r, sus, st);
+      pg = sgs;
+      pu = sus;
+    }
+    if (e != hipSuccess) return e;
+    tg = pg;
+    tu = pu;
+  }
+  const dim3 grid((unsigned)((n + 15) / 16));
+  const int T = gate_up_token_tiles(m);
+#define FP4RL_GATE_UP(TT)                                                                                          \
+  hipLaunchKernelGGL(gate_up_kernel<TT>, grid, dim3(256), 0, st, x, (int)m, (int)n, (int)k, cg, sg, stg, cu, su, \
+                     stu, tg, tu, bg, bu, (int)r, h)
+  if (T == 1) FP4RL_GATE_UP(1);
+  else if (T == 2) FP4RL_GATE_UP(2);
+  else if (T == 4) FP4RL_GATE_UP(4);
+  else FP4RL_GATE_UP(8);
+#undef FP4RL_GATE_UP
+  return hipGetLastError();
+}
+
+// [t_g K-slices][t_u K-slices] and, when split, [t_g][t_u] summed (fp32)
+size_t gate_up_workspace(int64_t m, int64_t k, int64_t r) {
+  if (r <= 0) return 0;
+  const int tsl = lora_slices(k, lora_splits(m, k, r));
+  const size_t part = ((size_t)tsl * m * r + 63) / 64 * 64, one = ((size_t)m * r + 63) / 64 * 64;
+  return 4 * (2 * part + (tsl > 1 ? 2 * one : 0));
+}
+
+}  // namespace fp4rl

@@ -1,0 +1,21 @@
+// Host-side launcher of the fused gate/up projections with the SiLU-gated
+// product (internal to libfp4rl); arguments are validated by the C ABI layer.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace fp4rl {
+
+constexpr int64_t kGateUpMaxTokens = 128;
+// token tiles of 16 per launch for m tokens (1, 2, 4 or 8)
+int gate_up_token_tiles(int64_t m);
+// fp32 workspace bytes: the K-slices of t_g and t_u and, when K is split, their sums
+size_t gate_up_workspace(int64_t m, int64_t k, int64_t r);
+hipError_t launch_gate_up(const uint16_t* x, int64_t m, int64_t n, int64_t k, const uint8_t* cg, const uint8_t* sg,
+                          const float* stg, const uint8_t* cu, const uint8_t* su, const float* stu,
+                          const uint16_t* ag, const uint16_t* bg, const uint16_t* au, const uint16_t* bu, int64_t r,
+                          float s, float* ws, uint16_t* h, hipStream_t stream);
+
+}  // namespace fp4rl

@@ -230,6 +230,29 @@ fp4rl_status fp4rl_fp4_lora_linear_backward(const uint16_t* dy, const uint16_t* 
                                             void* workspace, size_t workspace_bytes, fp4rl_stream stream);
 
 /* ------------------------------------------------------------------------
+ * Gate and up projections in one launch with the SiLU-gated product, for
+ * decode batches. The Qwen2.5 models QeRL trains (QeRL explainer,
+ * experiments) gate their MLP: h = SiLU(gate) * up. Each projection is an
+ * NVFP4 + LoRA linear of the same x (tiled layout, own tensor scale and
+ * adapters):
+ *   h = bf16(SiLU(g) * u),  g = x deq(Wg)^T + s (x Ag^T) Bg^T,  u likewise,
+ * g and u unrounded (fp32), SiLU(v) = v / (1 + exp(-v)).
+ * Arguments: x bf16 [m][k], 1 <= m <= 128 (else FP4RL_ERR_SHAPE); weights
+ *   [n][k] each; adapters A [r][k], B [n][r] bf16, all four NULL or all
+ *   set; h bf16 [m][n]. Shapes and alignment as for fp4rl_fp4_lora_linear.
+ * Workspace: fp4rl_fp4_gate_up_silu_workspace(m, n, k, r) bytes (0 without
+ *   adapters), 256-byte aligned, no initial contents needed (fp32 K-slices
+ *   of t for both projections). */
+size_t fp4rl_fp4_gate_up_silu_workspace(int64_t m, int64_t n, int64_t k, int64_t r);
+fp4rl_status fp4rl_fp4_gate_up_silu(const uint16_t* x, int64_t m, int64_t n, int64_t k, const uint8_t* gate_codes,
+                                    const uint8_t* gate_scales, const float* gate_tensor_scale,
+                                    const uint8_t* up_codes, const uint8_t* up_scales, const float* up_tensor_scale,
+                                    const uint16_t* lora_a_gate, const uint16_t* lora_b_gate,
+                                    const uint16_t* lora_a_up, const uint16_t* lora_b_up, int64_t r,
+                                    float lora_scale, uint16_t* h, void* workspace, size_t workspace_bytes,
+                                    fp4rl_stream stream);
+
+/* ------------------------------------------------------------------------
  * FP8 rollout weights (gist.science summary of adaptive importance sampling
  * for quantized RL, "Problem definition" and "Experimental results": the
  * rollout engine runs in FP8 while the trainer keeps BF16, halving the

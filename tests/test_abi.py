@@ -195,6 +195,31 @@ def test_fp8_rejects_bad_arguments(lib):
     assert call(m=0) == OK and call(n=0) == OK
 
 
+def test_gate_up_rejects_bad_arguments(lib):
+    f = lib.fp4rl_fp4_gate_up_silu
+    ws = lib.fp4rl_fp4_gate_up_silu_workspace(4, 8, 32, 8)
+    assert ws >= 2 * 4 * 8 * 4
+    assert lib.fp4rl_fp4_gate_up_silu_workspace(129, 8, 32, 8) == 0
+    args = dict(x=FAKE, m=4, n=8, k=32, gc=FAKE, gs=FAKE, gt=FAKE, uc=FAKE, us=FAKE, ut=FAKE, ag=FAKE, bg=FAKE,
+                au=FAKE, bu=FAKE, r=8, ls=2.0, h=FAKE, ws=FAKE, wsb=ws)
+
+    def call(**kw):
+        a = dict(args, **kw)
+        return f(a["x"], a["m"], a["n"], a["k"], a["gc"], a["gs"], a["gt"], a["uc"], a["us"], a["ut"], a["ag"],
+                 a["bg"], a["au"], a["bu"], a["r"], a["ls"], a["h"], a["ws"], a["wsb"], None)
+
+    assert call(m=129) == ERR_SHAPE
+    assert call(k=24) == ERR_SHAPE
+    assert call(r=257) == ERR_SHAPE
+    assert call(ls=float("nan")) == ERR_VALUE
+    assert call(au=None) == ERR_NULL
+    assert call(uc=None) == ERR_NULL
+    assert call(h=MIS) == ERR_ALIGN
+    assert call(ut=FAKE + 2) == ERR_ALIGN
+    assert call(wsb=ws - 1) == ERR_WORKSPACE
+    assert call(m=0) == OK and call(n=0) == OK
+
+
 def test_aqn_rejects_bad_arguments(lib):
     f = lib.fp4rl_aqn_rmsnorm
     assert f(FAKE, 4, 512, FAKE, -1.0, 0, 0, 0, 1e-6, FAKE, None, None) == ERR_VALUE

@@ -1,0 +1,60 @@
+"""GPU parity of the fused gate/up projections with the SiLU-gated product vs the oracle."""
+import numpy as np
+import pytest
+import torch
+
+import fp4_quantized_rl_amd as fr
+from oracle import gate_up as gu, nvfp4
+from oracle.numerics import bf16_to_f64, rel_l2
+from workloads import LORA_SCALE, QWEN25_7B, activations_bf16, lora_bf16, normal_f32, tensor_seed
+
+from gpu_util import REL_L2_TOL, bf16_from_dev, bf16_to_dev, device, nvfp4_to_dev, say
+
+pytestmark = pytest.mark.gpu
+
+
+def _run(dev, x, g, u, lg, lu, s):
+    wg, wu = nvfp4_to_dev(*g, dev), nvfp4_to_dev(*u, dev)
+    lgd = tuple(bf16_to_dev(t, dev) for t in lg) if lg is not None else None
+    lud = tuple(bf16_to_dev(t, dev) for t in lu) if lu is not None else None
+    h = fr.fp4_gate_up_silu(bf16_to_dev(x, dev), wg, wu, lgd, lud, s)
+    torch.cuda.synchronize()
+    return bf16_to_f64(bf16_from_dev(h))
+
+
+@pytest.mark.parametrize("shape", [(1, 16, 16, 0), (3, 40, 144, 4), (16, 64, 256, 8), (17, 100, 512, 32),
+                                   (33, 72, 1040, 5), (64, 130, 384, 16), (65, 48, 208, 64), (128, 64, 4112, 8)])
+def test_ragged_shapes(shape):
+    m, n, k, r = shape
+    dev = device()
+    say(f"gate/up SiLU m={m} n={n} k={k} r={r}")
+    seed = m + n + k + r
+    x = activations_bf16(m, k, seed)
+    g = nvfp4.quantize(normal_f32((n, k), 0.05, seed + 1))
+    u = nvfp4.quantize(normal_f32((n, k), 0.05, seed + 2))
+    lg = lora_bf16(r, k, n, seed + 3, std=0.02) if r else None
+    lu = lora_bf16(r, k, n, seed + 4, std=0.02) if r else None
+    got = _run(dev, x, g, u, lg, lu, LORA_SCALE)
+    want = gu.gate_up(x, g, u, *(lg or (None, None)), *(lu or (None, None)), LORA_SCALE)
+    err = rel_l2(got, want)
+    say(f"  rel-L2 {err:.3e}")
+    assert err <= REL_L2_TOL
+
+
+@pytest.mark.parametrize("m", [1, 32, 128])
+def test_full_size_7b(m):
+    """7B gate and up (18944 x 3584), r = 32, x with outlier channels; sampled output features."""
+    dev = device()
+    n, k = QWEN25_7B["gate"]
+    x = activations_bf16(m, k, 50 + m, outlier_frac=0.001)
+    g = nvfp4.quantize(normal_f32((n, k), 0.02, tensor_seed(8, 0, "gate")))
+    u = nvfp4.quantize(normal_f32((n, k), 0.02, tensor_seed(8, 0, "up")))
+    lg = lora_bf16(32, k, n, 51, std=0.01)
+    lu = lora_bf16(32, k, n, 52, std=0.01)
+    say(f"gate/up SiLU 7B {n}x{k}, m={m}")
+    got = _run(dev, x, g, u, lg, lu, LORA_SCALE)
+    rows = np.sort(np.random.default_rng(m).choice(n, 256, replace=False))
+    want = gu.gate_up(x, g, u, *lg, *lu, LORA_SCALE, rows=rows)
+    err = rel_l2(got[:, rows], want)
+    say(f"  rel-L2 {err:.3e}")
+    assert err <= REL_L2_TOL
