@@ -576,6 +576,7 @@ def run_extras(torch, fr, dev, shapes, layer, lora, fp32):
                       "frac_of_bf16_peak": round(flops / dt / 1e12 / BF16_PEAK_TFLOPS, 4)}
     res["lora_backward"] = run_backward(torch, fr, dev, shapes, layer, lora, xs, g, reps)
     res["fp8_linear"] = run_fp8(torch, fr, dev, shapes, lora, xs, g)
+    res["gate_up_silu"] = run_gate_up(torch, fr, dev, shapes, layer, lora, g)
     del xs, ys
 
     # quantiser on 14B shapes: one layer's five matrices, 0.02 t(3) weights with
@@ -711,6 +712,42 @@ def run_fp8(torch, fr, dev, shapes, lora, xs, g):
             out[f"decode_M{m}"] = {"us_per_layer": round(dt * 1e6, 1), "weight_GB/s": round(wbytes / dt / 1e9, 1),
                                    "frac_of_hbm": round(wbytes / dt / 1e9 / HBM_PEAK_GBS, 4)}
         del ys, wss
+    return out
+
+
+def run_gate_up(torch, fr, dev, shapes, layer, lora, g):
+    """The 7B layer's gate and up projections with the SiLU-gated product in one
+    launch, at 1, 8, 32, 64 and 128 tokens, beside the two separate linears
+    (which write gate and up and apply no SiLU)."""
+    n, k = shapes["gate"]
+    wbytes = 2 * nvfp4_bytes(n, k)
+    out = {}
+    for m in TOKENS + (128,):
+        x = torch.randn((m, k), generator=g, device=dev).to(torch.bfloat16)
+        h = torch.empty((m, n), dtype=torch.bfloat16, device=dev)
+        need = fr.fp4_lora_linear_workspace_bytes(m, n, k, RANK)
+        wsa, wsb = fr.linear_workspace(need, dev), fr.linear_workspace(need, dev)
+        ya, yb = torch.empty_like(h), torch.empty_like(h)
+
+        def fused():
+            fr.fp4_gate_up_silu(x, layer["gate"], layer["up"], lora["gate"], lora["up"], LORA_SCALE, out=h)
+
+        def separate():
+            fr.fp4_lora_linear(x, layer["gate"], *lora["gate"], LORA_SCALE, out=ya, workspace=wsa)
+            fr.fp4_lora_linear(x, layer["up"], *lora["up"], LORA_SCALE, out=yb, workspace=wsb)
+
+        res = {}
+        for name, f in (("fused_us", fused), ("two_linears_us", separate)):
+            f()
+            torch.cuda.synchronize()
+            t0 = time.perf_counter()
+            for _ in range(50):
+                f()
+            torch.cuda.synchronize()
+            res[name] = round((time.perf_counter() - t0) / 50 * 1e6, 1)
+        res["fused_weight_GB/s"] = round(wbytes / res["fused_us"] / 1e3, 1)
+        res["fused_frac_of_hbm"] = round(wbytes / res["fused_us"] / 1e3 / HBM_PEAK_GBS, 4)
+        out[f"M{m}"] = res
     return out
 
 

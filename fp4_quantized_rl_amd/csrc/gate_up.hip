@@ -8,9 +8,9 @@
 //   h = bf16(SiLU(g) * u),  g = s_tg acc_g + tg . Bg[n],  u = s_tu acc_u + tu . Bu[n],
 // with g and u kept in fp32 (one rounding, of h), SiLU(v) = v / (1 + e^-v).
 //
-// gate_up_kernel<T>: one workgroup per 16-row weight tile of BOTH matrices
-// (the same output features n); its four waves take the 128-k chunks in
-// turn. Per chunk a lane loads 16 code bytes and 4 scale bytes of each tile
+// gate_up_kernel<T, RT>: one workgroup per RT 16-row weight tiles of BOTH
+// matrices (the same output features n); its four waves take the 128-k
+// chunks in turn. Per chunk a lane loads 16 code bytes and 4 scale bytes of each tile
 // (word j of the tiled layout: row i, k = 32 j + 8 g .. + 7) and, for each of
 // the T token tiles, its 16-byte token fragments (token i, the same k), and
 // issues 4 x T MFMAs per matrix. Each wave scales its sums by the tensor
@@ -79,7 +79,7 @@ __device__ __forceinline__ void lora_mfma(f32x4 (&acc)[T], const float* __restri
   }
 }
 
-template <int T>
+template <int T, int RT>
 __global__ __launch_bounds__(256) void gate_up_kernel(const uint16_t* __restrict__ x, int M, int N, int K,
                                                       const uint8_t* __restrict__ cg, const uint8_t* __restrict__ sg,
                                                       const float* __restrict__ stg, const uint8_t* __restrict__ cu,
@@ -88,25 +88,37 @@ __global__ __launch_bounds__(256) void gate_up_kernel(const uint16_t* __restrict
                                                       const uint16_t* __restrict__ bg,
                                                       const uint16_t* __restrict__ bu, int r,
                                                       uint16_t* __restrict__ h) {
-  __shared__ f32x4 red[4][2 * T][64];
+  __shared__ f32x4 red[4][2 * RT * T][64];
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int li = lane & 15, lg = lane >> 4;
-  const int rt = blockIdx.x, KC = (K + 127) >> 7;
-  const int64_t tile0 = (int64_t)rt * KC;
-  const uint8_t* gcode = cg + tile0 * 1024 + 16 * lane;
-  const uint8_t* ucode = cu + tile0 * 1024 + 16 * lane;
-  const uint8_t* gsc = sg + tile0 * 128 + 4 * (16 * (lg >> 1) + li);
-  const uint8_t* usc = su + tile0 * 128 + 4 * (16 * (lg >> 1) + li);
+  const int KC = (K + 127) >> 7, NT = (N + 15) >> 4;
+  const uint8_t *gcode[RT], *ucode[RT], *gsc[RT], *usc[RT];
+#pragma unroll
+  for (int i = 0; i < RT; ++i) {  // row tiles past the matrix are clamped (never stored)
+    const int64_t tile0 = (int64_t)min(RT * (int)blockIdx.x + i, NT - 1) * KC;
+    gcode[i] = cg + tile0 * 1024 + 16 * lane;
+    ucode[i] = cu + tile0 * 1024 + 16 * lane;
+    gsc[i] = sg + tile0 * 128 + 4 * (16 * (lg >> 1) + li);
+    usc[i] = su + tile0 * 128 + 4 * (16 * (lg >> 1) + li);
+  }
   const uint16_t* xrow[T];  // tokens past M are clamped (their columns are never stored)
 #pragma unroll
   for (int j = 0; j < T; ++j) xrow[j] = x + (int64_t)min(16 * j + li, M - 1) * K + 8 * lg;
-  f32x4 ag[T], au[T];
+  f32x4 ag[RT][T], au[RT][T];
 #pragma unroll
-  for (int j = 0; j < T; ++j) ag[j] = au[j] = f32x4{0.f, 0.f, 0.f, 0.f};
+  for (int i = 0; i < RT; ++i)
+#pragma unroll
+    for (int j = 0; j < T; ++j) ag[i][j] = au[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
   for (int c = wave; c < KC; c += 4) {
-    const uint4 wg = ld_nt16(gcode + (int64_t)c * 1024), wu = ld_nt16(ucode + (int64_t)c * 1024);
-    const uint32_t sgw = *reinterpret_cast<const uint32_t*>(gsc + (int64_t)c * 128);
-    const uint32_t suw = *reinterpret_cast<const uint32_t*>(usc + (int64_t)c * 128);
+    uint4 wg[RT], wu[RT];
+    uint32_t sgw[RT], suw[RT];
+#pragma unroll
+    for (int i = 0; i < RT; ++i) {
+      wg[i] = ld_nt16(gcode[i] + (int64_t)c * 1024);
+      wu[i] = ld_nt16(ucode[i] + (int64_t)c * 1024);
+      sgw[i] = *reinterpret_cast<const uint32_t*>(gsc[i] + (int64_t)c * 128);
+      suw[i] = *reinterpret_cast<const uint32_t*>(usc[i] + (int64_t)c * 128);
+    }
     uint4 xv[4][T];
 #pragma unroll
     for (int st = 0; st < 4; ++st) {
@@ -115,19 +127,22 @@ __global__ __launch_bounds__(256) void gate_up_kernel(const uint16_t* __restrict
       for (int j = 0; j < T; ++j)
         xv[st][j] = k < K ? *reinterpret_cast<const uint4*>(xrow[j] + 128 * c + 32 * st) : make_uint4(0u, 0u, 0u, 0u);
     }
-    const uint32_t cwg[4] = {wg.x, wg.y, wg.z, wg.w}, cwu[4] = {wu.x, wu.y, wu.z, wu.w};
-    float scg[4], scu[4];
-    e4m3_scales(sgw, scg);
-    e4m3_scales(suw, scu);
 #pragma unroll
-    for (int st = 0; st < 4; ++st) {
-      const bf16x8 a_g = dequant8(cwg[st], scg[st]);
-      const bf16x8 a_u = dequant8(cwu[st], scu[st]);
+    for (int i = 0; i < RT; ++i) {
+      const uint32_t cwg[4] = {wg[i].x, wg[i].y, wg[i].z, wg[i].w}, cwu[4] = {wu[i].x, wu[i].y, wu[i].z, wu[i].w};
+      float scg[4], scu[4];
+      e4m3_scales(sgw[i], scg);
+      e4m3_scales(suw[i], scu);
 #pragma unroll
-      for (int j = 0; j < T; ++j) {
-        const bf16x8 b = as_bf16x8(xv[st][j]);
-        ag[j] = mfma16x16x32(a_g, b, ag[j]);
-        au[j] = mfma16x16x32(a_u, b, au[j]);
+      for (int st = 0; st < 4; ++st) {
+        const bf16x8 a_g = dequant8(cwg[st], scg[st]);
+        const bf16x8 a_u = dequant8(cwu[st], scu[st]);
+#pragma unroll
+        for (int j = 0; j < T; ++j) {
+          const bf16x8 b = as_bf16x8(xv[st][j]);
+          ag[i][j] = mfma16x16x32(a_g, b, ag[i][j]);
+          au[i][j] = mfma16x16x32(a_u, b, au[i][j]);
+        }
       }
     }
   }
@@ -135,27 +150,32 @@ __global__ __launch_bounds__(256) void gate_up_kernel(const uint16_t* __restrict
   // added by MFMA, the gate's by wave 0 and the up's by wave 1
   const float sgt = *stg, sut = *stu;
 #pragma unroll
-  for (int j = 0; j < T; ++j) {
-    ag[j] *= sgt;
-    au[j] *= sut;
-  }
-  if (r > 0 && wave == 0) lora_mfma<T>(ag, tg, bg, r, M, N, rt, li, lg);
-  if (r > 0 && wave == 1) lora_mfma<T>(au, tu, bu, r, M, N, rt, li, lg);
+  for (int i = 0; i < RT; ++i) {
 #pragma unroll
-  for (int j = 0; j < T; ++j) {
-    red[wave][j][lane] = ag[j];
-    red[wave][T + j][lane] = au[j];
+    for (int j = 0; j < T; ++j) {
+      ag[i][j] *= sgt;
+      au[i][j] *= sut;
+    }
+    if (r > 0 && wave == 0) lora_mfma<T>(ag[i], tg, bg, r, M, N, RT * (int)blockIdx.x + i, li, lg);
+    if (r > 0 && wave == 1) lora_mfma<T>(au[i], tu, bu, r, M, N, RT * (int)blockIdx.x + i, li, lg);
+#pragma unroll
+    for (int j = 0; j < T; ++j) {
+      red[wave][(2 * i) * T + j][lane] = ag[i][j];
+      red[wave][(2 * i + 1) * T + j][lane] = au[i][j];
+    }
   }
   __syncthreads();
-  // output e = (token tl, feature row rl of the tile): the four waves' sums in
-  // wave order, then the gated product
-  for (int e = threadIdx.x; e < 256 * T; e += 256) {
-    const int tl = e >> 4, rl = e & 15;
-    const int m = tl, n = 16 * rt + rl;
+  // output e = (row tile i, token tl, feature row rl): the four waves' sums
+  // in wave order, then the gated product
+  for (int e = threadIdx.x; e < 256 * RT * T; e += 256) {
+    const int i = e / (256 * T), el = e - i * 256 * T;
+    const int tl = el >> 4, rl = el & 15;
+    const int m = tl, n = 16 * (RT * (int)blockIdx.x + i) + rl;
     if (m >= M || n >= N) continue;
     const int j = tl >> 4, ln = 16 * (rl >> 2) + (tl & 15), v = rl & 3;
-    const float g = ((red[0][j][ln][v] + red[1][j][ln][v]) + red[2][j][ln][v]) + red[3][j][ln][v];
-    const float u = ((red[0][T + j][ln][v] + red[1][T + j][ln][v]) + red[2][T + j][ln][v]) + red[3][T + j][ln][v];
+    const int sg_ = (2 * i) * T + j, su_ = (2 * i + 1) * T + j;
+    const float g = ((red[0][sg_][ln][v] + red[1][sg_][ln][v]) + red[2][sg_][ln][v]) + red[3][sg_][ln][v];
+    const float u = ((red[0][su_][ln][v] + red[1][su_][ln][v]) + red[2][su_][ln][v]) + red[3][su_][ln][v];
     h[(int64_t)m * N + n] = (uint16_t)f32_to_bf16(g / (1.0f + expf(-g)) * u);
   }
 }
@@ -190,15 +210,16 @@ hipError_t launch_gate_up(const uint16_t* x, int64_t m, int64_t n, int64_t k, co
     tg = pg;
     tu = pu;
   }
-  const dim3 grid((unsigned)((n + 15) / 16));
   const int T = gate_up_token_tiles(m);
-#define FP4RL_GATE_UP(TT)                                                                                          \
-  hipLaunchKernelGGL(gate_up_kernel<TT>, grid, dim3(256), 0, st, x, (int)m, (int)n, (int)k, cg, sg, stg, cu, su, \
-                     stu, tg, tu, bg, bu, (int)r, h)
-  if (T == 1) FP4RL_GATE_UP(1);
-  else if (T == 2) FP4RL_GATE_UP(2);
-  else if (T == 4) FP4RL_GATE_UP(4);
-  else FP4RL_GATE_UP(8);
+  const int RT = T == 1 ? 1 : 2;  // row tiles per workgroup: two share each token fragment from 17 tokens on
+  const dim3 grid((unsigned)(((n + 15) / 16 + RT - 1) / RT));
+#define FP4RL_GATE_UP(TT, RR)                                                                                        \
+  hipLaunchKernelGGL((gate_up_kernel<TT, RR>), grid, dim3(256), 0, st, x, (int)m, (int)n, (int)k, cg, sg, stg, cu, \
+                     su, stu, tg, tu, bg, bu, (int)r, h)
+  if (T == 1) FP4RL_GATE_UP(1, 1);
+  else if (T == 2) FP4RL_GATE_UP(2, 2);
+  else if (T == 4) FP4RL_GATE_UP(4, 2);
+  else FP4RL_GATE_UP(8, 2);
 #undef FP4RL_GATE_UP
   return hipGetLastError();
 }
