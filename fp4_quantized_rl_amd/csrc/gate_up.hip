@@ -42,8 +42,9 @@ __device__ __forceinline__ void e4m3_scales(uint32_t w, float (&sc)[4]) {
 // token 16 j + li split into bf16 hi + lo (two MFMAs: t kept to ~2^-17).
 // Rows and tokens past N and M are clamped (never stored), ranks past r zero.
 template <int T>
-__device__ __forceinline__ void lora_mfma(f32x4 (&acc)[T], const float* __restrict__ t,
+__device__ __forceinline__ void lora_mfma(f32x4 (&acc)[T], const float* __restrict__ t, int tsl,
                                           const uint16_t* __restrict__ b, int r, int M, int N, int rt, int li, int lg) {
+  const int64_t tstride = (int64_t)M * r;  // t's K-slices, added in slice order
   const uint16_t* brow = b + (int64_t)min(16 * rt + li, N - 1) * r;
   const bool vec = (r & 7) == 0;
   for (int q0 = 0; q0 < r; q0 += 32) {
@@ -65,11 +66,22 @@ __device__ __forceinline__ void lora_mfma(f32x4 (&acc)[T], const float* __restri
       const float* trow = t + (int64_t)min(16 * j + li, M - 1) * r;
       float tv[8];
       if (vec && q < r) {
-        const float4 t0 = *reinterpret_cast<const float4*>(trow + q), t1 = *reinterpret_cast<const float4*>(trow + q + 4);
+        float4 t0 = *reinterpret_cast<const float4*>(trow + q), t1 = *reinterpret_cast<const float4*>(trow + q + 4);
+        for (int z = 1; z < tsl; ++z) {
+          const float4 u0 = *reinterpret_cast<const float4*>(trow + z * tstride + q);
+          const float4 u1 = *reinterpret_cast<const float4*>(trow + z * tstride + q + 4);
+          t0.x += u0.x; t0.y += u0.y; t0.z += u0.z; t0.w += u0.w;
+          t1.x += u1.x; t1.y += u1.y; t1.z += u1.z; t1.w += u1.w;
+        }
         tv[0] = t0.x; tv[1] = t0.y; tv[2] = t0.z; tv[3] = t0.w; tv[4] = t1.x; tv[5] = t1.y; tv[6] = t1.z; tv[7] = t1.w;
       } else {
 #pragma unroll
-        for (int e = 0; e < 8; ++e) tv[e] = q + e < r ? trow[q + e] : 0.0f;
+        for (int e = 0; e < 8; ++e) {
+          float v = 0.0f;
+          if (q + e < r)
+            for (int z = 0; z < tsl; ++z) v += trow[z * tstride + q + e];
+          tv[e] = v;
+        }
       }
       uint4 th, tl;
       split_bf16x8(tv, th, tl);
@@ -85,7 +97,7 @@ __global__ __launch_bounds__(256) void gate_up_kernel(const uint16_t* __restrict
                                                       const float* __restrict__ stg, const uint8_t* __restrict__ cu,
                                                       const uint8_t* __restrict__ su, const float* __restrict__ stu,
                                                       const float* __restrict__ tg, const float* __restrict__ tu,
-                                                      const uint16_t* __restrict__ bg,
+                                                      int tsl, const uint16_t* __restrict__ bg,
                                                       const uint16_t* __restrict__ bu, int r,
                                                       uint16_t* __restrict__ h) {
   __shared__ f32x4 red[4][2 * RT * T][64];
@@ -156,8 +168,8 @@ __global__ __launch_bounds__(256) void gate_up_kernel(const uint16_t* __restrict
       ag[i][j] *= sgt;
       au[i][j] *= sut;
     }
-    if (r > 0 && wave == 0) lora_mfma<T>(ag[i], tg, bg, r, M, N, RT * (int)blockIdx.x + i, li, lg);
-    if (r > 0 && wave == 1) lora_mfma<T>(au[i], tu, bu, r, M, N, RT * (int)blockIdx.x + i, li, lg);
+    if (r > 0 && wave == 0) lora_mfma<T>(ag[i], tg, tsl, bg, r, M, N, RT * (int)blockIdx.x + i, li, lg);
+    if (r > 0 && wave == 1) lora_mfma<T>(au[i], tu, tsl, bu, r, M, N, RT * (int)blockIdx.x + i, li, lg);
 #pragma unroll
     for (int j = 0; j < T; ++j) {
       red[wave][(2 * i) * T + j][lane] = ag[i][j];
@@ -188,34 +200,35 @@ hipError_t launch_gate_up(const uint16_t* x, int64_t m, int64_t n, int64_t k, co
                           const float* stg, const uint8_t* cu, const uint8_t* su, const float* stu,
                           const uint16_t* ag, const uint16_t* bg, const uint16_t* au, const uint16_t* bu, int64_t r,
                           float s, float* ws, uint16_t* h, hipStream_t st) {
-  const float *tg = nullptr, *tu = nullptr;
-  if (r > 0) {
-    // t = s x A^T in K-slices, the slices added in order into t (when split)
+  float *tg = nullptr, *tu = nullptr;
+  int tsl = 0;
+  if (r > 0) {  // t = s x A^T in K-slices
     const int splits = lora_splits(m, k, r);
-    const int tsl = lora_slices(k, splits);
-    const size_t part = ((size_t)tsl * m * r + 63) / 64 * 64, one = ((size_t)m * r + 63) / 64 * 64;
-    float* pg = ws;
-    float* pu = ws + part;
-    hipError_t e = launch_lora_down(x, m, k, ag, r, s, splits, pg, st);
-    if (e == hipSuccess) e = launch_lora_down(x, m, k, au, r, s, splits, pu, st);
-    if (e == hipSuccess && tsl > 1) {
-      float* sgs = ws + 2 * part;
-      float* sus = sgs + one;
-      e = launch_lora_reduce(pg, tsl, m * r, sgs, st);
-      if (e == hipSuccess) e = launch_lora_reduce(pu, tsl, m * r, sus, st);
-      pg = sgs;
-      pu = sus;
+    tsl = lora_slices(k, splits);
+    const size_t part = ((size_t)tsl * m * r + 63) / 64 * 64;
+    tg = ws;
+    tu = ws + part;
+    hipError_t e = launch_lora_down(x, m, k, ag, r, s, splits, tg, st);
+    if (e == hipSuccess) e = launch_lora_down(x, m, k, au, r, s, splits, tu, st);
+    if (e == hipSuccess && m > 16 && tsl > 1) {
+      // more than one token tile: the slices are added once, in order, by a
+      // reduction launch (up to 16 tokens the kernel adds them itself)
+      float* sg_ = ws + 2 * part;
+      float* su_ = sg_ + ((size_t)m * r + 63) / 64 * 64;
+      e = launch_lora_reduce(tg, tsl, m * r, sg_, st);
+      if (e == hipSuccess) e = launch_lora_reduce(tu, tsl, m * r, su_, st);
+      tg = sg_;
+      tu = su_;
+      tsl = 1;
     }
     if (e != hipSuccess) return e;
-    tg = pg;
-    tu = pu;
   }
   const int T = gate_up_token_tiles(m);
   const int RT = T == 1 ? 1 : 2;  // row tiles per workgroup: two share each token fragment from 17 tokens on
   const dim3 grid((unsigned)(((n + 15) / 16 + RT - 1) / RT));
 #define FP4RL_GATE_UP(TT, RR)                                                                                        \
   hipLaunchKernelGGL((gate_up_kernel<TT, RR>), grid, dim3(256), 0, st, x, (int)m, (int)n, (int)k, cg, sg, stg, cu, \
-                     su, stu, tg, tu, bg, bu, (int)r, h)
+                     su, stu, tg, tu, tsl, bg, bu, (int)r, h)
   if (T == 1) FP4RL_GATE_UP(1, 1);
   else if (T == 2) FP4RL_GATE_UP(2, 2);
   else if (T == 4) FP4RL_GATE_UP(4, 2);
@@ -224,12 +237,12 @@ hipError_t launch_gate_up(const uint16_t* x, int64_t m, int64_t n, int64_t k, co
   return hipGetLastError();
 }
 
-// [t_g K-slices][t_u K-slices] and, when split, [t_g][t_u] summed (fp32)
+// [t_g K-slices][t_u K-slices] and, above 16 tokens with K split, [t_g][t_u] summed (fp32)
 size_t gate_up_workspace(int64_t m, int64_t k, int64_t r) {
   if (r <= 0) return 0;
   const int tsl = lora_slices(k, lora_splits(m, k, r));
   const size_t part = ((size_t)tsl * m * r + 63) / 64 * 64, one = ((size_t)m * r + 63) / 64 * 64;
-  return 4 * (2 * part + (tsl > 1 ? 2 * one : 0));
+  return 4 * (2 * part + (m > 16 && tsl > 1 ? 2 * one : 0));
 }
 
 }  // namespace fp4rl

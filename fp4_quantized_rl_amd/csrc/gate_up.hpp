@@ -11,7 +11,7 @@ namespace fp4rl {
 constexpr int64_t kGateUpMaxTokens = 128;
 // token tiles of 16 per launch for m tokens (1, 2, 4 or 8)
 int gate_up_token_tiles(int64_t m);
-// fp32 workspace bytes: the K-slices of t_g and t_u and, when K is split, their sums
+// fp32 workspace bytes: the K-slices of t_g and t_u (and their sums above 16 tokens)
 size_t gate_up_workspace(int64_t m, int64_t k, int64_t r);
 hipError_t launch_gate_up(const uint16_t* x, int64_t m, int64_t n, int64_t k, const uint8_t* cg, const uint8_t* sg,
                           const float* stg, const uint8_t* cu, const uint8_t* su, const float* stu,
