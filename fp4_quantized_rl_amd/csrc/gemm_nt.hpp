@@ -138,10 +138,12 @@ __global__ __launch_bounds__(256) void nt_gemm_kernel(Seg s1, Seg s2, int M, int
 #pragma unroll
         for (int j = 0; j < 4 * WM; ++j)
           b[j] = as_bf16x8(*reinterpret_cast<const uint4*>(lsl + (64 * WM * wm + 16 * j + li) * kGPitch + 32 * st + 8 * lg));
+        __builtin_amdgcn_s_setprio(1);  // favour this wave's MFMA burst over waves still loading
 #pragma unroll
         for (int i = 0; i < 4; ++i)
 #pragma unroll
           for (int j = 0; j < 4 * WM; ++j) acc[i][j] = mfma16x16x32(a[i], b[j], acc[i][j]);
+        __builtin_amdgcn_s_setprio(0);
       }
     }
   };
