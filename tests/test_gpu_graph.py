@@ -89,3 +89,84 @@ def test_quantizer_graph_replays_match_eager(layout, dtype):
         fr.nvfp4_quantize(other, layout="tiled")  # unrelated eager work in between (its own workspace)
         torch.cuda.synchronize()
     say(f"  quantiser {layout} {dtype}: 4 replays identical to eager")
+
+
+def _replays_match(dev, path, outs, other):
+    path()
+    torch.cuda.synchronize()
+    refs = [o.clone() for o in outs]
+    gr = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(gr):
+        path()
+    for i in range(4):
+        for o in outs:
+            o.zero_()
+        torch.cuda.synchronize()
+        gr.replay()
+        torch.cuda.synchronize()
+        for o, ref in zip(outs, refs):
+            assert torch.equal(o, ref), f"replay {i}: output differs from eager"
+        other()  # unrelated eager work in between
+        torch.cuda.synchronize()
+
+
+@pytest.mark.parametrize("m", [1, 8, 64, 256])
+def test_fp8_linear_graph_replays(m):
+    """Decode (partials + finishing pass) and the one-launch prefill path under capture."""
+    dev = device()
+    n, k, r = 4608, 3584, 32
+    _, x, a, b = _inputs(dev, m, n, k, r, 300 + m)
+    w8 = fr.fp8_quantize(torch.randn((n, k), device=dev).mul_(0.02))
+    y = torch.empty((m, n), dtype=torch.bfloat16, device=dev)
+    ws = torch.empty(max(256, fr.fp8_lora_linear_workspace_bytes(m, n, k, r)), dtype=torch.uint8, device=dev)
+    other = (lambda: fr.fp8_lora_linear(x[:1], w8, a, b, 2.0))
+    _replays_match(dev, lambda: fr.fp8_lora_linear(x, w8, a, b, 2.0, out=y, workspace=ws), [y], other)
+    say(f"  FP8 M={m}: 4 replays identical to eager")
+
+
+@pytest.mark.parametrize("m", [4, 40])
+def test_gate_up_graph_replays(m):
+    dev = device()
+    n, k, r = 4608, 3584, 16
+    wq, x, a, b = _inputs(dev, m, n, k, r, 400 + m)
+    wu, _, a2, b2 = _inputs(dev, m, n, k, r, 500 + m)
+    h = torch.empty((m, n), dtype=torch.bfloat16, device=dev)
+    ws = torch.empty(max(256, fr.load_library().fp4rl_fp4_gate_up_silu_workspace(m, n, k, r)), dtype=torch.uint8,
+                     device=dev)
+    other = (lambda: fr.fp4_gate_up_silu(x[:1], wq, wu, (a, b), (a2, b2), 2.0))
+    _replays_match(dev, lambda: fr.fp4_gate_up_silu(x, wq, wu, (a, b), (a2, b2), 2.0, out=h, workspace=ws), [h],
+                   other)
+    say(f"  gate/up M={m}: 4 replays identical to eager")
+
+
+def test_backward_graph_replays():
+    dev = device()
+    m, n, k, r = 200, 1024, 768, 16
+    wq, x, a, b = _inputs(dev, m, n, k, r, 600)
+    dy = torch.randn((m, n), device=dev).mul_(0.05).to(torch.bfloat16)
+    ws = torch.empty(fr.fp4_lora_linear_backward_workspace_bytes(m, n, k, r), dtype=torch.uint8, device=dev)
+    outs = {}
+
+    def path():
+        outs["r"] = fr.fp4_lora_linear_backward(dy, x, wq, a, b, 2.0, workspace=ws)
+
+    # the call allocates its outputs: the tensors it returns while being
+    # captured (from the graph's memory pool) are the ones every replay writes
+    path()
+    torch.cuda.synchronize()
+    ref = [t.clone() for t in outs["r"]]
+    gr = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(gr):
+        path()
+    got = outs["r"]
+    for i in range(4):
+        for t in got:
+            t.zero_()
+        torch.cuda.synchronize()
+        gr.replay()
+        torch.cuda.synchronize()
+        for t, rf in zip(got, ref):
+            assert torch.equal(t, rf), f"replay {i}: backward output differs from eager"
+        fr.fp4_lora_linear_backward(dy[:8], x[:8], wq, a, b, 2.0)
+        torch.cuda.synchronize()
+    say("  backward: 4 replays identical to eager")
