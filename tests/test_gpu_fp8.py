@@ -106,3 +106,23 @@ def test_linear_full_size_7b_gate(m):
     err = rel_l2(bf16_to_f64(bf16_from_dev(y)[:, rows]), ref)
     say(f"  rel-L2 {err:.3e}")
     assert err <= REL_L2_TOL
+
+
+def test_decode_workspace_reused_across_shapes():
+    """One zero-filled workspace serves a sequence of decode shapes: the per-row-group counters
+    return to zero after every call, so each result equals a call with a fresh workspace."""
+    dev = device()
+    shapes = [(8, 4608, 3584, 32), (3, 520, 1040, 5), (64, 4608, 3584, 16), (1, 96, 272, 0), (33, 4608, 3584, 32)]
+    need = max(fr.fp8_lora_linear_workspace_bytes(m, n, k, r) for m, n, k, r in shapes)
+    ws = torch.zeros(need, dtype=torch.uint8, device=dev)
+    for (m, n, k, r) in shapes:
+        say(f"fp8 decode m={m} n={n} k={k} r={r}, shared workspace")
+        w, x, a, b = _linear_case(m, n, k, r, seed=2 * m + n)
+        w8 = fr.fp8_quantize(f32_to_dev(w, dev))
+        xt = bf16_to_dev(x, dev)
+        at = bf16_to_dev(a, dev) if r else None
+        bt = bf16_to_dev(b, dev) if r else None
+        y_shared = fr.fp8_lora_linear(xt, w8, at, bt, LORA_SCALE, workspace=ws)
+        y_fresh = fr.fp8_lora_linear(xt, w8, at, bt, LORA_SCALE)
+        torch.cuda.synchronize()
+        assert torch.equal(y_shared, y_fresh)
