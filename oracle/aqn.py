@@ -11,7 +11,7 @@ Noise (AQN)":
   additive noise on the weight becomes row-wise multiplicative noise on the
   next linear's input.
 
-Readings taken (listed in the design doc):
+Readings taken:
 
 * the normaliser is the mean of squares (root-MEAN-square; the printed
   equation lost the 1/d) — ``sum_mode=True`` gives the literal printed form;

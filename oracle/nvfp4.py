@@ -13,7 +13,7 @@ What it follows:
   on the E2M1 grid {0, 0.5, 1, 1.5, 2, 3, 4, 6} with a sign bit.
 
 The pages fix neither the scale recipe nor the rounding mode; the readings
-taken here (listed with the rest in the design doc) are:
+taken here are:
 
 1. s_t = fp32(amax / 2688), 2688 = 6 * 448 (largest E2M1 x largest E4M3).
 2. block byte = E4M3 nearest-even, saturating at 448, of
