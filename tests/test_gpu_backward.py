@@ -130,3 +130,9 @@ def test_full_size_7b_gate():
 
 def test_full_size_7b_down():
     _full_size("down", 512, 32, 41)
+
+
+def test_full_size_7b_gate_8192_tokens():
+    """The configuration the bench times: 7B gate, M = 8192, r = 32 (sampled dX columns, all of dA,
+    sampled dB rows)."""
+    _full_size("gate", 8192, 32, 42)
