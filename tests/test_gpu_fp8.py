@@ -87,7 +87,7 @@ def test_linear_ragged(shape):
     assert err <= REL_L2_TOL
 
 
-@pytest.mark.parametrize("m", [1, 32, 1024])
+@pytest.mark.parametrize("m", [1, 32, 1024, 8192])
 def test_linear_full_size_7b_gate(m):
     """GPU quantiser feeding the GPU linear at the 7B gate shape; sampled output columns vs the oracle."""
     dev = device()
