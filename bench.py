@@ -745,6 +745,33 @@ def run_gate_up(torch, fr, dev, shapes, layer, lora, g):
                 f()
             torch.cuda.synchronize()
             res[name] = round((time.perf_counter() - t0) / 50 * 1e6, 1)
+        if m <= 128:
+            # the AQN RMSNorm folded in (raw x in, normalised tokens never stored)
+            # against the norm launch followed by the fused projections
+            wn = torch.ones(k, dtype=torch.float32, device=dev)
+            xn = torch.empty_like(x)
+            aws = torch.empty(max(256, fr.load_library().fp4rl_aqn_gate_up_silu_workspace(m, n, k, RANK)),
+                              dtype=torch.uint8, device=dev)
+            gws = torch.empty(max(256, fr.load_library().fp4rl_fp4_gate_up_silu_workspace(m, n, k, RANK)),
+                              dtype=torch.uint8, device=dev)
+
+            def folded():
+                fr.aqn_gate_up_silu(x, wn, SIGMA, 4, 0, 1, EPS, layer["gate"], layer["up"], lora["gate"],
+                                    lora["up"], LORA_SCALE, out=h, workspace=aws)
+
+            def norm_then_fused():
+                fr.aqn_rmsnorm(x, wn, SIGMA, 4, 0, 1, EPS, out=xn)
+                fr.fp4_gate_up_silu(xn, layer["gate"], layer["up"], lora["gate"], lora["up"], LORA_SCALE, out=h,
+                                    workspace=gws)
+
+            for name, f in (("aqn_folded_us", folded), ("aqn_then_fused_us", norm_then_fused)):
+                f()
+                torch.cuda.synchronize()
+                t0 = time.perf_counter()
+                for _ in range(50):
+                    f()
+                torch.cuda.synchronize()
+                res[name] = round((time.perf_counter() - t0) / 50 * 1e6, 1)
         res["fused_weight_GB/s"] = round(wbytes / res["fused_us"] / 1e3, 1)
         res["fused_frac_of_hbm"] = round(wbytes / res["fused_us"] / 1e3 / HBM_PEAK_GBS, 4)
         out[f"M{m}"] = res

@@ -29,6 +29,7 @@ __all__ = [
     "LIB_PATH", "Fp4rlError", "load_library", "NVFP4Weight", "nvfp4_empty", "nvfp4_quantize", "nvfp4_to_tiled",
     "fp4_lora_linear", "fp4_lora_linear_backward", "fp4_lora_linear_backward_workspace_bytes",
     "FP8Weight", "fp8_quantize", "fp8_lora_linear", "fp8_lora_linear_workspace_bytes", "fp4_gate_up_silu",
+    "aqn_gate_up_silu",
     "lora_down", "fp4_linear_lora_up", "fp4_linear_kernel_name", "linear_workspace",
     "fp4_lora_linear_workspace_bytes", "fp4_linear_lora_up_workspace_bytes", "aqn_sigma", "aqn_rmsnorm", "philox_words",
     "EXPORTED_SYMBOLS",
@@ -67,6 +68,10 @@ _SIGNATURES = {
     "fp4rl_fp4_linear_kernel_name": (_c.c_char_p, [_I64, _I64, _I64, _I64]),
     "fp4rl_fp4_gate_up_silu_workspace": (_c.c_size_t, [_I64, _I64, _I64, _I64]),
     "fp4rl_fp4_gate_up_silu": (_STATUS, [_P, _I64, _I64, _I64, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _I64,
+                                         _c.c_float, _P, _P, _c.c_size_t, _P]),
+    "fp4rl_aqn_gate_up_silu_workspace": (_c.c_size_t, [_I64, _I64, _I64, _I64]),
+    "fp4rl_aqn_gate_up_silu": (_STATUS, [_P, _I64, _I64, _I64, _P, _c.c_float, _c.c_uint64, _c.c_uint64,
+                                         _c.c_uint32, _c.c_float, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _I64,
                                          _c.c_float, _P, _P, _c.c_size_t, _P]),
     "fp4rl_fp8_quantize": (_STATUS, [_P, _c.c_int32, _I64, _I64, _P, _P, _P]),
     "fp4rl_fp8_lora_linear_workspace": (_c.c_size_t, [_I64, _I64, _I64, _I64]),
@@ -305,6 +310,42 @@ def fp4_gate_up_silu(x, wg: NVFP4Weight, wu: NVFP4Weight, lora_gate=None, lora_u
                                           *[_ptr(p) for p in ptrs], r, float(lora_scale), _ptr(out),
                                           _ptr(workspace), 0 if workspace is None else workspace.numel(),
                                           _stream(x.device)), "fp4_gate_up_silu")
+    return out
+
+
+def aqn_gate_up_silu(x, norm_w, sigma: float, seed: int, step: int, norm_id: int, eps: float, wg: NVFP4Weight,
+                     wu: NVFP4Weight, lora_gate=None, lora_up=None, lora_scale: float = 0.0, out=None,
+                     workspace=None):
+    """fp4_gate_up_silu of the AQN RMSNorm of x (raw bf16 [m <= 128, k]), the norm folded in (never stored)."""
+    torch = _torch()
+    m, n, k = _linear_args(x, wg)
+    _linear_args(x, wu)
+    _dev_tensor(norm_w, "norm_w", (torch.float32,), 1)
+    if norm_w.shape[0] != k or wu.n != n:
+        raise ValueError("norm_w must be [k] and the gate and up weights the same shape")
+    r = 0
+    ptrs = [None] * 4
+    if lora_gate is not None or lora_up is not None:
+        (ag, bg), (au, bu) = lora_gate, lora_up
+        for t, nm in ((ag, "lora_a_gate"), (bg, "lora_b_gate"), (au, "lora_a_up"), (bu, "lora_b_up")):
+            _dev_tensor(t, nm, (torch.bfloat16,), 2)
+        r = ag.shape[0]
+        if ag.shape != (r, k) or au.shape != (r, k) or bg.shape != (n, r) or bu.shape != (n, r):
+            raise ValueError("LoRA shapes must be A [r, k] and B [n, r] for both projections")
+        ptrs = [ag, bg, au, bu]
+    if out is None:
+        out = torch.empty((m, n), dtype=torch.bfloat16, device=x.device)
+    lib = load_library()
+    need = lib.fp4rl_aqn_gate_up_silu_workspace(m, n, k, r)
+    if workspace is None:
+        workspace = torch.empty(max(need, 256), dtype=torch.uint8, device=x.device)
+    with torch.cuda.device(x.device):
+        _check(lib.fp4rl_aqn_gate_up_silu(_ptr(x), m, n, k, _ptr(norm_w), float(sigma), int(seed), int(step),
+                                          int(norm_id), float(eps), _ptr(wg.codes), _ptr(wg.scales),
+                                          _ptr(wg.tensor_scale), _ptr(wu.codes), _ptr(wu.scales),
+                                          _ptr(wu.tensor_scale), *[_ptr(p) for p in ptrs], r, float(lora_scale),
+                                          _ptr(out), _ptr(workspace), workspace.numel(), _stream(x.device)),
+               "aqn_gate_up_silu")
     return out
 
 

@@ -456,6 +456,57 @@ fp4rl_status fp4rl_fp4_gate_up_silu(const uint16_t* x, int64_t m, int64_t n, int
                   "fp4_gate_up_silu");
 }
 
+size_t fp4rl_aqn_gate_up_silu_workspace(int64_t m, int64_t n, int64_t k, int64_t r) {
+  if (check_linear_shape(m, n, k, r) != FP4RL_OK || m == 0 || n == 0 || m > fp4rl::kGateUpMaxTokens ||
+      k > fp4rl::kAqnMaxD)
+    return 0;
+  return fp4rl::aqn_gate_up_workspace(m, k, r);
+}
+
+fp4rl_status fp4rl_aqn_gate_up_silu(const uint16_t* x, int64_t m, int64_t n, int64_t k, const float* norm_w,
+                                    float sigma, uint64_t seed, uint64_t step, uint32_t norm_id, float eps,
+                                    const uint8_t* gate_codes, const uint8_t* gate_scales,
+                                    const float* gate_tensor_scale, const uint8_t* up_codes, const uint8_t* up_scales,
+                                    const float* up_tensor_scale, const uint16_t* lora_a_gate,
+                                    const uint16_t* lora_b_gate, const uint16_t* lora_a_up, const uint16_t* lora_b_up,
+                                    int64_t r, float lora_scale, uint16_t* h, void* workspace,
+                                    size_t workspace_bytes, fp4rl_stream stream) {
+  FP4RL_CHECK(check_linear_shape(m, n, k, r));
+  FP4RL_REQUIRE(m <= fp4rl::kGateUpMaxTokens, FP4RL_ERR_SHAPE, "m=%lld exceeds %lld tokens", (long long)m,
+                (long long)fp4rl::kGateUpMaxTokens);
+  FP4RL_REQUIRE(k <= fp4rl::kAqnMaxD, FP4RL_ERR_SHAPE, "k=%lld exceeds the norm's width %lld", (long long)k,
+                (long long)fp4rl::kAqnMaxD);
+  FP4RL_REQUIRE(std::isfinite(lora_scale), FP4RL_ERR_VALUE, "lora_scale is not finite");
+  FP4RL_REQUIRE(std::isfinite(sigma) && sigma >= 0.0f, FP4RL_ERR_VALUE, "sigma must be finite and >= 0");
+  FP4RL_REQUIRE(std::isfinite(eps) && eps >= 0.0f, FP4RL_ERR_VALUE, "eps must be finite and >= 0");
+  const bool any = lora_a_gate || lora_b_gate || lora_a_up || lora_b_up;
+  const bool all = lora_a_gate && lora_b_gate && lora_a_up && lora_b_up;
+  FP4RL_REQUIRE(any == all, FP4RL_ERR_NULL, "the four adapters must all be NULL or all be set");
+  if (!all) r = 0;
+  if (m == 0 || n == 0) return ok();
+  FP4RL_REQUIRE(x && norm_w && gate_codes && gate_scales && gate_tensor_scale && up_codes && up_scales &&
+                    up_tensor_scale && h,
+                FP4RL_ERR_NULL, "x, the norm weight, both weights and h must be non-NULL");
+  FP4RL_REQUIRE(aligned(x, 16) && aligned(norm_w, 16) && aligned(gate_codes, 16) && aligned(gate_scales, 16) &&
+                    aligned(up_codes, 16) && aligned(up_scales, 16) && aligned(h, 16) &&
+                    aligned(gate_tensor_scale, 4) && aligned(up_tensor_scale, 4),
+                FP4RL_ERR_ALIGN, "x, norm_w, codes, scales and h must be 16-byte aligned, tensor scales 4-byte aligned");
+  if (r > 0)
+    FP4RL_REQUIRE(aligned(lora_a_gate, 16) && aligned(lora_b_gate, 16) && aligned(lora_a_up, 16) &&
+                      aligned(lora_b_up, 16),
+                  FP4RL_ERR_ALIGN, "adapters must be 16-byte aligned");
+  const size_t need = fp4rl::aqn_gate_up_workspace(m, k, r);
+  FP4RL_REQUIRE(workspace != nullptr && workspace_bytes >= need, FP4RL_ERR_WORKSPACE, "workspace %zu < %zu bytes",
+                workspace_bytes, need);
+  FP4RL_REQUIRE(aligned(workspace, 256), FP4RL_ERR_ALIGN, "workspace must be 256-byte aligned");
+  FP4RL_CHECK(check_device());
+  return launched(fp4rl::launch_aqn_gate_up(x, m, n, k, norm_w, sigma, seed, step, norm_id, eps, gate_codes,
+                                            gate_scales, gate_tensor_scale, up_codes, up_scales, up_tensor_scale,
+                                            lora_a_gate, lora_b_gate, lora_a_up, lora_b_up, r, lora_scale, workspace,
+                                            h, stream),
+                  "aqn_gate_up_silu");
+}
+
 // --------------------------------------------------------------------- FP8 --
 
 fp4rl_status fp4rl_fp8_quantize(const void* w, int32_t w_dtype, int64_t n, int64_t k, uint8_t* codes,

@@ -38,7 +38,24 @@ __device__ __forceinline__ void e4m3_scales(uint32_t w, float (&sc)[4]) {
   sc[3] = __builtin_amdgcn_cvt_f32_fp8((int)w, 3);
 }
 
-template <int T, int RT>
+// One 8-value token fragment of x, optionally normalised on the way in:
+// bf16((x r_m) w_k), the AQN RMSNorm's rounding and order of operations
+// (r_m = 1 / sqrt(mean x^2 + eps), w = w + sigma z the noisy weight).
+template <bool NORM>
+__device__ __forceinline__ uint4 token_fragment(const uint16_t* p, float rinv, const float* wn) {
+  const uint4 v = *reinterpret_cast<const uint4*>(p);
+  if constexpr (!NORM) {
+    return v;
+  } else {
+    const float4 w0 = *reinterpret_cast<const float4*>(wn), w1 = *reinterpret_cast<const float4*>(wn + 4);
+    return make_uint4(pack_bf16x2(bf16_lo(v.x) * rinv * w0.x, bf16_hi(v.x) * rinv * w0.y),
+                      pack_bf16x2(bf16_lo(v.y) * rinv * w0.z, bf16_hi(v.y) * rinv * w0.w),
+                      pack_bf16x2(bf16_lo(v.z) * rinv * w1.x, bf16_hi(v.z) * rinv * w1.y),
+                      pack_bf16x2(bf16_lo(v.w) * rinv * w1.z, bf16_hi(v.w) * rinv * w1.w));
+  }
+}
+
+template <int T, int RT, bool NORM = false>
 __global__ __launch_bounds__(256) void gate_up_kernel(const uint16_t* __restrict__ x, int M, int N, int K,
                                                       const uint8_t* __restrict__ cg, const uint8_t* __restrict__ sg,
                                                       const float* __restrict__ stg, const uint8_t* __restrict__ cu,
@@ -46,7 +63,8 @@ __global__ __launch_bounds__(256) void gate_up_kernel(const uint16_t* __restrict
                                                       const float* __restrict__ tg, const float* __restrict__ tu,
                                                       int tsl, const uint16_t* __restrict__ bg,
                                                       const uint16_t* __restrict__ bu, int r,
-                                                      uint16_t* __restrict__ h) {
+                                                      uint16_t* __restrict__ h, const float* __restrict__ wn,
+                                                      const float* __restrict__ rinv) {
   __shared__ f32x4 red[4][2 * RT * T][64];
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int li = lane & 15, lg = lane >> 4;
@@ -61,8 +79,12 @@ __global__ __launch_bounds__(256) void gate_up_kernel(const uint16_t* __restrict
     usc[i] = su + tile0 * 128 + 4 * (16 * (lg >> 1) + li);
   }
   const uint16_t* xrow[T];  // tokens past M are clamped (their columns are never stored)
+  float rv[T];
 #pragma unroll
-  for (int j = 0; j < T; ++j) xrow[j] = x + (int64_t)min(16 * j + li, M - 1) * K + 8 * lg;
+  for (int j = 0; j < T; ++j) {
+    xrow[j] = x + (int64_t)min(16 * j + li, M - 1) * K + 8 * lg;
+    rv[j] = NORM ? rinv[min(16 * j + li, M - 1)] : 1.0f;
+  }
   f32x4 ag[RT][T], au[RT][T];
 #pragma unroll
   for (int i = 0; i < RT; ++i)
@@ -84,7 +106,7 @@ __global__ __launch_bounds__(256) void gate_up_kernel(const uint16_t* __restrict
       const int k = 128 * c + 32 * st + 8 * lg;  // K % 16 == 0: 8 values all in or all out
 #pragma unroll
       for (int j = 0; j < T; ++j)
-        xv[st][j] = k < K ? *reinterpret_cast<const uint4*>(xrow[j] + 128 * c + 32 * st) : make_uint4(0u, 0u, 0u, 0u);
+        xv[st][j] = k < K ? token_fragment<NORM>(xrow[j] + 128 * c + 32 * st, rv[j], wn + k) : make_uint4(0u, 0u, 0u, 0u);
     }
 #pragma unroll
     for (int i = 0; i < RT; ++i) {
@@ -139,6 +161,92 @@ __global__ __launch_bounds__(256) void gate_up_kernel(const uint16_t* __restrict
   }
 }
 
+// The AQN RMSNorm folded into the LoRA down-projections of gate and up: one
+// workgroup per 16-token tile, 16-rank tile, adapter and K-slice (blockIdx.z
+// = 2 slice + adapter). Its waves first take 4 tokens each for their sum of
+// squares (16-byte loads, all issued before the sums; r_m = 1 / sqrt(ss / K
+// + eps), the norm's formula; the (., 0, 0) workgroup writes r_m for the
+// projections), then take the slice's 32-k steps in turn, loading all their
+// fragments before the MFMAs: A operand = adapter row li (k = 32 s + 8 g ..
+// + 7), B operand = the normalised token fragment; the waves' sums are
+// added in wave order into t's K-slice. With r == 0 only r_m is made.
+// t = s xn A^T in K-slices; xn is never stored.
+constexpr int kNormLoraSteps = 4;  // 32-k steps per wave and slice (at most)
+
+__global__ __launch_bounds__(256) void norm_lora_down_kernel(const uint16_t* __restrict__ x, int M, int K,
+                                                             const float* __restrict__ wn, float eps,
+                                                             const uint16_t* __restrict__ ag,
+                                                             const uint16_t* __restrict__ au, int r, float s,
+                                                             int kslice, float* __restrict__ rinv,
+                                                             float* __restrict__ tg, float* __restrict__ tu) {
+  __shared__ float rs[16];
+  __shared__ f32x4 red[3][64];
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int li = lane & 15, lg = lane >> 4;
+  const int m0 = 16 * blockIdx.x, j0 = 16 * blockIdx.y;
+  const int adapter = blockIdx.z & 1, z = blockIdx.z >> 1;
+  const int nv = K >> 3;  // 16-byte pieces per token row
+  float ss[4] = {0.f, 0.f, 0.f, 0.f};
+  for (int c = lane; c < nv; c += 64) {
+    uint4 v[4];
+#pragma unroll
+    for (int q = 0; q < 4; ++q)
+      v[q] = *reinterpret_cast<const uint4*>(x + (int64_t)min(m0 + 4 * wave + q, M - 1) * K + 8 * c);
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const uint32_t w4[4] = {v[q].x, v[q].y, v[q].z, v[q].w};
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const float lo = bf16_lo(w4[e]), hi = bf16_hi(w4[e]);
+        ss[q] += lo * lo;
+        ss[q] += hi * hi;
+      }
+    }
+  }
+  const float inv_k = 1.0f / (float)K;
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    const float t = wave_sum(ss[q]);
+    if (lane == 0) rs[4 * wave + q] = 1.0f / sqrtf(t * inv_k + eps);
+  }
+  __syncthreads();
+  if (blockIdx.y == 0 && blockIdx.z == 0 && threadIdx.x < 16 && m0 + (int)threadIdx.x < M)
+    rinv[m0 + threadIdx.x] = rs[threadIdx.x];
+  if (r == 0) return;
+  const uint16_t* a = adapter == 0 ? ag : au;
+  float* t = (adapter == 0 ? tg : tu) + (int64_t)z * M * r;
+  const uint16_t* arow = a + (int64_t)min(j0 + li, r - 1) * K + 8 * lg;
+  const uint16_t* xrow = x + (int64_t)min(m0 + li, M - 1) * K + 8 * lg;
+  const float rm = rs[li];
+  const int k0 = z * kslice, k1 = min(K, k0 + kslice);
+  uint4 av[kNormLoraSteps], xv[kNormLoraSteps];
+#pragma unroll
+  for (int u = 0; u < kNormLoraSteps; ++u) {
+    const int k = k0 + 32 * (wave + 4 * u) + 8 * lg;  // K % 16 == 0: 8 values all in or all out
+    const bool in = k < k1;                            // lanes past the slice give zero operands
+    av[u] = in ? *reinterpret_cast<const uint4*>(arow + k - 8 * lg) : make_uint4(0u, 0u, 0u, 0u);
+    xv[u] = in ? token_fragment<true>(xrow + k - 8 * lg, rm, wn + k) : make_uint4(0u, 0u, 0u, 0u);
+  }
+  f32x4 acc = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int u = 0; u < kNormLoraSteps; ++u) acc = mfma16x16x32(as_bf16x8(av[u]), as_bf16x8(xv[u]), acc);
+  if (wave > 0) red[wave - 1][lane] = acc;
+  __syncthreads();
+  if (wave > 0) return;
+  acc = ((acc + red[0][lane]) + red[1][lane]) + red[2][lane];
+  // lane holds ranks j0 + 4 g + v of token m0 + li
+  const int m = m0 + li;
+  if (m >= M) return;
+#pragma unroll
+  for (int v = 0; v < 4; ++v) {
+    const int j = j0 + 4 * lg + v;
+    if (j < r) t[(int64_t)m * r + j] = s * acc[v];
+  }
+}
+
+// K-slices of the normalising LoRA down-projection: 4 waves x 4 steps of 32
+int norm_lora_slices(int64_t k) { return (int)((k + 32 * 4 * kNormLoraSteps - 1) / (32 * 4 * kNormLoraSteps)); }
+
 }  // namespace
 
 int gate_up_token_tiles(int64_t m) { return m <= 16 ? 1 : m <= 32 ? 2 : m <= 64 ? 4 : 8; }
@@ -175,7 +283,7 @@ hipError_t launch_gate_up(const uint16_t* x, int64_t m, int64_t n, int64_t k, co
   const dim3 grid((unsigned)(((n + 15) / 16 + RT - 1) / RT));
 #define FP4RL_GATE_UP(TT, RR)                                                                                        \
   hipLaunchKernelGGL((gate_up_kernel<TT, RR>), grid, dim3(256), 0, st, x, (int)m, (int)n, (int)k, cg, sg, stg, cu, \
-                     su, stu, tg, tu, tsl, bg, bu, (int)r, h)
+                     su, stu, tg, tu, tsl, bg, bu, (int)r, h, nullptr, nullptr)
   if (T == 1) FP4RL_GATE_UP(1, 1);
   else if (T == 2) FP4RL_GATE_UP(2, 2);
   else if (T == 4) FP4RL_GATE_UP(4, 2);
@@ -190,6 +298,46 @@ size_t gate_up_workspace(int64_t m, int64_t k, int64_t r) {
   const int tsl = lora_slices(k, lora_splits(m, k, r));
   const size_t part = ((size_t)tsl * m * r + 63) / 64 * 64, one = ((size_t)m * r + 63) / 64 * 64;
   return 4 * (2 * part + (m > 16 && tsl > 1 ? 2 * one : 0));
+}
+
+// [w_noise: k][r_m: m][t_g K-slices: S m r][t_u K-slices: S m r] (fp32, each 256-byte aligned)
+size_t aqn_gate_up_workspace(int64_t m, int64_t k, int64_t r) {
+  auto a = [](size_t v) { return (v * 4 + 255) / 256 * 256; };
+  return a((size_t)k) + a((size_t)m) + 2 * a((size_t)norm_lora_slices(k) * m * r);
+}
+
+hipError_t launch_aqn_gate_up(const uint16_t* x, int64_t m, int64_t n, int64_t k, const float* norm_w, float sigma,
+                              uint64_t seed, uint64_t step, uint32_t norm_id, float eps, const uint8_t* cg,
+                              const uint8_t* sg, const float* stg, const uint8_t* cu, const uint8_t* su,
+                              const float* stu, const uint16_t* ag, const uint16_t* bg, const uint16_t* au,
+                              const uint16_t* bu, int64_t r, float s, void* ws, uint16_t* h, hipStream_t st) {
+  auto a = [](size_t v) { return (v * 4 + 255) / 256 * 256; };
+  uint8_t* base = static_cast<uint8_t*>(ws);
+  float* wn = reinterpret_cast<float*>(base);
+  float* rinv = reinterpret_cast<float*>(base + a((size_t)k));
+  const int S = norm_lora_slices(k);
+  float* tg = reinterpret_cast<float*>(base + a((size_t)k) + a((size_t)m));
+  float* tu = reinterpret_cast<float*>(base + a((size_t)k) + a((size_t)m) + a((size_t)S * m * r));
+  // the noisy norm weight w + sigma z (no rows: the norm kernel's noise prologue alone)
+  hipError_t e = launch_aqn_rmsnorm(nullptr, 0, k, norm_w, sigma, seed, step, norm_id, eps, nullptr, wn, st);
+  if (e != hipSuccess) return e;
+  const dim3 lgrid((unsigned)((m + 15) / 16), (unsigned)(r > 0 ? (r + 15) / 16 : 1), r > 0 ? 2u * S : 1u);
+  hipLaunchKernelGGL(norm_lora_down_kernel, lgrid, dim3(256), 0, st, x, (int)m, (int)k, wn, eps, ag, au, (int)r, s,
+                     32 * 4 * kNormLoraSteps, rinv, tg, tu);
+  if ((e = hipGetLastError()) != hipSuccess) return e;
+  const int T = gate_up_token_tiles(m);
+  const int RT = T == 1 ? 1 : 2;
+  const dim3 grid((unsigned)(((n + 15) / 16 + RT - 1) / RT));
+  const int tsl = r > 0 ? S : 0;
+#define FP4RL_AQN_GATE_UP(TT, RR)                                                                                   \
+  hipLaunchKernelGGL((gate_up_kernel<TT, RR, true>), grid, dim3(256), 0, st, x, (int)m, (int)n, (int)k, cg, sg, stg, \
+                     cu, su, stu, tg, tu, tsl, bg, bu, (int)r, h, wn, rinv)
+  if (T == 1) FP4RL_AQN_GATE_UP(1, 1);
+  else if (T == 2) FP4RL_AQN_GATE_UP(2, 2);
+  else if (T == 4) FP4RL_AQN_GATE_UP(4, 2);
+  else FP4RL_AQN_GATE_UP(8, 2);
+#undef FP4RL_AQN_GATE_UP
+  return hipGetLastError();
 }
 
 }  // namespace fp4rl

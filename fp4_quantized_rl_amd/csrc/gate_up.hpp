@@ -18,4 +18,14 @@ hipError_t launch_gate_up(const uint16_t* x, int64_t m, int64_t n, int64_t k, co
                           const uint16_t* ag, const uint16_t* bg, const uint16_t* au, const uint16_t* bu, int64_t r,
                           float s, float* ws, uint16_t* h, hipStream_t stream);
 
+// The AQN RMSNorm of x folded in: the noisy weight (k fp32) and r_m (m fp32)
+// in the workspace, then t_g and t_u (m r fp32 each); the normalised tokens
+// are never stored. k <= the norm's width limit, k % 16 == 0.
+size_t aqn_gate_up_workspace(int64_t m, int64_t k, int64_t r);
+hipError_t launch_aqn_gate_up(const uint16_t* x, int64_t m, int64_t n, int64_t k, const float* norm_w, float sigma,
+                              uint64_t seed, uint64_t step, uint32_t norm_id, float eps, const uint8_t* cg,
+                              const uint8_t* sg, const float* stg, const uint8_t* cu, const uint8_t* su,
+                              const float* stu, const uint16_t* ag, const uint16_t* bg, const uint16_t* au,
+                              const uint16_t* bu, int64_t r, float s, void* ws, uint16_t* h, hipStream_t stream);
+
 }  // namespace fp4rl

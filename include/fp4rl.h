@@ -252,6 +252,26 @@ fp4rl_status fp4rl_fp4_gate_up_silu(const uint16_t* x, int64_t m, int64_t n, int
                                     float lora_scale, uint16_t* h, void* workspace, size_t workspace_bytes,
                                     fp4rl_stream stream);
 
+/* fp4rl_aqn_gate_up_silu: the same with the AQN RMSNorm of x folded in (QeRL
+ * explainer, "zero overhead: folding into layer normalization"): x is the
+ * raw bf16 input [m][k]; the projections see xn = bf16(x r_m (w + sigma z)),
+ * r_m = 1 / sqrt(mean_k x^2 + eps), z the Philox normals of
+ * (seed, step, norm_id) as in fp4rl_aqn_rmsnorm (norm_w fp32 [k],
+ * k <= 16384). xn is never stored: the LoRA down-projections and the
+ * projections normalise their fragments as they load them. Three launches
+ * (noise vector, normalising LoRA down-projection, gate/up).
+ * Workspace: fp4rl_aqn_gate_up_silu_workspace(m, n, k, r) bytes, 256-byte
+ *   aligned, no initial contents needed. */
+size_t fp4rl_aqn_gate_up_silu_workspace(int64_t m, int64_t n, int64_t k, int64_t r);
+fp4rl_status fp4rl_aqn_gate_up_silu(const uint16_t* x, int64_t m, int64_t n, int64_t k, const float* norm_w,
+                                    float sigma, uint64_t seed, uint64_t step, uint32_t norm_id, float eps,
+                                    const uint8_t* gate_codes, const uint8_t* gate_scales,
+                                    const float* gate_tensor_scale, const uint8_t* up_codes, const uint8_t* up_scales,
+                                    const float* up_tensor_scale, const uint16_t* lora_a_gate,
+                                    const uint16_t* lora_b_gate, const uint16_t* lora_a_up, const uint16_t* lora_b_up,
+                                    int64_t r, float lora_scale, uint16_t* h, void* workspace,
+                                    size_t workspace_bytes, fp4rl_stream stream);
+
 /* ------------------------------------------------------------------------
  * FP8 rollout weights (gist.science summary of adaptive importance sampling
  * for quantized RL, "Problem definition" and "Experimental results": the

@@ -58,3 +58,64 @@ def test_full_size_7b(m):
     err = rel_l2(got[:, rows], want)
     say(f"  rel-L2 {err:.3e}")
     assert err <= REL_L2_TOL
+
+
+def _aqn_case(m, k, seed):
+    x = activations_bf16(m, k, seed)
+    w = (1.0 + 0.1 * np.random.default_rng(seed).standard_normal(k)).astype(np.float32)
+    return x, w
+
+
+@pytest.mark.parametrize("shape", [(1, 16, 64, 0), (5, 40, 144, 4), (16, 64, 1040, 8), (40, 100, 512, 32),
+                                   (128, 64, 256, 5)])
+def test_aqn_folded_ragged(shape):
+    """The AQN RMSNorm folded into gate/up equals the norm oracle feeding the gate/up oracle."""
+    from oracle import aqn
+    from oracle.numerics import bf16_bits_of
+
+    m, n, k, r = shape
+    dev = device()
+    say(f"AQN-folded gate/up SiLU m={m} n={n} k={k} r={r}")
+    seed = 7 * m + n + k + r
+    x, w = _aqn_case(m, k, seed)
+    sigma, rseed, step, norm_id, eps = 1e-2, 3, 1, 5, 1e-6
+    g = nvfp4.quantize(normal_f32((n, k), 0.05, seed + 1))
+    u = nvfp4.quantize(normal_f32((n, k), 0.05, seed + 2))
+    lg = lora_bf16(r, k, n, seed + 3, std=0.02) if r else None
+    lu = lora_bf16(r, k, n, seed + 4, std=0.02) if r else None
+    wg, wu = nvfp4_to_dev(*g, dev), nvfp4_to_dev(*u, dev)
+    lgd = tuple(bf16_to_dev(t, dev) for t in lg) if r else None
+    lud = tuple(bf16_to_dev(t, dev) for t in lu) if r else None
+    h = fr.aqn_gate_up_silu(bf16_to_dev(x, dev), torch.from_numpy(w).to(dev), sigma, rseed, step, norm_id, eps, wg,
+                            wu, lgd, lud, LORA_SCALE)
+    torch.cuda.synchronize()
+    xn, _ = aqn.aqn_rmsnorm(x, w, sigma, rseed, step, norm_id, eps)
+    want = gu.gate_up(bf16_bits_of(xn), g, u, *(lg or (None, None)), *(lu or (None, None)), LORA_SCALE)
+    err = rel_l2(bf16_to_f64(bf16_from_dev(h)), want)
+    say(f"  rel-L2 {err:.3e}")
+    assert err <= REL_L2_TOL
+
+
+@pytest.mark.parametrize("m", [1, 16])
+def test_aqn_folded_full_size_7b(m):
+    from oracle import aqn
+    from oracle.numerics import bf16_bits_of
+
+    dev = device()
+    n, k = QWEN25_7B["gate"]
+    x, w = _aqn_case(m, k, 60 + m)
+    g = nvfp4.quantize(normal_f32((n, k), 0.02, tensor_seed(9, 0, "gate")))
+    u = nvfp4.quantize(normal_f32((n, k), 0.02, tensor_seed(9, 0, "up")))
+    lg = lora_bf16(32, k, n, 61, std=0.01)
+    lu = lora_bf16(32, k, n, 62, std=0.01)
+    say(f"AQN-folded gate/up SiLU 7B {n}x{k}, m={m}")
+    h = fr.aqn_gate_up_silu(bf16_to_dev(x, dev), torch.from_numpy(w).to(dev), 1e-2, 4, 0, 2, 1e-6,
+                            nvfp4_to_dev(*g, dev), nvfp4_to_dev(*u, dev),
+                            tuple(bf16_to_dev(t, dev) for t in lg), tuple(bf16_to_dev(t, dev) for t in lu), LORA_SCALE)
+    torch.cuda.synchronize()
+    xn, _ = aqn.aqn_rmsnorm(x, w, 1e-2, 4, 0, 2, 1e-6)
+    rows = np.sort(np.random.default_rng(m).choice(n, 256, replace=False))
+    want = gu.gate_up(bf16_bits_of(xn), g, u, *lg, *lu, LORA_SCALE, rows=rows)
+    err = rel_l2(bf16_to_f64(bf16_from_dev(h))[:, rows], want)
+    say(f"  rel-L2 {err:.3e}")
+    assert err <= REL_L2_TOL
