@@ -66,7 +66,13 @@ __global__ __launch_bounds__(256) void gate_up_kernel(const uint16_t* __restrict
                                                       uint16_t* __restrict__ h, const float* __restrict__ wn,
                                                       const float* __restrict__ rinv) {
   __shared__ f32x4 red[4][2 * RT * T][64];
+  extern __shared__ float wns[];  // NORM: the noisy norm weight, K floats (dynamic LDS)
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  if constexpr (NORM) {
+    for (int i = 4 * threadIdx.x; i < K; i += 1024)  // K % 16 == 0
+      *reinterpret_cast<float4*>(wns + i) = *reinterpret_cast<const float4*>(wn + i);
+    __syncthreads();
+  }
   const int li = lane & 15, lg = lane >> 4;
   const int KC = (K + 127) >> 7, NT = (N + 15) >> 4;
   const uint8_t *gcode[RT], *ucode[RT], *gsc[RT], *usc[RT];
@@ -106,7 +112,7 @@ __global__ __launch_bounds__(256) void gate_up_kernel(const uint16_t* __restrict
       const int k = 128 * c + 32 * st + 8 * lg;  // K % 16 == 0: 8 values all in or all out
 #pragma unroll
       for (int j = 0; j < T; ++j)
-        xv[st][j] = k < K ? token_fragment<NORM>(xrow[j] + 128 * c + 32 * st, rv[j], wn + k) : make_uint4(0u, 0u, 0u, 0u);
+        xv[st][j] = k < K ? token_fragment<NORM>(xrow[j] + 128 * c + 32 * st, rv[j], wns + k) : make_uint4(0u, 0u, 0u, 0u);
     }
 #pragma unroll
     for (int i = 0; i < RT; ++i) {
@@ -326,16 +332,19 @@ hipError_t launch_aqn_gate_up(const uint16_t* x, int64_t m, int64_t n, int64_t k
                      32 * 4 * kNormLoraSteps, rinv, tg, tu);
   if ((e = hipGetLastError()) != hipSuccess) return e;
   const int T = gate_up_token_tiles(m);
-  const int RT = T == 1 ? 1 : 2;
+  // LDS: the waves' sums (8 KB per row tile and token tile) plus k floats of
+  // the noisy weight (<= 64 KB): one row tile at 8 token tiles keeps it <= 128 KB
+  const int RT = T == 1 || T == 8 ? 1 : 2;
   const dim3 grid((unsigned)(((n + 15) / 16 + RT - 1) / RT));
   const int tsl = r > 0 ? S : 0;
 #define FP4RL_AQN_GATE_UP(TT, RR)                                                                                   \
-  hipLaunchKernelGGL((gate_up_kernel<TT, RR, true>), grid, dim3(256), 0, st, x, (int)m, (int)n, (int)k, cg, sg, stg, \
+  hipLaunchKernelGGL((gate_up_kernel<TT, RR, true>), grid, dim3(256), (size_t)k * 4, st, x, (int)m, (int)n, (int)k, cg, \
+                     sg, stg, \
                      cu, su, stu, tg, tu, tsl, bg, bu, (int)r, h, wn, rinv)
   if (T == 1) FP4RL_AQN_GATE_UP(1, 1);
   else if (T == 2) FP4RL_AQN_GATE_UP(2, 2);
   else if (T == 4) FP4RL_AQN_GATE_UP(4, 2);
-  else FP4RL_AQN_GATE_UP(8, 2);
+  else FP4RL_AQN_GATE_UP(8, 1);
 #undef FP4RL_AQN_GATE_UP
   return hipGetLastError();
 }
