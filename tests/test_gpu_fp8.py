@@ -69,7 +69,9 @@ def _linear_case(m, n, k, r, seed):
 
 
 @pytest.mark.parametrize("shape", [(1, 8, 16, 0), (3, 40, 80, 4), (17, 100, 512, 32), (64, 520, 1040, 8),
-                                   (130, 200, 400, 24), (257, 96, 272, 64), (5, 4100, 32, 1)])
+                                   (130, 200, 400, 24), (257, 96, 272, 64), (5, 4100, 32, 1),
+                                   # output widths not a multiple of 4: the scalar tails of every path
+                                   (5, 37, 80, 4), (40, 4101, 1040, 8), (130, 37, 272, 8), (300, 1027, 2064, 5)])
 def test_linear_ragged(shape):
     m, n, k, r = shape
     dev = device()
