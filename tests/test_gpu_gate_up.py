@@ -67,7 +67,7 @@ def _aqn_case(m, k, seed):
 
 
 @pytest.mark.parametrize("shape", [(1, 16, 64, 0), (5, 40, 144, 4), (16, 64, 1040, 8), (40, 100, 512, 32),
-                                   (128, 64, 256, 5)])
+                                   (128, 64, 256, 5), (3, 37, 208, 4), (70, 131, 4112, 16)])
 def test_aqn_folded_ragged(shape):
     """The AQN RMSNorm folded into gate/up equals the norm oracle feeding the gate/up oracle."""
     from oracle import aqn
