@@ -231,9 +231,6 @@ hipError_t launch_aqn_rmsnorm(const uint16_t* x, int64_t m, int64_t d, const flo
   // the rows: 65536 x 5120 takes 286 us with 2048 workgroups, 327 with 1024
   // and 316 with 4096.
   int64_t grid = std::max<int64_t>(1, std::min<int64_t>(rows_wg, 2048));
-#ifdef FP4RL_TUNING
-  if (const char* g = getenv("FP4RL_TUNE_AQN_GRID")) grid = std::max<int64_t>(1, std::min<int64_t>(rows_wg, atoi(g)));
-#endif
   const size_t lds = (size_t)((d + 7) / 8) * 8 * sizeof(float);
   const uint32_t sl = (uint32_t)seed, sh = (uint32_t)(seed >> 32);
   const uint32_t tl = (uint32_t)step, th = (uint32_t)(step >> 32);

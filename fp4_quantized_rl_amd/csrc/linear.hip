@@ -1240,20 +1240,10 @@ size_t gemv_lds_bytes(int mtok, int64_t k, int64_t r, int waves) {
   return (size_t)(mtok * kp * 2 + (mtok * r + 16 * r) * 4 + waves * mtok * 16 * 4);
 }
 
-#ifdef FP4RL_TUNING
-// scratch builds only: launch shapes forced from the environment
-int tune_env(const char* name) {
-  const char* v = getenv(name);
-  return v ? atoi(v) : 0;
-}
-#endif
 
 // More than 128 tokens: the prefill GEMM (128-token tiles, each weight
 // dequantised once per 128 tokens).
 static bool use_prefill(int64_t m) {
-#ifdef FP4RL_TUNING
-  if (tune_env("FP4RL_TUNE_PF_MIN") > 0) return m >= tune_env("FP4RL_TUNE_PF_MIN");
-#endif
   return m > 128;
 }
 
@@ -1268,10 +1258,6 @@ struct SkinnyCfg {
 // 3..16 tokens (one 16-token tile).
 SkinnyCfg pick_skinny(int64_t m, int64_t n, int64_t k) {
   (void)m;
-#ifdef FP4RL_TUNING
-  if (tune_env("FP4RL_TUNE_SK_W") > 0)
-    return SkinnyCfg{1, tune_env("FP4RL_TUNE_SK_NT") > 0 ? tune_env("FP4RL_TUNE_SK_NT") : 1, tune_env("FP4RL_TUNE_SK_W")};
-#endif
   const int64_t kc = (k + 127) / 128;
   if (n >= 4096) {
     // wide matrices: two row tiles share each activation fragment (halves the
@@ -1325,9 +1311,6 @@ hipError_t run_skinny_w(int w, dim3 grid, hipStream_t st, const uint16_t* x, int
 int lora_splits(int64_t m, int64_t k, int64_t r) {
   (void)r;
   if (use_prefill(m)) return 1;  // prefill: token tiles already fill the chip
-#ifdef FP4RL_TUNING
-  if (tune_env("FP4RL_TUNE_SLICES") > 0) return tune_env("FP4RL_TUNE_SLICES");
-#endif
   // Up to 8 K-slices of at least 512 k (the linear's epilogue adds them in
   // order): enough workgroups for a long K without a separate reduction.
   const int64_t by_k = std::max<int64_t>(1, k / 512);
@@ -1372,9 +1355,6 @@ static int gemv_waves(int64_t n, int64_t k) {
   const int64_t rt = (n + 15) / 16, kc = (k + 127) / 128;
   int w = 1;
   while (w < 16 && 8 * w <= kc && rt * w * 2 <= 8192) w *= 2;  // doubling keeps >= 4 chunks per wave
-#ifdef FP4RL_TUNING
-  if (tune_env("FP4RL_TUNE_GEMV_W") > 0) w = tune_env("FP4RL_TUNE_GEMV_W");
-#endif
   return w;
 }
 
@@ -1439,17 +1419,6 @@ static SplitkCfg pick_splitk(int64_t m, int64_t n, int64_t k) {
   while ((int64_t)c.gx * c.gy * s < 256 && (kc + 2 * s - 1) / (2 * s) >= c.w &&
          4.0 * (double)(2 * s) * (double)m * (double)n * 2.0 <= wbytes / 3.0)
     s *= 2;
-#ifdef FP4RL_TUNING
-  if (tune_env("FP4RL_TUNE_S") > 0) s = tune_env("FP4RL_TUNE_S");
-  if (tune_env("FP4RL_TUNE_TM") > 0) {
-    c.tm = tune_env("FP4RL_TUNE_TM");
-    c.gx = (int)((n + 16 * c.tm - 1) / (16 * c.tm));
-  }
-  if (tune_env("FP4RL_TUNE_TN") > 0) {
-    c.tn = tune_env("FP4RL_TUNE_TN");
-    c.gy = (int)((m + 16 * c.tn - 1) / (16 * c.tn));
-  }
-#endif
   c.cpz = (int)((kc + s - 1) / s);
   c.s = (int)((kc + c.cpz - 1) / c.cpz);  // no empty K range
   if ((int64_t)c.gx * c.gy > kSplitCounters) c.s = 1, c.cpz = (int)kc;  // a split needs one counter per tile
@@ -1459,9 +1428,6 @@ static SplitkCfg pick_splitk(int64_t m, int64_t n, int64_t k) {
   // 28.8 -> 26.1 us, down 18944 -> 3584 at 32 tokens 22.9 -> 21.8 us, while
   // o 3584 -> 3584 is 1 us slower with it)
   c.d = (int64_t)c.gx * c.gy > 256 || kc > 64 ? 2 : 3;
-#ifdef FP4RL_TUNING
-  if (tune_env("FP4RL_TUNE_D") > 0) c.d = tune_env("FP4RL_TUNE_D");
-#endif
   return c;
 }
 
@@ -1500,16 +1466,7 @@ static hipError_t launch_splitk(const SplitkCfg& c, hipStream_t st, const uint16
     return run_splitk<2, 4, 2, 2>(c, st, x, M, N, K, codes, scales, ts, t, tks, b, r, y, part, counters, lf);
   if (c.tm == 2 && c.tn == 2 && c.w == 4 && c.d == 3)
     return run_splitk<2, 4, 3, 2>(c, st, x, M, N, K, codes, scales, ts, t, tks, b, r, y, part, counters, lf);
-#ifdef FP4RL_TUNING
-  if (c.tm == 2 && c.tn == 4 && c.d == 2)
-    return run_splitk<4, 4, 2, 2>(c, st, x, M, N, K, codes, scales, ts, t, tks, b, r, y, part, counters, lf);
-  if (c.tm == 2 && c.tn == 4 && c.d == 3)
-    return run_splitk<4, 4, 3, 2>(c, st, x, M, N, K, codes, scales, ts, t, tks, b, r, y, part, counters, lf);
-#endif
   if (c.tm != 4) return hipErrorInvalidValue;
-#ifdef FP4RL_TUNING
-  FP4RL_SPLITK(4, 4)
-#endif
   FP4RL_SPLITK(2, 4)
 #undef FP4RL_SPLITK
   return hipErrorInvalidValue;
@@ -1578,23 +1535,6 @@ hipError_t launch_fp4_linear(const uint16_t* x, int64_t m, int64_t n, int64_t k,
     const int64_t gr = (n + kPfRows - 1) / kPfRows, gt = (m + kPfTok - 1) / kPfTok;
     const int64_t supers = (gr + 7) / 8 * ((gt + 3) / 4);  // super-tiles of 8 x 4 workgroups, dealt to 8 XCDs
     const int64_t grid = 8 * 32 * ((supers + 7) / 8);
-#ifdef FP4RL_TUNING
-    const int g_tune_w = tune_env("FP4RL_TUNE_PREFILL");
-    if (g_tune_w == 44) {
-      hipLaunchKernelGGL((prefill_kernel<4, 4>), dim3((unsigned)grid), dim3(512), 0, stream, x, M, N, K, codes, scales,
-                         tensor_scale, t, tks, b, R, y);
-      return hipGetLastError();
-    }
-    if (g_tune_w == 4 || g_tune_w == 1) {
-      if (g_tune_w == 4)
-        hipLaunchKernelGGL(prefill_kernel<4>, dim3((unsigned)grid), dim3(256), 0, stream, x, M, N, K, codes, scales,
-                           tensor_scale, t, tks, b, R, y);
-      else
-        hipLaunchKernelGGL(prefill_kernel<1>, dim3((unsigned)grid), dim3(1024), 0, stream, x, M, N, K, codes, scales,
-                           tensor_scale, t, tks, b, R, y);
-      return hipGetLastError();
-    }
-#endif
     // 8 waves of 32 features x 128 tokens: two waves per SIMD hide each
     // other's LDS, barrier and load waits
     hipLaunchKernelGGL(prefill_kernel<2>, dim3((unsigned)grid), dim3(512), 0, stream, x, M, N, K, codes, scales,

@@ -17,7 +17,9 @@ is bf16 and the LoRA product is kept unrounded (float64) before the sum.
 
 Pins (tests/test_oracle_linear.py): exact Fraction evaluation of the sum on
 tiny shapes; B = 0 and s = 0 reduce to the base product; W = 0 reduces to
-the LoRA product; y(2x) = 2 y(x) exactly.
+the LoRA product; y(2x) = 2 y(x) exactly. The down-projection t = s x A^T
+on its own (``lora_down``) is pinned term by term against Fractions on
+non-square adapters, at two scales, so a dropped s or a transposed A fails.
 """
 from __future__ import annotations
 
@@ -55,8 +57,25 @@ def lora_linear(x_bits, codes, scales, s_t, a_bits=None, b_bits=None,
 
 
 def lora_down(x_bits, a_bits, lora_scale: float) -> np.ndarray:
-    """t = s * x A^T, float64 [M, r] (the LoRA down-projection, unrounded)."""
+    """t = s * x A^T, float64 [M, r] (the LoRA down-projection, unrounded).
+
+    x bf16 [M, K] and A bf16 [r, K] as in the fused formula; s is taken at
+    fp32 precision, the precision the library receives it in.
+    """
     return np.float64(np.float32(lora_scale)) * (bf16_to_f64(x_bits) @ bf16_to_f64(a_bits).T)
+
+
+def lora_down_exact(x_bits, a_bits, lora_scale: float):
+    """The same t as nested lists of Fractions, every product written out; tiny shapes only."""
+    from fractions import Fraction as F
+
+    x = bf16_to_f64(x_bits)
+    a = bf16_to_f64(a_bits)
+    s = F(float(np.float32(lora_scale)))
+    m, k = x.shape
+    r = a.shape[0]
+    return [[s * sum((F(float(x[i, kk])) * F(float(a[j, kk])) for kk in range(k)), F(0))
+             for j in range(r)] for i in range(m)]
 
 
 def lora_linear_exact(x_bits, codes, scales, s_t, a_bits, b_bits, lora_scale):

@@ -22,7 +22,8 @@ to bf16 (nearest-even), the adapter gradients once to fp32; the pages fix
 neither precision.
 
 Pins (tests/test_oracle_lora_backward.py): exact Fraction evaluation on tiny
-shapes; the adjoint identities <dY, y(x + d) - y(x)> = <dX, d>, and the same
+shapes (also of ``adapter_terms_f64``, the weight-free form used for sampled
+checks at full size); the adjoint identities <dY, y(x + d) - y(x)> = <dX, d>, and the same
 for A and B, against the forward oracle (y is linear in x and in each
 adapter separately); r = 0 leaves only the base term; a zero weight leaves
 only the LoRA terms.
@@ -62,6 +63,28 @@ def lora_linear_backward(dy_bits, x_bits, codes, scales, s_t, a_bits=None, b_bit
                                           lora_scale)
     f32 = (lambda v: None if v is None else v.astype(np.float32).astype(np.float64))
     return bf16_round(dx), f32(da), f32(db)
+
+
+def adapter_terms_f64(dy_bits, x_bits, a_bits, b_bits, lora_scale: float, b_rows=None):
+    """(h, dA, dB[b_rows]) in float64, without building the dequantised weight.
+
+    h = s (dY B) [M, r] is the gradient that reaches the rank space (it also
+    feeds dX's LoRA term); dA = h^T x [r, K]; dB = s dY^T (x A^T), only the
+    output features ``b_rows`` (all when None). For checks at full size,
+    where the [N, K] float64 weight of ``lora_linear_backward_f64`` would be
+    needlessly large.
+    """
+    dy = bf16_to_f64(dy_bits)
+    x = bf16_to_f64(x_bits)
+    a = bf16_to_f64(a_bits)
+    b = bf16_to_f64(b_bits)
+    s = np.float64(np.float32(lora_scale))
+    h = s * (dy @ b)
+    da = h.T @ x
+    u = x @ a.T
+    dyr = dy if b_rows is None else dy[:, np.asarray(b_rows)]
+    db = s * (dyr.T @ u)
+    return h, da, db
 
 
 def dx_columns_f64(dy_bits, codes, scales, s_t, cols, a_bits=None, h=None):

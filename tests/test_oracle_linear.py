@@ -68,3 +68,36 @@ def test_base_product_against_torch_dequant():
     xt = torch.from_numpy((x.astype(np.uint32) << 16).view(np.float32).astype(np.float64))
     ref = bf16_round((xt @ wd.T).numpy())
     assert np.array_equal(linear.lora_linear(x, codes, scales, st), ref)
+
+
+def test_lora_down_matches_exact_rationals():
+    """t = s x A^T term by term in Fractions, on adapters that are not square (r != K)."""
+    for seed, (m, k, r, s) in enumerate([(2, 32, 3, 2.0), (3, 16, 5, 0.5), (1, 48, 2, 2.0)]):
+        rng = np.random.default_rng(100 + seed)
+        x = bf16_bits(rng.standard_normal((m, k), dtype=np.float32))
+        a = bf16_bits(rng.standard_normal((r, k), dtype=np.float32) * np.float32(0.05))
+        t = linear.lora_down(x, a, s)
+        assert t.shape == (m, r)
+        ex = np.array([[float(v) for v in row] for row in linear.lora_down_exact(x, a, s)])
+        assert np.allclose(t, ex, rtol=1e-13, atol=0)
+
+
+def test_lora_down_catches_a_dropped_scale_or_transposed_adapter():
+    """The pin above would fail for the two plausible slips: s left out, or A used untransposed
+    (a square A with A != A^T, so the shapes cannot catch it)."""
+    rng = np.random.default_rng(7)
+    m, k, s = 3, 16, 2.0
+    x = bf16_bits(rng.standard_normal((m, k), dtype=np.float32))
+    a = bf16_bits(rng.standard_normal((k, k), dtype=np.float32) * np.float32(0.05))
+    ex = np.array([[float(v) for v in row] for row in linear.lora_down_exact(x, a, s)])
+    xv = (x.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+    av = (a.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+    assert np.allclose(linear.lora_down(x, a, s), ex, rtol=1e-13, atol=0)
+    assert not np.allclose(xv @ av.T, ex, rtol=1e-6)        # s dropped
+    assert not np.allclose(s * (xv @ av), ex, rtol=1e-6)    # A not transposed
+    # and t is the LoRA term of the fused linear: zero base weight, B = I_r gives y = bf16(t)
+    zc = np.zeros((k, k // 2), np.uint8)
+    zs = np.zeros((k, k // 16), np.uint8)
+    eye = bf16_bits(np.eye(k, dtype=np.float32))
+    y = linear.lora_linear(x, zc, zs, np.float32(0.0), a, eye, s)
+    assert np.array_equal(y, bf16_round(ex))

@@ -86,3 +86,23 @@ def test_rounded_outputs_and_column_sampler():
     h = 2.0 * bf16_values(dy).astype(np.float64) @ bf16_values(b).astype(np.float64)
     cols = np.array([0, 15, 16, 50, 95])
     assert np.allclose(lb.dx_columns_f64(dy, codes, scales, st, cols, a, h), dx64[:, cols], rtol=1e-12)
+
+
+def test_adapter_terms_match_exact_rationals():
+    """The weight-free (h, dA, dB-rows) form used for sampled checks at full size."""
+    for seed, (m, n, k, r) in enumerate([(2, 3, 32, 2), (3, 5, 16, 4)]):
+        dy, x, codes, scales, st, a, b = _case(40 + seed, m, n, k, r)
+        _, da_ex, db_ex = lb.lora_backward_exact(dy, x, codes, scales, st, a, b, 2.0)
+        rows = np.array([n - 1, 0])
+        h, da, db = lb.adapter_terms_f64(dy, x, a, b, 2.0, b_rows=rows)
+        da_w = np.array([[float(v) for v in row] for row in da_ex])
+        db_w = np.array([[float(v) for v in row] for row in db_ex])
+        assert np.allclose(da, da_w, rtol=1e-12, atol=1e-300)
+        assert np.allclose(db, db_w[rows], rtol=1e-12, atol=1e-300)
+        # h = s dY B, written out
+        dyv, bv = bf16_values(dy).astype(np.float64), bf16_values(b).astype(np.float64)
+        for mm in range(m):
+            for j in range(r):
+                assert np.isclose(h[mm, j], 2.0 * sum(dyv[mm, i] * bv[i, j] for i in range(n)), rtol=1e-12)
+        _, _, db_all = lb.adapter_terms_f64(dy, x, a, b, 2.0)
+        assert np.allclose(db_all, db_w, rtol=1e-12, atol=1e-300)
