@@ -66,6 +66,9 @@ _SIGNATURES = {
     "fp4rl_fp4_linear_lora_up": (_STATUS, [_P, _I64, _I64, _I64, _P, _P, _P, _P, _P, _I64, _P, _P, _c.c_size_t,
                                            _P]),
     "fp4rl_fp4_linear_kernel_name": (_c.c_char_p, [_I64, _I64, _I64, _I64]),
+    "fp4rl_linear_workspace_check": (_STATUS, [_P, _c.c_size_t, _P]),
+    "fp4rl_linear_workspace_reset": (_STATUS, [_P, _c.c_size_t, _P]),
+    "fp4rl_debug_lora_handoff": (None, [_c.c_uint32, _c.c_int32]),
     "fp4rl_fp4_gate_up_silu_workspace": (_c.c_size_t, [_I64, _I64, _I64, _I64]),
     "fp4rl_fp4_gate_up_silu": (_STATUS, [_P, _I64, _I64, _I64, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _I64,
                                          _c.c_float, _P, _P, _c.c_size_t, _P]),
@@ -468,6 +471,32 @@ def linear_workspace(nbytes: int, device="cuda"):
     """A zero-filled workspace for fp4_lora_linear / fp4_linear_lora_up (its counter words start at zero;
     the library returns them to zero after every call, so the buffer can be reused)."""
     return _torch().zeros(max(int(nbytes), 16), dtype=_torch().uint8, device=device)
+
+
+def linear_workspace_check(workspace) -> None:
+    """Synchronise the current stream and raise Fp4rlError (FP4RL_ERR_TIMEOUT) if a fused linear on this
+    workspace gave up waiting for its in-launch LoRA producers."""
+    if workspace is None:
+        return
+    torch = _torch()
+    with torch.cuda.device(workspace.device):
+        _check(load_library().fp4rl_linear_workspace_check(_ptr(workspace), workspace.numel(),
+                                                           _stream(workspace.device)), "linear_workspace_check")
+
+
+def linear_workspace_reset(workspace) -> None:
+    """Zero the counter words of a linear workspace (a fill kernel on the current stream)."""
+    if workspace is None:
+        return
+    torch = _torch()
+    with torch.cuda.device(workspace.device):
+        _check(load_library().fp4rl_linear_workspace_reset(_ptr(workspace), workspace.numel(),
+                                                           _stream(workspace.device)), "linear_workspace_reset")
+
+
+def debug_lora_handoff(spin_limit: int = 0, withhold_ready: bool = False) -> None:
+    """Test hook: poll limit of the fused LoRA hand-off (0 = default) and whether producers withhold the flag."""
+    load_library().fp4rl_debug_lora_handoff(int(spin_limit), 1 if withhold_ready else 0)
 
 
 def fp4_lora_linear_workspace_bytes(m: int, n: int, k: int, r: int) -> int:

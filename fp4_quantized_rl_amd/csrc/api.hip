@@ -32,6 +32,11 @@ fp4rl_status ok() {
 bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
 
 constexpr int64_t kMaxDim = (int64_t)1 << 31;  // kernels index rows and columns with int
+
+// Test hooks of the fused LoRA hand-off (fp4rl_debug_lora_handoff): the
+// consumers' poll limit and whether producers leave the ready flags down.
+std::atomic<uint32_t> g_lora_spin{fp4rl::LoraFuse{}.spin};
+std::atomic<uint32_t> g_lora_withhold{0u};
 constexpr int kMaxDevices = 64;
 std::atomic<int> g_dev_state[kMaxDevices];  // 0 unknown, 1 gfx950, 2 other arch
 
@@ -104,6 +109,7 @@ const char* fp4rl_status_string(int32_t status) {
     case FP4RL_ERR_ARCH: return "FP4RL_ERR_ARCH";
     case FP4RL_ERR_HIP: return "FP4RL_ERR_HIP";
     case FP4RL_ERR_VALUE: return "FP4RL_ERR_VALUE";
+    case FP4RL_ERR_TIMEOUT: return "FP4RL_ERR_TIMEOUT";
     default: return "FP4RL_UNKNOWN_STATUS";
   }
 }
@@ -323,6 +329,9 @@ fp4rl_status fp4rl_fp4_lora_linear(const uint16_t* x, int64_t m, int64_t n, int6
       lf.tctr = reinterpret_cast<uint32_t*>(ws) + fp4rl::kLoraTileCtrOffset;
       lf.done = reinterpret_cast<uint32_t*>(ws) + fp4rl::kLoraDoneOffset;
       lf.lines = reinterpret_cast<uint32_t*>(ws) + fp4rl::kLoraLineOffset;
+      lf.err = reinterpret_cast<uint32_t*>(ws) + fp4rl::kLinearErrOffset;
+      lf.spin = g_lora_spin.load(std::memory_order_relaxed);
+      lf.withhold = g_lora_withhold.load(std::memory_order_relaxed);
     } else {
       fp4rl_status s =
           launched(fp4rl::launch_lora_down(x, m, k, lora_a, r, lora_scale, splits, t, stream), "lora_down");
@@ -335,6 +344,37 @@ fp4rl_status fp4rl_fp4_lora_linear(const uint16_t* x, int64_t m, int64_t n, int6
                                            lf.producers > 0 ? 1 : slices,
                                            r > 0 ? lora_b : nullptr, r, y, part, counters, lf, stream),
                   "fp4_linear");
+}
+
+fp4rl_status fp4rl_linear_workspace_check(const void* workspace, size_t workspace_bytes, fp4rl_stream stream) {
+  if (workspace == nullptr || workspace_bytes == 0) return ok();  // no counter words: nothing can have failed
+  FP4RL_REQUIRE(workspace_bytes >= fp4rl::kLinearCounterBytes, FP4RL_ERR_WORKSPACE,
+                "workspace %zu bytes holds no counter words (%zu)", workspace_bytes, fp4rl::kLinearCounterBytes);
+  FP4RL_REQUIRE(aligned(workspace, 16), FP4RL_ERR_ALIGN, "workspace must be 16-byte aligned");
+  FP4RL_CHECK(check_device());
+  uint32_t err = 0;
+  const uint32_t* word = static_cast<const uint32_t*>(workspace) + fp4rl::kLinearErrOffset;
+  hipError_t e = hipMemcpyAsync(&err, word, sizeof(err), hipMemcpyDeviceToHost, stream);
+  if (e == hipSuccess) e = hipStreamSynchronize(stream);
+  if (e != hipSuccess) return fail(FP4RL_ERR_HIP, "reading the workspace error word: %s", hipGetErrorString(e));
+  if (err & fp4rl::kLinearErrLoraWait)
+    return fail(FP4RL_ERR_TIMEOUT, "a fused linear on this workspace gave up waiting for its LoRA down-projection "
+                                   "(error bits 0x%x); results since then are not to be trusted", err);
+  return ok();
+}
+
+fp4rl_status fp4rl_linear_workspace_reset(void* workspace, size_t workspace_bytes, fp4rl_stream stream) {
+  if (workspace == nullptr || workspace_bytes == 0) return ok();
+  FP4RL_REQUIRE(workspace_bytes >= fp4rl::kLinearCounterBytes, FP4RL_ERR_WORKSPACE,
+                "workspace %zu bytes holds no counter words (%zu)", workspace_bytes, fp4rl::kLinearCounterBytes);
+  FP4RL_REQUIRE(aligned(workspace, 16), FP4RL_ERR_ALIGN, "workspace must be 16-byte aligned");
+  FP4RL_CHECK(check_device());
+  return launched(fp4rl::launch_zero_words(workspace, fp4rl::kLinearCounters, stream), "linear_workspace_reset");
+}
+
+void fp4rl_debug_lora_handoff(uint32_t spin_limit, int32_t withhold_ready) {
+  g_lora_spin.store(spin_limit == 0 ? fp4rl::LoraFuse{}.spin : spin_limit, std::memory_order_relaxed);
+  g_lora_withhold.store(withhold_ready != 0 ? 1u : 0u, std::memory_order_relaxed);
 }
 
 const char* fp4rl_fp4_linear_kernel_name(int64_t m, int64_t n, int64_t k, int64_t r) {

@@ -48,6 +48,8 @@ constexpr int kSplitCounters = 256;      // words [0, 256): K-split tile counter
 constexpr int kLoraTileCounters = 128;   // words [256, 384): one per 16x16 tile of t (m <= 128, r <= 256)
 constexpr int kLoraTileCtrOffset = 256;
 constexpr int kLoraDoneOffset = 384;     // word 384: finished tiles of t
+constexpr int kLinearErrOffset = 388;    // word 388: sticky device-side error bits (kLinearErr*)
+constexpr uint32_t kLinearErrLoraWait = 1u;  // a consumer gave up waiting for t (see LoraFuse::spin)
 constexpr int kLoraGroups = 64;          // ready flags: one 256-byte line per group of output tiles
 constexpr int kLoraLineWords = 64;
 constexpr int kLoraLineOffset = 512;     // line g: words 512 + 64 g (flag), + 1 (count)
@@ -66,7 +68,15 @@ constexpr size_t kLinearCounterBytes = kLinearCounters * sizeof(uint32_t);
 // group's last one clears the line. Spreading the consumers over many lines
 // keeps same-address atomics few. Producers have the lowest workgroup ids
 // and never wait on consumers, so they are dispatched first and always
-// finish.
+// finish. Flags and counters are agent-scope relaxed atomics; t itself is
+// written and read only with agent-coherent (sc1) accesses, after a
+// vmcnt(0) wait on the writer's side and behind the flag read (a dependent
+// branch and a barrier) on the reader's side, so a reader sees the data
+// without acquire/release cache maintenance (an L2 invalidate per output
+// workgroup, measured 13.1 -> 20.5 us for the 7B gate at one token). A
+// consumer that gives up after `spin` polls sets kLinearErrLoraWait in the
+// workspace's error word, which stays set (every later call on that
+// workspace is then suspect) until the caller clears the counter words.
 struct LoraFuse {
   const uint16_t* a = nullptr;  // A [r][K]; nullptr: no fused producers (t ready-made, or r == 0)
   float s = 0.0f;               // lora_scale
@@ -79,7 +89,11 @@ struct LoraFuse {
   uint32_t* tctr = nullptr;     // per-tile slice counters (mtiles * rtiles <= kLoraTileCounters)
   uint32_t* done = nullptr;     // finished tiles of t
   uint32_t* lines = nullptr;    // kLoraGroups lines of kLoraLineWords words: ready flag, consumer count
+  uint32_t* err = nullptr;      // the workspace's sticky error word
+  uint32_t spin = 1u << 22;     // polls (each after a short sleep) before a consumer gives up
+  uint32_t withhold = 0;        // test hook: the producers leave the ready flags down
 };
+
 // whether the main kernel chosen for this shape runs fused LoRA producers
 bool linear_fuses_lora(int64_t m, int64_t n, int64_t k);
 int64_t lora_slice_len(int64_t k, int splits);

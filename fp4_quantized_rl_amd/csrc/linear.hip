@@ -197,7 +197,7 @@ __device__ __forceinline__ void lora_produce(const LoraFuse& L, int pid, const u
   __syncthreads();
   if (*flag != 0u) {
     if (threadIdx.x == 0) __hip_atomic_store(L.done, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    if ((int)threadIdx.x < L.groups)
+    if ((int)threadIdx.x < L.groups && L.withhold == 0u)
       __hip_atomic_store(L.lines + kLoraLineWords * threadIdx.x, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   }
 }
@@ -205,10 +205,11 @@ __device__ __forceinline__ void lora_produce(const LoraFuse& L, int pid, const u
 // Consumers' side, for the workgroup that writes output tile `tile` of y
 // (thread 0 does the memory accesses). It reads its group's ready flag early
 // (lora_poll), so the latency overlaps other work; lora_wait then returns at
-// once if it was set, else polls (bounded: a missing producer gives wrong
-// results, never a hang). Right after its wait the consumer counts itself on
-// its group's line (lora_release) and, once its epilogue is issued, the
-// group's last consumer clears the line (lora_reset_if_last).
+// once if it was set, else polls (bounded: a producer that never raises the
+// flag leaves the error bit in the workspace, never a hang). Right after its
+// wait the consumer counts itself on its group's line
+// (lora_release) and, once its epilogue is issued, the group's last consumer
+// clears the line (lora_reset_if_last).
 __device__ __forceinline__ uint32_t* lora_line(const LoraFuse& L, int tile) {
   return L.lines + kLoraLineWords * (tile % L.groups);
 }
@@ -222,10 +223,12 @@ __device__ __forceinline__ uint32_t lora_poll(const LoraFuse& L, int tile) {
 __device__ __forceinline__ void lora_wait(const LoraFuse& L, int tile, uint32_t seen) {
   if (L.producers > 0 && threadIdx.x == 0) {
     const uint32_t* f = lora_line(L, tile);
-    for (int it = 0; seen == 0u && it < (1 << 22); ++it) {
+    for (uint32_t it = 0; seen == 0u && it < L.spin; ++it) {
       __builtin_amdgcn_s_sleep(8);
       seen = __hip_atomic_load(f, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     }
+    if (seen == 0u)
+      __hip_atomic_fetch_or(L.err, kLinearErrLoraWait, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   }
   __syncthreads();
 }

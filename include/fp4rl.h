@@ -61,7 +61,9 @@ typedef enum fp4rl_status {
   FP4RL_ERR_WORKSPACE = 5, /* workspace NULL or smaller than the matching *_workspace() size */
   FP4RL_ERR_ARCH = 6,      /* the current device is not gfx950 */
   FP4RL_ERR_HIP = 7,       /* a HIP runtime call failed; text in fp4rl_last_error() */
-  FP4RL_ERR_VALUE = 8      /* a scalar is out of range (negative or non-finite sigma/eps/scale) */
+  FP4RL_ERR_VALUE = 8,     /* a scalar is out of range (negative or non-finite sigma/eps/scale) */
+  FP4RL_ERR_TIMEOUT = 9    /* reported by fp4rl_linear_workspace_check: a fused launch on that workspace
+                              gave up waiting for its in-launch LoRA producers */
 } fp4rl_status;
 
 typedef enum fp4rl_dtype { FP4RL_F32 = 0, FP4RL_BF16 = 1 } fp4rl_dtype;
@@ -167,6 +169,30 @@ fp4rl_status fp4rl_fp4_lora_linear(const uint16_t* x, int64_t m, int64_t n, int6
                                    const uint16_t* lora_b, int64_t r, float lora_scale,
                                    uint16_t* y, void* workspace, size_t workspace_bytes,
                                    fp4rl_stream stream);
+
+/* Health of a linear workspace's in-launch hand-off (QeRL explainer,
+ * "NVFP4 quantization and LoRA": t = s x A^T feeds the LoRA term of the same
+ * fused forward). The output workgroups of a fused launch wait for the
+ * launch's own producer workgroups to finish t; the wait is bounded (about
+ * 2^22 polls), so a producer that never finishes cannot hang the GPU. A
+ * consumer that gives up sets an error bit in the workspace's counter words
+ * and computes with whatever t holds. The bit stays set: every later call on
+ * that workspace is suspect until the counter words are cleared.
+ * fp4rl_linear_workspace_check: synchronises `stream`, then reads the bit;
+ *   FP4RL_OK, or FP4RL_ERR_TIMEOUT (detail in fp4rl_last_error()).
+ *   workspace == NULL or workspace_bytes == 0: FP4RL_OK (no hand-off).
+ *   workspace_bytes smaller than the counter words: FP4RL_ERR_WORKSPACE.
+ * fp4rl_linear_workspace_reset: queues a fill kernel (no memset, so it may
+ *   be captured in a HIP graph) that zeroes the counter words: the state of
+ *   a fresh zero-filled workspace. Does not synchronise. */
+fp4rl_status fp4rl_linear_workspace_check(const void* workspace, size_t workspace_bytes, fp4rl_stream stream);
+fp4rl_status fp4rl_linear_workspace_reset(void* workspace, size_t workspace_bytes, fp4rl_stream stream);
+/* [host] Test hook of the hand-off above, process-wide, read when a fused
+ * launch is queued: consumers give up after spin_limit polls (0 restores
+ * the default), and with withhold_ready != 0 the producers compute t but
+ * leave the ready flags down, so every consumer gives up and every kernel
+ * still ends normally. For tests of the error path only. */
+void fp4rl_debug_lora_handoff(uint32_t spin_limit, int32_t withhold_ready);
 
 /* The two halves of fp4rl_fp4_lora_linear, for callers that produce t
  * elsewhere or time the main kernel alone.

@@ -45,8 +45,9 @@ def test_library_exports_every_declared_symbol(lib):
 
 
 def test_status_strings(lib):
-    names = [lib.fp4rl_status_string(i).decode() for i in range(9)]
+    names = [lib.fp4rl_status_string(i).decode() for i in range(10)]
     assert names[0] == "FP4RL_OK" and names[ERR_ALIGN] == "FP4RL_ERR_ALIGN"
+    assert names[9] == "FP4RL_ERR_TIMEOUT"
     assert lib.fp4rl_status_string(99).decode() == "FP4RL_UNKNOWN_STATUS"
 
 
@@ -293,3 +294,15 @@ def test_binding_fails_loudly_without_library(monkeypatch):
     monkeypatch.setattr(fr, "_LIB", None)
     with pytest.raises(fr.Fp4rlError):
         fr.load_library()
+
+
+def test_workspace_check_and_reset_validate_arguments(lib):
+    """Argument checks of the hand-off health calls, all decided before any device access."""
+    counter_bytes = 4 * (512 + 64 * 64)
+    assert lib.fp4rl_linear_workspace_check(None, 0, None) == OK          # no workspace: no hand-off
+    assert lib.fp4rl_linear_workspace_reset(None, 0, None) == OK
+    assert lib.fp4rl_linear_workspace_check(FAKE, counter_bytes - 4, None) == ERR_WORKSPACE
+    assert lib.fp4rl_linear_workspace_reset(FAKE, 16, None) == ERR_WORKSPACE
+    assert lib.fp4rl_linear_workspace_check(FAKE + 4, counter_bytes, None) == ERR_ALIGN
+    assert lib.fp4rl_linear_workspace_reset(FAKE + 8, counter_bytes, None) == ERR_ALIGN
+    lib.fp4rl_debug_lora_handoff(0, 0)  # the defaults; touches no device

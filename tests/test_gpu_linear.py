@@ -140,6 +140,40 @@ def test_fused_lora_shapes(m, n, k, r):
     assert err < 1e-5
 
 
+@pytest.mark.parametrize("m", [1, 8, 40])
+def test_lora_handoff_timeout_is_reported(m):
+    """The bounded wait of the in-launch LoRA hand-off, made to give up from the host (the producers leave
+    the ready flags down, the consumers poll 64 times): every kernel still ends, the workspace then reports
+    FP4RL_ERR_TIMEOUT, also after a later normal call, until it is reset; after the reset a call matches
+    the oracle and leaves the counter words at zero."""
+    dev = device()
+    n, k, r = 300, 1040, 16
+    w, x, a, b = _case(m, n, k, r, seed=4242 + m)
+    q = nvfp4.quantize(w)
+    xt, wq = bf16_to_dev(x, dev), nvfp4_to_dev(*q, dev)
+    at, bt = bf16_to_dev(a, dev), bf16_to_dev(b, dev)
+    ws = fr.linear_workspace(fr.fp4_lora_linear_workspace_bytes(m, n, k, r), dev)
+    say(f"linear hand-off timeout m={m} ({fr.fp4_linear_kernel_name(m, n, k, r)})")
+    fr.linear_workspace_check(ws)  # a fresh workspace is healthy
+    try:
+        fr.debug_lora_handoff(64, True)
+        fr.fp4_lora_linear(xt, wq, at, bt, LORA_SCALE, workspace=ws)
+        torch.cuda.synchronize()
+    finally:
+        fr.debug_lora_handoff(0, False)
+    with pytest.raises(fr.Fp4rlError) as err:
+        fr.linear_workspace_check(ws)
+    assert err.value.status == 9, err.value
+    fr.fp4_lora_linear(xt, wq, at, bt, LORA_SCALE, workspace=ws)
+    with pytest.raises(fr.Fp4rlError):
+        fr.linear_workspace_check(ws)  # sticky until the counter words are cleared
+    fr.linear_workspace_reset(ws)
+    y = fr.fp4_lora_linear(xt, wq, at, bt, LORA_SCALE, workspace=ws)
+    fr.linear_workspace_check(ws)
+    _check(bf16_from_dev(y), linear.lora_linear(x, *q, a, b, LORA_SCALE), f"{m}x{n}x{k} r{r} after reset")
+    assert not bool(ws[:COUNTER_BYTES].any()), "counter words not back at zero"
+
+
 PREFILL = [  # (m, n, k, r): more than 128 tokens (256-feature x 128-token workgroup tiles), ragged in every dim
     (129, 16, 128, 0), (200, 270, 400, 8), (384, 512, 1024, 16), (1000, 520, 2064, 32), (2048, 300, 4096, 64),
 ]
