@@ -55,6 +55,7 @@ _SIGNATURES = {
     "fp4rl_nvfp4_scales_bytes": (_c.c_size_t, [_I64, _I64, _c.c_int32]),
     "fp4rl_nvfp4_quantize": (_STATUS, [_P, _c.c_int32, _I64, _I64, _c.c_int32, _P, _P, _P, _P, _c.c_size_t, _P]),
     "fp4rl_nvfp4_to_tiled": (_STATUS, [_P, _P, _I64, _I64, _P, _P, _P]),
+    "fp4rl_nvfp4_quantize_noalloc": (_STATUS, [_P, _c.c_int32, _I64, _I64, _c.c_int32, _P, _P, _P, _P]),
     "fp4rl_nvfp4_quantize_record": (_STATUS, [_P, _c.c_int32, _I64, _I64, _c.c_int32, _P, _P, _P, _P, _P,
                                               _c.c_size_t, _P]),
     "fp4rl_fp4_lora_linear_workspace": (_c.c_size_t, [_I64, _I64, _I64, _I64]),

@@ -5,6 +5,7 @@
 #include <cstdarg>
 #include <cstdio>
 #include <cstring>
+#include <mutex>
 
 #include "fp4rl.h"
 #include "backward.hpp"
@@ -55,6 +56,37 @@ fp4rl_status check_device() {
     if (s == 2) return fail(FP4RL_ERR_ARCH, "device %d is %s, not gfx950", dev, p.gcnArchName);
   }
   if (s != 1) return fail(FP4RL_ERR_ARCH, "device %d is not gfx950", dev);
+  return FP4RL_OK;
+}
+
+// Scratch of fp4rl_nvfp4_quantize_noalloc: the amax pass's per-workgroup
+// partial maxima (kAmaxPartials words). Each GPU the library runs on holds
+// its own copy until the process ends; every call on one GPU shares it, so
+// calls that overlap on one GPU race. Host code never passes the array's
+// name to a kernel (on the host it is only a stand-in): the device address
+// of each GPU's copy is looked up once, on that GPU's first call, and kept.
+static __device__ __align__(256) uint32_t scratch[fp4rl::kAmaxPartials];
+constexpr size_t kScratchBytes = sizeof(uint32_t) * fp4rl::kAmaxPartials;
+std::atomic<void*> g_scratch[kMaxDevices];
+std::mutex g_scratch_mu;
+
+fp4rl_status scratch_address(void** out) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return fail(FP4RL_ERR_HIP, "hipGetDevice: %s", hipGetErrorString(e));
+  if (dev < 0 || dev >= kMaxDevices) return fail(FP4RL_ERR_HIP, "device ordinal %d out of range", dev);
+  void* p = g_scratch[dev].load(std::memory_order_acquire);
+  if (p == nullptr) {
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    p = g_scratch[dev].load(std::memory_order_relaxed);
+    if (p == nullptr) {
+      e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));  // with this device current
+      if (e != hipSuccess || p == nullptr)
+        return fail(FP4RL_ERR_HIP, "hipGetSymbolAddress(scratch): %s", hipGetErrorString(e));
+      g_scratch[dev].store(p, std::memory_order_release);
+    }
+  }
+  *out = p;
   return FP4RL_OK;
 }
 
@@ -136,9 +168,8 @@ size_t fp4rl_nvfp4_scales_bytes(int64_t n, int64_t k, int32_t layout) {
   return (size_t)fp4rl::nvfp4_scales_bytes(n, k, layout == FP4RL_TILED);
 }
 
-static fp4rl_status quantize_impl(const void* w, int32_t w_dtype, int64_t n, int64_t k, int32_t layout,
-                                  uint8_t* codes, uint8_t* scales, float* tensor_scale, uint8_t* record,
-                                  void* workspace, size_t workspace_bytes, fp4rl_stream stream) {
+static fp4rl_status check_quantize_args(const void* w, int32_t w_dtype, int64_t n, int64_t k, int32_t layout,
+                                        const uint8_t* codes, const uint8_t* scales, const float* tensor_scale) {
   FP4RL_REQUIRE(n >= 0 && k >= 0, FP4RL_ERR_SHAPE, "negative size (n=%lld k=%lld)", (long long)n, (long long)k);
   FP4RL_REQUIRE(k % 16 == 0, FP4RL_ERR_SHAPE, "k=%lld is not a multiple of 16", (long long)k);
   FP4RL_REQUIRE(n < kMaxDim && k < kMaxDim && n * k < ((int64_t)1 << 36), FP4RL_ERR_SHAPE, "matrix too large");
@@ -146,9 +177,20 @@ static fp4rl_status quantize_impl(const void* w, int32_t w_dtype, int64_t n, int
   FP4RL_REQUIRE(layout == FP4RL_ROW_MAJOR || layout == FP4RL_TILED, FP4RL_ERR_VALUE, "layout=%d", (int)layout);
   FP4RL_REQUIRE(tensor_scale != nullptr, FP4RL_ERR_NULL, "tensor_scale is NULL");
   FP4RL_REQUIRE(aligned(tensor_scale, 4), FP4RL_ERR_ALIGN, "tensor_scale not 4-byte aligned");
+  if (n > 0 && k > 0) {
+    FP4RL_REQUIRE(w && codes && scales, FP4RL_ERR_NULL, "w, codes and scales must be non-NULL");
+    FP4RL_REQUIRE(aligned(w, 16) && aligned(codes, 16) && aligned(scales, 16), FP4RL_ERR_ALIGN,
+                  "w, codes and scales must be 16-byte aligned");
+  }
+  return FP4RL_OK;
+}
+
+static fp4rl_status quantize_impl(const void* w, int32_t w_dtype, int64_t n, int64_t k, int32_t layout,
+                                  uint8_t* codes, uint8_t* scales, float* tensor_scale, uint8_t* record,
+                                  void* workspace, size_t workspace_bytes, fp4rl_stream stream) {
+  FP4RL_CHECK(check_quantize_args(w, w_dtype, n, k, layout, codes, scales, tensor_scale));
   const bool empty = n == 0 || k == 0;
   if (!empty) {
-    FP4RL_REQUIRE(w && codes && scales, FP4RL_ERR_NULL, "w, codes and scales must be non-NULL");
     FP4RL_REQUIRE(workspace != nullptr, FP4RL_ERR_WORKSPACE, "workspace is NULL");
     FP4RL_REQUIRE(workspace_bytes >= fp4rl::quantize_workspace_bytes(), FP4RL_ERR_WORKSPACE,
                   "workspace %zu < %zu bytes", workspace_bytes, fp4rl::quantize_workspace_bytes());
@@ -167,6 +209,19 @@ fp4rl_status fp4rl_nvfp4_quantize(const void* w, int32_t w_dtype, int64_t n, int
                                   size_t workspace_bytes, fp4rl_stream stream) {
   return quantize_impl(w, w_dtype, n, k, layout, codes, scales, tensor_scale, nullptr, workspace, workspace_bytes,
                        stream);
+}
+
+fp4rl_status fp4rl_nvfp4_quantize_noalloc(const void* w, int32_t w_dtype, int64_t n, int64_t k, int32_t layout,
+                                          uint8_t* codes, uint8_t* scales, float* tensor_scale,
+                                          fp4rl_stream stream) {
+  FP4RL_CHECK(check_quantize_args(w, w_dtype, n, k, layout, codes, scales, tensor_scale));
+  if (fp4rl::quantize_workspace_bytes() > kScratchBytes)  // the partials of any shape are this many words
+    return fail(FP4RL_ERR_WORKSPACE, "the quantiser needs %zu bytes of scratch, above the %zu-byte array",
+                fp4rl::quantize_workspace_bytes(), kScratchBytes);
+  FP4RL_CHECK(check_device());
+  void* ws = nullptr;
+  FP4RL_CHECK(scratch_address(&ws));
+  return quantize_impl(w, w_dtype, n, k, layout, codes, scales, tensor_scale, nullptr, ws, kScratchBytes, stream);
 }
 
 fp4rl_status fp4rl_nvfp4_quantize_record(const void* w, int32_t w_dtype, int64_t n, int64_t k, int32_t layout,

@@ -115,6 +115,19 @@ fp4rl_status fp4rl_nvfp4_quantize(const void* w, int32_t w_dtype, int64_t n, int
 fp4rl_status fp4rl_nvfp4_to_tiled(const uint8_t* codes, const uint8_t* scales, int64_t n, int64_t k,
                                   uint8_t* codes_tiled, uint8_t* scales_tiled, fp4rl_stream stream);
 
+/* For callers that cannot allocate device memory (code under HIP graph
+ * capture, tight serving or training loops, harnesses that forbid
+ * hipMalloc): fp4rl_nvfp4_quantize with the workspace replaced by a
+ * library-owned device array (the amax pass's 1024 partial maxima, 4 KB; the
+ * same for every shape, so no shape is rejected for its size). Same
+ * arguments otherwise, same results byte for byte, same errors. It calls no
+ * allocating routine. Each GPU holds one copy of the array until the process
+ * ends, looked up on that GPU's first call; calls that overlap on one GPU
+ * (several streams or threads) race on it. */
+fp4rl_status fp4rl_nvfp4_quantize_noalloc(const void* w, int32_t w_dtype, int64_t n, int64_t k, int32_t layout,
+                                          uint8_t* codes, uint8_t* scales, float* tensor_scale,
+                                          fp4rl_stream stream);
+
 /* Quantise as fp4rl_nvfp4_quantize (same codes, scales and tensor scale, same
  * arguments and errors) and also write the rounding record the rollout side
  * keeps for the trainer (TRACE article, "TRACE's core idea" and "Engineering
