@@ -412,11 +412,12 @@ def fp4_lora_linear_backward_workspace_bytes(m: int, n: int, k: int, r: int, wan
 
 
 def fp4_lora_linear_backward(dy, x, wq: NVFP4Weight, lora_a=None, lora_b=None, lora_scale: float = 0.0,
-                             want_dx: bool = True, workspace=None):
+                             want_dx: bool = True, workspace=None, out=None):
     """(dx, grad_a, grad_b) of y = x deq(Wq)^T + s (x A^T) B^T for dy bf16 [m, n].
 
     dx is bf16 [m, k] (None when want_dx is False); grad_a fp32 [r, k] and
     grad_b fp32 [n, r] (None without adapters). The base weight gets no gradient.
+    out: optional (dx, grad_a, grad_b) tensors to write into (None entries are allocated).
     """
     torch = _torch()
     m, n, k = _linear_args(x, wq)
@@ -431,9 +432,23 @@ def fp4_lora_linear_backward(dy, x, wq: NVFP4Weight, lora_a=None, lora_b=None, l
         if lora_a.shape != (r, k) or lora_b.shape != (n, r):
             raise ValueError("LoRA shapes must be A [r, k] and B [n, r]")
     dev = x.device
-    dx = torch.empty((m, k), dtype=torch.bfloat16, device=dev) if want_dx else None
-    ga = torch.empty((r, k), dtype=torch.float32, device=dev) if r else None
-    gb = torch.empty((n, r), dtype=torch.float32, device=dev) if r else None
+    dx, ga, gb = out if out is not None else (None, None, None)
+    if dx is None and want_dx:
+        dx = torch.empty((m, k), dtype=torch.bfloat16, device=dev)
+    if ga is None and r:
+        ga = torch.empty((r, k), dtype=torch.float32, device=dev)
+    if gb is None and r:
+        gb = torch.empty((n, r), dtype=torch.float32, device=dev)
+    if not want_dx:
+        dx = None
+    if not r:
+        ga = gb = None
+    for t, name, shape, dt in ((dx, "dx", (m, k), torch.bfloat16), (ga, "grad_a", (r, k), torch.float32),
+                               (gb, "grad_b", (n, r), torch.float32)):
+        if t is not None:
+            _dev_tensor(t, name, (dt,), 2)
+            if tuple(t.shape) != shape:
+                raise ValueError(f"{name} must be {list(shape)}")
     lib = load_library()
     ws_bytes = lib.fp4rl_fp4_lora_linear_backward_workspace(m, n, k, r, int(bool(want_dx)))
     if workspace is None:

@@ -20,6 +20,9 @@ tiny shapes; B = 0 and s = 0 reduce to the base product; W = 0 reduces to
 the LoRA product; y(2x) = 2 y(x) exactly. The down-projection t = s x A^T
 on its own (``lora_down``) is pinned term by term against Fractions on
 non-square adapters, at two scales, so a dropped s or a transposed A fails.
+The magnitude sums (``lora_linear_magnitude_f64``, test tolerances only)
+equal the linear itself on non-negative inputs and bound its absolute value
+everywhere.
 """
 from __future__ import annotations
 
@@ -54,6 +57,30 @@ def lora_linear(x_bits, codes, scales, s_t, a_bits=None, b_bits=None,
     """bf16-rounded y [M, N] (float64 values), the device output's reference."""
     return bf16_round(lora_linear_f64(x_bits, codes, scales, s_t, a_bits, b_bits,
                                       lora_scale, rows))
+
+
+def lora_linear_magnitude_f64(x_bits, codes, scales, s_t, a_bits=None, b_bits=None,
+                              lora_scale: float = 0.0, rows=None):
+    """(base, lora): sum_k |x_k| |W_nk| and |s| sum_j (sum_k |x_k| |A_jk|) |B_nj|, float64 [M, N].
+
+    The same sums as the linear with every term made non-negative: they bound
+    the rounding error of any order of summation, so tests derive their
+    per-element tolerances from them. ``rows`` selects output features as in
+    ``lora_linear_f64``.
+    """
+    x = np.abs(bf16_to_f64(x_bits))
+    if rows is not None:
+        rows = np.asarray(rows)
+        codes = np.asarray(codes)[rows]
+        scales = np.asarray(scales)[rows]
+        if b_bits is not None:
+            b_bits = np.asarray(b_bits)[rows]
+    base = x @ np.abs(dequantize(codes, scales, s_t)).T
+    lora = np.zeros_like(base)
+    if a_bits is not None and b_bits is not None and np.asarray(a_bits).shape[0] > 0:
+        t = x @ np.abs(bf16_to_f64(a_bits)).T
+        lora = abs(np.float64(np.float32(lora_scale))) * (t @ np.abs(bf16_to_f64(b_bits)).T)
+    return base, lora
 
 
 def lora_down(x_bits, a_bits, lora_scale: float) -> np.ndarray:

@@ -56,6 +56,27 @@ def lora_linear_backward_f64(dy_bits, x_bits, codes, scales, s_t, a_bits=None, b
     return dx, da, db
 
 
+def backward_magnitudes_f64(dy_bits, x_bits, codes, scales, s_t, a_bits=None, b_bits=None,
+                            lora_scale: float = 0.0):
+    """The backward's sums with every term made non-negative (test tolerances only).
+
+    Returns (dx_base, dx_lora, da, db): sum_n |dY||W|, sum_j |h_j| |A_jk| with
+    |h| = |s| |dY| |B|, and the magnitudes of dA and dB; the last three are None
+    without adapters. They bound the rounding error of any summation order.
+    """
+    dy = np.abs(bf16_to_f64(dy_bits))
+    x = np.abs(bf16_to_f64(x_bits))
+    dx_base = dy @ np.abs(dequantize(codes, scales, s_t))
+    if a_bits is None or b_bits is None or np.asarray(a_bits).shape[0] == 0:
+        return dx_base, None, None, None
+    a = np.abs(bf16_to_f64(a_bits))
+    b = np.abs(bf16_to_f64(b_bits))
+    s = abs(np.float64(np.float32(lora_scale)))
+    h = s * (dy @ b)
+    u = x @ a.T
+    return dx_base, h @ a, h.T @ x, s * (dy.T @ u)
+
+
 def lora_linear_backward(dy_bits, x_bits, codes, scales, s_t, a_bits=None, b_bits=None,
                          lora_scale: float = 0.0):
     """(dX bf16-rounded, dA fp32-rounded, dB fp32-rounded), all as float64 arrays."""

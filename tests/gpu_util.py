@@ -80,3 +80,65 @@ def nvfp4_from_dev(wq: fr.NVFP4Weight):
 
 def say(msg: str) -> None:
     print(msg, flush=True)
+
+
+# ---------------------------------------------------------------- guard pads
+GUARD_BYTES = 256   # sentinel bytes on each side of a guarded output
+GUARD_FILL = 0x5A
+
+
+def guarded(shape, dtype, dev):
+    """An uninitialised-looking (sentinel-filled) contiguous output of `shape` inside a larger buffer with
+    GUARD_BYTES of sentinel on each side; returns (buffer, view). The view stays 16-byte aligned."""
+    elem = torch.empty((), dtype=dtype).element_size()
+    nbytes = int(np.prod(shape)) * elem
+    buf = torch.full((2 * GUARD_BYTES + nbytes,), GUARD_FILL, dtype=torch.uint8, device=dev)
+    view = buf[GUARD_BYTES:GUARD_BYTES + nbytes].view(dtype).view(tuple(shape))
+    return buf, view
+
+
+def assert_guards(buf, what=""):
+    """The sentinel bytes on both sides of a guarded output are untouched (no out-of-bounds write)."""
+    b = buf.cpu().numpy()
+    lo, hi = b[:GUARD_BYTES], b[-GUARD_BYTES:]
+    assert (lo == GUARD_FILL).all() and (hi == GUARD_FILL).all(), f"{what}: a write landed outside the output"
+
+
+# ------------------------------------------------------- per-element bounds
+def bf16_ulp(v):
+    """Spacing of bf16 numbers in the binade of |v| (2^-133 below the normal range)."""
+    a = np.abs(np.asarray(v, dtype=np.float64))
+    _, e = np.frexp(np.maximum(a, 2.0 ** -126))  # a = f 2^e, f in [0.5, 1)
+    return np.ldexp(1.0, e.astype(np.int64) - 1 - 7)
+
+
+def f32_ulp(v):
+    """Spacing of fp32 numbers at |v|."""
+    return np.spacing(np.abs(np.asarray(v, dtype=np.float64)).astype(np.float32)).astype(np.float64)
+
+
+def assert_elementwise(got, want, slack, what, ulp=bf16_ulp):
+    """|got - want| <= 2 ulps of want (bf16 by default, or `ulp` = f32_ulp) + slack, element by element.
+
+    The ulps cover the two roundings of the output (device and oracle); `slack`
+    is the bound on the device's accumulation error the caller derives from
+    the magnitude of the summed terms.
+    """
+    got = np.asarray(got, dtype=np.float64)
+    want = np.asarray(want, dtype=np.float64)
+    err = np.abs(got - want)
+    bound = 2.0 * ulp(want) + np.asarray(slack, dtype=np.float64)
+    bad = np.argwhere(err > bound)
+    if bad.size:
+        i = tuple(bad[0])
+        raise AssertionError(f"{what}: {len(bad)} elements beyond the per-element bound, first at {i}: "
+                             f"got {got[i]!r} want {want[i]!r} bound {bound[i]!r}")
+    worst = float(np.max(err / bound)) if err.size else 0.0
+    say(f"  {what}: per-element error <= {worst:.3f} of the bound")
+
+
+def accumulation_slack(base, lora, terms):
+    """Bound on an fp32 accumulation of `terms` summands of total magnitude base + lora (each rounding
+    contributes at most 2^-24 of the running magnitude), plus 2^-15 of the LoRA magnitude for its
+    rank-space operand held as a bf16 hi + lo pair."""
+    return (terms + 64) * 2.0 ** -24 * (np.asarray(base) + np.asarray(lora)) + 2.0 ** -15 * np.asarray(lora)

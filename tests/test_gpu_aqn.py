@@ -8,17 +8,23 @@ from oracle import aqn
 from oracle.numerics import bf16_round, bf16_to_f64, rel_l2
 from workloads import activations_bf16, single_linear_config
 
-from gpu_util import REL_L2_TOL, bf16_from_dev, bf16_to_dev, device, f32_to_dev, say
+from gpu_util import (REL_L2_TOL, assert_elementwise, assert_guards, bf16_from_dev, bf16_to_dev, device, f32_to_dev,
+                      guarded, say)
 
 pytestmark = pytest.mark.gpu
 
 
 def _run(dev, x, w, sigma, seed, step, norm_id, eps, want_noise=True):
+    """The norm into guarded outputs (sentinel bytes around y and w_noise, checked untouched)."""
     xt = bf16_to_dev(x, dev)
     wt = f32_to_dev(w, dev)
-    wn = torch.empty(w.shape[0], dtype=torch.float32, device=dev) if want_noise else None
-    y = fr.aqn_rmsnorm(xt, wt, sigma, seed, step, norm_id, eps, w_noise_out=wn)
+    ybuf, y = guarded(x.shape, torch.bfloat16, dev)
+    wbuf, wn = guarded((w.shape[0],), torch.float32, dev) if want_noise else (None, None)
+    fr.aqn_rmsnorm(xt, wt, sigma, seed, step, norm_id, eps, out=y, w_noise_out=wn)
     torch.cuda.synchronize()
+    assert_guards(ybuf, f"AQN y {x.shape}")
+    if want_noise:
+        assert_guards(wbuf, f"AQN w_noise {w.shape}")
     return bf16_from_dev(y), (wn.cpu().numpy() if want_noise else None)
 
 
@@ -29,6 +35,11 @@ def _check(x, w, sigma, seed, step, norm_id, eps, dev, what, tol=REL_L2_TOL):
     e_w = rel_l2(wn, wn_ref)
     say(f"  {what}: y rel-L2 {e_y:.3e}, w_noise rel-L2 {e_w:.3e}")
     assert e_y <= tol and e_w <= 1e-6, what
+    # per element: the fp32 sum of d squares and the rsqrt bound the relative error by about
+    # (d + 8) 2^-24, the noise's transcendental functions by 2^-20 of sigma |z| (inside |y| too)
+    d = x.shape[1]
+    slack = np.abs(y_ref) * ((d + 8) * 2.0 ** -24 + 2.0 ** -20)
+    assert_elementwise(bf16_to_f64(y), y_ref, slack, f"{what} y")
 
 
 def test_philox_words_bit_exact():

@@ -8,7 +8,8 @@ from oracle import lora_backward as lb, nvfp4
 from oracle.numerics import bf16_round, bf16_to_f64, rel_l2
 from workloads import LORA_SCALE, QWEN25_7B, activations_bf16, bf16_bits, lora_bf16, normal_f32, tensor_seed
 
-from gpu_util import REL_L2_TOL, bf16_from_dev, bf16_to_dev, device, nvfp4_to_dev, say
+from gpu_util import (REL_L2_TOL, accumulation_slack, assert_elementwise, assert_guards, bf16_from_dev, bf16_to_dev,
+                      device, f32_ulp, guarded, nvfp4_to_dev, say)
 
 pytestmark = pytest.mark.gpu
 
@@ -54,13 +55,26 @@ def test_ragged_shapes(shape):
     w, x, dy, a, b = _case(m, n, k, r, seed=m * 7 + n + k + r)
     q = nvfp4.quantize(w)
     xt, dyt, wq, at, bt = _upload(dev, x, dy, q, a, b)
-    dx, ga, gb = fr.fp4_lora_linear_backward(dyt, xt, wq, at, bt, LORA_SCALE)
+    bufs = [guarded((m, k), torch.bfloat16, dev), guarded((r, k), torch.float32, dev),
+            guarded((n, r), torch.float32, dev)]
+    dx, ga, gb = fr.fp4_lora_linear_backward(dyt, xt, wq, at, bt, LORA_SCALE,
+                                             out=(bufs[0][1], bufs[1][1] if r else None, bufs[2][1] if r else None))
     torch.cuda.synchronize()
+    for (buf, _), what in zip(bufs, ("dX", "dA", "dB")):
+        assert_guards(buf, f"backward {what}")
     dx_ref, da_ref, db_ref = lb.lora_linear_backward(dy, x, *q, a if r else None, b if r else None, LORA_SCALE)
-    _err(bf16_to_f64(bf16_from_dev(dx)), dx_ref, "dX", REL_L2_TOL)
+    dxb, dxl, da_m, db_m = lb.backward_magnitudes_f64(dy, x, *q, a if r else None, b if r else None, LORA_SCALE)
+    dx_got = bf16_to_f64(bf16_from_dev(dx))
+    _err(dx_got, dx_ref, "dX", REL_L2_TOL)
+    assert_elementwise(dx_got, dx_ref, accumulation_slack(dxb, 0.0 if dxl is None else dxl, n + r), "dX")
     if r:
-        _err(ga.cpu().numpy().astype(np.float64), da_ref, "dA", GRAD_TOL)
-        _err(gb.cpu().numpy().astype(np.float64), db_ref, "dB", GRAD_TOL)
+        da_got, db_got = ga.cpu().numpy().astype(np.float64), gb.cpu().numpy().astype(np.float64)
+        _err(da_got, da_ref, "dA", GRAD_TOL)
+        _err(db_got, db_ref, "dB", GRAD_TOL)
+        # fp32 outputs: their own rounding (2^-24 relative) plus the accumulation over tokens and the
+        # rank-space operands' bf16 hi + lo split (2^-15 of the magnitude)
+        assert_elementwise(da_got, da_ref, (m + n + 64) * 2.0 ** -24 * da_m + 2.0 ** -15 * da_m, "dA", ulp=f32_ulp)
+        assert_elementwise(db_got, db_ref, (m + k + 64) * 2.0 ** -24 * db_m + 2.0 ** -15 * db_m, "dB", ulp=f32_ulp)
     else:
         assert ga is None and gb is None
 

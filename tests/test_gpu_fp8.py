@@ -9,7 +9,8 @@ from oracle.numerics import bf16_round, bf16_to_f64, rel_l2
 from workloads import (LORA_SCALE, QWEN25_7B, activations_bf16, bf16_bits, bf16_values, lora_bf16, normal_f32,
                        tensor_seed)
 
-from gpu_util import REL_L2_TOL, bf16_from_dev, bf16_to_dev, device, f32_to_dev, say, u8_to_dev
+from gpu_util import (REL_L2_TOL, accumulation_slack, assert_elementwise, assert_guards, bf16_from_dev, bf16_to_dev,
+                      device, f32_to_dev, guarded, say, u8_to_dev)
 
 pytestmark = pytest.mark.gpu
 
@@ -81,12 +82,22 @@ def test_linear_ragged(shape):
     w8 = fr.FP8Weight(u8_to_dev(codes, dev), f32_to_dev(s, dev))
     at = bf16_to_dev(a, dev) if r else None
     bt = bf16_to_dev(b, dev) if r else None
-    y = fr.fp8_lora_linear(bf16_to_dev(x, dev), w8, at, bt, LORA_SCALE)
+    buf, y = guarded((m, n), torch.bfloat16, dev)
+    fr.fp8_lora_linear(bf16_to_dev(x, dev), w8, at, bt, LORA_SCALE, out=y)
     torch.cuda.synchronize()
+    assert_guards(buf, "fp8 linear output")
     ref = fp8.lora_linear(x, codes, s, a if r else None, b if r else None, LORA_SCALE)
-    err = rel_l2(bf16_to_f64(bf16_from_dev(y)), ref)
+    got = bf16_to_f64(bf16_from_dev(y))
+    err = rel_l2(got, ref)
     say(f"  rel-L2 {err:.3e}")
     assert err <= REL_L2_TOL
+    # per element: |x| |W| and the LoRA magnitude, both from the oracle's dequantised rows
+    xa = np.abs(bf16_to_f64(x))
+    base = xa @ np.abs(fp8.dequantize(codes, s)).T
+    lora = 0.0
+    if r:
+        lora = abs(LORA_SCALE) * ((xa @ np.abs(bf16_to_f64(a)).T) @ np.abs(bf16_to_f64(b)).T)
+    assert_elementwise(got, ref, accumulation_slack(base, lora, k + r), "fp8 linear")
 
 
 @pytest.mark.parametrize("m", [1, 32, 1024, 8192])

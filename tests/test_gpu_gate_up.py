@@ -8,7 +8,7 @@ from oracle import gate_up as gu, nvfp4
 from oracle.numerics import bf16_to_f64, rel_l2
 from workloads import LORA_SCALE, QWEN25_7B, activations_bf16, lora_bf16, normal_f32, tensor_seed
 
-from gpu_util import REL_L2_TOL, bf16_from_dev, bf16_to_dev, device, nvfp4_to_dev, say
+from gpu_util import REL_L2_TOL, assert_guards, bf16_from_dev, bf16_to_dev, device, guarded, nvfp4_to_dev, say
 
 pytestmark = pytest.mark.gpu
 
@@ -17,8 +17,10 @@ def _run(dev, x, g, u, lg, lu, s):
     wg, wu = nvfp4_to_dev(*g, dev), nvfp4_to_dev(*u, dev)
     lgd = tuple(bf16_to_dev(t, dev) for t in lg) if lg is not None else None
     lud = tuple(bf16_to_dev(t, dev) for t in lu) if lu is not None else None
-    h = fr.fp4_gate_up_silu(bf16_to_dev(x, dev), wg, wu, lgd, lud, s)
+    buf, h = guarded((x.shape[0], g[0].shape[0]), torch.bfloat16, dev)
+    fr.fp4_gate_up_silu(bf16_to_dev(x, dev), wg, wu, lgd, lud, s, out=h)
     torch.cuda.synchronize()
+    assert_guards(buf, "gate/up output")
     return bf16_to_f64(bf16_from_dev(h))
 
 

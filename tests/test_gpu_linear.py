@@ -9,7 +9,8 @@ from oracle.numerics import bf16_to_f64, rel_l2
 from workloads import (LORA_SCALE, QWEN25_7B, QWEN25_32B, activations_bf16, bf16_bits, lora_bf16,
                        normal_f32, single_linear_config, tensor_seed)
 
-from gpu_util import (REL_L2_TOL, bf16_from_dev, bf16_to_dev, device, f32_to_dev, nvfp4_to_dev, say)
+from gpu_util import (REL_L2_TOL, accumulation_slack, assert_elementwise, assert_guards, bf16_from_dev, bf16_to_dev,
+                      device, f32_to_dev, guarded, nvfp4_to_dev, say)
 
 pytestmark = pytest.mark.gpu
 
@@ -24,12 +25,15 @@ def _case(m, n, k, r, seed, wstd=0.02, bstd=0.01, outliers=0.0):
 
 
 def _run(dev, x, q, a, b, s):
+    """The fused linear into a guarded output (sentinel bytes on both sides, checked untouched)."""
     xt = bf16_to_dev(x, dev)
     wq = nvfp4_to_dev(*q, dev)
     at = bf16_to_dev(a, dev) if a is not None and a.shape[0] else None
     bt = bf16_to_dev(b, dev) if b is not None and b.shape[1] else None
-    y = fr.fp4_lora_linear(xt, wq, at, bt, s)
+    buf, y = guarded((x.shape[0], wq.n), torch.bfloat16, dev)
+    fr.fp4_lora_linear(xt, wq, at, bt, s, out=y)
     torch.cuda.synchronize()
+    assert_guards(buf, "linear output")
     return bf16_from_dev(y)
 
 
@@ -37,6 +41,16 @@ def _check(y_bits, y_ref, what, tol=REL_L2_TOL):
     err = rel_l2(bf16_to_f64(y_bits), y_ref)
     say(f"  {what}: rel-L2 {err:.3e}")
     assert err <= tol, f"{what}: rel-L2 {err}"
+
+
+def _check_lin(y_bits, x, q, a, b, s, what, rows=None):
+    """rel-L2 against the oracle, and every element within 2 bf16 ulps plus the fp32 accumulation bound
+    derived from the magnitude of its terms."""
+    ref = linear.lora_linear(x, *q, a, b, s, rows=rows)
+    _check(y_bits, ref, what)
+    base, lora = linear.lora_linear_magnitude_f64(x, *q, a, b, s, rows=rows)
+    terms = x.shape[1] + (0 if a is None else np.asarray(a).shape[0])
+    assert_elementwise(bf16_to_f64(y_bits), ref, accumulation_slack(base, lora, terms), what)
 
 
 def test_single_linear_config():
@@ -48,8 +62,7 @@ def test_single_linear_config():
     y = fr.fp4_lora_linear(bf16_to_dev(cfg["x"], dev), wq, bf16_to_dev(cfg["lora_a"], dev),
                            bf16_to_dev(cfg["lora_b"], dev), cfg["lora_scale"])
     torch.cuda.synchronize()
-    ref = linear.lora_linear(cfg["x"], *q_ref, cfg["lora_a"], cfg["lora_b"], cfg["lora_scale"])
-    _check(bf16_from_dev(y), ref, "256x512 M=4 r=8")
+    _check_lin(bf16_from_dev(y), cfg["x"], q_ref, cfg["lora_a"], cfg["lora_b"], cfg["lora_scale"], "256x512 M=4 r=8")
 
 
 RAGGED = [  # (m, n, k, r)
@@ -66,7 +79,7 @@ def test_ragged_shapes(m, n, k, r):
     q = nvfp4.quantize(w)
     say(f"linear m={m} n={n} k={k} r={r}")
     y = _run(dev, x, q, a, b, LORA_SCALE)
-    _check(y, linear.lora_linear(x, *q, a, b, LORA_SCALE), f"{m}x{n}x{k} r{r}")
+    _check_lin(y, x, q, a, b, LORA_SCALE, f"{m}x{n}x{k} r{r}")
 
 
 SPLITK = [  # (m, n, k, r): few output tiles and a long K, so K is also split over workgroups
@@ -83,7 +96,7 @@ def test_split_k_shapes(m, n, k, r):
     q = nvfp4.quantize(w)
     say(f"linear split-K m={m} n={n} k={k} r={r} ({fr.fp4_linear_kernel_name(m, n, k, r)})")
     y = _run(dev, x, q, a, b, LORA_SCALE)
-    _check(y, linear.lora_linear(x, *q, a, b, LORA_SCALE), f"{m}x{n}x{k} r{r}")
+    _check_lin(y, x, q, a, b, LORA_SCALE, f"{m}x{n}x{k} r{r}")
 
 
 SPLITK_CONFIGS = [  # (m, n, k, r, kernel): every split-K instantiation, ragged in n and k
@@ -102,7 +115,7 @@ def test_split_k_launch_configs(m, n, k, r, kernel):
     q = nvfp4.quantize(w)
     say(f"linear {kernel} m={m} n={n} k={k} r={r}")
     y = _run(dev, x, q, a, b, LORA_SCALE)
-    _check(y, linear.lora_linear(x, *q, a, b, LORA_SCALE), f"{m}x{n}x{k} r{r}")
+    _check_lin(y, x, q, a, b, LORA_SCALE, f"{m}x{n}x{k} r{r}")
 
 
 # a linear workspace starts with 4608 counter words: K-split tile counters,
@@ -129,7 +142,7 @@ def test_fused_lora_shapes(m, n, k, r):
     y1 = fr.fp4_lora_linear(xt, wq, at, bt, LORA_SCALE, workspace=ws)
     y2 = fr.fp4_lora_linear(xt, wq, at, bt, LORA_SCALE, workspace=ws)
     torch.cuda.synchronize()
-    _check(bf16_from_dev(y1), linear.lora_linear(x, *q, a, b, LORA_SCALE), f"{m}x{n}x{k} r{r}")
+    _check_lin(bf16_from_dev(y1), x, q, a, b, LORA_SCALE, f"{m}x{n}x{k} r{r}")
     assert torch.equal(y1, y2), "second call on the same workspace differs"
     cb = COUNTER_BYTES
     assert not bool(ws[:cb].any()), "counter words not back at zero"
@@ -170,7 +183,7 @@ def test_lora_handoff_timeout_is_reported(m):
     fr.linear_workspace_reset(ws)
     y = fr.fp4_lora_linear(xt, wq, at, bt, LORA_SCALE, workspace=ws)
     fr.linear_workspace_check(ws)
-    _check(bf16_from_dev(y), linear.lora_linear(x, *q, a, b, LORA_SCALE), f"{m}x{n}x{k} r{r} after reset")
+    _check_lin(bf16_from_dev(y), x, q, a, b, LORA_SCALE, f"{m}x{n}x{k} r{r} after reset")
     assert not bool(ws[:COUNTER_BYTES].any()), "counter words not back at zero"
 
 
@@ -186,7 +199,7 @@ def test_prefill_shapes(m, n, k, r):
     q = nvfp4.quantize(w)
     say(f"linear prefill m={m} n={n} k={k} r={r} ({fr.fp4_linear_kernel_name(m, n, k, r)})")
     y = _run(dev, x, q, a, b, LORA_SCALE)
-    _check(y, linear.lora_linear(x, *q, a, b, LORA_SCALE), f"{m}x{n}x{k} r{r}")
+    _check_lin(y, x, q, a, b, LORA_SCALE, f"{m}x{n}x{k} r{r}")
 
 
 def test_workspace_reuse_across_shapes():
@@ -218,7 +231,7 @@ def test_lora_reductions_bit_identical():
     base = _run(dev, x, q, None, None, 0.0)
     assert np.array_equal(_run(dev, x, q, a, np.zeros_like(b), LORA_SCALE), base), "B = 0"
     assert np.array_equal(_run(dev, x, q, a, b, 0.0), base), "s = 0"
-    _check(base, linear.lora_linear(x, *q), "base only")
+    _check_lin(base, x, q, None, None, 0.0, "base only")
 
 
 def test_lora_dominant():
@@ -231,7 +244,7 @@ def test_lora_dominant():
     ref = linear.lora_linear(x, *q, a, b, LORA_SCALE)
     base = linear.lora_linear_f64(x, *q)
     assert np.linalg.norm(base) < 0.1 * np.linalg.norm(ref)
-    _check(y, ref, "LoRA-dominant")
+    _check_lin(y, x, q, a, b, LORA_SCALE, "LoRA-dominant")
 
 
 def test_power_of_two_homogeneity_and_determinism():
@@ -261,8 +274,8 @@ def test_halves_match_fused_call():
     # rounding order differs), so the outputs agree to bf16 rounding, and each
     # matches the oracle
     ref = linear.lora_linear(x, *q, a, b, LORA_SCALE)
-    _check(bf16_from_dev(y_halves), ref, "halves")
-    _check(bf16_from_dev(y_fused), ref, "fused")
+    _check_lin(bf16_from_dev(y_halves), x, q, a, b, LORA_SCALE, "halves")
+    _check_lin(bf16_from_dev(y_fused), x, q, a, b, LORA_SCALE, "fused")
     diff = (y_halves.float() - y_fused.float()).abs()
     assert float(diff.max()) <= 2.0 ** -7 * float(y_fused.float().abs().max())
     t_ref = linear.lora_down(x, a, LORA_SCALE)
@@ -284,11 +297,12 @@ def _full_size(dev, shapes, names, ms, r, config, outliers=0.0, sample=96):
         for m in ms:
             x = activations_bf16(m, k, seed + m, outlier_frac=outliers)
             say(f"  {name} {n}x{k} M={m} r={r}")
-            y = fr.fp4_lora_linear(bf16_to_dev(x, dev), wq, at, bt, LORA_SCALE)
+            buf, y = guarded((m, n), torch.bfloat16, dev)
+            fr.fp4_lora_linear(bf16_to_dev(x, dev), wq, at, bt, LORA_SCALE, out=y)
             torch.cuda.synchronize()
+            assert_guards(buf, f"{name} M={m} output")
             y_rows = bf16_from_dev(y)[:, rows]
-            ref = linear.lora_linear(x, q_rows[0], q_rows[1], q_rows[2], a, b[rows], LORA_SCALE)
-            _check(y_rows, ref, f"{name} M={m}")
+            _check_lin(y_rows, x, q_rows, a, b[rows], LORA_SCALE, f"{name} M={m}")
         del wq, w
 
 
@@ -298,13 +312,14 @@ def test_qwen7b_decode_layer():
     _full_size(dev, QWEN25_7B, ["qkv", "o", "gate", "up", "down"], [1, 8, 32, 64], 32, config=1)
 
 
-def test_qwen7b_prefill_outliers():
-    """7B qkv and down at M = 8192 with 0.1% outlier channels x20 (sampled output features)."""
+@pytest.mark.parametrize("name", ["qkv", "o", "gate", "up", "down"])
+def test_qwen7b_prefill_outliers(name):
+    """Each 7B linear at M = 8192 with 0.1% outlier channels x20 (sampled output features)."""
     dev = device()
-    _full_size(dev, QWEN25_7B, ["qkv", "down"], [8192], 32, config=2, outliers=0.001, sample=48)
+    _full_size(dev, QWEN25_7B, [name], [8192], 32, config=2, outliers=0.001, sample=48)
 
 
 def test_qwen32b_decode_m128():
     """32B layer linears at M = 128, r = 64 (sampled output features)."""
     dev = device()
-    _full_size(dev, QWEN25_32B, ["qkv", "o", "gate", "down"], [128], 64, config=3, sample=64)
+    _full_size(dev, QWEN25_32B, ["qkv", "o", "gate", "up", "down"], [128], 64, config=3, sample=64)

@@ -10,18 +10,31 @@ from oracle import nvfp4
 from workloads import (QWEN25_14B, bf16_bits, bf16_values, normal_f32, single_linear_config,
                        student_t3_weights, tensor_seed)
 
-from gpu_util import bf16_to_dev, device, f32_to_dev, nvfp4_from_dev, say, tile_host
+from gpu_util import assert_guards, bf16_to_dev, device, f32_to_dev, guarded, nvfp4_from_dev, say, tile_host
 from test_oracle_nvfp4 import _load_golden
 
 pytestmark = pytest.mark.gpu
 
 
 def _gpu_quantize(w_np, dev, bf16=False, layout="row_major"):
+    """Quantise on the GPU into guarded outputs (sentinel bytes around codes, scales and s_t, checked
+    untouched) and download them as row-major arrays."""
     if bf16:
         wt = bf16_to_dev(bf16_bits(w_np), dev)
     else:
         wt = f32_to_dev(w_np, dev)
-    return nvfp4_from_dev(fr.nvfp4_quantize(wt, layout=layout))
+    n, k = w_np.shape
+    lib = fr.load_library()
+    lay = 1 if layout == "tiled" else 0
+    cbuf, codes = guarded((lib.fp4rl_nvfp4_codes_bytes(n, k, lay),), torch.uint8, dev)
+    sbuf, scales = guarded((lib.fp4rl_nvfp4_scales_bytes(n, k, lay),), torch.uint8, dev)
+    tbuf, ts = guarded((1,), torch.float32, dev)
+    out = fr.NVFP4Weight(codes, scales, ts, n, k, layout)
+    fr.nvfp4_quantize(wt, layout=layout, out=out)
+    torch.cuda.synchronize()
+    for buf, what in ((cbuf, "codes"), (sbuf, "scales"), (tbuf, "tensor scale")):
+        assert_guards(buf, f"quantiser {what} {n}x{k} {layout}")
+    return nvfp4_from_dev(out)
 
 
 def _assert_exact(got, want, what):
@@ -113,19 +126,14 @@ def test_adversarial_midpoints():
     _assert_exact(_gpu_quantize(w, dev), nvfp4.quantize(w), "adversarial")
 
 
-def test_full_size_14b_heavy_tailed():
-    """14B shapes, Student-t(3) x0.02 with 1e-4 outliers x50: whole qkv matrix, sampled gate rows."""
+@pytest.mark.parametrize("name", ["qkv", "o", "gate", "up", "down"])
+def test_full_size_14b_heavy_tailed(name):
+    """Every 14B matrix shape, whole, Student-t(3) x0.02 with 1e-4 outliers x50, byte-exact."""
     dev = device()
-    n, k = QWEN25_14B["qkv"]
-    w = student_t3_weights((n, k), tensor_seed(4, 0, "qkv"))
-    say(f"quantize 14B qkv {n}x{k} full")
-    _assert_exact(_gpu_quantize(w, dev), nvfp4.quantize(w), "14B qkv")
-    n, k = QWEN25_14B["gate"]
-    w = student_t3_weights((n, k), tensor_seed(4, 0, "gate"))
-    rows = np.sort(np.random.default_rng(1).choice(n, 384, replace=False))
-    say(f"quantize 14B gate {n}x{k}, {len(rows)} sampled rows")
-    c, s, t = _gpu_quantize(w, dev)
-    _assert_exact((c[rows], s[rows], t), nvfp4.quantize_rows(w, rows), "14B gate rows")
+    n, k = QWEN25_14B[name]
+    w = student_t3_weights((n, k), tensor_seed(4, 0, name))
+    say(f"quantize 14B {name} {n}x{k} full")
+    _assert_exact(_gpu_quantize(w, dev), nvfp4.quantize(w), f"14B {name}")
 
 
 def test_tiled_layout_and_repack():

@@ -101,3 +101,24 @@ def test_lora_down_catches_a_dropped_scale_or_transposed_adapter():
     eye = bf16_bits(np.eye(k, dtype=np.float32))
     y = linear.lora_linear(x, zc, zs, np.float32(0.0), a, eye, s)
     assert np.array_equal(y, bf16_round(ex))
+
+
+def test_magnitude_sums():
+    """On non-negative operands the magnitude sums are the linear itself; elsewhere they bound |y|."""
+    rng = np.random.default_rng(9)
+    m, n, k, r = 3, 20, 64, 4
+    w = np.abs(rng.standard_normal((n, k)).astype(np.float32)) * np.float32(0.02)
+    x = bf16_bits(np.abs(rng.standard_normal((m, k), dtype=np.float32)))
+    a = bf16_bits(np.abs(rng.standard_normal((r, k), dtype=np.float32)) * np.float32(0.05))
+    b = bf16_bits(np.abs(rng.standard_normal((n, r), dtype=np.float32)) * np.float32(0.05))
+    codes, scales, st = quantize(w)
+    base, lora = linear.lora_linear_magnitude_f64(x, codes, scales, st, a, b, 2.0)
+    assert np.allclose(base + lora, linear.lora_linear_f64(x, codes, scales, st, a, b, 2.0), rtol=1e-13)
+    assert np.allclose(base, linear.lora_linear_f64(x, codes, scales, st), rtol=1e-13)
+    w2, x2, a2, b2 = _case(10, m, n, k, r)
+    q2 = quantize(w2)
+    base2, lora2 = linear.lora_linear_magnitude_f64(x2, *q2, a2, b2, -2.0)
+    y2 = linear.lora_linear_f64(x2, *q2, a2, b2, -2.0)
+    assert np.all(np.abs(y2) <= (base2 + lora2) * (1 + 1e-12))
+    rows = np.array([3, 0, 19])
+    assert np.array_equal(linear.lora_linear_magnitude_f64(x2, *q2, a2, b2, 2.0, rows=rows)[0], base2[:, rows])

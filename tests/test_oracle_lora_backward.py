@@ -106,3 +106,21 @@ def test_adapter_terms_match_exact_rationals():
                 assert np.isclose(h[mm, j], 2.0 * sum(dyv[mm, i] * bv[i, j] for i in range(n)), rtol=1e-12)
         _, _, db_all = lb.adapter_terms_f64(dy, x, a, b, 2.0)
         assert np.allclose(db_all, db_w, rtol=1e-12, atol=1e-300)
+
+
+def test_backward_magnitudes():
+    """On non-negative operands the magnitude sums are the backward's own results; elsewhere they bound them."""
+    rng = np.random.default_rng(50)
+    m, n, k, r = 4, 24, 48, 3
+    pos = (lambda shape, sc: bf16_bits(np.abs(rng.standard_normal(shape, dtype=np.float32)) * np.float32(sc)))
+    dy, x, a, b = pos((m, n), 0.1), pos((m, k), 1.0), pos((r, k), 0.05), pos((n, r), 0.05)
+    codes, scales, st = quantize(np.abs(rng.standard_normal((n, k))).astype(np.float32) * np.float32(0.02))
+    dxb, dxl, da_m, db_m = lb.backward_magnitudes_f64(dy, x, codes, scales, st, a, b, 2.0)
+    dx, da, db = lb.lora_linear_backward_f64(dy, x, codes, scales, st, a, b, 2.0)
+    assert np.allclose(dxb + dxl, dx, rtol=1e-13) and np.allclose(da_m, da, rtol=1e-13)
+    assert np.allclose(db_m, db, rtol=1e-13)
+    dy2, x2, c2, s2, t2, a2, b2 = _case(51, m, n, k, r)
+    dxb, dxl, da_m, db_m = lb.backward_magnitudes_f64(dy2, x2, c2, s2, t2, a2, b2, -2.0)
+    dx, da, db = lb.lora_linear_backward_f64(dy2, x2, c2, s2, t2, a2, b2, -2.0)
+    assert np.all(np.abs(dx) <= (dxb + dxl) * (1 + 1e-12)) and np.all(np.abs(da) <= da_m * (1 + 1e-12))
+    assert np.all(np.abs(db) <= db_m * (1 + 1e-12))
