@@ -69,6 +69,14 @@ def parse_args():
                    help="time only the LoRA backward of the 7B layer at 8192 tokens (--steps passes)")
     p.add_argument("--fp8-only", action="store_true",
                    help="time only the FP8 (E4M3) linears of the 7B layer: decode 1..64 tokens and the prefill")
+    p.add_argument("--prefill-only", action="store_true",
+                   help="time only the 7B layer's five linears at 8192 tokens (for counter runs)")
+    p.add_argument("--decode32b-only", action="store_true",
+                   help="time only the 32B decode pass at 128 tokens (for counter runs)")
+    p.add_argument("--layers32b", type=int, default=64, help="layers of the 32B decode pass")
+    p.add_argument("--summarize-mfma", nargs=2, metavar=("PMC_DIR", "WORKLOAD"),
+                   help="no GPU work: summarise a rocprofv3 --pmc run of the MFMA counters into "
+                        "profiles/mfma_counters.json")
     p.add_argument("--copy-calibration-mib", type=int, default=0,
                    help="first run a plain device-to-device copy of this many MiB three times (the reference "
                         "kernel that scales rocprofv3 FETCH_SIZE / WRITE_SIZE to bytes)")
@@ -129,7 +137,7 @@ def cpu_baseline(target_s: float):
     finally:
         os.sched_setaffinity(0, affinity)
     gbs = total_b / el / 1e9
-    return {"value": round(gbs, 6), "unit": "GB/s", "cores": 1, "kind": "oracle",
+    return {"value": round(gbs, 6), "unit": "GB/s", "cores": 1, "kind": "oracle", "cpu_model": cpu_model(),
             "sample": f"1/{frac} of every linear's output rows (qkv, o, gate, up, down), all of M = "
                       f"{list(TOKENS)}, AQN RMSNorm on the full token rows; {passes} pass(es) in {el:.1f} s "
                       f"on one core ({os.cpu_count()} visible)"}
@@ -150,16 +158,96 @@ def build_layer(torch, fr, dev, shapes, seed):
 
 
 PMC_TRAFFIC = os.path.join(ROOT, "profiles", "fp4_lora_linear_qwen25_7b_decode_pmc_traffic.json")
+MFMA_COUNTERS = os.path.join(ROOT, "profiles", "mfma_counters.json")
 KERNEL_SOURCES = ("linear.hip", "device.hpp", "launch.hpp")
+MFMA_SOURCES = ("linear.hip", "device.hpp", "launch.hpp", "backward.hip", "gemm_nt.hpp")
+MFMA_PMC = ("SQ_VALU_MFMA_BUSY_CYCLES", "GRBM_GUI_ACTIVE", "SQ_INSTS_VALU_MFMA_MOPS_BF16", "SQ_INSTS_MFMA",
+            "SQ_INSTS_VALU", "SQ_BUSY_CU_CYCLES")
+SIMDS = 1024  # 256 CUs x 4 SIMDs
+XCDS = 8      # GRBM_GUI_ACTIVE comes summed over the XCDs' graphics blocks (the busy time is the per-XCD value)
 
 
-def kernel_source_sha():
-    """Hash of the linear kernel sources: counter readings are void once these change."""
+def kernel_source_sha(files=KERNEL_SOURCES):
+    """Hash of the kernel sources: counter readings are void once these change."""
     h = hashlib.sha256()
-    for f in KERNEL_SOURCES:
+    for f in files:
         with open(os.path.join(ROOT, "fp4_quantized_rl_amd", "csrc", f), "rb") as fh:
             h.update(fh.read())
     return h.hexdigest()[:16]
+
+
+def mfma_roofline(achieved_tflops, kernels, workload=None):
+    """The roofline block of an MFMA-bound extra: achieved vs the dense bf16 peak, with the MFMA busy
+    fraction of its main kernels from the committed counter summary when that is current."""
+    out = {"bound": "mfma", "achieved": round(achieved_tflops, 2), "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
+           "frac": round(achieved_tflops / BF16_PEAK_TFLOPS, 4), "mfma_busy": None}
+    if os.path.exists(MFMA_COUNTERS):
+        with open(MFMA_COUNTERS) as fh:
+            rec = json.load(fh)
+        if rec.get("kernel_source_sha") == kernel_source_sha(MFMA_SOURCES):
+            busy = {k: v["mfma_busy"] for k, v in rec.get("kernels", {}).items()
+                    if any(same_kernel(v.get("kernel", k), name) for name in kernels)
+                    and (workload is None or v.get("workload") == workload)}
+            out["mfma_busy"] = busy or None
+    return out
+
+
+def summarize_mfma(pmc_dir, workload, command):
+    """MFMA busy fraction and bf16 MFMA ops per dispatch of every library kernel in a rocprofv3 --pmc run."""
+    import csv
+    import glob
+    rows = {}
+    for f in sorted(glob.glob(os.path.join(pmc_dir, "**", "*counter_collection.csv"), recursive=True)):
+        with open(f, newline="") as fh:
+            for r in csv.DictReader(fh):
+                key = (r["Kernel_Name"], r.get("Dispatch_Id", r.get("Correlation_Id", "")))
+                rows.setdefault(key, {})[r["Counter_Name"]] = float(r["Counter_Value"])
+    if not rows:
+        raise SystemExit(f"no counter rows under {pmc_dir}")
+    per = {}
+    for (kname, _), c in rows.items():
+        if not all(n in c for n in MFMA_PMC):
+            continue
+        short = short_kernel_name(kname)
+        if not any(t in short for t in ("prefill_kernel", "splitk_kernel", "nt_gemm_kernel", "skinny_kernel",
+                                          "gemv_kernel", "fp8_decode_kernel", "gate_up_kernel")):
+            continue
+        d = per.setdefault(short, {"dispatches": 0, "busy": 0.0, "gui": 0.0, "mops": 0.0, "mfma": 0.0,
+                                   "valu": 0.0, "busy_cu": 0.0})
+        d["dispatches"] += 1
+        d["busy"] += c["SQ_VALU_MFMA_BUSY_CYCLES"]
+        d["gui"] += c["GRBM_GUI_ACTIVE"]
+        d["mops"] += c["SQ_INSTS_VALU_MFMA_MOPS_BF16"]
+        d["mfma"] += c["SQ_INSTS_MFMA"]
+        d["valu"] += c["SQ_INSTS_VALU"]
+        d["busy_cu"] += c["SQ_BUSY_CU_CYCLES"]
+    kernels = {}
+    for k, d in sorted(per.items()):
+        n = d["dispatches"]
+        kernels[f"{k} @ {workload}"] = {"kernel": k, "workload": workload, "dispatches": n,
+                      "mfma_busy": round(d["busy"] * XCDS / (d["gui"] * SIMDS), 4) if d["gui"] else None,
+                      "bf16_mfma_flops_per_dispatch": d["mops"] * 512 / n,
+                      "mfma_instructions_per_dispatch": d["mfma"] / n,
+                      "valu_per_mfma": round(d["valu"] / d["mfma"], 2) if d["mfma"] else None,
+                      "gpu_active_cycles_per_dispatch": d["gui"] / n}
+    rec = {"what": "rocprofv3 --pmc " + " ".join(MFMA_PMC) + ", per dispatch, summed over each kernel's "
+                   "dispatches; mfma_busy = SQ_VALU_MFMA_BUSY_CYCLES / (GRBM_GUI_ACTIVE / 8 XCDs x 1024 SIMDs) "
+                   "(the counter file sums GRBM_GUI_ACTIVE over the 8 XCDs: its eighth at ~2.3 GHz matches the "
+                   "kernel-trace durations); bf16 MFMA flops = SQ_INSTS_VALU_MFMA_MOPS_BF16 x 512",
+           "command": command, "kernel_source_sha": kernel_source_sha(MFMA_SOURCES), "kernels": kernels}
+    old = {}
+    if os.path.exists(MFMA_COUNTERS):
+        with open(MFMA_COUNTERS) as fh:
+            old = json.load(fh)
+    if old.get("kernel_source_sha") == rec["kernel_source_sha"]:  # merge runs of the same sources
+        merged = dict(old.get("kernels", {}))
+        merged.update(kernels)
+        rec["kernels"] = merged
+        rec["command"] = old.get("command", "") + " ;\n" + command
+    with open(MFMA_COUNTERS, "w") as fh:
+        json.dump(rec, fh, indent=1)
+        fh.write("\n")
+    print(json.dumps(rec, indent=1))
 
 
 def short_kernel_name(full):
@@ -307,6 +395,36 @@ def progress(msg):
     print(f"[bench] {msg}", file=sys.stderr, flush=True)
 
 
+def median_time(torch, fn):
+    """Median time of fn() over separate runs, each bracketed by HIP events on the current stream (every
+    library call runs there): at least 50 runs, or 10 when one run takes over 10 ms. Returns (s, runs)."""
+    import statistics
+    fn()
+    torch.cuda.synchronize()
+    times = []
+    while True:
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        fn()
+        e1.record()
+        e1.synchronize()
+        times.append(e0.elapsed_time(e1) * 1e-3)
+        need = 10 if statistics.median(times) > 10e-3 else 50
+        if len(times) >= need:
+            return statistics.median(times), len(times)
+
+
+def cpu_model():
+    try:
+        with open("/proc/cpuinfo") as fh:
+            for line in fh:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
 def copy_calibration(torch, dev, mib):
     """A plain device-to-device copy of known size, the yardstick for the traffic counters."""
     n = mib * 2**20 // 4
@@ -325,6 +443,9 @@ def main():
         return
     if args.summarize_trace:
         summarize_trace(*args.summarize_trace, args.command)
+        return
+    if args.summarize_mfma:
+        summarize_mfma(*args.summarize_mfma, args.command)
         return
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
@@ -375,14 +496,22 @@ def main():
               for k in sorted({k for _, k in shapes.values()})}
         print(json.dumps({"fp8_linear": run_fp8(torch, fr, dev, shapes, lora, xs, gb)}))
         return
+    if args.decode32b_only:
+        progress(f"32B decode pass, {args.layers32b} layers")
+        print(json.dumps({"decode_32b": run_decode_32b(torch, fr, dev, layers=args.layers32b)}))
+        return
+    if args.prefill_only:
+        progress("prefill timing")
+        print(json.dumps({"prefill": run_prefill(torch, fr, dev, shapes, layers[0], lora,
+                                                 torch.Generator(device=dev).manual_seed(21))[0]}))
+        return
     if args.backward_only:
         progress("LoRA backward timing")
         gb = torch.Generator(device=dev)
         gb.manual_seed(21)
         xs = {k: torch.randn((PREFILL_M, k), generator=gb, device=dev).to(torch.bfloat16)
               for k in sorted({k for _, k in shapes.values()})}
-        print(json.dumps({"lora_backward": run_backward(torch, fr, dev, shapes, layers[0], lora, xs, gb,
-                                                        max(1, args.steps))}))
+        print(json.dumps({"lora_backward": run_backward(torch, fr, dev, shapes, layers[0], lora, xs, gb)}))
         return
 
     # activations and preallocated outputs / workspaces per token count
@@ -541,12 +670,8 @@ def main():
     print(json.dumps(out))
 
 
-def run_extras(torch, fr, dev, shapes, layer, lora, fp32):
-    res = {}
-    g = torch.Generator(device=dev)
-    g.manual_seed(21)
-    # prefill: M = 8192 tokens (16 x 512) with 0.1% outlier channels x20
-    flops, ts = 0, []
+def run_prefill(torch, fr, dev, shapes, layer, lora, g):
+    """The 7B layer's five linears at M = 8192 tokens (16 x 512) with 0.1% outlier channels x20."""
     xs = {}
     for k in sorted({k for _, k in shapes.values()}):
         x = torch.randn((PREFILL_M, k), generator=g, device=dev)
@@ -563,21 +688,23 @@ def run_extras(torch, fr, dev, shapes, layer, lora, fp32):
             a, b = lora[name]
             fr.fp4_lora_linear(xs[k], layer[name], a, b, LORA_SCALE, out=ys[name], workspace=pws)
 
-    prefill_pass()
-    torch.cuda.synchronize()
-    reps = 3
-    t0 = time.perf_counter()
-    for _ in range(reps):
-        prefill_pass()
-    torch.cuda.synchronize()
-    dt = (time.perf_counter() - t0) / reps
+    dt, runs = median_time(torch, prefill_pass)
     flops = sum(linear_flops(PREFILL_M, n, k, RANK) for n, k in shapes.values())
-    res["prefill"] = {"M": PREFILL_M, "tflops": round(flops / dt / 1e12, 2), "ms_per_layer": round(dt * 1e3, 3),
-                      "frac_of_bf16_peak": round(flops / dt / 1e12 / BF16_PEAK_TFLOPS, 4)}
-    res["lora_backward"] = run_backward(torch, fr, dev, shapes, layer, lora, xs, g, reps)
+    del ys
+    return ({"M": PREFILL_M, "tflops": round(flops / dt / 1e12, 2), "ms_per_layer": round(dt * 1e3, 3),
+             "frac_of_bf16_peak": round(flops / dt / 1e12 / BF16_PEAK_TFLOPS, 4), "timing": f"median of {runs}",
+             "roofline": mfma_roofline(flops / dt / 1e12, ("prefill_kernel<2>",), "7B prefill 8192 tokens")}, xs)
+
+
+def run_extras(torch, fr, dev, shapes, layer, lora, fp32):
+    res = {}
+    g = torch.Generator(device=dev)
+    g.manual_seed(21)
+    res["prefill"], xs = run_prefill(torch, fr, dev, shapes, layer, lora, g)
+    res["lora_backward"] = run_backward(torch, fr, dev, shapes, layer, lora, xs, g)
     res["fp8_linear"] = run_fp8(torch, fr, dev, shapes, lora, xs, g)
     res["gate_up_silu"] = run_gate_up(torch, fr, dev, shapes, layer, lora, g)
-    del xs, ys
+    del xs
 
     # quantiser on 14B shapes: one layer's five matrices, 0.02 t(3) weights with
     # 1e-4 outliers x50, fp32 (and bf16) input -> NVFP4; the 48 layers repeat
@@ -590,13 +717,12 @@ def run_extras(torch, fr, dev, shapes, layer, lora, fp32):
         ws = w14 if dt == "fp32" else {name: w.to(torch.bfloat16) for name, w in w14.items()}
         outs = {name: fr.nvfp4_quantize(w) for name, w in ws.items()}
         torch.cuda.synchronize()
-        reps = 3
-        t0 = time.perf_counter()
-        for _ in range(reps):
+
+        def quantize_layer():
             for name, w in ws.items():
                 fr.nvfp4_quantize(w, out=outs[name])
-        torch.cuda.synchronize()
-        dt_s = (time.perf_counter() - t0) / reps
+
+        dt_s, runs = median_time(torch, quantize_layer)
         esz = 4 if dt == "fp32" else 2
         two_pass = params * (2 * esz + 0.5625)
         res[f"quantize_{dt}"] = {"shapes": "Qwen2.5-14B layer (qkv 7168x5120, o 5120x5120, gate/up 13824x5120, "
@@ -604,20 +730,17 @@ def run_extras(torch, fr, dev, shapes, layer, lora, fp32):
                                  "params_per_layer": params, "ms_per_layer": round(dt_s * 1e3, 3),
                                  "ms_48_layers": round(dt_s * 48e3, 2),
                                  "GB/s_two_pass": round(two_pass / dt_s / 1e9, 1),
-                                 "frac_of_hbm": round(two_pass / dt_s / 1e9 / HBM_PEAK_GBS, 4)}
+                                 "frac_of_hbm": round(two_pass / dt_s / 1e9 / HBM_PEAK_GBS, 4),
+                                 "timing": f"median of {runs}"}
         if dt == "fp32":
             # the same pass also writing the rounding record (1 bit per weight)
             recs = {name: torch.empty((w.shape[0], w.shape[1] // 8), dtype=torch.uint8, device=dev)
                     for name, w in ws.items()}
-            for name, w in ws.items():
-                fr.nvfp4_quantize(w, out=outs[name], round_up=recs[name])
-            torch.cuda.synchronize()
-            t0 = time.perf_counter()
-            for _ in range(reps):
+            def quantize_layer_record():
                 for name, w in ws.items():
                     fr.nvfp4_quantize(w, out=outs[name], round_up=recs[name])
-            torch.cuda.synchronize()
-            dt_r = (time.perf_counter() - t0) / reps
+
+            dt_r, _ = median_time(torch, quantize_layer_record)
             rec_bytes = two_pass + params / 8
             res["quantize_fp32_with_rounding_record"] = {
                 "ms_per_layer": round(dt_r * 1e3, 3), "GB/s_two_pass": round(rec_bytes / dt_r / 1e9, 1),
@@ -633,22 +756,23 @@ def run_extras(torch, fr, dev, shapes, layer, lora, fp32):
     x = torch.randn((m, d), generator=g, device=dev).to(torch.bfloat16)
     y = torch.empty_like(x)
     w = torch.ones(d, dtype=torch.float32, device=dev)
-    fr.aqn_rmsnorm(x, w, SIGMA, 4, 0, 0, EPS, out=y)
-    torch.cuda.synchronize()
-    reps = 10
-    t0 = time.perf_counter()
-    for kk in range(reps):
-        fr.aqn_rmsnorm(x, w, fr.aqn_sigma(1e-2, 5e-4, kk, 10), 4, kk, 0, EPS, out=y)
-    torch.cuda.synchronize()
-    dt = (time.perf_counter() - t0) / reps
-    res["aqn_rmsnorm"] = {"shape": [m, d], "us_per_call": round(dt * 1e6, 2),
+    sigmas = [fr.aqn_sigma(1e-2, 5e-4, kk, 10) for kk in range(10)]
+    stage = [0]
+
+    def aqn_call():  # the ten stages of the schedule in turn
+        kk = stage[0] % 10
+        stage[0] += 1
+        fr.aqn_rmsnorm(x, w, sigmas[kk], 4, kk, 0, EPS, out=y)
+
+    dt, runs = median_time(torch, aqn_call)
+    res["aqn_rmsnorm"] = {"shape": [m, d], "us_per_call": round(dt * 1e6, 2), "timing": f"median of {runs}",
                           "GB/s": round(4 * m * d / dt / 1e9, 1), "frac_of_hbm": round(4 * m * d / dt / 1e9 / HBM_PEAK_GBS, 4)}
     del x, y
     res["decode_32b"] = run_decode_32b(torch, fr, dev)
     return res
 
 
-def run_backward(torch, fr, dev, shapes, layer, lora, xs, g, reps):
+def run_backward(torch, fr, dev, shapes, layer, lora, xs, g):
     """Backward through the frozen base (the training half of the step): the
     layer's five linears and adapters, M = 8192 tokens, dY ~ N(0, 0.05^2);
     dX, dA and dB of every linear per pass."""
@@ -662,18 +786,14 @@ def run_backward(torch, fr, dev, shapes, layer, lora, xs, g, reps):
             a, b = lora[name]
             fr.fp4_lora_linear_backward(dys[name], xs[k], layer[name], a, b, LORA_SCALE, workspace=bws)
 
-    backward_pass()
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    for _ in range(reps):
-        backward_pass()
-    torch.cuda.synchronize()
-    dt = (time.perf_counter() - t0) / reps
+    dt, runs = median_time(torch, backward_pass)
     # dX base 2MNK; LoRA: t and dA 2MrK each, h and dB 2MNr each, the dX LoRA term 2MrK
     bflops = sum(2 * PREFILL_M * n * k + 2 * PREFILL_M * RANK * (3 * k + 2 * n) for n, k in shapes.values())
     return {"M": PREFILL_M, "r": RANK, "tflops": round(bflops / dt / 1e12, 2), "ms_per_layer": round(dt * 1e3, 3),
-            "frac_of_bf16_peak": round(bflops / dt / 1e12 / BF16_PEAK_TFLOPS, 4),
-            "workspace_GB": round(bws.numel() / 1e9, 3)}
+            "frac_of_bf16_peak": round(bflops / dt / 1e12 / BF16_PEAK_TFLOPS, 4), "timing": f"median of {runs}",
+            "workspace_GB": round(bws.numel() / 1e9, 3),
+            "roofline": mfma_roofline(bflops / dt / 1e12, ("nt_gemm_kernel<true, 1, false>",),
+                                      "7B LoRA backward 8192 tokens")}
 
 
 def run_fp8(torch, fr, dev, shapes, lora, xs, g):
@@ -696,21 +816,16 @@ def run_fp8(torch, fr, dev, shapes, lora, xs, g):
                 a, b = lora[name]
                 fr.fp8_lora_linear(xm[k], w8[name], a, b, LORA_SCALE, out=ys[name], workspace=wss[name])
 
-        one()
-        torch.cuda.synchronize()
-        reps = 3 if m == PREFILL_M else 20
-        t0 = time.perf_counter()
-        for _ in range(reps):
-            one()
-        torch.cuda.synchronize()
-        dt = (time.perf_counter() - t0) / reps
+        dt, runs = median_time(torch, one)
         flops = sum(linear_flops(m, n, k, RANK) for n, k in shapes.values())
         if m == PREFILL_M:
             out["prefill"] = {"M": m, "ms_per_layer": round(dt * 1e3, 3), "tflops": round(flops / dt / 1e12, 2),
-                              "frac_of_bf16_peak": round(flops / dt / 1e12 / BF16_PEAK_TFLOPS, 4)}
+                              "frac_of_bf16_peak": round(flops / dt / 1e12 / BF16_PEAK_TFLOPS, 4),
+                              "timing": f"median of {runs}"}
         else:
             out[f"decode_M{m}"] = {"us_per_layer": round(dt * 1e6, 1), "weight_GB/s": round(wbytes / dt / 1e9, 1),
-                                   "frac_of_hbm": round(wbytes / dt / 1e9 / HBM_PEAK_GBS, 4)}
+                                   "frac_of_hbm": round(wbytes / dt / 1e9 / HBM_PEAK_GBS, 4),
+                                   "timing": f"median of {runs}"}
         del ys, wss
     return out
 
@@ -738,13 +853,7 @@ def run_gate_up(torch, fr, dev, shapes, layer, lora, g):
 
         res = {}
         for name, f in (("fused_us", fused), ("two_linears_us", separate)):
-            f()
-            torch.cuda.synchronize()
-            t0 = time.perf_counter()
-            for _ in range(50):
-                f()
-            torch.cuda.synchronize()
-            res[name] = round((time.perf_counter() - t0) / 50 * 1e6, 1)
+            res[name] = round(median_time(torch, f)[0] * 1e6, 1)
         if m <= 128:
             # the AQN RMSNorm folded in (raw x in, normalised tokens never stored)
             # against the norm launch followed by the fused projections
@@ -765,13 +874,7 @@ def run_gate_up(torch, fr, dev, shapes, layer, lora, g):
                                     workspace=gws)
 
             for name, f in (("aqn_folded_us", folded), ("aqn_then_fused_us", norm_then_fused)):
-                f()
-                torch.cuda.synchronize()
-                t0 = time.perf_counter()
-                for _ in range(50):
-                    f()
-                torch.cuda.synchronize()
-                res[name] = round((time.perf_counter() - t0) / 50 * 1e6, 1)
+                res[name] = round(median_time(torch, f)[0] * 1e6, 1)
         res["fused_weight_GB/s"] = round(wbytes / res["fused_us"] / 1e3, 1)
         res["fused_frac_of_hbm"] = round(wbytes / res["fused_us"] / 1e3 / HBM_PEAK_GBS, 4)
         out[f"M{m}"] = res
@@ -821,14 +924,7 @@ def run_decode_32b(torch, fr, dev, layers=64, m=128, r=RANK_32B):
     gr = torch.cuda.CUDAGraph()
     with torch.cuda.graph(gr):
         one_pass()
-    gr.replay()
-    torch.cuda.synchronize()
-    reps = 3
-    t0 = time.perf_counter()
-    for _ in range(reps):
-        gr.replay()
-    torch.cuda.synchronize()
-    dt = (time.perf_counter() - t0) / reps
+    dt, runs = median_time(torch, gr.replay)
     wbytes = layers * sum(nvfp4_bytes(n, k) for n, k in shapes.values())
     flops = layers * sum(linear_flops(m, n, k, r) for n, k in shapes.values())
     total_bytes = layers * (sum(nvfp4_bytes(n, k) + 2 * r * (k + n) + 2 * m * (k + n) for n, k in shapes.values())
@@ -838,7 +934,10 @@ def run_decode_32b(torch, fr, dev, layers=64, m=128, r=RANK_32B):
     return {"layers": layers, "M": m, "lora_rank": r, "ms_per_pass": round(dt * 1e3, 3),
             "weight_GB/s": round(wbytes / dt / 1e9, 1), "tflops": round(flops / dt / 1e12, 1),
             "nvfp4_weight_bytes": wbytes, "roofline_ms": round(roof_s * 1e3, 3),
-            "frac_of_roofline": round(roof_s / dt, 4)}
+            "frac_of_roofline": round(roof_s / dt, 4), "timing": f"median of {runs} graph replays",
+            "roofline": mfma_roofline(flops / dt / 1e12, (fr.fp4_linear_kernel_name(m, 27648, 5120, r),
+                                                          fr.fp4_linear_kernel_name(m, 5120, 27648, r)),
+                                      "32B decode 128 tokens")}
 
 
 if __name__ == "__main__":
