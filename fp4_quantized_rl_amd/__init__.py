@@ -13,7 +13,8 @@ Operations (names follow the C ABI):
   fp4_lora_linear(x, wq, lora_a, lora_b, s) -> y = x deq(Wq)^T + s (x A^T) B^T  (bf16)
   lora_down / fp4_linear_lora_up            -> the two halves of fp4_lora_linear
   fp4_lora_linear_backward(dy, x, wq, A, B, s) -> (dx bf16, dA fp32, dB fp32), the base frozen
-  fp8_quantize(w) / fp8_lora_linear(x, w8, A, B, s) -> FP8 (E4M3, per-row scale) rollout weights, W8A16
+  fp8_quantize(w) / fp8_lora_linear(x, w8, A, B, s, w8a8=False) -> FP8 (E4M3, per-row scale) rollout
+  weights, W8A16 or W8A8 (per-token activation scales)
   fp4_gate_up_silu(x, wg, wu, (Ag, Bg), (Au, Bu), s) -> bf16(SiLU(x Wg^T + ...) * (x Wu^T + ...)), one launch
   aqn_sigma(s0, s1, k, K)                   -> exponential AQN noise level
   aqn_rmsnorm(x, w, sigma, seed, step, ...) -> RMSNorm with W_noise = w + sigma z
@@ -80,6 +81,9 @@ _SIGNATURES = {
     "fp4rl_fp8_quantize": (_STATUS, [_P, _c.c_int32, _I64, _I64, _P, _P, _P]),
     "fp4rl_fp8_lora_linear_workspace": (_c.c_size_t, [_I64, _I64, _I64, _I64]),
     "fp4rl_fp8_lora_linear": (_STATUS, [_P, _I64, _I64, _I64, _P, _P, _P, _P, _I64, _c.c_float, _P, _P, _c.c_size_t,
+                                        _P]),
+    "fp4rl_fp8_lora_linear_w8a8_workspace": (_c.c_size_t, [_I64, _I64, _I64, _I64]),
+    "fp4rl_fp8_lora_linear_w8a8": (_STATUS, [_P, _I64, _I64, _I64, _P, _P, _P, _P, _I64, _c.c_float, _P, _P, _c.c_size_t,
                                         _P]),
     "fp4rl_fp4_lora_linear_backward_workspace": (_c.c_size_t, [_I64, _I64, _I64, _I64, _c.c_int32]),
     "fp4rl_fp4_lora_linear_backward": (_STATUS, [_P, _P, _I64, _I64, _I64, _P, _P, _P, _P, _P, _I64, _c.c_float,
@@ -373,12 +377,20 @@ def fp8_quantize(w) -> FP8Weight:
     return FP8Weight(codes, scales)
 
 
-def fp8_lora_linear_workspace_bytes(m: int, n: int, k: int, r: int) -> int:
-    return load_library().fp4rl_fp8_lora_linear_workspace(m, n, k, r)
+def fp8_lora_linear_workspace_bytes(m: int, n: int, k: int, r: int, w8a8: bool = False) -> int:
+    lib = load_library()
+    if w8a8:
+        return lib.fp4rl_fp8_lora_linear_w8a8_workspace(m, n, k, r)
+    return lib.fp4rl_fp8_lora_linear_workspace(m, n, k, r)
 
 
-def fp8_lora_linear(x, w8: FP8Weight, lora_a=None, lora_b=None, lora_scale: float = 0.0, out=None, workspace=None):
-    """y = bf16(x deq(W8)^T + lora_scale (x A^T) B^T); x bf16 [m, k]."""
+def fp8_lora_linear(x, w8: FP8Weight, lora_a=None, lora_b=None, lora_scale: float = 0.0, out=None, workspace=None,
+                    w8a8: bool = False):
+    """y = bf16(x deq(W8)^T + lora_scale (x A^T) B^T); x bf16 [m, k].
+
+    w8a8: quantise the tokens too (one E4M3 scale per row of x) and run the
+    base product on the FP8 matrix cores; the LoRA term reads the bf16 x.
+    """
     torch = _torch()
     _dev_tensor(x, "x", (torch.bfloat16,), 2)
     _dev_tensor(w8.codes, "codes", (torch.uint8,), 2)
@@ -397,13 +409,14 @@ def fp8_lora_linear(x, w8: FP8Weight, lora_a=None, lora_b=None, lora_scale: floa
     if out is None:
         out = torch.empty((m, n), dtype=torch.bfloat16, device=x.device)
     lib = load_library()
-    need = lib.fp4rl_fp8_lora_linear_workspace(m, n, k, r)
+    need = fp8_lora_linear_workspace_bytes(m, n, k, r, w8a8)
     if workspace is None:
         workspace = torch.empty(max(need, 256), dtype=torch.uint8, device=x.device)
+    call, name = ((lib.fp4rl_fp8_lora_linear_w8a8, "fp8_lora_linear_w8a8") if w8a8
+                  else (lib.fp4rl_fp8_lora_linear, "fp8_lora_linear"))
     with torch.cuda.device(x.device):
-        _check(lib.fp4rl_fp8_lora_linear(_ptr(x), m, n, k, _ptr(w8.codes), _ptr(w8.scales), _ptr(lora_a),
-                                         _ptr(lora_b), r, float(lora_scale), _ptr(out), _ptr(workspace),
-                                         workspace.numel(), _stream(x.device)), "fp8_lora_linear")
+        _check(call(_ptr(x), m, n, k, _ptr(w8.codes), _ptr(w8.scales), _ptr(lora_a), _ptr(lora_b), r,
+                    float(lora_scale), _ptr(out), _ptr(workspace), workspace.numel(), _stream(x.device)), name)
     return out
 
 

@@ -631,15 +631,23 @@ static fp4rl_status check_fp8_shape(int64_t m, int64_t n, int64_t k, int64_t r) 
   return FP4RL_OK;
 }
 
-size_t fp4rl_fp8_lora_linear_workspace(int64_t m, int64_t n, int64_t k, int64_t r) {
+static size_t fp8_workspace(int64_t m, int64_t n, int64_t k, int64_t r, bool a8) {
   if (check_fp8_shape(m, n, k, r) != FP4RL_OK || m == 0 || n == 0) return 0;
-  return fp4rl::fp8_linear_workspace(m, n, k, r, nullptr, nullptr);
+  return fp4rl::fp8_linear_workspace(m, n, k, r, a8, nullptr, nullptr);
 }
 
-fp4rl_status fp4rl_fp8_lora_linear(const uint16_t* x, int64_t m, int64_t n, int64_t k, const uint8_t* codes,
-                                   const float* row_scales, const uint16_t* lora_a, const uint16_t* lora_b, int64_t r,
-                                   float lora_scale, uint16_t* y, void* workspace, size_t workspace_bytes,
-                                   fp4rl_stream stream) {
+size_t fp4rl_fp8_lora_linear_workspace(int64_t m, int64_t n, int64_t k, int64_t r) {
+  return fp8_workspace(m, n, k, r, false);
+}
+
+size_t fp4rl_fp8_lora_linear_w8a8_workspace(int64_t m, int64_t n, int64_t k, int64_t r) {
+  return fp8_workspace(m, n, k, r, true);
+}
+
+static fp4rl_status fp8_linear(const char* name, bool a8, const uint16_t* x, int64_t m, int64_t n, int64_t k,
+                               const uint8_t* codes, const float* row_scales, const uint16_t* lora_a,
+                               const uint16_t* lora_b, int64_t r, float lora_scale, uint16_t* y, void* workspace,
+                               size_t workspace_bytes, fp4rl_stream stream) {
   FP4RL_CHECK(check_fp8_shape(m, n, k, r));
   FP4RL_REQUIRE(std::isfinite(lora_scale), FP4RL_ERR_VALUE, "lora_scale is not finite");
   FP4RL_REQUIRE((lora_a == nullptr) == (lora_b == nullptr), FP4RL_ERR_NULL,
@@ -651,16 +659,32 @@ fp4rl_status fp4rl_fp8_lora_linear(const uint16_t* x, int64_t m, int64_t n, int6
                 "x, codes and y must be 16-byte aligned, row_scales 4-byte aligned");
   if (r > 0)
     FP4RL_REQUIRE(aligned(lora_a, 16) && aligned(lora_b, 16), FP4RL_ERR_ALIGN, "lora_a and lora_b must be 16-byte aligned");
-  const size_t need = fp4rl::fp8_linear_workspace(m, n, k, r, nullptr, nullptr);
+  const size_t need = fp4rl::fp8_linear_workspace(m, n, k, r, a8, nullptr, nullptr);
   FP4RL_REQUIRE(workspace != nullptr && workspace_bytes >= need, FP4RL_ERR_WORKSPACE, "workspace %zu < %zu bytes",
                 workspace_bytes, need);
   FP4RL_REQUIRE(aligned(workspace, 256), FP4RL_ERR_ALIGN, "workspace must be 256-byte aligned");
   FP4RL_CHECK(check_device());
   fp4rl::Fp8Ws w;
-  fp4rl::fp8_linear_workspace(m, n, k, r, &w, workspace);
+  fp4rl::fp8_linear_workspace(m, n, k, r, a8, &w, workspace);
   return launched(fp4rl::launch_fp8_linear(x, m, n, k, codes, row_scales, r > 0 ? lora_a : nullptr,
-                                           r > 0 ? lora_b : nullptr, r, lora_scale, y, w, stream),
-                  "fp8_lora_linear");
+                                           r > 0 ? lora_b : nullptr, r, lora_scale, a8, y, w, stream),
+                  name);
+}
+
+fp4rl_status fp4rl_fp8_lora_linear(const uint16_t* x, int64_t m, int64_t n, int64_t k, const uint8_t* codes,
+                                   const float* row_scales, const uint16_t* lora_a, const uint16_t* lora_b, int64_t r,
+                                   float lora_scale, uint16_t* y, void* workspace, size_t workspace_bytes,
+                                   fp4rl_stream stream) {
+  return fp8_linear("fp8_lora_linear", false, x, m, n, k, codes, row_scales, lora_a, lora_b, r, lora_scale, y,
+                    workspace, workspace_bytes, stream);
+}
+
+fp4rl_status fp4rl_fp8_lora_linear_w8a8(const uint16_t* x, int64_t m, int64_t n, int64_t k, const uint8_t* codes,
+                                        const float* row_scales, const uint16_t* lora_a, const uint16_t* lora_b,
+                                        int64_t r, float lora_scale, uint16_t* y, void* workspace,
+                                        size_t workspace_bytes, fp4rl_stream stream) {
+  return fp8_linear("fp8_lora_linear_w8a8", true, x, m, n, k, codes, row_scales, lora_a, lora_b, r, lora_scale, y,
+                    workspace, workspace_bytes, stream);
 }
 
 // --------------------------------------------------------------------- AQN --

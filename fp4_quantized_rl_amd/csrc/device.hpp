@@ -94,6 +94,18 @@ __device__ __forceinline__ f32x4 mfma16x16x32(bf16x8 a, bf16x8 b, f32x4 c) {
   return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
 }
 
+typedef int32_t i32x8 __attribute__((ext_vector_type(8)));
+
+// 16 x 16 x 128 product of OCP E4M3 bytes (32 per lane, the same lane/slot
+// layout for both operands), unit block scales (E8M0 127 = 2^0)
+__device__ __forceinline__ f32x4 mfma16x16x128_e4m3(i32x8 a, i32x8 b, f32x4 c) {
+  return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, c, 0, 0, 0, 127, 0, 127);
+}
+__device__ __forceinline__ i32x8 as_i32x8(uint4 lo, uint4 hi) {
+  return i32x8{(int32_t)lo.x, (int32_t)lo.y, (int32_t)lo.z, (int32_t)lo.w,
+               (int32_t)hi.x, (int32_t)hi.y, (int32_t)hi.z, (int32_t)hi.w};
+}
+
 __device__ __forceinline__ f32x16 mfma32x32x16(bf16x8 a, bf16x8 b, f32x16 c) {
   return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
 }

@@ -1,4 +1,5 @@
-// FP8 (OCP E4M3) rollout weights and their W8A16 linear with LoRA (gfx950).
+// FP8 (OCP E4M3) rollout weights and their W8A16 / W8A8 linear with LoRA
+// (gfx950).
 //
 // Low-precision rollout engines commonly run the policy in FP8 while the
 // trainer keeps BF16 (gist.science summary of adaptive importance sampling
@@ -12,7 +13,7 @@
 // Kernels:
 //   fp8_quantize_kernel: one workgroup per row: the row's amax (exact max of
 //     |w| bit patterns), s_n, then the codes, 16 bytes per store.
-//   nt_gemm_kernel<false, 1, true>: x (bf16) against the E4M3 rows, converted
+//   nt_gemm_kernel<false, 1, kNtR8>: x (bf16) against the E4M3 rows, converted
 //     to bf16 exactly on the way into LDS (v_cvt_pk_f32_fp8), fp32
 //     accumulation scaled per row by s_n; the contraction is split over
 //     workgroups when there are few output tiles (decode), partials fp32.
@@ -21,6 +22,11 @@
 //   bf16 y in one launch, the LoRA term accumulated as a second contraction
 //   segment (t as bf16 hi | lo against B twice: lora_operands_kernel);
 //   split (decode), fp8_finish_kernel makes y = bf16(sum of slices + t . B[n]).
+// W8A8: the tokens are quantised like weight rows (one E4M3 scale per token,
+//   fp8_quantize_kernel into the workspace), the base product runs on the
+//   FP8 matrix cores with both operands as bytes (e4m3_decode_kernel,
+//   nt_gemm_kernel<., 1, kNtE4M3>), scaled by s_n xs[m]; the LoRA term still
+//   reads the bf16 tokens.
 #include <algorithm>
 
 #include "device.hpp"
@@ -260,18 +266,97 @@ __global__ __launch_bounds__(256) void fp8_decode_kernel(const uint16_t* __restr
   }
 }
 
-// K-slices of the decode kernel: about 512 workgroups (64-row groups x
-// slices), each slice a multiple of 64 and at least 256 long.
+// W8A8 decode: the same work split, with the tokens' E4M3 bytes x8 [M][K]
+// and per-token scales xs [M]. A chunk is 128 k; a lane loads bytes
+// 16 g .. + 15 and 64 + 16 g .. + 15 of its weight row's and token's chunk
+// straight into the FP8 MFMA's operand registers (no conversion; the same
+// slots on both operands). Partials are scaled by s_n xs[m].
+template <int T>
+__global__ __launch_bounds__(256) void e4m3_decode_kernel(const uint8_t* __restrict__ x8, const float* __restrict__ xs,
+                                                          int M, int N, int K, const uint8_t* __restrict__ codes,
+                                                          const float* __restrict__ scales, int slice,
+                                                          float* __restrict__ part) {
+  __shared__ f32x4 red[3][4 * T][64];
+  const int k0 = blockIdx.y * slice, klen = min(slice, K - k0);
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int li = lane & 15, lg = lane >> 4;
+  const int n0 = blockIdx.x * kDecRows;
+  const uint8_t* wrow[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) wrow[i] = codes + (int64_t)min(n0 + 16 * i + li, N - 1) * K + k0 + 16 * lg;
+  const uint8_t* xrow[T];  // tokens past M are clamped (their columns are never stored)
+#pragma unroll
+  for (int j = 0; j < T; ++j) xrow[j] = x8 + (int64_t)min(16 * j + li, M - 1) * K + k0 + 16 * lg;
+  f32x4 acc[4][T];
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < T; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+  const int nch = (klen + 127) / 128;
+  for (int c0 = wave; c0 < nch; c0 += 8) {
+    uint4 wv[2][4][2], xv[2][T][2];
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+      const int ch = c0 + 4 * u;
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        const int off = 128 * ch + 64 * h;
+        const bool in = ch < nch && off + 16 * lg < klen;  // klen % 16 == 0: all 16 bytes in or out
+#pragma unroll
+        for (int i = 0; i < 4; ++i) wv[u][i][h] = in ? ld_nt16(wrow[i] + off) : make_uint4(0u, 0u, 0u, 0u);
+#pragma unroll
+        for (int j = 0; j < T; ++j)
+          xv[u][j][h] = in ? *reinterpret_cast<const uint4*>(xrow[j] + off) : make_uint4(0u, 0u, 0u, 0u);
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < 2; ++u)
+#pragma unroll
+      for (int j = 0; j < T; ++j) {
+        const i32x8 b = as_i32x8(xv[u][j][0], xv[u][j][1]);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) acc[i][j] = mfma16x16x128_e4m3(as_i32x8(wv[u][i][0], wv[u][i][1]), b, acc[i][j]);
+      }
+  }
+  if (wave > 0) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int j = 0; j < T; ++j) red[wave - 1][i * T + j][lane] = acc[i][j];
+  }
+  __syncthreads();
+  if (wave > 0) return;
+  // lane holds rows n0 + 16 i + 4 g + v of token 16 j + li
+  float* out = part + (int64_t)blockIdx.y * M * N;
+#pragma unroll
+  for (int j = 0; j < T; ++j) {
+    const int m = 16 * j + li;
+    if (m >= M) continue;
+    const float sx = xs[m];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int n = n0 + 16 * i + 4 * lg;
+      const f32x4 v = ((acc[i][j] + red[0][i * T + j][lane]) + red[1][i * T + j][lane]) + red[2][i * T + j][lane];
+#pragma unroll
+      for (int e = 0; e < 4; ++e)
+        if (n + e < N) out[(int64_t)m * N + n + e] = v[e] * (scales[n + e] * sx);
+    }
+  }
+}
+
+// K-slices of the decode kernels: about 512 workgroups (64-row groups x
+// slices), each slice a multiple of the chunk (64, or 128 for E4M3 tokens)
+// and at least 256 long.
 struct DecSplit {
   int t = 0, slice = 0, slices = 0;
 };
-DecSplit dec_split(int64_t m, int64_t n, int64_t k) {
+DecSplit dec_split(int64_t m, int64_t n, int64_t k, int chunk) {
   DecSplit d;
   d.t = m <= 16 ? 1 : m <= 32 ? 2 : 4;
   const int64_t groups = (n + kDecRows - 1) / kDecRows;
   int64_t want = (512 + groups - 1) / groups;
   want = std::max<int64_t>(1, std::min<int64_t>(want, k / 256));
-  const int64_t len = ((k + want - 1) / want + 63) / 64 * 64;
+  const int64_t len = ((k + want - 1) / want + chunk - 1) / chunk * chunk;
   d.slice = (int)len;
   d.slices = (int)((k + len - 1) / len);
   return d;
@@ -294,10 +379,11 @@ hipError_t launch_fp8_quantize(const void* w, bool w_bf16, int64_t n, int64_t k,
   return hipGetLastError();
 }
 
-// Workspace: y partials [S][m][n] fp32 for decode or a split contraction; with
-// adapters the K-slices of t [St][m][r] fp32 and, unsplit, the bf16 LoRA
-// segment operands ts [m][2 rp], b2 [n][2 rp].
-size_t fp8_linear_workspace(int64_t m, int64_t n, int64_t k, int64_t r, Fp8Ws* w, void* base) {
+// Workspace: W8A8 token codes x8 [m][k] and scales xs [m]; y partials
+// [S][m][n] fp32 for decode or a split contraction; with adapters the
+// K-slices of t [St][m][r] fp32 and, unsplit, the bf16 LoRA segment operands
+// ts [m][2 rp], b2 [n][2 rp].
+size_t fp8_linear_workspace(int64_t m, int64_t n, int64_t k, int64_t r, bool a8, Fp8Ws* w, void* base) {
   size_t off = 0;
   auto take = [&](size_t bytes) {
     const size_t o = off;
@@ -305,9 +391,14 @@ size_t fp8_linear_workspace(int64_t m, int64_t n, int64_t k, int64_t r, Fp8Ws* w
     return base ? reinterpret_cast<float*>(static_cast<uint8_t*>(base) + o) : nullptr;
   };
   Fp8Ws v{};
+  if (a8) {
+    v.x8 = reinterpret_cast<uint8_t*>(take((size_t)m * k));
+    v.xs = take((size_t)m * 4);
+  }
   // decode (m <= 64) always writes partials; otherwise only a split contraction does
   const bool dec = m <= 64;
-  const int sl = dec ? dec_split(m, n, k).slices : nt_slices(nt_tiles(m, n), k);
+  const int chunk = a8 ? 128 : kGC;
+  const int sl = dec ? dec_split(m, n, k, chunk).slices : nt_slices(nt_tiles(m, n), k, chunk);
   const bool parts = dec || sl > 1;
   const int64_t rp = (r + 7) / 8 * 8;
   if (parts) v.ypart = take((size_t)sl * m * n * 4);
@@ -322,53 +413,81 @@ size_t fp8_linear_workspace(int64_t m, int64_t n, int64_t k, int64_t r, Fp8Ws* w
   return off;
 }
 
+namespace {
+
+template <int T>
+void launch_decode(bool a8, dim3 grid, const uint16_t* x, const Fp8Ws& w, int64_t m, int64_t n, int64_t k,
+                   const uint8_t* codes, const float* scales, int slice, hipStream_t st) {
+  if (a8)
+    hipLaunchKernelGGL(e4m3_decode_kernel<T>, grid, dim3(256), 0, st, w.x8, w.xs, (int)m, (int)n, (int)k, codes, scales,
+                       slice, w.ypart);
+  else
+    hipLaunchKernelGGL(fp8_decode_kernel<T>, grid, dim3(256), 0, st, x, (int)m, (int)n, (int)k, codes, scales, slice,
+                       w.ypart);
+}
+
+template <int MODE>
+void launch_gemm(bool split, int64_t tiles, int sl, const Seg& sw, const Seg& lora, int64_t m, int64_t n,
+                 const float* scales, uint16_t* y, float* ypart, hipStream_t st) {
+  if (!split)
+    hipLaunchKernelGGL((nt_gemm_kernel<true, 1, MODE>), dim3((unsigned)tiles), dim3(256), 0, st, sw, lora, (int)m,
+                       (int)n, nullptr, 1.0f, scales, y, nullptr);
+  else
+    hipLaunchKernelGGL((nt_gemm_kernel<false, 1, MODE>), dim3((unsigned)tiles, (unsigned)sl), dim3(256), 0, st, sw,
+                       Seg{}, (int)m, (int)n, nullptr, 1.0f, scales, nullptr, ypart);
+}
+
+}  // namespace
+
 hipError_t launch_fp8_linear(const uint16_t* x, int64_t m, int64_t n, int64_t k, const uint8_t* codes,
-                             const float* scales, const uint16_t* a, const uint16_t* b, int64_t r, float s,
+                             const float* scales, const uint16_t* a, const uint16_t* b, int64_t r, float s, bool a8,
                              uint16_t* y, const Fp8Ws& w, hipStream_t st) {
+  if (a8) {  // the tokens' E4M3 codes and scales: the weight quantiser, one workgroup per token
+    hipLaunchKernelGGL(fp8_quantize_kernel<true>, dim3((unsigned)m), dim3(256), 0, st, x, (int)k, w.x8, w.xs);
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
   int tsl = 0;
-  if (r > 0) {  // t = s x A^T in K-slices (the NVFP4 linear's LoRA down-projection kernel)
+  if (r > 0) {  // t = s x A^T in K-slices from the bf16 tokens (the NVFP4 linear's LoRA down-projection kernel)
     const int splits = lora_splits(m, k, r);
     tsl = lora_slices(k, splits);
     const hipError_t e = launch_lora_down(x, m, k, a, r, s, splits, w.tpart, st);
     if (e != hipSuccess) return e;
   }
+  const int chunk = a8 ? 128 : kGC;
   if (m <= 64) {
-    const DecSplit d = dec_split(m, n, k);
+    const DecSplit d = dec_split(m, n, k, chunk);
     const dim3 grid((unsigned)((n + kDecRows - 1) / kDecRows), (unsigned)d.slices);
     if (d.t == 1)
-      hipLaunchKernelGGL(fp8_decode_kernel<1>, grid, dim3(256), 0, st, x, (int)m, (int)n, (int)k, codes, scales, d.slice,
-                         w.ypart);
+      launch_decode<1>(a8, grid, x, w, m, n, k, codes, scales, d.slice, st);
     else if (d.t == 2)
-      hipLaunchKernelGGL(fp8_decode_kernel<2>, grid, dim3(256), 0, st, x, (int)m, (int)n, (int)k, codes, scales, d.slice,
-                         w.ypart);
+      launch_decode<2>(a8, grid, x, w, m, n, k, codes, scales, d.slice, st);
     else
-      hipLaunchKernelGGL(fp8_decode_kernel<4>, grid, dim3(256), 0, st, x, (int)m, (int)n, (int)k, codes, scales, d.slice,
-                         w.ypart);
+      launch_decode<4>(a8, grid, x, w, m, n, k, codes, scales, d.slice, st);
     hipLaunchKernelGGL(fp8_finish_kernel, dim3(flat_grid8(m * n)), dim3(256), 0, st, w.ypart, d.slices, (int)m, (int)n,
                        w.tpart, tsl, r > 0 ? b : nullptr, (int)r, y);
     return hipGetLastError();
   }
   const int64_t tiles = nt_tiles(m, n);
-  Seg sw{x, codes, (int)k, (int)k, nt_slice_len(tiles, k)};
-  const int sl = nt_slices(tiles, k);
-  if (sl == 1) {
+  const Seg sw = a8 ? Seg{w.x8, codes, (int)k, (int)k, nt_slice_len(tiles, k, chunk), w.xs}
+                    : Seg{x, codes, (int)k, (int)k, nt_slice_len(tiles, k, chunk)};
+  const int sl = nt_slices(tiles, k, chunk);
+  Seg lora{};
+  if (sl == 1 && r > 0) {
     // enough output tiles (prefill): bf16 out in one launch, the LoRA term as
     // a second segment (t split into bf16 hi | lo against B twice)
-    Seg lora{};
-    if (r > 0) {
-      const int64_t rp = (r + 7) / 8 * 8;
-      hipLaunchKernelGGL(lora_operands_kernel, dim3(flat_grid8((m + n) * rp)), dim3(256), 0, st, w.tpart, tsl, b,
-                         (int)m, (int)n, (int)r, (int)rp, w.ts, w.b2);
-      lora = Seg{w.ts, w.b2, (int)(2 * rp), (int)(2 * rp), (int)(2 * rp)};
-    }
-    hipLaunchKernelGGL((nt_gemm_kernel<true, 1, true>), dim3((unsigned)tiles), dim3(256), 0, st, sw, lora, (int)m,
-                       (int)n, nullptr, 1.0f, scales, y, nullptr);
-    return hipGetLastError();
+    const int64_t rp = (r + 7) / 8 * 8;
+    hipLaunchKernelGGL(lora_operands_kernel, dim3(flat_grid8((m + n) * rp)), dim3(256), 0, st, w.tpart, tsl, b, (int)m,
+                       (int)n, (int)r, (int)rp, w.ts, w.b2);
+    lora = Seg{w.ts, w.b2, (int)(2 * rp), (int)(2 * rp), (int)(2 * rp)};
   }
-  hipLaunchKernelGGL((nt_gemm_kernel<false, 1, true>), dim3((unsigned)tiles, (unsigned)sl), dim3(256), 0, st, sw,
-                     Seg{}, (int)m, (int)n, nullptr, 1.0f, scales, nullptr, w.ypart);
-  hipLaunchKernelGGL(fp8_finish_kernel, dim3(flat_grid8(m * n)), dim3(256), 0, st, w.ypart, sl, (int)m, (int)n,
-                     w.tpart, tsl, r > 0 ? b : nullptr, (int)r, y);
+  if (a8)
+    launch_gemm<kNtE4M3>(sl > 1, tiles, sl, sw, lora, m, n, scales, y, w.ypart, st);
+  else
+    launch_gemm<kNtR8>(sl > 1, tiles, sl, sw, lora, m, n, scales, y, w.ypart, st);
+  if (sl > 1)
+    hipLaunchKernelGGL(fp8_finish_kernel, dim3(flat_grid8(m * n)), dim3(256), 0, st, w.ypart, sl, (int)m, (int)n,
+                       w.tpart, tsl, r > 0 ? b : nullptr, (int)r, y);
   return hipGetLastError();
 }
 

@@ -326,6 +326,15 @@ fp4rl_status fp4rl_aqn_gate_up_silu(const uint16_t* x, int64_t m, int64_t n, int
  *   lora_b bf16 [n][r] (both NULL or both set), y bf16 [m][n]; m, n, k below
  *   2^22. Workspace: fp4rl_fp8_lora_linear_workspace(m, n, k, r) bytes,
  *   256-byte aligned, no initial contents needed (fp32 partial products).
+ * fp4rl_fp8_lora_linear_w8a8: the same product with the tokens quantised
+ *   too (W8A8; the page leaves activations open, this is the reading taken):
+ *   each row m of x gets s_x[m] = amax_m / 448 and E4M3 codes exactly as
+ *   fp4rl_fp8_quantize gives a bf16 weight row; then
+ *   y = bf16(s_x[m] s_n sum_k e4m3(x8[m,k]) e4m3(code[n,k]) + s (x A^T) B^T),
+ *   the base product on the FP8 matrix cores, the LoRA term from the bf16
+ *   x. Arguments, limits and ownership as for fp4rl_fp8_lora_linear; its
+ *   workspace, fp4rl_fp8_lora_linear_w8a8_workspace(m, n, k, r) bytes, also
+ *   holds the token codes and scales (no initial contents needed).
  * Errors as for the NVFP4 calls; nothing is launched on error. */
 fp4rl_status fp4rl_fp8_quantize(const void* w, int32_t w_dtype, int64_t n, int64_t k, uint8_t* codes,
                                 float* row_scales, fp4rl_stream stream);
@@ -334,6 +343,11 @@ fp4rl_status fp4rl_fp8_lora_linear(const uint16_t* x, int64_t m, int64_t n, int6
                                    const float* row_scales, const uint16_t* lora_a, const uint16_t* lora_b, int64_t r,
                                    float lora_scale, uint16_t* y, void* workspace, size_t workspace_bytes,
                                    fp4rl_stream stream);
+size_t fp4rl_fp8_lora_linear_w8a8_workspace(int64_t m, int64_t n, int64_t k, int64_t r);
+fp4rl_status fp4rl_fp8_lora_linear_w8a8(const uint16_t* x, int64_t m, int64_t n, int64_t k, const uint8_t* codes,
+                                        const float* row_scales, const uint16_t* lora_a, const uint16_t* lora_b,
+                                        int64_t r, float lora_scale, uint16_t* y, void* workspace,
+                                        size_t workspace_bytes, fp4rl_stream stream);
 
 /* ------------------------------------------------------------------------
  * AQN.
