@@ -840,6 +840,282 @@ __global__ __launch_bounds__(W * kWave) __attribute__((amdgpu_waves_per_eu(D == 
 }
 
 // ---------------------------------------------------------------------------
+// Mid-batch kernel for 96 < M <= 128 tokens on wide matrices: every weight
+// tile is fetched and dequantised for all the tokens at once.
+//   A workgroup computes 32 RW WR output features x 32 TGW WT tokens with
+//   W = WR WT waves: wave (wr, wt) owns RW groups of 32 features and TGW
+//   groups of 32 tokens, and runs the 32x32x16 bf16 MFMA with dequantised
+//   weights as the A operand and activations as the B operand, so a weight
+//   fragment feeds TGW MFMAs and an activation fragment read from LDS feeds
+//   RW. Eight waves (two per SIMD) let one wave's dequantisation and loads
+//   overlap another's MFMAs; a single wave per SIMD runs them one after the
+//   other (measured: loads and staging, MFMA and dequantisation added up).
+//   The waves share the activations: a chunk of 128 k for all the
+//   workgroup's tokens is loaded by the whole workgroup (16 lanes per token
+//   row) two chunks ahead, stored in one of two LDS slabs (rows padded to
+//   272 B: conflict-free fragment reads) and read by every wave; one barrier
+//   per chunk. Weights stream through a ring of D register stages per wave.
+//   MFMA slots: a lane (row r = lane % 32, half h = lane / 32) loads lane
+//   positions (r % 16, 2h) and (r % 16, 2h + 1) of its row's tile (16 bytes
+//   each, both under the block scales of p = h); step (j, q) of a chunk
+//   takes word j of position 2h + q, i.e. k = 32 j + 16 h + 8 q .. + 7, and
+//   the activation fragment of the same lane holds the same k. A lane's
+//   result holds token lane % 32 of its group and features 8 b + 4 h + e.
+//   The LoRA update runs after the contraction as further MFMA steps over r
+//   (B rows as the A operand, t split into bf16 hi + lo as the B operand),
+//   added to the s_t-scaled sums. One workgroup per row group covers all of
+//   K: the kernel serves matrices wide enough to give every CU one.
+//   Measured limit (32B gate at 128 tokens, 40 chunks per workgroup, about
+//   1.2 us each): loads, activation staging and the barrier take 0.7 us a
+//   chunk on their own (each workgroup pulls 32 KB of activations and 18 KB
+//   of weights through its CU's vector cache per chunk), MFMA and
+//   dequantisation add the rest; they overlap little because the barrier
+//   keeps the waves in step.
+// ---------------------------------------------------------------------------
+template <int RW, int TGW, int WR, int WT, int D>
+__global__ __launch_bounds__(WR * WT * kWave) void mid_kernel(
+    const uint16_t* __restrict__ x, int M, int N, int K, const uint8_t* __restrict__ codes,
+    const uint8_t* __restrict__ scales, const float* __restrict__ tensor_scale, const float* __restrict__ t, int tks,
+    const uint16_t* __restrict__ lb, int r, uint16_t* __restrict__ y, LoraFuse lf) {
+  constexpr int W = WR * WT;
+  constexpr int TOK = 32 * TGW * WT;  // tokens of the workgroup
+  constexpr int ROWS = 32 * RW * WR;  // features of the workgroup
+  constexpr int SLAB = TOK * kXRow;   // bf16 per activation slab
+  __shared__ __align__(16) uint16_t xs[2 * SLAB];
+  __shared__ uint32_t last_flag;
+  static_assert(2 * SLAB * 2 >= W * kWave * 16, "the LoRA producers' reduction fits in the slabs");
+  if ((int)blockIdx.x < lf.producers) {  // fused LoRA down-projection
+    lora_produce<W>(lf, blockIdx.x, x, M, K, r, reinterpret_cast<f32x4*>(xs), &last_flag);
+    return;
+  }
+  const int rg = (int)blockIdx.x - lf.producers;  // row group (the producers come first)
+  const int lane = threadIdx.x & (kWave - 1);
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
+  const int wr = wave % WR, wt = wave / WR;
+  const int lr = lane & 31, lh = lane >> 5;
+  const int RT = (N + 15) >> 4, KC = (K + 127) >> 7;
+  const int nw = ROWS * rg + 32 * RW * wr;  // this wave's features nw + 32 i + 0 .. 31, i < RW
+  const int mw = 32 * TGW * wt;             // this wave's tokens mw + 32 g + 0 .. 31, g < TGW
+  const int nch = KC;                       // chunks of 128 k
+
+  // weights: tile of row nw + 32 i + lr (clamped: rows past N are computed, never stored)
+  const uint8_t* cl[RW];
+  const uint8_t* sl[RW];
+#pragma unroll
+  for (int i = 0; i < RW; ++i) {
+    const int tile = min(((nw + 32 * i) >> 4) + (lr >> 4), RT - 1);
+    cl[i] = codes + (int64_t)tile * KC * 1024 + 16 * (32 * lh + (lr & 15));
+    sl[i] = scales + (int64_t)tile * KC * 128 + 64 * lh + 4 * (lr & 15);
+  }
+  // Every load below is unconditional (chunk indices past K are clamped to
+  // the last chunk, and their data is never used): with no
+  // branches around the loads, the compiler waits only for the ones a step
+  // consumes, so the prefetched chunks stay in flight across the loop.
+  struct WStage {
+    uint4 c0[RW], c1[RW];
+    uint32_t s[RW];
+  };
+  auto load_w = [&](int q, WStage& S) {
+    const int64_t c = min(q, nch - 1);
+#pragma unroll
+    for (int i = 0; i < RW; ++i) {
+      S.c0[i] = ld_nt16(cl[i] + c * 1024);
+      S.c1[i] = ld_nt16(cl[i] + c * 1024 + 256);
+      S.s[i] = *reinterpret_cast<const uint32_t*>(sl[i] + c * 128);
+    }
+  };
+  // activations: piece p = tid + 64 W u of the chunk is token row p / 16, k = 8 (p % 16) .. + 7,
+  // read through a buffer descriptor over x: pieces past K take an offset past
+  // the buffer, which reads as zero (K % 16 == 0: a piece is all in or out)
+  constexpr int XP = TOK * 16 / (W * kWave);  // pieces per thread
+  static_assert(XP * W * kWave == TOK * 16, "whole pieces per thread");
+  const __amdgpu_buffer_rsrc_t xrs =
+      __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(x), 0, 2 * M * K, kBufferWord3);
+  uint32_t xoff[XP];  // bytes (tokens past M clamped to the last)
+#pragma unroll
+  for (int u = 0; u < XP; ++u) {
+    const int p = (int)threadIdx.x + W * kWave * u;
+    xoff[u] = 2u * ((uint32_t)min(p >> 4, M - 1) * (uint32_t)K + 8u * (uint32_t)(p & 15));
+  }
+  const int kcol = 8 * ((int)threadIdx.x & 15);  // the same k offset for every piece of this thread
+  auto load_x = [&](int q, uint4 (&v)[XP]) {
+    const int c = min(q, nch - 1);
+    const uint32_t base = 256u * (uint32_t)c, past = 128 * c + kcol < K ? 0u : 0x80000000u;
+#pragma unroll
+    for (int u = 0; u < XP; ++u)
+      v[u] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(xrs, (int)((xoff[u] + base) | past), 0, 0));
+  };
+  auto store_x = [&](int slab, const uint4 (&v)[XP]) {
+#pragma unroll
+    for (int u = 0; u < XP; ++u) {
+      const int p = (int)threadIdx.x + W * kWave * u;
+      *reinterpret_cast<uint4*>(xs + slab * SLAB + (p >> 4) * kXRow + 8 * (p & 15)) = v[u];
+    }
+  };
+
+  f32x16 acc[RW][TGW];
+#pragma unroll
+  for (int i = 0; i < RW; ++i)
+#pragma unroll
+    for (int g = 0; g < TGW; ++g)
+#pragma unroll
+      for (int v = 0; v < 16; ++v) acc[i][g][v] = 0.0f;
+
+  auto compute = [&](int slab, const WStage& S) {
+    float sc[RW][4];
+#pragma unroll
+    for (int i = 0; i < RW; ++i) scale4(S.s[i], sc[i]);
+    const uint16_t* xb = xs + slab * SLAB + (mw + lr) * kXRow + 16 * lh;
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+#pragma unroll
+      for (int q = 0; q < 2; ++q) {
+        bf16x8 b[TGW];
+#pragma unroll
+        for (int g = 0; g < TGW; ++g)
+          b[g] = as_bf16x8(*reinterpret_cast<const uint4*>(xb + g * 32 * kXRow + 32 * j + 8 * q));
+#pragma unroll
+        for (int i = 0; i < RW; ++i) {
+          const uint4& cw = q == 0 ? S.c0[i] : S.c1[i];
+          const uint32_t word = j == 0 ? cw.x : j == 1 ? cw.y : j == 2 ? cw.z : cw.w;
+          const bf16x8 a = dequant8(word, sc[i][j]);
+#pragma unroll
+          for (int g = 0; g < TGW; ++g) acc[i][g] = mfma32x32x16(a, b[g], acc[i][g]);
+        }
+      }
+  };
+
+  // Pipeline: weight stages for chunks q + 1 .. q + D - 1 and activation
+  // stages for chunks q + 1 .. q + XS in registers while chunk q is
+  // computed; chunk q + 1's activations go to the other slab after the
+  // compute (the barrier that ended chunk q - 1 guarantees that no wave
+  // still reads it). The prologue issues its loads in the loop's order, so
+  // the loop entry and its back edge see the same loads in flight. A range
+  // of fewer chunks loads its last chunk again in their place (clamped,
+  // unused).
+  static_assert(D >= 2 && D <= 4, "two to four weight stages");
+  constexpr int XS = 3;                      // activation chunks in flight
+  constexpr int UNR = 12;                    // a multiple of D, XS and 2: every stage in fixed registers; the loads drain once per body (loop entry)
+  static_assert(UNR % D == 0 && UNR % XS == 0 && UNR % 2 == 0, "whole rings per unrolled body");
+  WStage ws[D];
+  uint4 xr[XS][XP];
+  if (nch > 0) {  // uniform across the workgroup
+    load_x(0, xr[0]);
+#pragma unroll
+    for (int u = 0; u < XS - 1; ++u) {
+      load_x(u + 1, xr[u + 1]);
+      if (u < D) load_w(u, ws[u]);
+    }
+#pragma unroll
+    for (int u = XS - 1; u < D; ++u) load_w(u, ws[u]);
+    store_x(0, xr[0]);
+    load_x(XS, xr[0]);
+  }
+  __syncthreads();
+  for (int q0 = 0; q0 < nch; q0 += UNR) {
+#pragma unroll
+    for (int u = 0; u < UNR; ++u) {
+      const int q = q0 + u;
+      if (q >= nch) break;  // uniform across the workgroup
+      // the next chunk's activations go to the other slab first (the
+      // barrier that ended chunk q - 1 guarantees that no wave still reads
+      // it) and a later chunk's activation loads are issued, so they are in
+      // flight during the compute of chunk q; the weight stage that chunk q
+      // used is refilled after it
+      store_x((u + 1) & 1, xr[(u + 1) % XS]);
+      load_x(q + 1 + XS, xr[(u + 1) % XS]);
+      compute(u & 1, ws[u % D]);
+      load_w(q + D, ws[u % D]);
+      __syncthreads();
+    }
+  }
+
+  const uint32_t t_seen = lora_poll(lf, rg);  // fused LoRA: read early, checked below
+  const float st = *tensor_scale;
+#pragma unroll
+  for (int i = 0; i < RW; ++i)
+#pragma unroll
+    for (int g = 0; g < TGW; ++g) acc[i][g] *= st;
+  uint32_t released = 0u;
+  if (r > 0) {
+    lora_wait(lf, rg, t_seen);
+    released = lora_release(lf, rg);
+    // y += t B^T: 16 ranks per step, lane (r, h) takes ranks 16 s + 8 h .. + 7
+    const bool coh = lf.producers > 0;  // t written by this launch's producers: agent-coherent loads
+    const __amdgpu_buffer_rsrc_t trs =
+        __builtin_amdgcn_make_buffer_rsrc(const_cast<float*>(t), 0, (int)(4 * (int64_t)tks * M * r), kBufferWord3);
+    const int64_t tstride = (int64_t)M * r;
+    for (int j0 = 0; j0 < r; j0 += 16) {
+      const int jj = j0 + 8 * lh;
+      uint4 th[TGW], tl[TGW];
+#pragma unroll
+      for (int g = 0; g < TGW; ++g) {
+        const int ma = min(mw + 32 * g + lr, M - 1);
+        float tv[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          if (jj + e < r) {
+            const int64_t o = (int64_t)ma * r + jj + e;
+            if (coh) {
+              tv[e] = ld_coherent4(trs, (int)(4 * o));
+            } else {
+              for (int z = 0; z < tks; ++z) tv[e] += t[(int64_t)z * tstride + o];
+            }
+          }
+        }
+        split_bf16x8(tv, th[g], tl[g]);
+      }
+#pragma unroll
+      for (int i = 0; i < RW; ++i) {
+        const int na = min(nw + 32 * i + lr, N - 1);
+        uint4 bw = make_uint4(0, 0, 0, 0);
+        if (jj < r) {
+          if ((r & 7) == 0) {
+            bw = ld16(lb + (int64_t)na * r + jj);
+          } else {
+            uint32_t hv[8];
+#pragma unroll
+            for (int e = 0; e < 8; ++e) hv[e] = jj + e < r ? lb[(int64_t)na * r + jj + e] : 0u;
+            bw = make_uint4(hv[0] | (hv[1] << 16), hv[2] | (hv[3] << 16), hv[4] | (hv[5] << 16), hv[6] | (hv[7] << 16));
+          }
+        }
+#pragma unroll
+        for (int g = 0; g < TGW; ++g) {
+          acc[i][g] = mfma32x32x16(as_bf16x8(bw), as_bf16x8(th[g]), acc[i][g]);
+          acc[i][g] = mfma32x32x16(as_bf16x8(bw), as_bf16x8(tl[g]), acc[i][g]);
+        }
+      }
+    }
+  }
+
+  // lane holds token mw + 32 g + lr, features nw + 32 i + 8 b + 4 lh + e (register 4 b + e)
+  auto store_y = [&](int i, int g, const f32x16& v) {
+    const int m = mw + 32 * g + lr;
+    if (m >= M) return;
+#pragma unroll
+    for (int b = 0; b < 4; ++b) {
+      const int nf = nw + 32 * i + 8 * b + 4 * lh;
+      uint16_t* yp = y + (int64_t)m * N + nf;
+      const uint32_t o01 = pack_bf16x2(v[4 * b], v[4 * b + 1]), o23 = pack_bf16x2(v[4 * b + 2], v[4 * b + 3]);
+      if ((N & 3) == 0 && nf + 3 < N) {
+        *reinterpret_cast<uint2*>(yp) = make_uint2(o01, o23);
+      } else {
+        const uint32_t o[4] = {o01 & 0xFFFFu, o01 >> 16, o23 & 0xFFFFu, o23 >> 16};
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+          if (nf + e < N) yp[e] = (uint16_t)o[e];
+      }
+    }
+  };
+
+#pragma unroll
+  for (int i = 0; i < RW; ++i)
+#pragma unroll
+    for (int g = 0; g < TGW; ++g) store_y(i, g, acc[i][g]);
+  if (r > 0) lora_reset_if_last(lf, rg, released);
+}
+
+// ---------------------------------------------------------------------------
 // Prefill GEMM (M > 128 tokens): a workgroup computes 256 output features x
 // 128 tokens over all of K with (256 / 16 TM) x (8 / TN) waves; each owns TM
 // row tiles (16 TM features) against TN of the 8 token tiles, so one
@@ -1405,6 +1681,32 @@ struct SplitkCfg {
 
 static bool use_splitk(int64_t m) { return m > 16 && !use_prefill(m); }
 
+// Mid-batch kernel: eight waves per workgroup, 4 x 2 waves of 32 features
+// x 64 tokens (128 features x 128 tokens per workgroup; 97..127 tokens use
+// the same tile, the rows past M clamped and never stored), one workgroup
+// per 128 features over all of K. Used where it beats the split-K kernel,
+// which fetches and dequantises each weight tile once per 32 tokens: more
+// than 96 tokens and at least 200 row groups, so that no K split is needed
+// (measured, 27648 x 5120 at 112 and 128 tokens: 63 vs 73 us; at 65..96
+// tokens the two are level, and narrower matrices, which would need a K
+// split, are faster on the split-K kernel).
+constexpr int kMidRows = 128;
+static bool use_mid(int64_t m, int64_t n) {
+  return m > 96 && m <= 128 && (n + kMidRows - 1) / kMidRows >= 200;
+}
+
+static hipError_t launch_mid(hipStream_t st, const uint16_t* x, int M, int N, int K, const uint8_t* codes,
+                             const uint8_t* scales, const float* ts, const float* t, int tks, const uint16_t* b, int r,
+                             uint16_t* y, LoraFuse lf) {
+  const int gx = (N + kMidRows - 1) / kMidRows;
+  lf.consumers = gx;  // one waiting workgroup per row group
+  lf.groups = std::min(kLoraGroups, lf.consumers);
+  const unsigned grid = (unsigned)(lf.producers + gx);
+  hipLaunchKernelGGL((mid_kernel<1, 2, 4, 2, 3>), dim3(grid), dim3(8 * kWave), 0, st, x, M, N, K, codes, scales, ts, t,
+                     tks, b, r, y, lf);
+  return hipGetLastError();
+}
+
 static SplitkCfg pick_splitk(int64_t m, int64_t n, int64_t k) {
   SplitkCfg c;
   c.tn = 2;
@@ -1435,7 +1737,7 @@ static SplitkCfg pick_splitk(int64_t m, int64_t n, int64_t k) {
 }
 
 size_t linear_partial_bytes(int64_t m, int64_t n, int64_t k) {
-  if (!use_splitk(m)) return 0;
+  if (use_mid(m, n) || !use_splitk(m)) return 0;
   const SplitkCfg c = pick_splitk(m, n, k);
   if (c.s == 1) return 0;
   return ((size_t)c.s * (size_t)m * (size_t)n * sizeof(float) + 255) / 256 * 256;
@@ -1495,6 +1797,7 @@ const char* fp4_linear_kernel_name(int64_t m, int64_t n, int64_t k, int64_t r) {
     return kGemv[m - 1][wi];
   }
   if (use_prefill(m)) return "prefill_kernel<2>";
+  if (use_mid(m, n)) return "mid_kernel<1, 2, 4, 2, 3>";
   if (use_splitk(m)) {
     const SplitkCfg sc = pick_splitk(m, n, k);
     static const char* const kSplitk[3][2] = {{"splitk_kernel<2, 2, 4, 2>", "splitk_kernel<2, 2, 4, 3>"},
@@ -1531,6 +1834,7 @@ hipError_t launch_fp4_linear(const uint16_t* x, int64_t m, int64_t n, int64_t k,
     return m == 1 ? run_gemv_w<1>(w, stream, x, M, N, K, codes, scales, tensor_scale, t, tks, b, R, y, lf)
                   : run_gemv_w<2>(w, stream, x, M, N, K, codes, scales, tensor_scale, t, tks, b, R, y, lf);
   }
+  if (use_mid(m, n)) return launch_mid(stream, x, M, N, K, codes, scales, tensor_scale, t, tks, b, R, y, lf);
   if (use_splitk(m))
     return launch_splitk(pick_splitk(m, n, k), stream, x, M, N, K, codes, scales, tensor_scale, t, tks, b, R, y, part,
                          counters, lf);

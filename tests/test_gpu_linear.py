@@ -118,6 +118,27 @@ def test_split_k_launch_configs(m, n, k, r, kernel):
     _check_lin(y, x, q, a, b, LORA_SCALE, f"{m}x{n}x{k} r{r}")
 
 
+MID_CONFIGS = [  # (m, n, k, r): more than 96 tokens on at least 200 row groups of 128 features
+    (100, 30000, 1040, 0),    # no adapters, a ragged last chunk
+    (128, 30001, 272, 3),     # n % 4 != 0 (scalar stores), a short ragged K, r % 8 != 0 (scalar B loads)
+    (97, 25601, 2064, 5),     # the fewest tokens, one feature past 200 row groups of 128
+    (113, 26000, 3568, 32),   # tokens past M inside the last token group, a ragged K
+    (128, 25473, 1040, 256),  # the largest rank: 128 tiles of t from the fused producers
+]
+
+
+@pytest.mark.parametrize("m,n,k,r", MID_CONFIGS)
+def test_mid_kernel_configs(m, n, k, r):
+    dev = device()
+    kernel = fr.fp4_linear_kernel_name(m, n, k, r)
+    assert kernel == "mid_kernel<1, 2, 4, 2, 3>"
+    w, x, a, b = _case(m, n, k, r, seed=m * 89 + n * 11 + k)
+    q = nvfp4.quantize(w)
+    say(f"linear {kernel} m={m} n={n} k={k} r={r}")
+    y = _run(dev, x, q, a, b, LORA_SCALE)
+    _check_lin(y, x, q, a, b, LORA_SCALE, f"{m}x{n}x{k} r{r}")
+
+
 # a linear workspace starts with 4608 counter words: K-split tile counters,
 # t tile counters, finished-tile count, 64 ready-flag lines of 256 bytes
 COUNTER_BYTES = 4 * (512 + 64 * 64)
@@ -259,9 +280,10 @@ def test_power_of_two_homogeneity_and_determinism():
     assert np.array_equal(_run(dev, x, q, a, b, LORA_SCALE), y1)
 
 
-def test_halves_match_fused_call():
+@pytest.mark.parametrize("m", [40, 100])
+def test_halves_match_fused_call(m):
     dev = device()
-    m, n, k, r = 40, 300, 640, 32
+    n, k, r = 300, 640, 32
     w, x, a, b = _case(m, n, k, r, seed=45)
     q = nvfp4.quantize(w)
     xt, wq = bf16_to_dev(x, dev), nvfp4_to_dev(*q, dev)
