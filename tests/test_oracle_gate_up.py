@@ -46,3 +46,44 @@ def test_zero_cases():
     z = (np.zeros_like(u[0]), np.zeros_like(u[1]), np.float32(0))
     assert not gu.gate_up(x, g, z, ag, bg, au, np.zeros_like(bu), 2.0).any()
     assert not gu.gate_up(x, z, u, ag, np.zeros_like(bg), au, bu, 2.0).any()
+
+
+def _exact_case(seed, m=6, n=40, k=64):
+    """Linear outputs exact in bf16: one-hot power-of-two tokens, tensor scales 2^-7 and 2^-9.
+
+    A product e2m1 * e4m3 block scale * 2^a needs at most 6 significant bits.
+    """
+    rng = np.random.default_rng(seed)
+    x = np.zeros((m, k), np.float32)
+    x[np.arange(m), rng.integers(0, k, m)] = 2.0 ** rng.integers(-3, 4, m)
+    xb = bf16_bits(x)
+    def weight(s_t):
+        codes = rng.integers(0, 256, (n, k // 2), dtype=np.uint8)
+        scales = rng.integers(0x28, 0x50, (n, k // 16), dtype=np.uint8)  # E4M3 2^-2 .. 2^2 range, 4 significant bits
+        return codes, scales, np.float32(s_t)
+    return xb, weight(2.0 ** -7), weight(2.0 ** -9)
+
+
+def test_two_step_equals_fused_when_outputs_are_exact():
+    x, g, u = _exact_case(5)
+    yg = linear.lora_linear_f64(x, *g)
+    assert np.array_equal(bf16_round(yg), yg), "the constructed gate outputs are bf16-exact"
+    assert np.array_equal(gu.gate_up_two_step(x, g, u), gu.gate_up(x, g, u))
+
+
+def test_two_step_within_the_rounding_bound():
+    """|h2 - SiLU(g) u| <= 1.1 |u| |g - bf16(g)| + |SiLU(g)| |u - bf16(u)| + (2nd order) + half an ulp of h2."""
+    x, g, u, ag, bg, au, bu = _case(6, m=8, n=64, k=160, r=8)
+    yg = linear.lora_linear_f64(x, *g, ag, bg, 2.0)
+    yu = linear.lora_linear_f64(x, *u, au, bu, 2.0)
+    exact = gu.silu(yg) * yu
+    h2 = gu.gate_up_two_step(x, g, u, ag, bg, au, bu, 2.0)
+    dg, du = np.abs(yg - bf16_round(yg)), np.abs(yu - bf16_round(yu))
+    half_ulp = np.ldexp(1.0, np.floor(np.log2(np.maximum(np.abs(h2), 1e-300))).astype(int) - 8)
+    bound = 1.1 * np.abs(yu) * dg + np.abs(gu.silu(yg)) * du + 1.1 * dg * du + half_ulp
+    assert np.all(np.abs(h2 - exact) <= bound * (1 + 1e-9))
+    # and the roundings matter: the two forms differ somewhere on this data
+    assert not np.array_equal(h2, gu.gate_up(x, g, u, ag, bg, au, bu, 2.0))
+    # a planted slip, the gate and up outputs swapped, is far outside the bound
+    swapped = bf16_round(gu.silu(bf16_round(yu)) * bf16_round(yg))
+    assert np.any(np.abs(swapped - exact) > bound)
