@@ -33,6 +33,7 @@ sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0            # MI355X HBM3E, published
 BF16_PEAK_TFLOPS = 2500.0        # MI355X dense bf16 MFMA, published
+FP8_PEAK_TFLOPS = 5000.0         # MI355X dense fp8 MFMA, published
 TOKENS = (1, 8, 32, 64)
 RANK = 32
 RANK_32B = 64
@@ -67,6 +68,7 @@ def parse_args():
     p.add_argument("--no-extras", action="store_true", help="skip prefill / quantiser / AQN extra timings")
     p.add_argument("--backward-only", action="store_true",
                    help="time only the LoRA backward of the 7B layer at 8192 tokens (--steps passes)")
+    p.add_argument("--gate-up-only", action="store_true", help="time only the gate/up + SiLU extra and exit")
     p.add_argument("--fp8-only", action="store_true",
                    help="time only the FP8 (E4M3) linears of the 7B layer: decode 1..64 tokens and the prefill")
     p.add_argument("--prefill-only", action="store_true",
@@ -496,6 +498,11 @@ def main():
               for k in sorted({k for _, k in shapes.values()})}
         print(json.dumps({"fp8_linear": run_fp8(torch, fr, dev, shapes, lora, xs, gb)}))
         return
+    if args.gate_up_only:
+        progress("gate/up + SiLU timing")
+        print(json.dumps({"gate_up_silu": run_gate_up(torch, fr, dev, shapes, layers, lora,
+                                                      torch.Generator(device=dev).manual_seed(21))}))
+        return
     if args.decode32b_only:
         progress(f"32B decode pass, {args.layers32b} layers")
         print(json.dumps({"decode_32b": run_decode_32b(torch, fr, dev, layers=args.layers32b)}))
@@ -651,7 +658,7 @@ def main():
     extras = {}
     if not args.no_extras:
         progress("prefill, quantiser and AQN timings")
-        extras = run_extras(torch, fr, dev, shapes, layers[0], lora, None)
+        extras = run_extras(torch, fr, dev, shapes, layers, lora, None)
 
     out = {
         "metric": METRIC, "value": round(value, 3), "unit": "GB/s", "n_gpus": 1, "steps": args.steps,
@@ -696,14 +703,15 @@ def run_prefill(torch, fr, dev, shapes, layer, lora, g):
              "roofline": mfma_roofline(flops / dt / 1e12, ("prefill_kernel<2>",), "7B prefill 8192 tokens")}, xs)
 
 
-def run_extras(torch, fr, dev, shapes, layer, lora, fp32):
+def run_extras(torch, fr, dev, shapes, layers, lora, fp32):
+    layer = layers[0]
     res = {}
     g = torch.Generator(device=dev)
     g.manual_seed(21)
     res["prefill"], xs = run_prefill(torch, fr, dev, shapes, layer, lora, g)
     res["lora_backward"] = run_backward(torch, fr, dev, shapes, layer, lora, xs, g)
     res["fp8_linear"] = run_fp8(torch, fr, dev, shapes, lora, xs, g)
-    res["gate_up_silu"] = run_gate_up(torch, fr, dev, shapes, layer, lora, g)
+    res["gate_up_silu"] = run_gate_up(torch, fr, dev, shapes, layers, lora, g)
     del xs
 
     # quantiser on 14B shapes: one layer's five matrices, 0.02 t(3) weights with
@@ -792,14 +800,16 @@ def run_backward(torch, fr, dev, shapes, layer, lora, xs, g):
     return {"M": PREFILL_M, "r": RANK, "tflops": round(bflops / dt / 1e12, 2), "ms_per_layer": round(dt * 1e3, 3),
             "frac_of_bf16_peak": round(bflops / dt / 1e12 / BF16_PEAK_TFLOPS, 4), "timing": f"median of {runs}",
             "workspace_GB": round(bws.numel() / 1e9, 3),
-            "roofline": mfma_roofline(bflops / dt / 1e12, ("nt_gemm_kernel<true, 1, false>",),
+            "roofline": mfma_roofline(bflops / dt / 1e12, ("nt_gemm_kernel<true, 1, 0>",),
                                       "7B LoRA backward 8192 tokens")}
 
 
 def run_fp8(torch, fr, dev, shapes, lora, xs, g):
-    """FP8 (E4M3, per-row scale) W8A16 rollout linears of the same 7B layer and
-    adapters: decode at 1, 8, 32, 64 tokens (FP8 weight GB/s) and the
-    8192-token prefill (TFLOP/s)."""
+    """FP8 (E4M3, per-row scale) rollout linears of the same 7B layer and
+    adapters, W8A16 and W8A8 (tokens quantised per row inside the call):
+    decode at 1, 8, 32, 64 tokens (FP8 weight GB/s) and the 8192-token
+    prefill (TFLOP/s; W8A8 against the dense FP8 peak, its base product
+    running on the FP8 matrix cores)."""
     w8 = {name: fr.fp8_quantize(torch.randn((n, k), generator=g, device=dev).mul_(0.02))
           for name, (n, k) in shapes.items()}
     wbytes = sum(n * k + 4 * n for n, k in shapes.values())
@@ -808,34 +818,62 @@ def run_fp8(torch, fr, dev, shapes, lora, xs, g):
         xm = xs if m == PREFILL_M else {k: torch.randn((m, k), generator=g, device=dev).to(torch.bfloat16)
                                        for k in {k for _, k in shapes.values()}}
         ys = {name: torch.empty((m, n), dtype=torch.bfloat16, device=dev) for name, (n, k) in shapes.items()}
-        wss = {name: torch.empty(max(fr.fp8_lora_linear_workspace_bytes(m, n, k, RANK), 256), dtype=torch.uint8,
-                                 device=dev) for name, (n, k) in shapes.items()}
+        for a8 in (False, True):
+            wss = {name: torch.empty(max(fr.fp8_lora_linear_workspace_bytes(m, n, k, RANK, w8a8=a8), 256),
+                                     dtype=torch.uint8, device=dev) for name, (n, k) in shapes.items()}
 
-        def one():
-            for name, (n, k) in shapes.items():
-                a, b = lora[name]
-                fr.fp8_lora_linear(xm[k], w8[name], a, b, LORA_SCALE, out=ys[name], workspace=wss[name])
+            def one():
+                for name, (n, k) in shapes.items():
+                    a, b = lora[name]
+                    fr.fp8_lora_linear(xm[k], w8[name], a, b, LORA_SCALE, out=ys[name], workspace=wss[name],
+                                       w8a8=a8)
 
-        dt, runs = median_time(torch, one)
-        flops = sum(linear_flops(m, n, k, RANK) for n, k in shapes.values())
-        if m == PREFILL_M:
-            out["prefill"] = {"M": m, "ms_per_layer": round(dt * 1e3, 3), "tflops": round(flops / dt / 1e12, 2),
-                              "frac_of_bf16_peak": round(flops / dt / 1e12 / BF16_PEAK_TFLOPS, 4),
-                              "timing": f"median of {runs}"}
-        else:
-            out[f"decode_M{m}"] = {"us_per_layer": round(dt * 1e6, 1), "weight_GB/s": round(wbytes / dt / 1e9, 1),
-                                   "frac_of_hbm": round(wbytes / dt / 1e9 / HBM_PEAK_GBS, 4),
-                                   "timing": f"median of {runs}"}
-        del ys, wss
+            dt, runs = median_time(torch, one)
+            flops = sum(linear_flops(m, n, k, RANK) for n, k in shapes.values())
+            tag = "w8a8_" if a8 else ""
+            if m == PREFILL_M:
+                peak_key, peak = ("frac_of_fp8_peak", FP8_PEAK_TFLOPS) if a8 else ("frac_of_bf16_peak",
+                                                                                   BF16_PEAK_TFLOPS)
+                out[tag + "prefill"] = {"M": m, "ms_per_layer": round(dt * 1e3, 3),
+                                        "tflops": round(flops / dt / 1e12, 2),
+                                        peak_key: round(flops / dt / 1e12 / peak, 4), "timing": f"median of {runs}"}
+            else:
+                out[f"{tag}decode_M{m}"] = {"us_per_layer": round(dt * 1e6, 1),
+                                            "weight_GB/s": round(wbytes / dt / 1e9, 1),
+                                            "frac_of_hbm": round(wbytes / dt / 1e9 / HBM_PEAK_GBS, 4),
+                                            "timing": f"median of {runs}"}
+            del wss
+        del ys
     return out
 
 
-def run_gate_up(torch, fr, dev, shapes, layer, lora, g):
-    """The 7B layer's gate and up projections with the SiLU-gated product in one
-    launch, at 1, 8, 32, 64 and 128 tokens, beside the two separate linears
-    (which write gate and up and apply no SiLU)."""
+def graph_call_time(torch, calls):
+    """Median time of one call among `calls` (closures over distinct weights), run back to back as one
+    captured HIP graph: no host gaps between launches, and the weights rotate through more bytes than the
+    Infinity Cache holds. Returns (s per call, replays)."""
+    for c in calls:
+        c()
+    torch.cuda.synchronize()
+    gr = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(gr):
+        for c in calls:
+            c()
+    dt, runs = median_time(torch, gr.replay)
+    del gr
+    return dt / len(calls), runs
+
+
+def run_gate_up(torch, fr, dev, shapes, layers, lora, g):
+    """The 7B layer's gate and up projections with the SiLU-gated product
+    (fp4_gate_up_silu: one fused launch up to 16 tokens, two linears and the
+    product above) at 1, 8, 32, 64 and 128 tokens, beside the two separate
+    linears alone (which write gate and up and apply no SiLU), and the AQN
+    RMSNorm folded into the fused launch beside the norm launch followed by
+    fp4_gate_up_silu. Each variant runs over every weight copy as one graph;
+    every call gets a preallocated workspace."""
     n, k = shapes["gate"]
     wbytes = 2 * nvfp4_bytes(n, k)
+    lib = fr.load_library()
     out = {}
     for m in TOKENS + (128,):
         x = torch.randn((m, k), generator=g, device=dev).to(torch.bfloat16)
@@ -843,40 +881,44 @@ def run_gate_up(torch, fr, dev, shapes, layer, lora, g):
         need = fr.fp4_lora_linear_workspace_bytes(m, n, k, RANK)
         wsa, wsb = fr.linear_workspace(need, dev), fr.linear_workspace(need, dev)
         ya, yb = torch.empty_like(h), torch.empty_like(h)
+        gws = torch.zeros(max(256, fr.fp4_gate_up_silu_workspace_bytes(m, n, k, RANK)), dtype=torch.uint8,
+                          device=dev)
+        wn = torch.ones(k, dtype=torch.float32, device=dev)
+        xn = torch.empty_like(x)
+        aws = torch.empty(max(256, lib.fp4rl_aqn_gate_up_silu_workspace(m, n, k, RANK)), dtype=torch.uint8,
+                          device=dev)
 
-        def fused():
-            fr.fp4_gate_up_silu(x, layer["gate"], layer["up"], lora["gate"], lora["up"], LORA_SCALE, out=h)
+        def entry(L):
+            return lambda: fr.fp4_gate_up_silu(x, L["gate"], L["up"], lora["gate"], lora["up"], LORA_SCALE, out=h,
+                                               workspace=gws)
 
-        def separate():
-            fr.fp4_lora_linear(x, layer["gate"], *lora["gate"], LORA_SCALE, out=ya, workspace=wsa)
-            fr.fp4_lora_linear(x, layer["up"], *lora["up"], LORA_SCALE, out=yb, workspace=wsb)
+        def separate(L):
+            def f():
+                fr.fp4_lora_linear(x, L["gate"], *lora["gate"], LORA_SCALE, out=ya, workspace=wsa)
+                fr.fp4_lora_linear(x, L["up"], *lora["up"], LORA_SCALE, out=yb, workspace=wsb)
+            return f
 
-        res = {}
-        for name, f in (("fused_us", fused), ("two_linears_us", separate)):
-            res[name] = round(median_time(torch, f)[0] * 1e6, 1)
-        if m <= 128:
-            # the AQN RMSNorm folded in (raw x in, normalised tokens never stored)
-            # against the norm launch followed by the fused projections
-            wn = torch.ones(k, dtype=torch.float32, device=dev)
-            xn = torch.empty_like(x)
-            aws = torch.empty(max(256, fr.load_library().fp4rl_aqn_gate_up_silu_workspace(m, n, k, RANK)),
-                              dtype=torch.uint8, device=dev)
-            gws = torch.empty(max(256, fr.load_library().fp4rl_fp4_gate_up_silu_workspace(m, n, k, RANK)),
-                              dtype=torch.uint8, device=dev)
+        # the AQN RMSNorm folded into the fused launch (raw x in, normalised
+        # tokens never stored) against the norm launch followed by the entry point
+        def folded(L):
+            return lambda: fr.aqn_gate_up_silu(x, wn, SIGMA, 4, 0, 1, EPS, L["gate"], L["up"], lora["gate"],
+                                               lora["up"], LORA_SCALE, out=h, workspace=aws)
 
-            def folded():
-                fr.aqn_gate_up_silu(x, wn, SIGMA, 4, 0, 1, EPS, layer["gate"], layer["up"], lora["gate"],
-                                    lora["up"], LORA_SCALE, out=h, workspace=aws)
-
-            def norm_then_fused():
+        def norm_then_entry(L):
+            def f():
                 fr.aqn_rmsnorm(x, wn, SIGMA, 4, 0, 1, EPS, out=xn)
-                fr.fp4_gate_up_silu(xn, layer["gate"], layer["up"], lora["gate"], lora["up"], LORA_SCALE, out=h,
+                fr.fp4_gate_up_silu(xn, L["gate"], L["up"], lora["gate"], lora["up"], LORA_SCALE, out=h,
                                     workspace=gws)
+            return f
 
-            for name, f in (("aqn_folded_us", folded), ("aqn_then_fused_us", norm_then_fused)):
-                res[name] = round(median_time(torch, f)[0] * 1e6, 1)
-        res["fused_weight_GB/s"] = round(wbytes / res["fused_us"] / 1e3, 1)
-        res["fused_frac_of_hbm"] = round(wbytes / res["fused_us"] / 1e3 / HBM_PEAK_GBS, 4)
+        res = {"path": "fused" if m <= 16 else "two linears + gated product"}
+        for name, mk in (("entry_us", entry), ("two_linears_us", separate), ("aqn_folded_us", folded),
+                         ("aqn_then_entry_us", norm_then_entry)):
+            dt, runs = graph_call_time(torch, [mk(L) for L in layers])
+            res[name] = round(dt * 1e6, 1)
+        res["timing"] = f"median of {runs} replays of one graph over {len(layers)} weight copies"
+        res["entry_weight_GB/s"] = round(wbytes / res["entry_us"] / 1e3, 1)
+        res["entry_frac_of_hbm"] = round(wbytes / res["entry_us"] / 1e3 / HBM_PEAK_GBS, 4)
         out[f"M{m}"] = res
     return out
 

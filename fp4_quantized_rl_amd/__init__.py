@@ -30,6 +30,7 @@ __all__ = [
     "LIB_PATH", "Fp4rlError", "load_library", "NVFP4Weight", "nvfp4_empty", "nvfp4_quantize", "nvfp4_to_tiled",
     "fp4_lora_linear", "fp4_lora_linear_backward", "fp4_lora_linear_backward_workspace_bytes",
     "FP8Weight", "fp8_quantize", "fp8_lora_linear", "fp8_lora_linear_workspace_bytes", "fp4_gate_up_silu",
+    "fp4_gate_up_silu_workspace_bytes",
     "aqn_gate_up_silu",
     "lora_down", "fp4_linear_lora_up", "fp4_linear_kernel_name", "linear_workspace",
     "fp4_lora_linear_workspace_bytes", "fp4_linear_lora_up_workspace_bytes", "aqn_sigma", "aqn_rmsnorm", "philox_words",
@@ -288,9 +289,17 @@ def fp4_lora_linear(x, wq: NVFP4Weight, lora_a=None, lora_b=None, lora_scale: fl
     return out
 
 
+def fp4_gate_up_silu_workspace_bytes(m: int, n: int, k: int, r: int) -> int:
+    return load_library().fp4rl_fp4_gate_up_silu_workspace(m, n, k, r)
+
+
 def fp4_gate_up_silu(x, wg: NVFP4Weight, wu: NVFP4Weight, lora_gate=None, lora_up=None, lora_scale: float = 0.0,
                      out=None, workspace=None):
-    """h = bf16(SiLU(g) * u) for the NVFP4 + LoRA projections g (wg, lora_gate = (A, B)) and u of x [m <= 128, k]."""
+    """h = bf16(SiLU(g) * u) for the NVFP4 + LoRA projections g (wg, lora_gate = (A, B)) and u of x [m <= 128, k].
+
+    Up to 16 tokens one fused launch (g and u unrounded); from 17 tokens two
+    linears whose bf16 outputs feed the gated product.
+    """
     torch = _torch()
     m, n, k = _linear_args(x, wg)
     _linear_args(x, wu)
@@ -311,7 +320,8 @@ def fp4_gate_up_silu(x, wg: NVFP4Weight, wu: NVFP4Weight, lora_gate=None, lora_u
     lib = load_library()
     need = lib.fp4rl_fp4_gate_up_silu_workspace(m, n, k, r)
     if workspace is None and need:
-        workspace = torch.empty(need, dtype=torch.uint8, device=x.device)
+        # zero-filled: above 16 tokens it begins with a linear's counter words
+        workspace = torch.zeros(need, dtype=torch.uint8, device=x.device)
     with torch.cuda.device(x.device):
         _check(lib.fp4rl_fp4_gate_up_silu(_ptr(x), m, n, k, _ptr(wg.codes), _ptr(wg.scales), _ptr(wg.tensor_scale),
                                           _ptr(wu.codes), _ptr(wu.scales), _ptr(wu.tensor_scale),

@@ -346,25 +346,20 @@ fp4rl_status fp4rl_fp4_linear_lora_up(const uint16_t* x, int64_t m, int64_t n, i
                   "fp4_linear");
 }
 
-fp4rl_status fp4rl_fp4_lora_linear(const uint16_t* x, int64_t m, int64_t n, int64_t k, const uint8_t* codes,
-                                   const uint8_t* scales, const float* tensor_scale, const uint16_t* lora_a,
-                                   const uint16_t* lora_b, int64_t r, float lora_scale, uint16_t* y,
-                                   void* workspace, size_t workspace_bytes, fp4rl_stream stream) {
-  FP4RL_CHECK(check_linear_shape(m, n, k, r));
-  FP4RL_REQUIRE(std::isfinite(lora_scale), FP4RL_ERR_VALUE, "lora_scale is not finite");
-  FP4RL_REQUIRE((lora_a == nullptr) == (lora_b == nullptr), FP4RL_ERR_NULL,
-                "lora_a and lora_b must both be NULL or both be set");
-  if (lora_a == nullptr) r = 0;
-  if (m == 0 || n == 0) return ok();
+// The linear's launches on an argument-checked call (workspace sized by
+// fp4rl_fp4_lora_linear_workspace, its counter words zero): the t region and
+// the K-split partials are carved from the workspace, and with adapters t is
+// made either by producer workgroups inside the main launch or by a separate
+// down-projection launch.
+static fp4rl_status run_lora_linear(const uint16_t* x, int64_t m, int64_t n, int64_t k, const uint8_t* codes,
+                                    const uint8_t* scales, const float* tensor_scale, const uint16_t* lora_a,
+                                    const uint16_t* lora_b, int64_t r, float lora_scale, uint16_t* y, void* workspace,
+                                    fp4rl_stream stream) {
   const size_t tbytes = lora_part_bytes(m, k, r), pbytes = main_part_bytes(m, n, k);
-  FP4RL_CHECK(check_main_ws(workspace, workspace_bytes, linear_ws_bytes(tbytes, pbytes)));
-  if (r > 0) FP4RL_REQUIRE(aligned(lora_a, 16), FP4RL_ERR_ALIGN, "lora_a must be 16-byte aligned");
   uint8_t* ws = static_cast<uint8_t*>(workspace);
   float* t = tbytes ? reinterpret_cast<float*>(ws + fp4rl::kLinearCounterBytes) : nullptr;
   float* part = pbytes ? reinterpret_cast<float*>(ws + fp4rl::kLinearCounterBytes + tbytes) : nullptr;
   uint32_t* counters = pbytes ? reinterpret_cast<uint32_t*>(ws) : nullptr;
-  FP4RL_CHECK(check_linear_main(x, m, n, k, codes, scales, tensor_scale, t, lora_b, r, y));
-  FP4RL_CHECK(check_device());
   int slices = 1;
   fp4rl::LoraFuse lf{};
   if (r > 0) {
@@ -399,6 +394,26 @@ fp4rl_status fp4rl_fp4_lora_linear(const uint16_t* x, int64_t m, int64_t n, int6
                                            lf.producers > 0 ? 1 : slices,
                                            r > 0 ? lora_b : nullptr, r, y, part, counters, lf, stream),
                   "fp4_linear");
+}
+
+fp4rl_status fp4rl_fp4_lora_linear(const uint16_t* x, int64_t m, int64_t n, int64_t k, const uint8_t* codes,
+                                   const uint8_t* scales, const float* tensor_scale, const uint16_t* lora_a,
+                                   const uint16_t* lora_b, int64_t r, float lora_scale, uint16_t* y,
+                                   void* workspace, size_t workspace_bytes, fp4rl_stream stream) {
+  FP4RL_CHECK(check_linear_shape(m, n, k, r));
+  FP4RL_REQUIRE(std::isfinite(lora_scale), FP4RL_ERR_VALUE, "lora_scale is not finite");
+  FP4RL_REQUIRE((lora_a == nullptr) == (lora_b == nullptr), FP4RL_ERR_NULL,
+                "lora_a and lora_b must both be NULL or both be set");
+  if (lora_a == nullptr) r = 0;
+  if (m == 0 || n == 0) return ok();
+  const size_t tbytes = lora_part_bytes(m, k, r), pbytes = main_part_bytes(m, n, k);
+  FP4RL_CHECK(check_main_ws(workspace, workspace_bytes, linear_ws_bytes(tbytes, pbytes)));
+  if (r > 0) FP4RL_REQUIRE(aligned(lora_a, 16), FP4RL_ERR_ALIGN, "lora_a must be 16-byte aligned");
+  const float* t = tbytes ? reinterpret_cast<const float*>(static_cast<uint8_t*>(workspace) + fp4rl::kLinearCounterBytes)
+                         : nullptr;
+  FP4RL_CHECK(check_linear_main(x, m, n, k, codes, scales, tensor_scale, t, lora_b, r, y));
+  FP4RL_CHECK(check_device());
+  return run_lora_linear(x, m, n, k, codes, scales, tensor_scale, lora_a, lora_b, r, lora_scale, y, workspace, stream);
 }
 
 fp4rl_status fp4rl_linear_workspace_check(const void* workspace, size_t workspace_bytes, fp4rl_stream stream) {
@@ -507,9 +522,26 @@ fp4rl_status fp4rl_fp4_lora_linear_backward(const uint16_t* dy, const uint16_t* 
 
 // ----------------------------------------------------------------- gate/up --
 
+// Above kGateUpFusedMaxTokens: [linear workspace][g: m n bf16][u: m n bf16],
+// each region 256-byte aligned; the linear's counter words come first. Up to
+// kGateUpFusedMaxTokens: [counter words, untouched][fused launch's t slices],
+// so that one workspace serves both paths in any order.
+static size_t gate_up_two_linears_ws(int64_t m, int64_t n, int64_t k, int64_t r) {
+  return round_up(linear_ws_bytes(lora_part_bytes(m, k, r), main_part_bytes(m, n, k)), 256) +
+         2 * round_up((size_t)m * (size_t)n * 2, 256);
+}
+
+static size_t gate_up_fused_offset() { return round_up(fp4rl::kLinearCounterBytes, 256); }
+
+static size_t gate_up_ws_bytes(int64_t m, int64_t n, int64_t k, int64_t r) {
+  if (m > fp4rl::kGateUpFusedMaxTokens) return gate_up_two_linears_ws(m, n, k, r);
+  const size_t t = fp4rl::gate_up_workspace(m, k, r);
+  return t ? gate_up_fused_offset() + t : 0;
+}
+
 size_t fp4rl_fp4_gate_up_silu_workspace(int64_t m, int64_t n, int64_t k, int64_t r) {
   if (check_linear_shape(m, n, k, r) != FP4RL_OK || m == 0 || n == 0 || m > fp4rl::kGateUpMaxTokens) return 0;
-  return fp4rl::gate_up_workspace(m, k, r);
+  return gate_up_ws_bytes(m, n, k, r);
 }
 
 fp4rl_status fp4rl_fp4_gate_up_silu(const uint16_t* x, int64_t m, int64_t n, int64_t k, const uint8_t* gate_codes,
@@ -538,17 +570,31 @@ fp4rl_status fp4rl_fp4_gate_up_silu(const uint16_t* x, int64_t m, int64_t n, int
     FP4RL_REQUIRE(aligned(lora_a_gate, 16) && aligned(lora_b_gate, 16) && aligned(lora_a_up, 16) &&
                       aligned(lora_b_up, 16),
                   FP4RL_ERR_ALIGN, "adapters must be 16-byte aligned");
-  const size_t need = fp4rl::gate_up_workspace(m, k, r);
+  const size_t need = gate_up_ws_bytes(m, n, k, r);
   if (need) {
     FP4RL_REQUIRE(workspace != nullptr && workspace_bytes >= need, FP4RL_ERR_WORKSPACE, "workspace %zu < %zu bytes",
                   workspace_bytes, need);
     FP4RL_REQUIRE(aligned(workspace, 256), FP4RL_ERR_ALIGN, "workspace must be 256-byte aligned");
   }
   FP4RL_CHECK(check_device());
-  return launched(fp4rl::launch_gate_up(x, m, n, k, gate_codes, gate_scales, gate_tensor_scale, up_codes, up_scales,
-                                        up_tensor_scale, lora_a_gate, lora_b_gate, lora_a_up, lora_b_up, r,
-                                        lora_scale, static_cast<float*>(workspace), h, stream),
-                  "fp4_gate_up_silu");
+  if (m <= fp4rl::kGateUpFusedMaxTokens) {
+    float* tws = need ? reinterpret_cast<float*>(static_cast<uint8_t*>(workspace) + gate_up_fused_offset()) : nullptr;
+    return launched(fp4rl::launch_gate_up(x, m, n, k, gate_codes, gate_scales, gate_tensor_scale, up_codes, up_scales,
+                                          up_tensor_scale, lora_a_gate, lora_b_gate, lora_a_up, lora_b_up, r,
+                                          lora_scale, tws, h, stream),
+                    "fp4_gate_up_silu");
+  }
+  // two linears into bf16 g and u (one workspace, used in turn), then the gated product
+  uint8_t* ws = static_cast<uint8_t*>(workspace);
+  const size_t lin = round_up(linear_ws_bytes(lora_part_bytes(m, k, r), main_part_bytes(m, n, k)), 256);
+  uint16_t* g = reinterpret_cast<uint16_t*>(ws + lin);
+  uint16_t* u = reinterpret_cast<uint16_t*>(ws + lin + round_up((size_t)m * (size_t)n * 2, 256));
+  void* lws = lin ? ws : nullptr;
+  FP4RL_CHECK(run_lora_linear(x, m, n, k, gate_codes, gate_scales, gate_tensor_scale, r > 0 ? lora_a_gate : nullptr,
+                              r > 0 ? lora_b_gate : nullptr, r, lora_scale, g, lws, stream));
+  FP4RL_CHECK(run_lora_linear(x, m, n, k, up_codes, up_scales, up_tensor_scale, r > 0 ? lora_a_up : nullptr,
+                              r > 0 ? lora_b_up : nullptr, r, lora_scale, u, lws, stream));
+  return launched(fp4rl::launch_silu_mul(g, u, m * n, h, stream), "silu_mul");
 }
 
 size_t fp4rl_aqn_gate_up_silu_workspace(int64_t m, int64_t n, int64_t k, int64_t r) {

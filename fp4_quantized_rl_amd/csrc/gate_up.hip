@@ -298,6 +298,32 @@ hipError_t launch_gate_up(const uint16_t* x, int64_t m, int64_t n, int64_t k, co
   return hipGetLastError();
 }
 
+// h = bf16(SiLU(g) * u) from two bf16 linear outputs: the same fp32 formula
+// as the fused epilogue; eight elements per thread and step (count % 8
+// elements through the scalar tail)
+__global__ __launch_bounds__(256) void silu_mul_kernel(const uint16_t* __restrict__ g, const uint16_t* __restrict__ u,
+                                                       int64_t count, uint16_t* __restrict__ h) {
+  const int64_t n8 = count / 8, stride = (int64_t)gridDim.x * 256;
+  auto f = [](float gv, float uv) { return gv / (1.0f + expf(-gv)) * uv; };
+  for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < n8; i += stride) {
+    const uint4 gv = reinterpret_cast<const uint4*>(g)[i], uv = reinterpret_cast<const uint4*>(u)[i];
+    const uint32_t gw[4] = {gv.x, gv.y, gv.z, gv.w}, uw[4] = {uv.x, uv.y, uv.z, uv.w};
+    uint32_t o[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+      o[j] = pack_bf16x2(f(bf16_lo(gw[j]), bf16_lo(uw[j])), f(bf16_hi(gw[j]), bf16_hi(uw[j])));
+    reinterpret_cast<uint4*>(h)[i] = make_uint4(o[0], o[1], o[2], o[3]);
+  }
+  for (int64_t i = 8 * n8 + (int64_t)blockIdx.x * 256 + threadIdx.x; i < count; i += stride)
+    h[i] = (uint16_t)f32_to_bf16(f(bf16_lo(g[i]), bf16_lo(u[i])));
+}
+
+hipError_t launch_silu_mul(const uint16_t* g, const uint16_t* u, int64_t count, uint16_t* h, hipStream_t st) {
+  const int64_t blocks = std::max<int64_t>(1, std::min<int64_t>((count / 8 + 255) / 256, 2048));
+  hipLaunchKernelGGL(silu_mul_kernel, dim3((unsigned)blocks), dim3(256), 0, st, g, u, count, h);
+  return hipGetLastError();
+}
+
 // [t_g K-slices][t_u K-slices] and, above 16 tokens with K split, [t_g][t_u] summed (fp32)
 size_t gate_up_workspace(int64_t m, int64_t k, int64_t r) {
   if (r <= 0) return 0;

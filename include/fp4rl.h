@@ -269,19 +269,29 @@ fp4rl_status fp4rl_fp4_lora_linear_backward(const uint16_t* dy, const uint16_t* 
                                             void* workspace, size_t workspace_bytes, fp4rl_stream stream);
 
 /* ------------------------------------------------------------------------
- * Gate and up projections in one launch with the SiLU-gated product, for
- * decode batches. The Qwen2.5 models QeRL trains (QeRL explainer,
- * experiments) gate their MLP: h = SiLU(gate) * up. Each projection is an
- * NVFP4 + LoRA linear of the same x (tiled layout, own tensor scale and
- * adapters):
- *   h = bf16(SiLU(g) * u),  g = x deq(Wg)^T + s (x Ag^T) Bg^T,  u likewise,
- * g and u unrounded (fp32), SiLU(v) = v / (1 + exp(-v)).
+ * Gate and up projections with the SiLU-gated product, for decode batches.
+ * The Qwen2.5 models QeRL trains (QeRL explainer, experiments) gate their
+ * MLP: h = SiLU(gate) * up. Each projection is an NVFP4 + LoRA linear of the
+ * same x (tiled layout, own tensor scale and adapters):
+ *   g = x deq(Wg)^T + s (x Ag^T) Bg^T,  u likewise,  SiLU(v) = v / (1 + exp(-v)).
+ * Up to 16 tokens both projections run in one launch and h = bf16(SiLU(g) u)
+ *   with g and u unrounded (fp32). From 17 tokens on they run as two linears
+ *   (as fp4rl_fp4_lora_linear) into bf16 g and u in the workspace and a
+ *   third launch forms h = bf16(SiLU(g) u) from those rounded values; the
+ *   fused launch is the slower one there (measured, 7B gate/up 18944 x 3584,
+ *   r = 32, graph replays over 4 weight copies: fused 48.4 / 74.2 / 143.8 us
+ *   against 44.5 / 57.0 / 84.1 at 32 / 64 / 128 tokens; at 1 token fused
+ *   28.4 us, the two linears alone 27.6 plus about 3 for the product).
  * Arguments: x bf16 [m][k], 1 <= m <= 128 (else FP4RL_ERR_SHAPE); weights
  *   [n][k] each; adapters A [r][k], B [n][r] bf16, all four NULL or all
  *   set; h bf16 [m][n]. Shapes and alignment as for fp4rl_fp4_lora_linear.
- * Workspace: fp4rl_fp4_gate_up_silu_workspace(m, n, k, r) bytes (0 without
- *   adapters), 256-byte aligned, no initial contents needed (fp32 K-slices
- *   of t for both projections). */
+ * Workspace: fp4rl_fp4_gate_up_silu_workspace(m, n, k, r) bytes, 256-byte
+ *   aligned. It begins with 18 KB of counter words, as a linear workspace:
+ *   zero before the first call (e.g. a zero-filled workspace), left zero by
+ *   every call. Up to 16 tokens the fp32 K-slices of t for both projections
+ *   follow (0 bytes in all without adapters); from 17 tokens the rest of a
+ *   linear workspace, then g and u. One workspace, sized for the largest
+ *   call, serves calls of either path in any order (not at the same time). */
 size_t fp4rl_fp4_gate_up_silu_workspace(int64_t m, int64_t n, int64_t k, int64_t r);
 fp4rl_status fp4rl_fp4_gate_up_silu(const uint16_t* x, int64_t m, int64_t n, int64_t k, const uint8_t* gate_codes,
                                     const uint8_t* gate_scales, const float* gate_tensor_scale,
@@ -291,14 +301,19 @@ fp4rl_status fp4rl_fp4_gate_up_silu(const uint16_t* x, int64_t m, int64_t n, int
                                     float lora_scale, uint16_t* h, void* workspace, size_t workspace_bytes,
                                     fp4rl_stream stream);
 
-/* fp4rl_aqn_gate_up_silu: the same with the AQN RMSNorm of x folded in (QeRL
- * explainer, "zero overhead: folding into layer normalization"): x is the
- * raw bf16 input [m][k]; the projections see xn = bf16(x r_m (w + sigma z)),
- * r_m = 1 / sqrt(mean_k x^2 + eps), z the Philox normals of
- * (seed, step, norm_id) as in fp4rl_aqn_rmsnorm (norm_w fp32 [k],
- * k <= 16384). xn is never stored: the LoRA down-projections and the
- * projections normalise their fragments as they load them. Three launches
- * (noise vector, normalising LoRA down-projection, gate/up).
+/* fp4rl_aqn_gate_up_silu: the fused projections with the AQN RMSNorm of x
+ * folded in (QeRL explainer, "zero overhead: folding into layer
+ * normalization"): x is the raw bf16 input [m][k]; the projections see
+ * xn = bf16(x r_m (w + sigma z)), r_m = 1 / sqrt(mean_k x^2 + eps), z the
+ * Philox normals of (seed, step, norm_id) as in fp4rl_aqn_rmsnorm (norm_w
+ * fp32 [k], k <= 16384). xn is never stored: the LoRA down-projections and
+ * the projections normalise their fragments as they load them, at every
+ * token count (one fused launch, g and u unrounded). Three launches (noise
+ * vector, normalising LoRA down-projection, gate/up). It removes the round
+ * trip of xn through memory but is not faster than fp4rl_aqn_rmsnorm
+ * followed by fp4rl_fp4_gate_up_silu: every workgroup renormalises the
+ * fragments it loads (measured, 7B, graph replays: 41.8 vs 31.5 us at 1
+ * token, 333.3 vs 91.7 at 128).
  * Workspace: fp4rl_aqn_gate_up_silu_workspace(m, n, k, r) bytes, 256-byte
  *   aligned, no initial contents needed. */
 size_t fp4rl_aqn_gate_up_silu_workspace(int64_t m, int64_t n, int64_t k, int64_t r);
