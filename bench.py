@@ -211,8 +211,9 @@ def summarize_mfma(pmc_dir, workload, command):
         if not all(n in c for n in MFMA_PMC):
             continue
         short = short_kernel_name(kname)
-        if not any(t in short for t in ("prefill_kernel", "splitk_kernel", "nt_gemm_kernel", "skinny_kernel",
-                                          "gemv_kernel", "fp8_decode_kernel", "gate_up_kernel")):
+        if not any(t in short for t in ("prefill_kernel", "splitk_kernel", "mid_kernel", "nt_gemm_kernel",
+                                          "skinny_kernel", "gemv_kernel", "fp8_decode_kernel",
+                                          "e4m3_decode_kernel", "gate_up_kernel")):
             continue
         d = per.setdefault(short, {"dispatches": 0, "busy": 0.0, "gui": 0.0, "mops": 0.0, "mfma": 0.0,
                                    "valu": 0.0, "busy_cu": 0.0})

@@ -115,10 +115,11 @@ fp4rl_status check_linear_shape(int64_t m, int64_t n, int64_t k, int64_t r) {
   FP4RL_REQUIRE(m < kMaxDim && n < kMaxDim && k < kMaxDim, FP4RL_ERR_SHAPE, "dimension >= 2^31");
   // the kernels address activations with 32-bit byte offsets
   FP4RL_REQUIRE(m * k < ((int64_t)1 << 31), FP4RL_ERR_SHAPE, "m * k = %lld must be below 2^31", (long long)(m * k));
-  // the skinny (3..16 tokens) and prefill (> 128) kernels address activations
-  // with 32-bit byte offsets: from x, or from a 128-token group
-  FP4RL_REQUIRE(m <= 2 || m > 16 || m * k < ((int64_t)1 << 30), FP4RL_ERR_SHAPE,
-                "m * k = %lld must be below 2^30 for 3 <= m <= 16", (long long)(m * k));
+  // the skinny, split-K and mid-batch kernels (3..128 tokens) address x with
+  // 32-bit byte offsets whose top bit marks a piece past K (a buffer load
+  // that reads zero), and the prefill kernel (> 128) from a 128-token group
+  FP4RL_REQUIRE(m <= 2 || m > 128 || m * k < ((int64_t)1 << 30), FP4RL_ERR_SHAPE,
+                "m * k = %lld must be below 2^30 for 3 <= m <= 128", (long long)(m * k));
   FP4RL_REQUIRE(m <= 128 || k < ((int64_t)1 << 23), FP4RL_ERR_SHAPE, "k = %lld must be below 2^23 for m > 128",
                 (long long)k);
   FP4RL_REQUIRE(r <= fp4rl::kMaxRank, FP4RL_ERR_SHAPE, "rank r=%lld exceeds %lld", (long long)r,

@@ -150,7 +150,7 @@ fp4rl_status fp4rl_nvfp4_quantize_record(const void* w, int32_t w_dtype, int64_t
  *                       + sum_j t[m][j] B[n][j] ),   t = lora_scale * x A^T.
  * x bf16 [m][k]; codes/scales/tensor_scale of an [n][k] matrix in the
  * FP4RL_TILED layout; A bf16 [r][k]; B bf16 [n][r]; y bf16 [m][n].
- * k % 16 == 0; m * k < 2^31 (< 2^30 for 3 <= m <= 16); 0 <= r <= 256;
+ * k % 16 == 0; m * k < 2^31 (< 2^30 for 3 <= m <= 128); 0 <= r <= 256;
  * r == 0 or lora_a == lora_b ==
  * NULL means no LoRA term. Accumulation is fp32; the output is rounded once
  * to bf16.

@@ -104,6 +104,7 @@ def test_linear_rejects_bad_arguments(lib):
     assert call(m=-1) == ERR_SHAPE
     assert call(m=1 << 20, k=1 << 11) == ERR_SHAPE     # m * k = 2^31: beyond 32-bit activation offsets
     assert call(m=16, k=1 << 26) == ERR_SHAPE          # 3..16 tokens: 2 m k bytes must stay below 2^31
+    assert call(m=100, k=1 << 24) == ERR_SHAPE         # 17..128 tokens (split-K, mid-batch kernels): the same
     assert call(ls=float("nan")) == ERR_VALUE
     assert call(a=None) == ERR_NULL
     assert call(x=None) == ERR_NULL
