@@ -93,9 +93,12 @@ def _aqn_case(m, k, seed):
 
 
 @pytest.mark.parametrize("shape", [(1, 16, 64, 0), (5, 40, 144, 4), (16, 64, 1040, 8), (40, 100, 512, 32),
-                                   (128, 64, 256, 5), (3, 37, 208, 4), (70, 131, 4112, 16)])
+                                   (128, 64, 256, 5), (3, 37, 208, 4), (70, 131, 4112, 16),
+                                   (128, 72, 5120, 16), (100, 40, 16384, 8), (65, 24, 16384, 4)])
 def test_aqn_folded_ragged(shape):
-    """The AQN RMSNorm folded into gate/up equals the norm oracle feeding the gate/up oracle."""
+    """The AQN RMSNorm folded into gate/up equals the norm oracle feeding the gate/up oracle. The last three
+    shapes are the 32B hidden size at 128 tokens and the widest norm (k = 16384: 64 KB of noisy weight in LDS
+    beside the 64 KB reduction buffer of the 8-token-tile launch)."""
     from oracle import aqn
     from oracle.numerics import bf16_bits_of
 

@@ -131,7 +131,8 @@ def test_gate_up_graph_replays(m):
     wq, x, a, b = _inputs(dev, m, n, k, r, 400 + m)
     wu, _, a2, b2 = _inputs(dev, m, n, k, r, 500 + m)
     h = torch.empty((m, n), dtype=torch.bfloat16, device=dev)
-    ws = torch.empty(max(256, fr.load_library().fp4rl_fp4_gate_up_silu_workspace(m, n, k, r)), dtype=torch.uint8,
+    # counter words zero before the first call, as the workspace contract asks
+    ws = torch.zeros(max(256, fr.load_library().fp4rl_fp4_gate_up_silu_workspace(m, n, k, r)), dtype=torch.uint8,
                      device=dev)
     other = (lambda: fr.fp4_gate_up_silu(x[:1], wq, wu, (a, b), (a2, b2), 2.0))
     _replays_match(dev, lambda: fr.fp4_gate_up_silu(x, wq, wu, (a, b), (a2, b2), 2.0, out=h, workspace=ws), [h],
