@@ -501,8 +501,9 @@ def main():
         return
     if args.gate_up_only:
         progress("gate/up + SiLU timing")
-        print(json.dumps({"gate_up_silu": run_gate_up(torch, fr, dev, shapes, layers, lora,
-                                                      torch.Generator(device=dev).manual_seed(21))}))
+        gg = torch.Generator(device=dev).manual_seed(21)
+        print(json.dumps({"gate_up_silu": run_gate_up(torch, fr, dev, shapes, layers, lora, gg),
+                          "aqn_qkv_fold": run_qkv_fold(torch, fr, dev, shapes, layers, lora, gg)}))
         return
     if args.decode32b_only:
         progress(f"32B decode pass, {args.layers32b} layers")
@@ -713,6 +714,7 @@ def run_extras(torch, fr, dev, shapes, layers, lora, fp32):
     res["lora_backward"] = run_backward(torch, fr, dev, shapes, layer, lora, xs, g)
     res["fp8_linear"] = run_fp8(torch, fr, dev, shapes, lora, xs, g)
     res["gate_up_silu"] = run_gate_up(torch, fr, dev, shapes, layers, lora, g)
+    res["aqn_qkv_fold"] = run_qkv_fold(torch, fr, dev, shapes, layers, lora, g)
     del xs
 
     # quantiser on 14B shapes: one layer's five matrices, 0.02 t(3) weights with
@@ -920,6 +922,40 @@ def run_gate_up(torch, fr, dev, shapes, layers, lora, g):
         res["timing"] = f"median of {runs} replays of one graph over {len(layers)} weight copies"
         res["entry_weight_GB/s"] = round(wbytes / res["entry_us"] / 1e3, 1)
         res["entry_frac_of_hbm"] = round(wbytes / res["entry_us"] / 1e3 / HBM_PEAK_GBS, 4)
+        out[f"M{m}"] = res
+    return out
+
+
+def run_qkv_fold(torch, fr, dev, shapes, layers, lora, g):
+    """The 7B layer's qkv projection with the AQN RMSNorm folded in (fp4rl_aqn_lora_linear: raw x in, the
+    normalised tokens never stored) beside the norm launch followed by the linear, at 1, 8, 32, 64 and 128
+    tokens; each variant runs over every weight copy as one graph, with preallocated workspaces."""
+    n, k = shapes["qkv"]
+    out = {}
+    for m in TOKENS + (128,):
+        x = torch.randn((m, k), generator=g, device=dev).to(torch.bfloat16)
+        y = torch.empty((m, n), dtype=torch.bfloat16, device=dev)
+        xn = torch.empty_like(x)
+        wn = torch.ones(k, dtype=torch.float32, device=dev)
+        lws = fr.linear_workspace(fr.fp4_lora_linear_workspace_bytes(m, n, k, RANK), dev)
+        fws = torch.empty(max(256, fr.load_library().fp4rl_aqn_lora_linear_workspace(m, n, k, RANK)),
+                          dtype=torch.uint8, device=dev)
+
+        def folded(L):
+            return lambda: fr.aqn_lora_linear(x, wn, SIGMA, 4, 0, 0, EPS, L["qkv"], *lora["qkv"], LORA_SCALE, out=y,
+                                              workspace=fws)
+
+        def norm_then_linear(L):
+            def f():
+                fr.aqn_rmsnorm(x, wn, SIGMA, 4, 0, 0, EPS, out=xn)
+                fr.fp4_lora_linear(xn, L["qkv"], *lora["qkv"], LORA_SCALE, out=y, workspace=lws)
+            return f
+
+        res = {}
+        for name, mk in (("aqn_folded_us", folded), ("aqn_then_linear_us", norm_then_linear)):
+            dt, runs = graph_call_time(torch, [mk(L) for L in layers])
+            res[name] = round(dt * 1e6, 1)
+        res["timing"] = f"median of {runs} replays of one graph over {len(layers)} weight copies"
         out[f"M{m}"] = res
     return out
 

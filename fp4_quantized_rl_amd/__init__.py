@@ -31,7 +31,7 @@ __all__ = [
     "fp4_lora_linear", "fp4_lora_linear_backward", "fp4_lora_linear_backward_workspace_bytes",
     "FP8Weight", "fp8_quantize", "fp8_lora_linear", "fp8_lora_linear_workspace_bytes", "fp4_gate_up_silu",
     "fp4_gate_up_silu_workspace_bytes",
-    "aqn_gate_up_silu",
+    "aqn_gate_up_silu", "aqn_lora_linear",
     "lora_down", "fp4_linear_lora_up", "fp4_linear_kernel_name", "linear_workspace",
     "fp4_lora_linear_workspace_bytes", "fp4_linear_lora_up_workspace_bytes", "aqn_sigma", "aqn_rmsnorm", "philox_words",
     "EXPORTED_SYMBOLS",
@@ -79,6 +79,10 @@ _SIGNATURES = {
     "fp4rl_aqn_gate_up_silu": (_STATUS, [_P, _I64, _I64, _I64, _P, _c.c_float, _c.c_uint64, _c.c_uint64,
                                          _c.c_uint32, _c.c_float, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _I64,
                                          _c.c_float, _P, _P, _c.c_size_t, _P]),
+    "fp4rl_aqn_lora_linear_workspace": (_c.c_size_t, [_I64, _I64, _I64, _I64]),
+    "fp4rl_aqn_lora_linear": (_STATUS, [_P, _I64, _I64, _I64, _P, _c.c_float, _c.c_uint64, _c.c_uint64,
+                                        _c.c_uint32, _c.c_float, _P, _P, _P, _P, _P, _I64, _c.c_float, _P, _P,
+                                        _c.c_size_t, _P]),
     "fp4rl_fp8_quantize": (_STATUS, [_P, _c.c_int32, _I64, _I64, _P, _P, _P]),
     "fp4rl_fp8_lora_linear_workspace": (_c.c_size_t, [_I64, _I64, _I64, _I64]),
     "fp4rl_fp8_lora_linear": (_STATUS, [_P, _I64, _I64, _I64, _P, _P, _P, _P, _I64, _c.c_float, _P, _P, _c.c_size_t,
@@ -364,6 +368,36 @@ def aqn_gate_up_silu(x, norm_w, sigma: float, seed: int, step: int, norm_id: int
                                           _ptr(wu.tensor_scale), *[_ptr(p) for p in ptrs], r, float(lora_scale),
                                           _ptr(out), _ptr(workspace), workspace.numel(), _stream(x.device)),
                "aqn_gate_up_silu")
+    return out
+
+
+def aqn_lora_linear(x, norm_w, sigma: float, seed: int, step: int, norm_id: int, eps: float, wq: NVFP4Weight,
+                    lora_a=None, lora_b=None, lora_scale: float = 0.0, out=None, workspace=None):
+    """fp4_lora_linear of the AQN RMSNorm of x (raw bf16 [m <= 128, k]), the norm folded in (never stored)."""
+    torch = _torch()
+    m, n, k = _linear_args(x, wq)
+    _dev_tensor(norm_w, "norm_w", (torch.float32,), 1)
+    if norm_w.shape[0] != k:
+        raise ValueError("norm_w must be [k]")
+    r = 0
+    if lora_a is not None or lora_b is not None:
+        _dev_tensor(lora_a, "lora_a", (torch.bfloat16,), 2)
+        _dev_tensor(lora_b, "lora_b", (torch.bfloat16,), 2)
+        r = lora_a.shape[0]
+        if lora_a.shape != (r, k) or lora_b.shape != (n, r):
+            raise ValueError("LoRA shapes must be A [r, k] and B [n, r]")
+    if out is None:
+        out = torch.empty((m, n), dtype=torch.bfloat16, device=x.device)
+    lib = load_library()
+    need = lib.fp4rl_aqn_lora_linear_workspace(m, n, k, r)
+    if workspace is None:
+        workspace = torch.empty(max(need, 256), dtype=torch.uint8, device=x.device)
+    with torch.cuda.device(x.device):
+        _check(lib.fp4rl_aqn_lora_linear(_ptr(x), m, n, k, _ptr(norm_w), float(sigma), int(seed), int(step),
+                                         int(norm_id), float(eps), _ptr(wq.codes), _ptr(wq.scales),
+                                         _ptr(wq.tensor_scale), _ptr(lora_a), _ptr(lora_b), r, float(lora_scale),
+                                         _ptr(out), _ptr(workspace), workspace.numel(), _stream(x.device)),
+               "aqn_lora_linear")
     return out
 
 

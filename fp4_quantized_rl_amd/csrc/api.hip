@@ -649,6 +649,48 @@ fp4rl_status fp4rl_aqn_gate_up_silu(const uint16_t* x, int64_t m, int64_t n, int
                   "aqn_gate_up_silu");
 }
 
+size_t fp4rl_aqn_lora_linear_workspace(int64_t m, int64_t n, int64_t k, int64_t r) {
+  if (check_linear_shape(m, n, k, r) != FP4RL_OK || m == 0 || n == 0 || m > fp4rl::kGateUpMaxTokens ||
+      k > fp4rl::kAqnMaxD)
+    return 0;
+  return fp4rl::aqn_linear_workspace(m, k, r);
+}
+
+fp4rl_status fp4rl_aqn_lora_linear(const uint16_t* x, int64_t m, int64_t n, int64_t k, const float* norm_w,
+                                   float sigma, uint64_t seed, uint64_t step, uint32_t norm_id, float eps,
+                                   const uint8_t* codes, const uint8_t* scales, const float* tensor_scale,
+                                   const uint16_t* lora_a, const uint16_t* lora_b, int64_t r, float lora_scale,
+                                   uint16_t* y, void* workspace, size_t workspace_bytes, fp4rl_stream stream) {
+  FP4RL_CHECK(check_linear_shape(m, n, k, r));
+  FP4RL_REQUIRE(m <= fp4rl::kGateUpMaxTokens, FP4RL_ERR_SHAPE, "m=%lld exceeds %lld tokens", (long long)m,
+                (long long)fp4rl::kGateUpMaxTokens);
+  FP4RL_REQUIRE(k <= fp4rl::kAqnMaxD, FP4RL_ERR_SHAPE, "k=%lld exceeds the norm's width %lld", (long long)k,
+                (long long)fp4rl::kAqnMaxD);
+  FP4RL_REQUIRE(std::isfinite(lora_scale), FP4RL_ERR_VALUE, "lora_scale is not finite");
+  FP4RL_REQUIRE(std::isfinite(sigma) && sigma >= 0.0f, FP4RL_ERR_VALUE, "sigma must be finite and >= 0");
+  FP4RL_REQUIRE(std::isfinite(eps) && eps >= 0.0f, FP4RL_ERR_VALUE, "eps must be finite and >= 0");
+  FP4RL_REQUIRE((lora_a == nullptr) == (lora_b == nullptr), FP4RL_ERR_NULL,
+                "lora_a and lora_b must both be NULL or both be set");
+  if (lora_a == nullptr) r = 0;
+  if (m == 0 || n == 0) return ok();
+  FP4RL_REQUIRE(x && norm_w && codes && scales && tensor_scale && y, FP4RL_ERR_NULL,
+                "x, the norm weight, the weight and y must be non-NULL");
+  FP4RL_REQUIRE(aligned(x, 16) && aligned(norm_w, 16) && aligned(codes, 16) && aligned(scales, 16) &&
+                    aligned(y, 16) && aligned(tensor_scale, 4),
+                FP4RL_ERR_ALIGN, "x, norm_w, codes, scales and y must be 16-byte aligned, the tensor scale 4-byte aligned");
+  if (r > 0)
+    FP4RL_REQUIRE(aligned(lora_a, 16) && aligned(lora_b, 16), FP4RL_ERR_ALIGN, "adapters must be 16-byte aligned");
+  const size_t need = fp4rl::aqn_linear_workspace(m, k, r);
+  FP4RL_REQUIRE(workspace != nullptr && workspace_bytes >= need, FP4RL_ERR_WORKSPACE, "workspace %zu < %zu bytes",
+                workspace_bytes, need);
+  FP4RL_REQUIRE(aligned(workspace, 256), FP4RL_ERR_ALIGN, "workspace must be 256-byte aligned");
+  FP4RL_CHECK(check_device());
+  return launched(fp4rl::launch_aqn_linear(x, m, n, k, norm_w, sigma, seed, step, norm_id, eps, codes, scales,
+                                           tensor_scale, r > 0 ? lora_a : nullptr, r > 0 ? lora_b : nullptr, r,
+                                           lora_scale, workspace, y, stream),
+                  "aqn_lora_linear");
+}
+
 // --------------------------------------------------------------------- FP8 --
 
 fp4rl_status fp4rl_fp8_quantize(const void* w, int32_t w_dtype, int64_t n, int64_t k, uint8_t* codes,

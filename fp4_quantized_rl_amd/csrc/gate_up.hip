@@ -55,7 +55,8 @@ __device__ __forceinline__ uint4 token_fragment(const uint16_t* p, float rinv, c
   }
 }
 
-template <int T, int RT, bool NORM = false>
+// PAIR = false: one projection only (the gate's arguments), h = bf16(g).
+template <int T, int RT, bool NORM = false, bool PAIR = true>
 __global__ __launch_bounds__(256) void gate_up_kernel(const uint16_t* __restrict__ x, int M, int N, int K,
                                                       const uint8_t* __restrict__ cg, const uint8_t* __restrict__ sg,
                                                       const float* __restrict__ stg, const uint8_t* __restrict__ cu,
@@ -65,7 +66,8 @@ __global__ __launch_bounds__(256) void gate_up_kernel(const uint16_t* __restrict
                                                       const uint16_t* __restrict__ bu, int r,
                                                       uint16_t* __restrict__ h, const float* __restrict__ wn,
                                                       const float* __restrict__ rinv) {
-  __shared__ f32x4 red[4][2 * RT * T][64];
+  constexpr int P = PAIR ? 2 : 1;  // projections
+  __shared__ f32x4 red[4][P * RT * T][64];
   extern __shared__ float wns[];  // NORM: the noisy norm weight, K floats (dynamic LDS)
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   if constexpr (NORM) {
@@ -80,9 +82,9 @@ __global__ __launch_bounds__(256) void gate_up_kernel(const uint16_t* __restrict
   for (int i = 0; i < RT; ++i) {  // row tiles past the matrix are clamped (never stored)
     const int64_t tile0 = (int64_t)min(RT * (int)blockIdx.x + i, NT - 1) * KC;
     gcode[i] = cg + tile0 * 1024 + 16 * lane;
-    ucode[i] = cu + tile0 * 1024 + 16 * lane;
     gsc[i] = sg + tile0 * 128 + 4 * (16 * (lg >> 1) + li);
-    usc[i] = su + tile0 * 128 + 4 * (16 * (lg >> 1) + li);
+    ucode[i] = PAIR ? cu + tile0 * 1024 + 16 * lane : nullptr;
+    usc[i] = PAIR ? su + tile0 * 128 + 4 * (16 * (lg >> 1) + li) : nullptr;
   }
   const uint16_t* xrow[T];  // tokens past M are clamped (their columns are never stored)
   float rv[T];
@@ -97,14 +99,16 @@ __global__ __launch_bounds__(256) void gate_up_kernel(const uint16_t* __restrict
 #pragma unroll
     for (int j = 0; j < T; ++j) ag[i][j] = au[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
   for (int c = wave; c < KC; c += 4) {
-    uint4 wg[RT], wu[RT];
-    uint32_t sgw[RT], suw[RT];
+    uint4 wg[RT], wu[RT] = {};
+    uint32_t sgw[RT], suw[RT] = {};
 #pragma unroll
     for (int i = 0; i < RT; ++i) {
       wg[i] = ld_nt16(gcode[i] + (int64_t)c * 1024);
-      wu[i] = ld_nt16(ucode[i] + (int64_t)c * 1024);
       sgw[i] = *reinterpret_cast<const uint32_t*>(gsc[i] + (int64_t)c * 128);
-      suw[i] = *reinterpret_cast<const uint32_t*>(usc[i] + (int64_t)c * 128);
+      if constexpr (PAIR) {
+        wu[i] = ld_nt16(ucode[i] + (int64_t)c * 1024);
+        suw[i] = *reinterpret_cast<const uint32_t*>(usc[i] + (int64_t)c * 128);
+      }
     }
     uint4 xv[4][T];
 #pragma unroll
@@ -119,23 +123,23 @@ __global__ __launch_bounds__(256) void gate_up_kernel(const uint16_t* __restrict
       const uint32_t cwg[4] = {wg[i].x, wg[i].y, wg[i].z, wg[i].w}, cwu[4] = {wu[i].x, wu[i].y, wu[i].z, wu[i].w};
       float scg[4], scu[4];
       e4m3_scales(sgw[i], scg);
-      e4m3_scales(suw[i], scu);
+      if constexpr (PAIR) e4m3_scales(suw[i], scu);
 #pragma unroll
       for (int st = 0; st < 4; ++st) {
         const bf16x8 a_g = dequant8(cwg[st], scg[st]);
-        const bf16x8 a_u = dequant8(cwu[st], scu[st]);
 #pragma unroll
-        for (int j = 0; j < T; ++j) {
-          const bf16x8 b = as_bf16x8(xv[st][j]);
-          ag[i][j] = mfma16x16x32(a_g, b, ag[i][j]);
-          au[i][j] = mfma16x16x32(a_u, b, au[i][j]);
+        for (int j = 0; j < T; ++j) ag[i][j] = mfma16x16x32(a_g, as_bf16x8(xv[st][j]), ag[i][j]);
+        if constexpr (PAIR) {
+          const bf16x8 a_u = dequant8(cwu[st], scu[st]);
+#pragma unroll
+          for (int j = 0; j < T; ++j) au[i][j] = mfma16x16x32(a_u, as_bf16x8(xv[st][j]), au[i][j]);
         }
       }
     }
   }
   // each wave's partial sums times the tensor scales; the LoRA terms are
   // added by MFMA, the gate's by wave 0 and the up's by wave 1
-  const float sgt = *stg, sut = *stu;
+  const float sgt = *stg, sut = PAIR ? *stu : 0.0f;
 #pragma unroll
   for (int i = 0; i < RT; ++i) {
 #pragma unroll
@@ -144,11 +148,11 @@ __global__ __launch_bounds__(256) void gate_up_kernel(const uint16_t* __restrict
       au[i][j] *= sut;
     }
     if (r > 0 && wave == 0) lora_mfma<T>(ag[i], tg, tsl, bg, r, M, N, RT * (int)blockIdx.x + i, li, lg);
-    if (r > 0 && wave == 1) lora_mfma<T>(au[i], tu, tsl, bu, r, M, N, RT * (int)blockIdx.x + i, li, lg);
+    if (PAIR && r > 0 && wave == 1) lora_mfma<T>(au[i], tu, tsl, bu, r, M, N, RT * (int)blockIdx.x + i, li, lg);
 #pragma unroll
     for (int j = 0; j < T; ++j) {
-      red[wave][(2 * i) * T + j][lane] = ag[i][j];
-      red[wave][(2 * i + 1) * T + j][lane] = au[i][j];
+      red[wave][(P * i) * T + j][lane] = ag[i][j];
+      if constexpr (PAIR) red[wave][(P * i + 1) * T + j][lane] = au[i][j];
     }
   }
   __syncthreads();
@@ -160,16 +164,21 @@ __global__ __launch_bounds__(256) void gate_up_kernel(const uint16_t* __restrict
     const int m = tl, n = 16 * (RT * (int)blockIdx.x + i) + rl;
     if (m >= M || n >= N) continue;
     const int j = tl >> 4, ln = 16 * (rl >> 2) + (tl & 15), v = rl & 3;
-    const int sg_ = (2 * i) * T + j, su_ = (2 * i + 1) * T + j;
+    const int sg_ = (P * i) * T + j;
     const float g = ((red[0][sg_][ln][v] + red[1][sg_][ln][v]) + red[2][sg_][ln][v]) + red[3][sg_][ln][v];
-    const float u = ((red[0][su_][ln][v] + red[1][su_][ln][v]) + red[2][su_][ln][v]) + red[3][su_][ln][v];
-    h[(int64_t)m * N + n] = (uint16_t)f32_to_bf16(g / (1.0f + expf(-g)) * u);
+    if constexpr (PAIR) {
+      const int su_ = (P * i + 1) * T + j;
+      const float u = ((red[0][su_][ln][v] + red[1][su_][ln][v]) + red[2][su_][ln][v]) + red[3][su_][ln][v];
+      h[(int64_t)m * N + n] = (uint16_t)f32_to_bf16(g / (1.0f + expf(-g)) * u);
+    } else {
+      h[(int64_t)m * N + n] = (uint16_t)f32_to_bf16(g);
+    }
   }
 }
 
-// The AQN RMSNorm folded into the LoRA down-projections of gate and up: one
-// workgroup per 16-token tile, 16-rank tile, adapter and K-slice (blockIdx.z
-// = 2 slice + adapter). Its waves first take 4 tokens each for their sum of
+// The AQN RMSNorm folded into the LoRA down-projections of gate and up (nad
+// = 2) or of one projection (nad = 1): one workgroup per 16-token tile,
+// 16-rank tile, adapter and K-slice (blockIdx.z = nad slice + adapter). Its waves first take 4 tokens each for their sum of
 // squares (16-byte loads, all issued before the sums; r_m = 1 / sqrt(ss / K
 // + eps), the norm's formula; the (., 0, 0) workgroup writes r_m for the
 // projections), then take the slice's 32-k steps in turn, loading all their
@@ -184,13 +193,14 @@ __global__ __launch_bounds__(256) void norm_lora_down_kernel(const uint16_t* __r
                                                              const uint16_t* __restrict__ ag,
                                                              const uint16_t* __restrict__ au, int r, float s,
                                                              int kslice, float* __restrict__ rinv,
-                                                             float* __restrict__ tg, float* __restrict__ tu) {
+                                                             float* __restrict__ tg, float* __restrict__ tu,
+                                                             int nad) {
   __shared__ float rs[16];
   __shared__ f32x4 red[3][64];
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int li = lane & 15, lg = lane >> 4;
   const int m0 = 16 * blockIdx.x, j0 = 16 * blockIdx.y;
-  const int adapter = blockIdx.z & 1, z = blockIdx.z >> 1;
+  const int adapter = nad == 2 ? (int)(blockIdx.z & 1) : 0, z = (int)blockIdx.z / nad;
   const int nv = K >> 3;  // 16-byte pieces per token row
   float ss[4] = {0.f, 0.f, 0.f, 0.f};
   for (int c = lane; c < nv; c += 64) {
@@ -355,7 +365,7 @@ hipError_t launch_aqn_gate_up(const uint16_t* x, int64_t m, int64_t n, int64_t k
   if (e != hipSuccess) return e;
   const dim3 lgrid((unsigned)((m + 15) / 16), (unsigned)(r > 0 ? (r + 15) / 16 : 1), r > 0 ? 2u * S : 1u);
   hipLaunchKernelGGL(norm_lora_down_kernel, lgrid, dim3(256), 0, st, x, (int)m, (int)k, wn, eps, ag, au, (int)r, s,
-                     32 * 4 * kNormLoraSteps, rinv, tg, tu);
+                     32 * 4 * kNormLoraSteps, rinv, tg, tu, 2);
   if ((e = hipGetLastError()) != hipSuccess) return e;
   const int T = gate_up_token_tiles(m);
   // LDS: the waves' sums (8 KB per row tile and token tile) plus k floats of
@@ -372,6 +382,46 @@ hipError_t launch_aqn_gate_up(const uint16_t* x, int64_t m, int64_t n, int64_t k
   else if (T == 4) FP4RL_AQN_GATE_UP(4, 2);
   else FP4RL_AQN_GATE_UP(8, 1);
 #undef FP4RL_AQN_GATE_UP
+  return hipGetLastError();
+}
+
+// [w_noise: k][r_m: m][t K-slices: S m r] (fp32, each 256-byte aligned)
+size_t aqn_linear_workspace(int64_t m, int64_t k, int64_t r) {
+  auto a = [](size_t v) { return (v * 4 + 255) / 256 * 256; };
+  return a((size_t)k) + a((size_t)m) + a((size_t)norm_lora_slices(k) * m * r);
+}
+
+hipError_t launch_aqn_linear(const uint16_t* x, int64_t m, int64_t n, int64_t k, const float* norm_w, float sigma,
+                             uint64_t seed, uint64_t step, uint32_t norm_id, float eps, const uint8_t* codes,
+                             const uint8_t* scales, const float* ts, const uint16_t* a, const uint16_t* b, int64_t r,
+                             float s, void* ws, uint16_t* y, hipStream_t st) {
+  auto al = [](size_t v) { return (v * 4 + 255) / 256 * 256; };
+  uint8_t* base = static_cast<uint8_t*>(ws);
+  float* wn = reinterpret_cast<float*>(base);
+  float* rinv = reinterpret_cast<float*>(base + al((size_t)k));
+  float* t = reinterpret_cast<float*>(base + al((size_t)k) + al((size_t)m));
+  const int S = norm_lora_slices(k);
+  hipError_t e = launch_aqn_rmsnorm(nullptr, 0, k, norm_w, sigma, seed, step, norm_id, eps, nullptr, wn, st);
+  if (e != hipSuccess) return e;
+  const dim3 lgrid((unsigned)((m + 15) / 16), (unsigned)(r > 0 ? (r + 15) / 16 : 1), r > 0 ? (unsigned)S : 1u);
+  hipLaunchKernelGGL(norm_lora_down_kernel, lgrid, dim3(256), 0, st, x, (int)m, (int)k, wn, eps, a, nullptr, (int)r, s,
+                     32 * 4 * kNormLoraSteps, rinv, t, nullptr, 1);
+  if ((e = hipGetLastError()) != hipSuccess) return e;
+  const int T = gate_up_token_tiles(m);
+  // LDS: the waves' sums (4 KB per row tile and token tile) plus k floats of
+  // the noisy weight (<= 64 KB)
+  const int RT = T == 1 ? 1 : 2;
+  const dim3 grid((unsigned)(((n + 15) / 16 + RT - 1) / RT));
+  const int tsl = r > 0 ? S : 0;
+#define FP4RL_AQN_LINEAR(TT, RR)                                                                                     \
+  hipLaunchKernelGGL((gate_up_kernel<TT, RR, true, false>), grid, dim3(256), (size_t)k * 4, st, x, (int)m, (int)n,    \
+                     (int)k, codes, scales, ts, nullptr, nullptr, nullptr, t, nullptr, tsl, b, nullptr, (int)r, y, wn, \
+                     rinv)
+  if (T == 1) FP4RL_AQN_LINEAR(1, 1);
+  else if (T == 2) FP4RL_AQN_LINEAR(2, 2);
+  else if (T == 4) FP4RL_AQN_LINEAR(4, 2);
+  else FP4RL_AQN_LINEAR(8, 2);
+#undef FP4RL_AQN_LINEAR
   return hipGetLastError();
 }
 

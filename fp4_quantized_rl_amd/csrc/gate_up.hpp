@@ -36,4 +36,14 @@ hipError_t launch_aqn_gate_up(const uint16_t* x, int64_t m, int64_t n, int64_t k
                               const float* stu, const uint16_t* ag, const uint16_t* bg, const uint16_t* au,
                               const uint16_t* bu, int64_t r, float s, void* ws, uint16_t* h, hipStream_t stream);
 
+// The AQN RMSNorm of x folded into one NVFP4 + LoRA linear (e.g. qkv):
+// y = bf16(s_t x_n deq(W)^T + s (x_n A^T) B^T), x_n = bf16(x r_m w_noise),
+// never stored. Workspace: the noisy weight (k fp32), r_m (m fp32), then the
+// K-slices of t (m r fp32 each). k <= the norm's width limit, k % 16 == 0.
+size_t aqn_linear_workspace(int64_t m, int64_t k, int64_t r);
+hipError_t launch_aqn_linear(const uint16_t* x, int64_t m, int64_t n, int64_t k, const float* norm_w, float sigma,
+                             uint64_t seed, uint64_t step, uint32_t norm_id, float eps, const uint8_t* codes,
+                             const uint8_t* scales, const float* ts, const uint16_t* a, const uint16_t* b, int64_t r,
+                             float s, void* ws, uint16_t* y, hipStream_t stream);
+
 }  // namespace fp4rl

@@ -326,6 +326,33 @@ fp4rl_status fp4rl_aqn_gate_up_silu(const uint16_t* x, int64_t m, int64_t n, int
                                     int64_t r, float lora_scale, uint16_t* h, void* workspace,
                                     size_t workspace_bytes, fp4rl_stream stream);
 
+/* fp4rl_aqn_lora_linear: one NVFP4 + LoRA linear (e.g. the attention's qkv
+ * projection) with the AQN RMSNorm of x folded in (QeRL explainer, "zero
+ * overhead: folding into layer normalization"):
+ *   y = bf16(s_t xn deq(W)^T + s (xn A^T) B^T),  xn = bf16(x r_m (w + sigma z)),
+ * r_m = 1 / sqrt(mean_k x^2 + eps), z the Philox normals of (seed, step,
+ * norm_id) as in fp4rl_aqn_rmsnorm; xn is never stored. Three launches
+ * (noise vector; normalising LoRA down-projection and r_m; the projection,
+ * whose workgroups normalise the token fragments they load). The same
+ * values as fp4rl_aqn_rmsnorm followed by fp4rl_fp4_lora_linear, up to the
+ * order of the fp32 sums. It removes the round trip of xn through memory
+ * but is slower than those two launches (measured, 7B qkv 4608 x 3584,
+ * r = 32, graph replays: 25.8 vs 14.2 us at 1 token, 35.8 vs 18.9 at 32,
+ * 89.5 vs 26.5 at 128): it takes three launches, and every workgroup
+ * renormalises each fragment it loads.
+ * Arguments: x bf16 [m][k] raw (not normalised), 1 <= m <= 128 (else
+ *   FP4RL_ERR_SHAPE); norm_w fp32 [k], k <= 16384, k % 16 == 0; the weight
+ *   [n][k] (tiled codes, scales, tensor scale); A [r][k], B [n][r] bf16, both
+ *   NULL or both set; y bf16 [m][n]. Alignment as for fp4rl_aqn_gate_up_silu.
+ * Workspace: fp4rl_aqn_lora_linear_workspace(m, n, k, r) bytes, 256-byte
+ *   aligned, no initial contents needed (noise vector, r_m, K-slices of t). */
+size_t fp4rl_aqn_lora_linear_workspace(int64_t m, int64_t n, int64_t k, int64_t r);
+fp4rl_status fp4rl_aqn_lora_linear(const uint16_t* x, int64_t m, int64_t n, int64_t k, const float* norm_w,
+                                   float sigma, uint64_t seed, uint64_t step, uint32_t norm_id, float eps,
+                                   const uint8_t* codes, const uint8_t* scales, const float* tensor_scale,
+                                   const uint16_t* lora_a, const uint16_t* lora_b, int64_t r, float lora_scale,
+                                   uint16_t* y, void* workspace, size_t workspace_bytes, fp4rl_stream stream);
+
 /* ------------------------------------------------------------------------
  * FP8 rollout weights (gist.science summary of adaptive importance sampling
  * for quantized RL, "Problem definition" and "Experimental results": the

@@ -249,6 +249,37 @@ def test_aqn_gate_up_rejects_bad_arguments(lib):
     assert call(m=0) == OK
 
 
+def test_aqn_lora_linear_rejects_bad_arguments(lib):
+    f = lib.fp4rl_aqn_lora_linear
+    ws = lib.fp4rl_aqn_lora_linear_workspace(4, 8, 32, 8)
+    assert ws >= 32 * 4 + 4 * 4 + 4 * 8 * 4
+    assert lib.fp4rl_aqn_lora_linear_workspace(4, 8, 32768, 8) == 0  # wider than the norm
+    assert lib.fp4rl_aqn_lora_linear_workspace(129, 8, 32, 8) == 0   # more tokens than one launch takes
+    args = dict(x=FAKE, m=4, n=8, k=32, w=FAKE, sg=1e-2, seed=1, step=0, nid=0, eps=1e-6, c=FAKE, s=FAKE, t=FAKE,
+                a=FAKE, b=FAKE, r=8, ls=2.0, y=FAKE, ws=FAKE, wsb=ws)
+
+    def call(**kw):
+        a = dict(args, **kw)
+        return f(a["x"], a["m"], a["n"], a["k"], a["w"], a["sg"], a["seed"], a["step"], a["nid"], a["eps"], a["c"],
+                 a["s"], a["t"], a["a"], a["b"], a["r"], a["ls"], a["y"], a["ws"], a["wsb"], None)
+
+    assert call(m=129) == ERR_SHAPE
+    assert call(k=32768) == ERR_SHAPE
+    assert call(k=24) == ERR_SHAPE
+    assert call(r=257) == ERR_SHAPE
+    assert call(sg=-1.0) == ERR_VALUE
+    assert call(eps=float("nan")) == ERR_VALUE
+    assert call(ls=float("inf")) == ERR_VALUE
+    assert call(w=None) == ERR_NULL
+    assert call(b=None) == ERR_NULL
+    assert call(y=None) == ERR_NULL
+    assert call(w=MIS) == ERR_ALIGN
+    assert call(t=FAKE + 2) == ERR_ALIGN
+    assert call(wsb=ws - 1) == ERR_WORKSPACE
+    assert call(ws=None) == ERR_WORKSPACE
+    assert call(m=0) == OK and call(n=0) == OK
+
+
 def test_aqn_rejects_bad_arguments(lib):
     f = lib.fp4rl_aqn_rmsnorm
     assert f(FAKE, 4, 512, FAKE, -1.0, 0, 0, 0, 1e-6, FAKE, None, None) == ERR_VALUE
