@@ -73,14 +73,6 @@ __device__ __forceinline__ void scale4(uint32_t w, float (&sc)[4]) {
   sc[3] = __builtin_amdgcn_cvt_f32_fp8((int)w, 3);
 }
 
-// ---------------------------------------------------------------------------
-// LoRA down-projection, split along K into `gridDim.z` slices of `kslice`:
-//   part[z][m][j] = s * sum_{k in slice z} x[m][k] A[j][k].
-// One workgroup per 16x16 tile of t and K slice; its waves take the 32-wide
-// steps of the slice round-robin, U steps' loads at a time, and reduce
-// through LDS. With one slice, `part` is t itself; otherwise the slices are
-// summed in slice order by lora_reduce_kernel or by the linear's epilogue.
-// ---------------------------------------------------------------------------
 // One 16x16 tile of t (tokens m0.., ranks j0..) for K slice z, by WAVES
 // waves; red: WAVES x 64 f32x4 of LDS. COHERENT stores are agent-scope
 // atomics, for readers in the same launch on another XCD.
