@@ -38,6 +38,15 @@ constexpr int64_t kMaxDim = (int64_t)1 << 31;  // kernels index rows and columns
 // consumers' poll limit and whether producers leave the ready flags down.
 std::atomic<uint32_t> g_lora_spin{fp4rl::LoraFuse{}.spin};
 std::atomic<uint32_t> g_lora_withhold{0u};
+// Ready value of the next fused call's LoRA hand-off: unique per call in the
+// process (any workspace, device or thread), never 0 (the value of a cleared
+// workspace), so a flag raised late by an earlier call never matches.
+static std::atomic<uint32_t> g_lora_epoch{0};
+static uint32_t next_lora_epoch() {
+  uint32_t e = g_lora_epoch.fetch_add(1, std::memory_order_relaxed) + 1;
+  while (e == 0) e = g_lora_epoch.fetch_add(1, std::memory_order_relaxed) + 1;
+  return e;
+}
 constexpr int kMaxDevices = 64;
 std::atomic<int> g_dev_state[kMaxDevices];  // 0 unknown, 1 gfx950, 2 other arch
 
@@ -383,6 +392,7 @@ static fp4rl_status run_lora_linear(const uint16_t* x, int64_t m, int64_t n, int
       lf.err = reinterpret_cast<uint32_t*>(ws) + fp4rl::kLinearErrOffset;
       lf.spin = g_lora_spin.load(std::memory_order_relaxed);
       lf.withhold = g_lora_withhold.load(std::memory_order_relaxed);
+      lf.epoch = next_lora_epoch();
     } else {
       fp4rl_status s =
           launched(fp4rl::launch_lora_down(x, m, k, lora_a, r, lora_scale, splits, t, stream), "lora_down");

@@ -88,10 +88,12 @@ struct LoraFuse {
   float* part = nullptr;        // t slices [slices][M][r]; t itself ends up in slice 0
   uint32_t* tctr = nullptr;     // per-tile slice counters (mtiles * rtiles <= kLoraTileCounters)
   uint32_t* done = nullptr;     // finished tiles of t
-  uint32_t* lines = nullptr;    // kLoraGroups lines of kLoraLineWords words: ready flag, consumer count
+  uint32_t* lines = nullptr;    // kLoraGroups lines of kLoraLineWords words, word 0 the ready flag
   uint32_t* err = nullptr;      // the workspace's sticky error word
   uint32_t spin = 1u << 22;     // polls (each after a short sleep) before a consumer gives up
   uint32_t withhold = 0;        // test hook: the producers leave the ready flags down
+  uint32_t epoch = 1;           // this call's ready value (never 0, new for every call): a flag left raised by
+                                // an earlier call never satisfies this one
 };
 
 // whether the main kernel chosen for this shape runs fused LoRA producers

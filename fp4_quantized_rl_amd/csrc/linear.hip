@@ -190,18 +190,21 @@ __device__ __forceinline__ void lora_produce(const LoraFuse& L, int pid, const u
   if (*flag != 0u) {
     if (threadIdx.x == 0) __hip_atomic_store(L.done, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     if ((int)threadIdx.x < L.groups && L.withhold == 0u)
-      __hip_atomic_store(L.lines + kLoraLineWords * threadIdx.x, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      __hip_atomic_store(L.lines + kLoraLineWords * threadIdx.x, L.epoch, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   }
 }
 
 // Consumers' side, for the workgroup that writes output tile `tile` of y
 // (thread 0 does the memory accesses). It reads its group's ready flag early
 // (lora_poll), so the latency overlaps other work; lora_wait then returns at
-// once if it was set, else polls (bounded: a producer that never raises the
-// flag leaves the error bit in the workspace, never a hang). Right after its
-// wait the consumer counts itself on its group's line
+// once if it holds this call's epoch, else polls (bounded: a producer that
+// never raises the flag leaves the error bit in the workspace, never a
+// hang). Right after its wait the consumer counts itself on its group's line
 // (lora_release) and, once its epilogue is issued, the group's last consumer
-// clears the line (lora_reset_if_last).
+// clears the line (lora_reset_if_last), so every launch (a graph replay too)
+// starts from cleared flags. The epoch covers what clearing cannot: when all
+// of a group's consumers gave up, a flag its producer raises afterwards holds
+// that call's epoch and never releases a later call early.
 __device__ __forceinline__ uint32_t* lora_line(const LoraFuse& L, int tile) {
   return L.lines + kLoraLineWords * (tile % L.groups);
 }
@@ -215,11 +218,11 @@ __device__ __forceinline__ uint32_t lora_poll(const LoraFuse& L, int tile) {
 __device__ __forceinline__ void lora_wait(const LoraFuse& L, int tile, uint32_t seen) {
   if (L.producers > 0 && threadIdx.x == 0) {
     const uint32_t* f = lora_line(L, tile);
-    for (uint32_t it = 0; seen == 0u && it < L.spin; ++it) {
+    for (uint32_t it = 0; seen != L.epoch && it < L.spin; ++it) {
       __builtin_amdgcn_s_sleep(8);
       seen = __hip_atomic_load(f, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     }
-    if (seen == 0u)
+    if (seen != L.epoch)
       __hip_atomic_fetch_or(L.err, kLinearErrLoraWait, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   }
   __syncthreads();

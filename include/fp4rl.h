@@ -189,8 +189,13 @@ fp4rl_status fp4rl_fp4_lora_linear(const uint16_t* x, int64_t m, int64_t n, int6
  * launch's own producer workgroups to finish t; the wait is bounded (about
  * 2^22 polls), so a producer that never finishes cannot hang the GPU. A
  * consumer that gives up sets an error bit in the workspace's counter words
- * and computes with whatever t holds. The bit stays set: every later call on
- * that workspace is suspect until the counter words are cleared.
+ * and computes with whatever t holds; that call's output is wrong. Later
+ * calls are not affected: each fused call raises its ready flags to a value
+ * of its own (a process-wide call counter, never 0), so a flag that an
+ * earlier call's producer raised after its consumers had given up never
+ * releases a later call's consumers. The bit stays set until the counter
+ * words are cleared, so a check reports a timeout of any call since the
+ * last reset.
  * fp4rl_linear_workspace_check: synchronises `stream`, then reads the bit;
  *   FP4RL_OK, or FP4RL_ERR_TIMEOUT (detail in fp4rl_last_error()).
  *   workspace == NULL or workspace_bytes == 0: FP4RL_OK (no hand-off).

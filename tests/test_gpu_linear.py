@@ -208,6 +208,34 @@ def test_lora_handoff_timeout_is_reported(m):
     assert not bool(ws[:COUNTER_BYTES].any()), "counter words not back at zero"
 
 
+@pytest.mark.parametrize("m", [1, 8, 40])
+def test_late_ready_flag_does_not_release_next_call(m):
+    """Consumers made to give up after one poll while the producers still raise their ready flags, so a flag
+    can go up after every consumer of its group has finished and cleared it. The next call on that workspace,
+    made without a reset and on other tokens, still waits for its own producers (each call raises a ready
+    value of its own) and matches the oracle; after a reset the counter words are back at zero."""
+    dev = device()
+    n, k, r = 300, 1040, 16
+    w, x, a, b = _case(m, n, k, r, seed=5151 + m)
+    x2 = activations_bf16(m, k, 5152 + m)
+    q = nvfp4.quantize(w)
+    wq, at, bt = nvfp4_to_dev(*q, dev), bf16_to_dev(a, dev), bf16_to_dev(b, dev)
+    ws = fr.linear_workspace(fr.fp4_lora_linear_workspace_bytes(m, n, k, r), dev)
+    say(f"linear late ready flag m={m} ({fr.fp4_linear_kernel_name(m, n, k, r)})")
+    try:
+        fr.debug_lora_handoff(1, False)
+        fr.fp4_lora_linear(bf16_to_dev(x, dev), wq, at, bt, LORA_SCALE, workspace=ws)
+        torch.cuda.synchronize()
+    finally:
+        fr.debug_lora_handoff(0, False)
+    y = fr.fp4_lora_linear(bf16_to_dev(x2, dev), wq, at, bt, LORA_SCALE, workspace=ws)
+    torch.cuda.synchronize()
+    _check_lin(bf16_from_dev(y), x2, q, a, b, LORA_SCALE, f"{m}x{n}x{k} r{r} after a late flag")
+    fr.linear_workspace_reset(ws)
+    fr.linear_workspace_check(ws)
+    assert not bool(ws[:COUNTER_BYTES].any()), "counter words not back at zero"
+
+
 PREFILL = [  # (m, n, k, r): more than 128 tokens (256-feature x 128-token workgroup tiles), ragged in every dim
     (129, 16, 128, 0), (200, 270, 400, 8), (384, 512, 1024, 16), (1000, 520, 2064, 32), (2048, 300, 4096, 64),
 ]
