@@ -1112,35 +1112,42 @@ __global__ __launch_bounds__(WR * WT * kWave) void mid_kernel(
 
 // ---------------------------------------------------------------------------
 // Prefill GEMM (M > 128 tokens): a workgroup computes 256 output features x
-// 128 tokens over all of K with (256 / 16 TM) x (8 / TN) waves; each owns TM
-// row tiles (16 TM features) against TN of the 8 token tiles, so one
-// dequantised weight fragment feeds TN MFMAs and one activation fragment TM.
-// The LDS reads per MFMA fall with TM, the dequantisation per MFMA with TN.
-//   Activation chunks (128 tokens x 128 k, 32 KB) are loaded by all threads
-//   with consecutive threads on consecutive 16-byte pieces of a token row,
-//   held one chunk ahead in registers and written to one of two LDS slabs
-//   (rows padded to 272 B), from which every wave reads its B operands in
-//   the MFMA layout. Weights go to registers two chunks ahead. One barrier
-//   per chunk.
+// 128 tokens over all of K with four waves; wave w owns features 64 w .. +63
+// (two 32-row tiles, the 32x32x16 MFMA with dequantised weights as A) against
+// all four 32-token groups, so each dequantised fragment feeds four MFMAs.
+//   Activations go from HBM straight into LDS (buffer loads with an LDS
+//   destination: no staging registers, no LDS store instructions), in the
+//   MFMA operand order: one 1 KB fragment per (token group, 16-k step), lane
+//   l's 16 bytes at 16 l, so every operand read is one conflict-free
+//   contiguous 1 KB. Two slabs of 32 fragments (64 KB): chunk q + 1 loads
+//   into one while chunk q is read from the other; one barrier per chunk.
+//   Weights go to registers one chunk ahead.
+//   With 64 KB of LDS and at most 256 registers per lane, two workgroups
+//   share a CU (two waves per SIMD, one from each): the barrier and load
+//   waits of one overlap the MFMAs of the other.
+//   Within a chunk the fragments of the next 16-k step (four LDS reads, two
+//   dequantisations) are prepared while the current step's eight MFMAs run.
 //   Grid order is XCD-aware: the 8 XCDs take workgroups in turn, and each
 //   XCD works through super-tiles of 8 row groups x 4 token groups, so the
 //   workgroups that run together on one XCD share their weights and
 //   activations in its L2.
 // ---------------------------------------------------------------------------
 constexpr int kPfRows = 256, kPfTok = 128;
+typedef __attribute__((address_space(3))) void* lds_ptr;
 
-template <int TM, int TN = 8>
-__global__ __launch_bounds__(kPfRows / 16 / TM * (8 / TN) * kWave) void prefill_kernel(
+template <int D>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) void prefill_kernel(
     const uint16_t* __restrict__ x, int M, int N, int K, const uint8_t* __restrict__ codes,
     const uint8_t* __restrict__ scales, const float* __restrict__ tensor_scale, const float* __restrict__ t, int tks,
     const uint16_t* __restrict__ lb, int r, uint16_t* __restrict__ y) {
-  constexpr int FG = kPfRows / 16 / TM, W = FG * (8 / TN), D = 2;  // FG feature groups of waves
-  constexpr int NTH = W * kWave;
-  constexpr int XPT = kPfTok * 16 / NTH;  // 16-byte activation pieces per thread and chunk (8)
-  __shared__ __align__(16) uint16_t xs[2][kPfTok * kXRow];
+  constexpr int RW = 2, TG = 4, WAVES = 4;
+  static_assert(32 * RW * WAVES == kPfRows && 32 * TG == kPfTok, "tile shape");
+  constexpr int NFRAG = TG * 8;       // 1 KB activation fragments per chunk: (g, j, q)
+  constexpr int FPW = NFRAG / WAVES;  // fragments loaded per wave
+  __shared__ __align__(1024) uint8_t xs[2][NFRAG * 1024];
   const int lane = threadIdx.x & (kWave - 1);
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
-  const int li = lane & 15, lg = lane >> 4;
+  const int lr = lane & 31, lh = lane >> 5;
   const int RT = (N + 15) >> 4, KC = (K + 127) >> 7;
   const int GR = (N + kPfRows - 1) / kPfRows, GT = (M + kPfTok - 1) / kPfTok;
   // workgroup -> (row group, token group): XCD = L % 8; slot j = L / 8 of that
@@ -1152,197 +1159,200 @@ __global__ __launch_bounds__(kPfRows / 16 / TM * (8 / TN) * kWave) void prefill_
   const int sr = s / nstt, stt = s - sr * nstt;
   const int rg = 8 * sr + (within & 7), tg = 4 * stt + (within >> 3);
   if (rg >= GR || tg >= GT) return;
-  const int fw = wave % FG, tw = wave / FG;  // this wave's feature group and token-tile group
-  const int rt0 = rg * (kPfRows / 16) + fw * TM, n0 = 16 * rt0, m0 = tg * kPfTok;
-  const int tt0 = tw * TN;  // first token tile of this wave
+  const int m0 = tg * kPfTok;
+  const int nw = rg * kPfRows + 32 * RW * wave;  // this wave's features nw + 32 i + 0 .. 31
 
-  const uint8_t* cbase = codes + (int64_t)rt0 * KC * 1024;  // uniform per wave
-  const uint8_t* sbase = scales + (int64_t)rt0 * KC * 128;
-  const uint32_t clane = 16 * lane, slane = 4 * (16 * (lg >> 1) + li);
-  int toff[TM];  // row tiles past the matrix are clamped to the last (never stored)
+  // weights: lane (lr, lh) takes row nw + 32 i + lr (rows past N clamped to
+  // the last tile: computed, never stored); in chunk step (j, q) its word j
+  // of c_q holds k = 32 j + 16 lh + 8 q .. + 7, block 2 j + lh of its scales
+  const uint8_t* cl[RW];
+  const uint8_t* sl[RW];
 #pragma unroll
-  for (int i = 0; i < TM; ++i) toff[i] = (min(rt0 + i, RT - 1) - rt0) * KC;
-  // activation piece q of this thread: token row (threadIdx.x >> 4) + XR q
-  // (XR = threads / 16), 16 bytes at 16 (threadIdx.x & 15) of the chunk;
-  // tokens past M are clamped to the last one (never stored). Full token
-  // groups use a constant stride.
-  constexpr int XR = NTH / 16;
-  static_assert(XPT * XR == kPfTok, "the pieces of a chunk cover its token rows");
-  // Offsets are bytes from this token group's first row, through a buffer
-  // descriptor (32-bit offsets: the host keeps 256 K below 2^31); a piece
-  // past K gets an offset with bit 31 set and reads as zero.
-  const int xrow0 = threadIdx.x >> 4, xpc = threadIdx.x & 15;
-  const bool xfull = m0 + kPfTok <= M;
-  const uint32_t xoff0 = 2u * ((uint32_t)xrow0 * (uint32_t)K + 8 * xpc);
-  const uint32_t xstride = 2u * XR * (uint32_t)K;  // XR token rows
-  auto xoff = [&](int q) -> uint32_t {
-    return xfull ? xoff0 + (uint32_t)q * xstride
-                 : 2u * ((uint32_t)(min(m0 + xrow0 + XR * q, M - 1) - m0) * (uint32_t)K + 8 * xpc);
+  for (int i = 0; i < RW; ++i) {
+    const int tile = min(((nw + 32 * i) >> 4) + (lr >> 4), RT - 1);
+    cl[i] = codes + (int64_t)tile * KC * 1024 + 16 * (32 * lh + (lr & 15));
+    sl[i] = scales + (int64_t)tile * KC * 128 + 64 * lh + 4 * (lr & 15);
+  }
+  struct WStage {
+    uint4 c0[RW], c1[RW];
+    uint32_t s[RW];
   };
+  // every load of the main loop is unconditional (chunks past the last are
+  // clamped to it: loaded, never used), so the compiler counts the loads in
+  // flight and waits only for the ones a step uses
+  auto load_w = [&](int q, WStage& S) {
+    const int64_t c = min(q, KC - 1);
+#pragma unroll
+    for (int i = 0; i < RW; ++i) {
+      // plain (cached) loads: the other token groups of the super-tile reuse these tiles from L2
+      S.c0[i] = ld16(cl[i] + c * 1024);
+      S.c1[i] = ld16(cl[i] + c * 1024 + 256);
+      S.s[i] = *reinterpret_cast<const uint32_t*>(sl[i] + c * 128);
+    }
+  };
+  // Activation fragment f = 8 g + 2 j + q of a chunk: lane l holds token
+  // m0 + 32 g + (l % 32), k = 32 j + 16 (l / 32) + 8 q .. + 7 of the chunk.
+  // Offsets are bytes from this token group's first row, through a buffer
+  // descriptor (32-bit offsets: the host keeps 256 K below 2^31); a piece past
+  // K gets an offset with bit 31 set and reads as zero (K % 16 == 0: a piece
+  // is all in or out); tokens past M are clamped to the last one (never stored).
   const __amdgpu_buffer_rsrc_t xrs = __builtin_amdgcn_make_buffer_rsrc(
       const_cast<uint16_t*>(x + (int64_t)m0 * K), 0, (int)(2u * (uint32_t)min(kPfTok, M - m0) * (uint32_t)K),
       kBufferWord3);
-  const uint32_t xlds0 = xrow0 * kXRow + 8 * xpc;  // bf16 units; piece q adds XR q rows
-
-  struct WStage {
-    uint32_t cw[TM][4];
-    uint32_t sw[TM];
-  };
-  // Every load of the main loop is issued unconditionally (chunks past the
-  // last are clamped to it: loaded, never used), so the compiler can count
-  // the loads in flight and wait for exactly the ones a step uses; skipped
-  // or per-lane loads make it wait for all of them, which drains the
-  // prefetch every chunk.
-  auto load_w = [&](int c, WStage& S) {
+  uint32_t xoff[FPW];
+#pragma unroll
+  for (int u = 0; u < FPW; ++u) {
+    const int f = wave * FPW + u, g = f >> 3, jf = (f >> 1) & 3, q = f & 1;
+    const int tok = min(m0 + 32 * g + lr, M - 1) - m0;
+    xoff[u] = 2u * ((uint32_t)tok * (uint32_t)K + (uint32_t)(32 * jf + 16 * lh + 8 * q));
+  }
+  auto load_x = [&](int c, int slab) {
     c = min(c, KC - 1);
 #pragma unroll
-    for (int i = 0; i < TM; ++i) {
-      // plain (cached) loads: the other token groups of the super-tile reuse these tiles from L2
-      const uint4 v = ld16(cbase + (int64_t)(toff[i] + c) * 1024 + clane);
-      S.cw[i][0] = v.x; S.cw[i][1] = v.y; S.cw[i][2] = v.z; S.cw[i][3] = v.w;
-      S.sw[i] = *reinterpret_cast<const uint32_t*>(sbase + (int64_t)(toff[i] + c) * 128 + slane);
-    }
-  };
-  struct XStage {
-    uint4 v[XPT];
-  };
-  auto load_x = [&](int c, XStage& X) {
-    c = min(c, KC - 1);
-    // pieces past K (K % 16 == 0: a piece is all in or out) read as zero
-    const uint32_t kout = 128 * c + 8 * xpc < K ? 0u : 0x80000000u;
-#pragma unroll
-    for (int q = 0; q < XPT; ++q)
-      X.v[q] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(xrs, (int)((xoff(q) + 256u * c) | kout), 0, 0));
-  };
-  auto store_x = [&](const XStage& X, uint16_t* slab) {
-#pragma unroll
-    for (int q = 0; q < XPT; ++q) *reinterpret_cast<uint4*>(slab + xlds0 + q * XR * kXRow) = X.v[q];
-  };
-
-  f32x4 acc[TM][TN];
-#pragma unroll
-  for (int i = 0; i < TM; ++i)
-#pragma unroll
-    for (int jj = 0; jj < TN; ++jj) acc[i][jj] = f32x4{0.f, 0.f, 0.f, 0.f};
-
-  // Per 32-k step: 8 activation fragments from LDS, 32 MFMAs; the weight
-  // fragments of the next step are dequantised meanwhile (software
-  // pipelined), and the scheduler is asked to interleave one MFMA with two
-  // of those VALU instructions, so the dequantisation hides under the MFMAs.
-  auto compute = [&](const WStage& S, const uint16_t* slab) {
-    float sc[TM][4];
-#pragma unroll
-    for (int i = 0; i < TM; ++i) scale4(S.sw[i], sc[i]);
-    bf16x8 a[TM], an[TM];
-#pragma unroll
-    for (int i = 0; i < TM; ++i) a[i] = dequant8(S.cw[i][0], sc[i][0]);
-#pragma unroll
-    for (int st = 0; st < 4; ++st) {
-      bf16x8 b[TN];
-#pragma unroll
-      for (int jj = 0; jj < TN; ++jj)
-        b[jj] = as_bf16x8(*reinterpret_cast<const uint4*>(slab + (16 * (tt0 + jj) + li) * kXRow + 32 * st + 8 * lg));
-      if (st < 3) {
-#pragma unroll
-        for (int i = 0; i < TM; ++i) an[i] = dequant8(S.cw[i][st + 1], sc[i][st + 1]);
-      }
-#pragma unroll
-      for (int jj = 0; jj < TN; ++jj)
-#pragma unroll
-        for (int i = 0; i < TM; ++i) acc[i][jj] = mfma16x16x32(a[i], b[jj], acc[i][jj]);
-      constexpr int VPM = (TM * 17 + TM * TN - 1) / (TM * TN);  // VALU of the next step's dequantisation per MFMA
-#pragma unroll
-      for (int g = 0; g < TM * TN; ++g) {
-        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);    // one MFMA
-        __builtin_amdgcn_sched_group_barrier(0x002, VPM, 0);  // VPM VALU
-      }
-      if (st < 3) {
-#pragma unroll
-        for (int i = 0; i < TM; ++i) a[i] = an[i];
-      }
+    for (int u = 0; u < FPW; ++u) {
+      const int f = wave * FPW + u, jf = (f >> 1) & 3, q = f & 1;
+      const uint32_t past = 128 * c + 32 * jf + 16 * lh + 8 * q < K ? 0u : 0x80000000u;
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(xrs, (lds_ptr)(xs[slab] + f * 1024), 16,
+                                               (int)((xoff[u] + 256u * (uint32_t)c) | past), 0, 0, 0);
     }
   };
 
-  // chunk q is read from slab q % 2; after the barrier of iteration q the
-  // register stage holding chunk q + 1 goes to the other slab and is reloaded
-  // with chunk q + 3 (two iterations to arrive); weights of chunk q + D go
-  // into the stage chunk q used
+  f32x16 acc[RW][TG];
+#pragma unroll
+  for (int i = 0; i < RW; ++i)
+#pragma unroll
+    for (int g = 0; g < TG; ++g)
+#pragma unroll
+      for (int v = 0; v < 16; ++v) acc[i][g][v] = 0.0f;
+
+  // step st = 2 j + q of a chunk: weight word j of c_q, activation fragments (g, j, q)
+  auto read_b = [&](int slab, int st, bf16x8 (&bv)[TG]) {
+    const uint8_t* xb = xs[slab] + 16 * lane;
+#pragma unroll
+    for (int g = 0; g < TG; ++g) bv[g] = *reinterpret_cast<const bf16x8*>(xb + (8 * g + st) * 1024);
+  };
+  auto deq_a = [&](const WStage& S, const float (&sc)[RW][4], int st, bf16x8 (&av)[RW]) {
+    const int jj = st >> 1, q = st & 1;
+#pragma unroll
+    for (int i = 0; i < RW; ++i) {
+      const uint4& cw = q == 0 ? S.c0[i] : S.c1[i];
+      const uint32_t word = jj == 0 ? cw.x : jj == 1 ? cw.y : jj == 2 ? cw.z : cw.w;
+      av[i] = dequant8(word, sc[i][jj]);
+    }
+  };
+  auto compute = [&](int slab, const WStage& S) {
+    float sc[RW][4];
+#pragma unroll
+    for (int i = 0; i < RW; ++i) scale4(S.s[i], sc[i]);
+    bf16x8 av[2][RW], bv[2][TG];
+    read_b(slab, 0, bv[0]);
+    deq_a(S, sc, 0, av[0]);
+#pragma unroll
+    for (int st = 0; st < 8; ++st) {
+      const int cur = st & 1;
+      if (st < 7) {
+        read_b(slab, st + 1, bv[cur ^ 1]);
+        deq_a(S, sc, st + 1, av[cur ^ 1]);
+      }
+#pragma unroll
+      for (int i = 0; i < RW; ++i)
+#pragma unroll
+        for (int g = 0; g < TG; ++g) acc[i][g] = mfma32x32x16(av[cur][i], bv[cur][g], acc[i][g]);
+    }
+  };
+
+  // chunk q is read from slab q % 2; after the barrier of iteration q (this
+  // wave's loads of chunk q have landed, and every wave is done with chunk
+  // q - 1) chunk q + 1 is loaded into the other slab and the weights of
+  // chunk q + D - 1 into the stage chunk q - 1 used
+  static_assert(D >= 2 && D <= 3, "two or three weight stages");
   WStage ws[D];
-  XStage xr[2];
 #pragma unroll
-  for (int u = 0; u < D; ++u) load_w(u, ws[u]);
-  load_x(0, xr[0]);
-  load_x(1, xr[1]);
-  store_x(xr[0], xs[0]);
-  load_x(2, xr[0]);
-  for (int q0 = 0; q0 < KC; q0 += D) {
+  for (int u = 0; u < D - 1; ++u) load_w(u, ws[u]);
+  load_x(0, 0);
+  for (int q0 = 0; q0 < KC; q0 += 2 * D) {
 #pragma unroll
-    for (int u = 0; u < D; ++u) {
+    for (int u = 0; u < 2 * D; ++u) {
       const int q = q0 + u;
       if (q >= KC) break;  // uniform across the workgroup
-      __syncthreads();     // slab q % 2 is complete; slab (q + 1) % 2 is no longer read
-      // chunk q + 1 to the other slab (after the last chunk: a copy of it, never read)
-      store_x(xr[(u + 1) & 1], xs[(u + 1) & 1]);
-      load_x(q + 3, xr[(u + 1) & 1]);
-      compute(ws[u], xs[u & 1]);
-      load_w(q + D, ws[u]);
+      __syncthreads();
+      load_x(q + 1, (u + 1) & 1);
+      load_w(q + D - 1, ws[(u + D - 1) % D]);
+      compute(u & 1, ws[u % D]);
     }
   }
 
-  // Epilogue: acc *= s_t, then t B^T is accumulated onto it by MFMA, 32
-  // ranks at a time, from LDS: the workgroup stages its 128 t rows (K-slices
-  // summed in order, split into bf16 hi + lo) and its 256 B rows in the freed
-  // slabs (rows padded to 80 B: conflict-free 16-byte reads).
+  // Epilogue: acc *= s_t, then t B^T is accumulated onto it by MFMA, 16
+  // ranks per step (lane (lr, lh) takes ranks j0 + 8 lh .. + 7; t, its
+  // K-slices summed in order, split into bf16 hi + lo parts)
   const float st = *tensor_scale;
-  for_tiles<TM, TN>([&](auto I, auto J) { acc[I][J] *= st; });
+#pragma unroll
+  for (int i = 0; i < RW; ++i)
+#pragma unroll
+    for (int g = 0; g < TG; ++g) acc[i][g] *= st;
   if (r > 0) {
-    constexpr int LROW = 40;  // bf16 per staged row: 32 ranks + 8 of padding
-    uint16_t* bl = xs[0];                 // [256][LROW] B rows
-    uint16_t* th = bl + kPfRows * LROW;   // [128][LROW] t, high bf16 part
-    uint16_t* tlo = th + kPfTok * LROW;   // [128][LROW] t, low bf16 part
-    const int n0wg = rg * kPfRows;
     const int64_t tstride = (int64_t)M * r;
-    for (int j0 = 0; j0 < r; j0 += 32) {
-      __syncthreads();  // the slabs (or the previous piece) are no longer read
-      for (int e = threadIdx.x; e < kPfTok * 32; e += NTH) {  // t piece: 128 tokens x 32 ranks
-        const int tok = e >> 5, jj = e & 31, m = m0 + tok, j = j0 + jj;
-        float v = 0.0f;
-        if (m < M && j < r)
-          for (int q = 0; q < tks; ++q) v += t[q * tstride + (int64_t)m * r + j];
-        const uint32_t h = f32_to_bf16(v);
-        th[tok * LROW + jj] = (uint16_t)h;
-        tlo[tok * LROW + jj] = (uint16_t)f32_to_bf16(v - __uint_as_float(h << 16));
+    for (int j0 = 0; j0 < r; j0 += 16) {
+      const int jj = j0 + 8 * lh;
+      uint4 bw[RW];
+#pragma unroll
+      for (int i = 0; i < RW; ++i) {
+        const int na = min(nw + 32 * i + lr, N - 1);
+        bw[i] = make_uint4(0, 0, 0, 0);
+        if (jj < r) {
+          if ((r & 7) == 0) {
+            bw[i] = ld16(lb + (int64_t)na * r + jj);
+          } else {
+            uint32_t hv[8];
+#pragma unroll
+            for (int e = 0; e < 8; ++e) hv[e] = jj + e < r ? lb[(int64_t)na * r + jj + e] : 0u;
+            bw[i] = make_uint4(hv[0] | (hv[1] << 16), hv[2] | (hv[3] << 16), hv[4] | (hv[5] << 16), hv[6] | (hv[7] << 16));
+          }
+        }
       }
-      for (int e = threadIdx.x; e < kPfRows * 32; e += NTH) {  // B piece: 256 rows x 32 ranks
-        const int row = e >> 5, jj = e & 31, n = n0wg + row, j = j0 + jj;
-        bl[row * LROW + jj] = (n < N && j < r) ? lb[(int64_t)n * r + j] : (uint16_t)0;
+#pragma unroll
+      for (int g = 0; g < TG; ++g) {
+        const float* tp = t + (int64_t)min(m0 + 32 * g + lr, M - 1) * r + jj;
+        float tv[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+        for (int z = 0; z < tks; ++z) {
+#pragma unroll
+          for (int e = 0; e < 8; ++e)
+            if (jj + e < r) tv[e] += tp[(int64_t)z * tstride + e];
+        }
+        uint4 th, tl;
+        split_bf16x8(tv, th, tl);
+#pragma unroll
+        for (int i = 0; i < RW; ++i) {
+          acc[i][g] = mfma32x32x16(as_bf16x8(bw[i]), as_bf16x8(th), acc[i][g]);
+          acc[i][g] = mfma32x32x16(as_bf16x8(bw[i]), as_bf16x8(tl), acc[i][g]);
+        }
       }
-      __syncthreads();
-      for_tiles<TM, TN>([&](auto I, auto J) {
-        const bf16x8 a = as_bf16x8(*reinterpret_cast<const uint4*>(bl + (fw * 16 * TM + 16 * I + li) * LROW + 8 * lg));
-        const bf16x8 bh = as_bf16x8(*reinterpret_cast<const uint4*>(th + (16 * (tt0 + J) + li) * LROW + 8 * lg));
-        const bf16x8 bo = as_bf16x8(*reinterpret_cast<const uint4*>(tlo + (16 * (tt0 + J) + li) * LROW + 8 * lg));
-        acc[I][J] = mfma16x16x32(a, bh, acc[I][J]);
-        acc[I][J] = mfma16x16x32(a, bo, acc[I][J]);
-      });
     }
   }
-  // lane holds features n0 + 16 I + 4 lg + v of token m0 + 16 (tt0 + J) + li
+  // lane holds token m0 + 32 g + lr, features nw + 32 i + 8 b + 4 lh + e (register 4 b + e)
   const bool nvec = (N & 3) == 0;
-  for_tiles<TM, TN>([&](auto I, auto J) {
-    const int m = m0 + 16 * (tt0 + J) + li, nf = n0 + 16 * I + 4 * lg;
-    if (m < M) {
-      uint16_t* yp = y + (int64_t)m * N + nf;
-      const f32x4 v = acc[I][J];
-      if (nvec && nf + 3 < N) {
-        *reinterpret_cast<uint2*>(yp) = make_uint2(pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3]));
-      } else {
 #pragma unroll
-        for (int e = 0; e < 4; ++e)
-          if (nf + e < N) yp[e] = (uint16_t)f32_to_bf16(v[e]);
+  for (int i = 0; i < RW; ++i)
+#pragma unroll
+    for (int g = 0; g < TG; ++g) {
+      const int m = m0 + 32 * g + lr;
+      if (m >= M) continue;
+#pragma unroll
+      for (int bq = 0; bq < 4; ++bq) {
+        const int nf = nw + 32 * i + 8 * bq + 4 * lh;
+        uint16_t* yp = y + (int64_t)m * N + nf;
+        const f32x16& v = acc[i][g];
+        const uint32_t o01 = pack_bf16x2(v[4 * bq], v[4 * bq + 1]), o23 = pack_bf16x2(v[4 * bq + 2], v[4 * bq + 3]);
+        if (nvec && nf + 3 < N) {
+          *reinterpret_cast<uint2*>(yp) = make_uint2(o01, o23);
+        } else {
+          const uint32_t o[4] = {o01 & 0xFFFFu, o01 >> 16, o23 & 0xFFFFu, o23 >> 16};
+#pragma unroll
+          for (int e = 0; e < 4; ++e)
+            if (nf + e < N) yp[e] = (uint16_t)o[e];
+        }
       }
     }
-  });
 }
 
 // ---------------------------------------------------------------------------
@@ -1837,9 +1847,7 @@ hipError_t launch_fp4_linear(const uint16_t* x, int64_t m, int64_t n, int64_t k,
     const int64_t gr = (n + kPfRows - 1) / kPfRows, gt = (m + kPfTok - 1) / kPfTok;
     const int64_t supers = (gr + 7) / 8 * ((gt + 3) / 4);  // super-tiles of 8 x 4 workgroups, dealt to 8 XCDs
     const int64_t grid = 8 * 32 * ((supers + 7) / 8);
-    // 8 waves of 32 features x 128 tokens: two waves per SIMD hide each
-    // other's LDS, barrier and load waits
-    hipLaunchKernelGGL(prefill_kernel<2>, dim3((unsigned)grid), dim3(512), 0, stream, x, M, N, K, codes, scales,
+    hipLaunchKernelGGL(prefill_kernel<2>, dim3((unsigned)grid), dim3(256), 0, stream, x, M, N, K, codes, scales,
                        tensor_scale, t, tks, b, R, y);
     return hipGetLastError();
   }
