@@ -124,6 +124,78 @@ __device__ __forceinline__ void lora_tile(const uint16_t* __restrict__ x, int M,
   }
 }
 
+// All RTN 16-rank tiles of t for TT 16-token tiles (m0..) and K slice z, by
+// WAVES waves taking the 32-wide steps round-robin: each activation fragment
+// is loaded once and feeds RTN MFMAs, each adapter fragment TT (ranks past r
+// and tokens past M clamped, never stored); red: WAVES x TT x RTN x 64 f32x4
+// of LDS, reduced in wave order.
+template <int WAVES, int TT, int RTN, int U>
+__device__ __forceinline__ void lora_rows(const uint16_t* __restrict__ x, int M, int K, const uint16_t* __restrict__ a,
+                                          int r, float s, int kslice, int m0, int z, f32x4* red,
+                                          float* __restrict__ part) {
+  const int lane = threadIdx.x & (kWave - 1), wave = threadIdx.x / kWave;
+  const int li = lane & 15, lg = lane >> 4;
+  const uint16_t* xr[TT];
+#pragma unroll
+  for (int u = 0; u < TT; ++u) xr[u] = x + (int64_t)min(m0 + 16 * u + li, M - 1) * K;
+  const uint16_t* ar[RTN];
+#pragma unroll
+  for (int t = 0; t < RTN; ++t) ar[t] = a + (int64_t)min(16 * t + li, r - 1) * K;
+  const int kbeg = z * kslice;
+  const int kend = min(K, kbeg + kslice);
+  const int nsteps = (kend - kbeg + 31) / 32;
+  const int mine = nsteps > wave ? (nsteps - wave + WAVES - 1) / WAVES : 0;
+  f32x4 acc[TT][RTN];
+#pragma unroll
+  for (int u = 0; u < TT; ++u)
+#pragma unroll
+    for (int t = 0; t < RTN; ++t) acc[u][t] = f32x4{0.f, 0.f, 0.f, 0.f};
+  for (int g0 = 0; g0 < mine; g0 += U) {
+    uint4 xv[U][TT], av[U][RTN];
+#pragma unroll
+    for (int q = 0; q < U; ++q) {
+      const int k0 = kbeg + 32 * (wave + WAVES * (g0 + q)) + 8 * lg;
+      const bool kv = (g0 + q < mine) && k0 < kend;
+#pragma unroll
+      for (int u = 0; u < TT; ++u) xv[q][u] = kv ? ld16(xr[u] + k0) : make_uint4(0, 0, 0, 0);
+#pragma unroll
+      for (int t = 0; t < RTN; ++t) av[q][t] = kv ? ld16(ar[t] + k0) : make_uint4(0, 0, 0, 0);
+    }
+#pragma unroll
+    for (int q = 0; q < U; ++q)
+#pragma unroll
+      for (int u = 0; u < TT; ++u)
+#pragma unroll
+        for (int t = 0; t < RTN; ++t) acc[u][t] = mfma16x16x32(as_bf16x8(xv[q][u]), as_bf16x8(av[q][t]), acc[u][t]);
+  }
+#pragma unroll
+  for (int u = 0; u < TT; ++u)
+#pragma unroll
+    for (int t = 0; t < RTN; ++t) red[((wave * TT + u) * RTN + t) * kWave + lane] = acc[u][t];
+  __syncthreads();
+  float* dst = part + (int64_t)z * M * r;
+  for (int e = wave; e < TT * RTN; e += WAVES) {
+    const int u = e / RTN, t = e - u * RTN;
+    f32x4 sum = red[e * kWave + lane];
+#pragma unroll
+    for (int w = 1; w < WAVES; ++w) sum += red[(w * TT * RTN + e) * kWave + lane];
+    // lane holds rows 4*lg + v (tokens), column li (rank index)
+#pragma unroll
+    for (int v = 0; v < 4; ++v) {
+      const int mm = m0 + 16 * u + 4 * lg + v, jj = 16 * t + li;
+      if (mm < M && jj < r) dst[(int64_t)mm * r + jj] = s * sum[v];
+    }
+  }
+}
+
+template <int WAVES, int TT, int RTN, int U>
+__global__ __launch_bounds__(WAVES * kWave) void lora_down_rows_kernel(const uint16_t* __restrict__ x, int M, int K,
+                                                                        const uint16_t* __restrict__ a, int r, float s,
+                                                                        int kslice, float* __restrict__ part) {
+  __shared__ f32x4 red[WAVES * TT * RTN * kWave];
+  lora_rows<WAVES, TT, RTN, U>(x, M, K, a, r, s, kslice, blockIdx.x * 16 * TT, blockIdx.z, red, part);
+}
+
 // ---------------------------------------------------------------------------
 // LoRA down-projection, split along K into `gridDim.z` slices of `kslice`:
 //   part[z][m][j] = s * sum_{k in slice z} x[m][k] A[j][k].
@@ -1607,6 +1679,27 @@ hipError_t launch_lora_down(const uint16_t* x, int64_t m, int64_t k, const uint1
                             int splits, float* part, hipStream_t stream) {
   const int64_t ks = slice_len(k, splits);
   const dim3 grid((unsigned)((m + 15) / 16), (unsigned)((r + 15) / 16), (unsigned)((k + ks - 1) / ks));
+  if (use_prefill(m) && r <= 128) {
+    // many token tiles: a workgroup takes 32 tokens and computes every rank
+    // tile, so each activation row is read once and each adapter fragment
+    // feeds two token tiles (the adapter rows are re-read from L2 once per
+    // 32 tokens); 8 waves with several steps of loads each in flight
+    const dim3 g2((unsigned)((m + 31) / 32), 1, grid.z);
+    const int rtn = (int)((r + 15) / 16);
+#define FP4RL_ROWS(RTN_, U_)                                                                                     \
+  if (rtn <= RTN_) {                                                                                              \
+    hipLaunchKernelGGL((lora_down_rows_kernel<8, 2, RTN_, U_>), g2, dim3(8 * kWave), 0, stream, x, (int)m, (int)k, a, \
+                       (int)r, lora_scale, (int)ks, part);                                                        \
+    return hipGetLastError();                                                                                     \
+  }
+    FP4RL_ROWS(1, 8) FP4RL_ROWS(2, 4) FP4RL_ROWS(4, 2)
+#undef FP4RL_ROWS
+    if (rtn <= 8) {  // four waves: the reduction buffer stays at 64 KB
+      hipLaunchKernelGGL((lora_down_rows_kernel<4, 2, 8, 1>), g2, dim3(4 * kWave), 0, stream, x, (int)m, (int)k, a,
+                         (int)r, lora_scale, (int)ks, part);
+      return hipGetLastError();
+    }
+  }
   if ((m + 15) / 16 * ((r + 15) / 16) * grid.z <= 256)
     hipLaunchKernelGGL(lora_down_kernel<16>, grid, dim3(16 * kWave), 0, stream, x, (int)m, (int)k, a, (int)r,
                        lora_scale, (int)ks, part);

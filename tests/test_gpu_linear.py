@@ -308,10 +308,12 @@ def test_power_of_two_homogeneity_and_determinism():
     assert np.array_equal(_run(dev, x, q, a, b, LORA_SCALE), y1)
 
 
-@pytest.mark.parametrize("m", [40, 100])
-def test_halves_match_fused_call(m):
+@pytest.mark.parametrize("m,r", [(40, 32), (100, 32), (300, 32), (200, 100), (129, 3)])
+def test_halves_match_fused_call(m, r):
+    """The two halves (lora_down, then the linear with t) against the one-call form; above 128 tokens t comes
+    from the one-pass down-projection (every rank tile of 16 tokens per workgroup), ragged ranks included."""
     dev = device()
-    n, k, r = 300, 640, 32
+    n, k = 300, 640
     w, x, a, b = _case(m, n, k, r, seed=45)
     q = nvfp4.quantize(w)
     xt, wq = bf16_to_dev(x, dev), nvfp4_to_dev(*q, dev)
