@@ -44,15 +44,15 @@ const char* fp4_linear_kernel_name(int64_t m, int64_t n, int64_t k, int64_t r);
 // zero before the first call, and every launch leaves them at zero. The
 // other regions (t slices, K-split partials) follow and never overlap the
 // counters, whatever shapes share the workspace.
-constexpr int kSplitCounters = 256;      // words [0, 256): K-split tile counters
-constexpr int kLoraTileCounters = 128;   // words [256, 384): one per 16x16 tile of t (m <= 128, r <= 256)
-constexpr int kLoraTileCtrOffset = 256;
-constexpr int kLoraDoneOffset = 384;     // word 384: finished tiles of t
-constexpr int kLinearErrOffset = 388;    // word 388: sticky device-side error bits (kLinearErr*)
+constexpr int kSplitCounters = 1024;     // words [0, 1024): K-split tile counters
+constexpr int kLoraTileCounters = 128;   // words [1024, 1152): one per 16x16 tile of t (m <= 128, r <= 256)
+constexpr int kLoraTileCtrOffset = 1024;
+constexpr int kLoraDoneOffset = 1152;    // word 1152: finished tiles of t
+constexpr int kLinearErrOffset = 1156;   // word 1156: sticky device-side error bits (kLinearErr*)
 constexpr uint32_t kLinearErrLoraWait = 1u;  // a consumer gave up waiting for t (see LoraFuse::spin)
 constexpr int kLoraGroups = 64;          // ready flags: one 256-byte line per group of output tiles
 constexpr int kLoraLineWords = 64;
-constexpr int kLoraLineOffset = 512;     // line g: words 512 + 64 g (flag), + 1 (count)
+constexpr int kLoraLineOffset = 1280;    // line g: words 1280 + 64 g (flag), + 1 (count)
 constexpr int kLinearCounters = kLoraLineOffset + kLoraGroups * kLoraLineWords;
 constexpr size_t kLinearCounterBytes = kLinearCounters * sizeof(uint32_t);
 

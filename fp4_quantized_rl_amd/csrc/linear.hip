@@ -1822,6 +1822,12 @@ static SplitkCfg pick_splitk(int64_t m, int64_t n, int64_t k) {
   while ((int64_t)c.gx * c.gy * s < 256 && (kc + 2 * s - 1) / (2 * s) >= c.w &&
          4.0 * (double)(2 * s) * (double)m * (double)n * 2.0 <= wbytes / 3.0)
     s *= 2;
+  // Long K: split further until each wave has at most 24 chunks, within the
+  // same bound on the partials (measured: 32B down, 27648 k, at 128 tokens
+  // 108 -> 89 us with three ranges; 320 output tiles had left it unsplit)
+  while (s < 8 && (kc + (int64_t)s * c.w - 1) / ((int64_t)s * c.w) > 24 &&
+         4.0 * (double)(s + 1) * (double)m * (double)n * 2.0 <= wbytes / 3.0)
+    ++s;
   c.cpz = (int)((kc + s - 1) / s);
   c.s = (int)((kc + c.cpz - 1) / c.cpz);  // no empty K range
   if ((int64_t)c.gx * c.gy > kSplitCounters) c.s = 1, c.cpz = (int)kc;  // a split needs one counter per tile
@@ -1845,7 +1851,8 @@ template <int TN, int W, int D, int TM = 4>
 hipError_t run_splitk(const SplitkCfg& c, hipStream_t st, const uint16_t* x, int M, int N, int K, const uint8_t* codes,
                       const uint8_t* scales, const float* ts, const float* t, int tks, const uint16_t* b, int r,
                       uint16_t* y, float* part, uint32_t* counters, LoraFuse lf) {
-  // (a split has s * gx * gy < 512, so its partials stay below 4 MB)
+  // the partials are addressed with 32-bit byte offsets (at most 1024 tiles of
+  // 64 x 32 outputs are split, so they stay far below this bound)
   if (c.s > 1 && (int64_t)c.s * M * N * 4 > INT32_MAX) return hipErrorInvalidValue;
   const int main_grid = 8 * ((c.gx + 7) / 8) * c.gy * c.s;
   lf.consumers = c.gx * c.gy;  // one waiting workgroup per output tile (the last of its K split)

@@ -161,8 +161,8 @@ fp4rl_status fp4rl_nvfp4_quantize_record(const void* w, int32_t w_dtype, int64_t
  * main kernel are launched. The main kernel is chosen by m (see
  * fp4rl_fp4_linear_kernel_name).
  * Workspace: fp4rl_fp4_lora_linear_workspace(m, n, k, r) bytes (0 when
- * neither split below is used), 16-byte aligned. It starts with 4608
- * counter words (18 KB: K-split tile counters, then the hand-off words of the
+ * neither split below is used), 16-byte aligned. It starts with 5376
+ * counter words (21 KB: K-split tile counters, then the hand-off words of the
  * in-launch LoRA producers, spread over 64 lines of 256 bytes so that few
  * workgroups share an atomic address); then come the K-split partial sums of
  * t and, for shapes with
@@ -291,7 +291,7 @@ fp4rl_status fp4rl_fp4_lora_linear_backward(const uint16_t* dy, const uint16_t* 
  *   [n][k] each; adapters A [r][k], B [n][r] bf16, all four NULL or all
  *   set; h bf16 [m][n]. Shapes and alignment as for fp4rl_fp4_lora_linear.
  * Workspace: fp4rl_fp4_gate_up_silu_workspace(m, n, k, r) bytes, 256-byte
- *   aligned. It begins with 18 KB of counter words, as a linear workspace:
+ *   aligned. It begins with 21 KB of counter words, as a linear workspace:
  *   zero before the first call (e.g. a zero-filled workspace), left zero by
  *   every call. Up to 16 tokens the fp32 K-slices of t for both projections
  *   follow (0 bytes in all without adapters); from 17 tokens the rest of a

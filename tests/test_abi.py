@@ -330,7 +330,7 @@ def test_binding_fails_loudly_without_library(monkeypatch):
 
 def test_workspace_check_and_reset_validate_arguments(lib):
     """Argument checks of the hand-off health calls, all decided before any device access."""
-    counter_bytes = 4 * (512 + 64 * 64)
+    counter_bytes = 4 * (1280 + 64 * 64)
     assert lib.fp4rl_linear_workspace_check(None, 0, None) == OK          # no workspace: no hand-off
     assert lib.fp4rl_linear_workspace_reset(None, 0, None) == OK
     assert lib.fp4rl_linear_workspace_check(FAKE, counter_bytes - 4, None) == ERR_WORKSPACE

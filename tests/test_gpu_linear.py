@@ -139,9 +139,9 @@ def test_mid_kernel_configs(m, n, k, r):
     _check_lin(y, x, q, a, b, LORA_SCALE, f"{m}x{n}x{k} r{r}")
 
 
-# a linear workspace starts with 4608 counter words: K-split tile counters,
+# a linear workspace starts with 5376 counter words: 1024 K-split tile counters,
 # t tile counters, finished-tile count, 64 ready-flag lines of 256 bytes
-COUNTER_BYTES = 4 * (512 + 64 * 64)
+COUNTER_BYTES = 4 * (1280 + 64 * 64)
 
 FUSED = [  # (m, n, k, r): m <= 128 with r > 0 computes t inside the linear's launch, in K slices
     (1, 300, 4096, 32), (2, 100, 2048, 16), (1, 4608, 3584, 32), (8, 5000, 3584, 32), (13, 200, 1040, 7),
