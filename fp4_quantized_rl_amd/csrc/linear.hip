@@ -1119,14 +1119,26 @@ __global__ __launch_bounds__(WR * WT * kWave) void mid_kernel(
       for (int g = 0; g < TGW; ++g) {
         const int ma = min(mw + 32 * g + lr, M - 1);
         float tv[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+        if (coh && (r & 3) == 0) {  // 16-byte loads: (ma r + jj) is a multiple of 4
+          const int o = 4 * (ma * r + jj);
+          if (jj < r) {
+            const f32x4 v = ld_coherent16(trs, o);
+            tv[0] = v[0]; tv[1] = v[1]; tv[2] = v[2]; tv[3] = v[3];
+          }
+          if (jj + 4 < r) {
+            const f32x4 v = ld_coherent16(trs, o + 16);
+            tv[4] = v[0]; tv[5] = v[1]; tv[6] = v[2]; tv[7] = v[3];
+          }
+        } else {
 #pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          if (jj + e < r) {
-            const int64_t o = (int64_t)ma * r + jj + e;
-            if (coh) {
-              tv[e] = ld_coherent4(trs, (int)(4 * o));
-            } else {
-              for (int z = 0; z < tks; ++z) tv[e] += t[(int64_t)z * tstride + o];
+          for (int e = 0; e < 8; ++e) {
+            if (jj + e < r) {
+              const int64_t o = (int64_t)ma * r + jj + e;
+              if (coh) {
+                tv[e] = ld_coherent4(trs, (int)(4 * o));
+              } else {
+                for (int z = 0; z < tks; ++z) tv[e] += t[(int64_t)z * tstride + o];
+              }
             }
           }
         }
@@ -1387,9 +1399,21 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
         const float* tp = t + (int64_t)min(m0 + 32 * g + lr, M - 1) * r + jj;
         float tv[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
         for (int z = 0; z < tks; ++z) {
+          if ((r & 3) == 0) {  // 16-byte loads: (m r + jj) is a multiple of 4
+            const float* tz = tp + (int64_t)z * tstride;
+            if (jj < r) {
+              const f32x4 v = *reinterpret_cast<const f32x4*>(tz);
+              tv[0] += v[0]; tv[1] += v[1]; tv[2] += v[2]; tv[3] += v[3];
+            }
+            if (jj + 4 < r) {
+              const f32x4 v = *reinterpret_cast<const f32x4*>(tz + 4);
+              tv[4] += v[0]; tv[5] += v[1]; tv[6] += v[2]; tv[7] += v[3];
+            }
+          } else {
 #pragma unroll
-          for (int e = 0; e < 8; ++e)
-            if (jj + e < r) tv[e] += tp[(int64_t)z * tstride + e];
+            for (int e = 0; e < 8; ++e)
+              if (jj + e < r) tv[e] += tp[(int64_t)z * tstride + e];
+          }
         }
         uint4 th, tl;
         split_bf16x8(tv, th, tl);
@@ -1797,6 +1821,15 @@ static hipError_t launch_mid(hipStream_t st, const uint16_t* x, int M, int N, in
                              const uint8_t* scales, const float* ts, const float* t, int tks, const uint16_t* b, int r,
                              uint16_t* y, LoraFuse lf) {
   const int gx = (N + kMidRows - 1) / kMidRows;
+  if (lf.producers > 0 && lf.slices > 1) {
+    // one K slice per tile of t: each producer holds the kernel's LDS like a
+    // main workgroup, so a few long producers run beside the row groups
+    // instead of many short ones filling the chip before them (measured:
+    // 32B gate at 128 tokens, r = 64: 32 producers instead of 256)
+    lf.slices = 1;
+    lf.kslice = K;
+    lf.producers = (lf.mtiles * lf.rtiles + 7) / 8 * 8;
+  }
   lf.consumers = gx;  // one waiting workgroup per row group
   lf.groups = std::min(kLoraGroups, lf.consumers);
   const unsigned grid = (unsigned)(lf.producers + gx);
