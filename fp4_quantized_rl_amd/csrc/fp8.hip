@@ -17,11 +17,19 @@
 //     to bf16 exactly on the way into LDS (v_cvt_pk_f32_fp8), fp32
 //     accumulation scaled per row by s_n; the contraction is split over
 //     workgroups when there are few output tiles (decode), partials fp32.
+//   W8A16 decode, 17..64 tokens: the NVFP4 linear's split-K kernel in its
+//     E4M3 mode (activations staged through LDS); without a K split it
+//     stores y itself (row scales, t B^T by MFMA), else fp32 partials.
+//   W8A16 decode up to 16 tokens and W8A8 decode: fp8_decode_kernel /
+//     e4m3_decode_kernel, fp32 partials per K-slice.
 //   t = s x A^T in K-slices by the NVFP4 linear's LoRA down-projection
 //   kernel; the finishing kernels add the slices in order. With enough output tiles (prefill) the linear writes
 //   bf16 y in one launch, the LoRA term accumulated as a second contraction
 //   segment (t as bf16 hi | lo against B twice: lora_operands_kernel);
-//   split (decode), fp8_finish_kernel makes y = bf16(sum of slices + t . B[n]).
+//   split (decode), fp8_finish_kernel makes y = bf16(sum of slices + t . B[n]):
+//   a workgroup per 256 features x 2 tokens, t's K-slices summed once into
+//   LDS (it was once per output and rank: 38.5 -> 14.7 us for the 7B gate at
+//   64 tokens).
 // W8A8: the tokens are quantised like weight rows (one E4M3 scale per token,
 //   fp8_quantize_kernel into the workspace), the base product runs on the
 //   FP8 matrix cores with both operands as bytes (e4m3_decode_kernel,
@@ -98,44 +106,69 @@ __global__ __launch_bounds__(256) void fp8_quantize_kernel(const void* __restric
 }
 
 // y[m][n] = bf16(sum_s part[s][m][n] + sum_j t[m][j] B[n][j]), t the sum of
-// its K-slices tpart[q][m][j]; slices, K-slices and ranks in order
+// its K-slices tpart[q][m][j]; slices, K-slices and ranks in order. A
+// workgroup takes 256 features x kFinTok tokens: its tokens' t rows (K-slices
+// summed) are staged in LDS once, and each thread, one feature, reads its B
+// row 8 ranks at a time and accumulates the rank products of every token.
+constexpr int kFinTok = 2;
 __global__ __launch_bounds__(256) void fp8_finish_kernel(const float* __restrict__ part, int slices, int M, int N,
                                                          const float* __restrict__ tpart, int tsl,
                                                          const uint16_t* __restrict__ b, int r,
                                                          uint16_t* __restrict__ y) {
+  extern __shared__ float tsh[];  // [kFinTok][r]
   const int64_t count = (int64_t)M * N, tstride = (int64_t)M * r;
-  for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < count; i += (int64_t)gridDim.x * 256) {
-    float v = 0.0f;
-    for (int s = 0; s < slices; ++s) v += part[(int64_t)s * count + i];
-    if (r > 0) {
-      const int m = (int)(i / N), n = (int)(i - (int64_t)m * N);
-      const float* tm = tpart + (int64_t)m * r;
-      const uint16_t* bn = b + (int64_t)n * r;
-      float l = 0.0f;
-      int j = 0;
-      if ((r & 7) == 0)  // B and t rows 16-byte aligned: 8 ranks per step, same order
-        for (; j < r; j += 8) {
-          const uint4 bv = *reinterpret_cast<const uint4*>(bn + j);
-          float4 t0 = *reinterpret_cast<const float4*>(tm + j), t1 = *reinterpret_cast<const float4*>(tm + j + 4);
-          for (int q = 1; q < tsl; ++q) {
-            const float4 u0 = *reinterpret_cast<const float4*>(tm + q * tstride + j);
-            const float4 u1 = *reinterpret_cast<const float4*>(tm + q * tstride + j + 4);
-            t0.x += u0.x; t0.y += u0.y; t0.z += u0.z; t0.w += u0.w;
-            t1.x += u1.x; t1.y += u1.y; t1.z += u1.z; t1.w += u1.w;
-          }
-          l = fmaf(t0.x, bf16_lo(bv.x), l); l = fmaf(t0.y, bf16_hi(bv.x), l);
-          l = fmaf(t0.z, bf16_lo(bv.y), l); l = fmaf(t0.w, bf16_hi(bv.y), l);
-          l = fmaf(t1.x, bf16_lo(bv.z), l); l = fmaf(t1.y, bf16_hi(bv.z), l);
-          l = fmaf(t1.z, bf16_lo(bv.w), l); l = fmaf(t1.w, bf16_hi(bv.w), l);
-        }
-      for (; j < r; ++j) {
-        float tj = tm[j];
-        for (int q = 1; q < tsl; ++q) tj += tm[q * tstride + j];
-        l = fmaf(tj, bf16_lo(bn[j]), l);
-      }
-      v += l;
+  const int n = blockIdx.x * 256 + threadIdx.x;
+  const uint16_t* bn = b + (int64_t)min(n, N - 1) * r;
+  for (int m0 = blockIdx.y * kFinTok; m0 < M; m0 += gridDim.y * kFinTok) {  // uniform across the workgroup
+    const int mt = min(kFinTok, M - m0);
+    __syncthreads();  // the previous token block's t is no longer read
+    for (int e = threadIdx.x; e < mt * r; e += 256) {
+      const int mm = e / r, j = e - mm * r;
+      const float* tp = tpart + (int64_t)(m0 + mm) * r + j;
+      float tj = tp[0];
+      for (int q = 1; q < tsl; ++q) tj += tp[q * tstride];
+      tsh[mm * r + j] = tj;
     }
-    y[i] = (uint16_t)f32_to_bf16(v);
+    __syncthreads();
+    float l[kFinTok];
+#pragma unroll
+    for (int mm = 0; mm < kFinTok; ++mm) l[mm] = 0.0f;
+    for (int j0 = 0; j0 < r; j0 += 8) {
+      float bv[8];
+      if ((r & 7) == 0) {  // the B row is 16-byte aligned
+        const uint4 w = *reinterpret_cast<const uint4*>(bn + j0);
+        bv[0] = bf16_lo(w.x); bv[1] = bf16_hi(w.x); bv[2] = bf16_lo(w.y); bv[3] = bf16_hi(w.y);
+        bv[4] = bf16_lo(w.z); bv[5] = bf16_hi(w.z); bv[6] = bf16_lo(w.w); bv[7] = bf16_hi(w.w);
+      } else {
+#pragma unroll
+        for (int e = 0; e < 8; ++e) bv[e] = j0 + e < r ? bf16_lo(bn[j0 + e]) : 0.0f;
+      }
+      const int je = min(8, r - j0);
+#pragma unroll
+      for (int mm = 0; mm < kFinTok; ++mm)
+        if (mm < mt) {
+          if (je == 8) {
+            float tv[8];
+#pragma unroll
+            for (int e = 0; e < 8; ++e) tv[e] = tsh[mm * r + j0 + e];
+#pragma unroll
+            for (int e = 0; e < 8; ++e) l[mm] = fmaf(tv[e], bv[e], l[mm]);
+          } else {
+            for (int e = 0; e < je; ++e) l[mm] = fmaf(tsh[mm * r + j0 + e], bv[e], l[mm]);
+          }
+        }
+    }
+    if (n < N) {
+#pragma unroll
+      for (int mm = 0; mm < kFinTok; ++mm) {
+        if (mm < mt) {
+          const int64_t i = (int64_t)(m0 + mm) * N + n;
+          float v = 0.0f;
+          for (int s = 0; s < slices; ++s) v += part[(int64_t)s * count + i];
+          y[i] = (uint16_t)f32_to_bf16(v + l[mm]);
+        }
+      }
+    }
   }
 }
 
@@ -165,7 +198,7 @@ __global__ __launch_bounds__(256) void lora_operands_kernel(const float* __restr
 }
 
 // ---------------------------------------------------------------------------
-// Decode (M <= 64): a workgroup takes 64 weight rows (four 16-row MFMA
+// Decode (W8A16 up to 16 tokens): a workgroup takes 64 weight rows (four 16-row MFMA
 // tiles) and one K-slice; its four waves take the slice's 64-k chunks in
 // turn (adjacent chunks of the same rows at once), two chunks in flight per
 // wave. A lane loads 16 E4M3 bytes per weight tile and chunk straight into
@@ -368,6 +401,11 @@ unsigned flat_grid8(int64_t count) {
 
 size_t al256(size_t v) { return (v + 255) / 256 * 256; }
 
+dim3 finish_grid(int64_t m, int64_t n) {
+  return dim3((unsigned)((n + 255) / 256), (unsigned)std::min<int64_t>((m + kFinTok - 1) / kFinTok, 4096));
+}
+size_t finish_lds(int64_t r) { return (size_t)kFinTok * (size_t)r * sizeof(float); }
+
 }  // namespace
 
 hipError_t launch_fp8_quantize(const void* w, bool w_bf16, int64_t n, int64_t k, uint8_t* codes, float* scales,
@@ -398,7 +436,8 @@ size_t fp8_linear_workspace(int64_t m, int64_t n, int64_t k, int64_t r, bool a8,
   // decode (m <= 64) always writes partials; otherwise only a split contraction does
   const bool dec = m <= 64;
   const int chunk = a8 ? 128 : kGC;
-  const int sl = dec ? dec_split(m, n, k, chunk).slices : nt_slices(nt_tiles(m, n), k, chunk);
+  const int sl = dec ? (a8 || m <= 16 ? dec_split(m, n, k, chunk).slices : fp8_splitk_slices(m, n, k))
+                     : nt_slices(nt_tiles(m, n), k, chunk);
   const bool parts = dec || sl > 1;
   const int64_t rp = (r + 7) / 8 * 8;
   if (parts) v.ypart = take((size_t)sl * m * n * 4);
@@ -455,6 +494,16 @@ hipError_t launch_fp8_linear(const uint16_t* x, int64_t m, int64_t n, int64_t k,
     if (e != hipSuccess) return e;
   }
   const int chunk = a8 ? 128 : kGC;
+  if (m > 16 && m <= 64 && !a8) {  // W8A16 decode: the split-K kernel's E4M3 mode (+ the finishing launch for a K split)
+    const hipError_t e = launch_fp8_splitk(x, m, n, k, codes, scales, w.tpart, tsl, r > 0 ? b : nullptr, r, y,
+                                           w.ypart, st);
+    if (e != hipSuccess) return e;
+    const int sl = fp8_splitk_slices(m, n, k);
+    if (sl > 1)
+      hipLaunchKernelGGL(fp8_finish_kernel, finish_grid(m, n), dim3(256), finish_lds(r), st, w.ypart, sl, (int)m,
+                         (int)n, w.tpart, tsl, r > 0 ? b : nullptr, (int)r, y);
+    return hipGetLastError();
+  }
   if (m <= 64) {
     const DecSplit d = dec_split(m, n, k, chunk);
     const dim3 grid((unsigned)((n + kDecRows - 1) / kDecRows), (unsigned)d.slices);
@@ -464,8 +513,8 @@ hipError_t launch_fp8_linear(const uint16_t* x, int64_t m, int64_t n, int64_t k,
       launch_decode<2>(a8, grid, x, w, m, n, k, codes, scales, d.slice, st);
     else
       launch_decode<4>(a8, grid, x, w, m, n, k, codes, scales, d.slice, st);
-    hipLaunchKernelGGL(fp8_finish_kernel, dim3(flat_grid8(m * n)), dim3(256), 0, st, w.ypart, d.slices, (int)m, (int)n,
-                       w.tpart, tsl, r > 0 ? b : nullptr, (int)r, y);
+    hipLaunchKernelGGL(fp8_finish_kernel, finish_grid(m, n), dim3(256), finish_lds(r), st, w.ypart, d.slices, (int)m,
+                       (int)n, w.tpart, tsl, r > 0 ? b : nullptr, (int)r, y);
     return hipGetLastError();
   }
   const int64_t tiles = nt_tiles(m, n);
@@ -486,7 +535,7 @@ hipError_t launch_fp8_linear(const uint16_t* x, int64_t m, int64_t n, int64_t k,
   else
     launch_gemm<kNtR8>(sl > 1, tiles, sl, sw, lora, m, n, scales, y, w.ypart, st);
   if (sl > 1)
-    hipLaunchKernelGGL(fp8_finish_kernel, dim3(flat_grid8(m * n)), dim3(256), 0, st, w.ypart, sl, (int)m, (int)n,
+    hipLaunchKernelGGL(fp8_finish_kernel, finish_grid(m, n), dim3(256), finish_lds(r), st, w.ypart, sl, (int)m, (int)n,
                        w.tpart, tsl, r > 0 ? b : nullptr, (int)r, y);
   return hipGetLastError();
 }

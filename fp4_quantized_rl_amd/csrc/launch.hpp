@@ -33,6 +33,14 @@ hipError_t launch_philox_words(uint64_t seed, uint64_t step, uint32_t norm_id, i
 constexpr int64_t kMaxRank = 256;
 // K-split of the LoRA down-projection: `slices` partial sums [slices][m][r].
 int lora_splits(int64_t m, int64_t k, int64_t r);
+// FP8 (E4M3 row-major [n][k], fp32 row scales) decode main launch over
+// s = fp8_splitk_slices K ranges: with s == 1 it stores y = bf16(s_n sum +
+// t B^T) (t: tks K-slices [tks][m][r], or r == 0); otherwise fp32 partials
+// part[s][m][n] = s_n * (sum over K range s), left for a finishing launch.
+int fp8_splitk_slices(int64_t m, int64_t n, int64_t k);
+hipError_t launch_fp8_splitk(const uint16_t* x, int64_t m, int64_t n, int64_t k, const uint8_t* codes,
+                             const float* scales, const float* t, int tks, const uint16_t* b, int64_t r, uint16_t* y,
+                             float* part, hipStream_t stream);
 int lora_slices(int64_t k, int splits);
 hipError_t launch_lora_down(const uint16_t* x, int64_t m, int64_t k, const uint16_t* a, int64_t r, float lora_scale,
                             int splits, float* part, hipStream_t stream);

@@ -337,10 +337,11 @@ __global__ void lora_reduce_kernel(const float* __restrict__ part, int slices, i
 // COH: t was written by other workgroups of this launch, so it is read with
 // agent-coherent loads (16 bytes at a time, through a buffer descriptor).
 // KB: K-slices of t loaded at once.
+// rs: per-row scales (FP8 weights) in place of st, when set.
 template <bool COH = false, int KB = 4>
 __device__ __forceinline__ void store_tile(f32x4 v, int nb, int mb, int lane, int M, int N, float st,
                                            const float* __restrict__ t, int tks, const uint16_t* __restrict__ lb,
-                                           int r, uint16_t* __restrict__ y) {
+                                           int r, uint16_t* __restrict__ y, const float* __restrict__ rs = nullptr) {
   const int li = lane & 15, lg = lane >> 4;
   f32x4 lo = {0.f, 0.f, 0.f, 0.f};
   if (r > 0) {
@@ -416,8 +417,13 @@ __device__ __forceinline__ void store_tile(f32x4 v, int nb, int mb, int lane, in
   const int m = mb + li;
   const int nf = nb + 4 * lg;
   if (m < M) {
-    const uint32_t o01 = pack_bf16x2(st * v[0] + lo[0], st * v[1] + lo[1]);
-    const uint32_t o23 = pack_bf16x2(st * v[2] + lo[2], st * v[3] + lo[3]);
+    f32x4 sv = {st, st, st, st};
+    if (rs != nullptr) {
+#pragma unroll
+      for (int e = 0; e < 4; ++e) sv[e] = rs[min(nf + e, N - 1)];
+    }
+    const uint32_t o01 = pack_bf16x2(sv[0] * v[0] + lo[0], sv[1] * v[1] + lo[1]);
+    const uint32_t o23 = pack_bf16x2(sv[2] * v[2] + lo[2], sv[3] * v[3] + lo[3]);
     uint16_t* yp = y + (int64_t)m * N + nf;
     if ((N & 3) == 0 && nf + 3 < N) {
       *reinterpret_cast<uint2*>(yp) = make_uint2(o01, o23);
@@ -647,8 +653,17 @@ __global__ __launch_bounds__(WAVES * kWave) void skinny_kernel(
 // ---------------------------------------------------------------------------
 constexpr int kXRow = 136;  // bf16 per LDS token row: 128 + 8 of padding
 
-template <int TM, int TN, int W, int D>
-__global__ __launch_bounds__(W * kWave) __attribute__((amdgpu_waves_per_eu(D == 2 ? (TM <= 2 ? 4 : 3) : 1))) void splitk_kernel(
+// F8: the weights are E4M3 bytes [N][K] row-major with one fp32 scale per row
+// (`scales` then points to N floats): a lane loads the 32 contiguous bytes
+// k = 32 g .. + 31 of its row per chunk and step st takes k = 32 g + 8 st
+// .. + 7 (the same order on the activation side, so the sum is the plain
+// one); converted exactly to bf16, no block scale. With one K range the
+// workgroup stores y = bf16(s_n sum + t B^T), t (tks K-slices) made by a
+// separate down-projection launch; otherwise it writes its K range's partial
+// tile, times the row scales, to part[z] (plain stores; a later launch adds
+// the ranges and the LoRA term). No counters and no fused producers.
+template <int TM, int TN, int W, int D, bool F8 = false>
+__global__ __launch_bounds__(W * kWave) __attribute__((amdgpu_waves_per_eu(D == 2 ? (TM <= 2 ? 4 : (F8 ? 2 : 3)) : 1))) void splitk_kernel(
     const uint16_t* __restrict__ x, int M, int N, int K, const uint8_t* __restrict__ codes,
     const uint8_t* __restrict__ scales, const float* __restrict__ tensor_scale, const float* __restrict__ t, int tks,
     const uint16_t* __restrict__ lb, int r, uint16_t* __restrict__ y, int cpz, int nsplit, float* __restrict__ part,
@@ -686,6 +701,9 @@ __global__ __launch_bounds__(W * kWave) __attribute__((amdgpu_waves_per_eu(D == 
   int toff[TM];  // row tiles past the matrix are clamped to the last (never stored)
 #pragma unroll
   for (int i = 0; i < TM; ++i) toff[i] = (min(rt0 + i, RT - 1) - rt0) * KC;
+  const uint8_t* wrow[TM];  // F8: row n0 + 16 i + li (clamped), bytes from k = 32 g
+#pragma unroll
+  for (int i = 0; i < TM; ++i) wrow[i] = codes + (int64_t)min(n0 + 16 * i + li, N - 1) * K + 32 * lg;
   // Coalesced activation load: instruction q covers token rows 4 q + lg, 16 B
   // per lane, at a wave-uniform chunk base plus a 32-bit lane offset. Tokens
   // past M are clamped to the last one (their outputs are never stored).
@@ -695,7 +713,7 @@ __global__ __launch_bounds__(W * kWave) __attribute__((amdgpu_waves_per_eu(D == 
   uint16_t* slab = xs[wave];
 
   struct WStage {
-    uint32_t cw[TM][4];
+    uint32_t cw[TM][F8 ? 8 : 4];
     uint32_t sw[TM];
   };
   struct XStage {
@@ -704,6 +722,18 @@ __global__ __launch_bounds__(W * kWave) __attribute__((amdgpu_waves_per_eu(D == 
   auto chunk_of = [&](int q) { return __builtin_amdgcn_readfirstlane(cbeg + wave + W * q); };
   auto load_w = [&](int q, WStage& S) {
     const int c = chunk_of(q);
+    if constexpr (F8) {
+      // K % 16 == 0: a 16-byte piece is all in or out of the row
+#pragma unroll
+      for (int i = 0; i < TM; ++i)
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+          const bool in = 128 * c + 32 * lg + 16 * h < K;
+          const uint4 v = in ? ld_nt16(wrow[i] + 128 * (int64_t)c + 16 * h) : make_uint4(0u, 0u, 0u, 0u);
+          S.cw[i][4 * h] = v.x; S.cw[i][4 * h + 1] = v.y; S.cw[i][4 * h + 2] = v.z; S.cw[i][4 * h + 3] = v.w;
+        }
+      return;
+    }
 #pragma unroll
     for (int i = 0; i < TM; ++i) {
       // streaming loads: a row group's token groups follow each other on one XCD and find the tiles in L2
@@ -736,6 +766,30 @@ __global__ __launch_bounds__(W * kWave) __attribute__((amdgpu_waves_per_eu(D == 
     for (int j = 0; j < TN; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
 
   auto compute = [&](const WStage& S) {
+    if constexpr (F8) {
+#pragma unroll
+      for (int st = 0; st < 4; ++st) {
+        bf16x8 xv[TN];
+#pragma unroll
+        for (int j = 0; j < TN; ++j)
+          xv[j] = as_bf16x8(*reinterpret_cast<const uint4*>(slab + (16 * j + li) * kXRow + 32 * lg + 8 * st));
+#pragma unroll
+        for (int i = 0; i < TM; ++i) {
+          uint32_t o[4];
+#pragma unroll
+          for (int d = 0; d < 2; ++d) {
+            const uint32_t wd = S.cw[i][2 * st + d];
+            const f32x2 lo = __builtin_amdgcn_cvt_pk_f32_fp8(wd, false), hi = __builtin_amdgcn_cvt_pk_f32_fp8(wd, true);
+            o[2 * d] = pack_hi16(lo.x, lo.y);
+            o[2 * d + 1] = pack_hi16(hi.x, hi.y);
+          }
+          const bf16x8 a = __builtin_bit_cast(bf16x8, make_uint4(o[0], o[1], o[2], o[3]));
+#pragma unroll
+          for (int j = 0; j < TN; ++j) acc[i][j] = mfma16x16x32(a, xv[j], acc[i][j]);
+        }
+      }
+      return;
+    }
     float sc[TM][4];
 #pragma unroll
     for (int i = 0; i < TM; ++i) scale4(S.sw[i], sc[i]);
@@ -795,7 +849,7 @@ __global__ __launch_bounds__(W * kWave) __attribute__((amdgpu_waves_per_eu(D == 
 #pragma unroll
     for (int j = 0; j < TN; ++j) *reinterpret_cast<f32x4*>(red + ((i * TN + j) * kWave + lane) * 4) = acc[i][j];
   __syncthreads();
-  const float st = *tensor_scale;
+  const float st = F8 ? 1.0f : *tensor_scale;
   constexpr int NTILE = TM * TN;
   f32x4 sums[(NTILE + W - 1) / W];
 #pragma unroll
@@ -808,6 +862,33 @@ __global__ __launch_bounds__(W * kWave) __attribute__((amdgpu_waves_per_eu(D == 
         sum += *reinterpret_cast<const f32x4*>(reinterpret_cast<const float*>(xs[w]) + (e * kWave + lane) * 4);
     }
     sums[e0] = sum;
+  }
+  if constexpr (F8) {
+    const float* rs = reinterpret_cast<const float*>(scales);
+    if (nsplit == 1) {  // one K range: y = bf16(s_n sum + t B^T) here, t from the separate down-projection
+#pragma unroll
+      for (int e0 = 0; e0 < (NTILE + W - 1) / W; ++e0) {
+        const int e = wave + W * e0;
+        if (e < NTILE)
+          store_tile(sums[e0], n0 + 16 * (e / TN), m0 + 16 * (e % TN), lane, M, N, 1.0f, t, tks, lb, r, y, rs);
+      }
+      return;
+    }
+    // part[kz][m][n] = s_n * (this K range's sum)
+    float* pz = part + (int64_t)kz * M * N;
+#pragma unroll
+    for (int e0 = 0; e0 < (NTILE + W - 1) / W; ++e0) {
+      const int e = wave + W * e0;
+      if (e < NTILE) {
+        const int m = m0 + 16 * (e % TN) + li, nf = n0 + 16 * (e / TN) + 4 * lg;
+        if (m < M) {
+#pragma unroll
+          for (int v = 0; v < 4; ++v)
+            if (nf + v < N) pz[(int64_t)m * N + nf + v] = rs[nf + v] * sums[e0][v];
+        }
+      }
+    }
+    return;
   }
   if (nsplit == 1) {
     lora_wait(lf, ytile, t_seen);
@@ -1912,6 +1993,52 @@ static hipError_t launch_splitk(const SplitkCfg& c, hipStream_t st, const uint16
   if (c.tm != 4) return hipErrorInvalidValue;
   FP4RL_SPLITK(2, 4)
 #undef FP4RL_SPLITK
+  return hipErrorInvalidValue;
+}
+
+// FP8 (E4M3) decode, 17..64 tokens: the split-K kernel's F8 mode (y, or
+// with a K split fp32 partials [s][m][n] times the row scales, which the FP8
+// linear's finishing launch adds with the LoRA term). Two 16-token tiles per
+// workgroup, K split as for NVFP4 weights (their bytes are n k here).
+static SplitkCfg pick_fp8_splitk(int64_t m, int64_t n, int64_t k) {
+  SplitkCfg c;
+  c.tn = 2;
+  c.w = 4;
+  c.gy = (int)((m + 16 * c.tn - 1) / (16 * c.tn));
+  const int64_t kc = (k + 127) / 128;
+  c.tm = (n + 63) / 64 * c.gy <= 256 && kc <= 64 ? 2 : 4;
+  c.gx = (int)((n + 16 * c.tm - 1) / (16 * c.tm));
+  const double wbytes = (double)n * (double)k;
+  int s = 1;
+  while ((int64_t)c.gx * c.gy * s < 256 && (kc + 2 * s - 1) / (2 * s) >= c.w &&
+         4.0 * (double)(2 * s) * (double)m * (double)n * 2.0 <= wbytes / 3.0)
+    s *= 2;
+  while (s < 8 && (kc + (int64_t)s * c.w - 1) / ((int64_t)s * c.w) > 24 &&
+         4.0 * (double)(s + 1) * (double)m * (double)n * 2.0 <= wbytes / 3.0)
+    ++s;
+  c.cpz = (int)((kc + s - 1) / s);
+  c.s = (int)((kc + c.cpz - 1) / c.cpz);
+  c.d = (int64_t)c.gx * c.gy > 256 || kc > 64 ? 2 : 3;
+  return c;
+}
+
+int fp8_splitk_slices(int64_t m, int64_t n, int64_t k) { return pick_fp8_splitk(m, n, k).s; }
+
+hipError_t launch_fp8_splitk(const uint16_t* x, int64_t m, int64_t n, int64_t k, const uint8_t* codes,
+                             const float* scales, const float* t, int tks, const uint16_t* b, int64_t r, uint16_t* y,
+                             float* part, hipStream_t stream) {
+  const SplitkCfg c = pick_fp8_splitk(m, n, k);
+  const unsigned grid = (unsigned)(8 * ((c.gx + 7) / 8) * c.gy * c.s);
+  const uint8_t* sc = reinterpret_cast<const uint8_t*>(scales);
+#define FP4RL_F8(TM_, TN_, D_)                                                                                       \
+  if (c.tm == TM_ && c.tn == TN_ && c.d == D_) {                                                                      \
+    hipLaunchKernelGGL((splitk_kernel<TM_, TN_, 4, D_, true>), dim3(grid), dim3(4 * kWave), 0, stream, x, (int)m,     \
+                       (int)n, (int)k, codes, sc, scales, t, tks, b, (int)r, y, c.cpz, c.s, part, nullptr,            \
+                       LoraFuse{});                                                                                   \
+    return hipGetLastError();                                                                                         \
+  }
+  FP4RL_F8(4, 2, 2) FP4RL_F8(4, 2, 3) FP4RL_F8(2, 2, 2) FP4RL_F8(2, 2, 3)
+#undef FP4RL_F8
   return hipErrorInvalidValue;
 }
 

@@ -100,7 +100,7 @@ def test_linear_ragged(shape):
     assert_elementwise(got, ref, accumulation_slack(base, lora, k + r), "fp8 linear")
 
 
-@pytest.mark.parametrize("m", [1, 32, 1024, 8192])
+@pytest.mark.parametrize("m", [1, 8, 32, 64, 1024, 8192])
 def test_linear_full_size_7b_gate(m):
     """GPU quantiser feeding the GPU linear at the 7B gate shape; sampled output columns vs the oracle."""
     dev = device()
