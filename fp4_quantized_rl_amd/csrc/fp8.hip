@@ -17,11 +17,14 @@
 //     to bf16 exactly on the way into LDS (v_cvt_pk_f32_fp8), fp32
 //     accumulation scaled per row by s_n; the contraction is split over
 //     workgroups when there are few output tiles (decode), partials fp32.
-//   W8A16 decode, 17..64 tokens: the NVFP4 linear's split-K kernel in its
-//     E4M3 mode (activations staged through LDS); without a K split it
-//     stores y itself (row scales, t B^T by MFMA), else fp32 partials.
-//   W8A16 decode up to 16 tokens and W8A8 decode: fp8_decode_kernel /
-//     e4m3_decode_kernel, fp32 partials per K-slice.
+//   Decode, 17..64 tokens: the NVFP4 linear's split-K kernel in its E4M3
+//     mode (activations staged through LDS); without a K split it stores y
+//     itself (row scales, t B^T by MFMA), else fp32 partials. W8A8 gives it
+//     the token codes widened to bf16 (exact; written by the token
+//     quantiser) and multiplies by the token scales: the same exact E4M3
+//     products, accumulated in fp32, as on the FP8 matrix cores.
+//   Decode up to 16 tokens: fp8_decode_kernel / e4m3_decode_kernel, fp32
+//     partials per K-slice.
 //   t = s x A^T in K-slices by the NVFP4 linear's LoRA down-projection
 //   kernel; the finishing kernels add the slices in order. With enough output tiles (prefill) the linear writes
 //   bf16 y in one launch, the LoRA term accumulated as a second contraction
@@ -66,9 +69,11 @@ __device__ __forceinline__ float4 load4(const void* w, int64_t i) {
   }
 }
 
+// wide (optional): the codes' values as bf16 (exact: 4 significant bits)
 template <bool BF16>
 __global__ __launch_bounds__(256) void fp8_quantize_kernel(const void* __restrict__ w, int K,
-                                                           uint8_t* __restrict__ codes, float* __restrict__ scales) {
+                                                           uint8_t* __restrict__ codes, float* __restrict__ scales,
+                                                           uint16_t* __restrict__ wide = nullptr) {
   __shared__ uint32_t red[4];
   const int64_t row = blockIdx.x;
   const int64_t base = row * K;
@@ -102,6 +107,17 @@ __global__ __launch_bounds__(256) void fp8_quantize_kernel(const void* __restric
       o[d] = word;
     }
     *reinterpret_cast<uint4*>(codes + base + k) = make_uint4(o[0], o[1], o[2], o[3]);
+    if (wide != nullptr) {
+      uint32_t h[8];
+#pragma unroll
+      for (int d = 0; d < 4; ++d) {
+        const f32x2 lo = __builtin_amdgcn_cvt_pk_f32_fp8(o[d], false), hi = __builtin_amdgcn_cvt_pk_f32_fp8(o[d], true);
+        h[2 * d] = pack_hi16(lo.x, lo.y);
+        h[2 * d + 1] = pack_hi16(hi.x, hi.y);
+      }
+      *reinterpret_cast<uint4*>(wide + base + k) = make_uint4(h[0], h[1], h[2], h[3]);
+      *reinterpret_cast<uint4*>(wide + base + k + 8) = make_uint4(h[4], h[5], h[6], h[7]);
+    }
   }
 }
 
@@ -432,11 +448,12 @@ size_t fp8_linear_workspace(int64_t m, int64_t n, int64_t k, int64_t r, bool a8,
   if (a8) {
     v.x8 = reinterpret_cast<uint8_t*>(take((size_t)m * k));
     v.xs = take((size_t)m * 4);
+    if (m > 16 && m <= 64) v.xb = reinterpret_cast<uint16_t*>(take((size_t)m * k * 2));
   }
   // decode (m <= 64) always writes partials; otherwise only a split contraction does
   const bool dec = m <= 64;
   const int chunk = a8 ? 128 : kGC;
-  const int sl = dec ? (a8 || m <= 16 ? dec_split(m, n, k, chunk).slices : fp8_splitk_slices(m, n, k))
+  const int sl = dec ? (m <= 16 ? dec_split(m, n, k, chunk).slices : fp8_splitk_slices(m, n, k))
                      : nt_slices(nt_tiles(m, n), k, chunk);
   const bool parts = dec || sl > 1;
   const int64_t rp = (r + 7) / 8 * 8;
@@ -482,7 +499,7 @@ hipError_t launch_fp8_linear(const uint16_t* x, int64_t m, int64_t n, int64_t k,
                              const float* scales, const uint16_t* a, const uint16_t* b, int64_t r, float s, bool a8,
                              uint16_t* y, const Fp8Ws& w, hipStream_t st) {
   if (a8) {  // the tokens' E4M3 codes and scales: the weight quantiser, one workgroup per token
-    hipLaunchKernelGGL(fp8_quantize_kernel<true>, dim3((unsigned)m), dim3(256), 0, st, x, (int)k, w.x8, w.xs);
+    hipLaunchKernelGGL(fp8_quantize_kernel<true>, dim3((unsigned)m), dim3(256), 0, st, x, (int)k, w.x8, w.xs, w.xb);
     const hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
@@ -494,9 +511,10 @@ hipError_t launch_fp8_linear(const uint16_t* x, int64_t m, int64_t n, int64_t k,
     if (e != hipSuccess) return e;
   }
   const int chunk = a8 ? 128 : kGC;
-  if (m > 16 && m <= 64 && !a8) {  // W8A16 decode: the split-K kernel's E4M3 mode (+ the finishing launch for a K split)
-    const hipError_t e = launch_fp8_splitk(x, m, n, k, codes, scales, w.tpart, tsl, r > 0 ? b : nullptr, r, y,
-                                           w.ypart, st);
+  if (m > 16 && m <= 64) {  // decode: the split-K kernel's E4M3 mode (+ the finishing launch for a K split);
+                            // W8A8 feeds it the token codes widened to bf16 and their scales
+    const hipError_t e = launch_fp8_splitk(a8 ? w.xb : x, m, n, k, codes, scales, w.tpart, tsl, r > 0 ? b : nullptr,
+                                           r, y, w.ypart, a8 ? w.xs : nullptr, st);
     if (e != hipSuccess) return e;
     const int sl = fp8_splitk_slices(m, n, k);
     if (sl > 1)

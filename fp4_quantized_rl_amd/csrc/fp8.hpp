@@ -15,6 +15,7 @@ hipError_t launch_fp8_quantize(const void* w, bool w_bf16, int64_t n, int64_t k,
 struct Fp8Ws {
   uint8_t* x8 = nullptr;   // [m][k] E4M3 codes of the tokens (W8A8)
   float* xs = nullptr;     // [m] their scales
+  uint16_t* xb = nullptr;  // [m][k] the token codes widened to bf16 (W8A8 decode, 17..64 tokens)
   float* ypart = nullptr;  // [S][m][n] partial products of the base (S contraction slices)
   float* tpart = nullptr;  // [St][m][r] K-slices of t = s x A^T
   uint16_t* ts = nullptr;  // [m][2 rp] bf16 hi | lo of t (unsplit launches; rp = r rounded up to 8)

@@ -37,10 +37,11 @@ int lora_splits(int64_t m, int64_t k, int64_t r);
 // s = fp8_splitk_slices K ranges: with s == 1 it stores y = bf16(s_n sum +
 // t B^T) (t: tks K-slices [tks][m][r], or r == 0); otherwise fp32 partials
 // part[s][m][n] = s_n * (sum over K range s), left for a finishing launch.
+// tok_scale (W8A8): x holds E4M3 token codes as bf16, sums times xs[m].
 int fp8_splitk_slices(int64_t m, int64_t n, int64_t k);
 hipError_t launch_fp8_splitk(const uint16_t* x, int64_t m, int64_t n, int64_t k, const uint8_t* codes,
                              const float* scales, const float* t, int tks, const uint16_t* b, int64_t r, uint16_t* y,
-                             float* part, hipStream_t stream);
+                             float* part, const float* tok_scale, hipStream_t stream);
 int lora_slices(int64_t k, int splits);
 hipError_t launch_lora_down(const uint16_t* x, int64_t m, int64_t k, const uint16_t* a, int64_t r, float lora_scale,
                             int splits, float* part, hipStream_t stream);

@@ -657,7 +657,9 @@ constexpr int kXRow = 136;  // bf16 per LDS token row: 128 + 8 of padding
 // (`scales` then points to N floats): a lane loads the 32 contiguous bytes
 // k = 32 g .. + 31 of its row per chunk and step st takes k = 32 g + 8 st
 // .. + 7 (the same order on the activation side, so the sum is the plain
-// one); converted exactly to bf16, no block scale. With one K range the
+// one); converted exactly to bf16, no block scale. With tok_scale set, x
+// holds the tokens' E4M3 codes widened to bf16 (exact) and the sums are
+// multiplied by each token's scale (W8A8). With one K range the
 // workgroup stores y = bf16(s_n sum + t B^T), t (tks K-slices) made by a
 // separate down-projection launch; otherwise it writes its K range's partial
 // tile, times the row scales, to part[z] (plain stores; a later launch adds
@@ -667,7 +669,7 @@ __global__ __launch_bounds__(W * kWave) __attribute__((amdgpu_waves_per_eu(D == 
     const uint16_t* __restrict__ x, int M, int N, int K, const uint8_t* __restrict__ codes,
     const uint8_t* __restrict__ scales, const float* __restrict__ tensor_scale, const float* __restrict__ t, int tks,
     const uint16_t* __restrict__ lb, int r, uint16_t* __restrict__ y, int cpz, int nsplit, float* __restrict__ part,
-    uint32_t* __restrict__ counters, LoraFuse lf) {
+    uint32_t* __restrict__ counters, LoraFuse lf, const float* __restrict__ tok_scale = nullptr) {
   static_assert(TM <= 4, "the reduction reuses the activation slabs: TM * TN KB <= TN * 4.25 KB");
   constexpr int TOK = 16 * TN;
   __shared__ __align__(16) uint16_t xs[W][TOK * kXRow];
@@ -865,6 +867,13 @@ __global__ __launch_bounds__(W * kWave) __attribute__((amdgpu_waves_per_eu(D == 
   }
   if constexpr (F8) {
     const float* rs = reinterpret_cast<const float*>(scales);
+    if (tok_scale != nullptr) {  // W8A8: the tokens are E4M3 codes, times their per-token scale
+#pragma unroll
+      for (int e0 = 0; e0 < (NTILE + W - 1) / W; ++e0) {
+        const int e = wave + W * e0;
+        if (e < NTILE) sums[e0] *= tok_scale[min(m0 + 16 * (e % TN) + li, M - 1)];
+      }
+    }
     if (nsplit == 1) {  // one K range: y = bf16(s_n sum + t B^T) here, t from the separate down-projection
 #pragma unroll
       for (int e0 = 0; e0 < (NTILE + W - 1) / W; ++e0) {
@@ -2026,7 +2035,7 @@ int fp8_splitk_slices(int64_t m, int64_t n, int64_t k) { return pick_fp8_splitk(
 
 hipError_t launch_fp8_splitk(const uint16_t* x, int64_t m, int64_t n, int64_t k, const uint8_t* codes,
                              const float* scales, const float* t, int tks, const uint16_t* b, int64_t r, uint16_t* y,
-                             float* part, hipStream_t stream) {
+                             float* part, const float* tok_scale, hipStream_t stream) {
   const SplitkCfg c = pick_fp8_splitk(m, n, k);
   const unsigned grid = (unsigned)(8 * ((c.gx + 7) / 8) * c.gy * c.s);
   const uint8_t* sc = reinterpret_cast<const uint8_t*>(scales);
@@ -2034,7 +2043,7 @@ hipError_t launch_fp8_splitk(const uint16_t* x, int64_t m, int64_t n, int64_t k,
   if (c.tm == TM_ && c.tn == TN_ && c.d == D_) {                                                                      \
     hipLaunchKernelGGL((splitk_kernel<TM_, TN_, 4, D_, true>), dim3(grid), dim3(4 * kWave), 0, stream, x, (int)m,     \
                        (int)n, (int)k, codes, sc, scales, t, tks, b, (int)r, y, c.cpz, c.s, part, nullptr,            \
-                       LoraFuse{});                                                                                   \
+                       LoraFuse{}, tok_scale);                                                                        \
     return hipGetLastError();                                                                                         \
   }
   FP4RL_F8(4, 2, 2) FP4RL_F8(4, 2, 3) FP4RL_F8(2, 2, 2) FP4RL_F8(2, 2, 3)

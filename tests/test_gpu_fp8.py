@@ -244,7 +244,8 @@ def test_w8a8_full_size_7b_gate(m):
 def test_w8a8_workspace_reused_across_shapes():
     """One workspace, sized for the largest call, serves decode, split and prefill W8A8 shapes in turn."""
     dev = device()
-    shapes = [(8, 4608, 3584, 32), (300, 1027, 2064, 5), (3, 520, 1040, 5), (1024, 512, 2048, 16), (64, 96, 272, 0)]
+    shapes = [(8, 4608, 3584, 32), (300, 1027, 2064, 5), (3, 520, 1040, 5), (1024, 512, 2048, 16), (64, 96, 272, 0),
+              (40, 4608, 3584, 32)]
     need = max(fr.fp8_lora_linear_workspace_bytes(m, n, k, r, w8a8=True) for m, n, k, r in shapes)
     ws = torch.full((need,), 0xA5, dtype=torch.uint8, device=dev)
     for (m, n, k, r) in shapes:
