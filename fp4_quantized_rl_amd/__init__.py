@@ -432,8 +432,8 @@ def fp8_lora_linear(x, w8: FP8Weight, lora_a=None, lora_b=None, lora_scale: floa
                     w8a8: bool = False):
     """y = bf16(x deq(W8)^T + lora_scale (x A^T) B^T); x bf16 [m, k].
 
-    w8a8: quantise the tokens too (one E4M3 scale per row of x) and run the
-    base product on the FP8 matrix cores; the LoRA term reads the bf16 x.
+    w8a8: quantise the tokens too (one E4M3 scale per row of x); the base product multiplies the E4M3 codes
+    exactly (FP8 matrix cores, or widened to bf16 at 17..64 tokens); the LoRA term reads the bf16 x.
     """
     torch = _torch()
     _dev_tensor(x, "x", (torch.bfloat16,), 2)

@@ -378,10 +378,13 @@ fp4rl_status fp4rl_aqn_lora_linear(const uint16_t* x, int64_t m, int64_t n, int6
  *   each row m of x gets s_x[m] = amax_m / 448 and E4M3 codes exactly as
  *   fp4rl_fp8_quantize gives a bf16 weight row; then
  *   y = bf16(s_x[m] s_n sum_k e4m3(x8[m,k]) e4m3(code[n,k]) + s (x A^T) B^T),
- *   the base product on the FP8 matrix cores, the LoRA term from the bf16
- *   x. Arguments, limits and ownership as for fp4rl_fp8_lora_linear; its
- *   workspace, fp4rl_fp8_lora_linear_w8a8_workspace(m, n, k, r) bytes, also
- *   holds the token codes and scales (no initial contents needed).
+ *   the LoRA term from the bf16 x. The products e4m3 x e4m3 are exact in
+ *   fp32: up to 16 and above 64 tokens they run on the FP8 matrix cores, at
+ *   17..64 tokens on the bf16 ones with both codes widened to bf16 exactly
+ *   (the same values, fp32 accumulation). Arguments, limits and ownership
+ *   as for fp4rl_fp8_lora_linear; its workspace,
+ *   fp4rl_fp8_lora_linear_w8a8_workspace(m, n, k, r) bytes, also holds the
+ *   token codes and scales (no initial contents needed).
  * Errors as for the NVFP4 calls; nothing is launched on error. */
 fp4rl_status fp4rl_fp8_quantize(const void* w, int32_t w_dtype, int64_t n, int64_t k, uint8_t* codes,
                                 float* row_scales, fp4rl_stream stream);
