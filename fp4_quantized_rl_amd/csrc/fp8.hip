@@ -393,15 +393,15 @@ __global__ __launch_bounds__(256) void e4m3_decode_kernel(const uint8_t* __restr
   }
 }
 
-// K-slices of the decode kernels: about 512 workgroups (64-row groups x
-// slices), each slice a multiple of the chunk (64, or 128 for E4M3 tokens)
-// and at least 256 long.
+// K-slices of the decode kernels (up to 16 tokens: one token tile): about
+// 512 workgroups (64-row groups x slices), each slice a multiple of the
+// chunk (64, or 128 for E4M3 tokens) and at least 256 long.
 struct DecSplit {
-  int t = 0, slice = 0, slices = 0;
+  int slice = 0, slices = 0;
 };
 DecSplit dec_split(int64_t m, int64_t n, int64_t k, int chunk) {
+  (void)m;
   DecSplit d;
-  d.t = m <= 16 ? 1 : m <= 32 ? 2 : 4;
   const int64_t groups = (n + kDecRows - 1) / kDecRows;
   int64_t want = (512 + groups - 1) / groups;
   want = std::max<int64_t>(1, std::min<int64_t>(want, k / 256));
@@ -522,15 +522,10 @@ hipError_t launch_fp8_linear(const uint16_t* x, int64_t m, int64_t n, int64_t k,
                          (int)n, w.tpart, tsl, r > 0 ? b : nullptr, (int)r, y);
     return hipGetLastError();
   }
-  if (m <= 64) {
+  if (m <= 16) {  // one token tile
     const DecSplit d = dec_split(m, n, k, chunk);
     const dim3 grid((unsigned)((n + kDecRows - 1) / kDecRows), (unsigned)d.slices);
-    if (d.t == 1)
-      launch_decode<1>(a8, grid, x, w, m, n, k, codes, scales, d.slice, st);
-    else if (d.t == 2)
-      launch_decode<2>(a8, grid, x, w, m, n, k, codes, scales, d.slice, st);
-    else
-      launch_decode<4>(a8, grid, x, w, m, n, k, codes, scales, d.slice, st);
+    launch_decode<1>(a8, grid, x, w, m, n, k, codes, scales, d.slice, st);
     hipLaunchKernelGGL(fp8_finish_kernel, finish_grid(m, n), dim3(256), finish_lds(r), st, w.ypart, d.slices, (int)m,
                        (int)n, w.tpart, tsl, r > 0 ? b : nullptr, (int)r, y);
     return hipGetLastError();
