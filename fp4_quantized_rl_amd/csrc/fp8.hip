@@ -424,6 +424,13 @@ size_t finish_lds(int64_t r) { return (size_t)kFinTok * (size_t)r * sizeof(float
 
 }  // namespace
 
+hipError_t launch_partials_finish(const float* part, int slices, int64_t m, int64_t n, const float* t, int tks,
+                                  const uint16_t* b, int64_t r, uint16_t* y, hipStream_t stream) {
+  hipLaunchKernelGGL(fp8_finish_kernel, finish_grid(m, n), dim3(256), finish_lds(r), stream, part, slices, (int)m,
+                     (int)n, t, tks, b, (int)r, y);
+  return hipGetLastError();
+}
+
 hipError_t launch_fp8_quantize(const void* w, bool w_bf16, int64_t n, int64_t k, uint8_t* codes, float* scales,
                                hipStream_t st) {
   if (w_bf16)

@@ -39,6 +39,10 @@ int lora_splits(int64_t m, int64_t k, int64_t r);
 // part[s][m][n] = s_n * (sum over K range s), left for a finishing launch.
 // tok_scale (W8A8): x holds E4M3 token codes as bf16, sums times xs[m].
 int fp8_splitk_slices(int64_t m, int64_t n, int64_t k);
+// y[m][n] = bf16(sum_z part[z][m][n] + sum_j t[m][j] B[n][j]) (t: tks K-slices [tks][m][r], summed in order;
+// t and b may be NULL with r == 0): the finishing launch of split contractions.
+hipError_t launch_partials_finish(const float* part, int slices, int64_t m, int64_t n, const float* t, int tks,
+                                  const uint16_t* b, int64_t r, uint16_t* y, hipStream_t stream);
 hipError_t launch_fp8_splitk(const uint16_t* x, int64_t m, int64_t n, int64_t k, const uint8_t* codes,
                              const float* scales, const float* t, int tks, const uint16_t* b, int64_t r, uint16_t* y,
                              float* part, const float* tok_scale, hipStream_t stream);

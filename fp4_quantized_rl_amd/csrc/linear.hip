@@ -1033,7 +1033,8 @@ template <int RW, int TGW, int WR, int WT, int D>
 __global__ __launch_bounds__(WR * WT * kWave) void mid_kernel(
     const uint16_t* __restrict__ x, int M, int N, int K, const uint8_t* __restrict__ codes,
     const uint8_t* __restrict__ scales, const float* __restrict__ tensor_scale, const float* __restrict__ t, int tks,
-    const uint16_t* __restrict__ lb, int r, uint16_t* __restrict__ y, LoraFuse lf) {
+    const uint16_t* __restrict__ lb, int r, uint16_t* __restrict__ y, LoraFuse lf, int nsplit = 1, int cps = 0,
+    float* __restrict__ part = nullptr) {
   constexpr int W = WR * WT;
   constexpr int TOK = 32 * TGW * WT;  // tokens of the workgroup
   constexpr int ROWS = 32 * RW * WR;  // features of the workgroup
@@ -1045,7 +1046,11 @@ __global__ __launch_bounds__(WR * WT * kWave) void mid_kernel(
     lora_produce<W>(lf, blockIdx.x, x, M, K, r, reinterpret_cast<f32x4*>(xs), &last_flag);
     return;
   }
-  const int rg = (int)blockIdx.x - lf.producers;  // row group (the producers come first)
+  // row group (the producers come first); with part set, K range z of it:
+  // chunks cbeg .. cbeg + cps - 1
+  const int L = (int)blockIdx.x - lf.producers;
+  const int rg = part != nullptr ? L / nsplit : L;
+  const int z = part != nullptr ? L - rg * nsplit : 0;
   const int lane = threadIdx.x & (kWave - 1);
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
   const int wr = wave % WR, wt = wave / WR;
@@ -1053,7 +1058,8 @@ __global__ __launch_bounds__(WR * WT * kWave) void mid_kernel(
   const int RT = (N + 15) >> 4, KC = (K + 127) >> 7;
   const int nw = ROWS * rg + 32 * RW * wr;  // this wave's features nw + 32 i + 0 .. 31, i < RW
   const int mw = 32 * TGW * wt;             // this wave's tokens mw + 32 g + 0 .. 31, g < TGW
-  const int nch = KC;                       // chunks of 128 k
+  const int cbeg = part != nullptr ? z * cps : 0;
+  const int nch = part != nullptr ? min(KC - cbeg, cps) : KC;  // chunks of 128 k
 
   // weights: tile of row nw + 32 i + lr (clamped: rows past N are computed, never stored)
   const uint8_t* cl[RW];
@@ -1073,7 +1079,7 @@ __global__ __launch_bounds__(WR * WT * kWave) void mid_kernel(
     uint32_t s[RW];
   };
   auto load_w = [&](int q, WStage& S) {
-    const int64_t c = min(q, nch - 1);
+    const int64_t c = cbeg + min(q, nch - 1);
 #pragma unroll
     for (int i = 0; i < RW; ++i) {
       S.c0[i] = ld_nt16(cl[i] + c * 1024);
@@ -1096,7 +1102,7 @@ __global__ __launch_bounds__(WR * WT * kWave) void mid_kernel(
   }
   const int kcol = 8 * ((int)threadIdx.x & 15);  // the same k offset for every piece of this thread
   auto load_x = [&](int q, uint4 (&v)[XP]) {
-    const int c = min(q, nch - 1);
+    const int c = cbeg + min(q, nch - 1);
     const uint32_t base = 256u * (uint32_t)c, past = 128 * c + kcol < K ? 0u : 0x80000000u;
 #pragma unroll
     for (int u = 0; u < XP; ++u)
@@ -1187,6 +1193,32 @@ __global__ __launch_bounds__(WR * WT * kWave) void mid_kernel(
     }
   }
 
+  if (part != nullptr) {  // K range z: s_t times its sums as fp32 partials (a later launch adds them)
+    const float st = *tensor_scale;
+    float* pz = part + (int64_t)z * M * N;
+#pragma unroll
+    for (int i = 0; i < RW; ++i)
+#pragma unroll
+      for (int g = 0; g < TGW; ++g) {
+        const int m = mw + 32 * g + lr;
+        if (m >= M) continue;
+#pragma unroll
+        for (int b = 0; b < 4; ++b) {
+          const int nf = nw + 32 * i + 8 * b + 4 * lh;
+          const f32x4 v = {st * acc[i][g][4 * b], st * acc[i][g][4 * b + 1], st * acc[i][g][4 * b + 2],
+                           st * acc[i][g][4 * b + 3]};
+          float* pp = pz + (int64_t)m * N + nf;
+          if ((N & 3) == 0 && nf + 3 < N) {
+            *reinterpret_cast<f32x4*>(pp) = v;
+          } else {
+#pragma unroll
+            for (int e = 0; e < 4; ++e)
+              if (nf + e < N) pp[e] = v[e];
+          }
+        }
+      }
+    return;
+  }
   const uint32_t t_seen = lora_poll(lf, rg);  // fused LoRA: read early, checked below
   const float st = *tensor_scale;
 #pragma unroll
@@ -1928,6 +1960,30 @@ static hipError_t launch_mid(hipStream_t st, const uint16_t* x, int M, int N, in
   return hipGetLastError();
 }
 
+// Mid-batch kernel with a K split (96 < m <= 128, fewer than 200 row groups
+// of 128 and long K, e.g. 32B down): every weight tile is still dequantised
+// once for all the tokens; each row group's K is split into s ranges so that
+// about 240 workgroups run, each writes s_t times its sums as fp32 partials,
+// and a finishing launch adds the ranges and the LoRA term (t from a separate
+// down-projection). The in-kernel alternative, the last workgroup of a tile
+// adding the ranges, left that sum to one CU per tile.
+struct MidSplit {
+  int s, cps;
+};
+// (measured at 128 tokens: 32B down, 27648 k, 91 -> 80 us; 7B down, 18944 k,
+// 50 -> 52 us, so K of at least 192 chunks)
+static bool use_mid_split(int64_t m, int64_t n, int64_t k) {
+  return m > 96 && m <= 128 && (n + kMidRows - 1) / kMidRows < 200 && (k + 127) / 128 >= 192;
+}
+static MidSplit pick_mid_split(int64_t n, int64_t k) {
+  const int64_t gx = (n + kMidRows - 1) / kMidRows, kc = (k + 127) / 128;
+  const int64_t s = std::max<int64_t>(1, std::min<int64_t>((240 + gx - 1) / gx, kc / 16));
+  MidSplit c;
+  c.cps = (int)((kc + s - 1) / s);
+  c.s = (int)((kc + c.cps - 1) / c.cps);  // no empty K range
+  return c;
+}
+
 static SplitkCfg pick_splitk(int64_t m, int64_t n, int64_t k) {
   SplitkCfg c;
   c.tn = 2;
@@ -1964,6 +2020,8 @@ static SplitkCfg pick_splitk(int64_t m, int64_t n, int64_t k) {
 }
 
 size_t linear_partial_bytes(int64_t m, int64_t n, int64_t k) {
+  if (use_mid_split(m, n, k))
+    return ((size_t)pick_mid_split(n, k).s * (size_t)m * (size_t)n * sizeof(float) + 255) / 256 * 256;
   if (use_mid(m, n) || !use_splitk(m)) return 0;
   const SplitkCfg c = pick_splitk(m, n, k);
   if (c.s == 1) return 0;
@@ -2071,7 +2129,7 @@ const char* fp4_linear_kernel_name(int64_t m, int64_t n, int64_t k, int64_t r) {
     return kGemv[m - 1][wi];
   }
   if (use_prefill(m)) return "prefill_kernel<2>";
-  if (use_mid(m, n)) return "mid_kernel<1, 2, 4, 2, 3>";
+  if (use_mid(m, n) || use_mid_split(m, n, k)) return "mid_kernel<1, 2, 4, 2, 3>";
   if (use_splitk(m)) {
     const SplitkCfg sc = pick_splitk(m, n, k);
     static const char* const kSplitk[3][2] = {{"splitk_kernel<2, 2, 4, 2>", "splitk_kernel<2, 2, 4, 3>"},
@@ -2086,9 +2144,9 @@ const char* fp4_linear_kernel_name(int64_t m, int64_t n, int64_t k, int64_t r) {
 }
 
 bool linear_fuses_lora(int64_t m, int64_t n, int64_t k) {
-  (void)n;
-  (void)k;
-  return !use_prefill(m);  // every decode kernel (GEMV, skinny: one token group; split-K)
+  // every decode kernel (GEMV, skinny: one token group; split-K; mid-batch)
+  // but the mid-batch kernel's K split, whose finishing launch adds t B^T
+  return !use_prefill(m) && !use_mid_split(m, n, k);
 }
 
 int64_t lora_slice_len(int64_t k, int splits) { return ((k + splits - 1) / splits + 31) / 32 * 32; }
@@ -2107,6 +2165,16 @@ hipError_t launch_fp4_linear(const uint16_t* x, int64_t m, int64_t n, int64_t k,
     const int w = gemv_waves(n, k);
     return m == 1 ? run_gemv_w<1>(w, stream, x, M, N, K, codes, scales, tensor_scale, t, tks, b, R, y, lf)
                   : run_gemv_w<2>(w, stream, x, M, N, K, codes, scales, tensor_scale, t, tks, b, R, y, lf);
+  }
+  if (use_mid_split(m, n, k)) {
+    const MidSplit c = pick_mid_split(n, k);
+    if (part == nullptr || lf.producers > 0) return hipErrorInvalidValue;
+    const int gx = (N + kMidRows - 1) / kMidRows;
+    hipLaunchKernelGGL((mid_kernel<1, 2, 4, 2, 3>), dim3((unsigned)(gx * c.s)), dim3(8 * kWave), 0, stream, x, M, N, K,
+                       codes, scales, tensor_scale, t, tks, b, R, y, LoraFuse{}, c.s, c.cps, part);
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    return launch_partials_finish(part, c.s, m, n, r > 0 ? t : nullptr, tks, r > 0 ? b : nullptr, r, y, stream);
   }
   if (use_mid(m, n)) return launch_mid(stream, x, M, N, K, codes, scales, tensor_scale, t, tks, b, R, y, lf);
   if (use_splitk(m))

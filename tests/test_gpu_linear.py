@@ -118,12 +118,16 @@ def test_split_k_launch_configs(m, n, k, r, kernel):
     _check_lin(y, x, q, a, b, LORA_SCALE, f"{m}x{n}x{k} r{r}")
 
 
-MID_CONFIGS = [  # (m, n, k, r): more than 96 tokens on at least 200 row groups of 128 features
+MID_CONFIGS = [  # (m, n, k, r): more than 96 tokens on at least 200 row groups of 128 features, or long K
     (100, 30000, 1040, 0),    # no adapters, a ragged last chunk
     (128, 30001, 272, 3),     # n % 4 != 0 (scalar stores), a short ragged K, r % 8 != 0 (scalar B loads)
     (97, 25601, 2064, 5),     # the fewest tokens, one feature past 200 row groups of 128
     (113, 26000, 3568, 32),   # tokens past M inside the last token group, a ragged K
     (128, 25473, 1040, 256),  # the largest rank: 128 tiles of t from the fused producers
+    # fewer row groups and long K: the K split, fp32 partials and the finishing launch (t made separately)
+    (113, 1001, 24592, 8),    # n % 4 != 0, a ragged last chunk, tokens past M in the last group
+    (128, 300, 28672, 0),     # no adapters
+    (97, 640, 24576, 100),    # a rank that is not a multiple of 8
 ]
 
 
