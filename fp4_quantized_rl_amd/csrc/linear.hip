@@ -1317,10 +1317,11 @@ __global__ __launch_bounds__(WR * WT * kWave) void mid_kernel(
 }
 
 // ---------------------------------------------------------------------------
-// Prefill GEMM (M > 128 tokens): a workgroup computes 256 output features x
-// 128 tokens over all of K with four waves; wave w owns features 64 w .. +63
-// (two 32-row tiles, the 32x32x16 MFMA with dequantised weights as A) against
-// all four 32-token groups, so each dequantised fragment feeds four MFMAs.
+// Prefill GEMM (M > 128 tokens): a workgroup computes 64 WAVES output
+// features x 128 tokens over all of K with WAVES waves (4 or 8); wave w owns
+// features 64 w .. +63 (two 32-row tiles, the 32x32x16 MFMA with dequantised
+// weights as A) against all four 32-token groups, so each dequantised
+// fragment feeds four MFMAs.
 //   Activations go from HBM straight into LDS (buffer loads with an LDS
 //   destination: no staging registers, no LDS store instructions), in the
 //   MFMA operand order: one 1 KB fragment per (token group, 16-k step), lane
@@ -1328,9 +1329,11 @@ __global__ __launch_bounds__(WR * WT * kWave) void mid_kernel(
 //   contiguous 1 KB. Two slabs of 32 fragments (64 KB): chunk q + 1 loads
 //   into one while chunk q is read from the other; one barrier per chunk.
 //   Weights go to registers one chunk ahead.
-//   With 64 KB of LDS and at most 256 registers per lane, two workgroups
-//   share a CU (two waves per SIMD, one from each): the barrier and load
-//   waits of one overlap the MFMAs of the other.
+//   With 64 KB of LDS and at most 256 registers per lane, a CU holds two
+//   waves per SIMD: two four-wave workgroups (the barrier and load waits of
+//   one overlap the MFMAs of the other) or one eight-wave workgroup, whose
+//   512 features share each activation chunk (68 KB of loads per chunk
+//   instead of 100 KB for the same flops on the CU).
 //   Within a chunk the fragments of the next 16-k step (four LDS reads, two
 //   dequantisations) are prepared while the current step's eight MFMAs run.
 //   Grid order is XCD-aware: the 8 XCDs take workgroups in turn, and each
@@ -1338,16 +1341,16 @@ __global__ __launch_bounds__(WR * WT * kWave) void mid_kernel(
 //   workgroups that run together on one XCD share their weights and
 //   activations in its L2.
 // ---------------------------------------------------------------------------
-constexpr int kPfRows = 256, kPfTok = 128;
+constexpr int kPfTok = 128;
 typedef __attribute__((address_space(3))) void* lds_ptr;
 
-template <int D>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) void prefill_kernel(
+template <int D, int WAVES>
+__global__ __launch_bounds__(64 * WAVES) __attribute__((amdgpu_waves_per_eu(2, 2))) void prefill_kernel(
     const uint16_t* __restrict__ x, int M, int N, int K, const uint8_t* __restrict__ codes,
     const uint8_t* __restrict__ scales, const float* __restrict__ tensor_scale, const float* __restrict__ t, int tks,
     const uint16_t* __restrict__ lb, int r, uint16_t* __restrict__ y) {
-  constexpr int RW = 2, TG = 4, WAVES = 4;
-  static_assert(32 * RW * WAVES == kPfRows && 32 * TG == kPfTok, "tile shape");
+  constexpr int RW = 2, TG = 4, ROWS = 32 * RW * WAVES;
+  static_assert((WAVES == 4 || WAVES == 8) && 32 * TG == kPfTok, "tile shape");
   constexpr int NFRAG = TG * 8;       // 1 KB activation fragments per chunk: (g, j, q)
   constexpr int FPW = NFRAG / WAVES;  // fragments loaded per wave
   __shared__ __align__(1024) uint8_t xs[2][NFRAG * 1024];
@@ -1355,7 +1358,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
   const int lr = lane & 31, lh = lane >> 5;
   const int RT = (N + 15) >> 4, KC = (K + 127) >> 7;
-  const int GR = (N + kPfRows - 1) / kPfRows, GT = (M + kPfTok - 1) / kPfTok;
+  const int GR = (N + ROWS - 1) / ROWS, GT = (M + kPfTok - 1) / kPfTok;
   // workgroup -> (row group, token group): XCD = L % 8; slot j = L / 8 of that
   // XCD; super-tile s = 8 (j / 32) + XCD covers row groups 8 sr .. +7 and
   // token groups 4 stt .. +3, its 32 tiles taken row group fastest
@@ -1366,7 +1369,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   const int rg = 8 * sr + (within & 7), tg = 4 * stt + (within >> 3);
   if (rg >= GR || tg >= GT) return;
   const int m0 = tg * kPfTok;
-  const int nw = rg * kPfRows + 32 * RW * wave;  // this wave's features nw + 32 i + 0 .. 31
+  const int nw = rg * ROWS + 32 * RW * wave;  // this wave's features nw + 32 i + 0 .. 31
 
   // weights: lane (lr, lh) takes row nw + 32 i + lr (rows past N clamped to
   // the last tile: computed, never stored); in chunk step (j, q) its word j
@@ -1934,6 +1937,23 @@ static bool use_splitk(int64_t m) { return m > 16 && !use_prefill(m); }
 // (measured, 27648 x 5120 at 112 and 128 tokens: 63 vs 73 us; at 65..96
 // tokens the two are level, and narrower matrices, which would need a K
 // split, are faster on the split-K kernel).
+// Prefill workgroup shape: eight waves (512 features, one workgroup per CU)
+// move a third fewer bytes per flop through each CU than two four-wave
+// workgroups, but come in half as many, coarser pieces. A launch runs in
+// rounds of 256 workgroups (one per CU); eight waves are used when rounding
+// the workgroup count up to whole rounds wastes at most 1/7 of a round's
+// work, else four, whose pairs per CU also run a thin last round faster.
+// (Measured at 8192 tokens: 7B gate 1021 -> 1007 us, down 1113 -> 985, o 226
+// -> 208, 14B gate 1040 -> 980, 32B gate 2011 -> 1942; kept on four waves:
+// 7B qkv, 576 workgroups, 273 against 304 us, and 32B o, 640, 391 against
+// 421; at 4096 tokens 7B down 545 -> 510, and up to 2048 tokens four waves
+// throughout.)
+static int prefill_waves(int64_t m, int64_t n) {
+  const int64_t tiles = (n + 511) / 512 * ((m + kPfTok - 1) / kPfTok);
+  const int64_t rounds = (tiles + 255) / 256;
+  return 7 * 256 * rounds <= 8 * tiles ? 8 : 4;
+}
+
 constexpr int kMidRows = 128;
 static bool use_mid(int64_t m, int64_t n) {
   return m > 96 && m <= 128 && (n + kMidRows - 1) / kMidRows >= 200;
@@ -2128,7 +2148,7 @@ const char* fp4_linear_kernel_name(int64_t m, int64_t n, int64_t k, int64_t r) {
     while ((1 << wi) < gemv_waves(n, k)) ++wi;
     return kGemv[m - 1][wi];
   }
-  if (use_prefill(m)) return "prefill_kernel<2>";
+  if (use_prefill(m)) return prefill_waves(m, n) == 8 ? "prefill_kernel<2, 8>" : "prefill_kernel<2, 4>";
   if (use_mid(m, n) || use_mid_split(m, n, k)) return "mid_kernel<1, 2, 4, 2, 3>";
   if (use_splitk(m)) {
     const SplitkCfg sc = pick_splitk(m, n, k);
@@ -2181,11 +2201,16 @@ hipError_t launch_fp4_linear(const uint16_t* x, int64_t m, int64_t n, int64_t k,
     return launch_splitk(pick_splitk(m, n, k), stream, x, M, N, K, codes, scales, tensor_scale, t, tks, b, R, y, part,
                          counters, lf);
   if (use_prefill(m)) {
-    const int64_t gr = (n + kPfRows - 1) / kPfRows, gt = (m + kPfTok - 1) / kPfTok;
+    const int waves = prefill_waves(m, n);
+    const int64_t gr = (n + 64 * waves - 1) / (64 * waves), gt = (m + kPfTok - 1) / kPfTok;
     const int64_t supers = (gr + 7) / 8 * ((gt + 3) / 4);  // super-tiles of 8 x 4 workgroups, dealt to 8 XCDs
     const int64_t grid = 8 * 32 * ((supers + 7) / 8);
-    hipLaunchKernelGGL(prefill_kernel<2>, dim3((unsigned)grid), dim3(256), 0, stream, x, M, N, K, codes, scales,
-                       tensor_scale, t, tks, b, R, y);
+    if (waves == 8)
+      hipLaunchKernelGGL((prefill_kernel<2, 8>), dim3((unsigned)grid), dim3(512), 0, stream, x, M, N, K, codes,
+                         scales, tensor_scale, t, tks, b, R, y);
+    else
+      hipLaunchKernelGGL((prefill_kernel<2, 4>), dim3((unsigned)grid), dim3(256), 0, stream, x, M, N, K, codes,
+                         scales, tensor_scale, t, tks, b, R, y);
     return hipGetLastError();
   }
   // 3..16 tokens: one token tile, so grid.y is 1

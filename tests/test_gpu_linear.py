@@ -240,8 +240,10 @@ def test_late_ready_flag_does_not_release_next_call(m):
     assert not bool(ws[:COUNTER_BYTES].any()), "counter words not back at zero"
 
 
-PREFILL = [  # (m, n, k, r): more than 128 tokens (256-feature x 128-token workgroup tiles), ragged in every dim
+PREFILL = [  # (m, n, k, r): more than 128 tokens (256- or 512-feature x 128-token workgroup tiles), ragged in
+    # every dim; the last two take the eight-wave, 512-feature workgroups (at least 224 of them)
     (129, 16, 128, 0), (200, 270, 400, 8), (384, 512, 1024, 16), (1000, 520, 2064, 32), (2048, 300, 4096, 64),
+    (4046, 3544, 1040, 24), (3970, 3600, 272, 0),
 ]
 
 
@@ -250,7 +252,9 @@ def test_prefill_shapes(m, n, k, r):
     dev = device()
     w, x, a, b = _case(m, n, k, r, seed=m * 13 + n * 7 + k, outliers=0.001)
     q = nvfp4.quantize(w)
-    say(f"linear prefill m={m} n={n} k={k} r={r} ({fr.fp4_linear_kernel_name(m, n, k, r)})")
+    kernel = fr.fp4_linear_kernel_name(m, n, k, r)
+    say(f"linear prefill m={m} n={n} k={k} r={r} ({kernel})")
+    assert kernel == ("prefill_kernel<2, 8>" if m * n > 10**7 else "prefill_kernel<2, 4>")
     y = _run(dev, x, q, a, b, LORA_SCALE)
     _check_lin(y, x, q, a, b, LORA_SCALE, f"{m}x{n}x{k} r{r}")
 
