@@ -127,16 +127,36 @@ __global__ __launch_bounds__(256) void fp8_quantize_kernel(const void* __restric
 // summed) are staged in LDS once, and each thread, one feature, reads its B
 // row 8 ranks at a time and accumulates the rank products of every token.
 constexpr int kFinTok = 2;
+template <int FT>
 __global__ __launch_bounds__(256) void fp8_finish_kernel(const float* __restrict__ part, int slices, int M, int N,
                                                          const float* __restrict__ tpart, int tsl,
                                                          const uint16_t* __restrict__ b, int r,
                                                          uint16_t* __restrict__ y) {
-  extern __shared__ float tsh[];  // [kFinTok][r]
+  extern __shared__ float tsh[];  // [FT][r]
   const int64_t count = (int64_t)M * N, tstride = (int64_t)M * r;
   const int n = blockIdx.x * 256 + threadIdx.x;
   const uint16_t* bn = b + (int64_t)min(n, N - 1) * r;
-  for (int m0 = blockIdx.y * kFinTok; m0 < M; m0 += gridDim.y * kFinTok) {  // uniform across the workgroup
-    const int mt = min(kFinTok, M - m0);
+  // up to 64 ranks of the B row (r % 8 == 0) are loaded once, all at once,
+  // before any rank product; other r read it 8 ranks at a time
+  constexpr int kBRegs = 8;
+  const bool breg = r <= 8 * kBRegs && (r & 7) == 0;
+  uint4 bw[kBRegs];
+  if (breg) {
+#pragma unroll
+    for (int q = 0; q < kBRegs; ++q) bw[q] = 8 * q < r ? *reinterpret_cast<const uint4*>(bn + 8 * q) : make_uint4(0, 0, 0, 0);
+  }
+  for (int m0 = blockIdx.y * FT; m0 < M; m0 += gridDim.y * FT) {  // uniform across the workgroup
+    const int mt = min(FT, M - m0);
+    // the partial sums first: their loads are in flight during the t staging
+    float v[FT];
+#pragma unroll
+    for (int mm = 0; mm < FT; ++mm) {
+      v[mm] = 0.0f;
+      if (n < N && mm < mt) {
+        const int64_t i = (int64_t)(m0 + mm) * N + n;
+        for (int s = 0; s < slices; ++s) v[mm] += part[(int64_t)s * count + i];
+      }
+    }
     __syncthreads();  // the previous token block's t is no longer read
     for (int e = threadIdx.x; e < mt * r; e += 256) {
       const int mm = e / r, j = e - mm * r;
@@ -146,44 +166,45 @@ __global__ __launch_bounds__(256) void fp8_finish_kernel(const float* __restrict
       tsh[mm * r + j] = tj;
     }
     __syncthreads();
-    float l[kFinTok];
+    float l[FT];
 #pragma unroll
-    for (int mm = 0; mm < kFinTok; ++mm) l[mm] = 0.0f;
-    for (int j0 = 0; j0 < r; j0 += 8) {
-      float bv[8];
-      if ((r & 7) == 0) {  // the B row is 16-byte aligned
-        const uint4 w = *reinterpret_cast<const uint4*>(bn + j0);
-        bv[0] = bf16_lo(w.x); bv[1] = bf16_hi(w.x); bv[2] = bf16_lo(w.y); bv[3] = bf16_hi(w.y);
-        bv[4] = bf16_lo(w.z); bv[5] = bf16_hi(w.z); bv[6] = bf16_lo(w.w); bv[7] = bf16_hi(w.w);
-      } else {
+    for (int mm = 0; mm < FT; ++mm) l[mm] = 0.0f;
+    if (breg) {
 #pragma unroll
-        for (int e = 0; e < 8; ++e) bv[e] = j0 + e < r ? bf16_lo(bn[j0 + e]) : 0.0f;
+      for (int q = 0; q < kBRegs; ++q) {
+        if (8 * q >= r) break;  // uniform
+        const float bv[8] = {bf16_lo(bw[q].x), bf16_hi(bw[q].x), bf16_lo(bw[q].y), bf16_hi(bw[q].y),
+                             bf16_lo(bw[q].z), bf16_hi(bw[q].z), bf16_lo(bw[q].w), bf16_hi(bw[q].w)};
+#pragma unroll
+        for (int mm = 0; mm < FT; ++mm)
+          if (mm < mt) {
+#pragma unroll
+            for (int e = 0; e < 8; ++e) l[mm] = fmaf(tsh[mm * r + 8 * q + e], bv[e], l[mm]);
+          }
       }
-      const int je = min(8, r - j0);
+    } else {
+      for (int j0 = 0; j0 < r; j0 += 8) {
+        float bv[8];
+        if ((r & 7) == 0) {  // the B row is 16-byte aligned
+          const uint4 w = *reinterpret_cast<const uint4*>(bn + j0);
+          bv[0] = bf16_lo(w.x); bv[1] = bf16_hi(w.x); bv[2] = bf16_lo(w.y); bv[3] = bf16_hi(w.y);
+          bv[4] = bf16_lo(w.z); bv[5] = bf16_hi(w.z); bv[6] = bf16_lo(w.w); bv[7] = bf16_hi(w.w);
+        } else {
 #pragma unroll
-      for (int mm = 0; mm < kFinTok; ++mm)
-        if (mm < mt) {
-          if (je == 8) {
-            float tv[8];
+          for (int e = 0; e < 8; ++e) bv[e] = j0 + e < r ? bf16_lo(bn[j0 + e]) : 0.0f;
+        }
+        const int je = min(8, r - j0);
 #pragma unroll
-            for (int e = 0; e < 8; ++e) tv[e] = tsh[mm * r + j0 + e];
-#pragma unroll
-            for (int e = 0; e < 8; ++e) l[mm] = fmaf(tv[e], bv[e], l[mm]);
-          } else {
+        for (int mm = 0; mm < FT; ++mm)
+          if (mm < mt) {
             for (int e = 0; e < je; ++e) l[mm] = fmaf(tsh[mm * r + j0 + e], bv[e], l[mm]);
           }
-        }
+      }
     }
     if (n < N) {
 #pragma unroll
-      for (int mm = 0; mm < kFinTok; ++mm) {
-        if (mm < mt) {
-          const int64_t i = (int64_t)(m0 + mm) * N + n;
-          float v = 0.0f;
-          for (int s = 0; s < slices; ++s) v += part[(int64_t)s * count + i];
-          y[i] = (uint16_t)f32_to_bf16(v + l[mm]);
-        }
-      }
+      for (int mm = 0; mm < FT; ++mm)
+        if (mm < mt) y[(int64_t)(m0 + mm) * N + n] = (uint16_t)f32_to_bf16(v[mm] + l[mm]);
     }
   }
 }
@@ -417,17 +438,19 @@ unsigned flat_grid8(int64_t count) {
 
 size_t al256(size_t v) { return (v + 255) / 256 * 256; }
 
-dim3 finish_grid(int64_t m, int64_t n) {
-  return dim3((unsigned)((n + 255) / 256), (unsigned)std::min<int64_t>((m + kFinTok - 1) / kFinTok, 4096));
+dim3 finish_grid(int64_t m, int64_t n, int ft = kFinTok) {
+  return dim3((unsigned)((n + 255) / 256), (unsigned)std::min<int64_t>((m + ft - 1) / ft, 4096));
 }
-size_t finish_lds(int64_t r) { return (size_t)kFinTok * (size_t)r * sizeof(float); }
+size_t finish_lds(int64_t r, int ft = kFinTok) { return (size_t)ft * (size_t)r * sizeof(float); }
 
 }  // namespace
 
+constexpr int kPartFinTok = 2;  // tokens per workgroup of the NVFP4 K-split finish
+
 hipError_t launch_partials_finish(const float* part, int slices, int64_t m, int64_t n, const float* t, int tks,
                                   const uint16_t* b, int64_t r, uint16_t* y, hipStream_t stream) {
-  hipLaunchKernelGGL(fp8_finish_kernel, finish_grid(m, n), dim3(256), finish_lds(r), stream, part, slices, (int)m,
-                     (int)n, t, tks, b, (int)r, y);
+  hipLaunchKernelGGL(fp8_finish_kernel<kPartFinTok>, finish_grid(m, n, kPartFinTok), dim3(256),
+                     finish_lds(r, kPartFinTok), stream, part, slices, (int)m, (int)n, t, tks, b, (int)r, y);
   return hipGetLastError();
 }
 
@@ -525,7 +548,7 @@ hipError_t launch_fp8_linear(const uint16_t* x, int64_t m, int64_t n, int64_t k,
     if (e != hipSuccess) return e;
     const int sl = fp8_splitk_slices(m, n, k);
     if (sl > 1)
-      hipLaunchKernelGGL(fp8_finish_kernel, finish_grid(m, n), dim3(256), finish_lds(r), st, w.ypart, sl, (int)m,
+      hipLaunchKernelGGL(fp8_finish_kernel<kFinTok>, finish_grid(m, n), dim3(256), finish_lds(r), st, w.ypart, sl, (int)m,
                          (int)n, w.tpart, tsl, r > 0 ? b : nullptr, (int)r, y);
     return hipGetLastError();
   }
@@ -533,7 +556,7 @@ hipError_t launch_fp8_linear(const uint16_t* x, int64_t m, int64_t n, int64_t k,
     const DecSplit d = dec_split(m, n, k, chunk);
     const dim3 grid((unsigned)((n + kDecRows - 1) / kDecRows), (unsigned)d.slices);
     launch_decode<1>(a8, grid, x, w, m, n, k, codes, scales, d.slice, st);
-    hipLaunchKernelGGL(fp8_finish_kernel, finish_grid(m, n), dim3(256), finish_lds(r), st, w.ypart, d.slices, (int)m,
+    hipLaunchKernelGGL(fp8_finish_kernel<kFinTok>, finish_grid(m, n), dim3(256), finish_lds(r), st, w.ypart, d.slices, (int)m,
                        (int)n, w.tpart, tsl, r > 0 ? b : nullptr, (int)r, y);
     return hipGetLastError();
   }
@@ -555,7 +578,7 @@ hipError_t launch_fp8_linear(const uint16_t* x, int64_t m, int64_t n, int64_t k,
   else
     launch_gemm<kNtR8>(sl > 1, tiles, sl, sw, lora, m, n, scales, y, w.ypart, st);
   if (sl > 1)
-    hipLaunchKernelGGL(fp8_finish_kernel, finish_grid(m, n), dim3(256), finish_lds(r), st, w.ypart, sl, (int)m, (int)n,
+    hipLaunchKernelGGL(fp8_finish_kernel<kFinTok>, finish_grid(m, n), dim3(256), finish_lds(r), st, w.ypart, sl, (int)m, (int)n,
                        w.tpart, tsl, r > 0 ? b : nullptr, (int)r, y);
   return hipGetLastError();
 }
