@@ -338,3 +338,26 @@ def test_workspace_check_and_reset_validate_arguments(lib):
     assert lib.fp4rl_linear_workspace_check(FAKE + 4, counter_bytes, None) == ERR_ALIGN
     assert lib.fp4rl_linear_workspace_reset(FAKE + 8, counter_bytes, None) == ERR_ALIGN
     lib.fp4rl_debug_lora_handoff(0, 0)  # the defaults; touches no device
+
+
+@pytest.mark.parametrize("m,n,k,r,kernel", [
+    # decode: one or two tokens, 3..16 tokens, 17..128 tokens
+    (1, 18944, 3584, 32, "gemv_kernel<1, 4, 4>"),
+    (1, 3584, 18944, 32, "gemv_kernel<1, 16, 4>"),
+    (8, 4608, 3584, 32, "skinny_kernel<1, 2, 8>"),
+    (32, 18944, 3584, 32, "splitk_kernel<4, 2, 4, 2>"),
+    # 97..128 tokens: the mid-batch kernel on wide matrices, with a K split on long K, else split-K
+    (128, 27648, 5120, 64, "mid_kernel<1, 2, 4, 2, 3>"),
+    (128, 5120, 27648, 64, "mid_kernel<1, 2, 4, 2, 3>"),
+    (128, 3584, 18944, 32, "splitk_kernel<4, 2, 4, 2>"),
+    # prefill: eight waves where the 512-feature workgroups fill whole rounds of 256, else four
+    (8192, 18944, 3584, 32, "prefill_kernel<2, 8>"),
+    (8192, 3584, 18944, 32, "prefill_kernel<2, 8>"),
+    (8192, 3584, 3584, 32, "prefill_kernel<2, 8>"),
+    (8192, 4608, 3584, 32, "prefill_kernel<2, 4>"),
+    (8192, 5120, 5120, 32, "prefill_kernel<2, 4>"),
+    (2048, 18944, 3584, 32, "prefill_kernel<2, 4>"),
+])
+def test_kernel_dispatch(lib, m, n, k, r, kernel):
+    """The main kernel the library picks for the measured shapes (a host query: no GPU needed)."""
+    assert fr.fp4_linear_kernel_name(m, n, k, r) == kernel
